@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Throughput of the gfx950 gated diagonal linear-recurrence scans on one MI355X.
+
+Headline (the JSON ``value``): the multi-scale selective scan at B=4, L=2048, D=1536, N=16,
+bf16 inputs, fp32 state and output, in state updates per second.  One step is one full
+selective scan (softplus, discretisation, recurrence, readout, skip and silu gate) over one
+batch of synthetic input already resident in HBM.  Three input sets rotate so the 256 MB
+Infinity Cache cannot serve the 126 MB working set.
+
+The JSON line also carries:
+  roofline      the dominant kernel against its roofline, with per-step HIP-event timing on
+                the stream the kernels run on;
+  cpu_baseline  the fp64 CPU oracle timed on the host (reported baseline, not a target);
+  forms         the other workloads (RG-LRU fp32 and bf16, RG-LRU decode, HGRN2, packed
+                variable-length selective scan) with their own throughput and GB/s.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-forms] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+FP32_VECTOR_TFLOPS = 157.3   # MI355X fp32 vector, published
+BF16_MFMA_TFLOPS = 2500.0    # MI355X dense bf16 matrix, published
+
+
+# ----------------------------------------------------------------------------- algorithmic sizes
+def selective_bytes(B, L, D, N, in_b=2, out_b=4, z=True, skip=True, nseq=None):
+    act = B * L * D
+    b = act * in_b * (3 if z else 2) + 2 * B * L * N * in_b + D * N * 4 + act * out_b
+    if skip:
+        b += D * 4
+    if nseq is not None:
+        b += (nseq + 1) * 4
+    return b
+
+
+# Algorithmic flops per selective state update: delta*A (1), exp (1), (delta*x)*B_n (1),
+# h = abar*h + bbar (2), y += C_n*h (2).
+SELECTIVE_FLOPS_PER_UPDATE = 7
+
+
+def rglru_bytes(B, L, D, in_b=2, out_b=4):
+    return B * L * D * (3 * in_b + out_b) + D * 4
+
+
+def hgrn2_bytes(B, L, H, d, in_b=2, out_b=4):
+    return B * L * H * d * (4 * in_b + out_b)
+
+
+# ----------------------------------------------------------------------------- timing helpers
+def time_calls(fn, n_sets, steps, warmup):
+    """Run ``fn(i % n_sets)`` warmup times, then time ``steps`` calls with one event pair per call
+    on torch's current stream (the stream the library launches on).  Returns (ms_per_step,
+    mean per-call event ms, min per-call event ms)."""
+    import torch
+    for i in range(warmup):
+        fn(i % n_sets)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        fn(i % n_sets)
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    total = starts[0].elapsed_time(ends[-1])
+    return total / steps, float(np.mean(per)), float(np.min(per)), wall / steps
+
+
+def dev_bf16(bits, device):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+# ----------------------------------------------------------------------------- headline
+def headline(args, device):
+    import torch
+    import selective_state_space_diag_amd as ssd
+    from selective_state_space_diag_amd import synth
+
+    cfg = synth.CONFIGS[1]
+    B, L, D, N = cfg["B"], cfg["L"], cfg["D"], cfg["N"]
+    n_sets = 3
+    sets = []
+    host_inputs = None
+    for k in range(n_sets):
+        inp = synth.config_inputs(1, seed=1001 + 100 * k)
+        if k == 0:
+            host_inputs = inp
+        t = {n: dev_bf16(v.data, device) for n, v in inp.t.items()}
+        sets.append(dict(t=t, A=torch.from_numpy(inp.p["A"]).to(device),
+                         Dskip=torch.from_numpy(inp.p["Dskip"]).to(device)))
+
+    def step(i):
+        s = sets[i]
+        t = s["t"]
+        return ssd.selective_scan(t["x"], t["dt"], s["A"], t["Bm"], t["Cm"], Dskip=s["Dskip"], z=t["z"],
+                                  dt_softplus=True)
+
+    ms, mean_call, min_call, wall = time_calls(step, n_sets, args.steps, args.warmup)
+    updates = B * L * D * N
+    nbytes = selective_bytes(B, L, D, N)
+    res = dict(ms=ms, mean_call_ms=mean_call, min_call_ms=min_call, updates=updates, bytes=nbytes,
+               host_ms=wall)
+    return res, host_inputs
+
+
+def cpu_baseline(host_inputs):
+    """The fp64 oracle on the first batch row of the headline workload (1 x 2048 x 1536 x 16)."""
+    import oracle
+    t = host_inputs.t
+    sl = slice(0, 1)
+    g = lambda n: t[n].f64()[sl]
+    x, dt, z, Bm, Cm = g("x"), g("dt"), g("z"), g("Bm"), g("Cm")
+    A = host_inputs.p["A"].astype(np.float64)
+    Dskip = host_inputs.p["Dskip"].astype(np.float64)
+    oracle.lib()
+    t0 = time.perf_counter()
+    oracle.selective_scan(x, dt, A, Bm, Cm, Dskip=Dskip, z=z, dt_softplus=True)
+    sec = time.perf_counter() - t0
+    updates = x.shape[0] * x.shape[1] * x.shape[2] * A.shape[1]
+    return dict(value=updates / sec, unit="state-updates/s", cores=1, kind="oracle",
+                sample=f"batch row 0 of the headline workload: 1x2048x1536 channels x 16 states "
+                       f"({updates} updates) in {sec:.2f} s, single-threaded fp64")
+
+
+# ----------------------------------------------------------------------------- other workloads
+def forms(args, device):
+    import torch
+    import selective_state_space_diag_amd as ssd
+    from selective_state_space_diag_amd import synth
+
+    out = {}
+    gen = torch.Generator(device=device)
+    gen.manual_seed(7)
+
+    def randn(shape, std=1.0, mean=0.0, dtype=torch.bfloat16):
+        t = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+        return (t * std + mean).to(dtype)
+
+    def record(name, ms, updates, nbytes, extra=None):
+        d = dict(ms=round(ms, 5), state_updates_per_s=updates / (ms * 1e-3),
+                 hbm_gbs=nbytes / (ms * 1e-3) / 1e9, hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                 algorithmic_bytes=nbytes, state_updates=updates)
+        if extra:
+            d.update(extra)
+        out[name] = d
+        print(f"# {name}: {ms:.4f} ms  {d['state_updates_per_s']:.3e} upd/s  {d['hbm_gbs']:.0f} GB/s",
+              file=sys.stderr, flush=True)
+
+    # --- RG-LRU fp32, B=2 L=128 D=64 (latency bound)
+    B, L, D = 2, 128, 64
+    x, r, i = (randn((B, L, D), dtype=torch.float32) for _ in range(3))
+    a_log = torch.log(torch.empty(D, device=device).uniform_(0.9, 0.999, generator=gen))
+    ms = time_calls(lambda k: ssd.rglru_scan(x, r, i, a_log, 8.0), 1, 50, 5)[1]
+    record("rglru_fp32_B2_L128_D64", ms, B * L * D, rglru_bytes(B, L, D, 4, 4))
+
+    # --- RG-LRU bf16, B=8 L=8192 D=2560
+    B, L, D = 8, 8192, 2560
+    x, r, i = (randn((B, L, D)) for _ in range(3))
+    a_log = torch.log(torch.empty(D, device=device).uniform_(0.9, 0.999, generator=gen))
+    ms = time_calls(lambda k: ssd.rglru_scan(x, r, i, a_log, 8.0), 1, 10, 2)[1]
+    record("rglru_bf16_B8_L8192_D2560", ms, B * L * D, rglru_bytes(B, L, D))
+    del x, r, i
+
+    # --- RG-LRU decode, B=256 D=2560, 256 steps carrying the state (one launch per step)
+    B, D, S = 256, 2560, 256
+    xs, rs, is_ = (randn((S, B, D)) for _ in range(3))
+    state = torch.zeros(B, D, device=device)
+
+    def decode(k):
+        for s in range(S):
+            ssd.rglru_update(xs[s], rs[s], is_[s], a_log, 8.0, state)
+
+    ms = time_calls(decode, 1, 3, 1)[1]
+    per_step_bytes = B * D * (3 * 2 + 4 + 4 + 4)
+    record("rglru_decode_B256_D2560_256steps", ms, B * D * S, per_step_bytes * S,
+           dict(us_per_step=ms * 1e3 / S))
+    del xs, rs, is_
+
+    # --- HGRN2 bf16, B=8 H=16 d=128 L=4096, lower bound 0.5
+    B, L, H, dd = 8, 4096, 16, 128
+    q, k, v = (randn((B, L, H, dd), std=dd ** -0.5) for _ in range(3))
+    g = randn((B, L, H, dd), mean=2.0)
+    ms = time_calls(lambda kk: ssd.hgrn2_scan(q, k, v, g, 0.5), 1, 3, 1)[1]
+    flops = 2 * B * L * H * (2 * 64 * dd + 2 * dd * dd)  # chunked form at chunk 64
+    record("hgrn2_bf16_B8_H16_d128_L4096", ms, B * L * H * dd * dd, hgrn2_bytes(B, L, H, dd),
+           dict(mfma_equiv_tflops=flops / (ms * 1e-3) / 1e12,
+                mfma_util=flops / (ms * 1e-3) / 1e12 / BF16_MFMA_TFLOPS))
+    del q, k, v, g
+
+    # --- packed varlen selective, L=131072, 32 sequences, D=4096, N=16
+    Lt, D, N, ns = 131072, 4096, 16, 32
+    lengths = synth.varlen_lengths(Lt, ns, 1004)
+    cu = torch.from_numpy(synth.cu_seqlens_from_lengths(lengths)).to(device)
+    x, z = randn((1, Lt, D)), randn((1, Lt, D))
+    A = torch.from_numpy(synth.multiscale_A(D, N, 4)).to(device)
+    delta0 = torch.exp(torch.empty(D, device=device).uniform_(np.log(1e-3), np.log(1e-1), generator=gen))
+    delta = torch.exp(randn((1, Lt, D), std=0.1, dtype=torch.float32)) * delta0
+    dt = (delta + torch.log(-torch.expm1(-delta))).to(torch.bfloat16)
+    del delta
+    Bm, Cm = randn((1, Lt, N), std=1.0 / N), randn((1, Lt, N), std=1.0 / N)
+    Dskip = torch.ones(D, device=device)
+    ms = time_calls(lambda kk: ssd.selective_scan(x, dt, A, Bm, Cm, Dskip=Dskip, z=z, cu_seqlens=cu,
+                                                  check_cu_seqlens=False), 1, 5, 1)[1]
+    record("selective_varlen_L131072_D4096_N16_32seq", ms, Lt * D * N, selective_bytes(1, Lt, D, N, nseq=ns))
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-forms", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the scans shard with no communication across channels, batches "
+              "and heads, and this build runs on a single MI355X; use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+
+    head, host_inputs = headline(args, device)
+    ms = head["ms"]
+    value = head["updates"] / (ms * 1e-3)
+    call_s = head["mean_call_ms"] * 1e-3
+    achieved_tflops = head["updates"] * SELECTIVE_FLOPS_PER_UPDATE / call_s / 1e12
+    hbm_gbs = head["bytes"] / call_s / 1e9
+    print(f"# headline: {ms:.4f} ms/step, mean call {head['mean_call_ms']:.4f} ms, {value:.3e} upd/s, "
+          f"{hbm_gbs:.0f} GB/s", file=sys.stderr, flush=True)
+
+    line = {
+        "metric": "scan state-updates/s + achieved HBM GB/s (% of peak), fwd, 1 MI355X",
+        "value": value,
+        "unit": "state-updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "multi-scale selective scan, B=4 L=2048 D=1536 N=16, 4 scales, bf16 in, "
+                               "fp32 state and out, softplus dt, skip D=1, silu(z) gate",
+                   "B": 4, "L": 2048, "D": 1536, "N": 16, "input_dtype": "bf16", "output_dtype": "f32"},
+        "hbm": {"achieved_gbs": hbm_gbs, "peak_gbs": HBM_PEAK_GBS, "frac": hbm_gbs / HBM_PEAK_GBS,
+                "algorithmic_bytes": head["bytes"]},
+        "roofline": {"bound": "alu", "achieved": achieved_tflops, "peak": FP32_VECTOR_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved_tflops / FP32_VECTOR_TFLOPS, "traffic": None,
+                     "kernel": "selective scan (aggregate + scan kernels of one call)",
+                     "flops_per_update": SELECTIVE_FLOPS_PER_UPDATE,
+                     "mean_call_ms": head["mean_call_ms"], "min_call_ms": head["min_call_ms"]},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(host_inputs)
+    if not args.no_forms:
+        line["forms"] = forms(args, device)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

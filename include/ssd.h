@@ -1,0 +1,154 @@
+/*
+ * ssd.h -- C ABI of the MI355X (gfx950) gated diagonal linear-recurrence scans.
+ *
+ * Three forms of h_t = a_t (.) h_{t-1} + b_t, each as a full-sequence scan and a
+ * single-step decode update:
+ *
+ *   RG-LRU        state size 1 per channel          ssd_rglru_scan / ssd_rglru_update
+ *   selective     N <= 16 states per channel        ssd_selective_scan / ssd_selective_update
+ *   HGRN2         d x d matrix state per head       ssd_hgrn2_scan / ssd_hgrn2_update
+ *
+ * Conventions (every entry point):
+ *   - Sizes are int64_t element counts; every pointer is DEVICE memory owned by
+ *     the caller, dense row-major, with the layout given per function.
+ *   - Activations are SSD_F32 or SSD_BF16 (the `in` dtype); parameters (a_log,
+ *     A, Dskip, dt_bias) and recurrent state are always fp32.  Outputs are fp32
+ *     or, when `in` is SSD_BF16, optionally bf16 (round-to-nearest-even).
+ *   - The library computes in fp32 from the input bits; state stays fp32.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously; the call returns after the launch.
+ *   - Every argument is validated on the host before anything is enqueued.  A
+ *     non-zero status means nothing was launched and nothing was written;
+ *     ssd_last_error() then holds a thread-local message.  Faults during
+ *     execution surface at the caller's next synchronisation, as with any HIP
+ *     call.
+ *   - Base pointers must be 16-byte aligned.  Outputs must not overlap inputs.
+ *   - Empty problems (a zero size) launch nothing except copying the initial
+ *     state to the final-state output (or zero-filling it).
+ *   - The scans use a device scratch buffer that the library allocates on first
+ *     use per (device, stream) and keeps until the process ends (it grows when a
+ *     larger problem needs it).  Calls on one stream are serialised by the
+ *     stream; calls on different streams use different scratch buffers.
+ *   - NaN / Inf inputs propagate by IEEE rules; nothing is trapped.
+ */
+#ifndef SSD_H
+#define SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+enum {
+  SSD_OK = 0,
+  SSD_ERR_NULL = 1,   /* a required pointer is NULL                              */
+  SSD_ERR_SHAPE = 2,  /* a size is negative or outside the supported range        */
+  SSD_ERR_DTYPE = 3,  /* unsupported dtype or dtype combination                   */
+  SSD_ERR_ALIGN = 4,  /* a base pointer is not 16-byte aligned                    */
+  SSD_ERR_VALUE = 5,  /* a scalar argument is out of range (c, lower_bound, ...)  */
+  SSD_ERR_ALIAS = 6,  /* an output overlaps an input                              */
+  SSD_ERR_HIP = 7     /* the HIP runtime reported an error (allocation, launch)   */
+};
+
+/* Static description of a status code. */
+const char* ssd_status_str(int status);
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char* ssd_last_error(void);
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int ssd_version(void);
+
+/* ---------------------------------------------------------------------------------------------
+ * RG-LRU scan.  Defined by the lrnnx documentation, "lrnnx.models.ltv.rglru" (RGLRU.forward gate
+ * computation and RGLRU.step recurrence):  for each batch b, channel d and step t
+ *     r = sigmoid(r_logit), i = sigmoid(i_logit), log a_t = c * r * a_log[d],
+ *     h_t = a_t * h_{t-1} + sqrt(1 - a_t^2) * (i * x),     y_t = h_t,
+ * starting from h0 (or 0).  The base a = exp(a_log) lies in (0, 1) for a_log < 0.
+ *   x, r_logit, i_logit : [B, L, D] activations (in dtype)
+ *   a_log               : [D] fp32          c : finite scalar (8 in the Griffin block)
+ *   h0                  : [B, D] fp32 or NULL (= zeros)
+ *   y                   : [B, L, D] (out dtype)
+ *   h_last              : [B, D] fp32 or NULL; receives h_{L-1} (h0 when L = 0)
+ * Errors: SSD_ERR_NULL (x, r_logit, i_logit, a_log, y when B*L*D > 0), SSD_ERR_SHAPE (negative
+ * size), SSD_ERR_DTYPE, SSD_ERR_ALIGN, SSD_ERR_VALUE (c not finite), SSD_ERR_ALIAS.
+ * ------------------------------------------------------------------------------------------- */
+int ssd_rglru_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype,
+                   const void* x, const void* r_logit, const void* i_logit,
+                   const float* a_log, float c, const float* h0,
+                   void* y, float* h_last, void* stream);
+
+/* One RG-LRU decode step (RGLRU.step: single token, state carried by the caller).
+ *   x, r_logit, i_logit : [B, D] (in dtype);  a_log : [D] fp32
+ *   state               : [B, D] fp32, read then overwritten with h_t (in place)
+ *   y                   : [B, D] (out dtype), y = h_t
+ * Errors as ssd_rglru_scan; y must not overlap state. */
+int ssd_rglru_update(int64_t B, int64_t D, int in_dtype, int out_dtype,
+                     const void* x, const void* r_logit, const void* i_logit,
+                     const float* a_log, float c, float* state, void* y, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Multi-scale selective scan.  Defined by the cortexnet 3.2.1 package, cortexnet/ssm.py,
+ * MultiScaleSSM.forward and MultiScaleSSM._selective_scan:  for each sequence, channel d, state
+ * n and step t
+ *     delta = dt + dt_bias[d], then softplus(delta) if dt_softplus (identity above 20),
+ *     abar  = exp(min(delta * A[d][n], 20)),      h_n = abar * h_n + (delta * B_n) * x,
+ *     y     = (sum_n C_n * h_n + Dskip[d] * x) * silu(z).
+ *   x, dt, z, y  : [B, L, D] (z NULL = no gate)       A : [D, N] fp32
+ *   Bm, Cm       : [B, L, N] (in dtype)                Dskip, dt_bias : [D] fp32 or NULL (= 0)
+ *   cu_seqlens   : device int32[nseq + 1] or NULL.  With it, B must be 1 and the L rows are
+ *                  nseq packed sequences, sequence s = rows [cu_seqlens[s], cu_seqlens[s+1]);
+ *                  each starts from its own h0 (or 0).  The table must satisfy cu_seqlens[0] = 0,
+ *                  non-decreasing, cu_seqlens[nseq] = L (the caller's duty: it is device memory
+ *                  and is not read on the host).  Zero-length sequences are allowed.
+ *   h0, h_last   : [B or nseq, D, N] fp32 or NULL.
+ *   Supported N : 1, 2, 4, 8, 16.
+ * Errors: SSD_ERR_NULL, SSD_ERR_SHAPE (negative size, unsupported N, cu_seqlens with B != 1,
+ * nseq < 0), SSD_ERR_DTYPE, SSD_ERR_ALIGN, SSD_ERR_ALIAS.
+ * ------------------------------------------------------------------------------------------- */
+int ssd_selective_scan(int64_t B, int64_t L, int64_t D, int64_t N, int in_dtype, int out_dtype,
+                       const void* x, const void* dt, const float* A,
+                       const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                       const float* dt_bias, int dt_softplus,
+                       const int32_t* cu_seqlens, int64_t nseq,
+                       const float* h0, void* y, float* h_last, void* stream);
+
+/* One selective decode step (the L == 1 path of MultiScaleSSM.forward with past_state).
+ *   x, dt, z, y : [B, D];  Bm, Cm : [B, N];  A : [D, N] fp32;  state : [B, D, N] fp32 in place.
+ * Other arguments and errors as ssd_selective_scan. */
+int ssd_selective_update(int64_t B, int64_t D, int64_t N, int in_dtype, int out_dtype,
+                         const void* x, const void* dt, const float* A,
+                         const void* Bm, const void* Cm, const float* Dskip,
+                         const void* z, const float* dt_bias, int dt_softplus,
+                         float* state, void* y, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * HGRN2 matrix-state scan.  Defined by the frankenstein-transformer documentation, "HGRN2
+ * Attention" (state-update equation and forget gate):  per batch b, head h and step t
+ *     g_i  = lower_bound + (1 - lower_bound) * sigmoid(g_logit_i),
+ *     S[i][j] = g_i * S[i][j] + v_i * k_j,        o_i = sum_j S[i][j] * q_j,
+ * i.e. S_t = diag(g_t) S_{t-1} + v_t k_t^T and o_t = S_t q_t (readout includes token t).
+ *   q, k, v, g_logit, o : [B, L, H, d] (in dtype / out dtype)
+ *   S0, S_last          : [B, H, d, d] fp32 or NULL; S[i][j] with i = value row, j = key column
+ *   lower_bound         : in [0, 1]
+ *   Supported d : multiples of 16 up to 128.
+ * Errors: SSD_ERR_NULL, SSD_ERR_SHAPE, SSD_ERR_DTYPE, SSD_ERR_ALIGN, SSD_ERR_VALUE
+ * (lower_bound outside [0, 1]), SSD_ERR_ALIAS.
+ * ------------------------------------------------------------------------------------------- */
+int ssd_hgrn2_scan(int64_t B, int64_t L, int64_t H, int64_t d, int in_dtype, int out_dtype,
+                   const void* q, const void* k, const void* v, const void* g_logit,
+                   float lower_bound, const float* S0, void* o, float* S_last, void* stream);
+
+/* One HGRN2 decode step.  q, k, v, g_logit, o : [B, H, d];  S : [B, H, d, d] fp32 in place.
+ * Errors as ssd_hgrn2_scan. */
+int ssd_hgrn2_update(int64_t B, int64_t H, int64_t d, int in_dtype, int out_dtype,
+                     const void* q, const void* k, const void* v, const void* g_logit,
+                     float lower_bound, float* S, void* o, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H */

@@ -1,0 +1,277 @@
+"""Python binding of the gfx950 gated diagonal linear-recurrence scans.
+
+A thin ctypes layer over ``libssd.so`` (the C ABI declared in ``include/ssd.h``).
+It only marshals arguments: checks tensor placement, dtype, shape and contiguity,
+allocates outputs with torch, and passes raw device pointers plus torch's current
+HIP stream.  Every step of every scan runs in the HIP kernels.  There is no CPU
+or eager fallback: importing works without a GPU, but each call raises if the
+library is not built or no GPU is present.
+
+Entry points (same names as the C ABI without the ``ssd_`` prefix):
+    rglru_scan, rglru_update, selective_scan, selective_update, hgrn2_scan, hgrn2_update
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libssd.so")
+
+SSD_F32, SSD_BF16 = 0, 1
+STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_DTYPE", 4: "SSD_ERR_ALIGN",
+                5: "SSD_ERR_VALUE", 6: "SSD_ERR_ALIAS", 7: "SSD_ERR_HIP"}
+
+# Every symbol include/ssd.h declares.
+EXPORTS = ("ssd_status_str", "ssd_last_error", "ssd_version", "ssd_rglru_scan", "ssd_rglru_update",
+           "ssd_selective_scan", "ssd_selective_update", "ssd_hgrn2_scan", "ssd_hgrn2_update")
+
+
+class SSDError(RuntimeError):
+    def __init__(self, status: int, fn: str, detail: str):
+        self.status = status
+        super().__init__(f"{fn}: {STATUS_NAMES.get(status, status)}: {detail}")
+
+
+class SSDValueError(SSDError, ValueError):
+    pass
+
+
+_lib = None
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_fp = ctypes.c_void_p
+
+
+def lib() -> ctypes.CDLL:
+    """Load ``libssd.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m selective_state_space_diag_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.ssd_status_str.restype = ctypes.c_char_p
+        L.ssd_status_str.argtypes = [ctypes.c_int]
+        L.ssd_last_error.restype = ctypes.c_char_p
+        L.ssd_last_error.argtypes = []
+        L.ssd_version.restype = ctypes.c_int
+        L.ssd_rglru_scan.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _fp, ctypes.c_float,
+                                     _fp, _vp, _fp, _vp]
+        L.ssd_rglru_update.argtypes = [_i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _fp, ctypes.c_float, _fp,
+                                       _vp, _vp]
+        L.ssd_selective_scan.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _fp, _vp, _vp,
+                                         _fp, _vp, _fp, ctypes.c_int, _vp, _i64, _fp, _vp, _fp, _vp]
+        L.ssd_selective_update.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _fp, _vp, _vp, _fp,
+                                           _vp, _fp, ctypes.c_int, _fp, _vp, _vp]
+        L.ssd_hgrn2_scan.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                     ctypes.c_float, _fp, _vp, _fp, _vp]
+        L.ssd_hgrn2_update.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                       ctypes.c_float, _fp, _vp, _vp]
+        for name in EXPORTS[3:]:
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _raise(status: int, fn: str):
+    if status == 0:
+        return
+    detail = lib().ssd_last_error().decode(errors="replace")
+    if status == 7:
+        raise SSDError(status, fn, detail)
+    raise SSDValueError(status, fn, detail)
+
+
+# ----------------------------------------------------------------------------- torch marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return SSD_F32
+    if t.dtype == torch.bfloat16:
+        return SSD_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: activations must be float32 or bfloat16")
+
+
+def _out_code(out_dtype) -> int:
+    torch = _torch()
+    if out_dtype in (None, torch.float32):
+        return SSD_F32
+    if out_dtype == torch.bfloat16:
+        return SSD_BF16
+    raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+
+
+def _dev(t, name, shape=None, dtype=None):
+    """Check a device tensor argument and return its data pointer (None for None)."""
+    if t is None:
+        return None
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _act(ts, names):
+    """All activation tensors share one dtype; returns its code."""
+    code = None
+    for t, n in zip(ts, names):
+        if t is None:
+            continue
+        c = _dtype_code(t)
+        if code is None:
+            code = c
+        elif c != code:
+            raise TypeError(f"{n} has dtype {t.dtype}; all activations must share one dtype")
+    return code
+
+
+# ----------------------------------------------------------------------------- RG-LRU
+def rglru_scan(x, r_logit, i_logit, a_log, c: float = 8.0, h0=None, return_last_state: bool = False,
+               out_dtype=None):
+    """RG-LRU scan over [B, L, D] (see ``ssd_rglru_scan``).  Returns y, or (y, h_last)."""
+    torch = _torch()
+    B, L, D = x.shape
+    code = _act([x, r_logit, i_logit], ["x", "r_logit", "i_logit"])
+    oc = _out_code(out_dtype)
+    y = torch.empty((B, L, D), device=x.device, dtype=torch.bfloat16 if oc == SSD_BF16 else torch.float32)
+    h_last = torch.empty((B, D), device=x.device, dtype=torch.float32) if return_last_state else None
+    st = lib().ssd_rglru_scan(B, L, D, code, oc, _dev(x, "x"), _dev(r_logit, "r_logit", x.shape),
+                              _dev(i_logit, "i_logit", x.shape), _dev(a_log, "a_log", (D,), torch.float32),
+                              float(c), _dev(h0, "h0", (B, D), torch.float32), _dev(y, "y"),
+                              _dev(h_last, "h_last"), _stream(x.device))
+    _raise(st, "rglru_scan")
+    return (y, h_last) if return_last_state else y
+
+
+def rglru_update(x, r_logit, i_logit, a_log, c: float, state, out_dtype=None):
+    """One decode step; ``state`` [B, D] fp32 is updated in place.  Returns y [B, D]."""
+    torch = _torch()
+    B, D = x.shape
+    code = _act([x, r_logit, i_logit], ["x", "r_logit", "i_logit"])
+    oc = _out_code(out_dtype)
+    y = torch.empty((B, D), device=x.device, dtype=torch.bfloat16 if oc == SSD_BF16 else torch.float32)
+    st = lib().ssd_rglru_update(B, D, code, oc, _dev(x, "x"), _dev(r_logit, "r_logit", x.shape),
+                                _dev(i_logit, "i_logit", x.shape), _dev(a_log, "a_log", (D,), torch.float32),
+                                float(c), _dev(state, "state", (B, D), torch.float32), _dev(y, "y"), _stream(x.device))
+    _raise(st, "rglru_update")
+    return y
+
+
+# ----------------------------------------------------------------------------- selective
+def _cu_seqlens_device(cu_seqlens, L, device, check: bool):
+    torch = _torch()
+    if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.device.type == "cuda":
+        dev = cu_seqlens
+        host = cu_seqlens.cpu().numpy() if check else None
+    else:
+        host = np.ascontiguousarray(np.asarray(cu_seqlens), dtype=np.int32)
+        dev = torch.from_numpy(host).to(device)
+    if dev.dtype != torch.int32 or dev.dim() != 1 or not dev.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor")
+    if host is not None:
+        if host.size < 1 or host[0] != 0 or host[-1] != L or np.any(np.diff(host.astype(np.int64)) < 0):
+            raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at L")
+    return dev
+
+
+def selective_scan(x, dt, A, Bm, Cm, Dskip=None, z=None, dt_bias=None, dt_softplus: bool = True,
+                   cu_seqlens=None, h0=None, return_last_state: bool = False, out_dtype=None,
+                   check_cu_seqlens: bool = True):
+    """Multi-scale selective scan over [B, L, D] with N states (see ``ssd_selective_scan``).
+
+    ``cu_seqlens`` (int32 [nseq + 1], host or device) packs nseq sequences into B = 1.
+    Returns y, or (y, h_last) with h_last [B or nseq, D, N]."""
+    torch = _torch()
+    B, L, D = x.shape
+    N = A.shape[1]
+    code = _act([x, dt, Bm, Cm, z], ["x", "dt", "Bm", "Cm", "z"])
+    oc = _out_code(out_dtype)
+    cu = None
+    nseq = B
+    if cu_seqlens is not None:
+        cu = _cu_seqlens_device(cu_seqlens, L, x.device, check_cu_seqlens)
+        nseq = cu.numel() - 1
+    y = torch.empty((B, L, D), device=x.device, dtype=torch.bfloat16 if oc == SSD_BF16 else torch.float32)
+    h_last = torch.empty((nseq, D, N), device=x.device, dtype=torch.float32) if return_last_state else None
+    st = lib().ssd_selective_scan(
+        B, L, D, N, code, oc, _dev(x, "x"), _dev(dt, "dt", x.shape), _dev(A, "A", (D, N), torch.float32),
+        _dev(Bm, "Bm", (B, L, N)), _dev(Cm, "Cm", (B, L, N)), _dev(Dskip, "Dskip", (D,), torch.float32),
+        _dev(z, "z", x.shape), _dev(dt_bias, "dt_bias", (D,), torch.float32), int(bool(dt_softplus)),
+        _dev(cu, "cu_seqlens"), nseq, _dev(h0, "h0", (nseq, D, N), torch.float32), _dev(y, "y"),
+        _dev(h_last, "h_last"), _stream(x.device))
+    _raise(st, "selective_scan")
+    return (y, h_last) if return_last_state else y
+
+
+def selective_update(x, dt, A, Bm, Cm, state, Dskip=None, z=None, dt_bias=None, dt_softplus: bool = True,
+                     out_dtype=None):
+    """One decode step; ``state`` [B, D, N] fp32 is updated in place.  Returns y [B, D]."""
+    torch = _torch()
+    B, D = x.shape
+    N = A.shape[1]
+    code = _act([x, dt, Bm, Cm, z], ["x", "dt", "Bm", "Cm", "z"])
+    oc = _out_code(out_dtype)
+    y = torch.empty((B, D), device=x.device, dtype=torch.bfloat16 if oc == SSD_BF16 else torch.float32)
+    st = lib().ssd_selective_update(
+        B, D, N, code, oc, _dev(x, "x"), _dev(dt, "dt", x.shape), _dev(A, "A", (D, N), torch.float32),
+        _dev(Bm, "Bm", (B, N)), _dev(Cm, "Cm", (B, N)), _dev(Dskip, "Dskip", (D,), torch.float32),
+        _dev(z, "z", x.shape), _dev(dt_bias, "dt_bias", (D,), torch.float32), int(bool(dt_softplus)),
+        _dev(state, "state", (B, D, N), torch.float32), _dev(y, "y"), _stream(x.device))
+    _raise(st, "selective_update")
+    return y
+
+
+# ----------------------------------------------------------------------------- HGRN2
+def hgrn2_scan(q, k, v, g_logit, lower_bound: float, S0=None, return_last_state: bool = False, out_dtype=None):
+    """HGRN2 matrix-state scan over [B, L, H, d] (see ``ssd_hgrn2_scan``).  Returns o, or (o, S_last)."""
+    torch = _torch()
+    B, L, H, d = q.shape
+    code = _act([q, k, v, g_logit], ["q", "k", "v", "g_logit"])
+    oc = _out_code(out_dtype)
+    o = torch.empty((B, L, H, d), device=q.device, dtype=torch.bfloat16 if oc == SSD_BF16 else torch.float32)
+    S_last = torch.empty((B, H, d, d), device=q.device, dtype=torch.float32) if return_last_state else None
+    st = lib().ssd_hgrn2_scan(B, L, H, d, code, oc, _dev(q, "q"), _dev(k, "k", q.shape), _dev(v, "v", q.shape),
+                              _dev(g_logit, "g_logit", q.shape), float(lower_bound),
+                              _dev(S0, "S0", (B, H, d, d), torch.float32), _dev(o, "o"), _dev(S_last, "S_last"),
+                              _stream(q.device))
+    _raise(st, "hgrn2_scan")
+    return (o, S_last) if return_last_state else o
+
+
+def hgrn2_update(q, k, v, g_logit, lower_bound: float, S, out_dtype=None):
+    """One decode step; ``S`` [B, H, d, d] fp32 is updated in place.  Returns o [B, H, d]."""
+    torch = _torch()
+    B, H, d = q.shape
+    code = _act([q, k, v, g_logit], ["q", "k", "v", "g_logit"])
+    oc = _out_code(out_dtype)
+    o = torch.empty((B, H, d), device=q.device, dtype=torch.bfloat16 if oc == SSD_BF16 else torch.float32)
+    st = lib().ssd_hgrn2_update(B, H, d, code, oc, _dev(q, "q"), _dev(k, "k", q.shape), _dev(v, "v", q.shape),
+                                _dev(g_logit, "g_logit", q.shape), float(lower_bound),
+                                _dev(S, "S", (B, H, d, d), torch.float32), _dev(o, "o"), _stream(q.device))
+    _raise(st, "hgrn2_update")
+    return o
+
+
+__all__ = ["rglru_scan", "rglru_update", "selective_scan", "selective_update", "hgrn2_scan", "hgrn2_update", "lib",
+           "LIB_PATH", "EXPORTS", "SSDError", "SSDValueError", "SSD_F32", "SSD_BF16"]

@@ -1,0 +1,330 @@
+// api.cpp -- the C ABI declared in include/ssd.h: host-side validation, scratch management and
+// dispatch to the kernel launchers.  Nothing is enqueued unless every check passes.
+#include "ssd.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <utility>
+#include <vector>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return SSD_OK;
+}
+
+// ------------------------------------------------------------------ scratch buffers
+// One buffer per (device, stream, purpose), allocated zero-filled, grown on demand, kept until
+// process exit.  Purposes are kept apart so that one kernel family never reads another's data.
+enum ScratchKind { kScratchRglru = 0, kScratchSelective = 1 };
+
+struct ScratchBuf {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+
+std::mutex g_scratch_mu;
+std::map<std::tuple<int, void*, int>, ScratchBuf> g_scratch;
+
+int get_scratch(void* stream, int kind, size_t need, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(SSD_ERR_HIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchBuf& sb = g_scratch[std::make_tuple(dev, stream, kind)];
+  if (sb.bytes < need) {
+    if (sb.ptr) {
+      // the stream may still be using the old buffer
+      if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)
+        return fail(SSD_ERR_HIP, "hipStreamSynchronize failed while growing scratch");
+      (void)hipFree(sb.ptr);
+      sb.ptr = nullptr;
+      sb.bytes = 0;
+    }
+    size_t bytes = need < (1u << 20) ? (1u << 20) : need;
+    bytes = (bytes + 4095) / 4096 * 4096;
+    void* p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess) return fail(SSD_ERR_HIP, "hipMalloc of scratch failed");
+    if (hipMemset(p, 0, bytes) != hipSuccess) {
+      (void)hipFree(p);
+      return fail(SSD_ERR_HIP, "hipMemset of scratch failed");
+    }
+    sb.ptr = p;
+    sb.bytes = bytes;
+  }
+  *out = sb.ptr;
+  return SSD_OK;
+}
+
+// ------------------------------------------------------------------ validation helpers
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+  const char* name;
+  const void* p;
+  size_t bytes;
+};
+
+bool overlap(const Span& a, const Span& b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), a1 = a0 + a.bytes;
+  const uintptr_t b0 = reinterpret_cast<uintptr_t>(b.p), b1 = b0 + b.bytes;
+  return a0 < b1 && b0 < a1;
+}
+
+int check_alias(const std::vector<Span>& outs, const std::vector<Span>& ins) {
+  for (size_t i = 0; i < outs.size(); ++i) {
+    for (const Span& s : ins)
+      if (overlap(outs[i], s))
+        return fail(SSD_ERR_ALIAS, std::string(outs[i].name) + " overlaps input " + s.name);
+    for (size_t j = i + 1; j < outs.size(); ++j)
+      if (overlap(outs[i], outs[j]))
+        return fail(SSD_ERR_ALIAS, std::string(outs[i].name) + " overlaps output " + outs[j].name);
+  }
+  return SSD_OK;
+}
+
+int check_align(const std::vector<Span>& all) {
+  for (const Span& s : all)
+    if (s.p && !aligned16(s.p)) return fail(SSD_ERR_ALIGN, std::string(s.name) + " is not 16-byte aligned");
+  return SSD_OK;
+}
+
+int check_dtypes(int in, int out) {
+  if (in != SSD_F32 && in != SSD_BF16) return fail(SSD_ERR_DTYPE, "in_dtype must be SSD_F32 or SSD_BF16");
+  if (out != SSD_F32 && out != SSD_BF16) return fail(SSD_ERR_DTYPE, "out_dtype must be SSD_F32 or SSD_BF16");
+  if (in == SSD_F32 && out == SSD_BF16) return fail(SSD_ERR_DTYPE, "bf16 output requires bf16 input");
+  return SSD_OK;
+}
+
+size_t esize(int dtype) { return dtype == SSD_BF16 ? 2 : 4; }
+
+// a*b*c... without signed overflow for the sizes we accept (each factor < 2^40)
+bool too_big(std::initializer_list<int64_t> dims) {
+  double prod = 1.0;
+  for (int64_t d : dims) prod *= (double)d;
+  return prod > 9.0e15;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SSD_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return ok();
+}
+
+#define SSD_TRY(expr)          \
+  do {                         \
+    int _st = (expr);          \
+    if (_st != SSD_OK) return _st; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* ssd_status_str(int status) {
+  switch (status) {
+    case SSD_OK: return "ok";
+    case SSD_ERR_NULL: return "required pointer is NULL";
+    case SSD_ERR_SHAPE: return "invalid or unsupported size";
+    case SSD_ERR_DTYPE: return "unsupported dtype";
+    case SSD_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case SSD_ERR_VALUE: return "scalar argument out of range";
+    case SSD_ERR_ALIAS: return "output overlaps another buffer";
+    case SSD_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* ssd_last_error(void) { return g_last_error.c_str(); }
+
+int ssd_version(void) { return 100; }
+
+// ============================================================================ RG-LRU
+int ssd_rglru_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype, const void* x, const void* r_logit,
+                   const void* i_logit, const float* a_log, float c, const float* h0, void* y, float* h_last,
+                   void* stream) {
+  SSD_TRY(check_dtypes(in_dtype, out_dtype));
+  if (B < 0 || L < 0 || D < 0) return fail(SSD_ERR_SHAPE, "negative size");
+  if (too_big({B, L, D}) || B * ((L + 63) / 64) * ((D + 63) / 64) >= (int64_t)1 << 31)
+    return fail(SSD_ERR_SHAPE, "problem too large");
+  if (!std::isfinite(c)) return fail(SSD_ERR_VALUE, "c must be finite");
+  const int64_t nact = B * L * D;
+  if (nact > 0 && (!x || !r_logit || !i_logit || !y)) return fail(SSD_ERR_NULL, "x, r_logit, i_logit and y are required");
+  if (B * D > 0 && !a_log) return fail(SSD_ERR_NULL, "a_log is required");
+  const size_t ab = (size_t)nact * esize(in_dtype), yb = (size_t)nact * esize(out_dtype);
+  const size_t sb = (size_t)(B * D) * 4;
+  std::vector<Span> ins = {{"x", x, ab}, {"r_logit", r_logit, ab}, {"i_logit", i_logit, ab},
+                           {"a_log", a_log, (size_t)D * 4}, {"h0", h0, sb}};
+  std::vector<Span> outs = {{"y", y, yb}, {"h_last", h_last, sb}};
+  std::vector<Span> all = ins;
+  all.insert(all.end(), outs.begin(), outs.end());
+  SSD_TRY(check_align(all));
+  SSD_TRY(check_alias(outs, ins));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (B * D == 0) return ok();
+  if (L == 0) return hip_status(ssd::launch_copy_or_zero(h_last, h0, B * D, s), "rglru_scan");
+  ssd::RglruScanArgs a{B, L, D, in_dtype == SSD_BF16, out_dtype == SSD_BF16, x, r_logit, i_logit, a_log, c, h0, y, h_last,
+                       nullptr};
+  SSD_TRY(get_scratch(stream, kScratchRglru, ssd::rglru_scan_scratch_bytes(B, L, D), &a.scratch));
+  return hip_status(ssd::launch_rglru_scan(a, s), "rglru_scan launch");
+}
+
+int ssd_rglru_update(int64_t B, int64_t D, int in_dtype, int out_dtype, const void* x, const void* r_logit,
+                     const void* i_logit, const float* a_log, float c, float* state, void* y, void* stream) {
+  SSD_TRY(check_dtypes(in_dtype, out_dtype));
+  if (B < 0 || D < 0) return fail(SSD_ERR_SHAPE, "negative size");
+  if (too_big({B, D}) || B * D >= (int64_t)1 << 38) return fail(SSD_ERR_SHAPE, "problem too large");
+  if (!std::isfinite(c)) return fail(SSD_ERR_VALUE, "c must be finite");
+  const int64_t n = B * D;
+  if (n > 0 && (!x || !r_logit || !i_logit || !a_log || !state || !y))
+    return fail(SSD_ERR_NULL, "x, r_logit, i_logit, a_log, state and y are required");
+  const size_t ab = (size_t)n * esize(in_dtype);
+  std::vector<Span> ins = {{"x", x, ab}, {"r_logit", r_logit, ab}, {"i_logit", i_logit, ab},
+                           {"a_log", a_log, (size_t)D * 4}};
+  std::vector<Span> outs = {{"y", y, (size_t)n * esize(out_dtype)}, {"state", state, (size_t)n * 4}};
+  std::vector<Span> all = ins;
+  all.insert(all.end(), outs.begin(), outs.end());
+  SSD_TRY(check_align(all));
+  SSD_TRY(check_alias(outs, ins));
+  if (n == 0) return ok();
+  ssd::RglruUpdateArgs a{B, D, in_dtype == SSD_BF16, out_dtype == SSD_BF16, x, r_logit, i_logit, a_log, c, state, y};
+  return hip_status(ssd::launch_rglru_update(a, static_cast<hipStream_t>(stream)), "rglru_update launch");
+}
+
+// ============================================================================ selective
+static bool supported_n(int64_t N) { return N == 1 || N == 2 || N == 4 || N == 8 || N == 16; }
+
+int ssd_selective_scan(int64_t B, int64_t L, int64_t D, int64_t N, int in_dtype, int out_dtype, const void* x,
+                       const void* dt, const float* A, const void* Bm, const void* Cm, const float* Dskip,
+                       const void* z, const float* dt_bias, int dt_softplus, const int32_t* cu_seqlens, int64_t nseq,
+                       const float* h0, void* y, float* h_last, void* stream) {
+  SSD_TRY(check_dtypes(in_dtype, out_dtype));
+  if (B < 0 || L < 0 || D < 0 || N < 0) return fail(SSD_ERR_SHAPE, "negative size");
+  if (!supported_n(N)) return fail(SSD_ERR_SHAPE, "N must be 1, 2, 4, 8 or 16");
+  if (cu_seqlens) {
+    if (B != 1) return fail(SSD_ERR_SHAPE, "cu_seqlens requires B == 1");
+    if (nseq < 0) return fail(SSD_ERR_SHAPE, "nseq must be >= 0");
+    if (nseq == 0 && L != 0) return fail(SSD_ERR_SHAPE, "nseq == 0 requires L == 0");
+    if (L >= (int64_t)1 << 31 || nseq >= (int64_t)1 << 30) return fail(SSD_ERR_SHAPE, "packed length too large");
+  } else {
+    nseq = B;
+  }
+  if (too_big({B, L, D}) || too_big({nseq, D, N}) || (D + 255) / 256 > 65535)
+    return fail(SSD_ERR_SHAPE, "problem too large");
+  const int64_t nact = B * L * D;
+  if (nact > 0 && (!x || !dt || !y)) return fail(SSD_ERR_NULL, "x, dt and y are required");
+  if (B * L * N > 0 && (!Bm || !Cm)) return fail(SSD_ERR_NULL, "Bm and Cm are required");
+  if (D * N > 0 && !A) return fail(SSD_ERR_NULL, "A is required");
+  const size_t ab = (size_t)nact * esize(in_dtype);
+  const size_t bb = (size_t)(B * L * N) * esize(in_dtype);
+  const size_t sb = (size_t)(nseq * D * N) * 4;
+  std::vector<Span> ins = {{"x", x, ab}, {"dt", dt, ab}, {"A", A, (size_t)(D * N) * 4}, {"Bm", Bm, bb}, {"Cm", Cm, bb},
+                           {"Dskip", Dskip, (size_t)D * 4}, {"z", z, ab}, {"dt_bias", dt_bias, (size_t)D * 4},
+                           {"cu_seqlens", cu_seqlens, (size_t)(nseq + 1) * 4}, {"h0", h0, sb}};
+  std::vector<Span> outs = {{"y", y, (size_t)nact * esize(out_dtype)}, {"h_last", h_last, sb}};
+  std::vector<Span> all = ins;
+  all.insert(all.end(), outs.begin(), outs.end());
+  SSD_TRY(check_align(all));
+  SSD_TRY(check_alias(outs, ins));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (D * N == 0 || nseq == 0) return ok();
+  if (L == 0) return hip_status(ssd::launch_copy_or_zero(h_last, h0, nseq * D * N, s), "selective_scan");
+  ssd::SelectiveScanArgs a{B, L, D, N, in_dtype == SSD_BF16, out_dtype == SSD_BF16, x, dt, A, Bm, Cm, Dskip, z,
+                           dt_bias, dt_softplus ? 1 : 0, cu_seqlens, nseq, h0, y, h_last, nullptr};
+  SSD_TRY(get_scratch(stream, kScratchSelective, ssd::selective_scan_scratch_bytes(a), &a.scratch));
+  return hip_status(ssd::launch_selective_scan(a, s), "selective_scan launch");
+}
+
+int ssd_selective_update(int64_t B, int64_t D, int64_t N, int in_dtype, int out_dtype, const void* x, const void* dt,
+                         const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                         const float* dt_bias, int dt_softplus, float* state, void* y, void* stream) {
+  SSD_TRY(check_dtypes(in_dtype, out_dtype));
+  if (B < 0 || D < 0 || N < 0) return fail(SSD_ERR_SHAPE, "negative size");
+  if (!supported_n(N)) return fail(SSD_ERR_SHAPE, "N must be 1, 2, 4, 8 or 16");
+  if (too_big({B, D, N}) || B * D >= (int64_t)1 << 38) return fail(SSD_ERR_SHAPE, "problem too large");
+  const int64_t n = B * D;
+  if (n > 0 && (!x || !dt || !state || !y)) return fail(SSD_ERR_NULL, "x, dt, state and y are required");
+  if (B * N > 0 && (!Bm || !Cm)) return fail(SSD_ERR_NULL, "Bm and Cm are required");
+  if (D * N > 0 && !A) return fail(SSD_ERR_NULL, "A is required");
+  const size_t ab = (size_t)n * esize(in_dtype);
+  const size_t bb = (size_t)(B * N) * esize(in_dtype);
+  std::vector<Span> ins = {{"x", x, ab}, {"dt", dt, ab}, {"A", A, (size_t)(D * N) * 4}, {"Bm", Bm, bb}, {"Cm", Cm, bb},
+                           {"Dskip", Dskip, (size_t)D * 4}, {"z", z, ab}, {"dt_bias", dt_bias, (size_t)D * 4}};
+  std::vector<Span> outs = {{"y", y, (size_t)n * esize(out_dtype)}, {"state", state, (size_t)(n * N) * 4}};
+  std::vector<Span> all = ins;
+  all.insert(all.end(), outs.begin(), outs.end());
+  SSD_TRY(check_align(all));
+  SSD_TRY(check_alias(outs, ins));
+  if (n == 0 || N == 0) return ok();
+  ssd::SelectiveUpdateArgs a{B, D, N, in_dtype == SSD_BF16, out_dtype == SSD_BF16, x, dt, A, Bm, Cm, Dskip, z, dt_bias,
+                             dt_softplus ? 1 : 0, state, y};
+  return hip_status(ssd::launch_selective_update(a, static_cast<hipStream_t>(stream)), "selective_update launch");
+}
+
+// ============================================================================ HGRN2
+static bool supported_d(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+int ssd_hgrn2_scan(int64_t B, int64_t L, int64_t H, int64_t d, int in_dtype, int out_dtype, const void* q,
+                   const void* k, const void* v, const void* g_logit, float lower_bound, const float* S0, void* o,
+                   float* S_last, void* stream) {
+  SSD_TRY(check_dtypes(in_dtype, out_dtype));
+  if (B < 0 || L < 0 || H < 0 || d < 0) return fail(SSD_ERR_SHAPE, "negative size");
+  if (!supported_d(d)) return fail(SSD_ERR_SHAPE, "head dim d must be 16, 32, 64 or 128");
+  if (too_big({B, L, H, d}) || B * H >= (int64_t)1 << 31) return fail(SSD_ERR_SHAPE, "problem too large");
+  if (!(lower_bound >= 0.0f && lower_bound <= 1.0f)) return fail(SSD_ERR_VALUE, "lower_bound must be in [0, 1]");
+  const int64_t nact = B * L * H * d;
+  if (nact > 0 && (!q || !k || !v || !g_logit || !o)) return fail(SSD_ERR_NULL, "q, k, v, g_logit and o are required");
+  const size_t ab = (size_t)nact * esize(in_dtype);
+  const size_t sb = (size_t)(B * H * d * d) * 4;
+  std::vector<Span> ins = {{"q", q, ab}, {"k", k, ab}, {"v", v, ab}, {"g_logit", g_logit, ab}, {"S0", S0, sb}};
+  std::vector<Span> outs = {{"o", o, (size_t)nact * esize(out_dtype)}, {"S_last", S_last, sb}};
+  std::vector<Span> all = ins;
+  all.insert(all.end(), outs.begin(), outs.end());
+  SSD_TRY(check_align(all));
+  SSD_TRY(check_alias(outs, ins));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (B * H == 0) return ok();
+  if (L == 0) return hip_status(ssd::launch_copy_or_zero(S_last, S0, B * H * d * d, s), "hgrn2_scan");
+  ssd::Hgrn2ScanArgs a{B, L, H, d, in_dtype == SSD_BF16, out_dtype == SSD_BF16, q, k, v, g_logit, lower_bound, S0, o,
+                       S_last};
+  return hip_status(ssd::launch_hgrn2_scan(a, s), "hgrn2_scan launch");
+}
+
+int ssd_hgrn2_update(int64_t B, int64_t H, int64_t d, int in_dtype, int out_dtype, const void* q, const void* k,
+                     const void* v, const void* g_logit, float lower_bound, float* S, void* o, void* stream) {
+  SSD_TRY(check_dtypes(in_dtype, out_dtype));
+  if (B < 0 || H < 0 || d < 0) return fail(SSD_ERR_SHAPE, "negative size");
+  if (!supported_d(d)) return fail(SSD_ERR_SHAPE, "head dim d must be 16, 32, 64 or 128");
+  if (too_big({B, H, d, d}) || B * H * d >= (int64_t)1 << 33) return fail(SSD_ERR_SHAPE, "problem too large");
+  if (!(lower_bound >= 0.0f && lower_bound <= 1.0f)) return fail(SSD_ERR_VALUE, "lower_bound must be in [0, 1]");
+  const int64_t n = B * H * d;
+  if (n > 0 && (!q || !k || !v || !g_logit || !S || !o)) return fail(SSD_ERR_NULL, "q, k, v, g_logit, S and o are required");
+  const size_t ab = (size_t)n * esize(in_dtype);
+  std::vector<Span> ins = {{"q", q, ab}, {"k", k, ab}, {"v", v, ab}, {"g_logit", g_logit, ab}};
+  std::vector<Span> outs = {{"o", o, (size_t)n * esize(out_dtype)}, {"S", S, (size_t)(n * d) * 4}};
+  std::vector<Span> all = ins;
+  all.insert(all.end(), outs.begin(), outs.end());
+  SSD_TRY(check_align(all));
+  SSD_TRY(check_alias(outs, ins));
+  if (n == 0) return ok();
+  ssd::Hgrn2UpdateArgs a{B, H, d, in_dtype == SSD_BF16, out_dtype == SSD_BF16, q, k, v, g_logit, lower_bound, S, o};
+  return hip_status(ssd::launch_hgrn2_update(a, static_cast<hipStream_t>(stream)), "hgrn2_update launch");
+}
+
+}  // extern "C"

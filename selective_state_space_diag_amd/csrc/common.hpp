@@ -1,0 +1,140 @@
+// common.hpp -- device helpers shared by the gfx950 scan kernels.
+//
+// Number formats: activations arrive as fp32 or bf16 bit patterns; all arithmetic is fp32.
+// Transcendentals use the hardware instructions directly (v_exp_f32 = 2^x, v_log_f32 = log2,
+// v_rcp_f32, v_sqrt_f32; each about 1 ulp); where a cancellation would cost accuracy the
+// formula is rearranged (see one_minus_exp2x and softplus_f).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ------------------------------------------------------------------ bf16 <-> fp32
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Element access by storage type.
+template <typename T> struct io;
+template <> struct io<float> {
+  static __device__ __forceinline__ float load(const void* p, int64_t i) {
+    return static_cast<const float*>(p)[i];
+  }
+  static __device__ __forceinline__ void store(void* p, int64_t i, float v) { static_cast<float*>(p)[i] = v; }
+};
+template <> struct io<bf16_t> {
+  static __device__ __forceinline__ float load(const void* p, int64_t i) {
+    return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+  }
+  static __device__ __forceinline__ void store(void* p, int64_t i, float v) {
+    static_cast<uint16_t*>(p)[i] = f32_to_bf16(v);
+  }
+};
+
+// Two consecutive elements (index i even, base 16-byte aligned, row length even).
+template <typename T> struct io2;
+template <> struct io2<float> {
+  using raw = float2;
+  static __device__ __forceinline__ raw load(const void* p, int64_t i) {
+    return *reinterpret_cast<const float2*>(static_cast<const float*>(p) + i);
+  }
+  static __device__ __forceinline__ float lo(raw r) { return r.x; }
+  static __device__ __forceinline__ float hi(raw r) { return r.y; }
+  static __device__ __forceinline__ void store(void* p, int64_t i, float a, float b) {
+    *reinterpret_cast<float2*>(static_cast<float*>(p) + i) = make_float2(a, b);
+  }
+};
+template <> struct io2<bf16_t> {
+  using raw = uint32_t;
+  static __device__ __forceinline__ raw load(const void* p, int64_t i) {
+    return *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p) + i);
+  }
+  static __device__ __forceinline__ float lo(raw r) { return bf16_lo(r); }
+  static __device__ __forceinline__ float hi(raw r) { return bf16_hi(r); }
+  static __device__ __forceinline__ void store(void* p, int64_t i, float a, float b) {
+    uint32_t w = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p) + i) = w;
+  }
+};
+
+// ------------------------------------------------------------------ hardware transcendentals
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float hw_sqrt(float x) { return __builtin_amdgcn_sqrtf(x); }
+
+// sigmoid(v) = 1 / (1 + e^-v); saturates cleanly to 0 / 1 for large |v|.
+__device__ __forceinline__ float sigmoid_f(float v) { return hw_rcp(1.0f + hw_exp2(-v * kLog2e)); }
+
+// silu(z) = z * sigmoid(z)
+__device__ __forceinline__ float silu_f(float z) { return z * sigmoid_f(z); }
+
+// softplus with the usual threshold: v for v > 20, else log(1 + e^v).  log1p is kept accurate
+// for small e^v by the correction log1p(e) = log(u) * e / (u - 1), u = 1 + e (u - 1 is exact).
+__device__ __forceinline__ float softplus_f(float v) {
+  float e = hw_exp2(v * kLog2e);
+  float u = 1.0f + e;
+  float um1 = u - 1.0f;
+  float lg = hw_log2(u) * kLn2;
+  float r = (um1 == 0.0f) ? e : lg * (e * hw_rcp(um1));
+  return v > 20.0f ? v : r;
+}
+
+// 1 - 2^x for x <= 0, accurate also near x = 0 (where 1 - 2^x cancels): for |x ln2| < 0.25 the
+// Taylor series of -expm1 to degree 6 (truncation < 5e-8 relative), else 1 - 2^x directly.
+__device__ __forceinline__ float one_minus_exp2x(float x) {
+  float u = x * kLn2;  // natural-log argument
+  float p = fmaf(u, 1.0f / 720.0f, 1.0f / 120.0f);
+  p = fmaf(u, p, 1.0f / 24.0f);
+  p = fmaf(u, p, 1.0f / 6.0f);
+  p = fmaf(u, p, 0.5f);
+  p = fmaf(u, p, 1.0f);
+  float small = -u * p;
+  float big = 1.0f - hw_exp2(x);
+  return fabsf(u) < 0.25f ? small : big;
+}
+
+// ------------------------------------------------------------------ lookback words
+// A 64-bit word = (epoch << 32) | float bits.  Written and read with agent-scope relaxed atomics,
+// so each word is self-validating and needs no separate flag or fence.
+__device__ __forceinline__ void word_store(unsigned long long* p, uint32_t epoch, float v) {
+  unsigned long long w = ((unsigned long long)epoch << 32) | (unsigned long long)__float_as_uint(v);
+  __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long word_load(const unsigned long long* p) {
+  return __hip_atomic_load(const_cast<unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool word_ready(unsigned long long w, uint32_t epoch) {
+  return (uint32_t)(w >> 32) == epoch;
+}
+__device__ __forceinline__ float word_value(unsigned long long w) { return __uint_as_float((uint32_t)w); }
+
+// Per-launch control block at the head of a lookback scratch buffer.  `tick` packs the number of
+// completed launches (high 32 bits) with the next work-unit ticket (low 32 bits), so one atomic
+// add hands a workgroup both its ticket and the launch epoch.
+struct LookbackCtl {
+  unsigned long long tick;
+  unsigned int done;     // workgroups finished in the current launch
+  unsigned int error;    // set if a bounded wait ever expired (must never happen)
+};
+
+constexpr unsigned int kSpinLimit = 1u << 20;  // each spin is a memory round trip: ~1-2 s bound
+
+}  // namespace ssd

@@ -1,0 +1,101 @@
+// kernels.hpp -- host-side launchers of the gfx950 kernels.  Called by api.cpp after every
+// argument has been validated; each returns the hipError_t of its launch(es).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+// ------------------------------------------------------------------ RG-LRU
+struct RglruScanArgs {
+  int64_t B, L, D;
+  int in_bf16, out_bf16;
+  const void *x, *r_logit, *i_logit;
+  const float* a_log;
+  float c;
+  const float* h0;
+  void* y;
+  float* h_last;
+  // lookback scratch (control block + words), sized by rglru_scan_scratch_bytes
+  void* scratch;
+};
+size_t rglru_scan_scratch_bytes(int64_t B, int64_t L, int64_t D);
+hipError_t launch_rglru_scan(const RglruScanArgs& a, hipStream_t s);
+
+struct RglruUpdateArgs {
+  int64_t B, D;
+  int in_bf16, out_bf16;
+  const void *x, *r_logit, *i_logit;
+  const float* a_log;
+  float c;
+  float* state;
+  void* y;
+};
+hipError_t launch_rglru_update(const RglruUpdateArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------------ selective
+struct SelectiveScanArgs {
+  int64_t B, L, D, N;
+  int in_bf16, out_bf16;
+  const void *x, *dt;
+  const float* A;
+  const void *Bm, *Cm;
+  const float* Dskip;
+  const void* z;
+  const float* dt_bias;
+  int dt_softplus;
+  const int32_t* cu_seqlens;  // device, or NULL (batched)
+  int64_t nseq;               // sequences (B when batched)
+  const float* h0;
+  void* y;
+  float* h_last;
+  void* scratch;
+};
+// Segment length the launcher will use, and the scratch it needs.
+int64_t selective_segment_len(const SelectiveScanArgs& a);
+size_t selective_scan_scratch_bytes(const SelectiveScanArgs& a);
+hipError_t launch_selective_scan(const SelectiveScanArgs& a, hipStream_t s);
+
+struct SelectiveUpdateArgs {
+  int64_t B, D, N;
+  int in_bf16, out_bf16;
+  const void *x, *dt;
+  const float* A;
+  const void *Bm, *Cm;
+  const float* Dskip;
+  const void* z;
+  const float* dt_bias;
+  int dt_softplus;
+  float* state;
+  void* y;
+};
+hipError_t launch_selective_update(const SelectiveUpdateArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------------ HGRN2
+struct Hgrn2ScanArgs {
+  int64_t B, L, H, d;
+  int in_bf16, out_bf16;
+  const void *q, *k, *v, *g_logit;
+  float lower_bound;
+  const float* S0;
+  void* o;
+  float* S_last;
+};
+hipError_t launch_hgrn2_scan(const Hgrn2ScanArgs& a, hipStream_t s);
+
+struct Hgrn2UpdateArgs {
+  int64_t B, H, d;
+  int in_bf16, out_bf16;
+  const void *q, *k, *v, *g_logit;
+  float lower_bound;
+  float* S;
+  void* o;
+};
+hipError_t launch_hgrn2_update(const Hgrn2UpdateArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------------ utilities
+// dst[i] = src ? src[i] : 0 for i < n (used for empty problems: final state = initial state).
+hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t s);
+
+}  // namespace ssd

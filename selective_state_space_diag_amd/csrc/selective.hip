@@ -1,0 +1,583 @@
+// selective.hip -- multi-scale selective scan (batched and packed varlen) and its decode update.
+//
+// Recurrence (cortexnet 3.2.1, cortexnet/ssm.py, MultiScaleSSM.forward / _selective_scan):
+//   delta = softplus(dt + dt_bias) (or dt + dt_bias), abar_n = exp(min(delta A_n, 20)),
+//   h_n = abar_n h_n + (delta B_n) x,  y = (sum_n C_n h_n + Dskip x) * silu(z).
+//
+// Layout: one lane per channel d (rows of [rows, D] are coalesced along d), the N states of the
+// channel in registers, B_n / C_n of the current row uniform across the wave (scalar loads).
+//
+// Time parallelism: each sequence is cut into segments of T rows.  Pass 1 runs every segment
+// except a sequence's last from a zero state and stores its aggregate per state (P = prod abar,
+// H = end state).  Pass 2 folds the aggregates of the earlier segments of the same sequence onto
+// h0 to get its carry-in, then runs the full recurrence with the readout, skip and gate, writing
+// y (and the final state for a sequence's last segment).  No workgroup waits for another: the
+// only dependency is the kernel boundary between the passes.
+//
+// When dt goes through softplus (delta >= 0) and every A of the wave is <= 0, delta*A <= 0 and
+// the clamp at 20 cannot act; that wave-uniform case skips it and forms P as 2^(A sum delta).
+// Otherwise the clamp is applied and P = 2^(sum of the clamped exponents), both exact readings of
+// prod abar.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ssd {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr float kClampLog2 = 20.0f * kLog2e;  // clamp(delta*A, max=20) in the base-2 exponent
+
+struct SelParams {
+  int64_t L;        // rows per sequence (batched)
+  int64_t D;
+  int64_t N;
+  int64_t nseq;
+  int64_t T;        // segment length
+  int64_t nseg;     // segments per sequence (batched)
+  const int32_t* cu;      // varlen boundaries or NULL
+  const int2* units;      // varlen (seq, seg) table or NULL
+  const int* n_units;     // varlen unit count (device)
+  const void* x;
+  const void* dt;
+  const float* A;
+  const void* Bm;
+  const void* Cm;
+  const float* Dskip;
+  const void* z;
+  const float* dt_bias;
+  const float* h0;
+  void* y;
+  float* h_last;
+  float* aggP;   // [unit][N][D]  product of abar over the segment
+  float* aggH;   // [unit][N][D]  state reached from zero at the segment end
+  float* carry;  // [unit][N][D]  state entering the segment
+  const int2* seq_units;  // varlen: (first unit, unit count) per sequence
+};
+
+struct Unit {
+  int64_t seq, seg, row0, row1;
+  bool last, valid;
+};
+
+__device__ __forceinline__ Unit unit_of(const SelParams& p, int64_t u) {
+  Unit r;
+  if (p.cu == nullptr) {
+    r.seq = u / p.nseg;
+    r.seg = u - r.seq * p.nseg;
+    r.row0 = r.seq * p.L + r.seg * p.T;
+    const int64_t end = (r.seq + 1) * p.L;
+    r.row1 = min(r.row0 + p.T, end);
+    r.last = (r.row1 == end);
+    r.valid = true;
+  } else {
+    r.valid = u < (int64_t)(*p.n_units);
+    if (!r.valid) return r;
+    const int2 e = p.units[u];
+    r.seq = e.x;
+    r.seg = e.y;
+    const int64_t start = p.cu[r.seq];
+    const int64_t end = p.cu[r.seq + 1];
+    r.row0 = start + r.seg * p.T;
+    r.row1 = min(r.row0 + p.T, end);
+    r.last = (r.row1 == end);
+  }
+  return r;
+}
+
+// ----------------------------------------------------------------------------- row inputs
+// Raw activation element kept in a VGPR until use (the load stays in flight meanwhile).
+template <typename Tin> struct Raw;
+template <> struct Raw<float> {
+  using T = float;
+  static __device__ __forceinline__ T load(const void* p, int64_t i) { return static_cast<const float*>(p)[i]; }
+  static __device__ __forceinline__ float cvt(T r) { return r; }
+};
+template <> struct Raw<bf16_t> {
+  using T = uint32_t;
+  static __device__ __forceinline__ T load(const void* p, int64_t i) { return static_cast<const uint16_t*>(p)[i]; }
+  static __device__ __forceinline__ float cvt(T r) { return __uint_as_float(r << 16); }
+};
+
+constexpr int kPrefetch = 4;   // rows of x / dt / z in flight per lane (also the unroll factor)
+constexpr int kRowBlock = 64;  // rows of B / C staged in LDS at a time
+
+// B_n and C_n are shared by every channel of a row, so the workgroup (all of whose lanes work on
+// the same rows) stages them once per block of kRowBlock rows in LDS as fp32, one block ahead of
+// use; lanes then read them as broadcasts.
+template <int NS, bool READOUT>
+struct BCStage {
+  static constexpr int PER_ROW = READOUT ? 2 * NS : NS;         // B then C
+  static constexpr int PER_BLOCK = kRowBlock * PER_ROW;
+  static constexpr int PER_THREAD = (PER_BLOCK + kThreads - 1) / kThreads;
+  float v[PER_THREAD];
+
+  // element e of the block: row e / PER_ROW, column e % PER_ROW (B for col < NS, else C)
+  template <typename Tin>
+  __device__ __forceinline__ void fetch(const SelParams& p, int64_t row0, int64_t nrows, int64_t blk) {
+#pragma unroll
+    for (int q = 0; q < PER_THREAD; ++q) {
+      const int e = q * kThreads + threadIdx.x;
+      const int r = e / PER_ROW, col = e - r * PER_ROW;
+      const int64_t row = row0 + min(blk * kRowBlock + r, nrows - 1);
+      const void* M = col < NS ? p.Bm : p.Cm;
+      const int n = col < NS ? col : col - NS;
+      v[q] = (e < PER_BLOCK) ? io<Tin>::load(M, row * NS + n) : 0.0f;
+    }
+  }
+  __device__ __forceinline__ void put(float* lds) const {
+#pragma unroll
+    for (int q = 0; q < PER_THREAD; ++q) {
+      const int e = q * kThreads + threadIdx.x;
+      if (e < PER_BLOCK) lds[e] = v[q];
+    }
+  }
+};
+
+// ----------------------------------------------------------------------------- the row loop
+// One row of one channel: discretise, advance the N states, optionally read out.
+template <int NS, bool SOFTPLUS, bool CLAMP, bool READOUT, bool GATE>
+__device__ __forceinline__ float row_step(float xx, float dd, float zz, const float* bc, const float* A2, float dskip,
+                                          float* h, float* e, float& sum_delta) {
+  const float delta = SOFTPLUS ? softplus_f(dd) : dd;
+  const float dx = delta * xx;
+  float acc = 0.0f;
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    float dA = delta * A2[n];
+    if (CLAMP) {
+      dA = dA > kClampLog2 ? kClampLog2 : dA;
+      if (!READOUT) e[n] += dA;
+    }
+    h[n] = fmaf(hw_exp2(dA), h[n], dx * bc[n]);
+    if (READOUT) acc = fmaf(bc[NS + n], h[n], acc);
+  }
+  if (!CLAMP && !READOUT) sum_delta += delta;
+  if (READOUT) {
+    acc = fmaf(dskip, xx, acc);
+    if (GATE) acc *= silu_f(zz);
+  }
+  return acc;
+}
+
+// Runs rows [row0, row1) of one segment for channel dl.  Every lane of the workgroup must call it
+// with the same rows (B / C staging uses barriers).  x / dt / z are prefetched kPrefetch rows ahead
+// in registers.  Loads and stores are unconditional inside the unrolled groups (indices are
+// clamped in range) so the compiler counts outstanding memory operations exactly; a lane without a
+// channel of its own recomputes channel D-1 bit for bit and rewrites the same value.
+template <typename Tin, typename Tout, int NS, bool SOFTPLUS, bool CLAMP, bool READOUT, bool GATE>
+__device__ __forceinline__ void run_rows(const SelParams& p, int64_t row0, int64_t row1, int64_t dl,
+                                         const float* A2, float bias, float dskip, float* h, float* e,
+                                         float& sum_delta, float* lds) {
+  using R = Raw<Tin>;
+  using Stage = BCStage<NS, READOUT>;
+  constexpr int PR = Stage::PER_ROW;
+  const int64_t nrows = row1 - row0;
+  if (nrows <= 0) return;
+  typename R::T rx[kPrefetch], rd[kPrefetch], rz[kPrefetch];
+#pragma unroll
+  for (int k = 0; k < kPrefetch; ++k) {
+    const int64_t r = row0 + min((int64_t)k, nrows - 1);
+    rx[k] = R::load(p.x, r * p.D + dl);
+    rd[k] = R::load(p.dt, r * p.D + dl);
+    if (GATE) rz[k] = R::load(p.z, r * p.D + dl);
+  }
+  Stage st;
+  st.template fetch<Tin>(p, row0, nrows, 0);
+  st.put(lds);
+  const int64_t nblk = (nrows + kRowBlock - 1) / kRowBlock;
+  for (int64_t blk = 0; blk < nblk; ++blk) {
+    float* cur = lds + (blk & 1) * Stage::PER_BLOCK;
+    if (blk + 1 < nblk) st.template fetch<Tin>(p, row0, nrows, blk + 1);
+    __syncthreads();  // block blk is in LDS; the other buffer is free
+    const int64_t r_begin = blk * kRowBlock;
+    const int64_t r_end = min(r_begin + kRowBlock, nrows);
+    const int64_t r_full = r_begin + (r_end - r_begin) / kPrefetch * kPrefetch;
+    for (int64_t base = r_begin; base < r_full; base += kPrefetch) {
+#pragma unroll
+      for (int k = 0; k < kPrefetch; ++k) {
+        // slot of row i in the prefetch ring is i % kPrefetch = k (r_begin is a multiple of it)
+        const int64_t i = base + k;
+        const int64_t row = row0 + i;
+        const float xx = R::cvt(rx[k]);
+        const float dd = R::cvt(rd[k]) + bias;
+        const float zz = GATE ? R::cvt(rz[k]) : 0.0f;
+        const int64_t rp = row0 + min(i + kPrefetch, nrows - 1);
+        rx[k] = R::load(p.x, rp * p.D + dl);
+        rd[k] = R::load(p.dt, rp * p.D + dl);
+        if (GATE) rz[k] = R::load(p.z, rp * p.D + dl);
+        float bc[PR];
+        if constexpr (PR % 4 == 0) {
+          const float4* src = reinterpret_cast<const float4*>(cur + (i - r_begin) * PR);
+#pragma unroll
+          for (int q = 0; q < PR / 4; ++q) {
+            const float4 t = src[q];
+            bc[4 * q] = t.x; bc[4 * q + 1] = t.y; bc[4 * q + 2] = t.z; bc[4 * q + 3] = t.w;
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < PR; ++q) bc[q] = cur[(i - r_begin) * PR + q];
+        }
+        const float y = row_step<NS, SOFTPLUS, CLAMP, READOUT, GATE>(xx, dd, zz, bc, A2, dskip, h, e, sum_delta);
+        if (READOUT) io<Tout>::store(p.y, row * p.D + dl, y);
+        // keep rows in program order so the B / C of later rows are not all read into registers early
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // rows of this block past the last full group (only in the sequence's final block)
+#pragma unroll
+    for (int k = 0; k < kPrefetch; ++k) {
+      const int64_t i = r_full + k;
+      if (i < r_end) {
+        const int64_t row = row0 + i;
+        float bc[PR];
+#pragma unroll
+        for (int q = 0; q < PR; ++q) bc[q] = cur[(i - r_begin) * PR + q];
+        const float y = row_step<NS, SOFTPLUS, CLAMP, READOUT, GATE>(
+            R::cvt(rx[k]), R::cvt(rd[k]) + bias, GATE ? R::cvt(rz[k]) : 0.0f, bc, A2, dskip, h, e, sum_delta);
+        if (READOUT) io<Tout>::store(p.y, row * p.D + dl, y);
+      }
+    }
+    if (blk + 1 < nblk) st.put(lds + ((blk + 1) & 1) * Stage::PER_BLOCK);
+  }
+}
+
+// ----------------------------------------------------------------------------- pass 1: aggregates
+template <typename Tin, int NS, bool SOFTPLUS>
+__global__ __launch_bounds__(kThreads, 4) void selective_aggregate_kernel(SelParams p) {
+  const int64_t u = blockIdx.x;
+  const Unit U = unit_of(p, u);
+  if (!U.valid || U.last) return;
+  const int64_t d = (int64_t)blockIdx.y * kThreads + threadIdx.x;
+  const bool active = d < p.D;
+  const int64_t dl = active ? d : p.D - 1;  // lanes past D recompute channel D-1, store nothing
+  float A2[NS];
+  bool nonpos = true;
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    A2[n] = p.A[dl * NS + n] * kLog2e;
+    nonpos = nonpos && !(A2[n] > 0.0f);
+  }
+  const float bias = p.dt_bias ? p.dt_bias[dl] : 0.0f;
+  float h[NS], e[NS];
+#pragma unroll
+  for (int n = 0; n < NS; ++n) { h[n] = 0.0f; e[n] = 0.0f; }
+  float sum_delta = 0.0f;
+  __shared__ float lds[2 * BCStage<NS, false>::PER_BLOCK];
+  const bool noclamp = SOFTPLUS && __all(nonpos);
+  if (noclamp)
+    run_rows<Tin, float, NS, SOFTPLUS, false, false, false>(p, U.row0, U.row1, dl, A2, bias, 0.0f, h, e, sum_delta,
+                                                            lds);
+  else
+    run_rows<Tin, float, NS, SOFTPLUS, true, false, false>(p, U.row0, U.row1, dl, A2, bias, 0.0f, h, e, sum_delta,
+                                                           lds);
+  if (!active) return;
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    const float P = noclamp ? hw_exp2(A2[n] * sum_delta) : hw_exp2(e[n]);
+    p.aggP[(u * NS + n) * p.D + d] = P;
+    p.aggH[(u * NS + n) * p.D + d] = h[n];
+  }
+}
+
+template <typename Tin, typename Tout, int NS, bool SOFTPLUS>
+__global__ __launch_bounds__(kThreads) void selective_scan_kernel(SelParams p) {
+  const int64_t u = blockIdx.x;
+  const Unit U = unit_of(p, u);
+  if (!U.valid) return;
+  const int64_t d = (int64_t)blockIdx.y * kThreads + threadIdx.x;
+  const bool active = d < p.D;
+  const int64_t dl = active ? d : p.D - 1;  // lanes past D recompute channel D-1 exactly
+  float A2[NS];
+  bool nonpos = true;
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    A2[n] = p.A[dl * NS + n] * kLog2e;
+    nonpos = nonpos && !(A2[n] > 0.0f);
+  }
+  const float bias = p.dt_bias ? p.dt_bias[dl] : 0.0f;
+  const float dskip = p.Dskip ? p.Dskip[dl] : 0.0f;
+
+  // carry-in of this segment: h0 (or zero) for a sequence's first segment, else the carry pass's
+  float h[NS], e[NS];
+  if (U.seg == 0) {
+#pragma unroll
+    for (int n = 0; n < NS; ++n) h[n] = p.h0 ? p.h0[(U.seq * p.D + dl) * NS + n] : 0.0f;
+  } else {
+#pragma unroll
+    for (int n = 0; n < NS; ++n) h[n] = p.carry[(u * NS + n) * p.D + dl];
+  }
+  float sum_delta = 0.0f;
+  __shared__ float lds[2 * BCStage<NS, true>::PER_BLOCK];
+  const bool noclamp = SOFTPLUS && __all(nonpos);
+  if (p.z) {
+    if (noclamp)
+      run_rows<Tin, Tout, NS, SOFTPLUS, false, true, true>(p, U.row0, U.row1, dl, A2, bias, dskip, h, e, sum_delta,
+                                                           lds);
+    else
+      run_rows<Tin, Tout, NS, SOFTPLUS, true, true, true>(p, U.row0, U.row1, dl, A2, bias, dskip, h, e, sum_delta,
+                                                          lds);
+  } else {
+    if (noclamp)
+      run_rows<Tin, Tout, NS, SOFTPLUS, false, true, false>(p, U.row0, U.row1, dl, A2, bias, dskip, h, e, sum_delta,
+                                                            lds);
+    else
+      run_rows<Tin, Tout, NS, SOFTPLUS, true, true, false>(p, U.row0, U.row1, dl, A2, bias, dskip, h, e, sum_delta,
+                                                           lds);
+  }
+
+  if (U.last && p.h_last && active) {
+#pragma unroll
+    for (int n = 0; n < NS; ++n) p.h_last[(U.seq * p.D + d) * NS + n] = h[n];
+  }
+}
+
+// ----------------------------------------------------------------------------- carry pass
+// One thread per (sequence, state n, channel d): walks the sequence's segments in order,
+// carry[s] = h; h = P[s] h + H[s], starting from h0 (or zero).  The aggregate loads do not depend
+// on h, so they are issued ahead of the multiply-add chain.
+template <int NS>
+__global__ __launch_bounds__(kThreads) void selective_carry_kernel(SelParams p) {
+  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t per_seq = NS * p.D;
+  const int64_t seq = gid / per_seq;
+  if (seq >= p.nseq) return;
+  const int64_t e = gid - seq * per_seq;  // n * D + d
+  const int64_t n = e / p.D;
+  const int64_t d = e - n * p.D;
+  int64_t first, count;
+  if (p.cu == nullptr) {
+    first = seq * p.nseg;
+    count = p.nseg;
+  } else {
+    const int2 r = p.seq_units[seq];
+    first = r.x;
+    count = r.y;
+  }
+  float h = p.h0 ? p.h0[(seq * p.D + d) * NS + n] : 0.0f;
+  constexpr int K = 8;
+  for (int64_t s0 = 0; s0 < count; s0 += K) {
+    float P[K], H[K];
+#pragma unroll
+    for (int q = 0; q < K; ++q) {
+      const int64_t s = min(s0 + q, count - 1);
+      const int64_t idx = ((first + s) * NS + n) * p.D + d;
+      P[q] = p.aggP[idx];
+      H[q] = p.aggH[idx];
+    }
+#pragma unroll
+    for (int q = 0; q < K; ++q) {
+      const int64_t s = s0 + q;
+      if (s > 0 && s < count) p.carry[((first + s) * NS + n) * p.D + d] = h;
+      if (s + 1 < count) h = fmaf(P[q], h, H[q]);  // a sequence's last segment has no aggregate
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- varlen planner
+// One workgroup: unit table (seq, seg) in sequence order, unit count, and the final state of
+// zero-length sequences (= their initial state, or zero).
+__global__ __launch_bounds__(1024) void selective_plan_kernel(const int32_t* cu, int64_t nseq, int64_t T,
+                                                              int2* units, int* n_units, int2* seq_units, int64_t D,
+                                                              int64_t N, const float* h0, float* h_last) {
+  __shared__ int s_scan[1024];
+  __shared__ int s_base;
+  if (threadIdx.x == 0) s_base = 0;
+  __syncthreads();
+  for (int64_t blk = 0; blk < nseq; blk += 1024) {
+    const int64_t sq = blk + threadIdx.x;
+    int cnt = 0;
+    if (sq < nseq) {
+      const int64_t len = (int64_t)cu[sq + 1] - cu[sq];
+      cnt = (int)((len + T - 1) / T);
+    }
+    s_scan[threadIdx.x] = cnt;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int add = threadIdx.x >= off ? s_scan[threadIdx.x - off] : 0;
+      __syncthreads();
+      s_scan[threadIdx.x] += add;
+      __syncthreads();
+    }
+    const int base = s_base + s_scan[threadIdx.x] - cnt;
+    for (int sgi = 0; sgi < cnt; ++sgi) units[base + sgi] = make_int2((int)sq, sgi);
+    if (sq < nseq) seq_units[sq] = make_int2(base, cnt);
+    __syncthreads();
+    if (threadIdx.x == 1023) s_base += s_scan[1023];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *n_units = s_base;
+  if (h_last) {
+    for (int64_t sq = 0; sq < nseq; ++sq) {
+      if (cu[sq + 1] != cu[sq]) continue;
+      for (int64_t e = threadIdx.x; e < D * N; e += 1024)
+        h_last[sq * D * N + e] = h0 ? h0[sq * D * N + e] : 0.0f;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- decode update
+template <typename Tin, typename Tout, int NS, bool SOFTPLUS>
+__global__ __launch_bounds__(kThreads) void selective_update_kernel(
+    int64_t B, int64_t D, const void* x, const void* dt, const float* A, const void* Bm, const void* Cm,
+    const float* Dskip, const void* z, const float* dt_bias, float* state, void* y) {
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= B * D) return;
+  const int64_t b = idx / D;
+  const int64_t d = idx - b * D;
+  float dd = io<Tin>::load(dt, idx) + (dt_bias ? dt_bias[d] : 0.0f);
+  const float delta = SOFTPLUS ? softplus_f(dd) : dd;
+  const float xx = io<Tin>::load(x, idx);
+  const float dx = delta * xx;
+  float acc = 0.0f;
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    float dA = delta * A[d * NS + n] * kLog2e;
+    dA = dA > kClampLog2 ? kClampLog2 : dA;
+    const float ab = hw_exp2(dA);
+    const float hn = fmaf(ab, state[idx * NS + n], dx * io<Tin>::load(Bm, b * NS + n));
+    state[idx * NS + n] = hn;
+    acc = fmaf(io<Tin>::load(Cm, b * NS + n), hn, acc);
+  }
+  if (Dskip) acc = fmaf(Dskip[d], xx, acc);
+  if (z) acc *= silu_f(io<Tin>::load(z, idx));
+  io<Tout>::store(y, idx, acc);
+}
+
+// ----------------------------------------------------------------------------- dispatch helpers
+constexpr int64_t kTargetWaves = 4096;  // enough waves in flight to fill 256 CUs
+
+template <typename Tin, typename Tout, int NS>
+hipError_t launch_passes(const SelParams& p, int64_t U, bool softplus, hipStream_t s) {
+  const dim3 grid((unsigned)U, (unsigned)((p.D + kThreads - 1) / kThreads));
+  const bool split = (p.cu != nullptr) || (p.nseg > 1);
+  if (split) {
+    if (softplus)
+      hipLaunchKernelGGL((selective_aggregate_kernel<Tin, NS, true>), grid, dim3(kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL((selective_aggregate_kernel<Tin, NS, false>), grid, dim3(kThreads), 0, s, p);
+    const int64_t nthreads = p.nseq * NS * p.D;
+    hipLaunchKernelGGL((selective_carry_kernel<NS>), dim3((unsigned)((nthreads + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, s, p);
+  }
+  if (softplus)
+    hipLaunchKernelGGL((selective_scan_kernel<Tin, Tout, NS, true>), grid, dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((selective_scan_kernel<Tin, Tout, NS, false>), grid, dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+template <typename Tin, typename Tout>
+hipError_t launch_by_n(const SelParams& p, int64_t U, bool softplus, hipStream_t s) {
+  switch (p.N) {
+    case 1: return launch_passes<Tin, Tout, 1>(p, U, softplus, s);
+    case 2: return launch_passes<Tin, Tout, 2>(p, U, softplus, s);
+    case 4: return launch_passes<Tin, Tout, 4>(p, U, softplus, s);
+    case 8: return launch_passes<Tin, Tout, 8>(p, U, softplus, s);
+    default: return launch_passes<Tin, Tout, 16>(p, U, softplus, s);
+  }
+}
+
+template <typename Tin, typename Tout, int NS>
+void launch_update_n(const SelectiveUpdateArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)((a.B * a.D + kThreads - 1) / kThreads));
+  if (a.dt_softplus)
+    hipLaunchKernelGGL((selective_update_kernel<Tin, Tout, NS, true>), grid, dim3(kThreads), 0, s, a.B, a.D, a.x,
+                       a.dt, a.A, a.Bm, a.Cm, a.Dskip, a.z, a.dt_bias, a.state, a.y);
+  else
+    hipLaunchKernelGGL((selective_update_kernel<Tin, Tout, NS, false>), grid, dim3(kThreads), 0, s, a.B, a.D, a.x,
+                       a.dt, a.A, a.Bm, a.Cm, a.Dskip, a.z, a.dt_bias, a.state, a.y);
+}
+
+template <typename Tin, typename Tout>
+void launch_update_t(const SelectiveUpdateArgs& a, hipStream_t s) {
+  switch (a.N) {
+    case 1: launch_update_n<Tin, Tout, 1>(a, s); break;
+    case 2: launch_update_n<Tin, Tout, 2>(a, s); break;
+    case 4: launch_update_n<Tin, Tout, 4>(a, s); break;
+    case 8: launch_update_n<Tin, Tout, 8>(a, s); break;
+    default: launch_update_n<Tin, Tout, 16>(a, s); break;
+  }
+}
+
+struct Plan {
+  int64_t T, nseg, U;
+};
+
+Plan make_plan(const SelectiveScanArgs& a) {
+  Plan pl;
+  const int64_t waves_per_row = (a.D + 63) / 64;
+  if (a.cu_seqlens == nullptr) {
+    const int64_t row_waves = a.B * waves_per_row;
+    int64_t want = (kTargetWaves + row_waves - 1) / row_waves;  // segments per sequence
+    if (want < 1) want = 1;
+    int64_t T = (a.L + want - 1) / want;
+    T = ((T + 15) / 16) * 16;
+    if (T < 16) T = 16;
+    if (T > a.L) T = a.L;
+    pl.T = T;
+    pl.nseg = (a.L + T - 1) / T;
+    pl.U = a.B * pl.nseg;
+  } else {
+    int64_t want = (kTargetWaves + waves_per_row - 1) / waves_per_row;  // units over the packed rows
+    if (want < 1) want = 1;
+    int64_t T = (a.L + want - 1) / want;
+    T = ((T + 15) / 16) * 16;
+    if (T < 16) T = 16;
+    pl.T = T;
+    pl.nseg = 0;
+    pl.U = (a.L + T - 1) / T + a.nseq;  // upper bound on sum of ceil(len / T)
+  }
+  return pl;
+}
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+}  // namespace
+
+int64_t selective_segment_len(const SelectiveScanArgs& a) { return make_plan(a).T; }
+
+size_t selective_scan_scratch_bytes(const SelectiveScanArgs& a) {
+  const Plan pl = make_plan(a);
+  size_t bytes = 3 * align256((size_t)pl.U * a.N * a.D * sizeof(float));
+  if (a.cu_seqlens) bytes += align256(256 + (size_t)pl.U * sizeof(int2)) + align256((size_t)a.nseq * sizeof(int2));
+  return bytes;
+}
+
+hipError_t launch_selective_scan(const SelectiveScanArgs& a, hipStream_t s) {
+  const Plan pl = make_plan(a);
+  SelParams p;
+  p.L = a.L; p.D = a.D; p.N = a.N; p.nseq = a.nseq; p.T = pl.T; p.nseg = pl.nseg;
+  p.cu = a.cu_seqlens; p.units = nullptr; p.n_units = nullptr; p.seq_units = nullptr;
+  p.x = a.x; p.dt = a.dt; p.A = a.A; p.Bm = a.Bm; p.Cm = a.Cm; p.Dskip = a.Dskip; p.z = a.z;
+  p.dt_bias = a.dt_bias; p.h0 = a.h0; p.y = a.y; p.h_last = a.h_last;
+  char* base = static_cast<char*>(a.scratch);
+  const size_t agg = align256((size_t)pl.U * a.N * a.D * sizeof(float));
+  p.aggP = reinterpret_cast<float*>(base);
+  p.aggH = reinterpret_cast<float*>(base + agg);
+  p.carry = reinterpret_cast<float*>(base + 2 * agg);
+  if (a.cu_seqlens) {
+    char* tbl = base + 3 * agg;
+    const size_t tbl_bytes = align256(256 + (size_t)pl.U * sizeof(int2));
+    p.n_units = reinterpret_cast<int*>(tbl);
+    p.units = reinterpret_cast<const int2*>(tbl + 256);
+    p.seq_units = reinterpret_cast<const int2*>(tbl + tbl_bytes);
+    hipLaunchKernelGGL(selective_plan_kernel, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.nseq, pl.T,
+                       reinterpret_cast<int2*>(tbl + 256), reinterpret_cast<int*>(tbl),
+                       reinterpret_cast<int2*>(tbl + tbl_bytes), a.D, a.N, a.h0, a.h_last);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (pl.U == 0) return hipSuccess;
+  if (!a.in_bf16) return launch_by_n<float, float>(p, pl.U, a.dt_softplus != 0, s);
+  return a.out_bf16 ? launch_by_n<bf16_t, bf16_t>(p, pl.U, a.dt_softplus != 0, s)
+                    : launch_by_n<bf16_t, float>(p, pl.U, a.dt_softplus != 0, s);
+}
+
+hipError_t launch_selective_update(const SelectiveUpdateArgs& a, hipStream_t s) {
+  if (!a.in_bf16) launch_update_t<float, float>(a, s);
+  else if (a.out_bf16) launch_update_t<bf16_t, bf16_t>(a, s);
+  else launch_update_t<bf16_t, float>(a, s);
+  return hipGetLastError();
+}
+
+}  // namespace ssd

@@ -13,7 +13,7 @@ Workloads (sizes as named by the five benchmark configurations):
 
 * ``rglru``: x, r_logit, i_logit ~ N(0,1); ``a_log[d] = ln U(0.9, 0.999)``
   (the RG-LRU base ``a`` initialised in [0.9, 0.999]); c = 8.
-* ``selective``: A[d][n] = -(n+1) * 2**s for scale s = floor(d / (D/S)) (the
+* ``selective``: A[d][n] = -(n+1) * 2**s for scale s = floor(d * S / D) (the
   multi-scale A of the cortexnet MultiScaleSSM, scales in contiguous channel
   blocks); per-channel step delta0 = exp(U[ln 1e-3, ln 1e-1]) times
   exp(N(0, 0.1)) per token; passed either raw (``dt_softplus=False``) or as
@@ -125,11 +125,9 @@ def rglru_decode_inputs(B: int, D: int, steps: int, dtype: str = BF16, seed: int
 
 # ----------------------------------------------------------------------------- selective
 def multiscale_A(D: int, N: int, num_scales: int = 4) -> np.ndarray:
-    """A[d][n] = -(n+1) * 2**s, scale s = floor(d / (D/num_scales))."""
-    if D % num_scales:
-        raise ValueError("D must be divisible by num_scales")
-    per = D // num_scales
-    s = (np.arange(D) // per).astype(np.float64)
+    """A[d][n] = -(n+1) * 2**s, scale s = floor(d * num_scales / D) (equal contiguous channel blocks
+    when num_scales divides D)."""
+    s = ((np.arange(D) * num_scales) // max(D, 1)).astype(np.float64)
     n = np.arange(1, N + 1, dtype=np.float64)
     return (-(n[None, :] * (2.0 ** s)[:, None])).astype(np.float32)
 

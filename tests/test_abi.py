@@ -1,0 +1,149 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every symbol that
+include/ssd.h declares, and rejects invalid arguments before anything touches the GPU.
+
+Pointers passed here are fake addresses: validation never dereferences them, and every call
+below fails validation, so no HIP call is made."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import selective_state_space_diag_amd as ssd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, VALUE, ALIAS = 0, 1, 2, 3, 4, 5, 6
+F32, BF16 = 0, 1
+P = 0x10000000  # fake, 16-byte aligned device addresses, far apart
+MB = 1 << 20
+
+
+def ptr(i):
+    return ctypes.c_void_p(P + i * 64 * MB)
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(ssd_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ssd.LIB_PATH):
+        import selective_state_space_diag_amd.build as b
+        b.build()
+    return ssd.lib()
+
+
+def test_library_exports_every_declared_symbol(L):
+    decl = declared_symbols()
+    assert set(decl) == set(ssd.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", ssd.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (ssd_[a-z0-9_]+)$", out, re.M))
+    for name in decl:
+        assert name in exported, name
+        assert getattr(L, name) is not None
+
+
+def test_status_strings_and_version(L):
+    assert L.ssd_version() >= 100
+    for code in range(8):
+        assert L.ssd_status_str(code)
+    assert L.ssd_status_str(99) == b"unknown status"
+
+
+def rglru(L, B=2, Lq=8, D=4, ind=F32, outd=F32, x=0, r=1, i=2, a=3, c=8.0, h0=None, y=4, hl=None):
+    p = lambda k: None if k is None else ptr(k)
+    return L.ssd_rglru_scan(B, Lq, D, ind, outd, p(x), p(r), p(i), p(a), c, p(h0), p(y), p(hl), None)
+
+
+def test_rglru_scan_validation(L):
+    assert rglru(L, B=-1) == SHAPE
+    assert rglru(L, ind=2) == DTYPE
+    assert rglru(L, ind=F32, outd=BF16) == DTYPE
+    assert rglru(L, x=None) == NULL
+    assert rglru(L, a=None) == NULL
+    assert rglru(L, c=float("inf")) == VALUE
+    assert rglru(L, c=float("nan")) == VALUE
+    assert rglru(L, y=0) == ALIAS                  # y on top of x
+    assert rglru(L, h0=5, hl=5) == ALIAS           # h_last on top of h0
+    assert L.ssd_rglru_scan(2, 8, 4, F32, F32, ctypes.c_void_p(P + 8), ptr(1), ptr(2), ptr(3), 8.0, None, ptr(4),
+                            None, None) == ALIGN
+    assert b"aligned" in L.ssd_last_error()
+    # empty problem: nothing to do, no launch
+    assert rglru(L, B=0) == OK
+    assert L.ssd_last_error() == b""
+
+
+def test_rglru_update_validation(L):
+    f = lambda **kw: L.ssd_rglru_update(kw.get("B", 4), kw.get("D", 8), kw.get("ind", BF16), kw.get("outd", F32),
+                                        ptr(0), ptr(1), ptr(2), ptr(3), kw.get("c", 8.0),
+                                        kw.get("state", ptr(4)), kw.get("y", ptr(5)), None)
+    assert f(D=-3) == SHAPE
+    assert f(state=None) == NULL
+    assert f(y=ptr(4)) == ALIAS
+    assert f(y=ptr(0)) == ALIAS
+    assert f(B=0) == OK
+
+
+def sel(L, B=1, Lq=16, D=8, N=16, ind=BF16, outd=F32, cu=None, nseq=0, y=9, A=2, Bm=3, Cm=4, h0=None, hl=None):
+    p = lambda k: None if k is None else ptr(k)
+    return L.ssd_selective_scan(B, Lq, D, N, ind, outd, ptr(0), ptr(1), p(A), p(Bm), p(Cm), None, None, None, 1,
+                                p(cu), nseq, p(h0), p(y), p(hl), None)
+
+
+def test_selective_scan_validation(L):
+    assert sel(L, N=3) == SHAPE
+    assert sel(L, N=32) == SHAPE
+    assert sel(L, B=2, cu=6, nseq=2) == SHAPE       # varlen needs B == 1
+    assert sel(L, cu=6, nseq=-1) == SHAPE
+    assert sel(L, cu=6, nseq=0) == SHAPE            # no sequences but L > 0
+    assert sel(L, A=None) == NULL
+    assert sel(L, Bm=None) == NULL
+    assert sel(L, y=1) == ALIAS
+    assert sel(L, h0=7, hl=7) == ALIAS
+    assert sel(L, ind=F32, outd=BF16) == DTYPE
+    assert sel(L, D=0) == OK
+
+
+def test_selective_update_validation(L):
+    f = lambda **kw: L.ssd_selective_update(kw.get("B", 2), kw.get("D", 8), kw.get("N", 16), BF16, F32, ptr(0),
+                                            ptr(1), ptr(2), ptr(3), ptr(4), None, None, None, 1,
+                                            kw.get("state", ptr(5)), kw.get("y", ptr(6)), None)
+    assert f(N=5) == SHAPE
+    assert f(state=None) == NULL
+    assert f(y=ptr(5)) == ALIAS
+    assert f(B=0) == OK
+
+
+def h2(L, d=128, lb=0.5, o=5, S0=None, SL=None, B=2):
+    p = lambda k: None if k is None else ptr(k)
+    return L.ssd_hgrn2_scan(B, 16, 4, d, BF16, F32, ptr(0), ptr(1), ptr(2), ptr(3), lb, p(S0), p(o), p(SL), None)
+
+
+def test_hgrn2_validation(L):
+    assert h2(L, d=48) == SHAPE
+    assert h2(L, d=256) == SHAPE
+    assert h2(L, lb=-0.1) == VALUE
+    assert h2(L, lb=1.5) == VALUE
+    assert h2(L, lb=float("nan")) == VALUE
+    assert h2(L, o=None) == NULL
+    assert h2(L, o=2) == ALIAS
+    assert h2(L, S0=6, SL=6) == ALIAS
+    assert h2(L, B=0) == OK
+    f = lambda **kw: L.ssd_hgrn2_update(2, 4, kw.get("d", 64), BF16, F32, ptr(0), ptr(1), ptr(2), ptr(3),
+                                        kw.get("lb", 0.5), kw.get("S", ptr(4)), kw.get("o", ptr(5)), None)
+    assert f(d=100) == SHAPE
+    assert f(S=None) == NULL
+    assert f(o=ptr(4)) == ALIAS
+    assert f(lb=2.0) == VALUE
+
+
+def test_python_layer_requires_gpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 4, 8)
+    with pytest.raises(ValueError):
+        ssd.rglru_scan(x, x, x, torch.zeros(8), 8.0)

@@ -1,0 +1,145 @@
+"""GPU parity of the RG-LRU kernels against the fp64 oracle (called through the C ABI).
+
+Tolerance: max|err| <= tau * RMS(oracle) on every output element and on h_last, tau = 1e-5 for
+fp32 inputs and 2e-2 for bf16 inputs (fp32 state)."""
+import numpy as np
+import pytest
+
+import oracle
+import selective_state_space_diag_amd as ssd
+from selective_state_space_diag_amd import synth
+from tests.helpers import TOL, assert_close, f64, host, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_case(B, L, D, dtype, seed, with_h0=True, c=8.0):
+    import torch
+    inp = synth.rglru_inputs(B, L, D, dtype, seed, c=c, with_h0=with_h0)
+    x, r, i = (to_dev(inp.t[n]) for n in ("x", "r_logit", "i_logit"))
+    a_log = to_dev(inp.p["a_log"])
+    h0 = to_dev(inp.p["h0"]) if with_h0 else None
+    y, hl = ssd.rglru_scan(x, r, i, a_log, c, h0=h0, return_last_state=True)
+    torch.cuda.synchronize()
+    yr, hr = oracle.rglru_scan(f64(inp.t["x"]), f64(inp.t["r_logit"]), f64(inp.t["i_logit"]),
+                               f64(inp.p["a_log"]), c, f64(inp.p.get("h0")))
+    assert_close(host(y), yr, TOL[dtype], "y")
+    assert_close(host(hl), hr, TOL[dtype], "h_last")
+    return inp, y
+
+
+def test_config0_fp32():
+    run_case(2, 128, 64, synth.F32, 1000, with_h0=False)
+
+
+@pytest.mark.parametrize("L", [1, 63, 64, 65, 127, 200])
+def test_ragged_lengths_bf16(L):
+    run_case(3, L, 300, synth.BF16, 7 + L)
+
+
+@pytest.mark.parametrize("D", [1, 129, 130, 257])
+def test_ragged_channels(D):
+    # odd D takes the one-channel-per-lane path, even D the two-channel one
+    run_case(2, 150, D, synth.BF16, 11 + D)
+    run_case(1, 70, D, synth.F32, 12 + D)
+
+
+def test_many_chunks_lookback_fp32():
+    # 40 chunks per (b, tile): long lookback chains, fp32 tolerance
+    run_case(2, 64 * 40 + 5, 256, synth.F32, 21)
+
+
+def test_bf16_output_rounds_fp32_result():
+    import torch
+    inp = synth.rglru_inputs(2, 300, 256, synth.BF16, 31, with_h0=True)
+    args = [to_dev(inp.t[n]) for n in ("x", "r_logit", "i_logit")] + [to_dev(inp.p["a_log"]), 8.0]
+    y32 = ssd.rglru_scan(*args, h0=to_dev(inp.p["h0"]))
+    y16 = ssd.rglru_scan(*args, h0=to_dev(inp.p["h0"]), out_dtype=torch.bfloat16)
+    assert y16.dtype == torch.bfloat16
+    diff = (y16.float() - y32.to(torch.bfloat16).float()).abs()
+    ulp = y32.abs().clamp_min(1e-30) * 2.0 ** -7
+    assert bool((diff <= ulp).all())
+
+
+def test_every_output_written_and_deterministic():
+    import torch
+    inp = synth.rglru_inputs(2, 333, 384, synth.BF16, 41)
+    x, r, i = (to_dev(inp.t[n]) for n in ("x", "r_logit", "i_logit"))
+    a_log = to_dev(inp.p["a_log"])
+    outs = []
+    for _ in range(2):
+        y = torch.full((2, 333, 384), float("nan"), device="cuda")
+        hl = torch.full((2, 384), float("nan"), device="cuda")
+        st = ssd.lib().ssd_rglru_scan(2, 333, 384, ssd.SSD_BF16, ssd.SSD_F32, x.data_ptr(), r.data_ptr(),
+                                      i.data_ptr(), a_log.data_ptr(), 8.0, None, y.data_ptr(), hl.data_ptr(),
+                                      torch.cuda.current_stream().cuda_stream)
+        assert st == 0
+        torch.cuda.synchronize()
+        assert not torch.isnan(y).any() and not torch.isnan(hl).any()
+        outs.append((y.clone(), hl.clone()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_decode_steps_equal_scan_and_oracle():
+    import torch
+    B, L, D = 4, 40, 320
+    inp = synth.rglru_inputs(B, L, D, synth.BF16, 51, with_h0=True)
+    x, r, i = (to_dev(inp.t[n]) for n in ("x", "r_logit", "i_logit"))
+    a_log = to_dev(inp.p["a_log"])
+    y_scan, h_scan = ssd.rglru_scan(x, r, i, a_log, 8.0, h0=to_dev(inp.p["h0"]), return_last_state=True)
+    state = to_dev(inp.p["h0"]).clone()
+    ys = [ssd.rglru_update(x[:, t].contiguous(), r[:, t].contiguous(), i[:, t].contiguous(), a_log, 8.0, state)
+          for t in range(L)]
+    torch.cuda.synchronize()
+    y_dec = torch.stack(ys, 1)
+    yr, hr = oracle.rglru_scan(f64(inp.t["x"]), f64(inp.t["r_logit"]), f64(inp.t["i_logit"]), f64(inp.p["a_log"]),
+                               8.0, f64(inp.p["h0"]))
+    assert_close(host(y_dec), yr, TOL[synth.BF16], "decode y")
+    assert_close(host(state), hr, TOL[synth.BF16], "decode state")
+    assert_close(host(y_dec), host(y_scan), 1e-5, "decode vs scan")
+
+
+def test_split_scan_carries_state():
+    import torch
+    inp = synth.rglru_inputs(2, 250, 130, synth.F32, 61, with_h0=True)
+    t = {n: to_dev(inp.t[n]) for n in ("x", "r_logit", "i_logit")}
+    a_log, h0 = to_dev(inp.p["a_log"]), to_dev(inp.p["h0"])
+    y, hl = ssd.rglru_scan(t["x"], t["r_logit"], t["i_logit"], a_log, 8.0, h0=h0, return_last_state=True)
+    m = 97
+    y1, h1 = ssd.rglru_scan(*(t[n][:, :m].contiguous() for n in ("x", "r_logit", "i_logit")), a_log, 8.0, h0=h0,
+                            return_last_state=True)
+    y2, h2 = ssd.rglru_scan(*(t[n][:, m:].contiguous() for n in ("x", "r_logit", "i_logit")), a_log, 8.0, h0=h1,
+                            return_last_state=True)
+    torch.cuda.synchronize()
+    assert_close(host(torch.cat([y1, y2], 1)), host(y), 1e-5, "split y")
+    assert_close(host(h2), host(hl), 1e-5, "split h_last")
+
+
+def test_empty_sequence_copies_h0():
+    import torch
+    h0 = torch.randn(3, 64, device="cuda")
+    e = torch.empty(3, 0, 64, device="cuda")
+    y, hl = ssd.rglru_scan(e, e, e, torch.zeros(64, device="cuda"), 8.0, h0=h0, return_last_state=True)
+    torch.cuda.synchronize()
+    assert y.shape == (3, 0, 64) and torch.equal(hl, h0)
+
+
+def test_config2_full_size_sampled_channels():
+    """B=8, L=8192, D=2560 bf16 at full size; every output of 64 sampled (b, d) channels vs the oracle."""
+    import torch
+    cfg = synth.CONFIGS[2]
+    inp = synth.config_inputs(2)
+    B, L, D = cfg["B"], cfg["L"], cfg["D"]
+    x, r, i = (to_dev(inp.t[n]) for n in ("x", "r_logit", "i_logit"))
+    a_log = to_dev(inp.p["a_log"])
+    y, hl = ssd.rglru_scan(x, r, i, a_log, 8.0, return_last_state=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2024)
+    bs = rng.integers(0, B, 64)
+    ds = rng.integers(0, D, 64)
+    g = lambda n: np.ascontiguousarray(synth.bf16_to_f64(inp.t[n].data[bs, :, ds]).T[None])    # [1, L, 64]
+    yr, hr = oracle.rglru_scan(g("x"), g("r_logit"), g("i_logit"), inp.p["a_log"][ds].astype(np.float64), 8.0)
+    yg = host(y[torch.as_tensor(bs, device="cuda"), :, torch.as_tensor(ds, device="cuda")]).T[None]
+    assert_close(yg, yr, TOL[synth.BF16], "y sampled")
+    assert_close(host(hl)[bs, ds][None], hr, TOL[synth.BF16], "h_last sampled")
+    assert torch.isfinite(y).all()

@@ -1,0 +1,173 @@
+"""GPU parity of the selective-scan kernels against the fp64 oracle (through the C ABI).
+
+Tolerance: max|err| <= tau * RMS(oracle), tau = 1e-5 (fp32 inputs) or 2e-2 (bf16 inputs, fp32
+state), on every output element and on h_last.  Full-size workloads are checked on every output
+of sampled channels (exact for those channels, since channels are independent)."""
+import numpy as np
+import pytest
+
+import oracle
+import selective_state_space_diag_amd as ssd
+from selective_state_space_diag_amd import synth
+from tests.helpers import TOL, assert_close, f64, host, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_run(inp, out_dtype=None, return_last_state=True):
+    t = inp.t
+    return ssd.selective_scan(to_dev(t["x"]), to_dev(t["dt"]), to_dev(inp.p["A"]), to_dev(t["Bm"]), to_dev(t["Cm"]),
+                              Dskip=to_dev(inp.p.get("Dskip")), z=to_dev(t["z"]) if "z" in t else None,
+                              dt_bias=to_dev(inp.p.get("dt_bias")), dt_softplus=inp.s["dt_softplus"],
+                              cu_seqlens=inp.s.get("cu_seqlens"), h0=to_dev(inp.p.get("h0")),
+                              return_last_state=return_last_state, out_dtype=out_dtype)
+
+
+def oracle_run(inp):
+    t = inp.t
+    return oracle.selective_scan(f64(t["x"]), f64(t["dt"]), f64(inp.p["A"]), f64(t["Bm"]), f64(t["Cm"]),
+                                 Dskip=f64(inp.p.get("Dskip")), z=f64(t.get("z")), dt_bias=f64(inp.p.get("dt_bias")),
+                                 dt_softplus=inp.s["dt_softplus"], cu_seqlens=inp.s.get("cu_seqlens"),
+                                 h0=f64(inp.p.get("h0")))
+
+
+def check(inp, tol):
+    import torch
+    y, hl = gpu_run(inp)
+    torch.cuda.synchronize()
+    yr, hr = oracle_run(inp)
+    e1 = assert_close(host(y), yr, tol, "y")
+    e2 = assert_close(host(hl), hr, tol, "h_last")
+    return e1, e2
+
+
+@pytest.mark.parametrize("L", [1, 17, 100, 333])
+def test_batched_bf16_ragged(L):
+    check(synth.selective_inputs(2, L, 200, 16, synth.BF16, 100 + L, with_h0=True), TOL[synth.BF16])
+
+
+def test_batched_fp32_tight_tolerance():
+    check(synth.selective_inputs(2, 300, 96, 16, synth.F32, 7, with_h0=True), TOL[synth.F32])
+
+
+def test_scan_term_alone_without_skip_and_gate():
+    # with Dskip and z absent the output is the scan readout only, so scan errors are not masked
+    check(synth.selective_inputs(3, 257, 130, 16, synth.BF16, 8, with_z=False, with_skip=False, with_h0=True),
+          TOL[synth.BF16])
+    check(synth.selective_inputs(2, 129, 64, 16, synth.F32, 9, with_z=False, with_skip=False), TOL[synth.F32])
+
+
+@pytest.mark.parametrize("N", [1, 2, 4, 8])
+def test_smaller_state_sizes(N):
+    check(synth.selective_inputs(2, 90, 70, N, synth.F32, 10 + N, num_scales=2, with_h0=True), TOL[synth.F32])
+
+
+def test_raw_delta_without_softplus_and_bias():
+    inp = synth.selective_inputs(2, 150, 64, 16, synth.F32, 20, dt_softplus=False, with_h0=True)
+    inp.p["dt_bias"] = np.full(64, 0.01, dtype=np.float32)
+    check(inp, TOL[synth.F32])
+
+
+def test_softplus_with_bias():
+    inp = synth.selective_inputs(2, 150, 64, 16, synth.BF16, 21)
+    inp.p["dt_bias"] = np.linspace(-1, 1, 64).astype(np.float32)
+    check(inp, TOL[synth.BF16])
+
+
+def test_clamp_acts_for_positive_A():
+    # delta*A > 20 for some states: abar is capped at e^20 (short sequence so values stay finite)
+    inp = synth.selective_inputs(1, 3, 64, 16, synth.F32, 22, dt_softplus=False)
+    inp.p["A"] = np.abs(inp.p["A"]) * 300.0
+    check(inp, TOL[synth.F32])
+
+
+def test_varlen_with_empty_and_unit_sequences():
+    lengths = [5, 0, 1, 300, 0, 77, 2, 0]
+    cu = synth.cu_seqlens_from_lengths(lengths)
+    inp = synth.selective_inputs(1, int(cu[-1]), 130, 16, synth.BF16, 30, cu_seqlens=cu, with_h0=True)
+    check(inp, TOL[synth.BF16])
+    inp = synth.selective_inputs(1, int(cu[-1]), 64, 16, synth.F32, 31, cu_seqlens=cu, with_h0=True)
+    check(inp, TOL[synth.F32])
+
+
+def test_varlen_single_sequence_equals_batched():
+    import torch
+    inp = synth.selective_inputs(1, 500, 96, 16, synth.BF16, 32, with_h0=True)
+    yb, hb = gpu_run(inp)
+    inp.s["cu_seqlens"] = np.array([0, 500], dtype=np.int32)
+    yv, hv = gpu_run(inp)
+    torch.cuda.synchronize()
+    assert_close(host(yv), host(yb), 1e-5, "varlen vs batched y")
+    assert_close(host(hv), host(hb), 1e-5, "varlen vs batched h_last")
+
+
+def test_bf16_output():
+    import torch
+    inp = synth.selective_inputs(2, 200, 128, 16, synth.BF16, 33)
+    y32 = gpu_run(inp, return_last_state=False)
+    y16 = gpu_run(inp, out_dtype=torch.bfloat16, return_last_state=False)
+    diff = (y16.float() - y32.to(torch.bfloat16).float()).abs()
+    assert bool((diff <= y32.abs().clamp_min(1e-30) * 2.0 ** -7).all())
+
+
+def test_deterministic_and_fully_written():
+    import torch
+    inp = synth.selective_inputs(2, 777, 200, 16, synth.BF16, 34)
+    a = gpu_run(inp)
+    b = gpu_run(inp)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert torch.isfinite(a[0]).all()
+
+
+def test_decode_steps_equal_scan():
+    import torch
+    B, L, D, N = 4, 30, 130, 16
+    inp = synth.selective_inputs(B, L, D, N, synth.BF16, 40, with_h0=True)
+    t = {k: to_dev(v) for k, v in inp.t.items()}
+    A, Dskip, h0 = to_dev(inp.p["A"]), to_dev(inp.p["Dskip"]), to_dev(inp.p["h0"])
+    state = h0.clone()
+    ys = [ssd.selective_update(t["x"][:, s].contiguous(), t["dt"][:, s].contiguous(), A, t["Bm"][:, s].contiguous(),
+                               t["Cm"][:, s].contiguous(), state, Dskip=Dskip, z=t["z"][:, s].contiguous())
+          for s in range(L)]
+    torch.cuda.synchronize()
+    yr, hr = oracle_run(inp)
+    assert_close(host(torch.stack(ys, 1)), yr, TOL[synth.BF16], "decode y")
+    assert_close(host(state), hr, TOL[synth.BF16], "decode state")
+
+
+def _sampled_check(inp, nsample, seed, tol):
+    """Every output of sampled channels vs the oracle (channels are independent)."""
+    import torch
+    y, hl = gpu_run(inp)
+    torch.cuda.synchronize()
+    B, L, D = inp.t["x"].shape
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for b in range(B):
+        ds = np.sort(rng.choice(D, nsample, replace=False))
+        g = lambda n: synth.bf16_to_f64(inp.t[n].data[b:b + 1][:, :, ds])
+        gn = lambda n: synth.bf16_to_f64(inp.t[n].data[b:b + 1])
+        yr, hr = oracle.selective_scan(g("x"), g("dt"), inp.p["A"][ds].astype(np.float64), gn("Bm"), gn("Cm"),
+                                       Dskip=f64(inp.p["Dskip"][ds]) if "Dskip" in inp.p else None,
+                                       z=g("z") if "z" in inp.t else None, dt_softplus=inp.s["dt_softplus"],
+                                       cu_seqlens=inp.s.get("cu_seqlens"))
+        dsel = torch.as_tensor(ds, device="cuda")
+        worst = max(worst, assert_close(host(y[b:b + 1][:, :, dsel]), yr, tol, f"y batch {b}"))
+        hsel = hl[b:b + 1] if inp.s.get("cu_seqlens") is None else hl
+        assert_close(host(hsel[:, dsel]), hr, tol, f"h_last batch {b}")
+    assert torch.isfinite(y).all()
+    return worst
+
+
+def test_config1_full_size_sampled_channels():
+    inp = synth.config_inputs(1)
+    _sampled_check(inp, 16, 1, TOL[synth.BF16])
+    inp.t.pop("z")
+    inp.p.pop("Dskip")
+    _sampled_check(inp, 16, 2, TOL[synth.BF16])
+
+
+def test_config4_varlen_full_size_sampled_channels():
+    inp = synth.config_inputs(4)
+    _sampled_check(inp, 8, 3, TOL[synth.BF16])
