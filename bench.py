@@ -58,6 +58,24 @@ def hgrn2_bytes(B, L, H, d, in_b=2, out_b=4):
     return B * L * H * d * (4 * in_b + out_b)
 
 
+def profiled_traffic(profile, sources):
+    """HBM bytes per call recorded by rocprofv3 counter runs in profiles/<profile>, if the kernel
+    sources are unchanged since (their sha256 is stored with the figure); else None."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", profile)
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"<!-- profile-data: (\{.*\}) -->", open(path).read())
+    if not m:
+        return None
+    data = json.loads(m.group(1))
+    h = hashlib.sha256()
+    for f in sources:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return data["traffic_bytes_per_call"] if h.hexdigest() == data["kernel_sources_sha256"] else None
+
+
 # ----------------------------------------------------------------------------- timing helpers
 def time_calls(fn, n_sets, steps, warmup):
     """Run ``fn(i % n_sets)`` warmup times, then time ``steps`` calls with one event pair per call
@@ -228,6 +246,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-forms", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="first run a plain device-to-device tensor copy of this many MiB three times (a known-size "
+                         "kernel for scaling hardware traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the scans shard with no communication across channels, batches "
@@ -240,6 +261,15 @@ def main():
         sys.exit(1)
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
+
+    if args.copy_calibration_mb > 0:
+        n = args.copy_calibration_mb * (1 << 20) // 4
+        src = torch.ones(n, device=device)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     head, host_inputs = headline(args, device)
     ms = head["ms"]
@@ -269,8 +299,11 @@ def main():
         "hbm": {"achieved_gbs": hbm_gbs, "peak_gbs": HBM_PEAK_GBS, "frac": hbm_gbs / HBM_PEAK_GBS,
                 "algorithmic_bytes": head["bytes"]},
         "roofline": {"bound": "alu", "achieved": achieved_tflops, "peak": FP32_VECTOR_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved_tflops / FP32_VECTOR_TFLOPS, "traffic": None,
-                     "kernel": "selective scan (aggregate + scan kernels of one call)",
+                     "unit": "TFLOP/s", "frac": achieved_tflops / FP32_VECTOR_TFLOPS,
+                     "traffic": profiled_traffic("selective_scan_B4_L2048_D1536_N16.md",
+                                                 ["selective_state_space_diag_amd/csrc/selective.hip",
+                                                  "selective_state_space_diag_amd/csrc/common.hpp"]),
+                     "kernel": "selective scan call: aggregate + carry + scan kernels",
                      "flops_per_update": SELECTIVE_FLOPS_PER_UPDATE,
                      "mean_call_ms": head["mean_call_ms"], "min_call_ms": head["min_call_ms"]},
     }

@@ -98,7 +98,7 @@ template <> struct Raw<bf16_t> {
   static __device__ __forceinline__ float cvt(T r) { return __uint_as_float(r << 16); }
 };
 
-constexpr int kPrefetch = 4;   // rows of x / dt / z in flight per lane (also the unroll factor)
+constexpr int kPrefetch = 2;   // rows of x / dt / z in flight per lane (also the unroll factor)
 constexpr int kRowBlock = 64;  // rows of B / C staged in LDS at a time
 
 // B_n and C_n are shared by every channel of a row, so the workgroup (all of whose lanes work on
@@ -150,6 +150,8 @@ __device__ __forceinline__ float row_step(float xx, float dd, float zz, const fl
     }
     h[n] = fmaf(hw_exp2(dA), h[n], dx * bc[n]);
     if (READOUT) acc = fmaf(bc[NS + n], h[n], acc);
+    // states in groups of 8: bounds the exponentials held in flight (register pressure)
+    if (NS > 8 && (n & 7) == 7) __builtin_amdgcn_sched_barrier(0);
   }
   if (!CLAMP && !READOUT) sum_delta += delta;
   if (READOUT) {
@@ -444,7 +446,22 @@ __global__ __launch_bounds__(kThreads) void selective_update_kernel(
 }
 
 // ----------------------------------------------------------------------------- dispatch helpers
-constexpr int64_t kTargetWaves = 4096;  // enough waves in flight to fill 256 CUs
+// Waves the scan pass keeps resident per CU (its register budget allows 3 per SIMD): the plan cuts
+// sequences so that all scan waves fit in one resident round.
+constexpr int64_t kScanWavesPerCU = 12;
+
+int64_t device_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) ==
+                                                hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return cus;
+}
 
 template <typename Tin, typename Tout, int NS>
 hipError_t launch_passes(const SelParams& p, int64_t U, bool softplus, hipStream_t s) {
@@ -505,6 +522,7 @@ struct Plan {
 
 Plan make_plan(const SelectiveScanArgs& a) {
   Plan pl;
+  const int64_t kTargetWaves = device_cus() * kScanWavesPerCU;
   const int64_t waves_per_row = (a.D + 63) / 64;
   if (a.cu_seqlens == nullptr) {
     const int64_t row_waves = a.B * waves_per_row;

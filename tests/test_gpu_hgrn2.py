@@ -46,8 +46,16 @@ def test_lower_bounds_bf16(lb):
 
 
 @pytest.mark.parametrize("L", [1, 63, 64, 65, 130])
-def test_ragged_lengths(L):
-    check(synth.hgrn2_inputs(1, L, 4, 64, synth.BF16, 100 + L), TOL[synth.BF16])
+@pytest.mark.parametrize("d", [64, 128])
+def test_ragged_lengths(L, d):
+    # d = 128 with bf16 inputs and lower bound 0.5 runs the chunked MFMA form; d = 64 the recurrent one
+    check(synth.hgrn2_inputs(1, L, 4, d, synth.BF16, 100 + L, with_S0=True), TOL[synth.BF16])
+
+
+@pytest.mark.parametrize("B,H", [(1, 3), (3, 8)])
+def test_chunked_form_head_mappings(B, H):
+    # B*H not a multiple of 8 and a multiple of 8 take the two workgroup-to-head mappings
+    check(synth.hgrn2_inputs(B, 150, H, 128, synth.BF16, 7 * B + H, with_S0=True), TOL[synth.BF16])
 
 
 def test_decode_steps_equal_scan():
