@@ -73,7 +73,8 @@ int ssd_version(void);
  *   y                   : [B, L, D] (out dtype)
  *   h_last              : [B, D] fp32 or NULL; receives h_{L-1} (h0 when L = 0)
  * Errors: SSD_ERR_NULL (x, r_logit, i_logit, a_log, y when B*L*D > 0), SSD_ERR_SHAPE (negative
- * size), SSD_ERR_DTYPE, SSD_ERR_ALIGN, SSD_ERR_VALUE (c not finite), SSD_ERR_ALIAS.
+ * size, D >= 2^22, or B * ceil(L/64) * ceil(D/64) >= 2^31), SSD_ERR_DTYPE, SSD_ERR_ALIGN,
+ * SSD_ERR_VALUE (c not finite), SSD_ERR_ALIAS.
  * ------------------------------------------------------------------------------------------- */
 int ssd_rglru_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype,
                    const void* x, const void* r_logit, const void* i_logit,

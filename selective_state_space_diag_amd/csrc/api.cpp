@@ -161,7 +161,7 @@ int ssd_rglru_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype,
                    void* stream) {
   SSD_TRY(check_dtypes(in_dtype, out_dtype));
   if (B < 0 || L < 0 || D < 0) return fail(SSD_ERR_SHAPE, "negative size");
-  if (too_big({B, L, D}) || B * ((L + 63) / 64) * ((D + 63) / 64) >= (int64_t)1 << 31)
+  if (too_big({B, L, D}) || D >= (int64_t)1 << 22 || B * ((L + 63) / 64) * ((D + 63) / 64) >= (int64_t)1 << 31)
     return fail(SSD_ERR_SHAPE, "problem too large");
   if (!std::isfinite(c)) return fail(SSD_ERR_VALUE, "c must be finite");
   const int64_t nact = B * L * D;

@@ -74,6 +74,67 @@ template <> struct io2<bf16_t> {
   }
 };
 
+// ------------------------------------------------------------------ buffer windows
+// A buffer resource over [p, p + bytes), bytes < 2^31.  Accesses through it take a per-lane byte
+// offset (vector register) plus a wave-uniform byte offset (scalar register), so a tile of rows
+// costs no per-lane 64-bit address arithmetic.  Callers keep every offset inside the window.
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_window(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// V consecutive elements of type T per lane through a window.
+template <typename T, int V> struct win;
+template <> struct win<float, 1> {
+  using raw = float;
+  static __device__ __forceinline__ raw load(__amdgpu_buffer_rsrc_t w, uint32_t lane_off, uint32_t row_off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(w, (int)lane_off, (int)row_off, 0));
+  }
+  static __device__ __forceinline__ float get(raw r, int) { return r; }
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t w, uint32_t lane_off, uint32_t row_off,
+                                               const float* v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[0]), w, (int)lane_off, (int)row_off, 0);
+  }
+};
+template <> struct win<float, 2> {
+  using raw = u32x2_t;
+  static __device__ __forceinline__ raw load(__amdgpu_buffer_rsrc_t w, uint32_t lane_off, uint32_t row_off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(w, (int)lane_off, (int)row_off, 0);
+  }
+  static __device__ __forceinline__ float get(raw r, int v) { return __uint_as_float(v == 0 ? r.x : r.y); }
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t w, uint32_t lane_off, uint32_t row_off,
+                                               const float* v) {
+    u32x2_t d;
+    d.x = __float_as_uint(v[0]);
+    d.y = __float_as_uint(v[1]);
+    __builtin_amdgcn_raw_buffer_store_b64(d, w, (int)lane_off, (int)row_off, 0);
+  }
+};
+template <> struct win<bf16_t, 1> {
+  using raw = unsigned short;
+  static __device__ __forceinline__ raw load(__amdgpu_buffer_rsrc_t w, uint32_t lane_off, uint32_t row_off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(w, (int)lane_off, (int)row_off, 0);
+  }
+  static __device__ __forceinline__ float get(raw r, int) { return bf16_to_f32(r); }
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t w, uint32_t lane_off, uint32_t row_off,
+                                               const float* v) {
+    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v[0]), w, (int)lane_off, (int)row_off, 0);
+  }
+};
+template <> struct win<bf16_t, 2> {
+  using raw = uint32_t;
+  static __device__ __forceinline__ raw load(__amdgpu_buffer_rsrc_t w, uint32_t lane_off, uint32_t row_off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(w, (int)lane_off, (int)row_off, 0);
+  }
+  static __device__ __forceinline__ float get(raw r, int v) { return v == 0 ? bf16_lo(r) : bf16_hi(r); }
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t w, uint32_t lane_off, uint32_t row_off,
+                                               const float* v) {
+    const uint32_t d = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    __builtin_amdgcn_raw_buffer_store_b32(d, w, (int)lane_off, (int)row_off, 0);
+  }
+};
+
 // ------------------------------------------------------------------ hardware transcendentals
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
