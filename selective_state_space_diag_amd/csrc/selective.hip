@@ -85,18 +85,13 @@ __device__ __forceinline__ Unit unit_of(const SelParams& p, int64_t u) {
 }
 
 // ----------------------------------------------------------------------------- row inputs
-// Raw activation element kept in a VGPR until use (the load stays in flight meanwhile).
-template <typename Tin> struct Raw;
-template <> struct Raw<float> {
-  using T = float;
-  static __device__ __forceinline__ T load(const void* p, int64_t i) { return static_cast<const float*>(p)[i]; }
-  static __device__ __forceinline__ float cvt(T r) { return r; }
-};
-template <> struct Raw<bf16_t> {
-  using T = uint32_t;
-  static __device__ __forceinline__ T load(const void* p, int64_t i) { return static_cast<const uint16_t*>(p)[i]; }
-  static __device__ __forceinline__ float cvt(T r) { return __uint_as_float(r << 16); }
-};
+// x / dt / z / y of a unit are addressed through buffer windows over the unit's rows: a per-lane
+// channel offset plus a wave-uniform row offset, no per-lane 64-bit address arithmetic.  The plan
+// keeps every unit's window under 2^31 bytes.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t unit_window(const void* a, int64_t row0, int64_t nrows, int64_t D,
+                                                              int es) {
+  return make_window(static_cast<const char*>(a) + row0 * D * es, (uint32_t)(nrows * D * es));
+}
 
 constexpr int kPrefetch = 2;   // rows of x / dt / z in flight per lane (also the unroll factor)
 constexpr int kRowBlock = 64;  // rows of B / C staged in LDS at a time
@@ -134,26 +129,46 @@ struct BCStage {
 };
 
 // ----------------------------------------------------------------------------- the row loop
+// How abar_n = exp(min(delta A_n, 20)) is formed (a wave-uniform choice):
+//   kClamp: exp of the clamped exponent, per state (any A, any delta);
+//   kExp:   exp per state without the clamp (delta >= 0 and all A <= 0, so delta A_n <= 0);
+//   kPow:   as kExp, for rows of A that are integer multiples of their first entry,
+//           A_n = (n+1) A_0: then abar_n = abar_0^(n+1), formed by products of earlier powers
+//           (depth ceil(log2(n+1))), one exponential per row instead of N.
+enum Disc { kClamp = 0, kExp = 1, kPow = 2 };
+
 // One row of one channel: discretise, advance the N states, optionally read out.
-template <int NS, bool SOFTPLUS, bool CLAMP, bool READOUT, bool GATE>
+template <int NS, bool SOFTPLUS, int DISC, bool READOUT, bool GATE>
 __device__ __forceinline__ float row_step(float xx, float dd, float zz, const float* bc, const float* A2, float dskip,
                                           float* h, float* e, float& sum_delta) {
   const float delta = SOFTPLUS ? softplus_f(dd) : dd;
   const float dx = delta * xx;
   float acc = 0.0f;
+  float pw[DISC == kPow ? NS : 1];
+  if constexpr (DISC == kPow) {
+    pw[0] = hw_exp2(delta * A2[0]);
+#pragma unroll
+    for (int k = 2; k <= NS; ++k) pw[k - 1] = pw[k / 2 - 1] * pw[k - k / 2 - 1];
+  }
 #pragma unroll
   for (int n = 0; n < NS; ++n) {
-    float dA = delta * A2[n];
-    if (CLAMP) {
-      dA = dA > kClampLog2 ? kClampLog2 : dA;
-      if (!READOUT) e[n] += dA;
+    float ab;
+    if constexpr (DISC == kPow) {
+      ab = pw[n];
+    } else {
+      float dA = delta * A2[n];
+      if (DISC == kClamp) {
+        dA = dA > kClampLog2 ? kClampLog2 : dA;
+        if (!READOUT) e[n] += dA;
+      }
+      ab = hw_exp2(dA);
     }
-    h[n] = fmaf(hw_exp2(dA), h[n], dx * bc[n]);
+    h[n] = fmaf(ab, h[n], dx * bc[n]);
     if (READOUT) acc = fmaf(bc[NS + n], h[n], acc);
     // states in groups of 8: bounds the exponentials held in flight (register pressure)
     if (NS > 8 && (n & 7) == 7) __builtin_amdgcn_sched_barrier(0);
   }
-  if (!CLAMP && !READOUT) sum_delta += delta;
+  if (DISC != kClamp && !READOUT) sum_delta += delta;
   if (READOUT) {
     acc = fmaf(dskip, xx, acc);
     if (GATE) acc *= silu_f(zz);
@@ -166,47 +181,53 @@ __device__ __forceinline__ float row_step(float xx, float dd, float zz, const fl
 // in registers.  Loads and stores are unconditional inside the unrolled groups (indices are
 // clamped in range) so the compiler counts outstanding memory operations exactly; a lane without a
 // channel of its own recomputes channel D-1 bit for bit and rewrites the same value.
-template <typename Tin, typename Tout, int NS, bool SOFTPLUS, bool CLAMP, bool READOUT, bool GATE>
+template <typename Tin, typename Tout, int NS, bool SOFTPLUS, int DISC, bool READOUT, bool GATE>
 __device__ __forceinline__ void run_rows(const SelParams& p, int64_t row0, int64_t row1, int64_t dl,
                                          const float* A2, float bias, float dskip, float* h, float* e,
                                          float& sum_delta, float* lds) {
-  using R = Raw<Tin>;
+  using W = win<Tin, 1>;
   using Stage = BCStage<NS, READOUT>;
   constexpr int PR = Stage::PER_ROW;
   const int64_t nrows = row1 - row0;
   if (nrows <= 0) return;
-  typename R::T rx[kPrefetch], rd[kPrefetch], rz[kPrefetch];
+  const auto wx = unit_window(p.x, row0, nrows, p.D, sizeof(Tin));
+  const auto wd = unit_window(p.dt, row0, nrows, p.D, sizeof(Tin));
+  const auto wz = unit_window(GATE ? p.z : p.x, row0, nrows, p.D, sizeof(Tin));
+  const auto wy = unit_window(READOUT ? p.y : p.x, row0, nrows, p.D, sizeof(Tout));
+  const uint32_t lane_in = (uint32_t)(dl * (int64_t)sizeof(Tin)), row_in = (uint32_t)(p.D * (int64_t)sizeof(Tin));
+  const uint32_t lane_out = (uint32_t)(dl * (int64_t)sizeof(Tout)), row_out = (uint32_t)(p.D * (int64_t)sizeof(Tout));
+  const int last = (int)nrows - 1;
+  typename W::raw rx[kPrefetch], rd[kPrefetch], rz[kPrefetch];
 #pragma unroll
   for (int k = 0; k < kPrefetch; ++k) {
-    const int64_t r = row0 + min((int64_t)k, nrows - 1);
-    rx[k] = R::load(p.x, r * p.D + dl);
-    rd[k] = R::load(p.dt, r * p.D + dl);
-    if (GATE) rz[k] = R::load(p.z, r * p.D + dl);
+    const uint32_t ro = (uint32_t)min(k, last) * row_in;
+    rx[k] = W::load(wx, lane_in, ro);
+    rd[k] = W::load(wd, lane_in, ro);
+    if (GATE) rz[k] = W::load(wz, lane_in, ro);
   }
   Stage st;
   st.template fetch<Tin>(p, row0, nrows, 0);
   st.put(lds);
-  const int64_t nblk = (nrows + kRowBlock - 1) / kRowBlock;
-  for (int64_t blk = 0; blk < nblk; ++blk) {
+  const int nblk = (int)((nrows + kRowBlock - 1) / kRowBlock);
+  for (int blk = 0; blk < nblk; ++blk) {
     float* cur = lds + (blk & 1) * Stage::PER_BLOCK;
     if (blk + 1 < nblk) st.template fetch<Tin>(p, row0, nrows, blk + 1);
     __syncthreads();  // block blk is in LDS; the other buffer is free
-    const int64_t r_begin = blk * kRowBlock;
-    const int64_t r_end = min(r_begin + kRowBlock, nrows);
-    const int64_t r_full = r_begin + (r_end - r_begin) / kPrefetch * kPrefetch;
-    for (int64_t base = r_begin; base < r_full; base += kPrefetch) {
+    const int r_begin = blk * kRowBlock;
+    const int r_end = min(r_begin + kRowBlock, (int)nrows);
+    const int r_full = r_begin + (r_end - r_begin) / kPrefetch * kPrefetch;
+    for (int base = r_begin; base < r_full; base += kPrefetch) {
 #pragma unroll
       for (int k = 0; k < kPrefetch; ++k) {
         // slot of row i in the prefetch ring is i % kPrefetch = k (r_begin is a multiple of it)
-        const int64_t i = base + k;
-        const int64_t row = row0 + i;
-        const float xx = R::cvt(rx[k]);
-        const float dd = R::cvt(rd[k]) + bias;
-        const float zz = GATE ? R::cvt(rz[k]) : 0.0f;
-        const int64_t rp = row0 + min(i + kPrefetch, nrows - 1);
-        rx[k] = R::load(p.x, rp * p.D + dl);
-        rd[k] = R::load(p.dt, rp * p.D + dl);
-        if (GATE) rz[k] = R::load(p.z, rp * p.D + dl);
+        const int i = base + k;
+        const float xx = W::get(rx[k], 0);
+        const float dd = W::get(rd[k], 0) + bias;
+        const float zz = GATE ? W::get(rz[k], 0) : 0.0f;
+        const uint32_t ro = (uint32_t)min(i + kPrefetch, last) * row_in;
+        rx[k] = W::load(wx, lane_in, ro);
+        rd[k] = W::load(wd, lane_in, ro);
+        if (GATE) rz[k] = W::load(wz, lane_in, ro);
         float bc[PR];
         if constexpr (PR % 4 == 0) {
           const float4* src = reinterpret_cast<const float4*>(cur + (i - r_begin) * PR);
@@ -219,8 +240,8 @@ __device__ __forceinline__ void run_rows(const SelParams& p, int64_t row0, int64
 #pragma unroll
           for (int q = 0; q < PR; ++q) bc[q] = cur[(i - r_begin) * PR + q];
         }
-        const float y = row_step<NS, SOFTPLUS, CLAMP, READOUT, GATE>(xx, dd, zz, bc, A2, dskip, h, e, sum_delta);
-        if (READOUT) io<Tout>::store(p.y, row * p.D + dl, y);
+        const float y = row_step<NS, SOFTPLUS, DISC, READOUT, GATE>(xx, dd, zz, bc, A2, dskip, h, e, sum_delta);
+        if (READOUT) win<Tout, 1>::store(wy, lane_out, (uint32_t)i * row_out, &y);
         // keep rows in program order so the B / C of later rows are not all read into registers early
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -228,19 +249,35 @@ __device__ __forceinline__ void run_rows(const SelParams& p, int64_t row0, int64
     // rows of this block past the last full group (only in the sequence's final block)
 #pragma unroll
     for (int k = 0; k < kPrefetch; ++k) {
-      const int64_t i = r_full + k;
+      const int i = r_full + k;
       if (i < r_end) {
-        const int64_t row = row0 + i;
         float bc[PR];
 #pragma unroll
         for (int q = 0; q < PR; ++q) bc[q] = cur[(i - r_begin) * PR + q];
-        const float y = row_step<NS, SOFTPLUS, CLAMP, READOUT, GATE>(
-            R::cvt(rx[k]), R::cvt(rd[k]) + bias, GATE ? R::cvt(rz[k]) : 0.0f, bc, A2, dskip, h, e, sum_delta);
-        if (READOUT) io<Tout>::store(p.y, row * p.D + dl, y);
+        const float y = row_step<NS, SOFTPLUS, DISC, READOUT, GATE>(
+            W::get(rx[k], 0), W::get(rd[k], 0) + bias, GATE ? W::get(rz[k], 0) : 0.0f, bc, A2, dskip, h, e,
+            sum_delta);
+        if (READOUT) win<Tout, 1>::store(wy, lane_out, (uint32_t)i * row_out, &y);
       }
     }
     if (blk + 1 < nblk) st.put(lds + ((blk + 1) & 1) * Stage::PER_BLOCK);
   }
+}
+
+// Loads the lane's row of A (scaled to base 2) and picks the wave's discretisation (see Disc).
+template <int NS, bool SOFTPLUS>
+__device__ __forceinline__ int load_A(const SelParams& p, int64_t dl, float* A2) {
+  bool nonpos = true, multiples = true;
+  const float a0 = p.A[dl * NS];
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    const float a = p.A[dl * NS + n];
+    A2[n] = a * kLog2e;
+    nonpos = nonpos && !(a > 0.0f);
+    multiples = multiples && (a == (float)(n + 1) * a0);
+  }
+  if (!(SOFTPLUS && __all(nonpos))) return kClamp;
+  return __all(multiples) ? kPow : kExp;
 }
 
 // ----------------------------------------------------------------------------- pass 1: aggregates
@@ -253,32 +290,40 @@ __global__ __launch_bounds__(kThreads, 4) void selective_aggregate_kernel(SelPar
   const bool active = d < p.D;
   const int64_t dl = active ? d : p.D - 1;  // lanes past D recompute channel D-1, store nothing
   float A2[NS];
-  bool nonpos = true;
-#pragma unroll
-  for (int n = 0; n < NS; ++n) {
-    A2[n] = p.A[dl * NS + n] * kLog2e;
-    nonpos = nonpos && !(A2[n] > 0.0f);
-  }
+  const int disc = load_A<NS, SOFTPLUS>(p, dl, A2);
   const float bias = p.dt_bias ? p.dt_bias[dl] : 0.0f;
   float h[NS], e[NS];
 #pragma unroll
   for (int n = 0; n < NS; ++n) { h[n] = 0.0f; e[n] = 0.0f; }
   float sum_delta = 0.0f;
   __shared__ float lds[2 * BCStage<NS, false>::PER_BLOCK];
-  const bool noclamp = SOFTPLUS && __all(nonpos);
-  if (noclamp)
-    run_rows<Tin, float, NS, SOFTPLUS, false, false, false>(p, U.row0, U.row1, dl, A2, bias, 0.0f, h, e, sum_delta,
-                                                            lds);
+  if (disc == kPow)
+    run_rows<Tin, float, NS, SOFTPLUS, kPow, false, false>(p, U.row0, U.row1, dl, A2, bias, 0.0f, h, e, sum_delta, lds);
+  else if (disc == kExp)
+    run_rows<Tin, float, NS, SOFTPLUS, kExp, false, false>(p, U.row0, U.row1, dl, A2, bias, 0.0f, h, e, sum_delta, lds);
   else
-    run_rows<Tin, float, NS, SOFTPLUS, true, false, false>(p, U.row0, U.row1, dl, A2, bias, 0.0f, h, e, sum_delta,
-                                                           lds);
+    run_rows<Tin, float, NS, SOFTPLUS, kClamp, false, false>(p, U.row0, U.row1, dl, A2, bias, 0.0f, h, e, sum_delta,
+                                                             lds);
   if (!active) return;
 #pragma unroll
   for (int n = 0; n < NS; ++n) {
-    const float P = noclamp ? hw_exp2(A2[n] * sum_delta) : hw_exp2(e[n]);
+    // prod abar = 2^(sum of the exponents): A2 sum(delta) without the clamp, else the clamped sum
+    const float P = disc != kClamp ? hw_exp2(A2[n] * sum_delta) : hw_exp2(e[n]);
     p.aggP[(u * NS + n) * p.D + d] = P;
     p.aggH[(u * NS + n) * p.D + d] = h[n];
   }
+}
+
+template <typename Tin, typename Tout, int NS, bool SOFTPLUS, bool GATE>
+__device__ __forceinline__ void scan_rows(const SelParams& p, const Unit& U, int disc, int64_t dl, const float* A2,
+                                          float bias, float dskip, float* h, float* e, float& sum_delta, float* lds) {
+  if (disc == kPow)
+    run_rows<Tin, Tout, NS, SOFTPLUS, kPow, true, GATE>(p, U.row0, U.row1, dl, A2, bias, dskip, h, e, sum_delta, lds);
+  else if (disc == kExp)
+    run_rows<Tin, Tout, NS, SOFTPLUS, kExp, true, GATE>(p, U.row0, U.row1, dl, A2, bias, dskip, h, e, sum_delta, lds);
+  else
+    run_rows<Tin, Tout, NS, SOFTPLUS, kClamp, true, GATE>(p, U.row0, U.row1, dl, A2, bias, dskip, h, e, sum_delta,
+                                                          lds);
 }
 
 template <typename Tin, typename Tout, int NS, bool SOFTPLUS>
@@ -290,12 +335,7 @@ __global__ __launch_bounds__(kThreads) void selective_scan_kernel(SelParams p) {
   const bool active = d < p.D;
   const int64_t dl = active ? d : p.D - 1;  // lanes past D recompute channel D-1 exactly
   float A2[NS];
-  bool nonpos = true;
-#pragma unroll
-  for (int n = 0; n < NS; ++n) {
-    A2[n] = p.A[dl * NS + n] * kLog2e;
-    nonpos = nonpos && !(A2[n] > 0.0f);
-  }
+  const int disc = load_A<NS, SOFTPLUS>(p, dl, A2);
   const float bias = p.dt_bias ? p.dt_bias[dl] : 0.0f;
   const float dskip = p.Dskip ? p.Dskip[dl] : 0.0f;
 
@@ -310,22 +350,10 @@ __global__ __launch_bounds__(kThreads) void selective_scan_kernel(SelParams p) {
   }
   float sum_delta = 0.0f;
   __shared__ float lds[2 * BCStage<NS, true>::PER_BLOCK];
-  const bool noclamp = SOFTPLUS && __all(nonpos);
-  if (p.z) {
-    if (noclamp)
-      run_rows<Tin, Tout, NS, SOFTPLUS, false, true, true>(p, U.row0, U.row1, dl, A2, bias, dskip, h, e, sum_delta,
-                                                           lds);
-    else
-      run_rows<Tin, Tout, NS, SOFTPLUS, true, true, true>(p, U.row0, U.row1, dl, A2, bias, dskip, h, e, sum_delta,
-                                                          lds);
-  } else {
-    if (noclamp)
-      run_rows<Tin, Tout, NS, SOFTPLUS, false, true, false>(p, U.row0, U.row1, dl, A2, bias, dskip, h, e, sum_delta,
-                                                            lds);
-    else
-      run_rows<Tin, Tout, NS, SOFTPLUS, true, true, false>(p, U.row0, U.row1, dl, A2, bias, dskip, h, e, sum_delta,
-                                                           lds);
-  }
+  if (p.z)
+    scan_rows<Tin, Tout, NS, SOFTPLUS, true>(p, U, disc, dl, A2, bias, dskip, h, e, sum_delta, lds);
+  else
+    scan_rows<Tin, Tout, NS, SOFTPLUS, false>(p, U, disc, dl, A2, bias, dskip, h, e, sum_delta, lds);
 
   if (U.last && p.h_last && active) {
 #pragma unroll
@@ -356,7 +384,7 @@ __global__ __launch_bounds__(kThreads) void selective_carry_kernel(SelParams p) 
     count = r.y;
   }
   float h = p.h0 ? p.h0[(seq * p.D + d) * NS + n] : 0.0f;
-  constexpr int K = 8;
+  constexpr int K = 32;
   for (int64_t s0 = 0; s0 < count; s0 += K) {
     float P[K], H[K];
 #pragma unroll
@@ -520,9 +548,16 @@ struct Plan {
   int64_t T, nseg, U;
 };
 
+// Longest segment whose rows span under 2^31 bytes of any activation (buffer windows).
+int64_t max_segment(int64_t D) {
+  const int64_t m = (((int64_t)1 << 31) - 1) / (D * 4) / 16 * 16;
+  return m < 16 ? 16 : m;
+}
+
 Plan make_plan(const SelectiveScanArgs& a) {
   Plan pl;
   const int64_t kTargetWaves = device_cus() * kScanWavesPerCU;
+  const int64_t max_T = max_segment(a.D);
   const int64_t waves_per_row = (a.D + 63) / 64;
   if (a.cu_seqlens == nullptr) {
     const int64_t row_waves = a.B * waves_per_row;
@@ -531,6 +566,7 @@ Plan make_plan(const SelectiveScanArgs& a) {
     int64_t T = (a.L + want - 1) / want;
     T = ((T + 15) / 16) * 16;
     if (T < 16) T = 16;
+    if (T > max_T) T = max_T;
     if (T > a.L) T = a.L;
     pl.T = T;
     pl.nseg = (a.L + T - 1) / T;
@@ -541,6 +577,7 @@ Plan make_plan(const SelectiveScanArgs& a) {
     int64_t T = (a.L + want - 1) / want;
     T = ((T + 15) / 16) * 16;
     if (T < 16) T = 16;
+    if (T > max_T) T = max_T;
     pl.T = T;
     pl.nseg = 0;
     pl.U = (a.L + T - 1) / T + a.nseq;  // upper bound on sum of ceil(len / T)
