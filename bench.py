@@ -180,6 +180,20 @@ def forms(args, device):
         print(f"# {name}: {ms:.4f} ms  {d['state_updates_per_s']:.3e} upd/s  {d['hbm_gbs']:.0f} GB/s",
               file=sys.stderr, flush=True)
 
+    # --- headline shape with unstructured A (no integer-multiple rows): one exponential per state
+    B, L, D, N = 4, 2048, 1536, 16
+    x, z = randn((B, L, D)), randn((B, L, D))
+    A = -torch.exp(torch.empty(D, N, device=device).uniform_(np.log(0.5), np.log(64.0), generator=gen))
+    delta0 = torch.exp(torch.empty(D, device=device).uniform_(np.log(1e-3), np.log(1e-1), generator=gen))
+    delta = torch.exp(randn((B, L, D), std=0.1, dtype=torch.float32)) * delta0
+    dt = (delta + torch.log(-torch.expm1(-delta))).to(torch.bfloat16)
+    del delta
+    Bm, Cm = randn((B, L, N), std=1.0 / N), randn((B, L, N), std=1.0 / N)
+    Dskip = torch.ones(D, device=device)
+    ms = time_calls(lambda kk: ssd.selective_scan(x, dt, A, Bm, Cm, Dskip=Dskip, z=z), 1, 30, 3)[1]
+    record("selective_unstructured_A_B4_L2048_D1536_N16", ms, B * L * D * N, selective_bytes(B, L, D, N))
+    del x, z, dt, Bm, Cm
+
     # --- RG-LRU fp32, B=2 L=128 D=64 (latency bound)
     B, L, D = 2, 128, 64
     x, r, i = (randn((B, L, D), dtype=torch.float32) for _ in range(3))

@@ -91,28 +91,41 @@ __global__ __launch_bounds__(256) void hgrn2_update_kernel(int64_t rows, int64_t
 // ----------------------------------------------------------------------------- chunked MFMA form
 // For chunks of 64 tokens with Gamma[t][i] = prod_{u<=t} g[u][i] (within the chunk) the row-gated
 // recurrence unrolls to
-//   O      = Gamma (.) ( (Q K^T (.) M) (V (/) Gamma)  +  Q S0^T )          (M: causal, diagonal included)
-//   S_next = diag(Gamma_C) S0  +  ((Gamma_C (/) Gamma) (.) V)^T K
-// (rows of S and columns of O index the value dimension).  All products run on
-// v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  Q, K are bf16 inputs and enter exactly; every
-// derived operand (Q K^T, V / Gamma, the W factor, the state copy) is split into a bf16 pair
-// hi + lo, so its products carry about 16 significant bits instead of 8; the state S itself stays in
-// fp32 accumulators for the whole sequence.
-// V (/) Gamma needs Gamma >= lower_bound^64 to stay far from underflow: the launcher uses this form
-// only for lower_bound >= 2^-1.5 (Gamma >= 2^-96); smaller bounds take the recurrent kernel.
+//   S_next = diag(Gamma_C) S0 + W^T K,            W[s][i] = V[s][i] Gamma_C[i] / Gamma[s][i]
+//   O      = Gamma (.) ( (Q K^T (.) M) W / Gamma_C  +  Q S0^T )     (M: causal, diagonal included)
+// (rows of S and columns of O index the value dimension; W is bounded by |V| because Gamma
+// decreases along the chunk).  All products run on v_mfma_f32_16x16x32_bf16 with fp32
+// accumulation.  Q, K are bf16 inputs and enter exactly; every derived operand (Q K^T, W, the state
+// copy) is split into a bf16 pair hi + lo, so its products carry about 16 significant bits instead
+// of 8; the state S itself stays in fp32 accumulators for the whole sequence.
+// Gamma_C >= lower_bound^64 must stay far from underflow: the launcher uses this form only for
+// lower_bound >= 2^-1.5 (Gamma_C >= 2^-96); smaller bounds take the recurrent kernel.
 //
-// Workgroup = (batch, head, half of the 128 value rows); 4 waves, wave w owns value rows
-// [16w, 16w+16) of the half: 16 x 128 state entries = 8 accumulator tiles.  LDS rows are padded by
-// 16 bytes so the 16-row operand reads of an MFMA spread over all banks.  The next chunk's global
-// data is loaded into registers while the current chunk computes.
+// Workgroup = (batch, head, half of the 128 value rows), 8 waves.  Wave (r, h) (r = wave % 4,
+// h = wave / 4) owns value rows i in [16r, 16r+16) of the half, the state columns j of tiles
+// [4h, 4h+4), and the output token tiles {0, 3} (h = 0) or {1, 2} (h = 1), which balances the
+// causal work.  The state is held transposed, S^T[j][i], in accumulator tiles, and O is formed
+// transposed, O^T[i][t], so that:
+//   * Q K^T is computed as D[s][t] tiles whose lanes hold exactly the (t, s) entries the next
+//     product needs as its B operand (the contraction slots of a lane are s = 32k + 16h' + 4g + r,
+//     h', r = 0..3, for lane group g); W is read in the same slot order, so Q K^T stays in
+//     registers;
+//   * the state enters O^T += S Q^T straight from accumulators (same slot order over j); the two
+//     waves of a row tile swap their halves of the incoming state through LDS once per chunk;
+//   * operands contracted over the token index (W, and K for the state update) are read from
+//     row-major LDS with the gfx950 transposing LDS read (4 rows x 1 column per lane).
+// Q and K are double-buffered in LDS (16-byte segments XOR-swizzled by row); the gate step writes
+// Gamma and W row-major (consecutive lanes, consecutive columns).  Two barriers per chunk; the next
+// chunk's global data is loaded while the current one computes.
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4_t;
+typedef int v4i_t __attribute__((ext_vector_type(4)));
 
 constexpr int kCh = 64;    // chunk length (tokens)
 constexpr int kDh = 128;   // head dim
 constexpr int kRows = 64;  // value rows per workgroup
-constexpr int kPadD = kDh + 8;
-constexpr int kPadC = kCh + 8;
+constexpr int kGamStride = kRows + 4;  // padded fp32 rows of Gamma
 
 __device__ __forceinline__ floatx4_t mfma(const uint4& a, const uint4& b, floatx4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
@@ -123,94 +136,205 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) 
   hi = f32_to_bf16(x);
   lo = f32_to_bf16(x - bf16_to_f32(hi));
 }
+// two values -> packed bf16 pairs (element 0 in the low half)
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  uint16_t h0, l0, h1, l1;
+  split_bf16(x0, h0, l0);
+  split_bf16(x1, h1, l1);
+  hi = (uint32_t)h0 | ((uint32_t)h1 << 16);
+  lo = (uint32_t)l0 | ((uint32_t)l1 << 16);
+}
+
+// Q / K tile [64 rows][128 cols] bf16: 16-byte segment s of row r stored at segment s ^ f(r).
+__device__ __forceinline__ int qk_off(int row, int col) {
+  const int f = (row ^ (row >> 3)) & 7;
+  return row * kDh + ((((col >> 3) ^ f)) << 3) + (col & 7);
+}
+// V / Gamma and W tiles [64 tokens][64 rows] bf16: 4-element chunk c of row r stored at c ^ (r & 15).
+__device__ __forceinline__ int vw_off(int row, int col) {
+  return row * kRows + ((((col >> 2) ^ (row & 15))) << 2) + (col & 3);
+}
+
+constexpr int kWaves = 8;
+constexpr int kGateParts = kWaves;           // token groups of the gate step
+constexpr int kGateTok = kCh / kGateParts;   // tokens per gate thread
 
 struct H2Lds {
-  uint16_t q[kCh][kPadD];          // Q chunk [t][j]
-  uint16_t k[kCh][kPadD];          // K chunk [s][j]
-  uint16_t kt[kDh][kPadC];         // K transposed [j][t]
-  union {
-    struct {
-      uint16_t vraw[kCh][kRows];   // V chunk [t][i]          (read by the gate step)
-      uint16_t graw[kCh][kRows];   // gate logits [t][i]      (read by the gate step)
-    } in;
-    struct {
-      uint16_t a[kCh][kPadC];      // masked Q K^T [t][s], hi (written after the gate step)
-      uint16_t a_lo[kCh][kPadC];
-    } qk;
-  } u;
-  uint16_t vs[kRows][kPadC];       // V / Gamma, [i][t], hi and lo
-  uint16_t vs_lo[kRows][kPadC];
-  uint16_t w[kRows][kPadC];        // V * Gamma_C / Gamma, [i][t], hi and lo
-  uint16_t w_lo[kRows][kPadC];
-  uint16_t sb[kRows][kPadD];       // state S [i][j] entering the chunk, hi and lo
-  uint16_t sb_lo[kRows][kPadD];
-  float gam[kRows][kCh + 4];       // Gamma [i][t]
-  float gtot[4][kRows];            // per-quarter gate products
+  uint16_t q[2][kCh * kDh];
+  uint16_t k[2][kCh * kDh];
+  float gam[kCh][kGamStride];  // Gamma [t][i]
+  uint16_t w[kCh * kRows];     // W = V * Gamma_C / Gamma [s][i], hi and lo
+  uint16_t w_lo[kCh * kRows];
+  float gpart[kGateParts][kRows];  // gate products per token group
+  float gcol[kRows];               // Gamma_C per value row
+  uint4 sx[4][2][2][2][64];        // incoming state as bf16 pairs: [row tile][half][k-step][hi, lo][lane]
 };
+
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+// Transposing LDS read: in each 16-lane group, lane 4b + c passes the address of 4 consecutive
+// elements (row b of a 4-row block, column chunk c); lane j receives column j of the 4 rows.
+__device__ __forceinline__ uint2 lds_tr(const uint16_t* p) {
+  const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)((uintptr_t)p));
+  return __builtin_bit_cast(uint2, v);
+}
 
 struct H2Prefetch {
-  uint4 q[4], k[4], v[2], g[2];
+  v4i_t q[2], k[2];                    // 16-byte segments of Q and K
+  uint32_t g[kGateTok], v[kGateTok];   // gate logit and value of column i, kGateTok tokens
 };
 
-__device__ __forceinline__ void h2_fetch(const H2Params& p, int64_t b, int64_t hh, int64_t i0, int64_t t0, int tid,
+// Window over the rows [t0, t0 + valid) of head hh of batch b in a [B, L, H, 128] bf16 array:
+// row r at byte r * H * 256; rows at or past `valid` fall outside and read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t h2_window(const H2Params& p, const void* a, int64_t b, int64_t hh,
+                                                            int64_t t0, int valid) {
+  const char* base = static_cast<const char*>(a) + (((b * p.L + t0) * p.H + hh) * kDh) * 2;
+  return make_window(base, (uint32_t)((int64_t)(valid - 1) * p.H * kDh * 2 + kDh * 2));
+}
+
+__device__ __forceinline__ void h2_fetch(const H2Params& p, int64_t b, int64_t hh, int i0, int64_t t0, int tid,
                                          H2Prefetch& f) {
-  const uint16_t* Q = static_cast<const uint16_t*>(p.q);
-  const uint16_t* K = static_cast<const uint16_t*>(p.k);
-  const uint16_t* V = static_cast<const uint16_t*>(p.v);
-  const uint16_t* G = static_cast<const uint16_t*>(p.g);
   const int valid = (int)min((int64_t)kCh, p.L - t0);
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int idx = it * 256 + tid;  // 1024 segments of 8 elements: row t, segment seg
-    const int t = idx >> 4, seg = idx & 15;
-    f.q[it] = f.k[it] = make_uint4(0, 0, 0, 0);
-    if (t < valid) {
-      const int64_t off = ((b * p.L + t0 + t) * p.H + hh) * kDh + seg * 8;
-      f.q[it] = *reinterpret_cast<const uint4*>(Q + off);
-      f.k[it] = *reinterpret_cast<const uint4*>(K + off);
-    }
-  }
+  const uint32_t row_bytes = (uint32_t)(p.H * kDh * 2);
+  const auto wq = h2_window(p, p.q, b, hh, t0, valid), wk = h2_window(p, p.k, b, hh, t0, valid);
+  const auto wv = h2_window(p, p.v, b, hh, t0, valid), wg = h2_window(p, p.g, b, hh, t0, valid);
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
-    const int idx = it * 256 + tid;  // 512 segments of 8 elements
-    const int t = idx >> 3, seg = idx & 7;
-    f.v[it] = f.g[it] = make_uint4(0, 0, 0, 0);
-    if (t < valid) {
-      const int64_t off = ((b * p.L + t0 + t) * p.H + hh) * kDh + i0 + seg * 8;
-      f.v[it] = *reinterpret_cast<const uint4*>(V + off);
-      f.g[it] = *reinterpret_cast<const uint4*>(G + off);
+    const int idx = it * 512 + tid;  // 1024 segments of 8 elements: row t, segment seg
+    const int t = idx >> 4, seg = idx & 15;
+    const uint32_t off = (uint32_t)t * row_bytes + (uint32_t)seg * 16;
+    f.q[it] = __builtin_amdgcn_raw_buffer_load_b128(wq, (int)off, 0, 0);
+    f.k[it] = __builtin_amdgcn_raw_buffer_load_b128(wk, (int)off, 0, 0);
+  }
+  const int i = tid & 63, part = tid >> 6;
+  const uint32_t lane_off = (uint32_t)(i0 + i) * 2;
+#pragma unroll
+  for (int u = 0; u < kGateTok; ++u) {
+    const uint32_t ro = (uint32_t)(part * kGateTok + u) * row_bytes;
+    f.g[u] = __builtin_amdgcn_raw_buffer_load_b16(wg, (int)lane_off, (int)ro, 0);
+    f.v[u] = __builtin_amdgcn_raw_buffer_load_b16(wv, (int)lane_off, (int)ro, 0);
+  }
+}
+
+// Token tiles of the output handled by half h of a row tile: {0, 3} or {1, 2}.
+template <int H> struct Tiles {
+  static constexpr int t0 = H ? 1 : 0, t1 = H ? 2 : 3;
+  static constexpr int n0 = t0 + 1, n1 = t1 + 1;  // key tiles st <= tt
+  static constexpr int n = n0 + n1;               // 5 for both halves
+  static constexpr int tt(int a) { return a ? t1 : t0; }
+  static constexpr int base(int a) { return a ? n0 : 0; }
+};
+
+// Q K^T tiles D[s][t] for this half's token tiles, causal mask, as bf16 hi / lo pairs.
+template <int H>
+__device__ __forceinline__ void h2_qk(const uint16_t* Qs, const uint16_t* Ks, int l16, int lg, uint32_t (&a_hi)[5][2],
+                                      uint32_t (&a_lo)[5][2]) {
+  using TL = Tiles<H>;
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    constexpr int dummy = 0;
+    (void)dummy;
+    const int tt = TL::tt(a);
+    floatx4_t acc[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) acc[st] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint4 qb = *reinterpret_cast<const uint4*>(&Qs[qk_off(16 * tt + l16, 32 * ks + 8 * lg)]);
+#pragma unroll
+      for (int st = 0; st < 4; ++st)  // independent accumulation chains, one per key tile
+        if (st <= tt)
+          acc[st] = mfma(*reinterpret_cast<const uint4*>(&Ks[qk_off(16 * st + l16, 32 * ks + 8 * lg)]), qb, acc[st]);
+    }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      if (st <= tt) {
+        if (st == tt) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (4 * lg + r > l16) acc[st][r] = 0.0f;  // s > t
+        }
+        const int ti = TL::base(a) + st;
+        split2(acc[st][0], acc[st][1], a_hi[ti][0], a_lo[ti][0]);
+        split2(acc[st][2], acc[st][3], a_hi[ti][1], a_lo[ti][1]);
+      }
     }
   }
 }
 
-__device__ __forceinline__ void h2_stage(H2Lds& sm, int tid, const H2Prefetch& f) {
+// O^T tiles of this half (rows i = iw + 4 lg + r, columns t = 16 tt + l16):
+//   O = Gamma (.) ( (A W) / Gamma_C + Q S^T )
+template <int H, typename Tout>
+__device__ __forceinline__ void h2_out(const H2Params& p, H2Lds& sm, const uint16_t* Qs, int iw, int l16, int lg,
+                                       const uint32_t (&a_hi)[5][2], const uint32_t (&a_lo)[5][2],
+                                       const uint4 (&s_hi)[4], const uint4 (&s_lo)[4], int64_t obase_row,
+                                       int64_t row_stride, int valid) {
+  using TL = Tiles<H>;
+  // W as A operands: slots s = 32 ks + 16 h' + 4 lg + r; lane 4b + c of a group points at
+  // row 32 ks + 16 h' + 4 lg + b, columns iw + 4c .. +3
+  uint4 w_hi[2], w_lo[2];
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int idx = it * 256 + tid;
-    const int t = idx >> 4, seg = idx & 15;
-    *reinterpret_cast<uint4*>(&sm.q[t][seg * 8]) = f.q[it];
-    *reinterpret_cast<uint4*>(&sm.k[t][seg * 8]) = f.k[it];
-    const uint16_t* ke = reinterpret_cast<const uint16_t*>(&f.k[it]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sm.kt[seg * 8 + e][t] = ke[e];
+  for (int ks = 0; ks < 2; ++ks) {
+    const int rb = 32 * ks + 4 * lg + (l16 >> 2), cb = iw + 4 * (l16 & 3);
+    const uint2 h0 = lds_tr(&sm.w[vw_off(rb, cb)]), h1 = lds_tr(&sm.w[vw_off(rb + 16, cb)]);
+    const uint2 l0 = lds_tr(&sm.w_lo[vw_off(rb, cb)]), l1 = lds_tr(&sm.w_lo[vw_off(rb + 16, cb)]);
+    w_hi[ks] = make_uint4(h0.x, h0.y, h1.x, h1.y);
+    w_lo[ks] = make_uint4(l0.x, l0.y, l1.x, l1.y);
   }
+  floatx4_t oa[2], os[2];
 #pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int idx = it * 256 + tid;
-    const int t = idx >> 3, seg = idx & 7;
-    *reinterpret_cast<uint4*>(&sm.u.in.vraw[t][seg * 8]) = f.v[it];
-    *reinterpret_cast<uint4*>(&sm.u.in.graw[t][seg * 8]) = f.g[it];
+  for (int a = 0; a < 2; ++a) oa[a] = os[a] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const int trow = 16 * TL::tt(a) + l16;
+      const uint2 q0 = *reinterpret_cast<const uint2*>(&Qs[qk_off(trow, 32 * ks + 4 * lg)]);
+      const uint2 q1 = *reinterpret_cast<const uint2*>(&Qs[qk_off(trow, 32 * ks + 16 + 4 * lg)]);
+      const uint4 qbv = make_uint4(q0.x, q0.y, q1.x, q1.y);
+      os[a] = mfma(s_hi[ks], qbv, os[a]);
+      os[a] = mfma(s_lo[ks], qbv, os[a]);
+    }
+    if (ks < 2) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const int tt = TL::tt(a);
+        if (2 * ks <= tt) {  // key tiles 2 ks, 2 ks + 1; tiles past tt are masked entirely
+          const int t0i = TL::base(a) + 2 * ks;
+          const bool second = 2 * ks + 1 <= tt;
+          uint4 ah, al;
+          ah.x = a_hi[t0i][0]; ah.y = a_hi[t0i][1];
+          al.x = a_lo[t0i][0]; al.y = a_lo[t0i][1];
+          ah.z = second ? a_hi[t0i + 1][0] : 0u; ah.w = second ? a_hi[t0i + 1][1] : 0u;
+          al.z = second ? a_lo[t0i + 1][0] : 0u; al.w = second ? a_lo[t0i + 1][1] : 0u;
+          oa[a] = mfma(w_hi[ks], ah, oa[a]);
+          oa[a] = mfma(w_lo[ks], ah, oa[a]);
+          oa[a] = mfma(w_hi[ks], al, oa[a]);
+        }
+      }
+    }
+  }
+  float igc[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) igc[r] = hw_rcp(sm.gcol[iw + 4 * lg + r]);
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int t = 16 * TL::tt(a) + l16;
+    const float4 gm = *reinterpret_cast<const float4*>(&sm.gam[t][iw + 4 * lg]);
+    if (t < valid) {
+      const int64_t ob = (obase_row + t) * row_stride + iw + 4 * lg;
+      io2<Tout>::store(p.o, ob, gm.x * fmaf(oa[a][0], igc[0], os[a][0]), gm.y * fmaf(oa[a][1], igc[1], os[a][1]));
+      io2<Tout>::store(p.o, ob + 2, gm.z * fmaf(oa[a][2], igc[2], os[a][2]),
+                       gm.w * fmaf(oa[a][3], igc[3], os[a][3]));
+    }
   }
 }
 
 template <typename Tout>
-__global__ __launch_bounds__(256) void hgrn2_chunk_kernel(H2Params p) {
+__global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
   __shared__ H2Lds sm;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int l16 = lane & 15;
-  const int lg = lane >> 4;  // 0..3
+  const int rt = wave & 3, half_t = wave >> 2;  // row tile, token / state half
   // both halves of a head on the same XCD (blockIdx % 8) so their Q / K reads share an L2
   int64_t bh, half;
   if ((p.B * p.H) % 8 == 0) {
@@ -222,160 +346,153 @@ __global__ __launch_bounds__(256) void hgrn2_chunk_kernel(H2Params p) {
     half = blockIdx.x % 2;
   }
   const int64_t b = bh / p.H, hh = bh - b * p.H;
-  const int64_t i0 = half * kRows;  // first value row of this workgroup
+  const int i0 = (int)half * kRows;  // first value row of this workgroup
+  const int iw = 16 * rt;            // first row of this wave within the half
   const float lb = p.lb, one_m_lb = 1.0f - p.lb;
 
-  // ---- state accumulators: rows r0 + 4*lg + e (e = 0..3) of the half, columns 16*nt + l16
-  const int r0 = wave * 16;
-  floatx4_t S[8];
+  // ---- S^T accumulators: tile q holds S^T[j = 16 (4 half_t + q) + 4 lg + r][i = iw + l16]
+  floatx4_t S[4];
+  {
+    const int l16 = tid & 15, lg = (tid >> 4) & 3;
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt)
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      S[nt][e] = p.S0 ? p.S0[(bh * kDh + i0 + r0 + 4 * lg + e) * kDh + 16 * nt + l16] : 0.0f;
+      for (int r = 0; r < 4; ++r)
+        S[q][r] = p.S0 ? p.S0[(bh * kDh + i0 + iw + l16) * kDh + 16 * (4 * half_t + q) + 4 * lg + r] : 0.0f;
+  }
 
   const int64_t nchunks = (p.L + kCh - 1) / kCh;
   H2Prefetch f;
   h2_fetch(p, b, hh, i0, 0, tid, f);
   for (int64_t c = 0; c < nchunks; ++c) {
+    // Lane indices re-derived per chunk from an opaque copy: keeps the compiler from hoisting the
+    // many per-lane LDS addresses out of the loop into registers.
+    int tidv = tid;
+    asm volatile("" : "+v"(tidv));
+    const int lane = tidv & 63;
+    const int l16 = lane & 15, lg = lane >> 4;
     const int64_t t0 = c * kCh;
     const int valid = (int)min((int64_t)kCh, p.L - t0);
-    h2_stage(sm, tid, f);
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        uint16_t hi, lo;
-        split_bf16(S[nt][e], hi, lo);
-        sm.sb[r0 + 4 * lg + e][16 * nt + l16] = hi;
-        sm.sb_lo[r0 + 4 * lg + e][16 * nt + l16] = lo;
-      }
-    __syncthreads();
-    if (c + 1 < nchunks) h2_fetch(p, b, hh, i0, t0 + kCh, tid, f);  // in flight during this chunk
+    const int buf = (int)(c & 1);
+    uint16_t* Qs = sm.q[buf];
+    uint16_t* Ks = sm.k[buf];
 
-    // ---- gates and their cumulative products: thread (row i, quarter q of the chunk)
+    // ---- stage Q, K (swizzled segments)
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int idx = it * 512 + tidv;
+      const int t = idx >> 4, seg = idx & 15;
+      *reinterpret_cast<v4i_t*>(&Qs[qk_off(t, seg * 8)]) = f.q[it];
+      *reinterpret_cast<v4i_t*>(&Ks[qk_off(t, seg * 8)]) = f.k[it];
+    }
+    // ---- incoming state as bf16 pairs in A-operand slot order (j = 32 ks + 16 h' + 4 lg + r);
+    //      this wave's half of the k-steps goes to LDS for its partner
+    uint4 my_hi[2], my_lo[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      split2(S[2 * kk][0], S[2 * kk][1], my_hi[kk].x, my_lo[kk].x);
+      split2(S[2 * kk][2], S[2 * kk][3], my_hi[kk].y, my_lo[kk].y);
+      split2(S[2 * kk + 1][0], S[2 * kk + 1][1], my_hi[kk].z, my_lo[kk].z);
+      split2(S[2 * kk + 1][2], S[2 * kk + 1][3], my_hi[kk].w, my_lo[kk].w);
+      sm.sx[rt][half_t][kk][0][lane] = my_hi[kk];
+      sm.sx[rt][half_t][kk][1][lane] = my_lo[kk];
+    }
+    // ---- gates, part 1: thread (column i, token group gp), running products over its tokens
+    const int gi = tidv & 63, gp = tidv >> 6;
+    float gam_run[kGateTok], vv[kGateTok];
     {
-      const int i = tid & 63, q = tid >> 6;
-      float gl[16], vv[16];
       float run = 1.0f;
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int t = q * 16 + u;
-        const float g = (t < valid) ? fmaf(one_m_lb, sigmoid_f(bf16_to_f32(sm.u.in.graw[t][i])), lb) : 1.0f;
-        run *= g;
-        gl[u] = run;
-        vv[u] = bf16_to_f32(sm.u.in.vraw[t][i]);
+      for (int u = 0; u < kGateTok; ++u) {
+        const int t = gp * kGateTok + u;
+        const float gv = (t < valid) ? fmaf(one_m_lb, sigmoid_f(bf16_to_f32((uint16_t)f.g[u])), lb) : 1.0f;
+        run *= gv;
+        gam_run[u] = run;
+        vv[u] = bf16_to_f32((uint16_t)f.v[u]);
       }
-      sm.gtot[q][i] = run;
-      __syncthreads();  // quarter products visible; vraw / graw fully read
+      sm.gpart[gp][gi] = run;
+    }
+    if (c + 1 < nchunks) h2_fetch(p, b, hh, i0, t0 + kCh, tid, f);  // in flight during this chunk
+    __syncthreads();  // Q, K, group products, state halves visible
+
+    // ---- gates, part 2: Gamma and W = V Gamma_C / Gamma (row-major, one column per lane)
+    {
       float pre = 1.0f, all = 1.0f;
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        if (qq < q) pre *= sm.gtot[qq][i];
-        all *= sm.gtot[qq][i];
+      for (int q2 = 0; q2 < kGateParts; ++q2) {
+        const float tq = sm.gpart[q2][gi];
+        if (q2 < gp) pre *= tq;
+        all *= tq;
       }
+      if (gp == 0) sm.gcol[gi] = all;
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int t = q * 16 + u;
-        const float gam = pre * gl[u];
-        const float inv = hw_rcp(gam);
-        sm.gam[i][t] = gam;
-        split_bf16(vv[u] * inv, sm.vs[i][t], sm.vs_lo[i][t]);
-        split_bf16(vv[u] * (all * inv), sm.w[i][t], sm.w_lo[i][t]);
+      for (int u = 0; u < kGateTok; ++u) {
+        const int t = gp * kGateTok + u;
+        const float gam = pre * gam_run[u];
+        sm.gam[t][gi] = gam;
+        const int o = vw_off(t, gi);
+        split_bf16(vv[u] * (all * hw_rcp(gam)), sm.w[o], sm.w_lo[o]);
       }
     }
-
-    // ---- A = Q K^T (rows t in [16*wave, +16)), causal mask, bf16 hi / lo into LDS
-    {
-      floatx4_t acc[4];
+    // ---- partner's half of the incoming state; k-steps in order (half 0 holds j < 64)
+    uint4 s_hi[4], s_lo[4];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const uint4 a = *reinterpret_cast<const uint4*>(&sm.q[16 * wave + l16][32 * ks + 8 * lg]);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const uint4 bb = *reinterpret_cast<const uint4*>(&sm.k[16 * nt + l16][32 * ks + 8 * lg]);
-          acc[nt] = mfma(a, bb, acc[nt]);
-        }
-      }
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * wave + 4 * lg + e, sidx = 16 * nt + l16;
-          split_bf16(sidx <= t ? acc[nt][e] : 0.0f, sm.u.qk.a[t][sidx], sm.u.qk.a_lo[t][sidx]);
-        }
+    for (int kk = 0; kk < 2; ++kk) {
+      const uint4 oh = sm.sx[rt][1 - half_t][kk][0][lane], ol = sm.sx[rt][1 - half_t][kk][1][lane];
+      s_hi[kk] = half_t ? oh : my_hi[kk];
+      s_lo[kk] = half_t ? ol : my_lo[kk];
+      s_hi[2 + kk] = half_t ? my_hi[kk] : oh;
+      s_lo[2 + kk] = half_t ? my_lo[kk] : ol;
     }
-    __syncthreads();
+    // ---- Q K^T for this half's token tiles
+    uint32_t a_hi[5][2], a_lo[5][2];
+    if (half_t == 0) h2_qk<0>(Qs, Ks, l16, lg, a_hi, a_lo);
+    else h2_qk<1>(Qs, Ks, l16, lg, a_hi, a_lo);
+    __syncthreads();  // Gamma, W, Gamma_C visible
 
-    // ---- O for this wave's 16 value rows, all 64 tokens: Gamma (.) (A Vs + Q S^T)
+    // ---- O^T for this half's token tiles
+    const int64_t obase_row = b * p.L + t0;
+    const int64_t row_stride = p.H * kDh;
     {
-      float gc[4];
+      H2Params pp = p;
+      pp.o = static_cast<char*>(p.o) + (hh * kDh + i0) * (int64_t)sizeof(Tout);
+      if (half_t == 0) h2_out<0, Tout>(pp, sm, Qs, iw, l16, lg, a_hi, a_lo, s_hi, s_lo, obase_row, row_stride, valid);
+      else h2_out<1, Tout>(pp, sm, Qs, iw, l16, lg, a_hi, a_lo, s_hi, s_lo, obase_row, row_stride, valid);
+    }
+
+    // ---- state update on this wave's tiles: S^T = S^T Gamma_C[i] + K^T W  (slots s = 32 ks + 8 lg + e)
+    {
+      const float gc = sm.gcol[iw + l16];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = r0 + 4 * lg + e;
-        gc[e] = sm.gtot[0][row] * sm.gtot[1][row] * sm.gtot[2][row] * sm.gtot[3][row];
-      }
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        floatx4_t acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          if (32 * ks <= 16 * mt + 15) {  // key blocks past the query block are fully masked
-            const uint4 ah = *reinterpret_cast<const uint4*>(&sm.u.qk.a[16 * mt + l16][32 * ks + 8 * lg]);
-            const uint4 al = *reinterpret_cast<const uint4*>(&sm.u.qk.a_lo[16 * mt + l16][32 * ks + 8 * lg]);
-            const uint4 vh = *reinterpret_cast<const uint4*>(&sm.vs[r0 + l16][32 * ks + 8 * lg]);
-            const uint4 vl = *reinterpret_cast<const uint4*>(&sm.vs_lo[r0 + l16][32 * ks + 8 * lg]);
-            acc = mfma(ah, vh, acc);
-            acc = mfma(al, vh, acc);
-            acc = mfma(ah, vl, acc);
-          }
-        }
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const uint4 a = *reinterpret_cast<const uint4*>(&sm.q[16 * mt + l16][32 * ks + 8 * lg]);
-          const uint4 sh = *reinterpret_cast<const uint4*>(&sm.sb[r0 + l16][32 * ks + 8 * lg]);
-          const uint4 sl = *reinterpret_cast<const uint4*>(&sm.sb_lo[r0 + l16][32 * ks + 8 * lg]);
-          acc = mfma(a, sh, acc);
-          acc = mfma(a, sl, acc);
-        }
-        // acc[e] = O[t = 16 mt + 4 lg + e][i = r0 + l16]
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * mt + 4 * lg + e;
-          if (t < valid) {
-            const float o = acc[e] * sm.gam[r0 + l16][t];
-            io<Tout>::store(p.o, ((b * p.L + t0 + t) * p.H + hh) * kDh + i0 + r0 + l16, o);
-          }
-        }
-      }
-      // ---- state update: S = diag(Gamma_C) S + W^T K  (rows r0 + 4 lg + e, columns 16 nt + l16)
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) S[nt][e] *= gc[e];
+        for (int r = 0; r < 4; ++r) S[q][r] *= gc;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const uint4 wh = *reinterpret_cast<const uint4*>(&sm.w[r0 + l16][32 * ks + 8 * lg]);
-        const uint4 wl = *reinterpret_cast<const uint4*>(&sm.w_lo[r0 + l16][32 * ks + 8 * lg]);
+        const int rb = 32 * ks + 8 * lg + (l16 >> 2);
+        const int cw = iw + 4 * (l16 & 3);
+        const uint2 w0 = lds_tr(&sm.w[vw_off(rb, cw)]), w1 = lds_tr(&sm.w[vw_off(rb + 4, cw)]);
+        const uint2 x0 = lds_tr(&sm.w_lo[vw_off(rb, cw)]), x1 = lds_tr(&sm.w_lo[vw_off(rb + 4, cw)]);
+        const uint4 wh = make_uint4(w0.x, w0.y, w1.x, w1.y), wl = make_uint4(x0.x, x0.y, x1.x, x1.y);
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-          const uint4 bb = *reinterpret_cast<const uint4*>(&sm.kt[16 * nt + l16][32 * ks + 8 * lg]);
-          S[nt] = mfma(wh, bb, S[nt]);
-          S[nt] = mfma(wl, bb, S[nt]);
+        for (int q = 0; q < 4; ++q) {
+          const int ck = 16 * (4 * half_t + q) + 4 * (l16 & 3);
+          const uint2 k0 = lds_tr(&Ks[qk_off(rb, ck)]), k1 = lds_tr(&Ks[qk_off(rb + 4, ck)]);
+          const uint4 kt = make_uint4(k0.x, k0.y, k1.x, k1.y);
+          S[q] = mfma(kt, wh, S[q]);
+          S[q] = mfma(kt, wl, S[q]);
         }
       }
     }
-    __syncthreads();  // LDS is rewritten by the next chunk
   }
 
   if (p.S_last) {
+    const int l16 = tid & 15, lg = (tid >> 4) & 3;
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        p.S_last[(bh * kDh + i0 + r0 + 4 * lg + e) * kDh + 16 * nt + l16] = S[nt][e];
+      for (int r = 0; r < 4; ++r)
+        p.S_last[(bh * kDh + i0 + iw + l16) * kDh + 16 * (4 * half_t + q) + 4 * lg + r] = S[q][r];
   }
 }
 
@@ -398,13 +515,14 @@ hipError_t launch_hgrn2_scan(const Hgrn2ScanArgs& a, hipStream_t s) {
   p.B = a.B; p.L = a.L; p.H = a.H; p.d = a.d;
   p.q = a.q; p.k = a.k; p.v = a.v; p.g = a.g_logit; p.lb = a.lower_bound;
   p.S0 = a.S0; p.o = a.o; p.S_last = a.S_last;
-  // chunked MFMA form: bf16 inputs, d = 128, lower_bound >= 2^-1.5 (see hgrn2_chunk_kernel)
-  if (a.in_bf16 && a.d == kDh && a.lower_bound >= 0.35355339f) {
+  // chunked MFMA form: bf16 inputs, d = 128, lower_bound >= 2^-1.5 (see hgrn2_chunk_kernel); a
+  // chunk's rows of one head span under 2^31 bytes (buffer windows) for H < 2^16
+  if (a.in_bf16 && a.d == kDh && a.lower_bound >= 0.35355339f && a.H < 65536) {
     const dim3 grid((unsigned)(a.B * a.H * 2));
     if (a.out_bf16)
-      hipLaunchKernelGGL((hgrn2_chunk_kernel<bf16_t>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((hgrn2_chunk_kernel<bf16_t>), grid, dim3(kWaves * 64), 0, s, p);
     else
-      hipLaunchKernelGGL((hgrn2_chunk_kernel<float>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((hgrn2_chunk_kernel<float>), grid, dim3(kWaves * 64), 0, s, p);
     return hipGetLastError();
   }
   if (!a.in_bf16) return launch_recurrent_t<float, float>(p, s);
