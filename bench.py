@@ -30,7 +30,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
-FP32_VECTOR_TFLOPS = 157.3   # MI355X fp32 vector, published
+FP32_VECTOR_TFLOPS = 157.3   # MI355X fp32 vector, published (counts packed two-wide FMA)
+# fp32 vector peak without packed instructions, which this library does not use: 256 CUs x 4 SIMDs x
+# 16 lanes x 2 flops per FMA x 2.4 GHz
+FP32_SCALAR_FMA_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 BF16_MFMA_TFLOPS = 2500.0    # MI355X dense bf16 matrix, published
 
 
@@ -78,25 +81,22 @@ def profiled_traffic(profile, sources):
 
 # ----------------------------------------------------------------------------- timing helpers
 def time_calls(fn, n_sets, steps, warmup):
-    """Run ``fn(i % n_sets)`` warmup times, then time ``steps`` calls with one event pair per call
-    on torch's current stream (the stream the library launches on).  Returns (ms_per_step,
-    mean per-call event ms, min per-call event ms)."""
+    """Run ``fn(i % n_sets)`` warmup times, then time ``steps`` back-to-back calls between one pair of
+    HIP events on torch's current stream (the stream the library launches on), synchronizing before
+    and after.  Returns (ms per step from the events, ms per step from the host clock)."""
     import torch
     for i in range(warmup):
         fn(i % n_sets)
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    start.record()
     for i in range(steps):
-        starts[i].record()
         fn(i % n_sets)
-        ends[i].record()
+    end.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3
-    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    total = starts[0].elapsed_time(ends[-1])
-    return total / steps, float(np.mean(per)), float(np.min(per)), wall / steps
+    return start.elapsed_time(end) / steps, wall / steps
 
 
 def dev_bf16(bits, device):
@@ -129,11 +129,10 @@ def headline(args, device):
         return ssd.selective_scan(t["x"], t["dt"], s["A"], t["Bm"], t["Cm"], Dskip=s["Dskip"], z=t["z"],
                                   dt_softplus=True)
 
-    ms, mean_call, min_call, wall = time_calls(step, n_sets, args.steps, args.warmup)
+    ms, wall = time_calls(step, n_sets, args.steps, args.warmup)
     updates = B * L * D * N
     nbytes = selective_bytes(B, L, D, N)
-    res = dict(ms=ms, mean_call_ms=mean_call, min_call_ms=min_call, updates=updates, bytes=nbytes,
-               host_ms=wall)
+    res = dict(ms=ms, updates=updates, bytes=nbytes, host_ms=wall)
     return res, host_inputs
 
 
@@ -190,7 +189,7 @@ def forms(args, device):
     del delta
     Bm, Cm = randn((B, L, N), std=1.0 / N), randn((B, L, N), std=1.0 / N)
     Dskip = torch.ones(D, device=device)
-    ms = time_calls(lambda kk: ssd.selective_scan(x, dt, A, Bm, Cm, Dskip=Dskip, z=z), 1, 30, 3)[1]
+    ms = time_calls(lambda kk: ssd.selective_scan(x, dt, A, Bm, Cm, Dskip=Dskip, z=z), 1, 30, 3)[0]
     record("selective_unstructured_A_B4_L2048_D1536_N16", ms, B * L * D * N, selective_bytes(B, L, D, N))
     del x, z, dt, Bm, Cm
 
@@ -198,14 +197,14 @@ def forms(args, device):
     B, L, D = 2, 128, 64
     x, r, i = (randn((B, L, D), dtype=torch.float32) for _ in range(3))
     a_log = torch.log(torch.empty(D, device=device).uniform_(0.9, 0.999, generator=gen))
-    ms = time_calls(lambda k: ssd.rglru_scan(x, r, i, a_log, 8.0), 1, 50, 5)[1]
+    ms = time_calls(lambda k: ssd.rglru_scan(x, r, i, a_log, 8.0), 1, 50, 5)[0]
     record("rglru_fp32_B2_L128_D64", ms, B * L * D, rglru_bytes(B, L, D, 4, 4))
 
     # --- RG-LRU bf16, B=8 L=8192 D=2560
     B, L, D = 8, 8192, 2560
     x, r, i = (randn((B, L, D)) for _ in range(3))
     a_log = torch.log(torch.empty(D, device=device).uniform_(0.9, 0.999, generator=gen))
-    ms = time_calls(lambda k: ssd.rglru_scan(x, r, i, a_log, 8.0), 1, 10, 2)[1]
+    ms = time_calls(lambda k: ssd.rglru_scan(x, r, i, a_log, 8.0), 1, 10, 2)[0]
     record("rglru_bf16_B8_L8192_D2560", ms, B * L * D, rglru_bytes(B, L, D))
     del x, r, i
 
@@ -218,17 +217,33 @@ def forms(args, device):
         for s in range(S):
             ssd.rglru_update(xs[s], rs[s], is_[s], a_log, 8.0, state)
 
-    ms = time_calls(decode, 1, 3, 1)[1]
+    ms = time_calls(decode, 1, 3, 1)[0]
     per_step_bytes = B * D * (3 * 2 + 4 + 4 + 4)
     record("rglru_decode_B256_D2560_256steps", ms, B * D * S, per_step_bytes * S,
            dict(us_per_step=ms * 1e3 / S))
-    del xs, rs, is_
+
+    # --- the same 256 decode steps captured once in a HIP graph and replayed (identical kernels)
+    state_g = torch.zeros(B, D, device=device)
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        decode_g = lambda: [ssd.rglru_update(xs[s], rs[s], is_[s], a_log, 8.0, state_g) for s in range(S)]
+        decode_g()  # warm up on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            decode_g()
+    torch.cuda.synchronize()
+    ms = time_calls(lambda k: graph.replay(), 1, 5, 1)[0]
+    record("rglru_decode_B256_D2560_256steps_hipgraph", ms, B * D * S, per_step_bytes * S,
+           dict(us_per_step=ms * 1e3 / S))
+    del xs, rs, is_, graph
 
     # --- HGRN2 bf16, B=8 H=16 d=128 L=4096, lower bound 0.5
     B, L, H, dd = 8, 4096, 16, 128
     q, k, v = (randn((B, L, H, dd), std=dd ** -0.5) for _ in range(3))
     g = randn((B, L, H, dd), mean=2.0)
-    ms = time_calls(lambda kk: ssd.hgrn2_scan(q, k, v, g, 0.5), 1, 3, 1)[1]
+    ms = time_calls(lambda kk: ssd.hgrn2_scan(q, k, v, g, 0.5), 1, 5, 1)[0]
     flops = 2 * B * L * H * (2 * 64 * dd + 2 * dd * dd)  # chunked form at chunk 64
     record("hgrn2_bf16_B8_H16_d128_L4096", ms, B * L * H * dd * dd, hgrn2_bytes(B, L, H, dd),
            dict(mfma_equiv_tflops=flops / (ms * 1e-3) / 1e12,
@@ -248,7 +263,7 @@ def forms(args, device):
     Bm, Cm = randn((1, Lt, N), std=1.0 / N), randn((1, Lt, N), std=1.0 / N)
     Dskip = torch.ones(D, device=device)
     ms = time_calls(lambda kk: ssd.selective_scan(x, dt, A, Bm, Cm, Dskip=Dskip, z=z, cu_seqlens=cu,
-                                                  check_cu_seqlens=False), 1, 5, 1)[1]
+                                                  check_cu_seqlens=False), 1, 5, 1)[0]
     record("selective_varlen_L131072_D4096_N16_32seq", ms, Lt * D * N, selective_bytes(1, Lt, D, N, nseq=ns))
     return out
 
@@ -256,8 +271,8 @@ def forms(args, device):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-forms", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -288,10 +303,10 @@ def main():
     head, host_inputs = headline(args, device)
     ms = head["ms"]
     value = head["updates"] / (ms * 1e-3)
-    call_s = head["mean_call_ms"] * 1e-3
+    call_s = ms * 1e-3
     achieved_tflops = head["updates"] * SELECTIVE_FLOPS_PER_UPDATE / call_s / 1e12
     hbm_gbs = head["bytes"] / call_s / 1e9
-    print(f"# headline: {ms:.4f} ms/step, mean call {head['mean_call_ms']:.4f} ms, {value:.3e} upd/s, "
+    print(f"# headline: {ms:.4f} ms/step (host clock {head['host_ms']:.4f}), {value:.3e} upd/s, "
           f"{hbm_gbs:.0f} GB/s", file=sys.stderr, flush=True)
 
     line = {
@@ -312,14 +327,16 @@ def main():
                    "B": 4, "L": 2048, "D": 1536, "N": 16, "input_dtype": "bf16", "output_dtype": "f32"},
         "hbm": {"achieved_gbs": hbm_gbs, "peak_gbs": HBM_PEAK_GBS, "frac": hbm_gbs / HBM_PEAK_GBS,
                 "algorithmic_bytes": head["bytes"]},
-        "roofline": {"bound": "alu", "achieved": achieved_tflops, "peak": FP32_VECTOR_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved_tflops / FP32_VECTOR_TFLOPS,
+        "roofline": {"bound": "alu", "achieved": achieved_tflops, "peak": FP32_SCALAR_FMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved_tflops / FP32_SCALAR_FMA_TFLOPS,
+                     "peak_basis": "fp32 FMA without packed instructions: 256 CU x 64 lanes x 2 flop x 2.4 GHz; "
+                                   "published 157.3 counts packed FMA",
+                     "published_peak": FP32_VECTOR_TFLOPS,
                      "traffic": profiled_traffic("selective_scan_B4_L2048_D1536_N16.md",
                                                  ["selective_state_space_diag_amd/csrc/selective.hip",
                                                   "selective_state_space_diag_amd/csrc/common.hpp"]),
                      "kernel": "selective scan call: aggregate + carry + scan kernels",
-                     "flops_per_update": SELECTIVE_FLOPS_PER_UPDATE,
-                     "mean_call_ms": head["mean_call_ms"], "min_call_ms": head["min_call_ms"]},
+                     "flops_per_update": SELECTIVE_FLOPS_PER_UPDATE, "ms_per_call": ms},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(host_inputs)

@@ -130,12 +130,9 @@ struct BCStage {
 
 // ----------------------------------------------------------------------------- the row loop
 // How abar_n = exp(min(delta A_n, 20)) is formed (a wave-uniform choice):
-//   kClamp: exp of the clamped exponent, per state (any A, any delta);
-//   kExp:   exp per state without the clamp (delta >= 0 and all A <= 0, so delta A_n <= 0);
-//   kPow:   as kExp, for rows of A that are integer multiples of their first entry,
-//           A_n = (n+1) A_0: then abar_n = abar_0^(n+1), formed by products of earlier powers
-//           (depth ceil(log2(n+1))), one exponential per row instead of N.
-enum Disc { kClamp = 0, kExp = 1, kPow = 2 };
+//   kClamp: exp of the clamped exponent (any A, any delta);
+//   kExp:   exp without the clamp, when delta >= 0 and every A <= 0 (then delta A_n <= 0).
+enum Disc { kClamp = 0, kExp = 1 };
 
 // One row of one channel: discretise, advance the N states, optionally read out.
 template <int NS, bool SOFTPLUS, int DISC, bool READOUT, bool GATE>
@@ -144,26 +141,14 @@ __device__ __forceinline__ float row_step(float xx, float dd, float zz, const fl
   const float delta = SOFTPLUS ? softplus_f(dd) : dd;
   const float dx = delta * xx;
   float acc = 0.0f;
-  float pw[DISC == kPow ? NS : 1];
-  if constexpr (DISC == kPow) {
-    pw[0] = hw_exp2(delta * A2[0]);
-#pragma unroll
-    for (int k = 2; k <= NS; ++k) pw[k - 1] = pw[k / 2 - 1] * pw[k - k / 2 - 1];
-  }
 #pragma unroll
   for (int n = 0; n < NS; ++n) {
-    float ab;
-    if constexpr (DISC == kPow) {
-      ab = pw[n];
-    } else {
-      float dA = delta * A2[n];
-      if (DISC == kClamp) {
-        dA = dA > kClampLog2 ? kClampLog2 : dA;
-        if (!READOUT) e[n] += dA;
-      }
-      ab = hw_exp2(dA);
+    float dA = delta * A2[n];
+    if (DISC == kClamp) {
+      dA = dA > kClampLog2 ? kClampLog2 : dA;
+      if (!READOUT) e[n] += dA;
     }
-    h[n] = fmaf(ab, h[n], dx * bc[n]);
+    h[n] = fmaf(hw_exp2(dA), h[n], dx * bc[n]);
     if (READOUT) acc = fmaf(bc[NS + n], h[n], acc);
     // states in groups of 8: bounds the exponentials held in flight (register pressure)
     if (NS > 8 && (n & 7) == 7) __builtin_amdgcn_sched_barrier(0);
@@ -267,17 +252,14 @@ __device__ __forceinline__ void run_rows(const SelParams& p, int64_t row0, int64
 // Loads the lane's row of A (scaled to base 2) and picks the wave's discretisation (see Disc).
 template <int NS, bool SOFTPLUS>
 __device__ __forceinline__ int load_A(const SelParams& p, int64_t dl, float* A2) {
-  bool nonpos = true, multiples = true;
-  const float a0 = p.A[dl * NS];
+  bool nonpos = true;
 #pragma unroll
   for (int n = 0; n < NS; ++n) {
     const float a = p.A[dl * NS + n];
     A2[n] = a * kLog2e;
     nonpos = nonpos && !(a > 0.0f);
-    multiples = multiples && (a == (float)(n + 1) * a0);
   }
-  if (!(SOFTPLUS && __all(nonpos))) return kClamp;
-  return __all(multiples) ? kPow : kExp;
+  return (SOFTPLUS && __all(nonpos)) ? kExp : kClamp;
 }
 
 // ----------------------------------------------------------------------------- pass 1: aggregates
@@ -297,9 +279,7 @@ __global__ __launch_bounds__(kThreads, 4) void selective_aggregate_kernel(SelPar
   for (int n = 0; n < NS; ++n) { h[n] = 0.0f; e[n] = 0.0f; }
   float sum_delta = 0.0f;
   __shared__ float lds[2 * BCStage<NS, false>::PER_BLOCK];
-  if (disc == kPow)
-    run_rows<Tin, float, NS, SOFTPLUS, kPow, false, false>(p, U.row0, U.row1, dl, A2, bias, 0.0f, h, e, sum_delta, lds);
-  else if (disc == kExp)
+  if (disc == kExp)
     run_rows<Tin, float, NS, SOFTPLUS, kExp, false, false>(p, U.row0, U.row1, dl, A2, bias, 0.0f, h, e, sum_delta, lds);
   else
     run_rows<Tin, float, NS, SOFTPLUS, kClamp, false, false>(p, U.row0, U.row1, dl, A2, bias, 0.0f, h, e, sum_delta,
@@ -308,7 +288,7 @@ __global__ __launch_bounds__(kThreads, 4) void selective_aggregate_kernel(SelPar
 #pragma unroll
   for (int n = 0; n < NS; ++n) {
     // prod abar = 2^(sum of the exponents): A2 sum(delta) without the clamp, else the clamped sum
-    const float P = disc != kClamp ? hw_exp2(A2[n] * sum_delta) : hw_exp2(e[n]);
+    const float P = disc == kExp ? hw_exp2(A2[n] * sum_delta) : hw_exp2(e[n]);
     p.aggP[(u * NS + n) * p.D + d] = P;
     p.aggH[(u * NS + n) * p.D + d] = h[n];
   }
@@ -317,9 +297,7 @@ __global__ __launch_bounds__(kThreads, 4) void selective_aggregate_kernel(SelPar
 template <typename Tin, typename Tout, int NS, bool SOFTPLUS, bool GATE>
 __device__ __forceinline__ void scan_rows(const SelParams& p, const Unit& U, int disc, int64_t dl, const float* A2,
                                           float bias, float dskip, float* h, float* e, float& sum_delta, float* lds) {
-  if (disc == kPow)
-    run_rows<Tin, Tout, NS, SOFTPLUS, kPow, true, GATE>(p, U.row0, U.row1, dl, A2, bias, dskip, h, e, sum_delta, lds);
-  else if (disc == kExp)
+  if (disc == kExp)
     run_rows<Tin, Tout, NS, SOFTPLUS, kExp, true, GATE>(p, U.row0, U.row1, dl, A2, bias, dskip, h, e, sum_delta, lds);
   else
     run_rows<Tin, Tout, NS, SOFTPLUS, kClamp, true, GATE>(p, U.row0, U.row1, dl, A2, bias, dskip, h, e, sum_delta,

@@ -99,6 +99,37 @@ def test_decode_steps_equal_scan_and_oracle():
     assert_close(host(y_dec), host(y_scan), 1e-5, "decode vs scan")
 
 
+def test_decode_steps_replayed_from_a_hip_graph():
+    """Decode steps captured once in a HIP graph: every replay, with eager work and synchronisations
+    between replays, equals the same steps run eagerly."""
+    import torch
+    B, L, D = 4, 12, 320
+    inp = synth.rglru_inputs(B, L, D, synth.BF16, 52, with_h0=True)
+    x, r, i = (to_dev(inp.t[n]) for n in ("x", "r_logit", "i_logit"))
+    a_log, h0 = to_dev(inp.p["a_log"]), to_dev(inp.p["h0"])
+    xs, rs, is_ = ([t[:, s].contiguous() for s in range(L)] for t in (x, r, i))
+    state_e = h0.clone()
+    y_e = torch.stack([ssd.rglru_update(xs[s], rs[s], is_[s], a_log, 8.0, state_e) for s in range(L)], 1)
+    state = h0.clone()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        ssd.rglru_update(xs[0], rs[0], is_[0], a_log, 8.0, h0.clone())  # warm up on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            ys = [ssd.rglru_update(xs[s], rs[s], is_[s], a_log, 8.0, state) for s in range(L)]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        state.copy_(h0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(torch.stack(ys, 1), y_e), f"replay {rep}: outputs differ from eager"
+        assert torch.equal(state, state_e), f"replay {rep}: state differs from eager"
+        ssd.rglru_update(xs[0], rs[0], is_[0], a_log, 8.0, h0.clone())  # eager work between replays
+
+
 def test_split_scan_carries_state():
     import torch
     inp = synth.rglru_inputs(2, 250, 130, synth.F32, 61, with_h0=True)
