@@ -93,7 +93,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t unit_window(const void* a, int
   return make_window(static_cast<const char*>(a) + row0 * D * es, (uint32_t)(nrows * D * es));
 }
 
-constexpr int kPrefetch = 2;   // rows of x / dt / z in flight per lane (also the unroll factor)
+constexpr int kPrefetch = 4;   // rows of x / dt / z in flight per lane (also the unroll factor)
 constexpr int kRowBlock = 64;  // rows of B / C staged in LDS at a time
 
 // B_n and C_n are shared by every channel of a row, so the workgroup (all of whose lanes work on
