@@ -69,6 +69,21 @@ template <> struct io2<bf16_t> {
   }
 };
 
+// Four consecutive elements (index a multiple of 4, base 16-byte aligned).
+template <typename T> struct io4;
+template <> struct io4<float> {
+  static __device__ __forceinline__ void store(void* p, int64_t i, float a, float b, float c, float d) {
+    *reinterpret_cast<float4*>(static_cast<float*>(p) + i) = make_float4(a, b, c, d);
+  }
+};
+template <> struct io4<bf16_t> {
+  static __device__ __forceinline__ void store(void* p, int64_t i, float a, float b, float c, float d) {
+    const uint32_t lo = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p) + i) = make_uint2(lo, hi);
+  }
+};
+
 // ------------------------------------------------------------------ buffer windows
 // A buffer resource over [p, p + bytes), bytes < 2^31.  Accesses through it take a per-lane byte
 // offset (vector register) plus a wave-uniform byte offset (scalar register), so a tile of rows

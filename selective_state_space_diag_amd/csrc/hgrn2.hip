@@ -168,6 +168,9 @@ struct H2Lds {
   float gpart[kGateParts][kRows];  // gate products per token group
   float gcol[kRows];               // Gamma_C per value row
   uint4 sx[4][2][2][2][64];        // incoming state as bf16 pairs: [row tile][half][k-step][hi, lo][lane]
+  uint2 qk[10][2][64];             // causal Q K^T tiles (st <= tt) as bf16 pairs: [tile][hi, lo][lane]
+  uint16_t gstage[kCh * kRows];    // next chunk's gate logits and values [t][i] (vw_off layout)
+  uint16_t vstage[kCh * kRows];
 };
 
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
@@ -179,8 +182,10 @@ __device__ __forceinline__ uint2 lds_tr(const uint16_t* p) {
 }
 
 struct H2Prefetch {
-  v4i_t q[2], k[2];                    // 16-byte segments of Q and K
-  uint32_t g[kGateTok], v[kGateTok];   // gate logit and value of column i, kGateTok tokens
+  v4i_t q[2], k[2];  // 16-byte segments of Q and K: segment it * 512 + tid
+};
+struct H2GatePrefetch {
+  v4i_t g, v;        // 8 gate logits / values: row tid / 8, columns 8 (tid % 8) .. +7 of the half
 };
 
 // Window over the rows [t0, t0 + valid) of head hh of batch b in a [B, L, H, 128] bf16 array:
@@ -191,12 +196,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t h2_window(const H2Params& p, c
   return make_window(base, (uint32_t)((int64_t)(valid - 1) * p.H * kDh * 2 + kDh * 2));
 }
 
-__device__ __forceinline__ void h2_fetch(const H2Params& p, int64_t b, int64_t hh, int i0, int64_t t0, int tid,
+__device__ __forceinline__ void h2_fetch(const H2Params& p, int64_t b, int64_t hh, int64_t t0, int tid,
                                          H2Prefetch& f) {
   const int valid = (int)min((int64_t)kCh, p.L - t0);
   const uint32_t row_bytes = (uint32_t)(p.H * kDh * 2);
   const auto wq = h2_window(p, p.q, b, hh, t0, valid), wk = h2_window(p, p.k, b, hh, t0, valid);
-  const auto wv = h2_window(p, p.v, b, hh, t0, valid), wg = h2_window(p, p.g, b, hh, t0, valid);
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
     const int idx = it * 512 + tid;  // 1024 segments of 8 elements: row t, segment seg
@@ -205,14 +209,45 @@ __device__ __forceinline__ void h2_fetch(const H2Params& p, int64_t b, int64_t h
     f.q[it] = __builtin_amdgcn_raw_buffer_load_b128(wq, (int)off, 0, 0);
     f.k[it] = __builtin_amdgcn_raw_buffer_load_b128(wk, (int)off, 0, 0);
   }
-  const int i = tid & 63, part = tid >> 6;
-  const uint32_t lane_off = (uint32_t)(i0 + i) * 2;
+}
+
+__device__ __forceinline__ void h2_fetch_gates(const H2Params& p, int64_t b, int64_t hh, int i0, int64_t t0, int tid,
+                                               H2GatePrefetch& f) {
+  const int valid = (int)min((int64_t)kCh, p.L - t0);
+  const uint32_t row_bytes = (uint32_t)(p.H * kDh * 2);
+  const auto wv = h2_window(p, p.v, b, hh, t0, valid), wg = h2_window(p, p.g, b, hh, t0, valid);
+  const uint32_t off = (uint32_t)(tid >> 3) * row_bytes + (uint32_t)(i0 + 8 * (tid & 7)) * 2;
+  f.g = __builtin_amdgcn_raw_buffer_load_b128(wg, (int)off, 0, 0);
+  f.v = __builtin_amdgcn_raw_buffer_load_b128(wv, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ void h2_stage_gates(H2Lds& sm, int tid, const H2GatePrefetch& f) {
+  const int t = tid >> 3, c0 = 8 * (tid & 7);
+  *reinterpret_cast<uint2*>(&sm.gstage[vw_off(t, c0)]) = make_uint2((uint32_t)f.g.x, (uint32_t)f.g.y);
+  *reinterpret_cast<uint2*>(&sm.gstage[vw_off(t, c0 + 4)]) = make_uint2((uint32_t)f.g.z, (uint32_t)f.g.w);
+  *reinterpret_cast<uint2*>(&sm.vstage[vw_off(t, c0)]) = make_uint2((uint32_t)f.v.x, (uint32_t)f.v.y);
+  *reinterpret_cast<uint2*>(&sm.vstage[vw_off(t, c0 + 4)]) = make_uint2((uint32_t)f.v.z, (uint32_t)f.v.w);
+}
+
+// Gates, part 1: thread (column gi = lane, token group gp = wave) reads its 8 staged gate logits and
+// values (two transposing reads each), forms g = lb + (1 - lb) sigmoid(logit) (1 past the chunk's
+// valid tokens) and its running products, and publishes the group product.
+__device__ __forceinline__ void h2_gate1(H2Lds& sm, int lane, int gp, int valid, float lb, float one_m_lb,
+                                         float (&gam_run)[kGateTok], float (&vv)[kGateTok]) {
+  const int rb = kGateTok * gp + ((lane & 15) >> 2), cb = 16 * (lane >> 4) + 4 * (lane & 3);
+  const uint2 g0 = lds_tr(&sm.gstage[vw_off(rb, cb)]), g1 = lds_tr(&sm.gstage[vw_off(rb + 4, cb)]);
+  const uint2 v0 = lds_tr(&sm.vstage[vw_off(rb, cb)]), v1 = lds_tr(&sm.vstage[vw_off(rb + 4, cb)]);
+  const uint32_t gw[4] = {g0.x, g0.y, g1.x, g1.y}, vw[4] = {v0.x, v0.y, v1.x, v1.y};
+  float run = 1.0f;
 #pragma unroll
   for (int u = 0; u < kGateTok; ++u) {
-    const uint32_t ro = (uint32_t)(part * kGateTok + u) * row_bytes;
-    f.g[u] = __builtin_amdgcn_raw_buffer_load_b16(wg, (int)lane_off, (int)ro, 0);
-    f.v[u] = __builtin_amdgcn_raw_buffer_load_b16(wv, (int)lane_off, (int)ro, 0);
+    const float glog = (u & 1) ? bf16_hi(gw[u >> 1]) : bf16_lo(gw[u >> 1]);
+    const float gv = (gp * kGateTok + u < valid) ? fmaf(one_m_lb, sigmoid_f(glog), lb) : 1.0f;
+    run *= gv;
+    gam_run[u] = run;
+    vv[u] = (u & 1) ? bf16_hi(vw[u >> 1]) : bf16_lo(vw[u >> 1]);
   }
+  sm.gpart[gp][lane] = run;
 }
 
 // Token tiles of the output handled by half h of a row tile: {0, 3} or {1, 2}.
@@ -224,51 +259,39 @@ template <int H> struct Tiles {
   static constexpr int base(int a) { return a ? n0 : 0; }
 };
 
-// Q K^T tiles D[s][t] for this half's token tiles, causal mask, as bf16 hi / lo pairs.
-template <int H>
-__device__ __forceinline__ void h2_qk(const uint16_t* Qs, const uint16_t* Ks, int l16, int lg, uint32_t (&a_hi)[5][2],
-                                      uint32_t (&a_lo)[5][2]) {
-  using TL = Tiles<H>;
+// Causal Q K^T tile ti = tt (tt + 1) / 2 + st (key tile st <= token tile tt) as D[s][t], masked and
+// split into bf16 hi / lo pairs in LDS (each lane keeps its own D-layout entries).
+__device__ __forceinline__ void h2_qk_tile(H2Lds& sm, const uint16_t* Qs, const uint16_t* Ks, int ti, int lane) {
+  const int tt = ti >= 6 ? 3 : ti >= 3 ? 2 : ti >= 1 ? 1 : 0;
+  const int st = ti - tt * (tt + 1) / 2;
+  const int l16 = lane & 15, lg = lane >> 4;
+  floatx4_t acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    constexpr int dummy = 0;
-    (void)dummy;
-    const int tt = TL::tt(a);
-    floatx4_t acc[4];
-#pragma unroll
-    for (int st = 0; st < 4; ++st) acc[st] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint4 qb = *reinterpret_cast<const uint4*>(&Qs[qk_off(16 * tt + l16, 32 * ks + 8 * lg)]);
-#pragma unroll
-      for (int st = 0; st < 4; ++st)  // independent accumulation chains, one per key tile
-        if (st <= tt)
-          acc[st] = mfma(*reinterpret_cast<const uint4*>(&Ks[qk_off(16 * st + l16, 32 * ks + 8 * lg)]), qb, acc[st]);
-    }
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      if (st <= tt) {
-        if (st == tt) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (4 * lg + r > l16) acc[st][r] = 0.0f;  // s > t
-        }
-        const int ti = TL::base(a) + st;
-        split2(acc[st][0], acc[st][1], a_hi[ti][0], a_lo[ti][0]);
-        split2(acc[st][2], acc[st][3], a_hi[ti][1], a_lo[ti][1]);
-      }
-    }
+  for (int ks = 0; ks < 4; ++ks) {
+    const uint4 ka = *reinterpret_cast<const uint4*>(&Ks[qk_off(16 * st + l16, 32 * ks + 8 * lg)]);
+    const uint4 qb = *reinterpret_cast<const uint4*>(&Qs[qk_off(16 * tt + l16, 32 * ks + 8 * lg)]);
+    acc = mfma(ka, qb, acc);
   }
+  if (st == tt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * lg + r > l16) acc[r] = 0.0f;  // s > t
+  }
+  uint2 hi, lo;
+  split2(acc[0], acc[1], hi.x, lo.x);
+  split2(acc[2], acc[3], hi.y, lo.y);
+  sm.qk[ti][0][lane] = hi;
+  sm.qk[ti][1][lane] = lo;
 }
 
 // O^T tiles of this half (rows i = iw + 4 lg + r, columns t = 16 tt + l16):
 //   O = Gamma (.) ( (A W) / Gamma_C + Q S^T )
 template <int H, typename Tout>
-__device__ __forceinline__ void h2_out(const H2Params& p, H2Lds& sm, const uint16_t* Qs, int iw, int l16, int lg,
-                                       const uint32_t (&a_hi)[5][2], const uint32_t (&a_lo)[5][2],
+__device__ __forceinline__ void h2_out(const H2Params& p, H2Lds& sm, const uint16_t* Qs, int iw, int lane,
                                        const uint4 (&s_hi)[4], const uint4 (&s_lo)[4], int64_t obase_row,
                                        int64_t row_stride, int valid) {
   using TL = Tiles<H>;
+  const int l16 = lane & 15, lg = lane >> 4;
   // W as A operands: slots s = 32 ks + 16 h' + 4 lg + r; lane 4b + c of a group points at
   // row 32 ks + 16 h' + 4 lg + b, columns iw + 4c .. +3
   uint4 w_hi[2], w_lo[2];
@@ -299,13 +322,12 @@ __device__ __forceinline__ void h2_out(const H2Params& p, H2Lds& sm, const uint1
       for (int a = 0; a < 2; ++a) {
         const int tt = TL::tt(a);
         if (2 * ks <= tt) {  // key tiles 2 ks, 2 ks + 1; tiles past tt are masked entirely
-          const int t0i = TL::base(a) + 2 * ks;
+          const int t0i = tt * (tt + 1) / 2 + 2 * ks;
           const bool second = 2 * ks + 1 <= tt;
-          uint4 ah, al;
-          ah.x = a_hi[t0i][0]; ah.y = a_hi[t0i][1];
-          al.x = a_lo[t0i][0]; al.y = a_lo[t0i][1];
-          ah.z = second ? a_hi[t0i + 1][0] : 0u; ah.w = second ? a_hi[t0i + 1][1] : 0u;
-          al.z = second ? a_lo[t0i + 1][0] : 0u; al.w = second ? a_lo[t0i + 1][1] : 0u;
+          const uint2 h0 = sm.qk[t0i][0][lane], l0 = sm.qk[t0i][1][lane];
+          const uint2 h1 = second ? sm.qk[t0i + 1][0][lane] : make_uint2(0u, 0u);
+          const uint2 l1 = second ? sm.qk[t0i + 1][1][lane] : make_uint2(0u, 0u);
+          const uint4 ah = make_uint4(h0.x, h0.y, h1.x, h1.y), al = make_uint4(l0.x, l0.y, l1.x, l1.y);
           oa[a] = mfma(w_hi[ks], ah, oa[a]);
           oa[a] = mfma(w_lo[ks], ah, oa[a]);
           oa[a] = mfma(w_hi[ks], al, oa[a]);
@@ -322,9 +344,8 @@ __device__ __forceinline__ void h2_out(const H2Params& p, H2Lds& sm, const uint1
     const float4 gm = *reinterpret_cast<const float4*>(&sm.gam[t][iw + 4 * lg]);
     if (t < valid) {
       const int64_t ob = (obase_row + t) * row_stride + iw + 4 * lg;
-      io2<Tout>::store(p.o, ob, gm.x * fmaf(oa[a][0], igc[0], os[a][0]), gm.y * fmaf(oa[a][1], igc[1], os[a][1]));
-      io2<Tout>::store(p.o, ob + 2, gm.z * fmaf(oa[a][2], igc[2], os[a][2]),
-                       gm.w * fmaf(oa[a][3], igc[3], os[a][3]));
+      io4<Tout>::store(p.o, ob, gm.x * fmaf(oa[a][0], igc[0], os[a][0]), gm.y * fmaf(oa[a][1], igc[1], os[a][1]),
+                       gm.z * fmaf(oa[a][2], igc[2], os[a][2]), gm.w * fmaf(oa[a][3], igc[3], os[a][3]));
     }
   }
 }
@@ -363,7 +384,16 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
 
   const int64_t nchunks = (p.L + kCh - 1) / kCh;
   H2Prefetch f;
-  h2_fetch(p, b, hh, i0, 0, tid, f);
+  H2GatePrefetch fg;
+  float gam_run[kGateTok], vv[kGateTok];
+  h2_fetch(p, b, hh, 0, tid, f);
+  // gate part 1 of chunk 0; the gates of chunk c + 1 are staged during chunk c and their part 1
+  // runs at the end of chunk c, so the gate step overlaps the previous chunk's products
+  h2_fetch_gates(p, b, hh, i0, 0, tid, fg);
+  h2_stage_gates(sm, tid, fg);
+  if (nchunks > 1) h2_fetch_gates(p, b, hh, i0, kCh, tid, fg);
+  __syncthreads();
+  h2_gate1(sm, tid & 63, wave, (int)min((int64_t)kCh, p.L), lb, one_m_lb, gam_run, vv);
   for (int64_t c = 0; c < nchunks; ++c) {
     // Lane indices re-derived per chunk from an opaque copy: keeps the compiler from hoisting the
     // many per-lane LDS addresses out of the loop into registers.
@@ -397,22 +427,8 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
       sm.sx[rt][half_t][kk][0][lane] = my_hi[kk];
       sm.sx[rt][half_t][kk][1][lane] = my_lo[kk];
     }
-    // ---- gates, part 1: thread (column i, token group gp), running products over its tokens
     const int gi = tidv & 63, gp = tidv >> 6;
-    float gam_run[kGateTok], vv[kGateTok];
-    {
-      float run = 1.0f;
-#pragma unroll
-      for (int u = 0; u < kGateTok; ++u) {
-        const int t = gp * kGateTok + u;
-        const float gv = (t < valid) ? fmaf(one_m_lb, sigmoid_f(bf16_to_f32((uint16_t)f.g[u])), lb) : 1.0f;
-        run *= gv;
-        gam_run[u] = run;
-        vv[u] = bf16_to_f32((uint16_t)f.v[u]);
-      }
-      sm.gpart[gp][gi] = run;
-    }
-    if (c + 1 < nchunks) h2_fetch(p, b, hh, i0, t0 + kCh, tid, f);  // in flight during this chunk
+    if (c + 1 < nchunks) h2_fetch(p, b, hh, t0 + kCh, tid, f);  // in flight during this chunk
     __syncthreads();  // Q, K, group products, state halves visible
 
     // ---- gates, part 2: Gamma and W = V Gamma_C / Gamma (row-major, one column per lane)
@@ -444,11 +460,15 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
       s_hi[2 + kk] = half_t ? my_hi[kk] : oh;
       s_lo[2 + kk] = half_t ? my_lo[kk] : ol;
     }
-    // ---- Q K^T for this half's token tiles
-    uint32_t a_hi[5][2], a_lo[5][2];
-    if (half_t == 0) h2_qk<0>(Qs, Ks, l16, lg, a_hi, a_lo);
-    else h2_qk<1>(Qs, Ks, l16, lg, a_hi, a_lo);
-    __syncthreads();  // Gamma, W, Gamma_C visible
+    // ---- the 10 causal Q K^T tiles, once per workgroup: wave w takes tiles w and w + 8
+    h2_qk_tile(sm, Qs, Ks, wave, lane);
+    if (wave < 2) h2_qk_tile(sm, Qs, Ks, wave + 8, lane);
+    // ---- next chunk's gate inputs into LDS; the chunk after that starts loading
+    if (c + 1 < nchunks) {
+      h2_stage_gates(sm, tidv, fg);
+      if (c + 2 < nchunks) h2_fetch_gates(p, b, hh, i0, t0 + 2 * kCh, tid, fg);
+    }
+    __syncthreads();  // Gamma, W, Gamma_C, Q K^T tiles visible
 
     // ---- O^T for this half's token tiles
     const int64_t obase_row = b * p.L + t0;
@@ -456,8 +476,8 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
     {
       H2Params pp = p;
       pp.o = static_cast<char*>(p.o) + (hh * kDh + i0) * (int64_t)sizeof(Tout);
-      if (half_t == 0) h2_out<0, Tout>(pp, sm, Qs, iw, l16, lg, a_hi, a_lo, s_hi, s_lo, obase_row, row_stride, valid);
-      else h2_out<1, Tout>(pp, sm, Qs, iw, l16, lg, a_hi, a_lo, s_hi, s_lo, obase_row, row_stride, valid);
+      if (half_t == 0) h2_out<0, Tout>(pp, sm, Qs, iw, lane, s_hi, s_lo, obase_row, row_stride, valid);
+      else h2_out<1, Tout>(pp, sm, Qs, iw, lane, s_hi, s_lo, obase_row, row_stride, valid);
     }
 
     // ---- state update on this wave's tiles: S^T = S^T Gamma_C[i] + K^T W  (slots s = 32 ks + 8 lg + e)
@@ -484,6 +504,8 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
         }
       }
     }
+    // ---- gate part 1 of the next chunk (its inputs were staged before the last barrier)
+    if (c + 1 < nchunks) h2_gate1(sm, lane, gp, (int)min((int64_t)kCh, p.L - t0 - kCh), lb, one_m_lb, gam_run, vv);
   }
 
   if (p.S_last) {
