@@ -136,13 +136,14 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) 
   hi = f32_to_bf16(x);
   lo = f32_to_bf16(x - bf16_to_f32(hi));
 }
-// two values -> packed bf16 pairs (element 0 in the low half)
+// two values -> packed bf16 pairs (element 0 in the low half): x = hi + lo per element
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  uint16_t h0, l0, h1, l1;
-  split_bf16(x0, h0, l0);
-  split_bf16(x1, h1, l1);
-  hi = (uint32_t)h0 | ((uint32_t)h1 << 16);
-  lo = (uint32_t)l0 | ((uint32_t)l1 << 16);
+  const f32x2_t x = {x0, x1};
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
+  const f32x2_t xh = {__uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u)};
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(x - xh, bf16x2_t));
 }
 
 // Q / K tile [64 rows][128 cols] bf16: 16-byte segment s of row r stored at segment s ^ f(r).
@@ -238,14 +239,23 @@ __device__ __forceinline__ void h2_gate1(H2Lds& sm, int lane, int gp, int valid,
   const uint2 g0 = lds_tr(&sm.gstage[vw_off(rb, cb)]), g1 = lds_tr(&sm.gstage[vw_off(rb + 4, cb)]);
   const uint2 v0 = lds_tr(&sm.vstage[vw_off(rb, cb)]), v1 = lds_tr(&sm.vstage[vw_off(rb + 4, cb)]);
   const uint32_t gw[4] = {g0.x, g0.y, g1.x, g1.y}, vw[4] = {v0.x, v0.y, v1.x, v1.y};
-  float run = 1.0f;
+  float gv[kGateTok];
 #pragma unroll
   for (int u = 0; u < kGateTok; ++u) {
     const float glog = (u & 1) ? bf16_hi(gw[u >> 1]) : bf16_lo(gw[u >> 1]);
-    const float gv = (gp * kGateTok + u < valid) ? fmaf(one_m_lb, sigmoid_f(glog), lb) : 1.0f;
-    run *= gv;
-    gam_run[u] = run;
+    gv[u] = fmaf(one_m_lb, sigmoid_f(glog), lb);
     vv[u] = (u & 1) ? bf16_hi(vw[u >> 1]) : bf16_lo(vw[u >> 1]);
+  }
+  if (valid < kCh) {  // ragged last chunk: tokens past it leave the state unchanged
+#pragma unroll
+    for (int u = 0; u < kGateTok; ++u)
+      if (gp * kGateTok + u >= valid) gv[u] = 1.0f;
+  }
+  float run = 1.0f;
+#pragma unroll
+  for (int u = 0; u < kGateTok; ++u) {
+    run *= gv[u];
+    gam_run[u] = run;
   }
   sm.gpart[gp][lane] = run;
 }
@@ -354,7 +364,7 @@ template <typename Tout>
 __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
   __shared__ H2Lds sm;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rt = wave & 3, half_t = wave >> 2;  // row tile, token / state half
   // both halves of a head on the same XCD (blockIdx % 8) so their Q / K reads share an L2
   int64_t bh, half;
@@ -427,27 +437,30 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
       sm.sx[rt][half_t][kk][0][lane] = my_hi[kk];
       sm.sx[rt][half_t][kk][1][lane] = my_lo[kk];
     }
-    const int gi = tidv & 63, gp = tidv >> 6;
+    const int gi = tidv & 63, gp = wave;
     if (c + 1 < nchunks) h2_fetch(p, b, hh, t0 + kCh, tid, f);  // in flight during this chunk
     __syncthreads();  // Q, K, group products, state halves visible
 
     // ---- gates, part 2: Gamma and W = V Gamma_C / Gamma (row-major, one column per lane)
     {
-      float pre = 1.0f, all = 1.0f;
-#pragma unroll
-      for (int q2 = 0; q2 < kGateParts; ++q2) {
-        const float tq = sm.gpart[q2][gi];
-        if (q2 < gp) pre *= tq;
-        all *= tq;
-      }
+      float pre = 1.0f, post = 1.0f;
+      for (int q2 = 0; q2 < gp; ++q2) pre *= sm.gpart[q2][gi];  // gp is wave-uniform
+      for (int q2 = gp; q2 < kGateParts; ++q2) post *= sm.gpart[q2][gi];
+      const float all = pre * post;
       if (gp == 0) sm.gcol[gi] = all;
 #pragma unroll
-      for (int u = 0; u < kGateTok; ++u) {
+      for (int u = 0; u < kGateTok; u += 2) {
         const int t = gp * kGateTok + u;
-        const float gam = pre * gam_run[u];
-        sm.gam[t][gi] = gam;
-        const int o = vw_off(t, gi);
-        split_bf16(vv[u] * (all * hw_rcp(gam)), sm.w[o], sm.w_lo[o]);
+        const float gam0 = pre * gam_run[u], gam1 = pre * gam_run[u + 1];
+        sm.gam[t][gi] = gam0;
+        sm.gam[t + 1][gi] = gam1;
+        uint32_t hi, lo;
+        split2(vv[u] * (all * hw_rcp(gam0)), vv[u + 1] * (all * hw_rcp(gam1)), hi, lo);
+        const int o0 = vw_off(t, gi), o1 = vw_off(t + 1, gi);
+        sm.w[o0] = (uint16_t)hi;
+        sm.w[o1] = (uint16_t)(hi >> 16);
+        sm.w_lo[o0] = (uint16_t)lo;
+        sm.w_lo[o1] = (uint16_t)(lo >> 16);
       }
     }
     // ---- partner's half of the incoming state; k-steps in order (half 0 holds j < 64)
