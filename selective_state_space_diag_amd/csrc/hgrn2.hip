@@ -7,6 +7,7 @@
 // Recurrent scan: one workgroup per (batch, head), one lane per value row i holding S[i][:] in
 // registers; k_t and q_t of each step are staged in LDS (double-buffered) and read as broadcasts.
 #include "common.hpp"
+#include "h2_layout.hpp"
 #include "kernels.hpp"
 
 namespace ssd {
@@ -146,15 +147,7 @@ __device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_
   lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(x - xh, bf16x2_t));
 }
 
-// Q / K tile [64 rows][128 cols] bf16: 16-byte segment s of row r stored at segment s ^ f(r).
-__device__ __forceinline__ int qk_off(int row, int col) {
-  const int f = (row ^ (row >> 3)) & 7;
-  return row * kDh + ((((col >> 3) ^ f)) << 3) + (col & 7);
-}
-// V / Gamma and W tiles [64 tokens][64 rows] bf16: 4-element chunk c of row r stored at c ^ (r & 15).
-__device__ __forceinline__ int vw_off(int row, int col) {
-  return row * kRows + ((((col >> 2) ^ (row & 15))) << 2) + (col & 3);
-}
+using h2::qk_off;
 
 constexpr int kWaves = 8;
 constexpr int kGateParts = kWaves;           // token groups of the gate step
@@ -170,7 +163,7 @@ struct H2Lds {
   float gcol[kRows];               // Gamma_C per value row
   uint4 sx[4][2][2][2][64];        // incoming state as bf16 pairs: [row tile][half][k-step][hi, lo][lane]
   uint2 qk[10][2][64];             // causal Q K^T tiles (st <= tt) as bf16 pairs: [tile][hi, lo][lane]
-  uint16_t gstage[kCh * kRows];    // next chunk's gate logits and values [t][i] (vw_off layout)
+  uint16_t gstage[kCh * kRows];    // next chunk's gate logits and values [t][i] (gv layout)
   uint16_t vstage[kCh * kRows];
 };
 
@@ -224,10 +217,10 @@ __device__ __forceinline__ void h2_fetch_gates(const H2Params& p, int64_t b, int
 
 __device__ __forceinline__ void h2_stage_gates(H2Lds& sm, int tid, const H2GatePrefetch& f) {
   const int t = tid >> 3, c0 = 8 * (tid & 7);
-  *reinterpret_cast<uint2*>(&sm.gstage[vw_off(t, c0)]) = make_uint2((uint32_t)f.g.x, (uint32_t)f.g.y);
-  *reinterpret_cast<uint2*>(&sm.gstage[vw_off(t, c0 + 4)]) = make_uint2((uint32_t)f.g.z, (uint32_t)f.g.w);
-  *reinterpret_cast<uint2*>(&sm.vstage[vw_off(t, c0)]) = make_uint2((uint32_t)f.v.x, (uint32_t)f.v.y);
-  *reinterpret_cast<uint2*>(&sm.vstage[vw_off(t, c0 + 4)]) = make_uint2((uint32_t)f.v.z, (uint32_t)f.v.w);
+  *reinterpret_cast<uint2*>(&sm.gstage[h2::gv_off(t, c0)]) = make_uint2((uint32_t)f.g.x, (uint32_t)f.g.y);
+  *reinterpret_cast<uint2*>(&sm.gstage[h2::gv_off(t, c0 + 4)]) = make_uint2((uint32_t)f.g.z, (uint32_t)f.g.w);
+  *reinterpret_cast<uint2*>(&sm.vstage[h2::gv_off(t, c0)]) = make_uint2((uint32_t)f.v.x, (uint32_t)f.v.y);
+  *reinterpret_cast<uint2*>(&sm.vstage[h2::gv_off(t, c0 + 4)]) = make_uint2((uint32_t)f.v.z, (uint32_t)f.v.w);
 }
 
 // Gates, part 1: thread (column gi = lane, token group gp = wave) reads its 8 staged gate logits and
@@ -235,9 +228,9 @@ __device__ __forceinline__ void h2_stage_gates(H2Lds& sm, int tid, const H2GateP
 // valid tokens) and its running products, and publishes the group product.
 __device__ __forceinline__ void h2_gate1(H2Lds& sm, int lane, int gp, int valid, float lb, float one_m_lb,
                                          float (&gam_run)[kGateTok], float (&vv)[kGateTok]) {
-  const int rb = kGateTok * gp + ((lane & 15) >> 2), cb = 16 * (lane >> 4) + 4 * (lane & 3);
-  const uint2 g0 = lds_tr(&sm.gstage[vw_off(rb, cb)]), g1 = lds_tr(&sm.gstage[vw_off(rb + 4, cb)]);
-  const uint2 v0 = lds_tr(&sm.vstage[vw_off(rb, cb)]), v1 = lds_tr(&sm.vstage[vw_off(rb + 4, cb)]);
+  const int o0 = h2::gv_gate_off(lane & 15, lane >> 4, gp, 0), o1 = h2::gv_gate_off(lane & 15, lane >> 4, gp, 1);
+  const uint2 g0 = lds_tr(&sm.gstage[o0]), g1 = lds_tr(&sm.gstage[o1]);
+  const uint2 v0 = lds_tr(&sm.vstage[o0]), v1 = lds_tr(&sm.vstage[o1]);
   const uint32_t gw[4] = {g0.x, g0.y, g1.x, g1.y}, vw[4] = {v0.x, v0.y, v1.x, v1.y};
   float gv[kGateTok];
 #pragma unroll
@@ -275,11 +268,12 @@ __device__ __forceinline__ void h2_qk_tile(H2Lds& sm, const uint16_t* Qs, const 
   const int tt = ti >= 6 ? 3 : ti >= 3 ? 2 : ti >= 1 ? 1 : 0;
   const int st = ti - tt * (tt + 1) / 2;
   const int l16 = lane & 15, lg = lane >> 4;
+  const int xa = h2::qk_seg_lane(l16, lg);
   floatx4_t acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    const uint4 ka = *reinterpret_cast<const uint4*>(&Ks[qk_off(16 * st + l16, 32 * ks + 8 * lg)]);
-    const uint4 qb = *reinterpret_cast<const uint4*>(&Qs[qk_off(16 * tt + l16, 32 * ks + 8 * lg)]);
+    const uint4 ka = *reinterpret_cast<const uint4*>(&Ks[h2::qk_seg_off(l16, xa, st, ks)]);
+    const uint4 qb = *reinterpret_cast<const uint4*>(&Qs[h2::qk_seg_off(l16, xa, tt, ks)]);
     acc = mfma(ka, qb, acc);
   }
   if (st == tt) {
@@ -305,24 +299,25 @@ __device__ __forceinline__ void h2_out(const H2Params& p, H2Lds& sm, const uint1
   // W as A operands: slots s = 32 ks + 16 h' + 4 lg + r; lane 4b + c of a group points at
   // row 32 ks + 16 h' + 4 lg + b, columns iw + 4c .. +3
   uint4 w_hi[2], w_lo[2];
+  const int wl = h2::vw_out_lane(l16, lg, iw >> 4);
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    const int rb = 32 * ks + 4 * lg + (l16 >> 2), cb = iw + 4 * (l16 & 3);
-    const uint2 h0 = lds_tr(&sm.w[vw_off(rb, cb)]), h1 = lds_tr(&sm.w[vw_off(rb + 16, cb)]);
-    const uint2 l0 = lds_tr(&sm.w_lo[vw_off(rb, cb)]), l1 = lds_tr(&sm.w_lo[vw_off(rb + 16, cb)]);
+    const int oa = h2::vw_out_off(wl, ks, 0), ob = h2::vw_out_off(wl, ks, 1);
+    const uint2 h0 = lds_tr(&sm.w[oa]), h1 = lds_tr(&sm.w[ob]);
+    const uint2 l0 = lds_tr(&sm.w_lo[oa]), l1 = lds_tr(&sm.w_lo[ob]);
     w_hi[ks] = make_uint4(h0.x, h0.y, h1.x, h1.y);
     w_lo[ks] = make_uint4(l0.x, l0.y, l1.x, l1.y);
   }
   floatx4_t oa[2], os[2];
 #pragma unroll
   for (int a = 0; a < 2; ++a) oa[a] = os[a] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  const int xb = h2::qk_quad_lane(l16, lg);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
-      const int trow = 16 * TL::tt(a) + l16;
-      const uint2 q0 = *reinterpret_cast<const uint2*>(&Qs[qk_off(trow, 32 * ks + 4 * lg)]);
-      const uint2 q1 = *reinterpret_cast<const uint2*>(&Qs[qk_off(trow, 32 * ks + 16 + 4 * lg)]);
+      const uint2 q0 = *reinterpret_cast<const uint2*>(&Qs[h2::qk_quad_off(l16, lg, xb, TL::tt(a), ks, 0)]);
+      const uint2 q1 = *reinterpret_cast<const uint2*>(&Qs[h2::qk_quad_off(l16, lg, xb, TL::tt(a), ks, 1)]);
       const uint4 qbv = make_uint4(q0.x, q0.y, q1.x, q1.y);
       os[a] = mfma(s_hi[ks], qbv, os[a]);
       os[a] = mfma(s_lo[ks], qbv, os[a]);
@@ -448,6 +443,7 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
       for (int q2 = gp; q2 < kGateParts; ++q2) post *= sm.gpart[q2][gi];
       const float all = pre * post;
       if (gp == 0) sm.gcol[gi] = all;
+      const int xg = h2::vw_gate_lane(gi, gp);
 #pragma unroll
       for (int u = 0; u < kGateTok; u += 2) {
         const int t = gp * kGateTok + u;
@@ -456,7 +452,7 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
         sm.gam[t + 1][gi] = gam1;
         uint32_t hi, lo;
         split2(vv[u] * (all * hw_rcp(gam0)), vv[u + 1] * (all * hw_rcp(gam1)), hi, lo);
-        const int o0 = vw_off(t, gi), o1 = vw_off(t + 1, gi);
+        const int o0 = h2::vw_gate_wr(gi, xg, gp, u), o1 = h2::vw_gate_wr(gi, xg, gp, u + 1);
         sm.w[o0] = (uint16_t)hi;
         sm.w[o1] = (uint16_t)(hi >> 16);
         sm.w_lo[o0] = (uint16_t)lo;
@@ -500,17 +496,19 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
       for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int r = 0; r < 4; ++r) S[q][r] *= gc;
+      const int ws0 = h2::vw_state_lane(l16, lg, rt, 0), ws1 = h2::vw_state_lane(l16, lg, rt, 1);
+      const int xd = h2::qk_tr_lane(l16, lg);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const int rb = 32 * ks + 8 * lg + (l16 >> 2);
-        const int cw = iw + 4 * (l16 & 3);
-        const uint2 w0 = lds_tr(&sm.w[vw_off(rb, cw)]), w1 = lds_tr(&sm.w[vw_off(rb + 4, cw)]);
-        const uint2 x0 = lds_tr(&sm.w_lo[vw_off(rb, cw)]), x1 = lds_tr(&sm.w_lo[vw_off(rb + 4, cw)]);
+        const int oa = h2::vw_state_off(ws0, ks), ob = h2::vw_state_off(ws1, ks);
+        const uint2 w0 = lds_tr(&sm.w[oa]), w1 = lds_tr(&sm.w[ob]);
+        const uint2 x0 = lds_tr(&sm.w_lo[oa]), x1 = lds_tr(&sm.w_lo[ob]);
         const uint4 wh = make_uint4(w0.x, w0.y, w1.x, w1.y), wl = make_uint4(x0.x, x0.y, x1.x, x1.y);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int ck = 16 * (4 * half_t + q) + 4 * (l16 & 3);
-          const uint2 k0 = lds_tr(&Ks[qk_off(rb, ck)]), k1 = lds_tr(&Ks[qk_off(rb + 4, ck)]);
+          const int jt = 4 * half_t + q;
+          const uint2 k0 = lds_tr(&Ks[h2::qk_tr_off(l16, lg, xd, ks, 0, jt)]);
+          const uint2 k1 = lds_tr(&Ks[h2::qk_tr_off(l16, lg, xd, ks, 1, jt)]);
           const uint4 kt = make_uint4(k0.x, k0.y, k1.x, k1.y);
           S[q] = mfma(kt, wh, S[q]);
           S[q] = mfma(kt, wl, S[q]);
