@@ -80,13 +80,22 @@ def profiled_traffic(profile, sources):
 
 
 # ----------------------------------------------------------------------------- timing helpers
+WARM_SECONDS = 0.3  # untimed running before each timed region, so clocks have left their idle state
+
+
 def time_calls(fn, n_sets, steps, warmup):
-    """Run ``fn(i % n_sets)`` warmup times, then time ``steps`` back-to-back calls between one pair of
-    HIP events on torch's current stream (the stream the library launches on), synchronizing before
-    and after.  Returns (ms per step from the events, ms per step from the host clock)."""
+    """Run ``fn(i % n_sets)`` at least ``warmup`` times and for at least WARM_SECONDS, then time
+    ``steps`` back-to-back calls between one pair of HIP events on torch's current stream (the stream
+    the library launches on), synchronizing before and after.  Returns (ms per step from the events,
+    ms per step from the host clock)."""
     import torch
-    for i in range(warmup):
+    t_warm = time.perf_counter()
+    i = 0
+    while i < warmup or time.perf_counter() - t_warm < WARM_SECONDS:
         fn(i % n_sets)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
