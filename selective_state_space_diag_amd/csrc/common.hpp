@@ -94,23 +94,30 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_window(const void* p, uin
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-// V consecutive elements of type T per lane through a window.
-template <typename T, int V> struct win;
-template <> struct win<float, 1> {
+// Cache-policy operand of the buffer instructions.  kStreaming sets the non-temporal bit: the lines
+// are not expected to be touched again, so the caches hold them under their streaming policy instead
+// of displacing reused data.  It pays for one-pass streams (input read once, output written once) and
+// costs a little where a later pass re-reads the same rows.
+constexpr int kCached = 0;
+constexpr int kStreaming = 2;
+
+// V consecutive elements of type T per lane through a window, with cache policy P.
+template <typename T, int V, int P = kCached> struct win;
+template <int P> struct win<float, 1, P> {
   using raw = float;
   static __device__ __forceinline__ raw load(__amdgpu_buffer_rsrc_t w, uint32_t lane_off, uint32_t row_off) {
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(w, (int)lane_off, (int)row_off, 0));
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(w, (int)lane_off, (int)row_off, P));
   }
   static __device__ __forceinline__ float get(raw r, int) { return r; }
   static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t w, uint32_t lane_off, uint32_t row_off,
                                                const float* v) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[0]), w, (int)lane_off, (int)row_off, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[0]), w, (int)lane_off, (int)row_off, P);
   }
 };
-template <> struct win<float, 2> {
+template <int P> struct win<float, 2, P> {
   using raw = u32x2_t;
   static __device__ __forceinline__ raw load(__amdgpu_buffer_rsrc_t w, uint32_t lane_off, uint32_t row_off) {
-    return __builtin_amdgcn_raw_buffer_load_b64(w, (int)lane_off, (int)row_off, 0);
+    return __builtin_amdgcn_raw_buffer_load_b64(w, (int)lane_off, (int)row_off, P);
   }
   static __device__ __forceinline__ float get(raw r, int v) { return __uint_as_float(v == 0 ? r.x : r.y); }
   static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t w, uint32_t lane_off, uint32_t row_off,
@@ -118,30 +125,30 @@ template <> struct win<float, 2> {
     u32x2_t d;
     d.x = __float_as_uint(v[0]);
     d.y = __float_as_uint(v[1]);
-    __builtin_amdgcn_raw_buffer_store_b64(d, w, (int)lane_off, (int)row_off, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(d, w, (int)lane_off, (int)row_off, P);
   }
 };
-template <> struct win<bf16_t, 1> {
+template <int P> struct win<bf16_t, 1, P> {
   using raw = unsigned short;
   static __device__ __forceinline__ raw load(__amdgpu_buffer_rsrc_t w, uint32_t lane_off, uint32_t row_off) {
-    return __builtin_amdgcn_raw_buffer_load_b16(w, (int)lane_off, (int)row_off, 0);
+    return __builtin_amdgcn_raw_buffer_load_b16(w, (int)lane_off, (int)row_off, P);
   }
   static __device__ __forceinline__ float get(raw r, int) { return bf16_to_f32(r); }
   static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t w, uint32_t lane_off, uint32_t row_off,
                                                const float* v) {
-    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v[0]), w, (int)lane_off, (int)row_off, 0);
+    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v[0]), w, (int)lane_off, (int)row_off, P);
   }
 };
-template <> struct win<bf16_t, 2> {
+template <int P> struct win<bf16_t, 2, P> {
   using raw = uint32_t;
   static __device__ __forceinline__ raw load(__amdgpu_buffer_rsrc_t w, uint32_t lane_off, uint32_t row_off) {
-    return __builtin_amdgcn_raw_buffer_load_b32(w, (int)lane_off, (int)row_off, 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(w, (int)lane_off, (int)row_off, P);
   }
   static __device__ __forceinline__ float get(raw r, int v) { return v == 0 ? bf16_lo(r) : bf16_hi(r); }
   static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t w, uint32_t lane_off, uint32_t row_off,
                                                const float* v) {
     const uint32_t d = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-    __builtin_amdgcn_raw_buffer_store_b32(d, w, (int)lane_off, (int)row_off, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(d, w, (int)lane_off, (int)row_off, P);
   }
 };
 

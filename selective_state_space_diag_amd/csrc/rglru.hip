@@ -27,7 +27,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kSteps = 16;                 // steps per wave
 constexpr int kChunk = kWaves * kSteps;    // steps per work unit
-constexpr int kBlock = 4;                  // chunks per lookback block
+constexpr int kBlock = 2;                  // chunks per lookback block
 
 struct RgParams {
   int64_t B, L, D;
@@ -73,7 +73,7 @@ __device__ __forceinline__ void rglru_ab(float xx, float rl, float il, float kc,
 // Raw inputs of one wave's kSteps steps (the loads of a unit, kept in flight until needed).
 template <typename Tin, int V>
 struct RgRaw {
-  typename win<Tin, V>::raw x[kSteps], r[kSteps], i[kSteps];
+  typename win<Tin, V, kStreaming>::raw x[kSteps], r[kSteps], i[kSteps];
 };
 
 struct RgUnit {
@@ -110,9 +110,9 @@ __device__ __forceinline__ void rg_fetch(const RgParams& p, const RgUnit& u, uin
 #pragma unroll
   for (int s = 0; s < kSteps; ++s) {
     const uint32_t ro = (uint32_t)min(wave * kSteps + s, u.rows - 1) * row_bytes;
-    raw.x[s] = win<Tin, V>::load(wx, lane_off, ro);
-    raw.r[s] = win<Tin, V>::load(wr, lane_off, ro);
-    raw.i[s] = win<Tin, V>::load(wi, lane_off, ro);
+    raw.x[s] = win<Tin, V, kStreaming>::load(wx, lane_off, ro);
+    raw.r[s] = win<Tin, V, kStreaming>::load(wr, lane_off, ro);
+    raw.i[s] = win<Tin, V, kStreaming>::load(wi, lane_off, ro);
   }
 }
 
@@ -136,7 +136,7 @@ void rglru_scan_kernel(RgParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t total = p.B * p.n_tiles * p.n_chunks;
-  using LD = win<Tin, V>;
+  using LD = win<Tin, V, kStreaming>;
 
   if (threadIdx.x == 0) s_tick[0] = atomicAdd(&p.ctl->tick, 1ull);
   __syncthreads();
@@ -289,7 +289,7 @@ void rglru_scan_kernel(RgParams p) {
           h[v] = fmaf(av[s][v], h[v], bv[s][v]);
           out[v] = h[v];
         }
-        if (ch_ok && s < nvalid) win<Tout, V>::store(wy, lo, (uint32_t)(wave * kSteps + s) * row_bytes, out);
+        if (ch_ok && s < nvalid) win<Tout, V, kStreaming>::store(wy, lo, (uint32_t)(wave * kSteps + s) * row_bytes, out);
       }
     }
     __syncthreads();  // LDS (aggregates, carry, ticket slot) is reused by the next unit
