@@ -152,6 +152,7 @@ using h2::qk_off;
 constexpr int kWaves = 8;
 constexpr int kGateParts = kWaves;           // token groups of the gate step
 constexpr int kGateTok = kCh / kGateParts;   // tokens per gate thread
+constexpr int kGpStride = 12;                // floats per gpart row: 16-byte reads of 16 lanes hit distinct banks
 
 struct H2Lds {
   uint16_t q[2][kCh * kDh];
@@ -159,7 +160,7 @@ struct H2Lds {
   float gam[kCh][kGamStride];  // Gamma [t][i]
   uint16_t w[kCh * kRows];     // W = V * Gamma_C / Gamma [s][i], hi and lo
   uint16_t w_lo[kCh * kRows];
-  float gpart[kGateParts][kRows];  // gate products per token group
+  alignas(16) float gpart[kRows][kGpStride];  // gate products per value row and token group (padded rows)
   float gcol[kRows];               // Gamma_C per value row
   uint4 sx[4][2][2][2][64];        // incoming state as bf16 pairs: [row tile][half][k-step][hi, lo][lane]
   uint2 qk[10][2][64];             // causal Q K^T tiles (st <= tt) as bf16 pairs: [tile][hi, lo][lane]
@@ -250,7 +251,7 @@ __device__ __forceinline__ void h2_gate1(H2Lds& sm, int lane, int gp, int valid,
     run *= gv[u];
     gam_run[u] = run;
   }
-  sm.gpart[gp][lane] = run;
+  sm.gpart[lane][gp] = run;
 }
 
 // Token tiles of the output handled by half h of a row tile: {0, 3} or {1, 2}.
@@ -290,10 +291,35 @@ __device__ __forceinline__ void h2_qk_tile(H2Lds& sm, const uint16_t* Qs, const 
 
 // O^T tiles of this half (rows i = iw + 4 lg + r, columns t = 16 tt + l16):
 //   O = Gamma (.) ( (A W) / Gamma_C + Q S^T )
+// Q S^T part of this half's O^T tiles: needs only Q and the incoming state, so it runs before the
+// gate step's results are published.  The state's k-steps 0, 1 hold j < 64 and 2, 3 the rest: half H
+// holds k-steps 2H, 2H + 1 itself (mine) and receives the others from its partner (other).
+template <int H>
+__device__ __forceinline__ void h2_out_state(const uint16_t* Qs, int lane, const uint4 (&mine_hi)[2],
+                                             const uint4 (&mine_lo)[2], const uint4 (&other_hi)[2],
+                                             const uint4 (&other_lo)[2], floatx4_t (&os)[2]) {
+  using TL = Tiles<H>;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int xb = h2::qk_quad_lane(l16, lg);
+#pragma unroll
+  for (int a = 0; a < 2; ++a) os[a] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const uint2 q0 = *reinterpret_cast<const uint2*>(&Qs[h2::qk_quad_off(l16, lg, xb, TL::tt(a), ks, 0)]);
+      const uint2 q1 = *reinterpret_cast<const uint2*>(&Qs[h2::qk_quad_off(l16, lg, xb, TL::tt(a), ks, 1)]);
+      const uint4 qbv = make_uint4(q0.x, q0.y, q1.x, q1.y);
+      const bool own = (ks >> 1) == H;
+      os[a] = mfma(own ? mine_hi[ks & 1] : other_hi[ks & 1], qbv, os[a]);
+      os[a] = mfma(own ? mine_lo[ks & 1] : other_lo[ks & 1], qbv, os[a]);
+    }
+  }
+}
+
 template <int H, typename Tout>
-__device__ __forceinline__ void h2_out(const H2Params& p, H2Lds& sm, const uint16_t* Qs, int iw, int lane,
-                                       const uint4 (&s_hi)[4], const uint4 (&s_lo)[4], int64_t obase_row,
-                                       int64_t row_stride, int valid) {
+__device__ __forceinline__ void h2_out(const H2Params& p, H2Lds& sm, int iw, int lane, const floatx4_t (&os)[2],
+                                       int64_t obase_row, int64_t row_stride, int valid) {
   using TL = Tiles<H>;
   const int l16 = lane & 15, lg = lane >> 4;
   // W as A operands: slots s = 32 ks + 16 h' + 4 lg + r; lane 4b + c of a group points at
@@ -308,21 +334,12 @@ __device__ __forceinline__ void h2_out(const H2Params& p, H2Lds& sm, const uint1
     w_hi[ks] = make_uint4(h0.x, h0.y, h1.x, h1.y);
     w_lo[ks] = make_uint4(l0.x, l0.y, l1.x, l1.y);
   }
-  floatx4_t oa[2], os[2];
+  floatx4_t oa[2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a) oa[a] = os[a] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  const int xb = h2::qk_quad_lane(l16, lg);
+  for (int a = 0; a < 2; ++a) oa[a] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const uint2 q0 = *reinterpret_cast<const uint2*>(&Qs[h2::qk_quad_off(l16, lg, xb, TL::tt(a), ks, 0)]);
-      const uint2 q1 = *reinterpret_cast<const uint2*>(&Qs[h2::qk_quad_off(l16, lg, xb, TL::tt(a), ks, 1)]);
-      const uint4 qbv = make_uint4(q0.x, q0.y, q1.x, q1.y);
-      os[a] = mfma(s_hi[ks], qbv, os[a]);
-      os[a] = mfma(s_lo[ks], qbv, os[a]);
-    }
-    if (ks < 2) {
+  for (int ks = 0; ks < 2; ++ks) {
+    {
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         const int tt = TL::tt(a);
@@ -436,12 +453,29 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
     if (c + 1 < nchunks) h2_fetch(p, b, hh, t0 + kCh, tid, f);  // in flight during this chunk
     __syncthreads();  // Q, K, group products, state halves visible
 
+    // ---- partner's half of the incoming state, then Q S^T for this half's token tiles
+    floatx4_t os[2];
+    {
+      uint4 oth_hi[2], oth_lo[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        oth_hi[kk] = sm.sx[rt][1 - half_t][kk][0][lane];
+        oth_lo[kk] = sm.sx[rt][1 - half_t][kk][1][lane];
+      }
+      if (half_t == 0) h2_out_state<0>(Qs, lane, my_hi, my_lo, oth_hi, oth_lo, os);
+      else h2_out_state<1>(Qs, lane, my_hi, my_lo, oth_hi, oth_lo, os);
+    }
     // ---- gates, part 2: Gamma and W = V Gamma_C / Gamma (row-major, one column per lane)
     {
-      float pre = 1.0f, post = 1.0f;
-      for (int q2 = 0; q2 < gp; ++q2) pre *= sm.gpart[q2][gi];  // gp is wave-uniform
-      for (int q2 = gp; q2 < kGateParts; ++q2) post *= sm.gpart[q2][gi];
-      const float all = pre * post;
+      const float4 ga = *reinterpret_cast<const float4*>(&sm.gpart[gi][0]);
+      const float4 gb = *reinterpret_cast<const float4*>(&sm.gpart[gi][4]);
+      const float gq[kGateParts] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+      float pre = 1.0f, all = 1.0f;  // products over the groups before this one, and over all groups
+#pragma unroll
+      for (int q2 = 0; q2 < kGateParts; ++q2) {
+        pre *= q2 < gp ? gq[q2] : 1.0f;
+        all *= gq[q2];
+      }
       if (gp == 0) sm.gcol[gi] = all;
       const int xg = h2::vw_gate_lane(gi, gp);
 #pragma unroll
@@ -459,16 +493,6 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
         sm.w_lo[o1] = (uint16_t)(lo >> 16);
       }
     }
-    // ---- partner's half of the incoming state; k-steps in order (half 0 holds j < 64)
-    uint4 s_hi[4], s_lo[4];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const uint4 oh = sm.sx[rt][1 - half_t][kk][0][lane], ol = sm.sx[rt][1 - half_t][kk][1][lane];
-      s_hi[kk] = half_t ? oh : my_hi[kk];
-      s_lo[kk] = half_t ? ol : my_lo[kk];
-      s_hi[2 + kk] = half_t ? my_hi[kk] : oh;
-      s_lo[2 + kk] = half_t ? my_lo[kk] : ol;
-    }
     // ---- the 10 causal Q K^T tiles, once per workgroup: wave w takes tiles w and w + 8
     h2_qk_tile(sm, Qs, Ks, wave, lane);
     if (wave < 2) h2_qk_tile(sm, Qs, Ks, wave + 8, lane);
@@ -485,8 +509,8 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
     {
       H2Params pp = p;
       pp.o = static_cast<char*>(p.o) + (hh * kDh + i0) * (int64_t)sizeof(Tout);
-      if (half_t == 0) h2_out<0, Tout>(pp, sm, Qs, iw, lane, s_hi, s_lo, obase_row, row_stride, valid);
-      else h2_out<1, Tout>(pp, sm, Qs, iw, lane, s_hi, s_lo, obase_row, row_stride, valid);
+      if (half_t == 0) h2_out<0, Tout>(pp, sm, iw, lane, os, obase_row, row_stride, valid);
+      else h2_out<1, Tout>(pp, sm, iw, lane, os, obase_row, row_stride, valid);
     }
 
     // ---- state update on this wave's tiles: S^T = S^T Gamma_C[i] + K^T W  (slots s = 32 ks + 8 lg + e)
