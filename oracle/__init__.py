@@ -44,8 +44,14 @@ def lib():
             build(force=False)
         L = ctypes.CDLL(_LIB_PATH)
         L.oracle_affine_scan.argtypes = [_i64, _dp, _dp, ctypes.c_double, _dp]
-        L.oracle_rglru_scan.argtypes = [_i64, _i64, _i64, _dp, _dp, _dp, _dp, ctypes.c_double, _dp, _dp, _dp]
-        L.oracle_rglru_update.argtypes = [_i64, _i64, _dp, _dp, _dp, _dp, ctypes.c_double, _dp, _dp]
+        L.oracle_gelu.argtypes = [ctypes.c_double]
+        L.oracle_gelu.restype = ctypes.c_double
+        L.oracle_rglru_scan.argtypes = [_i64, _i64, _i64, _dp, _dp, _dp, _dp, ctypes.c_double, _dp, _dp, _dp, _dp]
+        L.oracle_rglru_update.argtypes = [_i64, _i64, _dp, _dp, _dp, _dp, ctypes.c_double, _dp, _dp, _dp]
+        L.oracle_minmax_scan.argtypes = [_i64, _i64, _i64, _dp, _dp, _dp, _dp, _dp, _dp]
+        L.oracle_minmax_update.argtypes = [_i64, _i64, _dp, _dp, _dp, _dp, _dp]
+        L.oracle_causal_conv1d.argtypes = [_i64, _i64, _i64, _i64, _dp, _dp, _dp, _dp, _dp, _dp]
+        L.oracle_causal_conv1d_update.argtypes = [_i64, _i64, _i64, _dp, _dp, _dp, _dp, _dp]
         L.oracle_selective_scan.argtypes = [_i64, _i64, _i64, _i64, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
                                             ctypes.c_int, _ip, _i64, _dp, _dp, _dp]
         L.oracle_selective_update.argtypes = [_i64, _i64, _i64, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
@@ -53,7 +59,8 @@ def lib():
         L.oracle_hgrn2_scan.argtypes = [_i64, _i64, _i64, _i64, _dp, _dp, _dp, _dp, ctypes.c_double, _dp, _dp, _dp]
         L.oracle_hgrn2_update.argtypes = [_i64, _i64, _i64, _dp, _dp, _dp, _dp, ctypes.c_double, _dp, _dp]
         for fn in ("oracle_affine_scan", "oracle_rglru_scan", "oracle_rglru_update", "oracle_selective_scan",
-                   "oracle_selective_update", "oracle_hgrn2_scan", "oracle_hgrn2_update"):
+                   "oracle_selective_update", "oracle_hgrn2_scan", "oracle_hgrn2_update", "oracle_minmax_scan",
+                   "oracle_minmax_update", "oracle_causal_conv1d", "oracle_causal_conv1d_update"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -83,25 +90,29 @@ def affine_scan(a, b, h0=0.0):
     return h
 
 
-def rglru_scan(x, r_logit, i_logit, a_log, c, h0=None):
-    """Returns (y [B,L,D], h_last [B,D])."""
-    x, r_logit, i_logit, a_log, h0 = map(_f64, (x, r_logit, i_logit, a_log, h0))
+def gelu(v):
+    return lib().oracle_gelu(float(v))
+
+
+def rglru_scan(x, r_logit, i_logit, a_log, c, h0=None, gate=None):
+    """Returns (y [B,L,D], h_last [B,D]); y = gelu(gate) * h when gate is given."""
+    x, r_logit, i_logit, a_log, h0, gate = map(_f64, (x, r_logit, i_logit, a_log, h0, gate))
     B, L, D = x.shape
     y = np.empty((B, L, D))
     h_last = np.empty((B, D))
     _check(lib().oracle_rglru_scan(B, L, D, _p(x), _p(r_logit), _p(i_logit), _p(a_log), float(c), _p(h0),
-                                   _p(y), _p(h_last)), "rglru_scan")
+                                   _p(gate), _p(y), _p(h_last)), "rglru_scan")
     return y, h_last
 
 
-def rglru_update(x, r_logit, i_logit, a_log, c, state):
+def rglru_update(x, r_logit, i_logit, a_log, c, state, gate=None):
     """Returns (y [B,D], new_state [B,D]); the input state is not modified."""
-    x, r_logit, i_logit, a_log = map(_f64, (x, r_logit, i_logit, a_log))
+    x, r_logit, i_logit, a_log, gate = map(_f64, (x, r_logit, i_logit, a_log, gate))
     st = np.array(state, dtype=np.float64, copy=True, order="C")
     B, D = x.shape
     y = np.empty((B, D))
-    _check(lib().oracle_rglru_update(B, D, _p(x), _p(r_logit), _p(i_logit), _p(a_log), float(c), _p(st), _p(y)),
-           "rglru_update")
+    _check(lib().oracle_rglru_update(B, D, _p(x), _p(r_logit), _p(i_logit), _p(a_log), float(c), _p(gate),
+                                     _p(st), _p(y)), "rglru_update")
     return y, st
 
 
@@ -158,3 +169,47 @@ def hgrn2_update(q, k, v, g_logit, lower_bound, S):
     _check(lib().oracle_hgrn2_update(B, H, d, _p(q), _p(k), _p(v), _p(g_logit), float(lower_bound), _p(St), _p(o)),
            "hgrn2_update")
     return o, St
+
+
+def minmax_scan(r, s, x0=None, gate=None):
+    """Returns (y [B,L,D], x_last [B,D])."""
+    r, s, x0, gate = map(_f64, (r, s, x0, gate))
+    B, L, D = r.shape
+    y = np.empty((B, L, D))
+    x_last = np.empty((B, D))
+    _check(lib().oracle_minmax_scan(B, L, D, _p(r), _p(s), _p(x0), _p(gate), _p(y), _p(x_last)), "minmax_scan")
+    return y, x_last
+
+
+def minmax_update(r, s, state, gate=None):
+    """Returns (y [B,D], new_state [B,D]); the input state is not modified."""
+    r, s, gate = map(_f64, (r, s, gate))
+    st = np.array(state, dtype=np.float64, copy=True, order="C")
+    B, D = r.shape
+    y = np.empty((B, D))
+    _check(lib().oracle_minmax_update(B, D, _p(r), _p(s), _p(gate), _p(st), _p(y)), "minmax_update")
+    return y, st
+
+
+def causal_conv1d(x, weight, bias=None, state_in=None):
+    """Returns (y [B,L,D], state_out [B,D,W])."""
+    x, weight, bias, state_in = map(_f64, (x, weight, bias, state_in))
+    B, L, D = x.shape
+    W = weight.shape[1]
+    y = np.empty((B, L, D))
+    st = np.empty((B, D, W))
+    _check(lib().oracle_causal_conv1d(B, L, D, W, _p(x), _p(weight), _p(bias), _p(state_in), _p(y), _p(st)),
+           "causal_conv1d")
+    return y, st
+
+
+def causal_conv1d_update(x, weight, state, bias=None):
+    """Returns (y [B,D], new_state [B,D,W]); the input state is not modified."""
+    x, weight, bias = map(_f64, (x, weight, bias))
+    st = np.array(state, dtype=np.float64, copy=True, order="C")
+    B, D = x.shape
+    W = weight.shape[1]
+    y = np.empty((B, D))
+    _check(lib().oracle_causal_conv1d_update(B, D, W, _p(x), _p(weight), _p(bias), _p(st), _p(y)),
+           "causal_conv1d_update")
+    return y, st

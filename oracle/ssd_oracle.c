@@ -18,6 +18,16 @@
  *            state update S_t = diag(g_t) S_{t-1} + v_t k_t^T, forget gate
  *            sigmoid-activated and lower-bounded in [lower_bound, 1], token-by-
  *            token processing; readout o_t = S_t q_t.
+ *   [BLOCK]  lrnnx documentation, "lrnnx.models.ltv.rglru", the RG-LRU block
+ *            around the recurrence: the causal depthwise nn.Conv1d (groups =
+ *            channels, padding d_conv - 1, first L outputs kept) of forward(),
+ *            the conv_state window of step() (shift left, newest input last,
+ *            sum of window * weight plus bias), and the output multiply
+ *            gelu(gate) * y (torch's exact gelu, x * Phi(x)).
+ *   [MINMAX] minmaxrnc package diff, minmaxrnc/minmax_neuron.py and
+ *            minmax_operator.py: the MinMax recurrence
+ *            x_t = max(min(r_t, x_{t-1}), s_t) from the initial state, and the
+ *            optional output gate x_t * g_t.
  */
 #include "ssd_oracle.h"
 
@@ -51,9 +61,14 @@ static double rglru_step(double h, double x, double r_logit, double i_logit, dou
   return a_bar * h + beta * (i * x);
 }
 
+/* [BLOCK] torch's default gelu: v * Phi(v) = v/2 * (1 + erf(v / sqrt(2))). */
+static double gelu(double v) { return 0.5 * v * (1.0 + erf(v * 0.70710678118654752440)); }
+
+double oracle_gelu(double v) { return gelu(v); }
+
 int oracle_rglru_scan(int64_t B, int64_t L, int64_t D,
                       const double* x, const double* r_logit, const double* i_logit,
-                      const double* a_log, double c, const double* h0,
+                      const double* a_log, double c, const double* h0, const double* gate,
                       double* y, double* h_last) {
   if (B < 0 || L < 0 || D < 0) return 1;
   if (B * L * D > 0 && (!x || !r_logit || !i_logit || !y)) return 1;
@@ -64,7 +79,8 @@ int oracle_rglru_scan(int64_t B, int64_t L, int64_t D,
       for (int64_t t = 0; t < L; ++t) {
         int64_t idx = (b * L + t) * D + d;
         h = rglru_step(h, x[idx], r_logit[idx], i_logit[idx], a_log[d], c);
-        y[idx] = h; /* d_state = 1: the sum over the state dimension is h itself */
+        /* d_state = 1: the sum over the state dimension is h itself */
+        y[idx] = gate ? gelu(gate[idx]) * h : h;
       }
       if (h_last) h_last[b * D + d] = h;
     }
@@ -74,7 +90,7 @@ int oracle_rglru_scan(int64_t B, int64_t L, int64_t D,
 
 int oracle_rglru_update(int64_t B, int64_t D,
                         const double* x, const double* r_logit, const double* i_logit,
-                        const double* a_log, double c, double* state, double* y) {
+                        const double* a_log, double c, const double* gate, double* state, double* y) {
   if (B < 0 || D < 0) return 1;
   if (B * D > 0 && (!x || !r_logit || !i_logit || !a_log || !state || !y)) return 1;
   for (int64_t b = 0; b < B; ++b) {
@@ -82,7 +98,7 @@ int oracle_rglru_update(int64_t B, int64_t D,
       int64_t idx = b * D + d;
       double h = rglru_step(state[idx], x[idx], r_logit[idx], i_logit[idx], a_log[d], c);
       state[idx] = h;
-      y[idx] = h;
+      y[idx] = gate ? gelu(gate[idx]) * h : h;
     }
   }
   return 0;
@@ -213,6 +229,99 @@ int oracle_hgrn2_update(int64_t B, int64_t H, int64_t d,
   for (int64_t bh = 0; bh < B * H; ++bh) {
     hgrn2_step(S + bh * d * d, d, q + bh * d, k + bh * d, v + bh * d, g_logit + bh * d,
                lower_bound, o + bh * d);
+  }
+  return 0;
+}
+
+/* [MINMAX] min and max on the order of the real numbers with -0 placed below +0 (so that every
+ * result is one definite input value); a NaN operand gives NaN. */
+static double mm_min(double a, double b) {
+  if (isnan(a) || isnan(b)) return NAN;
+  if (a < b) return a;
+  if (b < a) return b;
+  return signbit(a) ? a : b;
+}
+static double mm_max(double a, double b) {
+  if (isnan(a) || isnan(b)) return NAN;
+  if (a > b) return a;
+  if (b > a) return b;
+  return signbit(a) ? b : a;
+}
+
+int oracle_minmax_scan(int64_t B, int64_t L, int64_t D, const double* r, const double* s,
+                       const double* x0, const double* gate, double* y, double* x_last) {
+  if (B < 0 || L < 0 || D < 0) return 1;
+  if (B * L * D > 0 && (!r || !s || !y)) return 1;
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t d = 0; d < D; ++d) {
+      double xv = x0 ? x0[b * D + d] : 0.0; /* the neuron's initial state is zero by default */
+      for (int64_t t = 0; t < L; ++t) {
+        int64_t idx = (b * L + t) * D + d;
+        xv = mm_max(mm_min(r[idx], xv), s[idx]);
+        y[idx] = gate ? xv * gate[idx] : xv;
+      }
+      if (x_last) x_last[b * D + d] = xv;
+    }
+  }
+  return 0;
+}
+
+int oracle_minmax_update(int64_t B, int64_t D, const double* r, const double* s, const double* gate,
+                         double* state, double* y) {
+  if (B < 0 || D < 0) return 1;
+  if (B * D > 0 && (!r || !s || !state || !y)) return 1;
+  for (int64_t idx = 0; idx < B * D; ++idx) {
+    double xv = mm_max(mm_min(r[idx], state[idx]), s[idx]);
+    state[idx] = xv;
+    y[idx] = gate ? xv * gate[idx] : xv;
+  }
+  return 0;
+}
+
+/* [BLOCK] input at time tau of channel (b, d): x itself for 0 <= tau < L, else the carried window
+ * (entry W + tau holds time tau, for -W <= tau < 0), else zero. */
+static double conv_input(int64_t b, int64_t d, int64_t tau, int64_t L, int64_t D, int64_t W,
+                         const double* x, const double* state_in) {
+  if (tau >= 0 && tau < L) return x[(b * L + tau) * D + d];
+  if (tau < 0 && tau >= -W && state_in) return state_in[(b * D + d) * W + (W + tau)];
+  return 0.0;
+}
+
+int oracle_causal_conv1d(int64_t B, int64_t L, int64_t D, int64_t W, const double* x,
+                         const double* weight, const double* bias, const double* state_in,
+                         double* y, double* state_out) {
+  if (B < 0 || L < 0 || D < 0 || W < 1) return 1;
+  if (B * L * D > 0 && (!x || !y)) return 1;
+  if (D > 0 && !weight) return 1;
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t d = 0; d < D; ++d) {
+      for (int64_t t = 0; t < L; ++t) {
+        double acc = bias ? bias[d] : 0.0;
+        for (int64_t k = 0; k < W; ++k)
+          acc += weight[d * W + k] * conv_input(b, d, t - (W - 1) + k, L, D, W, x, state_in);
+        y[(b * L + t) * D + d] = acc;
+      }
+      if (state_out)
+        for (int64_t k = 0; k < W; ++k)
+          state_out[(b * D + d) * W + k] = conv_input(b, d, L - W + k, L, D, W, x, state_in);
+    }
+  }
+  return 0;
+}
+
+int oracle_causal_conv1d_update(int64_t B, int64_t D, int64_t W, const double* x, const double* weight,
+                                const double* bias, double* state, double* y) {
+  if (B < 0 || D < 0 || W < 1) return 1;
+  if (B * D > 0 && (!x || !weight || !state || !y)) return 1;
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t d = 0; d < D; ++d) {
+      double* win = state + (b * D + d) * W;
+      for (int64_t k = 0; k + 1 < W; ++k) win[k] = win[k + 1];
+      win[W - 1] = x[b * D + d];
+      double acc = bias ? bias[d] : 0.0;
+      for (int64_t k = 0; k < W; ++k) acc += weight[d * W + k] * win[k];
+      y[b * D + d] = acc;
+    }
   }
   return 0;
 }

@@ -31,20 +31,26 @@ extern "C" {
  * starting from h_{-1} = h0; writes h[t].  The common core of all three forms. */
 int oracle_affine_scan(int64_t L, const double* a, const double* b, double h0, double* h);
 
+/* gelu(v) = v * Phi(v) = v/2 * (1 + erf(v / sqrt(2))) (torch's default, exact form). */
+double oracle_gelu(double v);
+
 /* RG-LRU scan (lrnnx RGLRU block; recurrence of its step() fallback branch).
- * x, r_logit, i_logit, y: [B,L,D]; a_log: [D]; h0, h_last: [B,D] or NULL.
+ * x, r_logit, i_logit, y: [B,L,D]; a_log: [D]; h0, h_last: [B,D] or NULL;
+ * gate: [B,L,D] or NULL (the block's output multiply).
  *   r = sigmoid(r_logit), i = sigmoid(i_logit), lambda = c * r * a_log[d],
  *   a = exp(lambda), beta = sqrt(1 - a^2) (as sqrt(-expm1(2 lambda))),
- *   h = a*h + beta*(i*x), y = h (sum over the single state). */
+ *   h = a*h + beta*(i*x), y = h (sum over the single state), times gelu(gate)
+ *   when gate is given; h_last is the ungated state. */
 int oracle_rglru_scan(int64_t B, int64_t L, int64_t D,
                       const double* x, const double* r_logit, const double* i_logit,
-                      const double* a_log, double c, const double* h0,
+                      const double* a_log, double c, const double* h0, const double* gate,
                       double* y, double* h_last);
 
-/* One RG-LRU decode step.  x, r_logit, i_logit, y: [B,D]; state: [B,D] in/out. */
+/* One RG-LRU decode step.  x, r_logit, i_logit, gate, y: [B,D] (gate may be
+ * NULL); state: [B,D] in/out. */
 int oracle_rglru_update(int64_t B, int64_t D,
                         const double* x, const double* r_logit, const double* i_logit,
-                        const double* a_log, double c, double* state, double* y);
+                        const double* a_log, double c, const double* gate, double* state, double* y);
 
 /* Multi-scale selective scan (cortexnet MultiScaleSSM: forward and
  * _selective_scan).
@@ -88,6 +94,35 @@ int oracle_hgrn2_scan(int64_t B, int64_t L, int64_t H, int64_t d,
 int oracle_hgrn2_update(int64_t B, int64_t H, int64_t d,
                         const double* q, const double* k, const double* v,
                         const double* g_logit, double lower_bound, double* S, double* o);
+
+/* MinMax recurrence (minmaxrnc MinMaxNeuron): x_t = max(min(r_t, x_{t-1}), s_t)
+ * from x0 (NULL = zero).  min / max order -0 below +0 and return NaN when an
+ * operand is NaN, so every state is one definite input value.
+ *   r, s, gate, y: [B,L,D] (gate NULL = none; else y = x * gate, else y = x);
+ *   x0, x_last: [B,D] or NULL. */
+int oracle_minmax_scan(int64_t B, int64_t L, int64_t D, const double* r, const double* s,
+                       const double* x0, const double* gate, double* y, double* x_last);
+
+/* One MinMax step.  r, s, gate, y: [B,D] (gate may be NULL); state: [B,D] in/out. */
+int oracle_minmax_update(int64_t B, int64_t D, const double* r, const double* s, const double* gate,
+                         double* state, double* y);
+
+/* Causal depthwise convolution of the RG-LRU block (nn.Conv1d, groups = D,
+ * kernel W, padding W-1, first L outputs):
+ *   y[b,t,d] = bias[d] + sum_{k<W} weight[d][k] * x[b, t-(W-1)+k, d].
+ * Inputs before the sequence come from state_in [B,D,W] (entry W+tau holds
+ * time tau < 0) or are zero when it is NULL.  state_out [B,D,W] (or NULL)
+ * receives the last W inputs (times L-W .. L-1, from state_in or zero where
+ * negative).  x, y: [B,L,D]; weight: [D,W]; bias: [D] or NULL. */
+int oracle_causal_conv1d(int64_t B, int64_t L, int64_t D, int64_t W, const double* x,
+                         const double* weight, const double* bias, const double* state_in,
+                         double* y, double* state_out);
+
+/* One decode step of the convolution (the block's step()): the window
+ * state [B,D,W] shifts left by one, x [B,D] enters last, and
+ * y = bias + sum_k weight[d][k] * window[k]. */
+int oracle_causal_conv1d_update(int64_t B, int64_t D, int64_t W, const double* x, const double* weight,
+                                const double* bias, double* state, double* y);
 
 #ifdef __cplusplus
 }
