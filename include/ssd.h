@@ -5,6 +5,8 @@
  * single-step decode update:
  *
  *   RG-LRU        state size 1 per channel          ssd_rglru_scan / ssd_rglru_update
+ *   MinMax        state size 1 per channel          ssd_minmax_scan / ssd_minmax_update
+ *   causal conv   depthwise, width W <= 4           ssd_causal_conv1d / ssd_causal_conv1d_update
  *   selective     N <= 16 states per channel        ssd_selective_scan / ssd_selective_update
  *   HGRN2         d x d matrix state per head       ssd_hgrn2_scan / ssd_hgrn2_update
  *
@@ -66,29 +68,85 @@ int ssd_version(void);
  * computation and RGLRU.step recurrence):  for each batch b, channel d and step t
  *     r = sigmoid(r_logit), i = sigmoid(i_logit), log a_t = c * r * a_log[d],
  *     h_t = a_t * h_{t-1} + sqrt(1 - a_t^2) * (i * x),     y_t = h_t,
- * starting from h0 (or 0).  The base a = exp(a_log) lies in (0, 1) for a_log < 0.
+ * starting from h0 (or 0).  The base a = exp(a_log) lies in (0, 1) for a_log < 0.  With a gate,
+ * y_t = gelu(gate_t) * h_t: the block's output multiply (gelu of its gate projection times the
+ * recurrence output), with torch's exact gelu v * Phi(v).
  *   x, r_logit, i_logit : [B, L, D] activations (in dtype)
  *   a_log               : [D] fp32          c : finite scalar (8 in the Griffin block)
  *   h0                  : [B, D] fp32 or NULL (= zeros)
+ *   gate                : [B, L, D] (in dtype) or NULL (= no output multiply)
  *   y                   : [B, L, D] (out dtype)
- *   h_last              : [B, D] fp32 or NULL; receives h_{L-1} (h0 when L = 0)
+ *   h_last              : [B, D] fp32 or NULL; receives h_{L-1} (h0 when L = 0), never gated
  * Errors: SSD_ERR_NULL (x, r_logit, i_logit, a_log, y when B*L*D > 0), SSD_ERR_SHAPE (negative
  * size, D >= 2^22, or B * ceil(L/64) * ceil(D/64) >= 2^31), SSD_ERR_DTYPE, SSD_ERR_ALIGN,
  * SSD_ERR_VALUE (c not finite), SSD_ERR_ALIAS.
  * ------------------------------------------------------------------------------------------- */
 int ssd_rglru_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype,
                    const void* x, const void* r_logit, const void* i_logit,
-                   const float* a_log, float c, const float* h0,
+                   const float* a_log, float c, const float* h0, const void* gate,
                    void* y, float* h_last, void* stream);
 
 /* One RG-LRU decode step (RGLRU.step: single token, state carried by the caller).
- *   x, r_logit, i_logit : [B, D] (in dtype);  a_log : [D] fp32
+ *   x, r_logit, i_logit : [B, D] (in dtype);  a_log : [D] fp32;  gate : [B, D] or NULL
  *   state               : [B, D] fp32, read then overwritten with h_t (in place)
- *   y                   : [B, D] (out dtype), y = h_t
+ *   y                   : [B, D] (out dtype), y = h_t, or gelu(gate) * h_t
  * Errors as ssd_rglru_scan; y must not overlap state. */
 int ssd_rglru_update(int64_t B, int64_t D, int in_dtype, int out_dtype,
                      const void* x, const void* r_logit, const void* i_logit,
-                     const float* a_log, float c, float* state, void* y, void* stream);
+                     const float* a_log, float c, const void* gate, float* state, void* y,
+                     void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * MinMax scan.  Defined by the minmaxrnc package (minmax_neuron.py, MinMaxNeuron: the state update
+ * of its docstring and forward(); minmax_operator.py: the operator and its composition):  for each
+ * batch b, channel d and step t
+ *     x_t = max(min(r_t, x_{t-1}), s_t),      y_t = x_t, or x_t * gate_t with a gate,
+ * starting from x0 (or 0, the neuron's default initial state).  min and max order -0 below +0 and
+ * return NaN when either operand is NaN, so every state is exactly one input value and the result
+ * is identical bit for bit to the sequential loop, however the scan is split.
+ *   r, s                : [B, L, D] (in dtype), the per-step upper and lower clamps
+ *   x0                  : [B, D] fp32 or NULL (= zeros)
+ *   gate                : [B, L, D] (in dtype) or NULL (the neuron's output gate values)
+ *   y                   : [B, L, D] (out dtype)
+ *   x_last              : [B, D] fp32 or NULL; receives x_{L-1} (x0 when L = 0), never gated
+ * Errors: as ssd_rglru_scan (no scalar arguments).
+ * ------------------------------------------------------------------------------------------- */
+int ssd_minmax_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype,
+                    const void* r, const void* s, const float* x0, const void* gate,
+                    void* y, float* x_last, void* stream);
+
+/* One MinMax decode step.  r, s, gate : [B, D] (gate may be NULL); state : [B, D] fp32 in/out;
+ * y : [B, D].  Errors as ssd_minmax_scan; y must not overlap state. */
+int ssd_minmax_update(int64_t B, int64_t D, int in_dtype, int out_dtype,
+                      const void* r, const void* s, const void* gate, float* state, void* y,
+                      void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Causal depthwise convolution in front of the RG-LRU recurrence.  Defined by the lrnnx
+ * documentation, "lrnnx.models.ltv.rglru": the block's nn.Conv1d (groups = channels, kernel
+ * d_conv = W, padding W - 1, first L outputs kept) and the conv_state window of its step():
+ *     y[b, t, d] = bias[d] + sum_{k < W} weight[d][k] * x[b, t - (W-1) + k, d].
+ * Inputs before t = 0 come from state_in (entry W + tau of a channel's window holds time tau < 0)
+ * or are zero when state_in is NULL.  state_out receives the window after the sequence: the last
+ * W inputs (times L-W .. L-1; from state_in or zero where negative), ready for
+ * ssd_causal_conv1d_update or a following ssd_causal_conv1d call.
+ *   x, y                : [B, L, D] (in / out dtype)
+ *   weight              : [D, W] fp32 (nn.Conv1d's [D, 1, W] weight)     bias : [D] fp32 or NULL
+ *   state_in, state_out : [B, D, W] fp32 or NULL; they must not overlap
+ * Errors: SSD_ERR_NULL (x, y when B*L*D > 0; weight when B*D > 0), SSD_ERR_SHAPE (negative size,
+ * W outside 1 .. 4, D >= 2^22, B * ceil(L/64) * ceil(D/64) >= 2^31), SSD_ERR_DTYPE,
+ * SSD_ERR_ALIGN, SSD_ERR_ALIAS.
+ * ------------------------------------------------------------------------------------------- */
+int ssd_causal_conv1d(int64_t B, int64_t L, int64_t D, int64_t W, int in_dtype, int out_dtype,
+                      const void* x, const float* weight, const float* bias, const float* state_in,
+                      void* y, float* state_out, void* stream);
+
+/* One convolution decode step (the block's step()): state [B, D, W] fp32 shifts left by one, x
+ * [B, D] enters last, y [B, D] = bias + sum_k weight[d][k] * state[b][d][k].  In place.
+ * Errors as ssd_causal_conv1d; y must not overlap state. */
+int ssd_causal_conv1d_update(int64_t B, int64_t D, int64_t W, int in_dtype, int out_dtype,
+                             const void* x, const float* weight, const float* bias, float* state,
+                             void* y, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Multi-scale selective scan.  Defined by the cortexnet 3.2.1 package, cortexnet/ssm.py,

@@ -8,7 +8,8 @@ or eager fallback: importing works without a GPU, but each call raises if the
 library is not built or no GPU is present.
 
 Entry points (same names as the C ABI without the ``ssd_`` prefix):
-    rglru_scan, rglru_update, selective_scan, selective_update, hgrn2_scan, hgrn2_update
+    rglru_scan, rglru_update, selective_scan, selective_update, hgrn2_scan, hgrn2_update,
+    minmax_scan, minmax_update, causal_conv1d, causal_conv1d_update
 """
 from __future__ import annotations
 
@@ -27,7 +28,8 @@ STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_
 
 # Every symbol include/ssd.h declares.
 EXPORTS = ("ssd_status_str", "ssd_last_error", "ssd_version", "ssd_rglru_scan", "ssd_rglru_update",
-           "ssd_selective_scan", "ssd_selective_update", "ssd_hgrn2_scan", "ssd_hgrn2_update")
+           "ssd_selective_scan", "ssd_selective_update", "ssd_hgrn2_scan", "ssd_hgrn2_update", "ssd_minmax_scan",
+           "ssd_minmax_update", "ssd_causal_conv1d", "ssd_causal_conv1d_update")
 
 
 class SSDError(RuntimeError):
@@ -59,9 +61,15 @@ def lib() -> ctypes.CDLL:
         L.ssd_last_error.argtypes = []
         L.ssd_version.restype = ctypes.c_int
         L.ssd_rglru_scan.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _fp, ctypes.c_float,
-                                     _fp, _vp, _fp, _vp]
-        L.ssd_rglru_update.argtypes = [_i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _fp, ctypes.c_float, _fp,
-                                       _vp, _vp]
+                                     _fp, _vp, _vp, _fp, _vp]
+        L.ssd_rglru_update.argtypes = [_i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _fp, ctypes.c_float, _vp,
+                                       _fp, _vp, _vp]
+        L.ssd_minmax_scan.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _fp, _vp, _vp, _fp, _vp]
+        L.ssd_minmax_update.argtypes = [_i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _fp, _vp, _vp]
+        L.ssd_causal_conv1d.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _fp, _fp, _fp, _vp,
+                                        _fp, _vp]
+        L.ssd_causal_conv1d_update.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _fp, _fp, _fp, _vp,
+                                               _vp]
         L.ssd_selective_scan.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _fp, _vp, _vp,
                                          _fp, _vp, _fp, ctypes.c_int, _vp, _i64, _fp, _vp, _fp, _vp]
         L.ssd_selective_update.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _fp, _vp, _vp, _fp,
@@ -148,33 +156,101 @@ def _act(ts, names):
 
 # ----------------------------------------------------------------------------- RG-LRU
 def rglru_scan(x, r_logit, i_logit, a_log, c: float = 8.0, h0=None, return_last_state: bool = False,
-               out_dtype=None):
-    """RG-LRU scan over [B, L, D] (see ``ssd_rglru_scan``).  Returns y, or (y, h_last)."""
+               out_dtype=None, gate=None):
+    """RG-LRU scan over [B, L, D] (see ``ssd_rglru_scan``); with ``gate``, y = gelu(gate) * h.
+    Returns y, or (y, h_last)."""
     torch = _torch()
     B, L, D = x.shape
-    code = _act([x, r_logit, i_logit], ["x", "r_logit", "i_logit"])
+    code = _act([x, r_logit, i_logit, gate], ["x", "r_logit", "i_logit", "gate"])
     oc = _out_code(out_dtype)
     y = torch.empty((B, L, D), device=x.device, dtype=torch.bfloat16 if oc == SSD_BF16 else torch.float32)
     h_last = torch.empty((B, D), device=x.device, dtype=torch.float32) if return_last_state else None
     st = lib().ssd_rglru_scan(B, L, D, code, oc, _dev(x, "x"), _dev(r_logit, "r_logit", x.shape),
                               _dev(i_logit, "i_logit", x.shape), _dev(a_log, "a_log", (D,), torch.float32),
-                              float(c), _dev(h0, "h0", (B, D), torch.float32), _dev(y, "y"),
-                              _dev(h_last, "h_last"), _stream(x.device))
+                              float(c), _dev(h0, "h0", (B, D), torch.float32), _dev(gate, "gate", x.shape),
+                              _dev(y, "y"), _dev(h_last, "h_last"), _stream(x.device))
     _raise(st, "rglru_scan")
     return (y, h_last) if return_last_state else y
 
 
-def rglru_update(x, r_logit, i_logit, a_log, c: float, state, out_dtype=None):
-    """One decode step; ``state`` [B, D] fp32 is updated in place.  Returns y [B, D]."""
+def rglru_update(x, r_logit, i_logit, a_log, c: float, state, out_dtype=None, gate=None):
+    """One decode step; ``state`` [B, D] fp32 is updated in place.  Returns y [B, D]
+    (gelu(gate) * h with a gate)."""
     torch = _torch()
     B, D = x.shape
-    code = _act([x, r_logit, i_logit], ["x", "r_logit", "i_logit"])
+    code = _act([x, r_logit, i_logit, gate], ["x", "r_logit", "i_logit", "gate"])
     oc = _out_code(out_dtype)
     y = torch.empty((B, D), device=x.device, dtype=torch.bfloat16 if oc == SSD_BF16 else torch.float32)
     st = lib().ssd_rglru_update(B, D, code, oc, _dev(x, "x"), _dev(r_logit, "r_logit", x.shape),
                                 _dev(i_logit, "i_logit", x.shape), _dev(a_log, "a_log", (D,), torch.float32),
-                                float(c), _dev(state, "state", (B, D), torch.float32), _dev(y, "y"), _stream(x.device))
+                                float(c), _dev(gate, "gate", x.shape), _dev(state, "state", (B, D), torch.float32),
+                                _dev(y, "y"), _stream(x.device))
     _raise(st, "rglru_update")
+    return y
+
+
+# ----------------------------------------------------------------------------- MinMax
+def minmax_scan(r, s, x0=None, gate=None, return_last_state: bool = False, out_dtype=None):
+    """MinMax scan x_t = max(min(r_t, x_{t-1}), s_t) over [B, L, D] (see ``ssd_minmax_scan``);
+    with ``gate``, y = x * gate.  Returns y, or (y, x_last)."""
+    torch = _torch()
+    B, L, D = r.shape
+    code = _act([r, s, gate], ["r", "s", "gate"])
+    oc = _out_code(out_dtype)
+    y = torch.empty((B, L, D), device=r.device, dtype=torch.bfloat16 if oc == SSD_BF16 else torch.float32)
+    x_last = torch.empty((B, D), device=r.device, dtype=torch.float32) if return_last_state else None
+    st = lib().ssd_minmax_scan(B, L, D, code, oc, _dev(r, "r"), _dev(s, "s", r.shape),
+                               _dev(x0, "x0", (B, D), torch.float32), _dev(gate, "gate", r.shape), _dev(y, "y"),
+                               _dev(x_last, "x_last"), _stream(r.device))
+    _raise(st, "minmax_scan")
+    return (y, x_last) if return_last_state else y
+
+
+def minmax_update(r, s, state, gate=None, out_dtype=None):
+    """One MinMax decode step; ``state`` [B, D] fp32 is updated in place.  Returns y [B, D]."""
+    torch = _torch()
+    B, D = r.shape
+    code = _act([r, s, gate], ["r", "s", "gate"])
+    oc = _out_code(out_dtype)
+    y = torch.empty((B, D), device=r.device, dtype=torch.bfloat16 if oc == SSD_BF16 else torch.float32)
+    st = lib().ssd_minmax_update(B, D, code, oc, _dev(r, "r"), _dev(s, "s", r.shape), _dev(gate, "gate", r.shape),
+                                 _dev(state, "state", (B, D), torch.float32), _dev(y, "y"), _stream(r.device))
+    _raise(st, "minmax_update")
+    return y
+
+
+# ----------------------------------------------------------------------------- causal conv1d
+def causal_conv1d(x, weight, bias=None, state_in=None, return_state: bool = False, out_dtype=None):
+    """Causal depthwise convolution over [B, L, D] with weight [D, W] (see ``ssd_causal_conv1d``).
+    ``state_in`` [B, D, W] fp32 supplies the inputs before t = 0.  Returns y, or (y, state_out)."""
+    torch = _torch()
+    B, L, D = x.shape
+    W = int(weight.shape[1]) if weight.dim() == 2 else -1
+    code = _act([x], ["x"])
+    oc = _out_code(out_dtype)
+    y = torch.empty((B, L, D), device=x.device, dtype=torch.bfloat16 if oc == SSD_BF16 else torch.float32)
+    st_out = torch.empty((B, D, max(W, 0)), device=x.device, dtype=torch.float32) if return_state else None
+    st = lib().ssd_causal_conv1d(B, L, D, W, code, oc, _dev(x, "x"), _dev(weight, "weight", (D, W), torch.float32),
+                                 _dev(bias, "bias", (D,), torch.float32),
+                                 _dev(state_in, "state_in", (B, D, W), torch.float32), _dev(y, "y"),
+                                 _dev(st_out, "state_out"), _stream(x.device))
+    _raise(st, "causal_conv1d")
+    return (y, st_out) if return_state else y
+
+
+def causal_conv1d_update(x, weight, state, bias=None, out_dtype=None):
+    """One convolution decode step; ``state`` [B, D, W] fp32 is updated in place.  Returns y [B, D]."""
+    torch = _torch()
+    B, D = x.shape
+    W = int(weight.shape[1]) if weight.dim() == 2 else -1
+    code = _act([x], ["x"])
+    oc = _out_code(out_dtype)
+    y = torch.empty((B, D), device=x.device, dtype=torch.bfloat16 if oc == SSD_BF16 else torch.float32)
+    st = lib().ssd_causal_conv1d_update(B, D, W, code, oc, _dev(x, "x"), _dev(weight, "weight", (D, W), torch.float32),
+                                        _dev(bias, "bias", (D,), torch.float32),
+                                        _dev(state, "state", (B, D, W), torch.float32), _dev(y, "y"),
+                                        _stream(x.device))
+    _raise(st, "causal_conv1d_update")
     return y
 
 
@@ -273,5 +349,6 @@ def hgrn2_update(q, k, v, g_logit, lower_bound: float, S, out_dtype=None):
     return o
 
 
-__all__ = ["rglru_scan", "rglru_update", "selective_scan", "selective_update", "hgrn2_scan", "hgrn2_update", "lib",
-           "LIB_PATH", "EXPORTS", "SSDError", "SSDValueError", "SSD_F32", "SSD_BF16"]
+__all__ = ["rglru_scan", "rglru_update", "selective_scan", "selective_update", "hgrn2_scan", "hgrn2_update",
+           "minmax_scan", "minmax_update", "causal_conv1d", "causal_conv1d_update", "lib", "LIB_PATH", "EXPORTS",
+           "SSDError", "SSDValueError", "SSD_F32", "SSD_BF16"]

@@ -33,7 +33,9 @@ int ok() {
 // ------------------------------------------------------------------ scratch buffers
 // One buffer per (device, stream, purpose), allocated zero-filled, grown on demand, kept until
 // process exit.  Purposes are kept apart so that one kernel family never reads another's data.
-enum ScratchKind { kScratchRglru = 0, kScratchSelective = 1 };
+// RG-LRU and MinMax share a kind: their launches use the same epoch-tagged lookback protocol, so
+// words left by one never validate for the next launch on the stream.
+enum ScratchKind { kScratchScan1 = 0, kScratchSelective = 1 };
 
 struct ScratchBuf {
   void* ptr = nullptr;
@@ -157,8 +159,8 @@ int ssd_version(void) { return 100; }
 
 // ============================================================================ RG-LRU
 int ssd_rglru_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype, const void* x, const void* r_logit,
-                   const void* i_logit, const float* a_log, float c, const float* h0, void* y, float* h_last,
-                   void* stream) {
+                   const void* i_logit, const float* a_log, float c, const float* h0, const void* gate, void* y,
+                   float* h_last, void* stream) {
   SSD_TRY(check_dtypes(in_dtype, out_dtype));
   if (B < 0 || L < 0 || D < 0) return fail(SSD_ERR_SHAPE, "negative size");
   if (too_big({B, L, D}) || D >= (int64_t)1 << 22 || B * ((L + 63) / 64) * ((D + 63) / 64) >= (int64_t)1 << 31)
@@ -170,7 +172,7 @@ int ssd_rglru_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype,
   const size_t ab = (size_t)nact * esize(in_dtype), yb = (size_t)nact * esize(out_dtype);
   const size_t sb = (size_t)(B * D) * 4;
   std::vector<Span> ins = {{"x", x, ab}, {"r_logit", r_logit, ab}, {"i_logit", i_logit, ab},
-                           {"a_log", a_log, (size_t)D * 4}, {"h0", h0, sb}};
+                           {"a_log", a_log, (size_t)D * 4}, {"h0", h0, sb}, {"gate", gate, ab}};
   std::vector<Span> outs = {{"y", y, yb}, {"h_last", h_last, sb}};
   std::vector<Span> all = ins;
   all.insert(all.end(), outs.begin(), outs.end());
@@ -179,14 +181,15 @@ int ssd_rglru_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype,
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (B * D == 0) return ok();
   if (L == 0) return hip_status(ssd::launch_copy_or_zero(h_last, h0, B * D, s), "rglru_scan");
-  ssd::RglruScanArgs a{B, L, D, in_dtype == SSD_BF16, out_dtype == SSD_BF16, x, r_logit, i_logit, a_log, c, h0, y, h_last,
-                       nullptr};
-  SSD_TRY(get_scratch(stream, kScratchRglru, ssd::rglru_scan_scratch_bytes(B, L, D), &a.scratch));
+  ssd::RglruScanArgs a{B, L, D, in_dtype == SSD_BF16, out_dtype == SSD_BF16, x, r_logit, i_logit, a_log, c, h0, gate,
+                       y, h_last, nullptr};
+  SSD_TRY(get_scratch(stream, kScratchScan1, ssd::scan1_scratch_bytes(B, L, D), &a.scratch));
   return hip_status(ssd::launch_rglru_scan(a, s), "rglru_scan launch");
 }
 
 int ssd_rglru_update(int64_t B, int64_t D, int in_dtype, int out_dtype, const void* x, const void* r_logit,
-                     const void* i_logit, const float* a_log, float c, float* state, void* y, void* stream) {
+                     const void* i_logit, const float* a_log, float c, const void* gate, float* state, void* y,
+                     void* stream) {
   SSD_TRY(check_dtypes(in_dtype, out_dtype));
   if (B < 0 || D < 0) return fail(SSD_ERR_SHAPE, "negative size");
   if (too_big({B, D}) || B * D >= (int64_t)1 << 38) return fail(SSD_ERR_SHAPE, "problem too large");
@@ -196,15 +199,107 @@ int ssd_rglru_update(int64_t B, int64_t D, int in_dtype, int out_dtype, const vo
     return fail(SSD_ERR_NULL, "x, r_logit, i_logit, a_log, state and y are required");
   const size_t ab = (size_t)n * esize(in_dtype);
   std::vector<Span> ins = {{"x", x, ab}, {"r_logit", r_logit, ab}, {"i_logit", i_logit, ab},
-                           {"a_log", a_log, (size_t)D * 4}};
+                           {"a_log", a_log, (size_t)D * 4}, {"gate", gate, ab}};
   std::vector<Span> outs = {{"y", y, (size_t)n * esize(out_dtype)}, {"state", state, (size_t)n * 4}};
   std::vector<Span> all = ins;
   all.insert(all.end(), outs.begin(), outs.end());
   SSD_TRY(check_align(all));
   SSD_TRY(check_alias(outs, ins));
   if (n == 0) return ok();
-  ssd::RglruUpdateArgs a{B, D, in_dtype == SSD_BF16, out_dtype == SSD_BF16, x, r_logit, i_logit, a_log, c, state, y};
+  ssd::RglruUpdateArgs a{B, D, in_dtype == SSD_BF16, out_dtype == SSD_BF16, x, r_logit, i_logit, a_log, c, gate, state, y};
   return hip_status(ssd::launch_rglru_update(a, static_cast<hipStream_t>(stream)), "rglru_update launch");
+}
+
+// ============================================================================ MinMax
+int ssd_minmax_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype, const void* r, const void* s_in,
+                    const float* x0, const void* gate, void* y, float* x_last, void* stream) {
+  SSD_TRY(check_dtypes(in_dtype, out_dtype));
+  if (B < 0 || L < 0 || D < 0) return fail(SSD_ERR_SHAPE, "negative size");
+  if (too_big({B, L, D}) || D >= (int64_t)1 << 22 || B * ((L + 63) / 64) * ((D + 63) / 64) >= (int64_t)1 << 31)
+    return fail(SSD_ERR_SHAPE, "problem too large");
+  const int64_t nact = B * L * D;
+  if (nact > 0 && (!r || !s_in || !y)) return fail(SSD_ERR_NULL, "r, s and y are required");
+  const size_t ab = (size_t)nact * esize(in_dtype), yb = (size_t)nact * esize(out_dtype);
+  const size_t sb = (size_t)(B * D) * 4;
+  std::vector<Span> ins = {{"r", r, ab}, {"s", s_in, ab}, {"x0", x0, sb}, {"gate", gate, ab}};
+  std::vector<Span> outs = {{"y", y, yb}, {"x_last", x_last, sb}};
+  std::vector<Span> all = ins;
+  all.insert(all.end(), outs.begin(), outs.end());
+  SSD_TRY(check_align(all));
+  SSD_TRY(check_alias(outs, ins));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (B * D == 0) return ok();
+  if (L == 0) return hip_status(ssd::launch_copy_or_zero(x_last, x0, B * D, st), "minmax_scan");
+  ssd::MinmaxScanArgs a{B, L, D, in_dtype == SSD_BF16, out_dtype == SSD_BF16, r, s_in, x0, gate, y, x_last, nullptr};
+  SSD_TRY(get_scratch(stream, kScratchScan1, ssd::scan1_scratch_bytes(B, L, D), &a.scratch));
+  return hip_status(ssd::launch_minmax_scan(a, st), "minmax_scan launch");
+}
+
+int ssd_minmax_update(int64_t B, int64_t D, int in_dtype, int out_dtype, const void* r, const void* s_in,
+                      const void* gate, float* state, void* y, void* stream) {
+  SSD_TRY(check_dtypes(in_dtype, out_dtype));
+  if (B < 0 || D < 0) return fail(SSD_ERR_SHAPE, "negative size");
+  if (too_big({B, D}) || B * D >= (int64_t)1 << 38) return fail(SSD_ERR_SHAPE, "problem too large");
+  const int64_t n = B * D;
+  if (n > 0 && (!r || !s_in || !state || !y)) return fail(SSD_ERR_NULL, "r, s, state and y are required");
+  const size_t ab = (size_t)n * esize(in_dtype);
+  std::vector<Span> ins = {{"r", r, ab}, {"s", s_in, ab}, {"gate", gate, ab}};
+  std::vector<Span> outs = {{"y", y, (size_t)n * esize(out_dtype)}, {"state", state, (size_t)n * 4}};
+  std::vector<Span> all = ins;
+  all.insert(all.end(), outs.begin(), outs.end());
+  SSD_TRY(check_align(all));
+  SSD_TRY(check_alias(outs, ins));
+  if (n == 0) return ok();
+  ssd::MinmaxUpdateArgs a{B, D, in_dtype == SSD_BF16, out_dtype == SSD_BF16, r, s_in, gate, state, y};
+  return hip_status(ssd::launch_minmax_update(a, static_cast<hipStream_t>(stream)), "minmax_update launch");
+}
+
+// ============================================================================ causal conv1d
+int ssd_causal_conv1d(int64_t B, int64_t L, int64_t D, int64_t W, int in_dtype, int out_dtype, const void* x,
+                      const float* weight, const float* bias, const float* state_in, void* y, float* state_out,
+                      void* stream) {
+  SSD_TRY(check_dtypes(in_dtype, out_dtype));
+  if (B < 0 || L < 0 || D < 0) return fail(SSD_ERR_SHAPE, "negative size");
+  if (W < 1 || W > 4) return fail(SSD_ERR_SHAPE, "kernel width W must be 1 .. 4");
+  if (too_big({B, L, D}) || D >= (int64_t)1 << 22 || B * ((L + 63) / 64) * ((D + 63) / 64) >= (int64_t)1 << 31)
+    return fail(SSD_ERR_SHAPE, "problem too large");
+  const int64_t nact = B * L * D;
+  if (nact > 0 && (!x || !y)) return fail(SSD_ERR_NULL, "x and y are required");
+  if (B * D > 0 && !weight) return fail(SSD_ERR_NULL, "weight is required");
+  const size_t xb = (size_t)nact * esize(in_dtype), yb = (size_t)nact * esize(out_dtype);
+  const size_t sb = (size_t)(B * D * W) * 4;
+  std::vector<Span> ins = {{"x", x, xb}, {"weight", weight, (size_t)(D * W) * 4}, {"bias", bias, (size_t)D * 4},
+                           {"state_in", state_in, sb}};
+  std::vector<Span> outs = {{"y", y, yb}, {"state_out", state_out, sb}};
+  std::vector<Span> all = ins;
+  all.insert(all.end(), outs.begin(), outs.end());
+  SSD_TRY(check_align(all));
+  SSD_TRY(check_alias(outs, ins));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (B * D == 0) return ok();
+  if (L == 0) return hip_status(ssd::launch_copy_or_zero(state_out, state_in, B * D * W, st), "causal_conv1d");
+  ssd::Conv1dArgs a{B, L, D, W, in_dtype == SSD_BF16, out_dtype == SSD_BF16, x, weight, bias, state_in, y, state_out};
+  return hip_status(ssd::launch_causal_conv1d(a, st), "causal_conv1d launch");
+}
+
+int ssd_causal_conv1d_update(int64_t B, int64_t D, int64_t W, int in_dtype, int out_dtype, const void* x,
+                             const float* weight, const float* bias, float* state, void* y, void* stream) {
+  SSD_TRY(check_dtypes(in_dtype, out_dtype));
+  if (B < 0 || D < 0) return fail(SSD_ERR_SHAPE, "negative size");
+  if (W < 1 || W > 4) return fail(SSD_ERR_SHAPE, "kernel width W must be 1 .. 4");
+  if (too_big({B, D, W}) || B * D >= (int64_t)1 << 38) return fail(SSD_ERR_SHAPE, "problem too large");
+  const int64_t n = B * D;
+  if (n > 0 && (!x || !weight || !state || !y)) return fail(SSD_ERR_NULL, "x, weight, state and y are required");
+  std::vector<Span> ins = {{"x", x, (size_t)n * esize(in_dtype)}, {"weight", weight, (size_t)(D * W) * 4},
+                           {"bias", bias, (size_t)D * 4}};
+  std::vector<Span> outs = {{"y", y, (size_t)n * esize(out_dtype)}, {"state", state, (size_t)(n * W) * 4}};
+  std::vector<Span> all = ins;
+  all.insert(all.end(), outs.begin(), outs.end());
+  SSD_TRY(check_align(all));
+  SSD_TRY(check_alias(outs, ins));
+  if (n == 0) return ok();
+  ssd::Conv1dUpdateArgs a{B, D, W, in_dtype == SSD_BF16, out_dtype == SSD_BF16, x, weight, bias, state, y};
+  return hip_status(ssd::launch_causal_conv1d_update(a, static_cast<hipStream_t>(stream)), "causal_conv1d_update launch");
 }
 
 // ============================================================================ selective

@@ -7,7 +7,11 @@
 
 namespace ssd {
 
-// ------------------------------------------------------------------ RG-LRU
+// ------------------------------------------------------------------ state-size-1 scans
+// (RG-LRU and MinMax share one kernel template and its lookback scratch layout)
+// Lookback scratch (control block + words) of a state-size-1 scan.
+size_t scan1_scratch_bytes(int64_t B, int64_t L, int64_t D);
+
 struct RglruScanArgs {
   int64_t B, L, D;
   int in_bf16, out_bf16;
@@ -15,12 +19,11 @@ struct RglruScanArgs {
   const float* a_log;
   float c;
   const float* h0;
+  const void* gate;  // y = gelu(gate) * h, or NULL
   void* y;
   float* h_last;
-  // lookback scratch (control block + words), sized by rglru_scan_scratch_bytes
-  void* scratch;
+  void* scratch;     // scan1_scratch_bytes
 };
-size_t rglru_scan_scratch_bytes(int64_t B, int64_t L, int64_t D);
 hipError_t launch_rglru_scan(const RglruScanArgs& a, hipStream_t s);
 
 struct RglruUpdateArgs {
@@ -29,10 +32,57 @@ struct RglruUpdateArgs {
   const void *x, *r_logit, *i_logit;
   const float* a_log;
   float c;
+  const void* gate;
   float* state;
   void* y;
 };
 hipError_t launch_rglru_update(const RglruUpdateArgs& a, hipStream_t s);
+
+struct MinmaxScanArgs {
+  int64_t B, L, D;
+  int in_bf16, out_bf16;
+  const void *r, *s;
+  const float* x0;
+  const void* gate;  // y = x * gate, or NULL
+  void* y;
+  float* x_last;
+  void* scratch;     // scan1_scratch_bytes
+};
+hipError_t launch_minmax_scan(const MinmaxScanArgs& a, hipStream_t s);
+
+struct MinmaxUpdateArgs {
+  int64_t B, D;
+  int in_bf16, out_bf16;
+  const void *r, *s;
+  const void* gate;
+  float* state;
+  void* y;
+};
+hipError_t launch_minmax_update(const MinmaxUpdateArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------------ causal depthwise conv
+struct Conv1dArgs {
+  int64_t B, L, D, W;
+  int in_bf16, out_bf16;
+  const void* x;
+  const float* weight;    // [D][W]
+  const float* bias;      // [D] or NULL
+  const float* state_in;  // [B][D][W] or NULL
+  void* y;
+  float* state_out;       // [B][D][W] or NULL
+};
+hipError_t launch_causal_conv1d(const Conv1dArgs& a, hipStream_t s);
+
+struct Conv1dUpdateArgs {
+  int64_t B, D, W;
+  int in_bf16, out_bf16;
+  const void* x;
+  const float* weight;
+  const float* bias;
+  float* state;           // [B][D][W] in / out
+  void* y;
+};
+hipError_t launch_causal_conv1d_update(const Conv1dUpdateArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------------ selective
 struct SelectiveScanArgs {

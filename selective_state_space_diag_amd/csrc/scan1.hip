@@ -1,0 +1,525 @@
+// scan1.hip -- diagonal scans with one state per channel for gfx950: the RG-LRU recurrence and the
+// MinMax recurrence, each with its decode step.
+//
+// RG-LRU (lrnnx documentation, "lrnnx.models.ltv.rglru": RGLRU.forward gates and the RGLRU.step
+// update): r = sigmoid(r_logit), i = sigmoid(i_logit), log a_t = c * r * a_log,
+// h_t = a_t h_{t-1} + sqrt(1 - a_t^2) (i x).  The block around it multiplies the result by
+// gelu(gate) before its output projection; that multiply is optional here.
+// MinMax (minmaxrnc package, minmax_neuron.py and minmax_operator.py): x_t = max(min(r_t, x_{t-1}),
+// s_t) from the initial state; the neuron's output gate multiplies x_t by g_t (optional here).
+//
+// Both steps are maps h -> f(a, b; h) of a family closed under composition:
+//   affine  f = a h + b,             (a2, b2) o (a1, b1) = (a2 a1, a2 b1 + b2)
+//   minmax  f = max(min(a, h), b),   (a2, b2) o (a1, b1) = (min(a2, a1), max(min(a2, b1), b2))
+// (the MinMax rule is the composition the minmax_operator page states), so one chunked scan serves
+// both.  MinMax's min and max order -0 below +0 and turn any NaN operand into NaN: each is then a
+// well-defined function of its operands' values, commutative and associative bit for bit, and the
+// chunked evaluation equals the sequential loop exactly.
+//
+// Scan design (single pass, every input read once from HBM):
+//   * A work unit is (batch b, channel tile k of 64*V channels, chunk c of 64 steps).  Lanes run
+//     along channels (coalesced rows of the [B, L, D] layout); the 4 waves of a workgroup each own
+//     16 consecutive steps of the chunk.
+//   * Each lane turns its 16 steps into pairs (a_t, b_t) kept in registers and folds them into the
+//     wave's aggregate (the composed map of its 16 steps).
+//   * Aggregates of the 4 waves meet in LDS; the chunk's carry-in comes from a lookback over
+//     earlier chunks of the same (b, k), which publish aggregates and block-end inclusive states
+//     as self-validating 64-bit words (value, launch epoch).  Tickets are handed out chunk-major,
+//     so a unit only ever waits for lower tickets, which are running or done: the lookback always
+//     terminates, and its fixed combine order makes the result bitwise reproducible.
+//   * With the carry known, each wave re-runs h = f(a_t, b_t; h) over its registers and stores y.
+#include <algorithm>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ssd {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kSteps = 16;                 // steps per wave
+constexpr int kChunk = kWaves * kSteps;    // steps per work unit
+constexpr int kBlock = 2;                  // chunks per lookback block
+
+struct Scan1Params {
+  int64_t B, L, D;
+  int64_t n_tiles, n_chunks;
+  const void* in[3];   // step inputs: RG-LRU (x, r_logit, i_logit), MinMax (r, s)
+  const void* gate;    // output gate or NULL
+  const float* a_log;  // RG-LRU only
+  float c;
+  const float* h0;
+  void* y;
+  float* h_last;
+  LookbackCtl* ctl;
+  unsigned long long* words;  // [unit][3][tile width]: aggregate a, aggregate b, inclusive h
+  int one_unit_each;          // grid == number of units: every workgroup takes exactly one ticket
+};
+
+// ------------------------------------------------------------------ RG-LRU step
+// 1 - a^2 for a = 2^l2 (l2 <= 0), accurate near a = 1: series of -expm1(2 l2 ln2) for small
+// arguments, else fma(-a, a, 1).
+__device__ __forceinline__ float one_minus_a2(float l2, float a) {
+  float u = 2.0f * l2 * kLn2;
+  float p = fmaf(u, 1.0f / 720.0f, 1.0f / 120.0f);
+  p = fmaf(u, p, 1.0f / 24.0f);
+  p = fmaf(u, p, 1.0f / 6.0f);
+  p = fmaf(u, p, 0.5f);
+  p = fmaf(u, p, 1.0f);
+  float small = -u * p;
+  float big = fmaf(-a, a, 1.0f);
+  return fabsf(u) < 0.25f ? small : big;
+}
+
+// gelu(v) = v * Phi(v) = v/2 (1 + erf(v / sqrt 2)), the exact form (torch's default).
+__device__ __forceinline__ float gelu_f(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
+
+struct AffineOp {
+  static constexpr int kIn = 3;
+  struct Chan {
+    float kc;  // c * a_log * log2(e), so that log2 a_t = kc * r
+  };
+  static __device__ __forceinline__ Chan chan(const Scan1Params& p, int64_t ch) {
+    return Chan{p.c * p.a_log[ch] * kLog2e};
+  }
+  static __device__ __forceinline__ void step(const float (&v)[3], const Chan& ch, float& a, float& b) {
+    const float r = sigmoid_f(v[1]);
+    const float i = sigmoid_f(v[2]);
+    const float l2 = ch.kc * r;
+    a = hw_exp2(l2);
+    b = hw_sqrt(one_minus_a2(l2, a)) * (i * v[0]);
+  }
+  static __device__ __forceinline__ float id_a() { return 1.0f; }
+  static __device__ __forceinline__ float id_b() { return 0.0f; }
+  static __device__ __forceinline__ float apply(float a, float b, float h) { return fmaf(a, h, b); }
+  static __device__ __forceinline__ float fold_a(float a2, float a1) { return a2 * a1; }
+  static __device__ __forceinline__ float gated(float h, float g) { return gelu_f(g) * h; }
+};
+
+// ------------------------------------------------------------------ MinMax step
+// min / max on the reals with -0 below +0; a NaN operand gives the canonical quiet NaN.
+__device__ __forceinline__ float canonical_nan() { return __int_as_float(0x7fc00000); }
+__device__ __forceinline__ float mm_min(float a, float b) {
+  const bool take_a = a < b || (a == b && __float_as_int(a) < 0);
+  const float m = take_a ? a : b;
+  return __builtin_isunordered(a, b) ? canonical_nan() : m;
+}
+__device__ __forceinline__ float mm_max(float a, float b) {
+  const bool take_a = a > b || (a == b && __float_as_int(a) >= 0);
+  const float m = take_a ? a : b;
+  return __builtin_isunordered(a, b) ? canonical_nan() : m;
+}
+
+struct MinMaxOp {
+  static constexpr int kIn = 2;
+  struct Chan {};
+  static __device__ __forceinline__ Chan chan(const Scan1Params&, int64_t) { return Chan{}; }
+  static __device__ __forceinline__ void step(const float (&v)[3], const Chan&, float& a, float& b) {
+    a = v[0];
+    b = v[1];
+  }
+  static __device__ __forceinline__ float id_a() { return __int_as_float(0x7f800000); }   // +inf
+  static __device__ __forceinline__ float id_b() { return __int_as_float((int)0xff800000u); }  // -inf
+  static __device__ __forceinline__ float apply(float a, float b, float h) { return mm_max(mm_min(a, h), b); }
+  static __device__ __forceinline__ float fold_a(float a2, float a1) { return mm_min(a2, a1); }
+  static __device__ __forceinline__ float gated(float h, float g) { return h * g; }
+};
+
+// ------------------------------------------------------------------ work units and loads
+// Raw inputs of one wave's kSteps steps (the loads of a unit, kept in flight until needed).
+template <class Op, typename Tin, int V>
+struct Raw {
+  typename win<Tin, V, kStreaming>::raw v[Op::kIn][kSteps];
+};
+
+struct Unit {
+  int64_t c, b, k;
+  int rows;  // valid steps in the chunk (kChunk except for a ragged last chunk)
+};
+
+__device__ __forceinline__ Unit unit_of(const Scan1Params& p, int64_t ticket) {
+  const int64_t per_round = p.B * p.n_tiles;
+  Unit u;
+  u.c = ticket / per_round;  // chunk-major ticket order
+  const int64_t rr = ticket - u.c * per_round;
+  u.b = rr / p.n_tiles;
+  u.k = rr - u.b * p.n_tiles;
+  u.rows = (int)min<int64_t>(kChunk, p.L - u.c * kChunk);
+  return u;
+}
+
+// Window over the unit's rows of a [B, L, D] array with elements of `es` bytes.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t unit_window(const Scan1Params& p, const Unit& u, const void* a,
+                                                              int es) {
+  const char* base = static_cast<const char*>(a) + ((u.b * p.L + u.c * kChunk) * p.D) * es;
+  return make_window(base, (uint32_t)(u.rows * p.D * es));
+}
+
+// Issue the loads of unit u for this wave.  Lanes past D read channel D - V and steps past the
+// chunk's valid rows read its last row: every offset stays inside the window (results unused).
+template <class Op, typename Tin, int V>
+__device__ __forceinline__ void fetch(const Scan1Params& p, const Unit& u, uint32_t lane_off, int wave,
+                                      Raw<Op, Tin, V>& raw) {
+  using LD = win<Tin, V, kStreaming>;
+  constexpr int es = sizeof(Tin);
+  __amdgpu_buffer_rsrc_t w[Op::kIn];
+#pragma unroll
+  for (int q = 0; q < Op::kIn; ++q) w[q] = unit_window(p, u, p.in[q], es);
+  const uint32_t row_bytes = (uint32_t)(p.D * es);
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    const uint32_t ro = (uint32_t)min(wave * kSteps + s, u.rows - 1) * row_bytes;
+#pragma unroll
+    for (int q = 0; q < Op::kIn; ++q) raw.v[q][s] = LD::load(w[q], lane_off, ro);
+  }
+}
+
+// The output gate of unit u for this wave (same clamping), loaded when the unit's carry is being
+// resolved and consumed by its stores.
+template <typename Tin, int V>
+__device__ __forceinline__ void fetch_gate(const Scan1Params& p, const Unit& u, uint32_t lane_off, int wave,
+                                           typename win<Tin, V, kStreaming>::raw (&g)[kSteps]) {
+  constexpr int es = sizeof(Tin);
+  const auto wg = unit_window(p, u, p.gate, es);
+  const uint32_t row_bytes = (uint32_t)(p.D * es);
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s)
+    g[s] = win<Tin, V, kStreaming>::load(wg, lane_off, (uint32_t)min(wave * kSteps + s, u.rows - 1) * row_bytes);
+}
+
+// ------------------------------------------------------------------ the scan kernel
+// Persistent workgroups: each takes tickets (work units) until none are left.  For unit t it
+//   1. folds the raw inputs of t (loaded earlier) into step pairs and wave aggregates,
+//   2. issues the loads of its next unit, so they are in flight during the lookback of t,
+//   3. resolves the carry of t (waves 0 .. V-1), then re-runs the recurrence and stores y.
+// The next ticket is requested one unit ahead, so its latency is hidden too.
+// Occupancy hint: with bf16 inputs the kernel fits 3 workgroups per SIMD group without spills.
+template <typename Tin> constexpr int waves_per_eu() { return sizeof(Tin) == 2 ? 3 : 1; }
+
+template <class Op, typename Tin, typename Tout, int V, bool GATE>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(waves_per_eu<Tin>())))
+void scan1_kernel(Scan1Params p) {
+  constexpr int TW = 64 * V;  // channels per tile
+  __shared__ unsigned long long s_tick[2];
+  __shared__ float s_aggA[kWaves][TW];
+  __shared__ float s_aggB[kWaves][TW];
+  __shared__ float s_carry[TW];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t total = p.B * p.n_tiles * p.n_chunks;
+  using LD = win<Tin, V, kStreaming>;
+
+  if (threadIdx.x == 0) s_tick[0] = atomicAdd(&p.ctl->tick, 1ull);
+  __syncthreads();
+  const uint32_t E = (uint32_t)(s_tick[0] >> 32) + 1u;  // epoch carried by this launch's words
+  int64_t ticket = (int64_t)(s_tick[0] & 0xffffffffull);
+  Raw<Op, Tin, V> raw;
+  // The lane's channels within a tile are the same for every unit; the tile base moves.
+  auto lane_off_of = [&](const Unit& u) -> uint32_t {
+    const int64_t ch0 = u.k * TW + (int64_t)lane * V;
+    return (uint32_t)(min<int64_t>(ch0, p.D - V) * (int64_t)sizeof(Tin));
+  };
+  if (ticket < total) {
+    const Unit u0 = unit_of(p, ticket);
+    fetch<Op, Tin, V>(p, u0, lane_off_of(u0), wave, raw);
+  }
+  int parity = 0;
+
+  while (ticket < total) {
+    const Unit u = unit_of(p, ticket);
+    if (threadIdx.x == 0)  // next ticket, one unit ahead (none needed when the grid covers every unit)
+      s_tick[parity ^ 1] = p.one_unit_each ? ~0ull : atomicAdd(&p.ctl->tick, 1ull);
+    const int64_t ch0 = u.k * TW + (int64_t)lane * V;
+    const bool ch_ok = ch0 < p.D;  // V = 2 only when D is even
+    const int64_t chl = ch_ok ? ch0 : p.D - V;
+    const int64_t t0 = u.c * kChunk + (int64_t)wave * kSteps;  // first step of this wave
+
+    // ---- step pairs and the wave's aggregate
+    typename Op::Chan cc[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) cc[v] = Op::chan(p, chl + v);
+    float av[kSteps][V], bv[kSteps][V];
+    float Ag[V], Bg[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) { Ag[v] = Op::id_a(); Bg[v] = Op::id_b(); }
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      const bool ok = ch_ok && (t0 + s < p.L);
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        float in[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int q = 0; q < Op::kIn; ++q) in[q] = LD::get(raw.v[q][s], v);
+        float a, bb;
+        Op::step(in, cc[v], a, bb);
+        a = ok ? a : Op::id_a();  // steps past L and idle lanes are the identity map
+        bb = ok ? bb : Op::id_b();
+        av[s][v] = a;
+        bv[s][v] = bb;
+        Bg[v] = Op::apply(a, bb, Bg[v]);
+        Ag[v] = Op::fold_a(a, Ag[v]);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      s_aggA[wave][lane * V + v] = Ag[v];
+      s_aggB[wave][lane * V + v] = Bg[v];
+    }
+    __syncthreads();  // aggregates in LDS; the next ticket is visible
+    const int64_t next = p.one_unit_each ? total : (int64_t)(s_tick[parity ^ 1] & 0xffffffffull);
+    if (next < total) {  // in flight during the lookback
+      const Unit un = unit_of(p, next);
+      fetch<Op, Tin, V>(p, un, lane_off_of(un), wave, raw);
+    }
+    typename LD::raw graw[GATE ? kSteps : 1];
+    if constexpr (GATE) fetch_gate<Tin, V>(p, u, lane_off_of(u), wave, graw);
+
+    // ---- waves 0 .. V-1: chunk aggregate, publish, carry-in, inclusive
+    // Chunks form blocks of kBlock.  The carry into chunk c is the inclusive state published by the
+    // last chunk of the previous block (h0 for the first block), followed by the aggregates of the
+    // earlier chunks of c's own block, applied in chunk order.  Every carry is therefore one fixed
+    // function of the inputs (bitwise reproducible), and the serial chain has n_chunks / kBlock
+    // links.  All the words a unit needs are requested at once; only missing ones are polled again.
+    // Each of these waves resolves 64 of the tile's channels, one per lane.
+    if (wave < V) {
+      const int64_t seq_unit = (u.b * p.n_tiles + u.k) * p.n_chunks;
+      unsigned long long* W = p.words + (seq_unit + u.c) * 3 * TW;
+      const int64_t base = (u.c / kBlock) * kBlock;
+      const int nprev = (int)(u.c - base);  // aggregates of block-mates before c
+      {
+        const int j = wave * 64 + lane;
+        const int64_t ch = u.k * TW + j;
+        const bool j_ok = ch < p.D;
+        float Ac = Op::id_a(), Bc = Op::id_b();
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          Bc = Op::apply(s_aggA[w][j], s_aggB[w][j], Bc);
+          Ac = Op::fold_a(s_aggA[w][j], Ac);
+        }
+        if (u.c + 1 < base + kBlock && u.c + 1 < p.n_chunks) {  // block-mates after c read the aggregate
+          word_store(&W[0 * TW + j], E, Ac);
+          word_store(&W[1 * TW + j], E, Bc);
+        }
+        // words: [0] inclusive of chunk base-1 (if base > 0), then (a, b) of chunks base .. c-1
+        unsigned long long wd[1 + 2 * (kBlock - 1)];
+        const unsigned long long* Wb = p.words + (seq_unit + base - 1) * 3 * TW;
+        wd[0] = base > 0 ? word_load(&Wb[2 * TW + j]) : ((unsigned long long)E << 32);
+#pragma unroll
+        for (int q = 0; q < kBlock - 1; ++q) {
+          const unsigned long long* Wq = p.words + (seq_unit + base + q) * 3 * TW;
+          if (q < nprev) {
+            wd[1 + 2 * q] = word_load(&Wq[0 * TW + j]);
+            wd[2 + 2 * q] = word_load(&Wq[1 * TW + j]);
+          } else {
+            wd[1 + 2 * q] = wd[2 + 2 * q] = (unsigned long long)E << 32;
+          }
+        }
+        unsigned int spins = 0;
+        while (true) {
+          bool all = word_ready(wd[0], E);
+#pragma unroll
+          for (int q = 0; q < 2 * (kBlock - 1); ++q) all = all && word_ready(wd[1 + q], E);
+          if (all || spins >= kSpinLimit) break;
+          ++spins;
+          __builtin_amdgcn_s_sleep(1);
+          if (!word_ready(wd[0], E)) wd[0] = word_load(&Wb[2 * TW + j]);
+#pragma unroll
+          for (int q = 0; q < kBlock - 1; ++q) {
+            const unsigned long long* Wq = p.words + (seq_unit + base + q) * 3 * TW;
+            if (!word_ready(wd[1 + 2 * q], E)) wd[1 + 2 * q] = word_load(&Wq[0 * TW + j]);
+            if (!word_ready(wd[2 + 2 * q], E)) wd[2 + 2 * q] = word_load(&Wq[1 * TW + j]);
+          }
+        }
+        if (spins >= kSpinLimit) atomicOr(&p.ctl->error, 1u);
+        float hin = (base > 0) ? word_value(wd[0]) : (p.h0 ? p.h0[u.b * p.D + (j_ok ? ch : p.D - 1)] : 0.0f);
+#pragma unroll
+        for (int q = 0; q < kBlock - 1; ++q)
+          if (q < nprev) hin = Op::apply(word_value(wd[1 + 2 * q]), word_value(wd[2 + 2 * q]), hin);
+        const float incl = Op::apply(Ac, Bc, hin);
+        if (u.c == base + kBlock - 1 && u.c + 1 < p.n_chunks) word_store(&W[2 * TW + j], E, incl);
+        if (p.h_last && j_ok && u.c == p.n_chunks - 1) p.h_last[u.b * p.D + ch] = incl;
+        s_carry[j] = hin;
+      }
+    }
+    __syncthreads();
+
+    // ---- carry into this wave, re-run the recurrence, store
+    float h[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int j = lane * V + v;
+      float hv = s_carry[j];
+      for (int w = 0; w < wave; ++w) hv = Op::apply(s_aggA[w][j], s_aggB[w][j], hv);
+      h[v] = hv;
+    }
+    {
+      const auto wy = unit_window(p, u, p.y, (int)sizeof(Tout));
+      const uint32_t row_bytes = (uint32_t)(p.D * (int64_t)sizeof(Tout));
+      const uint32_t lo = (uint32_t)(chl * (int64_t)sizeof(Tout));
+      const int nvalid = u.rows - wave * kSteps;  // rows of this wave inside the chunk
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) {
+        float out[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          h[v] = Op::apply(av[s][v], bv[s][v], h[v]);
+          out[v] = GATE ? Op::gated(h[v], LD::get(graw[GATE ? s : 0], v)) : h[v];
+        }
+        if (ch_ok && s < nvalid)
+          win<Tout, V, kStreaming>::store(wy, lo, (uint32_t)(wave * kSteps + s) * row_bytes, out);
+      }
+    }
+    __syncthreads();  // LDS (aggregates, carry, ticket slot) is reused by the next unit
+    ticket = next;
+    parity ^= 1;
+  }
+
+  // ---- last workgroup to finish resets the ticket and advances the epoch
+  if (threadIdx.x == 0) {
+    const unsigned int old = atomicAdd(&p.ctl->done, 1u);
+    if (old == gridDim.x - 1) {
+      __hip_atomic_store(&p.ctl->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&p.ctl->tick, (unsigned long long)E << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ decode steps
+struct Upd1Params {
+  int64_t B, D;
+  const void* in[3];
+  const void* gate;
+  const float* a_log;
+  float c;
+  float* state;
+  void* y;
+};
+
+template <class Op, typename Tin, typename Tout, bool GATE>
+__global__ __launch_bounds__(256) void update1_kernel(Upd1Params p) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= p.B * p.D) return;
+  const int64_t d = idx % p.D;
+  Scan1Params q{};
+  q.a_log = p.a_log;
+  q.c = p.c;
+  float in[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int k = 0; k < Op::kIn; ++k) in[k] = io<Tin>::load(p.in[k], idx);
+  float a, b;
+  Op::step(in, Op::chan(q, d), a, b);
+  const float h = Op::apply(a, b, p.state[idx]);
+  p.state[idx] = h;
+  io<Tout>::store(p.y, idx, GATE ? Op::gated(h, io<Tin>::load(p.gate, idx)) : h);
+}
+
+// ------------------------------------------------------------------ launchers
+// Persistent grid: as many workgroups as stay resident together (by the kernel's own occupancy),
+// never more than there are work units.
+template <class Op, typename Tin, typename Tout, int V, bool GATE>
+hipError_t launch_scan_t(const Scan1Params& p, hipStream_t s) {
+  const int64_t total = p.B * p.n_tiles * p.n_chunks;
+  static int per_cu = 0, cus = 0;
+  if (per_cu == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan1_kernel<Op, Tin, Tout, V, GATE>, kWaves * 64,
+                                                     0) != hipSuccess ||
+        per_cu <= 0)
+      per_cu = 1;
+  }
+  const int64_t grid = std::min<int64_t>(total, (int64_t)per_cu * cus);
+  Scan1Params q = p;
+  q.one_unit_each = grid == total;
+  hipLaunchKernelGGL((scan1_kernel<Op, Tin, Tout, V, GATE>), dim3((unsigned)grid), dim3(kWaves * 64), 0, s, q);
+  return hipGetLastError();
+}
+
+template <class Op, int V, bool GATE>
+hipError_t launch_scan_dt(const Scan1Params& p, int in_bf16, int out_bf16, hipStream_t s) {
+  if (!in_bf16) return launch_scan_t<Op, float, float, V, GATE>(p, s);
+  return out_bf16 ? launch_scan_t<Op, bf16_t, bf16_t, V, GATE>(p, s) : launch_scan_t<Op, bf16_t, float, V, GATE>(p, s);
+}
+
+int vec_width(int64_t D) { return (D % 2 == 0) ? 2 : 1; }
+
+template <class Op>
+hipError_t launch_scan_op(Scan1Params& p, int in_bf16, int out_bf16, void* scratch, hipStream_t s) {
+  const int V = vec_width(p.D);
+  const int64_t TW = 64 * V;
+  p.n_tiles = (p.D + TW - 1) / TW;
+  p.n_chunks = (p.L + kChunk - 1) / kChunk;
+  p.ctl = static_cast<LookbackCtl*>(scratch);
+  p.words = reinterpret_cast<unsigned long long*>(static_cast<char*>(scratch) + 256);
+  const bool gate = p.gate != nullptr;
+  if (V == 2)
+    return gate ? launch_scan_dt<Op, 2, true>(p, in_bf16, out_bf16, s) : launch_scan_dt<Op, 2, false>(p, in_bf16, out_bf16, s);
+  return gate ? launch_scan_dt<Op, 1, true>(p, in_bf16, out_bf16, s) : launch_scan_dt<Op, 1, false>(p, in_bf16, out_bf16, s);
+}
+
+template <class Op, bool GATE>
+hipError_t launch_update_g(const Upd1Params& p, int in_bf16, int out_bf16, hipStream_t s) {
+  const int64_t n = p.B * p.D;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (!in_bf16)
+    hipLaunchKernelGGL((update1_kernel<Op, float, float, GATE>), grid, dim3(256), 0, s, p);
+  else if (out_bf16)
+    hipLaunchKernelGGL((update1_kernel<Op, bf16_t, bf16_t, GATE>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((update1_kernel<Op, bf16_t, float, GATE>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <class Op>
+hipError_t launch_update_op(const Upd1Params& p, int in_bf16, int out_bf16, hipStream_t s) {
+  return p.gate ? launch_update_g<Op, true>(p, in_bf16, out_bf16, s) : launch_update_g<Op, false>(p, in_bf16, out_bf16, s);
+}
+
+}  // namespace
+
+size_t scan1_scratch_bytes(int64_t B, int64_t L, int64_t D) {
+  const int V = vec_width(D);
+  const int64_t TW = 64 * V;
+  const int64_t n_tiles = (D + TW - 1) / TW;
+  const int64_t n_chunks = (L + kChunk - 1) / kChunk;
+  return 256 + (size_t)(B * n_tiles * n_chunks) * 3 * TW * sizeof(unsigned long long);
+}
+
+hipError_t launch_rglru_scan(const RglruScanArgs& a, hipStream_t s) {
+  Scan1Params p{};
+  p.B = a.B; p.L = a.L; p.D = a.D;
+  p.in[0] = a.x; p.in[1] = a.r_logit; p.in[2] = a.i_logit;
+  p.gate = a.gate;
+  p.a_log = a.a_log; p.c = a.c; p.h0 = a.h0; p.y = a.y; p.h_last = a.h_last;
+  return launch_scan_op<AffineOp>(p, a.in_bf16, a.out_bf16, a.scratch, s);
+}
+
+hipError_t launch_minmax_scan(const MinmaxScanArgs& a, hipStream_t s) {
+  Scan1Params p{};
+  p.B = a.B; p.L = a.L; p.D = a.D;
+  p.in[0] = a.r; p.in[1] = a.s;
+  p.gate = a.gate;
+  p.h0 = a.x0; p.y = a.y; p.h_last = a.x_last;
+  return launch_scan_op<MinMaxOp>(p, a.in_bf16, a.out_bf16, a.scratch, s);
+}
+
+hipError_t launch_rglru_update(const RglruUpdateArgs& a, hipStream_t s) {
+  Upd1Params p{};
+  p.B = a.B; p.D = a.D;
+  p.in[0] = a.x; p.in[1] = a.r_logit; p.in[2] = a.i_logit;
+  p.gate = a.gate; p.a_log = a.a_log; p.c = a.c; p.state = a.state; p.y = a.y;
+  return launch_update_op<AffineOp>(p, a.in_bf16, a.out_bf16, s);
+}
+
+hipError_t launch_minmax_update(const MinmaxUpdateArgs& a, hipStream_t s) {
+  Upd1Params p{};
+  p.B = a.B; p.D = a.D;
+  p.in[0] = a.r; p.in[1] = a.s;
+  p.gate = a.gate; p.state = a.state; p.y = a.y;
+  return launch_update_op<MinMaxOp>(p, a.in_bf16, a.out_bf16, s);
+}
+
+}  // namespace ssd

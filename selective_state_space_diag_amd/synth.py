@@ -22,6 +22,13 @@ Workloads (sizes as named by the five benchmark configurations):
 * ``hgrn2``: q, k, v ~ N(0, 1/sqrt(d)); g_logit ~ N(2, 1); lower bound 0.5.
 * ``varlen``: sequence lengths log-uniform in [512, 16384], rescaled to sum to
   the packed length (largest-remainder rounding).
+* ``rglru`` with a gate: the block's gate pre-activation ~ N(0,1).
+* ``minmax``: r, s ~ N(0,1) (the neuron's two linear maps of the input), gate
+  ~ N(0,1), x0 ~ N(0,1); or, with ``ties=True``, values drawn from
+  {-2, -1, -0, +0, 1, 2} so that equal values and both zeros occur.
+* ``conv``: x ~ N(0,1); weight and bias ~ U(-1/sqrt(W), 1/sqrt(W)) (torch's
+  default Conv1d initialisation for a depthwise kernel of width W); carried
+  window ~ N(0,1).
 """
 from __future__ import annotations
 
@@ -98,7 +105,7 @@ class Inputs:
 
 # ----------------------------------------------------------------------------- RG-LRU
 def rglru_inputs(B: int, L: int, D: int, dtype: str = BF16, seed: int = 0, c: float = 8.0,
-                 with_h0: bool = False) -> Inputs:
+                 with_h0: bool = False, with_gate: bool = False) -> Inputs:
     rng = np.random.Generator(np.random.PCG64(seed))
     a = rng.uniform(0.9, 0.999, size=D)
     inp = Inputs("rglru", dict(B=B, L=L, D=D))
@@ -108,6 +115,42 @@ def rglru_inputs(B: int, L: int, D: int, dtype: str = BF16, seed: int = 0, c: fl
     inp.s["c"] = float(c)
     if with_h0:
         inp.p["h0"] = _normal(rng, (B, D))
+    if with_gate:
+        inp.t["gate"] = _store(_normal(rng, (B, L, D)), dtype)
+    return inp
+
+
+# ----------------------------------------------------------------------------- MinMax
+_TIE_VALUES = np.array([-2.0, -1.0, -0.0, 0.0, 1.0, 2.0], dtype=np.float32)
+
+
+def minmax_inputs(B: int, L: int, D: int, dtype: str = BF16, seed: int = 0, with_x0: bool = False,
+                  with_gate: bool = False, ties: bool = False) -> Inputs:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    inp = Inputs("minmax", dict(B=B, L=L, D=D))
+    draw = (lambda shape: _TIE_VALUES[rng.integers(0, _TIE_VALUES.size, size=shape)]) if ties else \
+        (lambda shape: _normal(rng, shape))
+    for name in ("r", "s"):
+        inp.t[name] = _store(draw((B, L, D)), dtype)
+    if with_x0:
+        inp.p["x0"] = draw((B, D)).astype(np.float32)
+    if with_gate:
+        inp.t["gate"] = _store(_normal(rng, (B, L, D)), dtype)
+    return inp
+
+
+# ----------------------------------------------------------------------------- causal conv
+def conv_inputs(B: int, L: int, D: int, W: int = 4, dtype: str = BF16, seed: int = 0, with_bias: bool = True,
+                with_state: bool = False) -> Inputs:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    inp = Inputs("conv", dict(B=B, L=L, D=D, W=W))
+    bound = 1.0 / math.sqrt(W)
+    inp.p["weight"] = rng.uniform(-bound, bound, size=(D, W)).astype(np.float32)
+    if with_bias:
+        inp.p["bias"] = rng.uniform(-bound, bound, size=D).astype(np.float32)
+    inp.t["x"] = _store(_normal(rng, (B, L, D)), dtype)
+    if with_state:
+        inp.p["state"] = _normal(rng, (B, D, W))
     return inp
 
 

@@ -55,9 +55,9 @@ def test_status_strings_and_version(L):
     assert L.ssd_status_str(99) == b"unknown status"
 
 
-def rglru(L, B=2, Lq=8, D=4, ind=F32, outd=F32, x=0, r=1, i=2, a=3, c=8.0, h0=None, y=4, hl=None):
+def rglru(L, B=2, Lq=8, D=4, ind=F32, outd=F32, x=0, r=1, i=2, a=3, c=8.0, h0=None, g=None, y=4, hl=None):
     p = lambda k: None if k is None else ptr(k)
-    return L.ssd_rglru_scan(B, Lq, D, ind, outd, p(x), p(r), p(i), p(a), c, p(h0), p(y), p(hl), None)
+    return L.ssd_rglru_scan(B, Lq, D, ind, outd, p(x), p(r), p(i), p(a), c, p(h0), p(g), p(y), p(hl), None)
 
 
 def test_rglru_scan_validation(L):
@@ -70,8 +70,9 @@ def test_rglru_scan_validation(L):
     assert rglru(L, c=float("nan")) == VALUE
     assert rglru(L, y=0) == ALIAS                  # y on top of x
     assert rglru(L, h0=5, hl=5) == ALIAS           # h_last on top of h0
-    assert L.ssd_rglru_scan(2, 8, 4, F32, F32, ctypes.c_void_p(P + 8), ptr(1), ptr(2), ptr(3), 8.0, None, ptr(4),
-                            None, None) == ALIGN
+    assert rglru(L, g=6, y=6) == ALIAS             # y on top of the gate
+    assert L.ssd_rglru_scan(2, 8, 4, F32, F32, ctypes.c_void_p(P + 8), ptr(1), ptr(2), ptr(3), 8.0, None, None,
+                            ptr(4), None, None) == ALIGN
     assert b"aligned" in L.ssd_last_error()
     # empty problem: nothing to do, no launch
     assert rglru(L, B=0) == OK
@@ -80,13 +81,53 @@ def test_rglru_scan_validation(L):
 
 def test_rglru_update_validation(L):
     f = lambda **kw: L.ssd_rglru_update(kw.get("B", 4), kw.get("D", 8), kw.get("ind", BF16), kw.get("outd", F32),
-                                        ptr(0), ptr(1), ptr(2), ptr(3), kw.get("c", 8.0),
+                                        ptr(0), ptr(1), ptr(2), ptr(3), kw.get("c", 8.0), kw.get("gate", None),
                                         kw.get("state", ptr(4)), kw.get("y", ptr(5)), None)
     assert f(D=-3) == SHAPE
     assert f(state=None) == NULL
     assert f(y=ptr(4)) == ALIAS
     assert f(y=ptr(0)) == ALIAS
+    assert f(gate=ptr(6), y=ptr(6)) == ALIAS
     assert f(B=0) == OK
+
+
+def test_minmax_validation(L):
+    p = lambda k: None if k is None else ptr(k)
+    f = lambda B=2, Lq=8, D=4, ind=BF16, outd=F32, r=0, s=1, x0=None, g=None, y=4, xl=None: L.ssd_minmax_scan(
+        B, Lq, D, ind, outd, p(r), p(s), p(x0), p(g), p(y), p(xl), None)
+    assert f(B=-1) == SHAPE
+    assert f(ind=F32, outd=BF16) == DTYPE
+    assert f(s=None) == NULL
+    assert f(y=1) == ALIAS
+    assert f(x0=5, xl=5) == ALIAS
+    assert f(g=6, y=6) == ALIAS
+    assert L.ssd_minmax_scan(2, 8, 4, BF16, F32, ptr(0), ctypes.c_void_p(P + 1), None, None, ptr(4), None,
+                             None) == ALIGN
+    assert f(D=0) == OK
+    u = lambda B=4, D=8, st=4, y=5, g=None: L.ssd_minmax_update(B, D, BF16, F32, ptr(0), ptr(1), p(g), p(st), p(y),
+                                                                None)
+    assert u(D=-1) == SHAPE
+    assert u(st=None) == NULL
+    assert u(y=4) == ALIAS
+    assert u(B=0) == OK
+
+
+def test_causal_conv1d_validation(L):
+    p = lambda k: None if k is None else ptr(k)
+    f = lambda B=2, Lq=8, D=4, W=4, x=0, w=1, b=None, si=None, y=4, so=None: L.ssd_causal_conv1d(
+        B, Lq, D, W, BF16, F32, p(x), p(w), p(b), p(si), p(y), p(so), None)
+    assert f(W=0) == SHAPE
+    assert f(W=5) == SHAPE
+    assert f(Lq=-2) == SHAPE
+    assert f(w=None) == NULL
+    assert f(x=None) == NULL
+    assert f(y=0) == ALIAS
+    assert f(si=6, so=6) == ALIAS
+    assert f(B=0) == OK
+    u = lambda W=4, st=4, y=5: L.ssd_causal_conv1d_update(4, 8, W, BF16, F32, ptr(0), ptr(1), None, p(st), p(y), None)
+    assert u(W=7) == SHAPE
+    assert u(st=None) == NULL
+    assert u(y=4) == ALIAS
 
 
 def sel(L, B=1, Lq=16, D=8, N=16, ind=BF16, outd=F32, cu=None, nseq=0, y=9, A=2, Bm=3, Cm=4, h0=None, hl=None):
