@@ -57,6 +57,18 @@ def rglru_bytes(B, L, D, in_b=2, out_b=4):
     return B * L * D * (3 * in_b + out_b) + D * 4
 
 
+def rglru_gated_bytes(B, L, D, in_b=2, out_b=4):
+    return B * L * D * (4 * in_b + out_b) + D * 4
+
+
+def minmax_bytes(B, L, D, in_b=2, out_b=4):
+    return B * L * D * (2 * in_b + out_b)
+
+
+def conv_bytes(B, L, D, W, in_b=2, out_b=4):
+    return B * L * D * (in_b + out_b) + D * (W + 1) * 4
+
+
 def hgrn2_bytes(B, L, H, d, in_b=2, out_b=4):
     return B * L * H * d * (4 * in_b + out_b)
 
@@ -215,6 +227,23 @@ def forms(args, device):
     a_log = torch.log(torch.empty(D, device=device).uniform_(0.9, 0.999, generator=gen))
     ms = time_calls(lambda k: ssd.rglru_scan(x, r, i, a_log, 8.0), 1, 10, 2)[0]
     record("rglru_bf16_B8_L8192_D2560", ms, B * L * D, rglru_bytes(B, L, D))
+
+    # --- the same scan with the block's gelu(gate) output multiply fused into its stores
+    gt = randn((B, L, D))
+    ms = time_calls(lambda k: ssd.rglru_scan(x, r, i, a_log, 8.0, gate=gt), 1, 10, 2)[0]
+    record("rglru_gated_bf16_B8_L8192_D2560", ms, B * L * D, rglru_gated_bytes(B, L, D))
+    del gt
+
+    # --- MinMax scan on the same shape (r, s ~ N(0, 1))
+    ms = time_calls(lambda k: ssd.minmax_scan(r, i), 1, 10, 2)[0]
+    record("minmax_bf16_B8_L8192_D2560", ms, B * L * D, minmax_bytes(B, L, D))
+
+    # --- causal depthwise conv (width 4) in front of the RG-LRU, same shape
+    W = 4
+    wconv = torch.empty(D, W, device=device).uniform_(-0.5, 0.5, generator=gen)
+    bconv = torch.empty(D, device=device).uniform_(-0.5, 0.5, generator=gen)
+    ms = time_calls(lambda k: ssd.causal_conv1d(x, wconv, bias=bconv), 1, 10, 2)[0]
+    record("causal_conv1d_bf16_B8_L8192_D2560_W4", ms, B * L * D, conv_bytes(B, L, D, W))
     del x, r, i
 
     # --- RG-LRU decode, B=256 D=2560, 256 steps carrying the state (one launch per step)
