@@ -317,9 +317,39 @@ __device__ __forceinline__ void h2_out_state(const uint16_t* Qs, int lane, const
   }
 }
 
+// Window over this workgroup's 64 output columns of rows [t0, t0 + valid) of head hh (row r at
+// byte r * H * 128 * es).  Rows at or past `valid` lie outside it, and the hardware's range check
+// drops stores there, so the ragged last chunk needs no per-lane condition.
+template <typename Tout>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t h2_out_window(const H2Params& p, int64_t b, int64_t hh, int i0,
+                                                                int64_t t0, int valid) {
+  constexpr int es = sizeof(Tout);
+  const char* base = static_cast<const char*>(p.o) + (((b * p.L + t0) * p.H + hh) * kDh + i0) * es;
+  return make_window(base, (uint32_t)((int64_t)(valid - 1) * p.H * kDh * es + kRows * es));
+}
+
+// Four consecutive outputs of one row through an output window.
+template <typename Tout> struct h2_store4;
+template <> struct h2_store4<float> {
+  static __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t w, uint32_t lane_off, uint32_t row_off, float a,
+                                             float b, float c, float d) {
+    const v4i_t v = {(int)__float_as_uint(a), (int)__float_as_uint(b), (int)__float_as_uint(c), (int)__float_as_uint(d)};
+    __builtin_amdgcn_raw_buffer_store_b128(v, w, (int)lane_off, (int)row_off, 0);
+  }
+};
+template <> struct h2_store4<bf16_t> {
+  static __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t w, uint32_t lane_off, uint32_t row_off, float a,
+                                             float b, float c, float d) {
+    u32x2_t v;
+    v.x = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+    v.y = (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
+    __builtin_amdgcn_raw_buffer_store_b64(v, w, (int)lane_off, (int)row_off, 0);
+  }
+};
+
 template <int H, typename Tout>
-__device__ __forceinline__ void h2_out(const H2Params& p, H2Lds& sm, int iw, int lane, const floatx4_t (&os)[2],
-                                       int64_t obase_row, int64_t row_stride, int valid) {
+__device__ __forceinline__ void h2_out(__amdgpu_buffer_rsrc_t wo, uint32_t row_bytes, H2Lds& sm, int iw, int lane,
+                                       const floatx4_t (&os)[2]) {
   using TL = Tiles<H>;
   const int l16 = lane & 15, lg = lane >> 4;
   // W as A operands: slots s = 32 ks + 16 h' + 4 lg + r; lane 4b + c of a group points at
@@ -360,15 +390,14 @@ __device__ __forceinline__ void h2_out(const H2Params& p, H2Lds& sm, int iw, int
   float igc[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) igc[r] = hw_rcp(sm.gcol[iw + 4 * lg + r]);
+  const uint32_t lane_off = (uint32_t)l16 * row_bytes + (uint32_t)(4 * lg * (int)sizeof(Tout));
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     const int t = 16 * TL::tt(a) + l16;
     const float4 gm = *reinterpret_cast<const float4*>(&sm.gam[t][iw + 4 * lg]);
-    if (t < valid) {
-      const int64_t ob = (obase_row + t) * row_stride + iw + 4 * lg;
-      io4<Tout>::store(p.o, ob, gm.x * fmaf(oa[a][0], igc[0], os[a][0]), gm.y * fmaf(oa[a][1], igc[1], os[a][1]),
-                       gm.z * fmaf(oa[a][2], igc[2], os[a][2]), gm.w * fmaf(oa[a][3], igc[3], os[a][3]));
-    }
+    h2_store4<Tout>::run(wo, lane_off, 16 * TL::tt(a) * row_bytes + iw * (uint32_t)sizeof(Tout),
+                         gm.x * fmaf(oa[a][0], igc[0], os[a][0]), gm.y * fmaf(oa[a][1], igc[1], os[a][1]),
+                         gm.z * fmaf(oa[a][2], igc[2], os[a][2]), gm.w * fmaf(oa[a][3], igc[3], os[a][3]));
   }
 }
 
@@ -417,10 +446,9 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
   __syncthreads();
   h2_gate1(sm, tid & 63, wave, (int)min((int64_t)kCh, p.L), lb, one_m_lb, gam_run, vv);
   for (int64_t c = 0; c < nchunks; ++c) {
-    // Lane indices re-derived per chunk from an opaque copy: keeps the compiler from hoisting the
-    // many per-lane LDS addresses out of the loop into registers.
-    int tidv = tid;
-    asm volatile("" : "+v"(tidv));
+    // Per-lane LDS addresses are loop-invariant and stay in registers across chunks: the LDS use
+    // already limits the kernel to two waves per SIMD, so the registers they take are free.
+    const int tidv = tid;
     const int lane = tidv & 63;
     const int l16 = lane & 15, lg = lane >> 4;
     const int64_t t0 = c * kCh;
@@ -504,13 +532,11 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
     __syncthreads();  // Gamma, W, Gamma_C, Q K^T tiles visible
 
     // ---- O^T for this half's token tiles
-    const int64_t obase_row = b * p.L + t0;
-    const int64_t row_stride = p.H * kDh;
     {
-      H2Params pp = p;
-      pp.o = static_cast<char*>(p.o) + (hh * kDh + i0) * (int64_t)sizeof(Tout);
-      if (half_t == 0) h2_out<0, Tout>(pp, sm, iw, lane, os, obase_row, row_stride, valid);
-      else h2_out<1, Tout>(pp, sm, iw, lane, os, obase_row, row_stride, valid);
+      const auto wo = h2_out_window<Tout>(p, b, hh, i0, t0, valid);
+      const uint32_t row_bytes = (uint32_t)(p.H * kDh * (int64_t)sizeof(Tout));
+      if (half_t == 0) h2_out<0, Tout>(wo, row_bytes, sm, iw, lane, os);
+      else h2_out<1, Tout>(wo, row_bytes, sm, iw, lane, os);
     }
 
     // ---- state update on this wave's tiles: S^T = S^T Gamma_C[i] + K^T W  (slots s = 32 ks + 8 lg + e)
