@@ -6,7 +6,9 @@
 // served in two phases of 32 lanes, a 16-byte access in four phases of 16 lanes, and a phase is
 // conflict-free when its lanes touch distinct bank words.
 //   qk: [64 rows][128 cols] bf16; 16-byte segment s of row r stored at s ^ f(r), with the 4-bit
-//       f(r) = (r2) | (r0 r1) << 1 | r3 << 3 (r_k: bit k of the row);
+//       f(r) = (r2) | (r0 r1) << 1 | r3 << 3 (r_k: bit k of the row), and 16 bytes of padding after
+//       every 16 rows, so that rows 16 apart (the two token tiles one wave reads in a single
+//       two-address instruction) fall on different banks;
 //   vw: [64 rows][64 cols] bf16; 4-element chunk c of row r stored at c ^ g(r),
 //       g(r) = r1 << 2 | (r2 ^ r3) << 3;
 //   gv: [64 rows][64 cols] bf16 (staged gate inputs); chunk c of row r stored at c ^ 9 r1.
@@ -21,6 +23,9 @@ namespace ssd {
 namespace h2 {
 
 constexpr int kQkCols = 128;
+constexpr int kQkGroupPad = 8;                      // elements (16 bytes) after every 16 rows
+constexpr int kQkGroup = 16 * kQkCols + kQkGroupPad;  // elements per 16-row group
+constexpr int kQkTile = 4 * kQkGroup;                 // elements per 64-row tile
 constexpr int kVwCols = 64;
 
 __host__ __device__ __forceinline__ int qk_f(int row) { return ((row >> 2) & 1) | ((row & 3) << 1) | (row & 8); }
@@ -28,7 +33,7 @@ __host__ __device__ __forceinline__ int vw_g(int row) {
   return (((row >> 1) & 1) << 2) | ((((row >> 2) ^ (row >> 3)) & 1) << 3);
 }
 __host__ __device__ __forceinline__ int qk_off(int row, int col) {
-  return row * kQkCols + (((col >> 3) ^ qk_f(row)) << 3) + (col & 7);
+  return row * kQkCols + (row >> 4) * kQkGroupPad + (((col >> 3) ^ qk_f(row)) << 3) + (col & 7);
 }
 __host__ __device__ __forceinline__ int vw_off(int row, int col) {
   return row * kVwCols + (((col >> 2) ^ vw_g(row)) << 2) + (col & 3);
@@ -43,13 +48,13 @@ __host__ __device__ __forceinline__ int gv_off(int row, int col) {
 // (A) row 16a + l16, 8-element segment at column 32 ks + 8 lg (MFMA A / B operand rows).
 __host__ __device__ __forceinline__ int qk_seg_lane(int l16, int lg) { return lg ^ qk_f(l16); }
 __host__ __device__ __forceinline__ int qk_seg_off(int l16, int xa, int a, int ks) {
-  return l16 * kQkCols + 16 * kQkCols * a + ((xa ^ (4 * ks)) << 3);
+  return l16 * kQkCols + kQkGroup * a + ((xa ^ (4 * ks)) << 3);
 }
 
 // (B) row 16a + l16, 4 elements at column 32 ks + 16 h + 4 lg.
 __host__ __device__ __forceinline__ int qk_quad_lane(int l16, int lg) { return (lg >> 1) ^ qk_f(l16); }
 __host__ __device__ __forceinline__ int qk_quad_off(int l16, int lg, int xb, int a, int ks, int h) {
-  return l16 * kQkCols + 16 * kQkCols * a + ((xb ^ (4 * ks) ^ (2 * h)) << 3) + 4 * (lg & 1);
+  return l16 * kQkCols + kQkGroup * a + ((xb ^ (4 * ks) ^ (2 * h)) << 3) + 4 * (lg & 1);
 }
 
 // (C) transposing read of K: row 32 ks + 8 lg + b + 4 h, 4 elements at column 16 jt + 4 c.
@@ -58,7 +63,8 @@ __host__ __device__ __forceinline__ int qk_tr_lane(int l16, int lg) {
 }
 __host__ __device__ __forceinline__ int qk_tr_off(int l16, int lg, int xd, int ks, int h, int jt) {
   const int b = l16 >> 2, c = l16 & 3;
-  return (8 * lg + b) * kQkCols + (32 * ks + 4 * h) * kQkCols + ((xd ^ (2 * jt) ^ h) << 3) + 4 * (c & 1);
+  return (8 * lg + b) * kQkCols + (lg >> 1) * kQkGroupPad + (32 * ks + 4 * h) * kQkCols + 2 * ks * kQkGroupPad +
+         ((xd ^ (2 * jt) ^ h) << 3) + 4 * (c & 1);
 }
 
 // (D) transposing read of the W tile for the output product: row 32 ks + 16 h + 4 lg + b,

@@ -155,8 +155,8 @@ constexpr int kGateTok = kCh / kGateParts;   // tokens per gate thread
 constexpr int kGpStride = 12;                // floats per gpart row: 16-byte reads of 16 lanes hit distinct banks
 
 struct H2Lds {
-  uint16_t q[2][kCh * kDh];
-  uint16_t k[2][kCh * kDh];
+  uint16_t q[2][h2::kQkTile];
+  uint16_t k[2][h2::kQkTile];
   float gam[kCh][kGamStride];  // Gamma [t][i]
   uint16_t w[kCh * kRows];     // W = V * Gamma_C / Gamma [s][i], hi and lo
   uint16_t w_lo[kCh * kRows];

@@ -1,6 +1,6 @@
 // Host-side exhaustive check of the chunked HGRN2 kernel's LDS address forms: every factored form in
 // h2_layout.hpp equals the direct layout function (qk_off / vw_off / gv_off) over all of its lane
-// and loop indices.  Built with hipcc and run on the CPU (no GPU call).
+// and loop indices, and each layout maps its tile one-to-one into the tile's storage.  Built with hipcc and run on the CPU (no GPU call).
 #include <hip/hip_runtime.h>
 #include <cstdio>
 #include "h2_layout.hpp"
@@ -38,6 +38,22 @@ int main() {
       for (int u = 0; u < 8; ++u) {
         ++n; if (vw_gate_wr(gi, vw_gate_lane(gi, gp), gp, u) != vw_off(8 * gp + u, gi)) ++bad;
       }
+  // each layout is a bijection of its tile's elements into the tile's storage
+  {
+    static unsigned char seen[kQkTile];
+    for (int r = 0; r < 64; ++r)
+      for (int c = 0; c < kQkCols; ++c) {
+        const int o = qk_off(r, c);
+        ++n; if (o < 0 || o >= kQkTile || seen[o]++) ++bad;
+      }
+    static unsigned char seen_vw[64 * kVwCols], seen_gv[64 * kVwCols];
+    for (int r = 0; r < 64; ++r)
+      for (int c = 0; c < kVwCols; ++c) {
+        const int o = vw_off(r, c), g = gv_off(r, c);
+        ++n; if (o < 0 || o >= 64 * kVwCols || seen_vw[o]++) ++bad;
+        ++n; if (g < 0 || g >= 64 * kVwCols || seen_gv[g]++) ++bad;
+      }
+  }
   printf("%ld cases, %ld mismatches\n", n, bad);
   return bad != 0;
 }
