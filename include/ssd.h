@@ -5,6 +5,7 @@
  * single-step decode update:
  *
  *   RG-LRU        state size 1 per channel          ssd_rglru_scan / ssd_rglru_update
+ *                 (gradients)                       ssd_rglru_scan_backward
  *   MinMax        state size 1 per channel          ssd_minmax_scan / ssd_minmax_update
  *   causal conv   depthwise, width W <= 4           ssd_causal_conv1d / ssd_causal_conv1d_update
  *   selective     N <= 16 states per channel        ssd_selective_scan / ssd_selective_update
@@ -85,6 +86,29 @@ int ssd_rglru_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype,
                    const void* x, const void* r_logit, const void* i_logit,
                    const float* a_log, float c, const float* h0, const void* gate,
                    void* y, float* h_last, void* stream);
+
+/* Gradients of ssd_rglru_scan (reverse-time adjoint; the pages train through autograd and print no
+ * backward pass, so this is the gradient of the forward definition above) for the loss
+ *     sum_{b,t,d} dy * y  +  sum_{b,d} dh_last * h_last:
+ *   g_t = dL/dh_t = dy_t G_t + a_{t+1} g_{t+1} (G_t = gelu(gate_t) or 1; g_{L-1} adds dh_last), and
+ *   dx = g beta i,  d i_logit = g beta x i (1-i),  with l = log a_t = c r a_log,
+ *   dl = g (a h_{t-1} - i x a^2 / beta),  d r_logit = dl c a_log r (1-r),  d a_log = sum_{b,t} dl c r,
+ *   dgate = dy h_t gelu'(gate),  dh0 = a_0 g_0.
+ *   x, r_logit, i_logit, gate, a_log, c, h0 : as ssd_rglru_scan (the forward's inputs)
+ *   dy                  : [B, L, D] (in dtype) gradient of y;   dh_last : [B, D] fp32 or NULL (= 0)
+ *   dx, dr_logit, di_logit : [B, L, D] (out dtype), overwritten
+ *   dgate               : [B, L, D] (out dtype) or NULL; written only when gate is given
+ *   da_log              : [D] fp32, overwritten (not accumulated)
+ *   dh0                 : [B, D] fp32 or NULL
+ * The forward states are recomputed (one forward pass records each 64-step chunk's incoming state in
+ * the library's scratch), so the call needs no saved activations.  Results are deterministic.
+ * Errors as ssd_rglru_scan, plus SSD_ERR_NULL for missing dy / dx / dr_logit / di_logit / da_log. */
+int ssd_rglru_scan_backward(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype,
+                            const void* x, const void* r_logit, const void* i_logit,
+                            const float* a_log, float c, const float* h0, const void* gate,
+                            const void* dy, const float* dh_last,
+                            void* dx, void* dr_logit, void* di_logit, float* da_log, float* dh0,
+                            void* dgate, void* stream);
 
 /* One RG-LRU decode step (RGLRU.step: single token, state carried by the caller).
  *   x, r_logit, i_logit : [B, D] (in dtype);  a_log : [D] fp32;  gate : [B, D] or NULL

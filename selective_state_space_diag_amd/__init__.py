@@ -8,7 +8,7 @@ or eager fallback: importing works without a GPU, but each call raises if the
 library is not built or no GPU is present.
 
 Entry points (same names as the C ABI without the ``ssd_`` prefix):
-    rglru_scan, rglru_update, selective_scan, selective_update, hgrn2_scan, hgrn2_update,
+    rglru_scan, rglru_scan_backward, rglru_update, selective_scan, selective_update, hgrn2_scan, hgrn2_update,
     minmax_scan, minmax_update, causal_conv1d, causal_conv1d_update
 """
 from __future__ import annotations
@@ -27,7 +27,8 @@ STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_
                 5: "SSD_ERR_VALUE", 6: "SSD_ERR_ALIAS", 7: "SSD_ERR_HIP"}
 
 # Every symbol include/ssd.h declares.
-EXPORTS = ("ssd_status_str", "ssd_last_error", "ssd_version", "ssd_rglru_scan", "ssd_rglru_update",
+EXPORTS = ("ssd_status_str", "ssd_last_error", "ssd_version", "ssd_rglru_scan", "ssd_rglru_scan_backward",
+           "ssd_rglru_update",
            "ssd_selective_scan", "ssd_selective_update", "ssd_hgrn2_scan", "ssd_hgrn2_update", "ssd_minmax_scan",
            "ssd_minmax_update", "ssd_causal_conv1d", "ssd_causal_conv1d_update")
 
@@ -64,6 +65,8 @@ def lib() -> ctypes.CDLL:
                                      _fp, _vp, _vp, _fp, _vp]
         L.ssd_rglru_update.argtypes = [_i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _fp, ctypes.c_float, _vp,
                                        _fp, _vp, _vp]
+        L.ssd_rglru_scan_backward.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _fp,
+                                              ctypes.c_float, _fp, _vp, _vp, _fp, _vp, _vp, _vp, _fp, _fp, _vp, _vp]
         L.ssd_minmax_scan.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _fp, _vp, _vp, _fp, _vp]
         L.ssd_minmax_update.argtypes = [_i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _fp, _vp, _vp]
         L.ssd_causal_conv1d.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _fp, _fp, _fp, _vp,
@@ -187,6 +190,30 @@ def rglru_update(x, r_logit, i_logit, a_log, c: float, state, out_dtype=None, ga
                                 _dev(y, "y"), _stream(x.device))
     _raise(st, "rglru_update")
     return y
+
+
+def rglru_scan_backward(x, r_logit, i_logit, a_log, c, dy, h0=None, gate=None, dh_last=None, out_dtype=None):
+    """Gradients of ``rglru_scan`` for the loss sum(dy * y) + sum(dh_last * h_last) (see
+    ``ssd_rglru_scan_backward``).  Returns a dict: dx, dr_logit, di_logit [B, L, D] (out dtype),
+    da_log [D], dh0 [B, D] (fp32), and dgate when a gate is given."""
+    torch = _torch()
+    B, L, D = x.shape
+    code = _act([x, r_logit, i_logit, gate, dy], ["x", "r_logit", "i_logit", "gate", "dy"])
+    oc = _out_code(out_dtype)
+    odt = torch.bfloat16 if oc == SSD_BF16 else torch.float32
+    g = {n: torch.empty((B, L, D), device=x.device, dtype=odt) for n in ("dx", "dr_logit", "di_logit")}
+    if gate is not None:
+        g["dgate"] = torch.empty((B, L, D), device=x.device, dtype=odt)
+    g["da_log"] = torch.empty((D,), device=x.device, dtype=torch.float32)
+    g["dh0"] = torch.empty((B, D), device=x.device, dtype=torch.float32)
+    st = lib().ssd_rglru_scan_backward(
+        B, L, D, code, oc, _dev(x, "x"), _dev(r_logit, "r_logit", x.shape), _dev(i_logit, "i_logit", x.shape),
+        _dev(a_log, "a_log", (D,), torch.float32), float(c), _dev(h0, "h0", (B, D), torch.float32),
+        _dev(gate, "gate", x.shape), _dev(dy, "dy", x.shape), _dev(dh_last, "dh_last", (B, D), torch.float32),
+        _dev(g["dx"], "dx"), _dev(g["dr_logit"], "dr_logit"), _dev(g["di_logit"], "di_logit"),
+        _dev(g["da_log"], "da_log"), _dev(g["dh0"], "dh0"), _dev(g.get("dgate"), "dgate"), _stream(x.device))
+    _raise(st, "rglru_scan_backward")
+    return g
 
 
 # ----------------------------------------------------------------------------- MinMax
@@ -349,6 +376,6 @@ def hgrn2_update(q, k, v, g_logit, lower_bound: float, S, out_dtype=None):
     return o
 
 
-__all__ = ["rglru_scan", "rglru_update", "selective_scan", "selective_update", "hgrn2_scan", "hgrn2_update",
+__all__ = ["rglru_scan", "rglru_scan_backward", "rglru_update", "selective_scan", "selective_update", "hgrn2_scan", "hgrn2_update",
            "minmax_scan", "minmax_update", "causal_conv1d", "causal_conv1d_update", "lib", "LIB_PATH", "EXPORTS",
            "SSDError", "SSDValueError", "SSD_F32", "SSD_BF16"]

@@ -35,7 +35,7 @@ int ok() {
 // process exit.  Purposes are kept apart so that one kernel family never reads another's data.
 // RG-LRU and MinMax share a kind: their launches use the same epoch-tagged lookback protocol, so
 // words left by one never validate for the next launch on the stream.
-enum ScratchKind { kScratchScan1 = 0, kScratchSelective = 1 };
+enum ScratchKind { kScratchScan1 = 0, kScratchSelective = 1, kScratchScan1Bwd = 2 };
 
 struct ScratchBuf {
   void* ptr = nullptr;
@@ -208,6 +208,42 @@ int ssd_rglru_update(int64_t B, int64_t D, int in_dtype, int out_dtype, const vo
   if (n == 0) return ok();
   ssd::RglruUpdateArgs a{B, D, in_dtype == SSD_BF16, out_dtype == SSD_BF16, x, r_logit, i_logit, a_log, c, gate, state, y};
   return hip_status(ssd::launch_rglru_update(a, static_cast<hipStream_t>(stream)), "rglru_update launch");
+}
+
+int ssd_rglru_scan_backward(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype, const void* x,
+                            const void* r_logit, const void* i_logit, const float* a_log, float c, const float* h0,
+                            const void* gate, const void* dy, const float* dh_last, void* dx, void* dr_logit,
+                            void* di_logit, float* da_log, float* dh0, void* dgate, void* stream) {
+  SSD_TRY(check_dtypes(in_dtype, out_dtype));
+  if (B < 0 || L < 0 || D < 0) return fail(SSD_ERR_SHAPE, "negative size");
+  if (too_big({B, L, D}) || D >= (int64_t)1 << 22 || B * ((L + 63) / 64) * ((D + 63) / 64) >= (int64_t)1 << 31)
+    return fail(SSD_ERR_SHAPE, "problem too large");
+  if (!std::isfinite(c)) return fail(SSD_ERR_VALUE, "c must be finite");
+  const int64_t nact = B * L * D;
+  if (nact > 0 && (!x || !r_logit || !i_logit || !dy || !dx || !dr_logit || !di_logit))
+    return fail(SSD_ERR_NULL, "x, r_logit, i_logit, dy, dx, dr_logit and di_logit are required");
+  if (D > 0 && (!a_log || !da_log)) return fail(SSD_ERR_NULL, "a_log and da_log are required");
+  const size_t ab = (size_t)nact * esize(in_dtype), ob = (size_t)nact * esize(out_dtype);
+  const size_t sb = (size_t)(B * D) * 4;
+  std::vector<Span> ins = {{"x", x, ab},           {"r_logit", r_logit, ab}, {"i_logit", i_logit, ab},
+                           {"a_log", a_log, (size_t)D * 4}, {"h0", h0, sb}, {"gate", gate, ab},
+                           {"dy", dy, ab},         {"dh_last", dh_last, sb}};
+  std::vector<Span> outs = {{"dx", dx, ob},        {"dr_logit", dr_logit, ob}, {"di_logit", di_logit, ob},
+                            {"da_log", da_log, (size_t)D * 4}, {"dh0", dh0, sb}, {"dgate", gate ? dgate : nullptr, ob}};
+  std::vector<Span> all = ins;
+  all.insert(all.end(), outs.begin(), outs.end());
+  SSD_TRY(check_align(all));
+  SSD_TRY(check_alias(outs, ins));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (D == 0) return ok();
+  if (nact == 0) {  // no steps: d a_log = 0, dh0 = dh_last
+    SSD_TRY(hip_status(ssd::launch_copy_or_zero(da_log, nullptr, D, s), "rglru_scan_backward"));
+    return hip_status(ssd::launch_copy_or_zero(dh0, dh_last, B * D, s), "rglru_scan_backward");
+  }
+  ssd::RglruBwdArgs a{B, L, D, in_dtype == SSD_BF16, out_dtype == SSD_BF16, x, r_logit, i_logit, a_log, c, h0, gate,
+                      dy, dh_last, dx, dr_logit, di_logit, gate ? dgate : nullptr, da_log, dh0, nullptr};
+  SSD_TRY(get_scratch(stream, kScratchScan1Bwd, ssd::rglru_bwd_scratch_bytes(B, L, D), &a.scratch));
+  return hip_status(ssd::launch_rglru_scan_backward(a, s), "rglru_scan_backward launch");
 }
 
 // ============================================================================ MinMax

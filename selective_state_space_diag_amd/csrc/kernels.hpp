@@ -38,6 +38,26 @@ struct RglruUpdateArgs {
 };
 hipError_t launch_rglru_update(const RglruUpdateArgs& a, hipStream_t s);
 
+// Gradients of the RG-LRU scan (loss = sum dy * y + sum dh_last * h_last): a forward pass that
+// records the chunk carries, a reverse-time pass, and a fixed-order reduction for d a_log.
+struct RglruBwdArgs {
+  int64_t B, L, D;
+  int in_bf16, out_bf16;
+  const void *x, *r_logit, *i_logit;
+  const float* a_log;
+  float c;
+  const float* h0;
+  const void* gate;
+  const void* dy;         // in dtype
+  const float* dh_last;   // [B][D] or NULL
+  void *dx, *dr_logit, *di_logit, *dgate;  // out dtype; dgate may be NULL
+  float* da_log;          // [D]
+  float* dh0;             // [B][D] or NULL
+  void* scratch;          // rglru_bwd_scratch_bytes
+};
+size_t rglru_bwd_scratch_bytes(int64_t B, int64_t L, int64_t D);
+hipError_t launch_rglru_scan_backward(const RglruBwdArgs& a, hipStream_t s);
+
 struct MinmaxScanArgs {
   int64_t B, L, D;
   int in_bf16, out_bf16;

@@ -49,8 +49,9 @@ struct Scan1Params {
   const float* a_log;  // RG-LRU only
   float c;
   const float* h0;
-  void* y;
+  void* y;             // or NULL: no output (a pass that only records chunk carries)
   float* h_last;
+  float* carry_out;    // [B][n_chunks][D]: state entering each chunk, or NULL
   LookbackCtl* ctl;
   unsigned long long* words;  // [unit][3][tile width]: aggregate a, aggregate b, inclusive h
   int one_unit_each;          // grid == number of units: every workgroup takes exactly one ticket
@@ -344,6 +345,7 @@ void scan1_kernel(Scan1Params p) {
         const float incl = Op::apply(Ac, Bc, hin);
         if (u.c == base + kBlock - 1 && u.c + 1 < p.n_chunks) word_store(&W[2 * TW + j], E, incl);
         if (p.h_last && j_ok && u.c == p.n_chunks - 1) p.h_last[u.b * p.D + ch] = incl;
+        if (p.carry_out && j_ok) p.carry_out[(u.b * p.n_chunks + u.c) * p.D + ch] = hin;
         s_carry[j] = hin;
       }
     }
@@ -358,7 +360,7 @@ void scan1_kernel(Scan1Params p) {
       for (int w = 0; w < wave; ++w) hv = Op::apply(s_aggA[w][j], s_aggB[w][j], hv);
       h[v] = hv;
     }
-    {
+    if (p.y) {
       const auto wy = unit_window(p, u, p.y, (int)sizeof(Tout));
       const uint32_t row_bytes = (uint32_t)(p.D * (int64_t)sizeof(Tout));
       const uint32_t lo = (uint32_t)(chl * (int64_t)sizeof(Tout));
@@ -417,6 +419,254 @@ __global__ __launch_bounds__(256) void update1_kernel(Upd1Params p) {
   const float h = Op::apply(a, b, p.state[idx]);
   p.state[idx] = h;
   io<Tout>::store(p.y, idx, GATE ? Op::gated(h, io<Tin>::load(p.gate, idx)) : h);
+}
+
+// ------------------------------------------------------------------ RG-LRU backward
+// Reverse-time adjoint of the affine recurrence (the gradient of  sum dy y + sum dh_last h_last).
+// With e_t = dy_t G_t (G_t = gelu(gate_t), or 1) and q_t the gradient leaving step t towards
+// h_{t-1}:  g_t = dL/dh_t = e_t + q_{t+1},  q_t = a_t g_t,  q_L = dh_last.  So q runs backwards
+// through the affine maps q -> a_t q + a_t e_t: the chunked lookback applies unchanged with the
+// chunks taken in reverse order.  Per step, with h_{t-1} recomputed forward inside the chunk from
+// the chunk's carry-in (recorded by a forward pass), l = log a = c r a_log and b = beta i x:
+//   dx = g beta i,  d i_logit = g beta x i (1 - i),  dl = g h_{t-1} a - g (i x) a^2 / beta,
+//   d r_logit = dl c a_log r (1 - r),  d a_log += dl c r,  d gate = dy h_t gelu'(gate),
+//   and dh0 = q_0.
+// One work unit per workgroup: (batch, 64-channel tile, chunk), one channel per lane, 4 waves x 16
+// steps; units are ticketed in reverse chunk order.
+struct Bwd1Params {
+  int64_t B, L, D;
+  int64_t n_tiles, n_chunks;
+  const void* x;
+  const void* r;
+  const void* i;
+  const void* gate;   // or NULL
+  const void* dy;
+  const float* a_log;
+  float c;
+  const float* carry;    // [B][n_chunks][D] forward state entering each chunk
+  const float* dh_last;  // [B][D] or NULL
+  void* dx;
+  void* dr;
+  void* di;
+  void* dgate;           // or NULL
+  float* dalog_part;     // [B][n_chunks][D]: per-unit partial sums of d a_log
+  float* dh0;            // [B][D] or NULL
+  LookbackCtl* ctl;
+  unsigned long long* words;
+};
+
+// gelu'(v) = Phi(v) + v phi(v), with Phi through the same erf as gelu_f.
+__device__ __forceinline__ float gelu_grad_f(float v) {
+  const float x = fabsf(v) * 0.70710678118654752f;
+  const float t = hw_rcp(fmaf(0.3275911f, x, 1.0f));
+  float poly = fmaf(t, 1.061405429f, -1.453152027f);
+  poly = fmaf(t, poly, 1.421413741f);
+  poly = fmaf(t, poly, -0.284496736f);
+  poly = fmaf(t, poly, 0.254829592f);
+  const float ex = hw_exp2(-(x * x) * kLog2e);  // e^(-v^2/2)
+  const float q = poly * t * ex;                // 1 - erf(|v| / sqrt 2)
+  const float Phi = 0.5f * (v >= 0.0f ? 2.0f - q : q);
+  return Phi + v * (0.3989422804014327f * ex);  // phi(v) = e^(-v^2/2) / sqrt(2 pi)
+}
+
+template <typename Tin, typename Tout, bool GATE>
+__global__ __launch_bounds__(kWaves * 64) void rglru_bwd_kernel(Bwd1Params p) {
+  constexpr int TW = 64;
+  __shared__ unsigned long long s_tick;
+  __shared__ float s_fA[kWaves][TW], s_fB[kWaves][TW];  // forward wave aggregates
+  __shared__ float s_rA[kWaves][TW], s_rB[kWaves][TW];  // reverse wave aggregates
+  __shared__ float s_qin[TW];
+  __shared__ float s_dal[kWaves][TW];
+  using LD = win<Tin, 1, kStreaming>;
+  using ST = win<Tout, 1, kStreaming>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (threadIdx.x == 0) s_tick = atomicAdd(&p.ctl->tick, 1ull);
+  __syncthreads();
+  const uint32_t E = (uint32_t)(s_tick >> 32) + 1u;
+  const int64_t ticket = (int64_t)(s_tick & 0xffffffffull);  // the grid holds exactly one per unit
+  const int64_t per_round = p.B * p.n_tiles;
+  const int64_t cr = ticket / per_round;  // reverse chunk index
+  const int64_t c = p.n_chunks - 1 - cr;
+  const int64_t rr = ticket - cr * per_round;
+  const int64_t b = rr / p.n_tiles, k = rr - b * p.n_tiles;
+  const int rows = (int)min<int64_t>(kChunk, p.L - c * kChunk);
+  const int64_t ch = k * TW + lane;
+  const bool ch_ok = ch < p.D;
+  const int64_t chl = ch_ok ? ch : p.D - 1;
+  const int64_t t0 = c * kChunk + (int64_t)wave * kSteps;
+  const int nvalid = rows - wave * kSteps;
+
+  // ---- loads of the unit's rows (rows past the chunk read its last row; results unused)
+  constexpr int es = sizeof(Tin);
+  auto window = [&](const void* a, int e) {
+    return make_window(static_cast<const char*>(a) + ((b * p.L + c * kChunk) * p.D) * e, (uint32_t)(rows * p.D * e));
+  };
+  const auto wx = window(p.x, es), wr = window(p.r, es), wi = window(p.i, es), wd = window(p.dy, es);
+  const auto wg = window(GATE ? p.gate : p.x, es);
+  const uint32_t row_in = (uint32_t)(p.D * es), lane_in = (uint32_t)(chl * es);
+  typename LD::raw rx[kSteps], rrl[kSteps], ril[kSteps], rdy[kSteps], rg[GATE ? kSteps : 1];
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    const uint32_t ro = (uint32_t)min(wave * kSteps + s, rows - 1) * row_in;
+    rx[s] = LD::load(wx, lane_in, ro);
+    rrl[s] = LD::load(wr, lane_in, ro);
+    ril[s] = LD::load(wi, lane_in, ro);
+    rdy[s] = LD::load(wd, lane_in, ro);
+    if (GATE) rg[GATE ? s : 0] = LD::load(wg, lane_in, ro);
+  }
+  const float kc = p.c * p.a_log[chl] * kLog2e;
+
+  // ---- forward pairs, reverse pairs, and both wave aggregates
+  float av[kSteps], bv[kSteps], ev[kSteps];
+  float fA = 1.0f, fB = 0.0f;
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    const bool ok = ch_ok && (t0 + s < p.L);
+    const float in3[3] = {LD::get(rx[s], 0), LD::get(rrl[s], 0), LD::get(ril[s], 0)};
+    float a, bb;
+    AffineOp::step(in3, AffineOp::Chan{kc}, a, bb);
+    const float G = GATE ? gelu_f(LD::get(rg[GATE ? s : 0], 0)) : 1.0f;
+    av[s] = ok ? a : 1.0f;
+    bv[s] = ok ? bb : 0.0f;
+    ev[s] = ok ? LD::get(rdy[s], 0) * G : 0.0f;
+    fB = fmaf(av[s], fB, bv[s]);
+    fA *= av[s];
+  }
+  float rA = 1.0f, rB = 0.0f;
+#pragma unroll
+  for (int s = kSteps - 1; s >= 0; --s) {
+    rB = fmaf(av[s], rB, av[s] * ev[s]);
+    rA *= av[s];
+  }
+  s_fA[wave][lane] = fA;
+  s_fB[wave][lane] = fB;
+  s_rA[wave][lane] = rA;
+  s_rB[wave][lane] = rB;
+  __syncthreads();
+
+  // ---- wave 0: chunk reverse aggregate, publish, reverse carry (lookback over later chunks)
+  if (wave == 0) {
+    const int64_t seq_unit = (b * p.n_tiles + k) * p.n_chunks;
+    unsigned long long* W = p.words + (seq_unit + cr) * 3 * TW;
+    const int64_t base = (cr / kBlock) * kBlock;
+    const int nprev = (int)(cr - base);
+    float Ac = 1.0f, Bc = 0.0f;
+#pragma unroll
+    for (int w = kWaves - 1; w >= 0; --w) {
+      Bc = fmaf(s_rA[w][lane], Bc, s_rB[w][lane]);
+      Ac *= s_rA[w][lane];
+    }
+    if (cr + 1 < base + kBlock && cr + 1 < p.n_chunks) {
+      word_store(&W[0 * TW + lane], E, Ac);
+      word_store(&W[1 * TW + lane], E, Bc);
+    }
+    unsigned long long wd[1 + 2 * (kBlock - 1)];
+    const unsigned long long* Wb = p.words + (seq_unit + base - 1) * 3 * TW;
+    wd[0] = base > 0 ? word_load(&Wb[2 * TW + lane]) : ((unsigned long long)E << 32);
+#pragma unroll
+    for (int q = 0; q < kBlock - 1; ++q) {
+      const unsigned long long* Wq = p.words + (seq_unit + base + q) * 3 * TW;
+      if (q < nprev) {
+        wd[1 + 2 * q] = word_load(&Wq[0 * TW + lane]);
+        wd[2 + 2 * q] = word_load(&Wq[1 * TW + lane]);
+      } else {
+        wd[1 + 2 * q] = wd[2 + 2 * q] = (unsigned long long)E << 32;
+      }
+    }
+    unsigned int spins = 0;
+    while (true) {
+      bool all = word_ready(wd[0], E);
+#pragma unroll
+      for (int q = 0; q < 2 * (kBlock - 1); ++q) all = all && word_ready(wd[1 + q], E);
+      if (all || spins >= kSpinLimit) break;
+      ++spins;
+      __builtin_amdgcn_s_sleep(1);
+      if (!word_ready(wd[0], E)) wd[0] = word_load(&Wb[2 * TW + lane]);
+#pragma unroll
+      for (int q = 0; q < kBlock - 1; ++q) {
+        const unsigned long long* Wq = p.words + (seq_unit + base + q) * 3 * TW;
+        if (!word_ready(wd[1 + 2 * q], E)) wd[1 + 2 * q] = word_load(&Wq[0 * TW + lane]);
+        if (!word_ready(wd[2 + 2 * q], E)) wd[2 + 2 * q] = word_load(&Wq[1 * TW + lane]);
+      }
+    }
+    if (spins >= kSpinLimit) atomicOr(&p.ctl->error, 1u);
+    float qin = (base > 0) ? word_value(wd[0]) : (p.dh_last ? p.dh_last[b * p.D + chl] : 0.0f);
+#pragma unroll
+    for (int q = 0; q < kBlock - 1; ++q)
+      if (q < nprev) qin = fmaf(word_value(wd[1 + 2 * q]), qin, word_value(wd[2 + 2 * q]));
+    const float incl = fmaf(Ac, qin, Bc);
+    if (cr == base + kBlock - 1 && cr + 1 < p.n_chunks) word_store(&W[2 * TW + lane], E, incl);
+    s_qin[lane] = qin;
+  }
+  __syncthreads();
+
+  // ---- forward states entering each step of this wave
+  float h = p.carry[(b * p.n_chunks + c) * p.D + chl];
+  for (int w = 0; w < wave; ++w) h = fmaf(s_fA[w][lane], h, s_fB[w][lane]);
+  float hp[kSteps];
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    hp[s] = h;
+    h = fmaf(av[s], h, bv[s]);
+  }
+  // ---- reverse carry into this wave, then the per-step gradients, last step first
+  float q = s_qin[lane];
+  for (int w = kWaves - 1; w > wave; --w) q = fmaf(s_rA[w][lane], q, s_rB[w][lane]);
+  const auto wdx = window(p.dx, (int)sizeof(Tout)), wdr = window(p.dr, (int)sizeof(Tout));
+  const auto wdi = window(p.di, (int)sizeof(Tout)), wdg = window(GATE && p.dgate ? p.dgate : p.dx, (int)sizeof(Tout));
+  const uint32_t row_out = (uint32_t)(p.D * (int64_t)sizeof(Tout)), lane_out = (uint32_t)(chl * (int64_t)sizeof(Tout));
+  const float ca = p.c * p.a_log[chl];
+  float dal = 0.0f;
+#pragma unroll
+  for (int s = kSteps - 1; s >= 0; --s) {
+    const float g = ev[s] + q;
+    q = av[s] * g;
+    const float xx = LD::get(rx[s], 0);
+    const float r = sigmoid_f(LD::get(rrl[s], 0));
+    const float i = sigmoid_f(LD::get(ril[s], 0));
+    const float a = av[s];
+    const float beta = hw_sqrt(one_minus_a2(kc * r, a));
+    const float gb = g * beta;
+    const float dl = g * a * (hp[s] - (i * xx) * a * hw_rcp(beta));
+    float o_dx = gb * i, o_di = gb * xx * i * (1.0f - i), o_dr = dl * ca * r * (1.0f - r);
+    const bool ok = ch_ok && s < nvalid;
+    if (ok) {
+      dal = fmaf(dl * p.c, r, dal);
+      const uint32_t ro = (uint32_t)(wave * kSteps + s) * row_out;
+      ST::store(wdx, lane_out, ro, &o_dx);
+      ST::store(wdr, lane_out, ro, &o_dr);
+      ST::store(wdi, lane_out, ro, &o_di);
+      if (GATE && p.dgate) {
+        const float gv = LD::get(rg[GATE ? s : 0], 0);
+        float o_dg = LD::get(rdy[s], 0) * fmaf(a, hp[s], bv[s]) * gelu_grad_f(gv);
+        ST::store(wdg, lane_out, ro, &o_dg);
+      }
+    }
+  }
+  if (p.dh0 && ch_ok && c == 0 && wave == 0) p.dh0[b * p.D + ch] = q;
+  s_dal[wave][lane] = dal;
+  __syncthreads();
+  if (wave == 0 && ch_ok)
+    p.dalog_part[(b * p.n_chunks + c) * p.D + ch] = (s_dal[0][lane] + s_dal[1][lane]) + (s_dal[2][lane] + s_dal[3][lane]);
+
+  // ---- last workgroup to finish resets the ticket and advances the epoch
+  if (threadIdx.x == 0) {
+    const unsigned int old = atomicAdd(&p.ctl->done, 1u);
+    if (old == gridDim.x - 1) {
+      __hip_atomic_store(&p.ctl->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&p.ctl->tick, (unsigned long long)E << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// d a_log[d] = sum over (batch, chunk) of the unit partials, in a fixed order.
+__global__ __launch_bounds__(256) void dalog_reduce_kernel(const float* part, int64_t n, int64_t D, float* out) {
+  const int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (d >= D) return;
+  float acc = 0.0f;
+  for (int64_t u = 0; u < n; ++u) acc += part[u * D + d];
+  out[d] = acc;
 }
 
 // ------------------------------------------------------------------ launchers
@@ -509,6 +759,65 @@ hipError_t launch_minmax_scan(const MinmaxScanArgs& a, hipStream_t s) {
   p.gate = a.gate;
   p.h0 = a.x0; p.y = a.y; p.h_last = a.x_last;
   return launch_scan_op<MinMaxOp>(p, a.in_bf16, a.out_bf16, a.scratch, s);
+}
+
+// Scratch of the backward call: lookback control block and words (sized for the larger of the
+// forward and reverse tilings), then the chunk carries and the d a_log partials.
+namespace {
+int64_t bwd_words_bytes(int64_t B, int64_t L, int64_t D) {
+  const int64_t n_chunks = (L + kChunk - 1) / kChunk;
+  const int64_t fw = (int64_t)scan1_scratch_bytes(B, L, D) - 256;
+  const int64_t rv = B * ((D + 63) / 64) * n_chunks * 3 * 64 * (int64_t)sizeof(unsigned long long);
+  return (std::max(fw, rv) + 255) / 256 * 256;
+}
+}  // namespace
+
+size_t rglru_bwd_scratch_bytes(int64_t B, int64_t L, int64_t D) {
+  const int64_t n_chunks = (L + kChunk - 1) / kChunk;
+  const int64_t per = (B * n_chunks * D * 4 + 255) / 256 * 256;
+  return (size_t)(256 + bwd_words_bytes(B, L, D) + 2 * per);
+}
+
+hipError_t launch_rglru_scan_backward(const RglruBwdArgs& a, hipStream_t s) {
+  const int64_t n_chunks = (a.L + kChunk - 1) / kChunk;
+  const int64_t per = (a.B * n_chunks * a.D * 4 + 255) / 256 * 256;
+  char* base = static_cast<char*>(a.scratch);
+  float* carry = reinterpret_cast<float*>(base + 256 + bwd_words_bytes(a.B, a.L, a.D));
+  float* dal = reinterpret_cast<float*>(reinterpret_cast<char*>(carry) + per);
+  // 1. forward pass that records the state entering every chunk (no outputs)
+  Scan1Params f{};
+  f.B = a.B; f.L = a.L; f.D = a.D;
+  f.in[0] = a.x; f.in[1] = a.r_logit; f.in[2] = a.i_logit;
+  f.a_log = a.a_log; f.c = a.c; f.h0 = a.h0; f.y = nullptr; f.h_last = nullptr; f.carry_out = carry;
+  hipError_t e = launch_scan_op<AffineOp>(f, a.in_bf16, a.out_bf16, a.scratch, s);
+  if (e != hipSuccess) return e;
+  // 2. reverse pass, one workgroup per (batch, 64-channel tile, chunk)
+  Bwd1Params q{};
+  q.B = a.B; q.L = a.L; q.D = a.D;
+  q.n_tiles = (a.D + 63) / 64; q.n_chunks = n_chunks;
+  q.x = a.x; q.r = a.r_logit; q.i = a.i_logit; q.gate = a.gate; q.dy = a.dy;
+  q.a_log = a.a_log; q.c = a.c; q.carry = carry; q.dh_last = a.dh_last;
+  q.dx = a.dx; q.dr = a.dr_logit; q.di = a.di_logit; q.dgate = a.dgate; q.dalog_part = dal; q.dh0 = a.dh0;
+  q.ctl = static_cast<LookbackCtl*>(a.scratch);
+  q.words = reinterpret_cast<unsigned long long*>(base + 256);
+  const dim3 grid((unsigned)(a.B * q.n_tiles * n_chunks)), blk(kWaves * 64);
+  const bool g = a.gate != nullptr;
+  if (!a.in_bf16) {
+    if (g) hipLaunchKernelGGL((rglru_bwd_kernel<float, float, true>), grid, blk, 0, s, q);
+    else hipLaunchKernelGGL((rglru_bwd_kernel<float, float, false>), grid, blk, 0, s, q);
+  } else if (a.out_bf16) {
+    if (g) hipLaunchKernelGGL((rglru_bwd_kernel<bf16_t, bf16_t, true>), grid, blk, 0, s, q);
+    else hipLaunchKernelGGL((rglru_bwd_kernel<bf16_t, bf16_t, false>), grid, blk, 0, s, q);
+  } else {
+    if (g) hipLaunchKernelGGL((rglru_bwd_kernel<bf16_t, float, true>), grid, blk, 0, s, q);
+    else hipLaunchKernelGGL((rglru_bwd_kernel<bf16_t, float, false>), grid, blk, 0, s, q);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // 3. d a_log
+  hipLaunchKernelGGL(dalog_reduce_kernel, dim3((unsigned)((a.D + 255) / 256)), dim3(256), 0, s, dal, a.B * n_chunks,
+                     a.D, a.da_log);
+  return hipGetLastError();
 }
 
 hipError_t launch_rglru_update(const RglruUpdateArgs& a, hipStream_t s) {

@@ -1,0 +1,77 @@
+"""GPU parity of the RG-LRU backward kernels against the gradient oracle (float64 autograd over the
+sequential forward, pinned to finite differences in tests/test_oracle_grad.py), called through the
+C ABI.  Tolerance per gradient tensor, as for the forward: max|err| <= tau * RMS(oracle gradient),
+tau = 1e-5 for fp32 inputs and 2e-2 for bf16 inputs; d a_log, a sum over batch and time, is checked
+to the same relative bound."""
+import numpy as np
+import pytest
+
+import selective_state_space_diag_amd as ssd
+from oracle import grad as og
+from selective_state_space_diag_amd import synth
+from tests.helpers import assert_close, f64, host, to_dev
+
+pytestmark = pytest.mark.gpu
+TOLB = {synth.F32: 1e-5, synth.BF16: 2e-2}
+
+
+def run_bwd(B, L, D, dtype, seed, gated=False, with_h0=True, with_dhl=True):
+    import torch
+    inp = synth.rglru_inputs(B, L, D, dtype, seed, with_h0=with_h0, with_gate=gated)
+    rng = np.random.default_rng(seed + 7)
+    dy32 = rng.standard_normal((B, L, D)).astype(np.float32)
+    dy = synth.Tensor(dtype, synth.f32_to_bf16_bits(dy32)) if dtype == synth.BF16 else synth.Tensor(dtype, dy32)
+    dhl = rng.standard_normal((B, D)).astype(np.float32) if with_dhl else None
+    x, r, i = (to_dev(inp.t[n]) for n in ("x", "r_logit", "i_logit"))
+    G = ssd.rglru_scan_backward(x, r, i, to_dev(inp.p["a_log"]), 8.0, to_dev(dy), h0=to_dev(inp.p.get("h0")),
+                                gate=to_dev(inp.t["gate"]) if gated else None, dh_last=to_dev(dhl))
+    torch.cuda.synchronize()
+    R = og.rglru_scan_grads(f64(inp.t["x"]), f64(inp.t["r_logit"]), f64(inp.t["i_logit"]), f64(inp.p["a_log"]), 8.0,
+                            f64(dy), h0=f64(inp.p.get("h0")), gate=f64(inp.t["gate"]) if gated else None,
+                            dh_last=None if dhl is None else dhl.astype(np.float64))
+    for name in ("dx", "dr_logit", "di_logit", "da_log", "dh0") + (("dgate",) if gated else ()):
+        assert_close(host(G[name]), R[name], TOLB[dtype], name)
+    return G
+
+
+def test_backward_fp32_small():
+    run_bwd(2, 128, 64, synth.F32, 4000)
+
+
+@pytest.mark.parametrize("L,D", [(1, 64), (63, 65), (64, 130), (65, 128), (200, 257)])
+def test_backward_bf16_ragged(L, D):
+    run_bwd(2, L, D, synth.BF16, 4100 + L + D)
+
+
+def test_backward_gated_fp32_long_chain():
+    run_bwd(1, 64 * 9 + 11, 96, synth.F32, 4200, gated=True)
+
+
+def test_backward_gated_bf16_no_state_inputs():
+    run_bwd(3, 150, 192, synth.BF16, 4300, gated=True, with_h0=False, with_dhl=False)
+
+
+def test_backward_deterministic_and_bf16_output():
+    import torch
+    inp = synth.rglru_inputs(2, 300, 256, synth.BF16, 4400, with_h0=True)
+    x, r, i = (to_dev(inp.t[n]) for n in ("x", "r_logit", "i_logit"))
+    dy = torch.randn((2, 300, 256), device="cuda").to(torch.bfloat16)
+    args = (x, r, i, to_dev(inp.p["a_log"]), 8.0, dy)
+    g1 = ssd.rglru_scan_backward(*args, h0=to_dev(inp.p["h0"]))
+    g2 = ssd.rglru_scan_backward(*args, h0=to_dev(inp.p["h0"]))
+    g16 = ssd.rglru_scan_backward(*args, h0=to_dev(inp.p["h0"]), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    for k in g1:
+        assert torch.equal(g1[k], g2[k]), k
+    for k in ("dx", "dr_logit", "di_logit"):
+        assert torch.equal(g16[k], g1[k].to(torch.bfloat16)), k
+
+
+def test_backward_empty_sequence():
+    import torch
+    x = torch.empty((2, 0, 8), device="cuda")
+    dhl = torch.randn((2, 8), device="cuda")
+    a_log = torch.full((8,), -0.05, device="cuda")
+    g = ssd.rglru_scan_backward(x, x, x, a_log, 8.0, x, dh_last=dhl)
+    torch.cuda.synchronize()
+    assert torch.equal(g["dh0"], dhl) and torch.all(g["da_log"] == 0)
