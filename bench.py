@@ -61,6 +61,11 @@ def rglru_gated_bytes(B, L, D, in_b=2, out_b=4):
     return B * L * D * (4 * in_b + out_b) + D * 4
 
 
+def rglru_bwd_bytes(B, L, D, in_b=2, out_b=4):
+    # x, r, i, dy read once; dx, dr_logit, di_logit written; a_log in, d a_log out
+    return B * L * D * (4 * in_b + 3 * out_b) + 2 * D * 4
+
+
 def minmax_bytes(B, L, D, in_b=2, out_b=4):
     return B * L * D * (2 * in_b + out_b)
 
@@ -233,6 +238,12 @@ def forms(args, device):
     ms = time_calls(lambda k: ssd.rglru_scan(x, r, i, a_log, 8.0, gate=gt), 1, 10, 2)[0]
     record("rglru_gated_bf16_B8_L8192_D2560", ms, B * L * D, rglru_gated_bytes(B, L, D))
     del gt
+
+    # --- gradients of the RG-LRU scan on the same shape (dy ~ N(0, 1))
+    dy = randn((B, L, D))
+    ms = time_calls(lambda k: ssd.rglru_scan_backward(x, r, i, a_log, 8.0, dy), 1, 5, 1)[0]
+    record("rglru_backward_bf16_B8_L8192_D2560", ms, B * L * D, rglru_bwd_bytes(B, L, D))
+    del dy
 
     # --- MinMax scan on the same shape (r, s ~ N(0, 1))
     ms = time_calls(lambda k: ssd.minmax_scan(r, i), 1, 10, 2)[0]

@@ -660,12 +660,22 @@ __global__ __launch_bounds__(kWaves * 64) void rglru_bwd_kernel(Bwd1Params p) {
   }
 }
 
-// d a_log[d] = sum over (batch, chunk) of the unit partials, in a fixed order.
-__global__ __launch_bounds__(256) void dalog_reduce_kernel(const float* part, int64_t n, int64_t D, float* out) {
+// d a_log[d] = sum over (batch, chunk) of the unit partials, in a fixed order: slice s of
+// kDalSlices sums units [s n / S, (s + 1) n / S), then the slices are added in order.
+constexpr int kDalSlices = 32;
+__global__ __launch_bounds__(256) void dalog_slice_kernel(const float* part, int64_t n, int64_t D, float* slices) {
+  const int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (d >= D) return;
+  const int64_t s = blockIdx.y, u0 = s * n / kDalSlices, u1 = (s + 1) * n / kDalSlices;
+  float acc = 0.0f;
+  for (int64_t u = u0; u < u1; ++u) acc += part[u * D + d];
+  slices[s * D + d] = acc;
+}
+__global__ __launch_bounds__(256) void dalog_final_kernel(const float* slices, int64_t D, float* out) {
   const int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (d >= D) return;
   float acc = 0.0f;
-  for (int64_t u = 0; u < n; ++u) acc += part[u * D + d];
+  for (int s = 0; s < kDalSlices; ++s) acc += slices[s * D + d];
   out[d] = acc;
 }
 
@@ -775,7 +785,7 @@ int64_t bwd_words_bytes(int64_t B, int64_t L, int64_t D) {
 size_t rglru_bwd_scratch_bytes(int64_t B, int64_t L, int64_t D) {
   const int64_t n_chunks = (L + kChunk - 1) / kChunk;
   const int64_t per = (B * n_chunks * D * 4 + 255) / 256 * 256;
-  return (size_t)(256 + bwd_words_bytes(B, L, D) + 2 * per);
+  return (size_t)(256 + bwd_words_bytes(B, L, D) + 2 * per + (int64_t)kDalSlices * D * 4);
 }
 
 hipError_t launch_rglru_scan_backward(const RglruBwdArgs& a, hipStream_t s) {
@@ -815,8 +825,10 @@ hipError_t launch_rglru_scan_backward(const RglruBwdArgs& a, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // 3. d a_log
-  hipLaunchKernelGGL(dalog_reduce_kernel, dim3((unsigned)((a.D + 255) / 256)), dim3(256), 0, s, dal, a.B * n_chunks,
-                     a.D, a.da_log);
+  float* slices = reinterpret_cast<float*>(reinterpret_cast<char*>(dal) + per);
+  const unsigned nb = (unsigned)((a.D + 255) / 256);
+  hipLaunchKernelGGL(dalog_slice_kernel, dim3(nb, kDalSlices), dim3(256), 0, s, dal, a.B * n_chunks, a.D, slices);
+  hipLaunchKernelGGL(dalog_final_kernel, dim3(nb), dim3(256), 0, s, slices, a.D, a.da_log);
   return hipGetLastError();
 }
 
