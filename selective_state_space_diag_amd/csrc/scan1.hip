@@ -469,16 +469,19 @@ __device__ __forceinline__ float gelu_grad_f(float v) {
   return Phi + v * (0.3989422804014327f * ex);  // phi(v) = e^(-v^2/2) / sqrt(2 pi)
 }
 
-template <typename Tin, typename Tout, bool GATE>
-__global__ __launch_bounds__(kWaves * 64) void rglru_bwd_kernel(Bwd1Params p) {
-  constexpr int TW = 64;
+constexpr int kBWaves = 8;                 // waves of a backward workgroup
+constexpr int kBSteps = kChunk / kBWaves;  // steps per wave
+
+template <typename Tin, typename Tout, int V, bool GATE>
+__global__ __launch_bounds__(kBWaves * 64) void rglru_bwd_kernel(Bwd1Params p) {
+  constexpr int TW = 64 * V;  // channels per tile
   __shared__ unsigned long long s_tick;
-  __shared__ float s_fA[kWaves][TW], s_fB[kWaves][TW];  // forward wave aggregates
-  __shared__ float s_rA[kWaves][TW], s_rB[kWaves][TW];  // reverse wave aggregates
+  __shared__ float s_fA[kBWaves][TW], s_fB[kBWaves][TW];  // forward wave aggregates
+  __shared__ float s_rA[kBWaves][TW], s_rB[kBWaves][TW];  // reverse wave aggregates
   __shared__ float s_qin[TW];
-  __shared__ float s_dal[kWaves][TW];
-  using LD = win<Tin, 1, kStreaming>;
-  using ST = win<Tout, 1, kStreaming>;
+  __shared__ float s_dal[kBWaves][TW];
+  using LD = win<Tin, V, kStreaming>;
+  using ST = win<Tout, V, kStreaming>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (threadIdx.x == 0) s_tick = atomicAdd(&p.ctl->tick, 1ull);
@@ -491,11 +494,11 @@ __global__ __launch_bounds__(kWaves * 64) void rglru_bwd_kernel(Bwd1Params p) {
   const int64_t rr = ticket - cr * per_round;
   const int64_t b = rr / p.n_tiles, k = rr - b * p.n_tiles;
   const int rows = (int)min<int64_t>(kChunk, p.L - c * kChunk);
-  const int64_t ch = k * TW + lane;
-  const bool ch_ok = ch < p.D;
-  const int64_t chl = ch_ok ? ch : p.D - 1;
-  const int64_t t0 = c * kChunk + (int64_t)wave * kSteps;
-  const int nvalid = rows - wave * kSteps;
+  const int64_t ch0 = k * TW + (int64_t)lane * V;
+  const bool ch_ok = ch0 < p.D;  // V = 2 only when D is even
+  const int64_t chl = ch_ok ? ch0 : p.D - V;
+  const int64_t t0 = c * kChunk + (int64_t)wave * kBSteps;
+  const int nvalid = rows - wave * kBSteps;
 
   // ---- loads of the unit's rows (rows past the chunk read its last row; results unused)
   constexpr int es = sizeof(Tin);
@@ -505,71 +508,84 @@ __global__ __launch_bounds__(kWaves * 64) void rglru_bwd_kernel(Bwd1Params p) {
   const auto wx = window(p.x, es), wr = window(p.r, es), wi = window(p.i, es), wd = window(p.dy, es);
   const auto wg = window(GATE ? p.gate : p.x, es);
   const uint32_t row_in = (uint32_t)(p.D * es), lane_in = (uint32_t)(chl * es);
-  typename LD::raw rx[kSteps], rrl[kSteps], ril[kSteps], rdy[kSteps], rg[GATE ? kSteps : 1];
+  typename LD::raw rx[kBSteps], rrl[kBSteps], ril[kBSteps], rdy[kBSteps], rg[GATE ? kBSteps : 1];
 #pragma unroll
-  for (int s = 0; s < kSteps; ++s) {
-    const uint32_t ro = (uint32_t)min(wave * kSteps + s, rows - 1) * row_in;
+  for (int s = 0; s < kBSteps; ++s) {
+    const uint32_t ro = (uint32_t)min(wave * kBSteps + s, rows - 1) * row_in;
     rx[s] = LD::load(wx, lane_in, ro);
     rrl[s] = LD::load(wr, lane_in, ro);
     ril[s] = LD::load(wi, lane_in, ro);
     rdy[s] = LD::load(wd, lane_in, ro);
     if (GATE) rg[GATE ? s : 0] = LD::load(wg, lane_in, ro);
   }
-  const float kc = p.c * p.a_log[chl] * kLog2e;
+  float kc[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) kc[v] = p.c * p.a_log[chl + v] * kLog2e;
 
   // ---- forward pairs, reverse pairs, and both wave aggregates
-  float av[kSteps], bv[kSteps], ev[kSteps];
-  float fA = 1.0f, fB = 0.0f;
+  float av[kBSteps][V], bv[kBSteps][V], ev[kBSteps][V];
+  float fA[V], fB[V], rA[V], rB[V];
 #pragma unroll
-  for (int s = 0; s < kSteps; ++s) {
+  for (int v = 0; v < V; ++v) { fA[v] = 1.0f; fB[v] = 0.0f; rA[v] = 1.0f; rB[v] = 0.0f; }
+#pragma unroll
+  for (int s = 0; s < kBSteps; ++s) {
     const bool ok = ch_ok && (t0 + s < p.L);
-    const float in3[3] = {LD::get(rx[s], 0), LD::get(rrl[s], 0), LD::get(ril[s], 0)};
-    float a, bb;
-    AffineOp::step(in3, AffineOp::Chan{kc}, a, bb);
-    const float G = GATE ? gelu_f(LD::get(rg[GATE ? s : 0], 0)) : 1.0f;
-    av[s] = ok ? a : 1.0f;
-    bv[s] = ok ? bb : 0.0f;
-    ev[s] = ok ? LD::get(rdy[s], 0) * G : 0.0f;
-    fB = fmaf(av[s], fB, bv[s]);
-    fA *= av[s];
-  }
-  float rA = 1.0f, rB = 0.0f;
 #pragma unroll
-  for (int s = kSteps - 1; s >= 0; --s) {
-    rB = fmaf(av[s], rB, av[s] * ev[s]);
-    rA *= av[s];
+    for (int v = 0; v < V; ++v) {
+      const float in3[3] = {LD::get(rx[s], v), LD::get(rrl[s], v), LD::get(ril[s], v)};
+      float a, bb;
+      AffineOp::step(in3, AffineOp::Chan{kc[v]}, a, bb);
+      const float G = GATE ? gelu_f(LD::get(rg[GATE ? s : 0], v)) : 1.0f;
+      av[s][v] = ok ? a : 1.0f;
+      bv[s][v] = ok ? bb : 0.0f;
+      ev[s][v] = ok ? LD::get(rdy[s], v) * G : 0.0f;
+      fB[v] = fmaf(av[s][v], fB[v], bv[s][v]);
+      fA[v] *= av[s][v];
+    }
   }
-  s_fA[wave][lane] = fA;
-  s_fB[wave][lane] = fB;
-  s_rA[wave][lane] = rA;
-  s_rB[wave][lane] = rB;
+#pragma unroll
+  for (int s = kBSteps - 1; s >= 0; --s)
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      rB[v] = fmaf(av[s][v], rB[v], av[s][v] * ev[s][v]);
+      rA[v] *= av[s][v];
+    }
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    s_fA[wave][lane * V + v] = fA[v];
+    s_fB[wave][lane * V + v] = fB[v];
+    s_rA[wave][lane * V + v] = rA[v];
+    s_rB[wave][lane * V + v] = rB[v];
+  }
   __syncthreads();
 
-  // ---- wave 0: chunk reverse aggregate, publish, reverse carry (lookback over later chunks)
-  if (wave == 0) {
+  // ---- waves 0 .. V-1: chunk reverse aggregate, publish, reverse carry (lookback over later
+  //      chunks), one channel of the tile per lane
+  if (wave < V) {
+    const int j = wave * 64 + lane;
     const int64_t seq_unit = (b * p.n_tiles + k) * p.n_chunks;
     unsigned long long* W = p.words + (seq_unit + cr) * 3 * TW;
     const int64_t base = (cr / kBlock) * kBlock;
     const int nprev = (int)(cr - base);
     float Ac = 1.0f, Bc = 0.0f;
 #pragma unroll
-    for (int w = kWaves - 1; w >= 0; --w) {
-      Bc = fmaf(s_rA[w][lane], Bc, s_rB[w][lane]);
-      Ac *= s_rA[w][lane];
+    for (int w = kBWaves - 1; w >= 0; --w) {
+      Bc = fmaf(s_rA[w][j], Bc, s_rB[w][j]);
+      Ac *= s_rA[w][j];
     }
     if (cr + 1 < base + kBlock && cr + 1 < p.n_chunks) {
-      word_store(&W[0 * TW + lane], E, Ac);
-      word_store(&W[1 * TW + lane], E, Bc);
+      word_store(&W[0 * TW + j], E, Ac);
+      word_store(&W[1 * TW + j], E, Bc);
     }
     unsigned long long wd[1 + 2 * (kBlock - 1)];
     const unsigned long long* Wb = p.words + (seq_unit + base - 1) * 3 * TW;
-    wd[0] = base > 0 ? word_load(&Wb[2 * TW + lane]) : ((unsigned long long)E << 32);
+    wd[0] = base > 0 ? word_load(&Wb[2 * TW + j]) : ((unsigned long long)E << 32);
 #pragma unroll
     for (int q = 0; q < kBlock - 1; ++q) {
       const unsigned long long* Wq = p.words + (seq_unit + base + q) * 3 * TW;
       if (q < nprev) {
-        wd[1 + 2 * q] = word_load(&Wq[0 * TW + lane]);
-        wd[2 + 2 * q] = word_load(&Wq[1 * TW + lane]);
+        wd[1 + 2 * q] = word_load(&Wq[0 * TW + j]);
+        wd[2 + 2 * q] = word_load(&Wq[1 * TW + j]);
       } else {
         wd[1 + 2 * q] = wd[2 + 2 * q] = (unsigned long long)E << 32;
       }
@@ -582,73 +598,94 @@ __global__ __launch_bounds__(kWaves * 64) void rglru_bwd_kernel(Bwd1Params p) {
       if (all || spins >= kSpinLimit) break;
       ++spins;
       __builtin_amdgcn_s_sleep(1);
-      if (!word_ready(wd[0], E)) wd[0] = word_load(&Wb[2 * TW + lane]);
+      if (!word_ready(wd[0], E)) wd[0] = word_load(&Wb[2 * TW + j]);
 #pragma unroll
       for (int q = 0; q < kBlock - 1; ++q) {
         const unsigned long long* Wq = p.words + (seq_unit + base + q) * 3 * TW;
-        if (!word_ready(wd[1 + 2 * q], E)) wd[1 + 2 * q] = word_load(&Wq[0 * TW + lane]);
-        if (!word_ready(wd[2 + 2 * q], E)) wd[2 + 2 * q] = word_load(&Wq[1 * TW + lane]);
+        if (!word_ready(wd[1 + 2 * q], E)) wd[1 + 2 * q] = word_load(&Wq[0 * TW + j]);
+        if (!word_ready(wd[2 + 2 * q], E)) wd[2 + 2 * q] = word_load(&Wq[1 * TW + j]);
       }
     }
     if (spins >= kSpinLimit) atomicOr(&p.ctl->error, 1u);
-    float qin = (base > 0) ? word_value(wd[0]) : (p.dh_last ? p.dh_last[b * p.D + chl] : 0.0f);
+    const int64_t chj = k * TW + j;
+    const int64_t chjl = chj < p.D ? chj : p.D - 1;
+    float qin = (base > 0) ? word_value(wd[0]) : (p.dh_last ? p.dh_last[b * p.D + chjl] : 0.0f);
 #pragma unroll
     for (int q = 0; q < kBlock - 1; ++q)
       if (q < nprev) qin = fmaf(word_value(wd[1 + 2 * q]), qin, word_value(wd[2 + 2 * q]));
     const float incl = fmaf(Ac, qin, Bc);
-    if (cr == base + kBlock - 1 && cr + 1 < p.n_chunks) word_store(&W[2 * TW + lane], E, incl);
-    s_qin[lane] = qin;
+    if (cr == base + kBlock - 1 && cr + 1 < p.n_chunks) word_store(&W[2 * TW + j], E, incl);
+    s_qin[j] = qin;
   }
   __syncthreads();
 
-  // ---- forward states entering each step of this wave
-  float h = p.carry[(b * p.n_chunks + c) * p.D + chl];
-  for (int w = 0; w < wave; ++w) h = fmaf(s_fA[w][lane], h, s_fB[w][lane]);
-  float hp[kSteps];
+  // ---- forward states entering each step of this wave, and the reverse carry into it
+  float hp[kBSteps][V], q[V];
 #pragma unroll
-  for (int s = 0; s < kSteps; ++s) {
-    hp[s] = h;
-    h = fmaf(av[s], h, bv[s]);
+  for (int v = 0; v < V; ++v) {
+    const int j = lane * V + v;
+    float h = p.carry[(b * p.n_chunks + c) * p.D + chl + v];
+    for (int w = 0; w < wave; ++w) h = fmaf(s_fA[w][j], h, s_fB[w][j]);
+#pragma unroll
+    for (int s = 0; s < kBSteps; ++s) {
+      hp[s][v] = h;
+      h = fmaf(av[s][v], h, bv[s][v]);
+    }
+    float qq = s_qin[j];
+    for (int w = kBWaves - 1; w > wave; --w) qq = fmaf(s_rA[w][j], qq, s_rB[w][j]);
+    q[v] = qq;
   }
-  // ---- reverse carry into this wave, then the per-step gradients, last step first
-  float q = s_qin[lane];
-  for (int w = kWaves - 1; w > wave; --w) q = fmaf(s_rA[w][lane], q, s_rB[w][lane]);
+  // ---- per-step gradients, last step first
   const auto wdx = window(p.dx, (int)sizeof(Tout)), wdr = window(p.dr, (int)sizeof(Tout));
   const auto wdi = window(p.di, (int)sizeof(Tout)), wdg = window(GATE && p.dgate ? p.dgate : p.dx, (int)sizeof(Tout));
   const uint32_t row_out = (uint32_t)(p.D * (int64_t)sizeof(Tout)), lane_out = (uint32_t)(chl * (int64_t)sizeof(Tout));
-  const float ca = p.c * p.a_log[chl];
-  float dal = 0.0f;
+  float ca[V], dal[V];
 #pragma unroll
-  for (int s = kSteps - 1; s >= 0; --s) {
-    const float g = ev[s] + q;
-    q = av[s] * g;
-    const float xx = LD::get(rx[s], 0);
-    const float r = sigmoid_f(LD::get(rrl[s], 0));
-    const float i = sigmoid_f(LD::get(ril[s], 0));
-    const float a = av[s];
-    const float beta = hw_sqrt(one_minus_a2(kc * r, a));
-    const float gb = g * beta;
-    const float dl = g * a * (hp[s] - (i * xx) * a * hw_rcp(beta));
-    float o_dx = gb * i, o_di = gb * xx * i * (1.0f - i), o_dr = dl * ca * r * (1.0f - r);
-    const bool ok = ch_ok && s < nvalid;
-    if (ok) {
-      dal = fmaf(dl * p.c, r, dal);
-      const uint32_t ro = (uint32_t)(wave * kSteps + s) * row_out;
-      ST::store(wdx, lane_out, ro, &o_dx);
-      ST::store(wdr, lane_out, ro, &o_dr);
-      ST::store(wdi, lane_out, ro, &o_di);
-      if (GATE && p.dgate) {
-        const float gv = LD::get(rg[GATE ? s : 0], 0);
-        float o_dg = LD::get(rdy[s], 0) * fmaf(a, hp[s], bv[s]) * gelu_grad_f(gv);
-        ST::store(wdg, lane_out, ro, &o_dg);
-      }
+  for (int v = 0; v < V; ++v) { ca[v] = p.c * p.a_log[chl + v]; dal[v] = 0.0f; }
+#pragma unroll
+  for (int s = kBSteps - 1; s >= 0; --s) {
+    float o_dx[V], o_dr[V], o_di[V], o_dg[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const float g = ev[s][v] + q[v];
+      q[v] = av[s][v] * g;
+      const float xx = LD::get(rx[s], v);
+      const float r = sigmoid_f(LD::get(rrl[s], v));
+      const float i = sigmoid_f(LD::get(ril[s], v));
+      const float a = av[s][v];
+      const float beta = hw_sqrt(one_minus_a2(kc[v] * r, a));
+      const float gb = g * beta;
+      const float dl = g * a * (hp[s][v] - (i * xx) * a * hw_rcp(beta));
+      o_dx[v] = gb * i;
+      o_di[v] = gb * xx * i * (1.0f - i);
+      o_dr[v] = dl * ca[v] * r * (1.0f - r);
+      if (s < nvalid) dal[v] = fmaf(dl * p.c, r, dal[v]);
+      if (GATE) o_dg[v] = LD::get(rdy[s], v) * fmaf(a, hp[s][v], bv[s][v]) * gelu_grad_f(LD::get(rg[GATE ? s : 0], v));
+    }
+    if (ch_ok && s < nvalid) {
+      const uint32_t ro = (uint32_t)(wave * kBSteps + s) * row_out;
+      ST::store(wdx, lane_out, ro, o_dx);
+      ST::store(wdr, lane_out, ro, o_dr);
+      ST::store(wdi, lane_out, ro, o_di);
+      if (GATE && p.dgate) ST::store(wdg, lane_out, ro, o_dg);
     }
   }
-  if (p.dh0 && ch_ok && c == 0 && wave == 0) p.dh0[b * p.D + ch] = q;
-  s_dal[wave][lane] = dal;
+  if (p.dh0 && ch_ok && c == 0 && wave == 0)
+#pragma unroll
+    for (int v = 0; v < V; ++v) p.dh0[b * p.D + ch0 + v] = q[v];
+#pragma unroll
+  for (int v = 0; v < V; ++v) s_dal[wave][lane * V + v] = ch_ok ? dal[v] : 0.0f;
   __syncthreads();
-  if (wave == 0 && ch_ok)
-    p.dalog_part[(b * p.n_chunks + c) * p.D + ch] = (s_dal[0][lane] + s_dal[1][lane]) + (s_dal[2][lane] + s_dal[3][lane]);
+  if (wave < V) {
+    const int j = wave * 64 + lane;
+    const int64_t chj = k * TW + j;
+    if (chj < p.D) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kBWaves; ++w) acc += s_dal[w][j];
+      p.dalog_part[(b * p.n_chunks + c) * p.D + chj] = acc;
+    }
+  }
 
   // ---- last workgroup to finish resets the ticket and advances the epoch
   if (threadIdx.x == 0) {
@@ -771,14 +808,26 @@ hipError_t launch_minmax_scan(const MinmaxScanArgs& a, hipStream_t s) {
   return launch_scan_op<MinMaxOp>(p, a.in_bf16, a.out_bf16, a.scratch, s);
 }
 
+template <int V, bool G>
+hipError_t launch_bwd_g(const Bwd1Params& q, int in_bf16, int out_bf16, dim3 grid, hipStream_t s) {
+  const dim3 blk(kBWaves * 64);
+  if (!in_bf16) hipLaunchKernelGGL((rglru_bwd_kernel<float, float, V, G>), grid, blk, 0, s, q);
+  else if (out_bf16) hipLaunchKernelGGL((rglru_bwd_kernel<bf16_t, bf16_t, V, G>), grid, blk, 0, s, q);
+  else hipLaunchKernelGGL((rglru_bwd_kernel<bf16_t, float, V, G>), grid, blk, 0, s, q);
+  return hipGetLastError();
+}
+template <int V>
+hipError_t launch_bwd_dt(const Bwd1Params& q, bool gate, int in_bf16, int out_bf16, dim3 grid, hipStream_t s) {
+  return gate ? launch_bwd_g<V, true>(q, in_bf16, out_bf16, grid, s) : launch_bwd_g<V, false>(q, in_bf16, out_bf16, grid, s);
+}
+
 // Scratch of the backward call: lookback control block and words (sized for the larger of the
 // forward and reverse tilings), then the chunk carries and the d a_log partials.
 namespace {
+// The reverse pass uses the same tiling as the forward (64 V channels per tile, V = 2 for even D),
+// so one word layout serves both.
 int64_t bwd_words_bytes(int64_t B, int64_t L, int64_t D) {
-  const int64_t n_chunks = (L + kChunk - 1) / kChunk;
-  const int64_t fw = (int64_t)scan1_scratch_bytes(B, L, D) - 256;
-  const int64_t rv = B * ((D + 63) / 64) * n_chunks * 3 * 64 * (int64_t)sizeof(unsigned long long);
-  return (std::max(fw, rv) + 255) / 256 * 256;
+  return ((int64_t)scan1_scratch_bytes(B, L, D) - 256 + 255) / 256 * 256;
 }
 }  // namespace
 
@@ -802,27 +851,18 @@ hipError_t launch_rglru_scan_backward(const RglruBwdArgs& a, hipStream_t s) {
   hipError_t e = launch_scan_op<AffineOp>(f, a.in_bf16, a.out_bf16, a.scratch, s);
   if (e != hipSuccess) return e;
   // 2. reverse pass, one workgroup per (batch, 64-channel tile, chunk)
+  const int V = vec_width(a.D);
   Bwd1Params q{};
   q.B = a.B; q.L = a.L; q.D = a.D;
-  q.n_tiles = (a.D + 63) / 64; q.n_chunks = n_chunks;
+  q.n_tiles = (a.D + 64 * V - 1) / (64 * V); q.n_chunks = n_chunks;
   q.x = a.x; q.r = a.r_logit; q.i = a.i_logit; q.gate = a.gate; q.dy = a.dy;
   q.a_log = a.a_log; q.c = a.c; q.carry = carry; q.dh_last = a.dh_last;
   q.dx = a.dx; q.dr = a.dr_logit; q.di = a.di_logit; q.dgate = a.dgate; q.dalog_part = dal; q.dh0 = a.dh0;
   q.ctl = static_cast<LookbackCtl*>(a.scratch);
   q.words = reinterpret_cast<unsigned long long*>(base + 256);
-  const dim3 grid((unsigned)(a.B * q.n_tiles * n_chunks)), blk(kWaves * 64);
-  const bool g = a.gate != nullptr;
-  if (!a.in_bf16) {
-    if (g) hipLaunchKernelGGL((rglru_bwd_kernel<float, float, true>), grid, blk, 0, s, q);
-    else hipLaunchKernelGGL((rglru_bwd_kernel<float, float, false>), grid, blk, 0, s, q);
-  } else if (a.out_bf16) {
-    if (g) hipLaunchKernelGGL((rglru_bwd_kernel<bf16_t, bf16_t, true>), grid, blk, 0, s, q);
-    else hipLaunchKernelGGL((rglru_bwd_kernel<bf16_t, bf16_t, false>), grid, blk, 0, s, q);
-  } else {
-    if (g) hipLaunchKernelGGL((rglru_bwd_kernel<bf16_t, float, true>), grid, blk, 0, s, q);
-    else hipLaunchKernelGGL((rglru_bwd_kernel<bf16_t, float, false>), grid, blk, 0, s, q);
-  }
-  e = hipGetLastError();
+  const dim3 grid((unsigned)(a.B * q.n_tiles * n_chunks));
+  if (V == 2) e = launch_bwd_dt<2>(q, a.gate != nullptr, a.in_bf16, a.out_bf16, grid, s);
+  else e = launch_bwd_dt<1>(q, a.gate != nullptr, a.in_bf16, a.out_bf16, grid, s);
   if (e != hipSuccess) return e;
   // 3. d a_log
   float* slices = reinterpret_cast<float*>(reinterpret_cast<char*>(dal) + per);
