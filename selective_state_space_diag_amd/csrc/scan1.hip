@@ -49,9 +49,9 @@ struct Scan1Params {
   const float* a_log;  // RG-LRU only
   float c;
   const float* h0;
-  void* y;             // or NULL: no output (a pass that only records chunk carries)
+  void* y;
   float* h_last;
-  float* carry_out;    // [B][n_chunks][D]: state entering each chunk, or NULL
+  float* carry_out;    // [B][n_chunks][D]: state entering each chunk (record passes)
   LookbackCtl* ctl;
   unsigned long long* words;  // [unit][3][tile width]: aggregate a, aggregate b, inclusive h
   int one_unit_each;          // grid == number of units: every workgroup takes exactly one ticket
@@ -202,7 +202,8 @@ __device__ __forceinline__ void fetch_gate(const Scan1Params& p, const Unit& u, 
 // Occupancy hint: with bf16 inputs the kernel fits 3 workgroups per SIMD group without spills.
 template <typename Tin> constexpr int waves_per_eu() { return sizeof(Tin) == 2 ? 3 : 1; }
 
-template <class Op, typename Tin, typename Tout, int V, bool GATE>
+// RECORD: a pass that stores no outputs and records the state entering every chunk (carry_out).
+template <class Op, typename Tin, typename Tout, int V, bool GATE, bool RECORD>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(waves_per_eu<Tin>())))
 void scan1_kernel(Scan1Params p) {
   constexpr int TW = 64 * V;  // channels per tile
@@ -345,7 +346,7 @@ void scan1_kernel(Scan1Params p) {
         const float incl = Op::apply(Ac, Bc, hin);
         if (u.c == base + kBlock - 1 && u.c + 1 < p.n_chunks) word_store(&W[2 * TW + j], E, incl);
         if (p.h_last && j_ok && u.c == p.n_chunks - 1) p.h_last[u.b * p.D + ch] = incl;
-        if (p.carry_out && j_ok) p.carry_out[(u.b * p.n_chunks + u.c) * p.D + ch] = hin;
+        if (RECORD && j_ok) p.carry_out[(u.b * p.n_chunks + u.c) * p.D + ch] = hin;
         s_carry[j] = hin;
       }
     }
@@ -360,7 +361,7 @@ void scan1_kernel(Scan1Params p) {
       for (int w = 0; w < wave; ++w) hv = Op::apply(s_aggA[w][j], s_aggB[w][j], hv);
       h[v] = hv;
     }
-    if (p.y) {
+    if (!RECORD) {
       const auto wy = unit_window(p, u, p.y, (int)sizeof(Tout));
       const uint32_t row_bytes = (uint32_t)(p.D * (int64_t)sizeof(Tout));
       const uint32_t lo = (uint32_t)(chl * (int64_t)sizeof(Tout));
@@ -719,7 +720,7 @@ __global__ __launch_bounds__(256) void dalog_final_kernel(const float* slices, i
 // ------------------------------------------------------------------ launchers
 // Persistent grid: as many workgroups as stay resident together (by the kernel's own occupancy),
 // never more than there are work units.
-template <class Op, typename Tin, typename Tout, int V, bool GATE>
+template <class Op, typename Tin, typename Tout, int V, bool GATE, bool RECORD>
 hipError_t launch_scan_t(const Scan1Params& p, hipStream_t s) {
   const int64_t total = p.B * p.n_tiles * p.n_chunks;
   static int per_cu = 0, cus = 0;
@@ -728,34 +729,50 @@ hipError_t launch_scan_t(const Scan1Params& p, hipStream_t s) {
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan1_kernel<Op, Tin, Tout, V, GATE>, kWaves * 64,
-                                                     0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan1_kernel<Op, Tin, Tout, V, GATE, RECORD>,
+                                                     kWaves * 64, 0) != hipSuccess ||
         per_cu <= 0)
       per_cu = 1;
   }
   const int64_t grid = std::min<int64_t>(total, (int64_t)per_cu * cus);
   Scan1Params q = p;
   q.one_unit_each = grid == total;
-  hipLaunchKernelGGL((scan1_kernel<Op, Tin, Tout, V, GATE>), dim3((unsigned)grid), dim3(kWaves * 64), 0, s, q);
+  hipLaunchKernelGGL((scan1_kernel<Op, Tin, Tout, V, GATE, RECORD>), dim3((unsigned)grid), dim3(kWaves * 64), 0, s, q);
   return hipGetLastError();
 }
 
 template <class Op, int V, bool GATE>
 hipError_t launch_scan_dt(const Scan1Params& p, int in_bf16, int out_bf16, hipStream_t s) {
-  if (!in_bf16) return launch_scan_t<Op, float, float, V, GATE>(p, s);
-  return out_bf16 ? launch_scan_t<Op, bf16_t, bf16_t, V, GATE>(p, s) : launch_scan_t<Op, bf16_t, float, V, GATE>(p, s);
+  if (!in_bf16) return launch_scan_t<Op, float, float, V, GATE, false>(p, s);
+  return out_bf16 ? launch_scan_t<Op, bf16_t, bf16_t, V, GATE, false>(p, s)
+                  : launch_scan_t<Op, bf16_t, float, V, GATE, false>(p, s);
 }
 
 int vec_width(int64_t D) { return (D % 2 == 0) ? 2 : 1; }
 
 template <class Op>
-hipError_t launch_scan_op(Scan1Params& p, int in_bf16, int out_bf16, void* scratch, hipStream_t s) {
+void scan_geometry(Scan1Params& p, void* scratch) {
   const int V = vec_width(p.D);
   const int64_t TW = 64 * V;
   p.n_tiles = (p.D + TW - 1) / TW;
   p.n_chunks = (p.L + kChunk - 1) / kChunk;
   p.ctl = static_cast<LookbackCtl*>(scratch);
   p.words = reinterpret_cast<unsigned long long*>(static_cast<char*>(scratch) + 256);
+}
+
+// The record pass of the backward: no outputs, the state entering each chunk to p.carry_out.
+template <class Op>
+hipError_t launch_record_op(Scan1Params& p, int in_bf16, void* scratch, hipStream_t s) {
+  scan_geometry<Op>(p, scratch);
+  if (vec_width(p.D) == 2)
+    return in_bf16 ? launch_scan_t<Op, bf16_t, float, 2, false, true>(p, s) : launch_scan_t<Op, float, float, 2, false, true>(p, s);
+  return in_bf16 ? launch_scan_t<Op, bf16_t, float, 1, false, true>(p, s) : launch_scan_t<Op, float, float, 1, false, true>(p, s);
+}
+
+template <class Op>
+hipError_t launch_scan_op(Scan1Params& p, int in_bf16, int out_bf16, void* scratch, hipStream_t s) {
+  const int V = vec_width(p.D);
+  scan_geometry<Op>(p, scratch);
   const bool gate = p.gate != nullptr;
   if (V == 2)
     return gate ? launch_scan_dt<Op, 2, true>(p, in_bf16, out_bf16, s) : launch_scan_dt<Op, 2, false>(p, in_bf16, out_bf16, s);
@@ -848,7 +865,7 @@ hipError_t launch_rglru_scan_backward(const RglruBwdArgs& a, hipStream_t s) {
   f.B = a.B; f.L = a.L; f.D = a.D;
   f.in[0] = a.x; f.in[1] = a.r_logit; f.in[2] = a.i_logit;
   f.a_log = a.a_log; f.c = a.c; f.h0 = a.h0; f.y = nullptr; f.h_last = nullptr; f.carry_out = carry;
-  hipError_t e = launch_scan_op<AffineOp>(f, a.in_bf16, a.out_bf16, a.scratch, s);
+  hipError_t e = launch_record_op<AffineOp>(f, a.in_bf16, a.scratch, s);
   if (e != hipSuccess) return e;
   // 2. reverse pass, one workgroup per (batch, 64-channel tile, chunk)
   const int V = vec_width(a.D);
