@@ -61,3 +61,41 @@ def test_rglru_state_gradient_closed_form():
     want = np.exp(np.sum(c * (1.0 / (1.0 + np.exp(-r))) * a_log, axis=1))
     assert np.allclose(G["dh0"], want, rtol=1e-13, atol=0)
     assert np.all(G["dx"][:, :, :] != 0.0)  # every input reaches h_last
+
+
+def test_minmax_grads_match_central_differences():
+    """Away from ties the MinMax scan is piecewise linear in its inputs: differences are exact."""
+    rng = np.random.default_rng(21)
+    B, L, D = 2, 9, 3
+    r, s, g, dy = (rng.standard_normal((B, L, D)) for _ in range(4))
+    x0, dxl = rng.standard_normal((B, D)), rng.standard_normal((B, D))
+    G = og.minmax_scan_grads(r, s, dy, x0=x0, gate=g, dx_last=dxl)
+
+    def F(r=r, s=s, x0=x0, g=g):
+        y, xl = oracle.minmax_scan(r, s, x0=x0, gate=g)
+        return _loss(y, xl, dy, dxl)
+
+    eps = 1e-7
+    for arg, gname, base in (("r", "dr", r), ("s", "ds", s), ("x0", "dx0", x0), ("g", "dgate", g)):
+        num = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            p, m = base.copy(), base.copy()
+            p[idx] += eps
+            m[idx] -= eps
+            num[idx] = (F(**{arg: p}) - F(**{arg: m})) / (2 * eps)
+        assert np.max(np.abs(num - G[gname])) < 1e-6, gname
+
+
+def test_minmax_grads_route_and_split_at_ties():
+    one = lambda v: np.array(v, dtype=np.float64).reshape(1, -1, 1)
+    # the upper clamp wins: the gradient goes to r, none to the state
+    G = og.minmax_scan_grads(one([0.5]), one([-5.0]), one([1.0]), x0=np.array([[2.0]]))
+    assert G["dr"][0, 0, 0] == 1.0 and G["dx0"][0, 0] == 0.0 and G["ds"][0, 0, 0] == 0.0
+    # the lower clamp wins
+    G = og.minmax_scan_grads(one([0.5]), one([0.7]), one([1.0]), x0=np.array([[2.0]]))
+    assert G["ds"][0, 0, 0] == 1.0 and G["dr"][0, 0, 0] == 0.0
+    # r equal to the state: half each; then s equal to that minimum: half of it again
+    G = og.minmax_scan_grads(one([1.0]), one([-5.0]), one([1.0]), x0=np.array([[1.0]]))
+    assert G["dr"][0, 0, 0] == 0.5 and G["dx0"][0, 0] == 0.5
+    G = og.minmax_scan_grads(one([1.0]), one([1.0]), one([1.0]), x0=np.array([[1.0]]))
+    assert G["ds"][0, 0, 0] == 0.5 and G["dr"][0, 0, 0] == 0.25 and G["dx0"][0, 0] == 0.25
