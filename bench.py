@@ -70,6 +70,11 @@ def minmax_bytes(B, L, D, in_b=2, out_b=4):
     return B * L * D * (2 * in_b + out_b)
 
 
+def minmax_bwd_bytes(B, L, D, in_b=2, out_b=4):
+    # r, s, dy read once; dr, ds written
+    return B * L * D * (3 * in_b + 2 * out_b)
+
+
 def conv_bytes(B, L, D, W, in_b=2, out_b=4):
     return B * L * D * (in_b + out_b) + D * (W + 1) * 4
 
@@ -248,6 +253,12 @@ def forms(args, device):
     # --- MinMax scan on the same shape (r, s ~ N(0, 1))
     ms = time_calls(lambda k: ssd.minmax_scan(r, i), 1, 10, 2)[0]
     record("minmax_bf16_B8_L8192_D2560", ms, B * L * D, minmax_bytes(B, L, D))
+
+    # --- gradients of the MinMax scan on the same shape (dy ~ N(0, 1))
+    dy = randn((B, L, D))
+    ms = time_calls(lambda k: ssd.minmax_scan_backward(r, i, dy), 1, 5, 1)[0]
+    record("minmax_backward_bf16_B8_L8192_D2560", ms, B * L * D, minmax_bwd_bytes(B, L, D))
+    del dy
 
     # --- causal depthwise conv (width 4) in front of the RG-LRU, same shape
     W = 4

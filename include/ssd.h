@@ -7,6 +7,7 @@
  *   RG-LRU        state size 1 per channel          ssd_rglru_scan / ssd_rglru_update
  *                 (gradients)                       ssd_rglru_scan_backward
  *   MinMax        state size 1 per channel          ssd_minmax_scan / ssd_minmax_update
+ *                 (gradients)                       ssd_minmax_scan_backward
  *   causal conv   depthwise, width W <= 4           ssd_causal_conv1d / ssd_causal_conv1d_update
  *   selective     N <= 16 states per channel        ssd_selective_scan / ssd_selective_update
  *   HGRN2         d x d matrix state per head       ssd_hgrn2_scan / ssd_hgrn2_update
@@ -138,6 +139,27 @@ int ssd_rglru_update(int64_t B, int64_t D, int in_dtype, int out_dtype,
 int ssd_minmax_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype,
                     const void* r, const void* s, const float* x0, const void* gate,
                     void* y, float* x_last, void* stream);
+
+/* Gradients of ssd_minmax_scan for the loss  sum dy * y + sum dx_last * x_last.  The package trains
+ * the neuron through torch autograd, so the derivative of min and max is torch's: the selected operand
+ * takes the gradient, equal operands take half each, and a NaN operand passes it to both.  With
+ * m_t = min(r_t, x_{t-1}), g_t = dL/dx_t = dy_t G_t + (gradient from step t+1) (G_t = gate_t or 1;
+ * g_{L-1} adds dx_last):
+ *   dr_t = g_t wM wR,   ds_t = g_t wS,   dgate_t = dy_t x_t,   dx0 = g_0 wM_0 wX_0,
+ * where wR, wX are the weights of r_t and x_{t-1} in min(r_t, x_{t-1}) and wM, wS those of m_t and
+ * s_t in max(m_t, s_t).
+ *   r, s, x0, gate      : as ssd_minmax_scan (the forward's inputs)
+ *   dy                  : [B, L, D] (in dtype);   dx_last : [B, D] fp32 or NULL (= 0)
+ *   dr, ds              : [B, L, D] (out dtype), overwritten
+ *   dgate               : [B, L, D] (out dtype) or NULL; written only when gate is given
+ *   dx0                 : [B, D] fp32 or NULL
+ * The forward states are recomputed (one forward pass records each 64-step chunk's incoming state
+ * in the library's scratch).  Results are deterministic.
+ * Errors as ssd_minmax_scan, plus SSD_ERR_NULL for missing dy / dr / ds. */
+int ssd_minmax_scan_backward(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype,
+                             const void* r, const void* s, const float* x0, const void* gate,
+                             const void* dy, const float* dx_last, void* dr, void* ds,
+                             float* dx0, void* dgate, void* stream);
 
 /* One MinMax decode step.  r, s, gate : [B, D] (gate may be NULL); state : [B, D] fp32 in/out;
  * y : [B, D].  Errors as ssd_minmax_scan; y must not overlap state. */

@@ -30,7 +30,7 @@ STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_
 EXPORTS = ("ssd_status_str", "ssd_last_error", "ssd_version", "ssd_rglru_scan", "ssd_rglru_scan_backward",
            "ssd_rglru_update",
            "ssd_selective_scan", "ssd_selective_update", "ssd_hgrn2_scan", "ssd_hgrn2_update", "ssd_minmax_scan",
-           "ssd_minmax_update", "ssd_causal_conv1d", "ssd_causal_conv1d_update")
+           "ssd_minmax_update", "ssd_minmax_scan_backward", "ssd_causal_conv1d", "ssd_causal_conv1d_update")
 
 
 class SSDError(RuntimeError):
@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
                                               ctypes.c_float, _fp, _vp, _vp, _fp, _vp, _vp, _vp, _fp, _fp, _vp, _vp]
         L.ssd_minmax_scan.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _fp, _vp, _vp, _fp, _vp]
         L.ssd_minmax_update.argtypes = [_i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _fp, _vp, _vp]
+        L.ssd_minmax_scan_backward.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _fp, _vp, _vp,
+                                               _fp, _vp, _vp, _fp, _vp, _vp]
         L.ssd_causal_conv1d.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _fp, _fp, _fp, _vp,
                                         _fp, _vp]
         L.ssd_causal_conv1d_update.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _fp, _fp, _fp, _vp,
@@ -246,6 +248,28 @@ def minmax_update(r, s, state, gate=None, out_dtype=None):
     return y
 
 
+def minmax_scan_backward(r, s, dy, x0=None, gate=None, dx_last=None, out_dtype=None):
+    """Gradients of ``minmax_scan`` for the loss sum(dy * y) + sum(dx_last * x_last) (see
+    ``ssd_minmax_scan_backward``).  Returns a dict: dr, ds [B, L, D] (out dtype), dx0 [B, D] (fp32),
+    and dgate when a gate is given."""
+    torch = _torch()
+    B, L, D = r.shape
+    code = _act([r, s, gate, dy], ["r", "s", "gate", "dy"])
+    oc = _out_code(out_dtype)
+    odt = torch.bfloat16 if oc == SSD_BF16 else torch.float32
+    g = {n: torch.empty((B, L, D), device=r.device, dtype=odt) for n in ("dr", "ds")}
+    if gate is not None:
+        g["dgate"] = torch.empty((B, L, D), device=r.device, dtype=odt)
+    g["dx0"] = torch.empty((B, D), device=r.device, dtype=torch.float32)
+    st = lib().ssd_minmax_scan_backward(
+        B, L, D, code, oc, _dev(r, "r"), _dev(s, "s", r.shape), _dev(x0, "x0", (B, D), torch.float32),
+        _dev(gate, "gate", r.shape), _dev(dy, "dy", r.shape), _dev(dx_last, "dx_last", (B, D), torch.float32),
+        _dev(g["dr"], "dr"), _dev(g["ds"], "ds"), _dev(g["dx0"], "dx0"), _dev(g.get("dgate"), "dgate"),
+        _stream(r.device))
+    _raise(st, "minmax_scan_backward")
+    return g
+
+
 # ----------------------------------------------------------------------------- causal conv1d
 def causal_conv1d(x, weight, bias=None, state_in=None, return_state: bool = False, out_dtype=None):
     """Causal depthwise convolution over [B, L, D] with weight [D, W] (see ``ssd_causal_conv1d``).
@@ -377,5 +401,5 @@ def hgrn2_update(q, k, v, g_logit, lower_bound: float, S, out_dtype=None):
 
 
 __all__ = ["rglru_scan", "rglru_scan_backward", "rglru_update", "selective_scan", "selective_update", "hgrn2_scan", "hgrn2_update",
-           "minmax_scan", "minmax_update", "causal_conv1d", "causal_conv1d_update", "lib", "LIB_PATH", "EXPORTS",
+           "minmax_scan", "minmax_update", "minmax_scan_backward", "causal_conv1d", "causal_conv1d_update", "lib", "LIB_PATH", "EXPORTS",
            "SSDError", "SSDValueError", "SSD_F32", "SSD_BF16"]

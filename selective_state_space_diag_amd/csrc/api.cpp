@@ -290,6 +290,33 @@ int ssd_minmax_update(int64_t B, int64_t D, int in_dtype, int out_dtype, const v
   return hip_status(ssd::launch_minmax_update(a, static_cast<hipStream_t>(stream)), "minmax_update launch");
 }
 
+int ssd_minmax_scan_backward(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype, const void* r,
+                             const void* s_in, const float* x0, const void* gate, const void* dy,
+                             const float* dx_last, void* dr, void* ds, float* dx0, void* dgate, void* stream) {
+  SSD_TRY(check_dtypes(in_dtype, out_dtype));
+  if (B < 0 || L < 0 || D < 0) return fail(SSD_ERR_SHAPE, "negative size");
+  if (too_big({B, L, D}) || D >= (int64_t)1 << 22 || B * ((L + 63) / 64) * ((D + 63) / 64) >= (int64_t)1 << 31)
+    return fail(SSD_ERR_SHAPE, "problem too large");
+  const int64_t nact = B * L * D;
+  if (nact > 0 && (!r || !s_in || !dy || !dr || !ds)) return fail(SSD_ERR_NULL, "r, s, dy, dr and ds are required");
+  const size_t ab = (size_t)nact * esize(in_dtype), ob = (size_t)nact * esize(out_dtype);
+  const size_t sb = (size_t)(B * D) * 4;
+  std::vector<Span> ins = {{"r", r, ab},   {"s", s_in, ab}, {"x0", x0, sb},
+                           {"gate", gate, ab}, {"dy", dy, ab}, {"dx_last", dx_last, sb}};
+  std::vector<Span> outs = {{"dr", dr, ob}, {"ds", ds, ob}, {"dx0", dx0, sb}, {"dgate", gate ? dgate : nullptr, ob}};
+  std::vector<Span> all = ins;
+  all.insert(all.end(), outs.begin(), outs.end());
+  SSD_TRY(check_align(all));
+  SSD_TRY(check_alias(outs, ins));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (B * D == 0) return ok();
+  if (L == 0) return hip_status(ssd::launch_copy_or_zero(dx0, dx_last, B * D, st), "minmax_scan_backward");
+  ssd::MinmaxBwdArgs a{B, L, D, in_dtype == SSD_BF16, out_dtype == SSD_BF16, r, s_in, x0, gate, dy, dx_last,
+                       dr, ds, gate ? dgate : nullptr, dx0, nullptr};
+  SSD_TRY(get_scratch(stream, kScratchScan1Bwd, ssd::minmax_bwd_scratch_bytes(B, L, D), &a.scratch));
+  return hip_status(ssd::launch_minmax_scan_backward(a, st), "minmax_scan_backward launch");
+}
+
 // ============================================================================ causal conv1d
 int ssd_causal_conv1d(int64_t B, int64_t L, int64_t D, int64_t W, int in_dtype, int out_dtype, const void* x,
                       const float* weight, const float* bias, const float* state_in, void* y, float* state_out,

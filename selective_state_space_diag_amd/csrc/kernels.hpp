@@ -70,6 +70,21 @@ struct MinmaxScanArgs {
 };
 hipError_t launch_minmax_scan(const MinmaxScanArgs& a, hipStream_t s);
 
+struct MinmaxBwdArgs {
+  int64_t B, L, D;
+  int in_bf16, out_bf16;
+  const void *r, *s;
+  const float* x0;        // [B][D] or NULL
+  const void* gate;       // or NULL
+  const void* dy;         // in dtype
+  const float* dx_last;   // [B][D] or NULL
+  void *dr, *ds, *dgate;  // out dtype; dgate may be NULL
+  float* dx0;             // [B][D] or NULL
+  void* scratch;          // minmax_bwd_scratch_bytes
+};
+size_t minmax_bwd_scratch_bytes(int64_t B, int64_t L, int64_t D);
+hipError_t launch_minmax_scan_backward(const MinmaxBwdArgs& a, hipStream_t s);
+
 struct MinmaxUpdateArgs {
   int64_t B, D;
   int in_bf16, out_bf16;

@@ -193,6 +193,67 @@ __device__ __forceinline__ void fetch_gate(const Scan1Params& p, const Unit& u, 
     g[s] = win<Tin, V, kStreaming>::load(wg, lane_off, (uint32_t)min(wave * kSteps + s, u.rows - 1) * row_bytes);
 }
 
+// ------------------------------------------------------------------ chunk lookback
+// Carry into chunk `cix` of one sequence of units (chunks of 64 steps, one channel per lane).
+// Chunks form blocks of kBlock.  The carry into chunk cix is the inclusive state published by the
+// last chunk of the previous block (`init` for the first block), followed by the aggregates of the
+// earlier chunks of its own block, applied in chunk order: every carry is one fixed function of the
+// inputs (bitwise reproducible), and the serial chain has n_chunks / kBlock links.  This chunk's
+// aggregate (Ac, Bc) is published for its later block-mates and, at a block end, its inclusive
+// state for the next block.  Words are (value, epoch) pairs; every wait is bounded, and a unit only
+// waits on units with lower tickets, which are running or done.  Returns the carry; *incl receives
+// the inclusive state.
+template <class Op, int TW>
+__device__ __forceinline__ float lookback_carry(LookbackCtl* ctl, unsigned long long* words, int64_t seq_unit,
+                                                int64_t cix, int64_t n_chunks, int j, uint32_t E, float Ac, float Bc,
+                                                float init, float* incl) {
+  unsigned long long* W = words + (seq_unit + cix) * 3 * TW;
+  const int64_t base = (cix / kBlock) * kBlock;
+  const int nprev = (int)(cix - base);  // aggregates of block-mates before cix
+  if (cix + 1 < base + kBlock && cix + 1 < n_chunks) {
+    word_store(&W[0 * TW + j], E, Ac);
+    word_store(&W[1 * TW + j], E, Bc);
+  }
+  // words: [0] inclusive of chunk base-1 (if base > 0), then (a, b) of chunks base .. cix-1
+  unsigned long long wd[1 + 2 * (kBlock - 1)];
+  const unsigned long long* Wb = words + (seq_unit + base - 1) * 3 * TW;
+  wd[0] = base > 0 ? word_load(&Wb[2 * TW + j]) : ((unsigned long long)E << 32);
+#pragma unroll
+  for (int q = 0; q < kBlock - 1; ++q) {
+    const unsigned long long* Wq = words + (seq_unit + base + q) * 3 * TW;
+    if (q < nprev) {
+      wd[1 + 2 * q] = word_load(&Wq[0 * TW + j]);
+      wd[2 + 2 * q] = word_load(&Wq[1 * TW + j]);
+    } else {
+      wd[1 + 2 * q] = wd[2 + 2 * q] = (unsigned long long)E << 32;
+    }
+  }
+  unsigned int spins = 0;
+  while (true) {
+    bool all = word_ready(wd[0], E);
+#pragma unroll
+    for (int q = 0; q < 2 * (kBlock - 1); ++q) all = all && word_ready(wd[1 + q], E);
+    if (all || spins >= kSpinLimit) break;
+    ++spins;
+    __builtin_amdgcn_s_sleep(1);
+    if (!word_ready(wd[0], E)) wd[0] = word_load(&Wb[2 * TW + j]);
+#pragma unroll
+    for (int q = 0; q < kBlock - 1; ++q) {
+      const unsigned long long* Wq = words + (seq_unit + base + q) * 3 * TW;
+      if (!word_ready(wd[1 + 2 * q], E)) wd[1 + 2 * q] = word_load(&Wq[0 * TW + j]);
+      if (!word_ready(wd[2 + 2 * q], E)) wd[2 + 2 * q] = word_load(&Wq[1 * TW + j]);
+    }
+  }
+  if (spins >= kSpinLimit) atomicOr(&ctl->error, 1u);
+  float hin = base > 0 ? word_value(wd[0]) : init;
+#pragma unroll
+  for (int q = 0; q < kBlock - 1; ++q)
+    if (q < nprev) hin = Op::apply(word_value(wd[1 + 2 * q]), word_value(wd[2 + 2 * q]), hin);
+  *incl = Op::apply(Ac, Bc, hin);
+  if (cix == base + kBlock - 1 && cix + 1 < n_chunks) word_store(&W[2 * TW + j], E, *incl);
+  return hin;
+}
+
 // ------------------------------------------------------------------ the scan kernel
 // Persistent workgroups: each takes tickets (work units) until none are left.  For unit t it
 //   1. folds the raw inputs of t (loaded earlier) into step pairs and wave aggregates,
@@ -291,64 +352,21 @@ void scan1_kernel(Scan1Params p) {
     // Each of these waves resolves 64 of the tile's channels, one per lane.
     if (wave < V) {
       const int64_t seq_unit = (u.b * p.n_tiles + u.k) * p.n_chunks;
-      unsigned long long* W = p.words + (seq_unit + u.c) * 3 * TW;
-      const int64_t base = (u.c / kBlock) * kBlock;
-      const int nprev = (int)(u.c - base);  // aggregates of block-mates before c
-      {
-        const int j = wave * 64 + lane;
-        const int64_t ch = u.k * TW + j;
-        const bool j_ok = ch < p.D;
-        float Ac = Op::id_a(), Bc = Op::id_b();
+      const int j = wave * 64 + lane;
+      const int64_t ch = u.k * TW + j;
+      const bool j_ok = ch < p.D;
+      float Ac = Op::id_a(), Bc = Op::id_b();
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          Bc = Op::apply(s_aggA[w][j], s_aggB[w][j], Bc);
-          Ac = Op::fold_a(s_aggA[w][j], Ac);
-        }
-        if (u.c + 1 < base + kBlock && u.c + 1 < p.n_chunks) {  // block-mates after c read the aggregate
-          word_store(&W[0 * TW + j], E, Ac);
-          word_store(&W[1 * TW + j], E, Bc);
-        }
-        // words: [0] inclusive of chunk base-1 (if base > 0), then (a, b) of chunks base .. c-1
-        unsigned long long wd[1 + 2 * (kBlock - 1)];
-        const unsigned long long* Wb = p.words + (seq_unit + base - 1) * 3 * TW;
-        wd[0] = base > 0 ? word_load(&Wb[2 * TW + j]) : ((unsigned long long)E << 32);
-#pragma unroll
-        for (int q = 0; q < kBlock - 1; ++q) {
-          const unsigned long long* Wq = p.words + (seq_unit + base + q) * 3 * TW;
-          if (q < nprev) {
-            wd[1 + 2 * q] = word_load(&Wq[0 * TW + j]);
-            wd[2 + 2 * q] = word_load(&Wq[1 * TW + j]);
-          } else {
-            wd[1 + 2 * q] = wd[2 + 2 * q] = (unsigned long long)E << 32;
-          }
-        }
-        unsigned int spins = 0;
-        while (true) {
-          bool all = word_ready(wd[0], E);
-#pragma unroll
-          for (int q = 0; q < 2 * (kBlock - 1); ++q) all = all && word_ready(wd[1 + q], E);
-          if (all || spins >= kSpinLimit) break;
-          ++spins;
-          __builtin_amdgcn_s_sleep(1);
-          if (!word_ready(wd[0], E)) wd[0] = word_load(&Wb[2 * TW + j]);
-#pragma unroll
-          for (int q = 0; q < kBlock - 1; ++q) {
-            const unsigned long long* Wq = p.words + (seq_unit + base + q) * 3 * TW;
-            if (!word_ready(wd[1 + 2 * q], E)) wd[1 + 2 * q] = word_load(&Wq[0 * TW + j]);
-            if (!word_ready(wd[2 + 2 * q], E)) wd[2 + 2 * q] = word_load(&Wq[1 * TW + j]);
-          }
-        }
-        if (spins >= kSpinLimit) atomicOr(&p.ctl->error, 1u);
-        float hin = (base > 0) ? word_value(wd[0]) : (p.h0 ? p.h0[u.b * p.D + (j_ok ? ch : p.D - 1)] : 0.0f);
-#pragma unroll
-        for (int q = 0; q < kBlock - 1; ++q)
-          if (q < nprev) hin = Op::apply(word_value(wd[1 + 2 * q]), word_value(wd[2 + 2 * q]), hin);
-        const float incl = Op::apply(Ac, Bc, hin);
-        if (u.c == base + kBlock - 1 && u.c + 1 < p.n_chunks) word_store(&W[2 * TW + j], E, incl);
-        if (p.h_last && j_ok && u.c == p.n_chunks - 1) p.h_last[u.b * p.D + ch] = incl;
-        if (RECORD && j_ok) p.carry_out[(u.b * p.n_chunks + u.c) * p.D + ch] = hin;
-        s_carry[j] = hin;
+      for (int w = 0; w < kWaves; ++w) {
+        Bc = Op::apply(s_aggA[w][j], s_aggB[w][j], Bc);
+        Ac = Op::fold_a(s_aggA[w][j], Ac);
       }
+      const float init = p.h0 ? p.h0[u.b * p.D + (j_ok ? ch : p.D - 1)] : 0.0f;
+      float incl;
+      const float hin = lookback_carry<Op, TW>(p.ctl, p.words, seq_unit, u.c, p.n_chunks, j, E, Ac, Bc, init, &incl);
+      if (p.h_last && j_ok && u.c == p.n_chunks - 1) p.h_last[u.b * p.D + ch] = incl;
+      if (RECORD && j_ok) p.carry_out[(u.b * p.n_chunks + u.c) * p.D + ch] = hin;
+      s_carry[j] = hin;
     }
     __syncthreads();
 
@@ -565,58 +583,16 @@ __global__ __launch_bounds__(kBWaves * 64) void rglru_bwd_kernel(Bwd1Params p) {
   if (wave < V) {
     const int j = wave * 64 + lane;
     const int64_t seq_unit = (b * p.n_tiles + k) * p.n_chunks;
-    unsigned long long* W = p.words + (seq_unit + cr) * 3 * TW;
-    const int64_t base = (cr / kBlock) * kBlock;
-    const int nprev = (int)(cr - base);
     float Ac = 1.0f, Bc = 0.0f;
 #pragma unroll
     for (int w = kBWaves - 1; w >= 0; --w) {
       Bc = fmaf(s_rA[w][j], Bc, s_rB[w][j]);
       Ac *= s_rA[w][j];
     }
-    if (cr + 1 < base + kBlock && cr + 1 < p.n_chunks) {
-      word_store(&W[0 * TW + j], E, Ac);
-      word_store(&W[1 * TW + j], E, Bc);
-    }
-    unsigned long long wd[1 + 2 * (kBlock - 1)];
-    const unsigned long long* Wb = p.words + (seq_unit + base - 1) * 3 * TW;
-    wd[0] = base > 0 ? word_load(&Wb[2 * TW + j]) : ((unsigned long long)E << 32);
-#pragma unroll
-    for (int q = 0; q < kBlock - 1; ++q) {
-      const unsigned long long* Wq = p.words + (seq_unit + base + q) * 3 * TW;
-      if (q < nprev) {
-        wd[1 + 2 * q] = word_load(&Wq[0 * TW + j]);
-        wd[2 + 2 * q] = word_load(&Wq[1 * TW + j]);
-      } else {
-        wd[1 + 2 * q] = wd[2 + 2 * q] = (unsigned long long)E << 32;
-      }
-    }
-    unsigned int spins = 0;
-    while (true) {
-      bool all = word_ready(wd[0], E);
-#pragma unroll
-      for (int q = 0; q < 2 * (kBlock - 1); ++q) all = all && word_ready(wd[1 + q], E);
-      if (all || spins >= kSpinLimit) break;
-      ++spins;
-      __builtin_amdgcn_s_sleep(1);
-      if (!word_ready(wd[0], E)) wd[0] = word_load(&Wb[2 * TW + j]);
-#pragma unroll
-      for (int q = 0; q < kBlock - 1; ++q) {
-        const unsigned long long* Wq = p.words + (seq_unit + base + q) * 3 * TW;
-        if (!word_ready(wd[1 + 2 * q], E)) wd[1 + 2 * q] = word_load(&Wq[0 * TW + j]);
-        if (!word_ready(wd[2 + 2 * q], E)) wd[2 + 2 * q] = word_load(&Wq[1 * TW + j]);
-      }
-    }
-    if (spins >= kSpinLimit) atomicOr(&p.ctl->error, 1u);
     const int64_t chj = k * TW + j;
-    const int64_t chjl = chj < p.D ? chj : p.D - 1;
-    float qin = (base > 0) ? word_value(wd[0]) : (p.dh_last ? p.dh_last[b * p.D + chjl] : 0.0f);
-#pragma unroll
-    for (int q = 0; q < kBlock - 1; ++q)
-      if (q < nprev) qin = fmaf(word_value(wd[1 + 2 * q]), qin, word_value(wd[2 + 2 * q]));
-    const float incl = fmaf(Ac, qin, Bc);
-    if (cr == base + kBlock - 1 && cr + 1 < p.n_chunks) word_store(&W[2 * TW + j], E, incl);
-    s_qin[j] = qin;
+    const float init = p.dh_last ? p.dh_last[b * p.D + (chj < p.D ? chj : p.D - 1)] : 0.0f;
+    float incl;
+    s_qin[j] = lookback_carry<AffineOp, TW>(p.ctl, p.words, seq_unit, cr, p.n_chunks, j, E, Ac, Bc, init, &incl);
   }
   __syncthreads();
 
@@ -687,6 +663,207 @@ __global__ __launch_bounds__(kBWaves * 64) void rglru_bwd_kernel(Bwd1Params p) {
       p.dalog_part[(b * p.n_chunks + c) * p.D + chj] = acc;
     }
   }
+
+  // ---- last workgroup to finish resets the ticket and advances the epoch
+  if (threadIdx.x == 0) {
+    const unsigned int old = atomicAdd(&p.ctl->done, 1u);
+    if (old == gridDim.x - 1) {
+      __hip_atomic_store(&p.ctl->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&p.ctl->tick, (unsigned long long)E << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ MinMax backward
+// Reverse-time adjoint of x_t = max(min(r_t, x_{t-1}), s_t), y_t = x_t (or x_t gate_t), for the loss
+// sum dy y + sum dx_last x_last, with the derivative convention of torch.minimum / torch.maximum
+// (the training framework of the minmaxrnc package): each operand receives the gradient when it is
+// the selected one, half of it when the two are equal, and -- as those comparisons give -- all of
+// it when either operand is NaN.  With m_t = min(r_t, x_{t-1}):
+//   wR = [r < x] + [r == x]/2 (to r),  wX = [r > x] + [r == x]/2 (to x_{t-1}), and the same pair
+//   wM (to m), wS (to s_t) for max(m, s_t), the NaN case giving 1 to both.
+// g_t = e_t + q_{t+1} (e_t = dy_t gate_t, or dy_t), q_t = wM wX g_t, q_L = dx_last:
+//   dr_t = g_t wM wR,  ds_t = g_t wS,  dgate_t = dy_t x_t,  dx0 = q_0.
+// q runs backwards through affine maps q -> a'_t q + a'_t e_t whose coefficients a'_t = wM wX are
+// in {0, 1/4, 1/2, 1} and depend on the forward state, so a unit first rebuilds the forward states
+// of its chunk (from the carry recorded by a forward pass and the MinMax wave aggregates), then
+// resolves the reverse carry with the affine lookback over chunks taken in reverse order.
+struct MmBwdParams {
+  int64_t B, L, D;
+  int64_t n_tiles, n_chunks;
+  const void* r;
+  const void* s;
+  const void* gate;      // or NULL
+  const void* dy;
+  const float* carry;    // [B][n_chunks][D] forward state entering each chunk
+  const float* dx_last;  // [B][D] or NULL
+  void* dr;
+  void* ds;
+  void* dgate;           // or NULL
+  float* dx0;            // [B][D] or NULL
+  LookbackCtl* ctl;
+  unsigned long long* words;
+};
+
+// d min(u, w) / du and d max(u, w) / du under the convention above.
+__device__ __forceinline__ float sel_lo(float u, float w) { return u == w ? 0.5f : (u > w ? 0.0f : 1.0f); }
+__device__ __forceinline__ float sel_hi(float u, float w) { return u == w ? 0.5f : (u < w ? 0.0f : 1.0f); }
+
+template <typename Tin, typename Tout, int V, bool GATE>
+__global__ __launch_bounds__(kBWaves * 64) void minmax_bwd_kernel(MmBwdParams p) {
+  constexpr int TW = 64 * V;  // channels per tile
+  __shared__ unsigned long long s_tick;
+  __shared__ float s_fA[kBWaves][TW], s_fB[kBWaves][TW];  // forward wave aggregates
+  __shared__ float s_rA[kBWaves][TW], s_rB[kBWaves][TW];  // reverse wave aggregates
+  __shared__ float s_qin[TW];
+  using LD = win<Tin, V, kStreaming>;
+  using ST = win<Tout, V, kStreaming>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (threadIdx.x == 0) s_tick = atomicAdd(&p.ctl->tick, 1ull);
+  __syncthreads();
+  const uint32_t E = (uint32_t)(s_tick >> 32) + 1u;
+  const int64_t ticket = (int64_t)(s_tick & 0xffffffffull);  // the grid holds exactly one per unit
+  const int64_t per_round = p.B * p.n_tiles;
+  const int64_t cr = ticket / per_round;  // reverse chunk index
+  const int64_t c = p.n_chunks - 1 - cr;
+  const int64_t rr = ticket - cr * per_round;
+  const int64_t b = rr / p.n_tiles, k = rr - b * p.n_tiles;
+  const int rows = (int)min<int64_t>(kChunk, p.L - c * kChunk);
+  const int64_t ch0 = k * TW + (int64_t)lane * V;
+  const bool ch_ok = ch0 < p.D;  // V = 2 only when D is even
+  const int64_t chl = ch_ok ? ch0 : p.D - V;
+  const int64_t t0 = c * kChunk + (int64_t)wave * kBSteps;
+  const int nvalid = rows - wave * kBSteps;
+
+  // ---- loads of the unit's rows (rows past the chunk read its last row; results unused)
+  constexpr int es = sizeof(Tin);
+  auto window = [&](const void* a, int e) {
+    return make_window(static_cast<const char*>(a) + ((b * p.L + c * kChunk) * p.D) * e, (uint32_t)(rows * p.D * e));
+  };
+  const auto wr = window(p.r, es), ws = window(p.s, es), wd = window(p.dy, es);
+  const auto wg = window(GATE ? p.gate : p.r, es);
+  const uint32_t row_in = (uint32_t)(p.D * es), lane_in = (uint32_t)(chl * es);
+  typename LD::raw raw_r[kBSteps], raw_s[kBSteps], rdy[kBSteps], rg[GATE ? kBSteps : 1];
+#pragma unroll
+  for (int s = 0; s < kBSteps; ++s) {
+    const uint32_t ro = (uint32_t)min(wave * kBSteps + s, rows - 1) * row_in;
+    raw_r[s] = LD::load(wr, lane_in, ro);
+    raw_s[s] = LD::load(ws, lane_in, ro);
+    rdy[s] = LD::load(wd, lane_in, ro);
+    if (GATE) rg[GATE ? s : 0] = LD::load(wg, lane_in, ro);
+  }
+  float hc[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) hc[v] = p.carry[(b * p.n_chunks + c) * p.D + chl + v];
+
+  // ---- forward maps (identity past L and on idle lanes) and the wave's forward aggregate
+  float av[kBSteps][V], bv[kBSteps][V];
+  float fA[V], fB[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) { fA[v] = MinMaxOp::id_a(); fB[v] = MinMaxOp::id_b(); }
+#pragma unroll
+  for (int s = 0; s < kBSteps; ++s) {
+    const bool ok = ch_ok && (t0 + s < p.L);
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      av[s][v] = ok ? LD::get(raw_r[s], v) : MinMaxOp::id_a();
+      bv[s][v] = ok ? LD::get(raw_s[s], v) : MinMaxOp::id_b();
+      fB[v] = MinMaxOp::apply(av[s][v], bv[s][v], fB[v]);
+      fA[v] = MinMaxOp::fold_a(av[s][v], fA[v]);
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    s_fA[wave][lane * V + v] = fA[v];
+    s_fB[wave][lane * V + v] = fB[v];
+  }
+  __syncthreads();
+
+  // ---- forward states of this wave's steps, the reverse coefficients, the reverse aggregate
+  float ap[kBSteps][V], ev[kBSteps][V], kr[kBSteps][V], ks[kBSteps][V], xt[GATE ? kBSteps : 1][V];
+  float rA[V], rB[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int j = lane * V + v;
+    float h = hc[v];
+    for (int w = 0; w < wave; ++w) h = MinMaxOp::apply(s_fA[w][j], s_fB[w][j], h);
+#pragma unroll
+    for (int s = 0; s < kBSteps; ++s) {
+      const bool ok = ch_ok && (t0 + s < p.L);
+      const float r = av[s][v], sv = bv[s][v];
+      const float m = mm_min(r, h);
+      const float wm = sel_hi(m, sv);
+      ap[s][v] = ok ? wm * sel_lo(h, r) : 1.0f;
+      kr[s][v] = wm * sel_lo(r, h);
+      ks[s][v] = sel_hi(sv, m);
+      const float G = GATE ? LD::get(rg[GATE ? s : 0], v) : 1.0f;
+      ev[s][v] = ok ? LD::get(rdy[s], v) * G : 0.0f;
+      h = mm_max(m, sv);
+      if (GATE) xt[GATE ? s : 0][v] = h;
+    }
+    rA[v] = 1.0f;
+    rB[v] = 0.0f;
+#pragma unroll
+    for (int s = kBSteps - 1; s >= 0; --s) {
+      rB[v] = fmaf(ap[s][v], rB[v], ap[s][v] * ev[s][v]);
+      rA[v] *= ap[s][v];
+    }
+    s_rA[wave][j] = rA[v];
+    s_rB[wave][j] = rB[v];
+  }
+  __syncthreads();
+
+  // ---- waves 0 .. V-1: chunk reverse aggregate, publish, reverse carry over later chunks
+  if (wave < V) {
+    const int j = wave * 64 + lane;
+    const int64_t seq_unit = (b * p.n_tiles + k) * p.n_chunks;
+    float Ac = 1.0f, Bc = 0.0f;
+#pragma unroll
+    for (int w = kBWaves - 1; w >= 0; --w) {
+      Bc = fmaf(s_rA[w][j], Bc, s_rB[w][j]);
+      Ac *= s_rA[w][j];
+    }
+    const int64_t chj = k * TW + j;
+    const float init = p.dx_last ? p.dx_last[b * p.D + (chj < p.D ? chj : p.D - 1)] : 0.0f;
+    float incl;
+    s_qin[j] = lookback_carry<AffineOp, TW>(p.ctl, p.words, seq_unit, cr, p.n_chunks, j, E, Ac, Bc, init, &incl);
+  }
+  __syncthreads();
+
+  // ---- per-step gradients, last step first
+  float q[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int j = lane * V + v;
+    float qq = s_qin[j];
+    for (int w = kBWaves - 1; w > wave; --w) qq = fmaf(s_rA[w][j], qq, s_rB[w][j]);
+    q[v] = qq;
+  }
+  const auto wdr = window(p.dr, (int)sizeof(Tout)), wds = window(p.ds, (int)sizeof(Tout));
+  const auto wdg = window(GATE && p.dgate ? p.dgate : p.dr, (int)sizeof(Tout));
+  const uint32_t row_out = (uint32_t)(p.D * (int64_t)sizeof(Tout)), lane_out = (uint32_t)(chl * (int64_t)sizeof(Tout));
+#pragma unroll
+  for (int s = kBSteps - 1; s >= 0; --s) {
+    float o_dr[V], o_ds[V], o_dg[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const float g = ev[s][v] + q[v];
+      q[v] = ap[s][v] * g;
+      o_dr[v] = g * kr[s][v];
+      o_ds[v] = g * ks[s][v];
+      if (GATE) o_dg[v] = LD::get(rdy[s], v) * xt[GATE ? s : 0][v];
+    }
+    if (ch_ok && s < nvalid) {
+      const uint32_t ro = (uint32_t)(wave * kBSteps + s) * row_out;
+      ST::store(wdr, lane_out, ro, o_dr);
+      ST::store(wds, lane_out, ro, o_ds);
+      if (GATE && p.dgate) ST::store(wdg, lane_out, ro, o_dg);
+    }
+  }
+  if (p.dx0 && ch_ok && c == 0 && wave == 0)
+#pragma unroll
+    for (int v = 0; v < V; ++v) p.dx0[b * p.D + ch0 + v] = q[v];
 
   // ---- last workgroup to finish resets the ticket and advances the epoch
   if (threadIdx.x == 0) {
@@ -887,6 +1064,51 @@ hipError_t launch_rglru_scan_backward(const RglruBwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(dalog_slice_kernel, dim3(nb, kDalSlices), dim3(256), 0, s, dal, a.B * n_chunks, a.D, slices);
   hipLaunchKernelGGL(dalog_final_kernel, dim3(nb), dim3(256), 0, s, slices, a.D, a.da_log);
   return hipGetLastError();
+}
+
+namespace {
+template <int V, bool G>
+hipError_t launch_mm_bwd_g(const MmBwdParams& q, int in_bf16, int out_bf16, dim3 grid, hipStream_t s) {
+  const dim3 blk(kBWaves * 64);
+  if (!in_bf16) hipLaunchKernelGGL((minmax_bwd_kernel<float, float, V, G>), grid, blk, 0, s, q);
+  else if (out_bf16) hipLaunchKernelGGL((minmax_bwd_kernel<bf16_t, bf16_t, V, G>), grid, blk, 0, s, q);
+  else hipLaunchKernelGGL((minmax_bwd_kernel<bf16_t, float, V, G>), grid, blk, 0, s, q);
+  return hipGetLastError();
+}
+template <int V>
+hipError_t launch_mm_bwd_dt(const MmBwdParams& q, bool gate, int in_bf16, int out_bf16, dim3 grid, hipStream_t s) {
+  return gate ? launch_mm_bwd_g<V, true>(q, in_bf16, out_bf16, grid, s) : launch_mm_bwd_g<V, false>(q, in_bf16, out_bf16, grid, s);
+}
+}  // namespace
+
+size_t minmax_bwd_scratch_bytes(int64_t B, int64_t L, int64_t D) {
+  const int64_t n_chunks = (L + kChunk - 1) / kChunk;
+  return (size_t)(256 + bwd_words_bytes(B, L, D) + B * n_chunks * D * 4);
+}
+
+hipError_t launch_minmax_scan_backward(const MinmaxBwdArgs& a, hipStream_t s) {
+  const int64_t n_chunks = (a.L + kChunk - 1) / kChunk;
+  char* base = static_cast<char*>(a.scratch);
+  float* carry = reinterpret_cast<float*>(base + 256 + bwd_words_bytes(a.B, a.L, a.D));
+  // 1. forward pass that records the state entering every chunk (no outputs)
+  Scan1Params f{};
+  f.B = a.B; f.L = a.L; f.D = a.D;
+  f.in[0] = a.r; f.in[1] = a.s;
+  f.h0 = a.x0; f.y = nullptr; f.h_last = nullptr; f.carry_out = carry;
+  hipError_t e = launch_record_op<MinMaxOp>(f, a.in_bf16, a.scratch, s);
+  if (e != hipSuccess) return e;
+  // 2. reverse pass, one workgroup per (batch, 64-channel tile, chunk)
+  const int V = vec_width(a.D);
+  MmBwdParams q{};
+  q.B = a.B; q.L = a.L; q.D = a.D;
+  q.n_tiles = (a.D + 64 * V - 1) / (64 * V); q.n_chunks = n_chunks;
+  q.r = a.r; q.s = a.s; q.gate = a.gate; q.dy = a.dy; q.carry = carry; q.dx_last = a.dx_last;
+  q.dr = a.dr; q.ds = a.ds; q.dgate = a.dgate; q.dx0 = a.dx0;
+  q.ctl = static_cast<LookbackCtl*>(a.scratch);
+  q.words = reinterpret_cast<unsigned long long*>(base + 256);
+  const dim3 grid((unsigned)(a.B * q.n_tiles * n_chunks));
+  return V == 2 ? launch_mm_bwd_dt<2>(q, a.gate != nullptr, a.in_bf16, a.out_bf16, grid, s)
+                : launch_mm_bwd_dt<1>(q, a.gate != nullptr, a.in_bf16, a.out_bf16, grid, s);
 }
 
 hipError_t launch_rglru_update(const RglruUpdateArgs& a, hipStream_t s) {

@@ -75,3 +75,73 @@ def test_backward_empty_sequence():
     g = ssd.rglru_scan_backward(x, x, x, a_log, 8.0, x, dh_last=dhl)
     torch.cuda.synchronize()
     assert torch.equal(g["dh0"], dhl) and torch.all(g["da_log"] == 0)
+
+
+# ----------------------------------------------------------------------------- MinMax
+def run_mm_bwd(B, L, D, dtype, seed, gated=False, with_x0=True, with_dxl=True, ties=False, nan_at=()):
+    inp = synth.minmax_inputs(B, L, D, dtype, seed, with_x0=with_x0, with_gate=gated, ties=ties)
+    for name, idx in nan_at:  # plant NaN inputs (the forward carries them; torch's rule routes gradients)
+        inp.t[name].data[idx] = 0x7FC0 if dtype == synth.BF16 else np.nan
+    rng = np.random.default_rng(seed + 7)
+    dy32 = rng.standard_normal((B, L, D)).astype(np.float32)
+    dy = synth.Tensor(dtype, synth.f32_to_bf16_bits(dy32)) if dtype == synth.BF16 else synth.Tensor(dtype, dy32)
+    dxl = rng.standard_normal((B, D)).astype(np.float32) if with_dxl else None
+    import torch
+    G = ssd.minmax_scan_backward(to_dev(inp.t["r"]), to_dev(inp.t["s"]), to_dev(dy), x0=to_dev(inp.p.get("x0")),
+                                 gate=to_dev(inp.t["gate"]) if gated else None, dx_last=to_dev(dxl))
+    torch.cuda.synchronize()
+    R = og.minmax_scan_grads(f64(inp.t["r"]), f64(inp.t["s"]), f64(dy), x0=f64(inp.p.get("x0")),
+                             gate=f64(inp.t["gate"]) if gated else None,
+                             dx_last=None if dxl is None else dxl.astype(np.float64))
+    names = ("dr", "ds", "dx0") + (("dgate",) if gated else ())
+    for name in names:
+        got, want = host(G[name]), R[name]
+        if nan_at:
+            assert np.array_equal(np.isnan(got), np.isnan(want)), name
+            keep = ~np.isnan(want)
+            got, want = got[keep], want[keep]
+        assert_close(got, want, TOLB[dtype], name)
+    return G
+
+
+def test_minmax_backward_fp32_gated():
+    run_mm_bwd(2, 64 * 5 + 9, 130, synth.F32, 5000, gated=True)
+
+
+@pytest.mark.parametrize("L,D", [(1, 64), (63, 65), (64, 130), (65, 128), (300, 257)])
+def test_minmax_backward_bf16_ragged(L, D):
+    run_mm_bwd(2, L, D, synth.BF16, 5100 + L + D)
+
+
+def test_minmax_backward_ties_split_the_gradient():
+    """Inputs drawn from {-2, -1, -0, +0, 1, 2}: equal operands at every other step."""
+    run_mm_bwd(2, 64 * 6 + 5, 96, synth.F32, 5200, gated=True, ties=True)
+    run_mm_bwd(1, 200, 64, synth.BF16, 5201, ties=True, with_x0=False, with_dxl=False)
+
+
+def test_minmax_backward_nan_inputs():
+    run_mm_bwd(2, 64 * 3 + 1, 64, synth.F32, 5300, gated=True, nan_at=[("r", (0, 70, 3)), ("s", (1, 150, 9))])
+
+
+def test_minmax_backward_deterministic_and_bf16_output():
+    import torch
+    inp = synth.minmax_inputs(2, 300, 256, synth.BF16, 5400, with_x0=True, with_gate=True)
+    r, s, gt = (to_dev(inp.t[n]) for n in ("r", "s", "gate"))
+    dy = torch.randn((2, 300, 256), device="cuda").to(torch.bfloat16)
+    g1 = ssd.minmax_scan_backward(r, s, dy, x0=to_dev(inp.p["x0"]), gate=gt)
+    g2 = ssd.minmax_scan_backward(r, s, dy, x0=to_dev(inp.p["x0"]), gate=gt)
+    g16 = ssd.minmax_scan_backward(r, s, dy, x0=to_dev(inp.p["x0"]), gate=gt, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    for k in g1:
+        assert torch.equal(g1[k], g2[k]), k
+    for k in ("dr", "ds", "dgate"):
+        assert torch.equal(g16[k], g1[k].to(torch.bfloat16)), k
+
+
+def test_minmax_backward_empty_sequence():
+    import torch
+    r = torch.empty((2, 0, 8), device="cuda")
+    dxl = torch.randn((2, 8), device="cuda")
+    g = ssd.minmax_scan_backward(r, r, r, dx_last=dxl)
+    torch.cuda.synchronize()
+    assert torch.equal(g["dx0"], dxl)
