@@ -244,21 +244,30 @@ def forms(args, device):
     record("rglru_gated_bf16_B8_L8192_D2560", ms, B * L * D, rglru_gated_bytes(B, L, D))
     del gt
 
-    # --- gradients of the RG-LRU scan on the same shape (dy ~ N(0, 1))
+    # --- gradients of the RG-LRU scan on the same shape (dy ~ N(0, 1)): with the chunk states a
+    #     training forward saves (1/64 of the states), and recomputing them from the inputs
     dy = randn((B, L, D))
+    cs = torch.empty(ssd.chunk_states_shape(B, L, D), device=device)
+    ssd.rglru_scan(x, r, i, a_log, 8.0, chunk_states=cs)
+    ms = time_calls(lambda k: ssd.rglru_scan_backward(x, r, i, a_log, 8.0, dy, chunk_states=cs), 1, 5, 1)[0]
+    record("rglru_backward_bf16_B8_L8192_D2560", ms, B * L * D, rglru_bwd_bytes(B, L, D) + cs.numel() * 4)
     ms = time_calls(lambda k: ssd.rglru_scan_backward(x, r, i, a_log, 8.0, dy), 1, 5, 1)[0]
-    record("rglru_backward_bf16_B8_L8192_D2560", ms, B * L * D, rglru_bwd_bytes(B, L, D))
+    record("rglru_backward_recompute_bf16_B8_L8192_D2560", ms, B * L * D, rglru_bwd_bytes(B, L, D))
     del dy
 
     # --- MinMax scan on the same shape (r, s ~ N(0, 1))
     ms = time_calls(lambda k: ssd.minmax_scan(r, i), 1, 10, 2)[0]
     record("minmax_bf16_B8_L8192_D2560", ms, B * L * D, minmax_bytes(B, L, D))
 
-    # --- gradients of the MinMax scan on the same shape (dy ~ N(0, 1))
+    # --- gradients of the MinMax scan on the same shape (dy ~ N(0, 1)), with and without the
+    #     forward's chunk states
     dy = randn((B, L, D))
+    ssd.minmax_scan(r, i, chunk_states=cs)
+    ms = time_calls(lambda k: ssd.minmax_scan_backward(r, i, dy, chunk_states=cs), 1, 5, 1)[0]
+    record("minmax_backward_bf16_B8_L8192_D2560", ms, B * L * D, minmax_bwd_bytes(B, L, D) + cs.numel() * 4)
     ms = time_calls(lambda k: ssd.minmax_scan_backward(r, i, dy), 1, 5, 1)[0]
-    record("minmax_backward_bf16_B8_L8192_D2560", ms, B * L * D, minmax_bwd_bytes(B, L, D))
-    del dy
+    record("minmax_backward_recompute_bf16_B8_L8192_D2560", ms, B * L * D, minmax_bwd_bytes(B, L, D))
+    del dy, cs
 
     # --- causal depthwise conv (width 4) in front of the RG-LRU, same shape
     W = 4

@@ -65,6 +65,12 @@ const char* ssd_last_error(void);
 /* Library ABI version (major * 10000 + minor * 100 + patch). */
 int ssd_version(void);
 
+/* Steps per chunk of the state-size-1 scans (RG-LRU, MinMax).  Their optional `chunk_states`
+ * buffers are [B, ceil(L / SSD_SCAN_CHUNK), D] fp32, entry [b, k, d] being the state entering step
+ * k * SSD_SCAN_CHUNK (h0 for k = 0): 1/64 of the per-step states, which a forward pass can save
+ * for the backward pass so that the latter need not recompute them. */
+#define SSD_SCAN_CHUNK 64
+
 /* ---------------------------------------------------------------------------------------------
  * RG-LRU scan.  Defined by the lrnnx documentation, "lrnnx.models.ltv.rglru" (RGLRU.forward gate
  * computation and RGLRU.step recurrence):  for each batch b, channel d and step t
@@ -79,6 +85,8 @@ int ssd_version(void);
  *   gate                : [B, L, D] (in dtype) or NULL (= no output multiply)
  *   y                   : [B, L, D] (out dtype)
  *   h_last              : [B, D] fp32 or NULL; receives h_{L-1} (h0 when L = 0), never gated
+ *   chunk_states        : [B, ceil(L/64), D] fp32 or NULL; receives the state entering each 64-step
+ *                         chunk (see SSD_SCAN_CHUNK), the same bits ssd_rglru_scan_backward recomputes
  * Errors: SSD_ERR_NULL (x, r_logit, i_logit, a_log, y when B*L*D > 0), SSD_ERR_SHAPE (negative
  * size, D >= 2^22, or B * ceil(L/64) * ceil(D/64) >= 2^31), SSD_ERR_DTYPE, SSD_ERR_ALIGN,
  * SSD_ERR_VALUE (c not finite), SSD_ERR_ALIAS.
@@ -86,7 +94,7 @@ int ssd_version(void);
 int ssd_rglru_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype,
                    const void* x, const void* r_logit, const void* i_logit,
                    const float* a_log, float c, const float* h0, const void* gate,
-                   void* y, float* h_last, void* stream);
+                   void* y, float* h_last, float* chunk_states, void* stream);
 
 /* Gradients of ssd_rglru_scan (reverse-time adjoint; the pages train through autograd and print no
  * backward pass, so this is the gradient of the forward definition above) for the loss
@@ -96,18 +104,21 @@ int ssd_rglru_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype,
  *   dl = g (a h_{t-1} - i x a^2 / beta),  d r_logit = dl c a_log r (1-r),  d a_log = sum_{b,t} dl c r,
  *   dgate = dy h_t gelu'(gate),  dh0 = a_0 g_0.
  *   x, r_logit, i_logit, gate, a_log, c, h0 : as ssd_rglru_scan (the forward's inputs)
+ *   chunk_states        : [B, ceil(L/64), D] fp32 from the forward call, or NULL
  *   dy                  : [B, L, D] (in dtype) gradient of y;   dh_last : [B, D] fp32 or NULL (= 0)
  *   dx, dr_logit, di_logit : [B, L, D] (out dtype), overwritten
  *   dgate               : [B, L, D] (out dtype) or NULL; written only when gate is given
  *   da_log              : [D] fp32, overwritten (not accumulated)
  *   dh0                 : [B, D] fp32 or NULL
- * The forward states are recomputed (one forward pass records each 64-step chunk's incoming state in
- * the library's scratch), so the call needs no saved activations.  Results are deterministic.
+ * The per-step forward states are rebuilt inside each 64-step chunk from the chunk's incoming state:
+ * the forward's chunk_states when given, else a forward pass first records them in the library's
+ * scratch (then the call needs no saved activations).  Results are deterministic, and identical
+ * with and without chunk_states.
  * Errors as ssd_rglru_scan, plus SSD_ERR_NULL for missing dy / dx / dr_logit / di_logit / da_log. */
 int ssd_rglru_scan_backward(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype,
                             const void* x, const void* r_logit, const void* i_logit,
                             const float* a_log, float c, const float* h0, const void* gate,
-                            const void* dy, const float* dh_last,
+                            const float* chunk_states, const void* dy, const float* dh_last,
                             void* dx, void* dr_logit, void* di_logit, float* da_log, float* dh0,
                             void* dgate, void* stream);
 
@@ -134,11 +145,12 @@ int ssd_rglru_update(int64_t B, int64_t D, int in_dtype, int out_dtype,
  *   gate                : [B, L, D] (in dtype) or NULL (the neuron's output gate values)
  *   y                   : [B, L, D] (out dtype)
  *   x_last              : [B, D] fp32 or NULL; receives x_{L-1} (x0 when L = 0), never gated
+ *   chunk_states        : [B, ceil(L/64), D] fp32 or NULL, as for ssd_rglru_scan
  * Errors: as ssd_rglru_scan (no scalar arguments).
  * ------------------------------------------------------------------------------------------- */
 int ssd_minmax_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype,
                     const void* r, const void* s, const float* x0, const void* gate,
-                    void* y, float* x_last, void* stream);
+                    void* y, float* x_last, float* chunk_states, void* stream);
 
 /* Gradients of ssd_minmax_scan for the loss  sum dy * y + sum dx_last * x_last.  The package trains
  * the neuron through torch autograd, so the derivative of min and max is torch's: the selected operand
@@ -149,16 +161,18 @@ int ssd_minmax_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype
  * where wR, wX are the weights of r_t and x_{t-1} in min(r_t, x_{t-1}) and wM, wS those of m_t and
  * s_t in max(m_t, s_t).
  *   r, s, x0, gate      : as ssd_minmax_scan (the forward's inputs)
+ *   chunk_states        : [B, ceil(L/64), D] fp32 from the forward call, or NULL
  *   dy                  : [B, L, D] (in dtype);   dx_last : [B, D] fp32 or NULL (= 0)
  *   dr, ds              : [B, L, D] (out dtype), overwritten
  *   dgate               : [B, L, D] (out dtype) or NULL; written only when gate is given
  *   dx0                 : [B, D] fp32 or NULL
- * The forward states are recomputed (one forward pass records each 64-step chunk's incoming state
- * in the library's scratch).  Results are deterministic.
+ * The forward states are rebuilt from each 64-step chunk's incoming state (the forward's
+ * chunk_states, else recorded by a forward pass first).  Results are deterministic, and identical
+ * with and without chunk_states.
  * Errors as ssd_minmax_scan, plus SSD_ERR_NULL for missing dy / dr / ds. */
 int ssd_minmax_scan_backward(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype,
                              const void* r, const void* s, const float* x0, const void* gate,
-                             const void* dy, const float* dx_last, void* dr, void* ds,
+                             const float* chunk_states, const void* dy, const float* dx_last, void* dr, void* ds,
                              float* dx0, void* dgate, void* stream);
 
 /* One MinMax decode step.  r, s, gate : [B, D] (gate may be NULL); state : [B, D] fp32 in/out;

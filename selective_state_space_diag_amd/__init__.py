@@ -27,6 +27,8 @@ STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_
                 5: "SSD_ERR_VALUE", 6: "SSD_ERR_ALIAS", 7: "SSD_ERR_HIP"}
 
 # Every symbol include/ssd.h declares.
+SCAN_CHUNK = 64  # SSD_SCAN_CHUNK of ssd.h
+
 EXPORTS = ("ssd_status_str", "ssd_last_error", "ssd_version", "ssd_rglru_scan", "ssd_rglru_scan_backward",
            "ssd_rglru_update",
            "ssd_selective_scan", "ssd_selective_update", "ssd_hgrn2_scan", "ssd_hgrn2_update", "ssd_minmax_scan",
@@ -62,15 +64,17 @@ def lib() -> ctypes.CDLL:
         L.ssd_last_error.argtypes = []
         L.ssd_version.restype = ctypes.c_int
         L.ssd_rglru_scan.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _fp, ctypes.c_float,
-                                     _fp, _vp, _vp, _fp, _vp]
+                                     _fp, _vp, _vp, _fp, _fp, _vp]
         L.ssd_rglru_update.argtypes = [_i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _fp, ctypes.c_float, _vp,
                                        _fp, _vp, _vp]
         L.ssd_rglru_scan_backward.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _fp,
-                                              ctypes.c_float, _fp, _vp, _vp, _fp, _vp, _vp, _vp, _fp, _fp, _vp, _vp]
-        L.ssd_minmax_scan.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _fp, _vp, _vp, _fp, _vp]
+                                              ctypes.c_float, _fp, _vp, _fp, _vp, _fp, _vp, _vp, _vp, _fp, _fp, _vp,
+                                              _vp]
+        L.ssd_minmax_scan.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _fp, _vp, _vp, _fp, _fp,
+                                      _vp]
         L.ssd_minmax_update.argtypes = [_i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _fp, _vp, _vp]
-        L.ssd_minmax_scan_backward.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _fp, _vp, _vp,
-                                               _fp, _vp, _vp, _fp, _vp, _vp]
+        L.ssd_minmax_scan_backward.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _fp, _vp, _fp,
+                                               _vp, _fp, _vp, _vp, _fp, _vp, _vp]
         L.ssd_causal_conv1d.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _fp, _fp, _fp, _vp,
                                         _fp, _vp]
         L.ssd_causal_conv1d_update.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _fp, _fp, _fp, _vp,
@@ -160,10 +164,17 @@ def _act(ts, names):
 
 
 # ----------------------------------------------------------------------------- RG-LRU
+def chunk_states_shape(B: int, L: int, D: int):
+    """Shape of the ``chunk_states`` buffer of the state-size-1 scans: the state entering each chunk
+    of SCAN_CHUNK steps."""
+    return (B, (L + SCAN_CHUNK - 1) // SCAN_CHUNK, D)
+
+
 def rglru_scan(x, r_logit, i_logit, a_log, c: float = 8.0, h0=None, return_last_state: bool = False,
-               out_dtype=None, gate=None):
+               out_dtype=None, gate=None, chunk_states=None):
     """RG-LRU scan over [B, L, D] (see ``ssd_rglru_scan``); with ``gate``, y = gelu(gate) * h.
-    Returns y, or (y, h_last)."""
+    ``chunk_states`` (fp32, ``chunk_states_shape``) receives the state entering each chunk, for
+    ``rglru_scan_backward``.  Returns y, or (y, h_last)."""
     torch = _torch()
     B, L, D = x.shape
     code = _act([x, r_logit, i_logit, gate], ["x", "r_logit", "i_logit", "gate"])
@@ -173,7 +184,9 @@ def rglru_scan(x, r_logit, i_logit, a_log, c: float = 8.0, h0=None, return_last_
     st = lib().ssd_rglru_scan(B, L, D, code, oc, _dev(x, "x"), _dev(r_logit, "r_logit", x.shape),
                               _dev(i_logit, "i_logit", x.shape), _dev(a_log, "a_log", (D,), torch.float32),
                               float(c), _dev(h0, "h0", (B, D), torch.float32), _dev(gate, "gate", x.shape),
-                              _dev(y, "y"), _dev(h_last, "h_last"), _stream(x.device))
+                              _dev(y, "y"), _dev(h_last, "h_last"),
+                              _dev(chunk_states, "chunk_states", chunk_states_shape(B, L, D), torch.float32),
+                              _stream(x.device))
     _raise(st, "rglru_scan")
     return (y, h_last) if return_last_state else y
 
@@ -194,10 +207,12 @@ def rglru_update(x, r_logit, i_logit, a_log, c: float, state, out_dtype=None, ga
     return y
 
 
-def rglru_scan_backward(x, r_logit, i_logit, a_log, c, dy, h0=None, gate=None, dh_last=None, out_dtype=None):
+def rglru_scan_backward(x, r_logit, i_logit, a_log, c, dy, h0=None, gate=None, dh_last=None, out_dtype=None,
+                        chunk_states=None):
     """Gradients of ``rglru_scan`` for the loss sum(dy * y) + sum(dh_last * h_last) (see
-    ``ssd_rglru_scan_backward``).  Returns a dict: dx, dr_logit, di_logit [B, L, D] (out dtype),
-    da_log [D], dh0 [B, D] (fp32), and dgate when a gate is given."""
+    ``ssd_rglru_scan_backward``); ``chunk_states`` from the forward call saves recomputing them.
+    Returns a dict: dx, dr_logit, di_logit [B, L, D] (out dtype), da_log [D], dh0 [B, D] (fp32), and
+    dgate when a gate is given."""
     torch = _torch()
     B, L, D = x.shape
     code = _act([x, r_logit, i_logit, gate, dy], ["x", "r_logit", "i_logit", "gate", "dy"])
@@ -211,7 +226,8 @@ def rglru_scan_backward(x, r_logit, i_logit, a_log, c, dy, h0=None, gate=None, d
     st = lib().ssd_rglru_scan_backward(
         B, L, D, code, oc, _dev(x, "x"), _dev(r_logit, "r_logit", x.shape), _dev(i_logit, "i_logit", x.shape),
         _dev(a_log, "a_log", (D,), torch.float32), float(c), _dev(h0, "h0", (B, D), torch.float32),
-        _dev(gate, "gate", x.shape), _dev(dy, "dy", x.shape), _dev(dh_last, "dh_last", (B, D), torch.float32),
+        _dev(gate, "gate", x.shape), _dev(chunk_states, "chunk_states", chunk_states_shape(B, L, D), torch.float32),
+        _dev(dy, "dy", x.shape), _dev(dh_last, "dh_last", (B, D), torch.float32),
         _dev(g["dx"], "dx"), _dev(g["dr_logit"], "dr_logit"), _dev(g["di_logit"], "di_logit"),
         _dev(g["da_log"], "da_log"), _dev(g["dh0"], "dh0"), _dev(g.get("dgate"), "dgate"), _stream(x.device))
     _raise(st, "rglru_scan_backward")
@@ -219,9 +235,9 @@ def rglru_scan_backward(x, r_logit, i_logit, a_log, c, dy, h0=None, gate=None, d
 
 
 # ----------------------------------------------------------------------------- MinMax
-def minmax_scan(r, s, x0=None, gate=None, return_last_state: bool = False, out_dtype=None):
+def minmax_scan(r, s, x0=None, gate=None, return_last_state: bool = False, out_dtype=None, chunk_states=None):
     """MinMax scan x_t = max(min(r_t, x_{t-1}), s_t) over [B, L, D] (see ``ssd_minmax_scan``);
-    with ``gate``, y = x * gate.  Returns y, or (y, x_last)."""
+    with ``gate``, y = x * gate; ``chunk_states`` as for ``rglru_scan``.  Returns y, or (y, x_last)."""
     torch = _torch()
     B, L, D = r.shape
     code = _act([r, s, gate], ["r", "s", "gate"])
@@ -230,7 +246,9 @@ def minmax_scan(r, s, x0=None, gate=None, return_last_state: bool = False, out_d
     x_last = torch.empty((B, D), device=r.device, dtype=torch.float32) if return_last_state else None
     st = lib().ssd_minmax_scan(B, L, D, code, oc, _dev(r, "r"), _dev(s, "s", r.shape),
                                _dev(x0, "x0", (B, D), torch.float32), _dev(gate, "gate", r.shape), _dev(y, "y"),
-                               _dev(x_last, "x_last"), _stream(r.device))
+                               _dev(x_last, "x_last"),
+                               _dev(chunk_states, "chunk_states", chunk_states_shape(B, L, D), torch.float32),
+                               _stream(r.device))
     _raise(st, "minmax_scan")
     return (y, x_last) if return_last_state else y
 
@@ -248,7 +266,7 @@ def minmax_update(r, s, state, gate=None, out_dtype=None):
     return y
 
 
-def minmax_scan_backward(r, s, dy, x0=None, gate=None, dx_last=None, out_dtype=None):
+def minmax_scan_backward(r, s, dy, x0=None, gate=None, dx_last=None, out_dtype=None, chunk_states=None):
     """Gradients of ``minmax_scan`` for the loss sum(dy * y) + sum(dx_last * x_last) (see
     ``ssd_minmax_scan_backward``).  Returns a dict: dr, ds [B, L, D] (out dtype), dx0 [B, D] (fp32),
     and dgate when a gate is given."""
@@ -263,7 +281,8 @@ def minmax_scan_backward(r, s, dy, x0=None, gate=None, dx_last=None, out_dtype=N
     g["dx0"] = torch.empty((B, D), device=r.device, dtype=torch.float32)
     st = lib().ssd_minmax_scan_backward(
         B, L, D, code, oc, _dev(r, "r"), _dev(s, "s", r.shape), _dev(x0, "x0", (B, D), torch.float32),
-        _dev(gate, "gate", r.shape), _dev(dy, "dy", r.shape), _dev(dx_last, "dx_last", (B, D), torch.float32),
+        _dev(gate, "gate", r.shape), _dev(chunk_states, "chunk_states", chunk_states_shape(B, L, D), torch.float32),
+        _dev(dy, "dy", r.shape), _dev(dx_last, "dx_last", (B, D), torch.float32),
         _dev(g["dr"], "dr"), _dev(g["ds"], "ds"), _dev(g["dx0"], "dx0"), _dev(g.get("dgate"), "dgate"),
         _stream(r.device))
     _raise(st, "minmax_scan_backward")
@@ -400,6 +419,6 @@ def hgrn2_update(q, k, v, g_logit, lower_bound: float, S, out_dtype=None):
     return o
 
 
-__all__ = ["rglru_scan", "rglru_scan_backward", "rglru_update", "selective_scan", "selective_update", "hgrn2_scan", "hgrn2_update",
+__all__ = ["chunk_states_shape", "SCAN_CHUNK", "rglru_scan", "rglru_scan_backward", "rglru_update", "selective_scan", "selective_update", "hgrn2_scan", "hgrn2_update",
            "minmax_scan", "minmax_update", "minmax_scan_backward", "causal_conv1d", "causal_conv1d_update", "lib", "LIB_PATH", "EXPORTS",
            "SSDError", "SSDValueError", "SSD_F32", "SSD_BF16"]

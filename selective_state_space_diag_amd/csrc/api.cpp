@@ -116,6 +116,10 @@ int check_dtypes(int in, int out) {
 }
 
 size_t esize(int dtype) { return dtype == SSD_BF16 ? 2 : 4; }
+// [B][ceil(L / SSD_SCAN_CHUNK)][D] fp32 chunk states
+size_t chunk_bytes(int64_t B, int64_t L, int64_t D) {
+  return (size_t)(B * ((L + SSD_SCAN_CHUNK - 1) / SSD_SCAN_CHUNK) * D) * 4;
+}
 
 // a*b*c... without signed overflow for the sizes we accept (each factor < 2^40)
 bool too_big(std::initializer_list<int64_t> dims) {
@@ -155,12 +159,12 @@ const char* ssd_status_str(int status) {
 
 const char* ssd_last_error(void) { return g_last_error.c_str(); }
 
-int ssd_version(void) { return 100; }
+int ssd_version(void) { return 200; }
 
 // ============================================================================ RG-LRU
 int ssd_rglru_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype, const void* x, const void* r_logit,
                    const void* i_logit, const float* a_log, float c, const float* h0, const void* gate, void* y,
-                   float* h_last, void* stream) {
+                   float* h_last, float* chunk_states, void* stream) {
   SSD_TRY(check_dtypes(in_dtype, out_dtype));
   if (B < 0 || L < 0 || D < 0) return fail(SSD_ERR_SHAPE, "negative size");
   if (too_big({B, L, D}) || D >= (int64_t)1 << 22 || B * ((L + 63) / 64) * ((D + 63) / 64) >= (int64_t)1 << 31)
@@ -173,7 +177,7 @@ int ssd_rglru_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype,
   const size_t sb = (size_t)(B * D) * 4;
   std::vector<Span> ins = {{"x", x, ab}, {"r_logit", r_logit, ab}, {"i_logit", i_logit, ab},
                            {"a_log", a_log, (size_t)D * 4}, {"h0", h0, sb}, {"gate", gate, ab}};
-  std::vector<Span> outs = {{"y", y, yb}, {"h_last", h_last, sb}};
+  std::vector<Span> outs = {{"y", y, yb}, {"h_last", h_last, sb}, {"chunk_states", chunk_states, chunk_bytes(B, L, D)}};
   std::vector<Span> all = ins;
   all.insert(all.end(), outs.begin(), outs.end());
   SSD_TRY(check_align(all));
@@ -182,7 +186,7 @@ int ssd_rglru_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype,
   if (B * D == 0) return ok();
   if (L == 0) return hip_status(ssd::launch_copy_or_zero(h_last, h0, B * D, s), "rglru_scan");
   ssd::RglruScanArgs a{B, L, D, in_dtype == SSD_BF16, out_dtype == SSD_BF16, x, r_logit, i_logit, a_log, c, h0, gate,
-                       y, h_last, nullptr};
+                       y, h_last, chunk_states, nullptr};
   SSD_TRY(get_scratch(stream, kScratchScan1, ssd::scan1_scratch_bytes(B, L, D), &a.scratch));
   return hip_status(ssd::launch_rglru_scan(a, s), "rglru_scan launch");
 }
@@ -212,7 +216,8 @@ int ssd_rglru_update(int64_t B, int64_t D, int in_dtype, int out_dtype, const vo
 
 int ssd_rglru_scan_backward(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype, const void* x,
                             const void* r_logit, const void* i_logit, const float* a_log, float c, const float* h0,
-                            const void* gate, const void* dy, const float* dh_last, void* dx, void* dr_logit,
+                            const void* gate, const float* chunk_states, const void* dy, const float* dh_last,
+                            void* dx, void* dr_logit,
                             void* di_logit, float* da_log, float* dh0, void* dgate, void* stream) {
   SSD_TRY(check_dtypes(in_dtype, out_dtype));
   if (B < 0 || L < 0 || D < 0) return fail(SSD_ERR_SHAPE, "negative size");
@@ -227,7 +232,8 @@ int ssd_rglru_scan_backward(int64_t B, int64_t L, int64_t D, int in_dtype, int o
   const size_t sb = (size_t)(B * D) * 4;
   std::vector<Span> ins = {{"x", x, ab},           {"r_logit", r_logit, ab}, {"i_logit", i_logit, ab},
                            {"a_log", a_log, (size_t)D * 4}, {"h0", h0, sb}, {"gate", gate, ab},
-                           {"dy", dy, ab},         {"dh_last", dh_last, sb}};
+                           {"dy", dy, ab},         {"dh_last", dh_last, sb},
+                           {"chunk_states", chunk_states, chunk_bytes(B, L, D)}};
   std::vector<Span> outs = {{"dx", dx, ob},        {"dr_logit", dr_logit, ob}, {"di_logit", di_logit, ob},
                             {"da_log", da_log, (size_t)D * 4}, {"dh0", dh0, sb}, {"dgate", gate ? dgate : nullptr, ob}};
   std::vector<Span> all = ins;
@@ -241,14 +247,14 @@ int ssd_rglru_scan_backward(int64_t B, int64_t L, int64_t D, int in_dtype, int o
     return hip_status(ssd::launch_copy_or_zero(dh0, dh_last, B * D, s), "rglru_scan_backward");
   }
   ssd::RglruBwdArgs a{B, L, D, in_dtype == SSD_BF16, out_dtype == SSD_BF16, x, r_logit, i_logit, a_log, c, h0, gate,
-                      dy, dh_last, dx, dr_logit, di_logit, gate ? dgate : nullptr, da_log, dh0, nullptr};
+                      chunk_states, dy, dh_last, dx, dr_logit, di_logit, gate ? dgate : nullptr, da_log, dh0, nullptr};
   SSD_TRY(get_scratch(stream, kScratchScan1Bwd, ssd::rglru_bwd_scratch_bytes(B, L, D), &a.scratch));
   return hip_status(ssd::launch_rglru_scan_backward(a, s), "rglru_scan_backward launch");
 }
 
 // ============================================================================ MinMax
 int ssd_minmax_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype, const void* r, const void* s_in,
-                    const float* x0, const void* gate, void* y, float* x_last, void* stream) {
+                    const float* x0, const void* gate, void* y, float* x_last, float* chunk_states, void* stream) {
   SSD_TRY(check_dtypes(in_dtype, out_dtype));
   if (B < 0 || L < 0 || D < 0) return fail(SSD_ERR_SHAPE, "negative size");
   if (too_big({B, L, D}) || D >= (int64_t)1 << 22 || B * ((L + 63) / 64) * ((D + 63) / 64) >= (int64_t)1 << 31)
@@ -258,7 +264,7 @@ int ssd_minmax_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype
   const size_t ab = (size_t)nact * esize(in_dtype), yb = (size_t)nact * esize(out_dtype);
   const size_t sb = (size_t)(B * D) * 4;
   std::vector<Span> ins = {{"r", r, ab}, {"s", s_in, ab}, {"x0", x0, sb}, {"gate", gate, ab}};
-  std::vector<Span> outs = {{"y", y, yb}, {"x_last", x_last, sb}};
+  std::vector<Span> outs = {{"y", y, yb}, {"x_last", x_last, sb}, {"chunk_states", chunk_states, chunk_bytes(B, L, D)}};
   std::vector<Span> all = ins;
   all.insert(all.end(), outs.begin(), outs.end());
   SSD_TRY(check_align(all));
@@ -266,7 +272,8 @@ int ssd_minmax_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (B * D == 0) return ok();
   if (L == 0) return hip_status(ssd::launch_copy_or_zero(x_last, x0, B * D, st), "minmax_scan");
-  ssd::MinmaxScanArgs a{B, L, D, in_dtype == SSD_BF16, out_dtype == SSD_BF16, r, s_in, x0, gate, y, x_last, nullptr};
+  ssd::MinmaxScanArgs a{B, L, D, in_dtype == SSD_BF16, out_dtype == SSD_BF16, r, s_in, x0, gate, y, x_last,
+                        chunk_states, nullptr};
   SSD_TRY(get_scratch(stream, kScratchScan1, ssd::scan1_scratch_bytes(B, L, D), &a.scratch));
   return hip_status(ssd::launch_minmax_scan(a, st), "minmax_scan launch");
 }
@@ -291,8 +298,9 @@ int ssd_minmax_update(int64_t B, int64_t D, int in_dtype, int out_dtype, const v
 }
 
 int ssd_minmax_scan_backward(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype, const void* r,
-                             const void* s_in, const float* x0, const void* gate, const void* dy,
-                             const float* dx_last, void* dr, void* ds, float* dx0, void* dgate, void* stream) {
+                             const void* s_in, const float* x0, const void* gate, const float* chunk_states,
+                             const void* dy, const float* dx_last, void* dr, void* ds, float* dx0, void* dgate,
+                             void* stream) {
   SSD_TRY(check_dtypes(in_dtype, out_dtype));
   if (B < 0 || L < 0 || D < 0) return fail(SSD_ERR_SHAPE, "negative size");
   if (too_big({B, L, D}) || D >= (int64_t)1 << 22 || B * ((L + 63) / 64) * ((D + 63) / 64) >= (int64_t)1 << 31)
@@ -302,7 +310,8 @@ int ssd_minmax_scan_backward(int64_t B, int64_t L, int64_t D, int in_dtype, int 
   const size_t ab = (size_t)nact * esize(in_dtype), ob = (size_t)nact * esize(out_dtype);
   const size_t sb = (size_t)(B * D) * 4;
   std::vector<Span> ins = {{"r", r, ab},   {"s", s_in, ab}, {"x0", x0, sb},
-                           {"gate", gate, ab}, {"dy", dy, ab}, {"dx_last", dx_last, sb}};
+                           {"gate", gate, ab}, {"dy", dy, ab}, {"dx_last", dx_last, sb},
+                           {"chunk_states", chunk_states, chunk_bytes(B, L, D)}};
   std::vector<Span> outs = {{"dr", dr, ob}, {"ds", ds, ob}, {"dx0", dx0, sb}, {"dgate", gate ? dgate : nullptr, ob}};
   std::vector<Span> all = ins;
   all.insert(all.end(), outs.begin(), outs.end());
@@ -311,7 +320,8 @@ int ssd_minmax_scan_backward(int64_t B, int64_t L, int64_t D, int in_dtype, int 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (B * D == 0) return ok();
   if (L == 0) return hip_status(ssd::launch_copy_or_zero(dx0, dx_last, B * D, st), "minmax_scan_backward");
-  ssd::MinmaxBwdArgs a{B, L, D, in_dtype == SSD_BF16, out_dtype == SSD_BF16, r, s_in, x0, gate, dy, dx_last,
+  ssd::MinmaxBwdArgs a{B, L, D, in_dtype == SSD_BF16, out_dtype == SSD_BF16, r, s_in, x0, gate, chunk_states, dy,
+                       dx_last,
                        dr, ds, gate ? dgate : nullptr, dx0, nullptr};
   SSD_TRY(get_scratch(stream, kScratchScan1Bwd, ssd::minmax_bwd_scratch_bytes(B, L, D), &a.scratch));
   return hip_status(ssd::launch_minmax_scan_backward(a, st), "minmax_scan_backward launch");

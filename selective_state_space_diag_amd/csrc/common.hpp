@@ -205,13 +205,27 @@ __device__ __forceinline__ bool word_ready(unsigned long long w, uint32_t epoch)
 __device__ __forceinline__ float word_value(unsigned long long w) { return __uint_as_float((uint32_t)w); }
 
 // Per-launch control block at the head of a lookback scratch buffer.  `tick` packs the number of
-// completed launches (high 32 bits) with the next work-unit ticket (low 32 bits), so one atomic
-// add hands a workgroup both its ticket and the launch epoch.
-struct LookbackCtl {
-  unsigned long long tick;
-  unsigned int done;     // workgroups finished in the current launch
-  unsigned int error;    // set if a bounded wait ever expired (must never happen)
+// completed launches (high 32 bits; a launch stamps its lookback words with that number + 1) with
+// the next work unit of a single-counter kernel (low 32 bits), so one atomic add hands a workgroup
+// both; the last workgroup of a launch resets the counters it used and advances the count.  The
+// atomics on one address retire one at a time (about 12 ns apiece on gfx950, near 80 units per
+// microsecond): enough for a forward scan, whose units are long, while kernels with shorter units
+// use kTicketClasses counters, each on a 128-byte line of its own.  Class x owns the sequences whose
+// index is x mod kTicketClasses and hands their units out in chunk order, so every unit a lookback
+// waits on comes from the same counter and was taken earlier.
+constexpr int kTicketClasses = 32;
+struct alignas(128) TicketLine {
+  unsigned int next;  // next local ticket of the class
+  unsigned int done;  // workgroups of this home class that have finished
 };
+struct LookbackCtl {
+  TicketLine cls[kTicketClasses];
+  alignas(128) unsigned long long tick;
+  unsigned int done;      // workgroups finished (single-counter kernels)
+  unsigned int done_all;  // home classes whose workgroups have all finished
+  unsigned int error;     // set if a bounded wait ever expired (must never happen)
+};
+constexpr int64_t kCtlBytes = (int64_t)((sizeof(LookbackCtl) + 255) / 256 * 256);
 
 constexpr unsigned int kSpinLimit = 1u << 20;  // each spin is a memory round trip: ~1-2 s bound
 

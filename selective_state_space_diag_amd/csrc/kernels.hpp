@@ -22,7 +22,8 @@ struct RglruScanArgs {
   const void* gate;  // y = gelu(gate) * h, or NULL
   void* y;
   float* h_last;
-  void* scratch;     // scan1_scratch_bytes
+  float* chunk_states;  // [B][ceil(L/64)][D] state entering each 64-step chunk, or NULL
+  void* scratch;        // scan1_scratch_bytes
 };
 hipError_t launch_rglru_scan(const RglruScanArgs& a, hipStream_t s);
 
@@ -48,6 +49,7 @@ struct RglruBwdArgs {
   float c;
   const float* h0;
   const void* gate;
+  const float* chunk_states;  // the forward's chunk states, or NULL (then recomputed)
   const void* dy;         // in dtype
   const float* dh_last;   // [B][D] or NULL
   void *dx, *dr_logit, *di_logit, *dgate;  // out dtype; dgate may be NULL
@@ -66,7 +68,8 @@ struct MinmaxScanArgs {
   const void* gate;  // y = x * gate, or NULL
   void* y;
   float* x_last;
-  void* scratch;     // scan1_scratch_bytes
+  float* chunk_states;  // as RglruScanArgs
+  void* scratch;        // scan1_scratch_bytes
 };
 hipError_t launch_minmax_scan(const MinmaxScanArgs& a, hipStream_t s);
 
@@ -76,6 +79,7 @@ struct MinmaxBwdArgs {
   const void *r, *s;
   const float* x0;        // [B][D] or NULL
   const void* gate;       // or NULL
+  const float* chunk_states;  // the forward's chunk states, or NULL (then recomputed)
   const void* dy;         // in dtype
   const float* dx_last;   // [B][D] or NULL
   void *dr, *ds, *dgate;  // out dtype; dgate may be NULL

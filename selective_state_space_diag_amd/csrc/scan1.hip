@@ -30,6 +30,9 @@
 //   * With the carry known, each wave re-runs h = f(a_t, b_t; h) over its registers and stores y.
 #include <algorithm>
 
+#include <mutex>
+#include <unordered_map>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -54,7 +57,6 @@ struct Scan1Params {
   float* carry_out;    // [B][n_chunks][D]: state entering each chunk (record passes)
   LookbackCtl* ctl;
   unsigned long long* words;  // [unit][3][tile width]: aggregate a, aggregate b, inclusive h
-  int one_unit_each;          // grid == number of units: every workgroup takes exactly one ticket
 };
 
 // ------------------------------------------------------------------ RG-LRU step
@@ -93,9 +95,9 @@ struct AffineOp {
   struct Chan {
     float kc;  // c * a_log * log2(e), so that log2 a_t = kc * r
   };
-  static __device__ __forceinline__ Chan chan(const Scan1Params& p, int64_t ch) {
-    return Chan{p.c * p.a_log[ch] * kLog2e};
-  }
+  // The channel parameter is loaded with a unit's inputs (param) and turned into Chan when used.
+  static __device__ __forceinline__ float param(const Scan1Params& p, int64_t ch) { return p.a_log[ch]; }
+  static __device__ __forceinline__ Chan chan(const Scan1Params& p, float a_log) { return Chan{p.c * a_log * kLog2e}; }
   static __device__ __forceinline__ void step(const float (&v)[3], const Chan& ch, float& a, float& b) {
     const float r = sigmoid_f(v[1]);
     const float i = sigmoid_f(v[2]);
@@ -119,7 +121,8 @@ __device__ __forceinline__ float mm_max(float a, float b) { return __builtin_ele
 struct MinMaxOp {
   static constexpr int kIn = 2;
   struct Chan {};
-  static __device__ __forceinline__ Chan chan(const Scan1Params&, int64_t) { return Chan{}; }
+  static __device__ __forceinline__ float param(const Scan1Params&, int64_t) { return 0.0f; }
+  static __device__ __forceinline__ Chan chan(const Scan1Params&, float) { return Chan{}; }
   static __device__ __forceinline__ void step(const float (&v)[3], const Chan&, float& a, float& b) {
     a = v[0];
     b = v[1];
@@ -131,11 +134,92 @@ struct MinMaxOp {
   static __device__ __forceinline__ float gated(float h, float g) { return h * g; }
 };
 
+// ------------------------------------------------------------------ work tickets
+// Sequences (batch row x channel tile) of ticket class x: x, x + K, x + 2K, ... below n_seq.  Every
+// count here is below 2^31 (the entry points bound the number of units).
+__device__ __forceinline__ uint32_t class_seqs(uint32_t n_seq, uint32_t x) {
+  return x < n_seq ? (n_seq - 1 - x) / kTicketClasses + 1 : 0u;
+}
+
+constexpr unsigned long long kNoUnit = ~0ull;
+
+// Taking a unit is split in two so that the atomic's round trip overlaps the caller's work (waiting
+// on it at once would also wait for every load issued before it).  Thread 0 only.  xc is the class
+// being drawn from (initially the home class, blockIdx mod kTicketClasses; it only moves forward)
+// and left counts the classes not yet found empty.
+__device__ __forceinline__ uint32_t take_begin(LookbackCtl* ctl, int xc, int left) {
+  return left > 0 ? atomicAdd(&ctl->cls[xc].next, 1u) : ~0u;
+}
+// The unit as (class << 32) | local ticket, or kNoUnit once every class is exhausted.  When the
+// ticket drawn by take_begin is past its class's end, the following classes are tried in turn; an
+// exhausted class is recognised there by a plain load before an atomic is spent on it.
+__device__ __forceinline__ unsigned long long take_next_class(LookbackCtl* ctl, uint32_t n_seq, uint32_t n_chunks,
+                                                              int* xc, int* left) {
+  while (--*left > 0) {
+    *xc = *xc + 1 == kTicketClasses ? 0 : *xc + 1;
+    const uint32_t lim = class_seqs(n_seq, (uint32_t)*xc) * n_chunks;
+    unsigned int* ctr = &ctl->cls[*xc].next;
+    if (lim > 0 && __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < lim) {
+      const uint32_t m = atomicAdd(ctr, 1u);
+      if (m < lim) return ((unsigned long long)*xc << 32) | m;
+    }
+  }
+  return kNoUnit;
+}
+__device__ __forceinline__ unsigned long long take_end(LookbackCtl* ctl, uint32_t n_seq, uint32_t n_chunks, int& xc,
+                                                       int& left, uint32_t m) {
+  if (left <= 0) return kNoUnit;
+  if (m < class_seqs(n_seq, (uint32_t)xc) * n_chunks) return ((unsigned long long)xc << 32) | m;
+  return take_next_class(ctl, n_seq, n_chunks, &xc, &left);
+}
+__device__ __forceinline__ unsigned long long take_unit(LookbackCtl* ctl, uint32_t n_seq, uint32_t n_chunks, int& xc,
+                                                       int& left) {
+  return take_end(ctl, n_seq, n_chunks, xc, left, take_begin(ctl, xc, left));
+}
+
+// A ticket read from LDS is the same in every lane: keep it (and all index arithmetic on it) scalar.
+__device__ __forceinline__ unsigned long long uniform_ticket(unsigned long long t) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)t), hi = __builtin_amdgcn_readfirstlane((uint32_t)(t >> 32));
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Sequence and chunk of a unit: a class hands its sequences' units out chunk by chunk.
+struct SeqChunk {
+  int64_t seq, chunk;
+};
+__device__ __forceinline__ SeqChunk unit_seq_chunk(unsigned long long t, uint32_t n_seq) {
+  const uint32_t x = (uint32_t)(t >> 32), m = (uint32_t)t;
+  const uint32_t n = class_seqs(n_seq, x);
+  const uint32_t c = m / n;
+  return SeqChunk{(int64_t)x + (int64_t)kTicketClasses * (m - c * n), (int64_t)c};
+}
+
+__device__ __forceinline__ uint32_t launch_epoch(LookbackCtl* ctl) {
+  return (uint32_t)(__hip_atomic_load(&ctl->tick, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 32) + 1u;
+}
+
+// Thread 0 of every workgroup, once, after its last unit.  The last workgroup of each home class
+// reports to done_all; the last of those resets every counter and publishes the launch count E (all
+// workgroups have then taken their last ticket).
+__device__ void finish_launch(LookbackCtl* ctl, uint32_t E) {
+  const int h = (int)(blockIdx.x % kTicketClasses);
+  const unsigned int n_home = (gridDim.x - 1 - h) / kTicketClasses + 1;
+  if (atomicAdd(&ctl->cls[h].done, 1u) != n_home - 1) return;
+  __hip_atomic_store(&ctl->cls[h].done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned int homes = gridDim.x < (unsigned)kTicketClasses ? gridDim.x : (unsigned)kTicketClasses;
+  if (atomicAdd(&ctl->done_all, 1u) != homes - 1) return;
+  for (int x = 0; x < kTicketClasses; ++x)
+    __hip_atomic_store(&ctl->cls[x].next, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&ctl->done_all, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&ctl->tick, (unsigned long long)E << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ------------------------------------------------------------------ work units and loads
 // Raw inputs of one wave's kSteps steps (the loads of a unit, kept in flight until needed).
 template <class Op, typename Tin, int V>
 struct Raw {
   typename win<Tin, V, kStreaming>::raw v[Op::kIn][kSteps];
+  float prm[V];  // the channels' parameters (Op::param)
 };
 
 struct Unit {
@@ -143,13 +227,23 @@ struct Unit {
   int rows;  // valid steps in the chunk (kChunk except for a ragged last chunk)
 };
 
-__device__ __forceinline__ Unit unit_of(const Scan1Params& p, int64_t ticket) {
-  const int64_t per_round = p.B * p.n_tiles;
+// CLASSES: the ticket is (class << 32) | local ticket; otherwise units go chunk by chunk, all
+// (batch row, tile) sequences of a chunk in turn.
+template <bool CLASSES>
+__device__ __forceinline__ Unit unit_of(const Scan1Params& p, unsigned long long ticket) {
   Unit u;
-  u.c = ticket / per_round;  // chunk-major ticket order
-  const int64_t rr = ticket - u.c * per_round;
-  u.b = rr / p.n_tiles;
-  u.k = rr - u.b * p.n_tiles;
+  if constexpr (CLASSES) {
+    const SeqChunk sc = unit_seq_chunk(ticket, (uint32_t)(p.B * p.n_tiles));
+    u.c = sc.chunk;
+    u.b = sc.seq / p.n_tiles;
+    u.k = sc.seq - u.b * p.n_tiles;
+  } else {
+    const int64_t per_round = p.B * p.n_tiles;
+    u.c = (int64_t)ticket / per_round;
+    const int64_t rr = (int64_t)ticket - u.c * per_round;
+    u.b = rr / p.n_tiles;
+    u.k = rr - u.b * p.n_tiles;
+  }
   u.rows = (int)min<int64_t>(kChunk, p.L - u.c * kChunk);
   return u;
 }
@@ -178,6 +272,9 @@ __device__ __forceinline__ void fetch(const Scan1Params& p, const Unit& u, uint3
 #pragma unroll
     for (int q = 0; q < Op::kIn; ++q) raw.v[q][s] = LD::load(w[q], lane_off, ro);
   }
+  const int64_t chl = lane_off / es;
+#pragma unroll
+  for (int v = 0; v < V; ++v) raw.prm[v] = Op::param(p, chl + v);
 }
 
 // The output gate of unit u for this wave (same clamping), loaded when the unit's carry is being
@@ -269,35 +366,57 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(wav
 void scan1_kernel(Scan1Params p) {
   constexpr int TW = 64 * V;  // channels per tile
   __shared__ unsigned long long s_tick[2];
+  __shared__ uint32_t s_epoch;
   __shared__ float s_aggA[kWaves][TW];
   __shared__ float s_aggB[kWaves][TW];
   __shared__ float s_carry[TW];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t total = p.B * p.n_tiles * p.n_chunks;
   using LD = win<Tin, V, kStreaming>;
 
-  if (threadIdx.x == 0) s_tick[0] = atomicAdd(&p.ctl->tick, 1ull);
+  // Tickets: the output pass, whose units are long, draws them from the single counter; the record
+  // pass, with short units, from the ticket classes.
+  constexpr bool CLS = RECORD;
+  const int64_t total = p.B * p.n_tiles * p.n_chunks;
+  const uint32_t n_seq = (uint32_t)(p.B * p.n_tiles);
+  auto unit_ticket = [&](unsigned long long t) -> unsigned long long {
+    if constexpr (CLS) return uniform_ticket(t);
+    const int64_t q = (int64_t)(t & 0xffffffffull);
+    return q < total ? (unsigned long long)q : kNoUnit;
+  };
+  int xc = (int)(blockIdx.x % kTicketClasses), left = kTicketClasses;  // class cursor (thread 0)
+  if (threadIdx.x == 0) {
+    if constexpr (CLS) {
+      s_epoch = launch_epoch(p.ctl);
+      s_tick[0] = take_unit(p.ctl, n_seq, (uint32_t)p.n_chunks, xc, left);
+    } else {
+      s_tick[0] = atomicAdd(&p.ctl->tick, 1ull);
+    }
+  }
   __syncthreads();
-  const uint32_t E = (uint32_t)(s_tick[0] >> 32) + 1u;  // epoch carried by this launch's words
-  int64_t ticket = (int64_t)(s_tick[0] & 0xffffffffull);
+  // epoch carried by this launch's words
+  const uint32_t E = CLS ? __builtin_amdgcn_readfirstlane(s_epoch) : (uint32_t)(s_tick[0] >> 32) + 1u;
+  unsigned long long ticket = unit_ticket(s_tick[0]);
   Raw<Op, Tin, V> raw;
   // The lane's channels within a tile are the same for every unit; the tile base moves.
   auto lane_off_of = [&](const Unit& u) -> uint32_t {
     const int64_t ch0 = u.k * TW + (int64_t)lane * V;
     return (uint32_t)(min<int64_t>(ch0, p.D - V) * (int64_t)sizeof(Tin));
   };
-  if (ticket < total) {
-    const Unit u0 = unit_of(p, ticket);
+  if (ticket != kNoUnit) {
+    const Unit u0 = unit_of<CLS>(p, ticket);
     fetch<Op, Tin, V>(p, u0, lane_off_of(u0), wave, raw);
   }
   int parity = 0;
 
-  while (ticket < total) {
-    const Unit u = unit_of(p, ticket);
-    if (threadIdx.x == 0)  // next ticket, one unit ahead (none needed when the grid covers every unit)
-      s_tick[parity ^ 1] = p.one_unit_each ? ~0ull : atomicAdd(&p.ctl->tick, 1ull);
+  while (ticket != kNoUnit) {
+    const Unit u = unit_of<CLS>(p, ticket);
+    uint32_t m_next = 0;  // next ticket, one unit ahead (thread 0)
+    if (threadIdx.x == 0) {
+      if constexpr (CLS) m_next = take_begin(p.ctl, xc, left);
+      else s_tick[parity ^ 1] = atomicAdd(&p.ctl->tick, 1ull);
+    }
     const int64_t ch0 = u.k * TW + (int64_t)lane * V;
     const bool ch_ok = ch0 < p.D;  // V = 2 only when D is even
     const int64_t chl = ch_ok ? ch0 : p.D - V;
@@ -306,7 +425,7 @@ void scan1_kernel(Scan1Params p) {
     // ---- step pairs and the wave's aggregate
     typename Op::Chan cc[V];
 #pragma unroll
-    for (int v = 0; v < V; ++v) cc[v] = Op::chan(p, chl + v);
+    for (int v = 0; v < V; ++v) cc[v] = Op::chan(p, raw.prm[v]);
     float av[kSteps][V], bv[kSteps][V];
     float Ag[V], Bg[V];
 #pragma unroll
@@ -334,22 +453,19 @@ void scan1_kernel(Scan1Params p) {
       s_aggA[wave][lane * V + v] = Ag[v];
       s_aggB[wave][lane * V + v] = Bg[v];
     }
+    if constexpr (CLS)
+      if (threadIdx.x == 0) s_tick[parity ^ 1] = take_end(p.ctl, n_seq, (uint32_t)p.n_chunks, xc, left, m_next);
     __syncthreads();  // aggregates in LDS; the next ticket is visible
-    const int64_t next = p.one_unit_each ? total : (int64_t)(s_tick[parity ^ 1] & 0xffffffffull);
-    if (next < total) {  // in flight during the lookback
-      const Unit un = unit_of(p, next);
+    const unsigned long long next = unit_ticket(s_tick[parity ^ 1]);
+    if (next != kNoUnit) {  // in flight during the lookback
+      const Unit un = unit_of<CLS>(p, next);
       fetch<Op, Tin, V>(p, un, lane_off_of(un), wave, raw);
     }
     typename LD::raw graw[GATE ? kSteps : 1];
     if constexpr (GATE) fetch_gate<Tin, V>(p, u, lane_off_of(u), wave, graw);
 
-    // ---- waves 0 .. V-1: chunk aggregate, publish, carry-in, inclusive
-    // Chunks form blocks of kBlock.  The carry into chunk c is the inclusive state published by the
-    // last chunk of the previous block (h0 for the first block), followed by the aggregates of the
-    // earlier chunks of c's own block, applied in chunk order.  Every carry is therefore one fixed
-    // function of the inputs (bitwise reproducible), and the serial chain has n_chunks / kBlock
-    // links.  All the words a unit needs are requested at once; only missing ones are polled again.
-    // Each of these waves resolves 64 of the tile's channels, one per lane.
+    // ---- waves 0 .. V-1: chunk aggregate, publish, carry-in, inclusive (64 of the tile's
+    //      channels per wave, one per lane)
     if (wave < V) {
       const int64_t seq_unit = (u.b * p.n_tiles + u.k) * p.n_chunks;
       const int j = wave * 64 + lane;
@@ -365,7 +481,7 @@ void scan1_kernel(Scan1Params p) {
       float incl;
       const float hin = lookback_carry<Op, TW>(p.ctl, p.words, seq_unit, u.c, p.n_chunks, j, E, Ac, Bc, init, &incl);
       if (p.h_last && j_ok && u.c == p.n_chunks - 1) p.h_last[u.b * p.D + ch] = incl;
-      if (RECORD && j_ok) p.carry_out[(u.b * p.n_chunks + u.c) * p.D + ch] = hin;
+      if ((RECORD || p.carry_out) && j_ok) p.carry_out[(u.b * p.n_chunks + u.c) * p.D + ch] = hin;
       s_carry[j] = hin;
     }
     __syncthreads();
@@ -401,8 +517,9 @@ void scan1_kernel(Scan1Params p) {
     parity ^= 1;
   }
 
-  // ---- last workgroup to finish resets the ticket and advances the epoch
-  if (threadIdx.x == 0) {
+  // ---- the last workgroup to finish resets the counters and advances the launch count
+  if (CLS && threadIdx.x == 0) finish_launch(p.ctl, E);
+  if (!CLS && threadIdx.x == 0) {
     const unsigned int old = atomicAdd(&p.ctl->done, 1u);
     if (old == gridDim.x - 1) {
       __hip_atomic_store(&p.ctl->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -434,7 +551,7 @@ __global__ __launch_bounds__(256) void update1_kernel(Upd1Params p) {
 #pragma unroll
   for (int k = 0; k < Op::kIn; ++k) in[k] = io<Tin>::load(p.in[k], idx);
   float a, b;
-  Op::step(in, Op::chan(q, d), a, b);
+  Op::step(in, Op::chan(q, Op::param(q, d)), a, b);
   const float h = Op::apply(a, b, p.state[idx]);
   p.state[idx] = h;
   io<Tout>::store(p.y, idx, GATE ? Op::gated(h, io<Tin>::load(p.gate, idx)) : h);
@@ -450,8 +567,8 @@ __global__ __launch_bounds__(256) void update1_kernel(Upd1Params p) {
 //   dx = g beta i,  d i_logit = g beta x i (1 - i),  dl = g h_{t-1} a - g (i x) a^2 / beta,
 //   d r_logit = dl c a_log r (1 - r),  d a_log += dl c r,  d gate = dy h_t gelu'(gate),
 //   and dh0 = q_0.
-// One work unit per workgroup: (batch, 64-channel tile, chunk), one channel per lane, 4 waves x 16
-// steps; units are ticketed in reverse chunk order.
+// Work units are (batch row, tile of 64 V channels, chunk), one channel pair per lane, 8 waves x 8
+// steps; a resident grid takes them from the ticket classes, chunks in reverse order.
 struct Bwd1Params {
   int64_t B, L, D;
   int64_t n_tiles, n_chunks;
@@ -494,7 +611,8 @@ constexpr int kBSteps = kChunk / kBWaves;  // steps per wave
 template <typename Tin, typename Tout, int V, bool GATE>
 __global__ __launch_bounds__(kBWaves * 64) void rglru_bwd_kernel(Bwd1Params p) {
   constexpr int TW = 64 * V;  // channels per tile
-  __shared__ unsigned long long s_tick;
+  __shared__ unsigned long long s_tick[2];
+  __shared__ uint32_t s_epoch;
   __shared__ float s_fA[kBWaves][TW], s_fB[kBWaves][TW];  // forward wave aggregates
   __shared__ float s_rA[kBWaves][TW], s_rB[kBWaves][TW];  // reverse wave aggregates
   __shared__ float s_qin[TW];
@@ -503,175 +621,178 @@ __global__ __launch_bounds__(kBWaves * 64) void rglru_bwd_kernel(Bwd1Params p) {
   using ST = win<Tout, V, kStreaming>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (threadIdx.x == 0) s_tick = atomicAdd(&p.ctl->tick, 1ull);
-  __syncthreads();
-  const uint32_t E = (uint32_t)(s_tick >> 32) + 1u;
-  const int64_t ticket = (int64_t)(s_tick & 0xffffffffull);  // the grid holds exactly one per unit
-  const int64_t per_round = p.B * p.n_tiles;
-  const int64_t cr = ticket / per_round;  // reverse chunk index
-  const int64_t c = p.n_chunks - 1 - cr;
-  const int64_t rr = ticket - cr * per_round;
-  const int64_t b = rr / p.n_tiles, k = rr - b * p.n_tiles;
-  const int rows = (int)min<int64_t>(kChunk, p.L - c * kChunk);
-  const int64_t ch0 = k * TW + (int64_t)lane * V;
-  const bool ch_ok = ch0 < p.D;  // V = 2 only when D is even
-  const int64_t chl = ch_ok ? ch0 : p.D - V;
-  const int64_t t0 = c * kChunk + (int64_t)wave * kBSteps;
-  const int nvalid = rows - wave * kBSteps;
-
-  // ---- loads of the unit's rows (rows past the chunk read its last row; results unused)
-  constexpr int es = sizeof(Tin);
-  auto window = [&](const void* a, int e) {
-    return make_window(static_cast<const char*>(a) + ((b * p.L + c * kChunk) * p.D) * e, (uint32_t)(rows * p.D * e));
-  };
-  const auto wx = window(p.x, es), wr = window(p.r, es), wi = window(p.i, es), wd = window(p.dy, es);
-  const auto wg = window(GATE ? p.gate : p.x, es);
-  const uint32_t row_in = (uint32_t)(p.D * es), lane_in = (uint32_t)(chl * es);
-  typename LD::raw rx[kBSteps], rrl[kBSteps], ril[kBSteps], rdy[kBSteps], rg[GATE ? kBSteps : 1];
-#pragma unroll
-  for (int s = 0; s < kBSteps; ++s) {
-    const uint32_t ro = (uint32_t)min(wave * kBSteps + s, rows - 1) * row_in;
-    rx[s] = LD::load(wx, lane_in, ro);
-    rrl[s] = LD::load(wr, lane_in, ro);
-    ril[s] = LD::load(wi, lane_in, ro);
-    rdy[s] = LD::load(wd, lane_in, ro);
-    if (GATE) rg[GATE ? s : 0] = LD::load(wg, lane_in, ro);
-  }
-  float kc[V];
-#pragma unroll
-  for (int v = 0; v < V; ++v) kc[v] = p.c * p.a_log[chl + v] * kLog2e;
-
-  // ---- forward pairs, reverse pairs, and both wave aggregates
-  float av[kBSteps][V], bv[kBSteps][V], ev[kBSteps][V];
-  float fA[V], fB[V], rA[V], rB[V];
-#pragma unroll
-  for (int v = 0; v < V; ++v) { fA[v] = 1.0f; fB[v] = 0.0f; rA[v] = 1.0f; rB[v] = 0.0f; }
-#pragma unroll
-  for (int s = 0; s < kBSteps; ++s) {
-    const bool ok = ch_ok && (t0 + s < p.L);
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      const float in3[3] = {LD::get(rx[s], v), LD::get(rrl[s], v), LD::get(ril[s], v)};
-      float a, bb;
-      AffineOp::step(in3, AffineOp::Chan{kc[v]}, a, bb);
-      const float G = GATE ? gelu_f(LD::get(rg[GATE ? s : 0], v)) : 1.0f;
-      av[s][v] = ok ? a : 1.0f;
-      bv[s][v] = ok ? bb : 0.0f;
-      ev[s][v] = ok ? LD::get(rdy[s], v) * G : 0.0f;
-      fB[v] = fmaf(av[s][v], fB[v], bv[s][v]);
-      fA[v] *= av[s][v];
-    }
-  }
-#pragma unroll
-  for (int s = kBSteps - 1; s >= 0; --s)
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      rB[v] = fmaf(av[s][v], rB[v], av[s][v] * ev[s][v]);
-      rA[v] *= av[s][v];
-    }
-#pragma unroll
-  for (int v = 0; v < V; ++v) {
-    s_fA[wave][lane * V + v] = fA[v];
-    s_fB[wave][lane * V + v] = fB[v];
-    s_rA[wave][lane * V + v] = rA[v];
-    s_rB[wave][lane * V + v] = rB[v];
-  }
-  __syncthreads();
-
-  // ---- waves 0 .. V-1: chunk reverse aggregate, publish, reverse carry (lookback over later
-  //      chunks), one channel of the tile per lane
-  if (wave < V) {
-    const int j = wave * 64 + lane;
-    const int64_t seq_unit = (b * p.n_tiles + k) * p.n_chunks;
-    float Ac = 1.0f, Bc = 0.0f;
-#pragma unroll
-    for (int w = kBWaves - 1; w >= 0; --w) {
-      Bc = fmaf(s_rA[w][j], Bc, s_rB[w][j]);
-      Ac *= s_rA[w][j];
-    }
-    const int64_t chj = k * TW + j;
-    const float init = p.dh_last ? p.dh_last[b * p.D + (chj < p.D ? chj : p.D - 1)] : 0.0f;
-    float incl;
-    s_qin[j] = lookback_carry<AffineOp, TW>(p.ctl, p.words, seq_unit, cr, p.n_chunks, j, E, Ac, Bc, init, &incl);
-  }
-  __syncthreads();
-
-  // ---- forward states entering each step of this wave, and the reverse carry into it
-  float hp[kBSteps][V], q[V];
-#pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const int j = lane * V + v;
-    float h = p.carry[(b * p.n_chunks + c) * p.D + chl + v];
-    for (int w = 0; w < wave; ++w) h = fmaf(s_fA[w][j], h, s_fB[w][j]);
-#pragma unroll
-    for (int s = 0; s < kBSteps; ++s) {
-      hp[s][v] = h;
-      h = fmaf(av[s][v], h, bv[s][v]);
-    }
-    float qq = s_qin[j];
-    for (int w = kBWaves - 1; w > wave; --w) qq = fmaf(s_rA[w][j], qq, s_rB[w][j]);
-    q[v] = qq;
-  }
-  // ---- per-step gradients, last step first
-  const auto wdx = window(p.dx, (int)sizeof(Tout)), wdr = window(p.dr, (int)sizeof(Tout));
-  const auto wdi = window(p.di, (int)sizeof(Tout)), wdg = window(GATE && p.dgate ? p.dgate : p.dx, (int)sizeof(Tout));
-  const uint32_t row_out = (uint32_t)(p.D * (int64_t)sizeof(Tout)), lane_out = (uint32_t)(chl * (int64_t)sizeof(Tout));
-  float ca[V], dal[V];
-#pragma unroll
-  for (int v = 0; v < V; ++v) { ca[v] = p.c * p.a_log[chl + v]; dal[v] = 0.0f; }
-#pragma unroll
-  for (int s = kBSteps - 1; s >= 0; --s) {
-    float o_dx[V], o_dr[V], o_di[V], o_dg[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      const float g = ev[s][v] + q[v];
-      q[v] = av[s][v] * g;
-      const float xx = LD::get(rx[s], v);
-      const float r = sigmoid_f(LD::get(rrl[s], v));
-      const float i = sigmoid_f(LD::get(ril[s], v));
-      const float a = av[s][v];
-      const float beta = hw_sqrt(one_minus_a2(kc[v] * r, a));
-      const float gb = g * beta;
-      const float dl = g * a * (hp[s][v] - (i * xx) * a * hw_rcp(beta));
-      o_dx[v] = gb * i;
-      o_di[v] = gb * xx * i * (1.0f - i);
-      o_dr[v] = dl * ca[v] * r * (1.0f - r);
-      if (s < nvalid) dal[v] = fmaf(dl * p.c, r, dal[v]);
-      if (GATE) o_dg[v] = LD::get(rdy[s], v) * fmaf(a, hp[s][v], bv[s][v]) * gelu_grad_f(LD::get(rg[GATE ? s : 0], v));
-    }
-    if (ch_ok && s < nvalid) {
-      const uint32_t ro = (uint32_t)(wave * kBSteps + s) * row_out;
-      ST::store(wdx, lane_out, ro, o_dx);
-      ST::store(wdr, lane_out, ro, o_dr);
-      ST::store(wdi, lane_out, ro, o_di);
-      if (GATE && p.dgate) ST::store(wdg, lane_out, ro, o_dg);
-    }
-  }
-  if (p.dh0 && ch_ok && c == 0 && wave == 0)
-#pragma unroll
-    for (int v = 0; v < V; ++v) p.dh0[b * p.D + ch0 + v] = q[v];
-#pragma unroll
-  for (int v = 0; v < V; ++v) s_dal[wave][lane * V + v] = ch_ok ? dal[v] : 0.0f;
-  __syncthreads();
-  if (wave < V) {
-    const int j = wave * 64 + lane;
-    const int64_t chj = k * TW + j;
-    if (chj < p.D) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kBWaves; ++w) acc += s_dal[w][j];
-      p.dalog_part[(b * p.n_chunks + c) * p.D + chj] = acc;
-    }
-  }
-
-  // ---- last workgroup to finish resets the ticket and advances the epoch
+  int xc = (int)(blockIdx.x % kTicketClasses), left = kTicketClasses;  // ticket cursor (thread 0)
+  const uint32_t n_seq = (uint32_t)(p.B * p.n_tiles);
   if (threadIdx.x == 0) {
-    const unsigned int old = atomicAdd(&p.ctl->done, 1u);
-    if (old == gridDim.x - 1) {
-      __hip_atomic_store(&p.ctl->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&p.ctl->tick, (unsigned long long)E << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    s_epoch = launch_epoch(p.ctl);
+    s_tick[0] = take_unit(p.ctl, n_seq, (uint32_t)p.n_chunks, xc, left);
   }
+  __syncthreads();
+  const uint32_t E = __builtin_amdgcn_readfirstlane(s_epoch);
+  for (int parity = 0;; parity ^= 1) {
+    const unsigned long long ticket = uniform_ticket(s_tick[parity]);
+    if (ticket == kNoUnit) break;
+    const SeqChunk sc = unit_seq_chunk(ticket, n_seq);
+    const int64_t cr = sc.chunk;  // reverse chunk index
+    const int64_t c = p.n_chunks - 1 - cr;
+    const int64_t b = sc.seq / p.n_tiles, k = sc.seq - b * p.n_tiles;
+    const int rows = (int)min<int64_t>(kChunk, p.L - c * kChunk);
+    const int64_t ch0 = k * TW + (int64_t)lane * V;
+    const bool ch_ok = ch0 < p.D;  // V = 2 only when D is even
+    const int64_t chl = ch_ok ? ch0 : p.D - V;
+    const int64_t t0 = c * kChunk + (int64_t)wave * kBSteps;
+    const int nvalid = rows - wave * kBSteps;
+
+    // ---- loads of the unit's rows (rows past the chunk read its last row; results unused)
+    constexpr int es = sizeof(Tin);
+    auto window = [&](const void* a, int e) {
+      return make_window(static_cast<const char*>(a) + ((b * p.L + c * kChunk) * p.D) * e, (uint32_t)(rows * p.D * e));
+    };
+    const auto wx = window(p.x, es), wr = window(p.r, es), wi = window(p.i, es), wd = window(p.dy, es);
+    const auto wg = window(GATE ? p.gate : p.x, es);
+    const uint32_t row_in = (uint32_t)(p.D * es), lane_in = (uint32_t)(chl * es);
+    typename LD::raw rx[kBSteps], rrl[kBSteps], ril[kBSteps], rdy[kBSteps], rg[GATE ? kBSteps : 1];
+  #pragma unroll
+    for (int s = 0; s < kBSteps; ++s) {
+      const uint32_t ro = (uint32_t)min(wave * kBSteps + s, rows - 1) * row_in;
+      rx[s] = LD::load(wx, lane_in, ro);
+      rrl[s] = LD::load(wr, lane_in, ro);
+      ril[s] = LD::load(wi, lane_in, ro);
+      rdy[s] = LD::load(wd, lane_in, ro);
+      if (GATE) rg[GATE ? s : 0] = LD::load(wg, lane_in, ro);
+    }
+    uint32_t m_next = 0;  // next unit, one ahead (thread 0; resolved at the end of this unit)
+    if (threadIdx.x == 0) m_next = take_begin(p.ctl, xc, left);
+    float kc[V];
+  #pragma unroll
+    for (int v = 0; v < V; ++v) kc[v] = p.c * p.a_log[chl + v] * kLog2e;
+
+    // ---- forward pairs, reverse pairs, and both wave aggregates
+    float av[kBSteps][V], bv[kBSteps][V], ev[kBSteps][V];
+    float fA[V], fB[V], rA[V], rB[V];
+  #pragma unroll
+    for (int v = 0; v < V; ++v) { fA[v] = 1.0f; fB[v] = 0.0f; rA[v] = 1.0f; rB[v] = 0.0f; }
+  #pragma unroll
+    for (int s = 0; s < kBSteps; ++s) {
+      const bool ok = ch_ok && (t0 + s < p.L);
+  #pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const float in3[3] = {LD::get(rx[s], v), LD::get(rrl[s], v), LD::get(ril[s], v)};
+        float a, bb;
+        AffineOp::step(in3, AffineOp::Chan{kc[v]}, a, bb);
+        const float G = GATE ? gelu_f(LD::get(rg[GATE ? s : 0], v)) : 1.0f;
+        av[s][v] = ok ? a : 1.0f;
+        bv[s][v] = ok ? bb : 0.0f;
+        ev[s][v] = ok ? LD::get(rdy[s], v) * G : 0.0f;
+        fB[v] = fmaf(av[s][v], fB[v], bv[s][v]);
+        fA[v] *= av[s][v];
+      }
+    }
+  #pragma unroll
+    for (int s = kBSteps - 1; s >= 0; --s)
+  #pragma unroll
+      for (int v = 0; v < V; ++v) {
+        rB[v] = fmaf(av[s][v], rB[v], av[s][v] * ev[s][v]);
+        rA[v] *= av[s][v];
+      }
+  #pragma unroll
+    for (int v = 0; v < V; ++v) {
+      s_fA[wave][lane * V + v] = fA[v];
+      s_fB[wave][lane * V + v] = fB[v];
+      s_rA[wave][lane * V + v] = rA[v];
+      s_rB[wave][lane * V + v] = rB[v];
+    }
+    __syncthreads();
+
+    // ---- waves 0 .. V-1: chunk reverse aggregate, publish, reverse carry (lookback over later
+    //      chunks), one channel of the tile per lane
+    if (wave < V) {
+      const int j = wave * 64 + lane;
+      const int64_t seq_unit = (b * p.n_tiles + k) * p.n_chunks;
+      float Ac = 1.0f, Bc = 0.0f;
+  #pragma unroll
+      for (int w = kBWaves - 1; w >= 0; --w) {
+        Bc = fmaf(s_rA[w][j], Bc, s_rB[w][j]);
+        Ac *= s_rA[w][j];
+      }
+      const int64_t chj = k * TW + j;
+      const float init = p.dh_last ? p.dh_last[b * p.D + (chj < p.D ? chj : p.D - 1)] : 0.0f;
+      float incl;
+      s_qin[j] = lookback_carry<AffineOp, TW>(p.ctl, p.words, seq_unit, cr, p.n_chunks, j, E, Ac, Bc, init, &incl);
+    }
+    __syncthreads();
+
+    // ---- forward states entering each step of this wave, and the reverse carry into it
+    float hp[kBSteps][V], q[V];
+  #pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int j = lane * V + v;
+      float h = p.carry[(b * p.n_chunks + c) * p.D + chl + v];
+      for (int w = 0; w < wave; ++w) h = fmaf(s_fA[w][j], h, s_fB[w][j]);
+  #pragma unroll
+      for (int s = 0; s < kBSteps; ++s) {
+        hp[s][v] = h;
+        h = fmaf(av[s][v], h, bv[s][v]);
+      }
+      float qq = s_qin[j];
+      for (int w = kBWaves - 1; w > wave; --w) qq = fmaf(s_rA[w][j], qq, s_rB[w][j]);
+      q[v] = qq;
+    }
+    // ---- per-step gradients, last step first
+    const auto wdx = window(p.dx, (int)sizeof(Tout)), wdr = window(p.dr, (int)sizeof(Tout));
+    const auto wdi = window(p.di, (int)sizeof(Tout)), wdg = window(GATE && p.dgate ? p.dgate : p.dx, (int)sizeof(Tout));
+    const uint32_t row_out = (uint32_t)(p.D * (int64_t)sizeof(Tout)), lane_out = (uint32_t)(chl * (int64_t)sizeof(Tout));
+    float ca[V], dal[V];
+  #pragma unroll
+    for (int v = 0; v < V; ++v) { ca[v] = p.c * p.a_log[chl + v]; dal[v] = 0.0f; }
+  #pragma unroll
+    for (int s = kBSteps - 1; s >= 0; --s) {
+      float o_dx[V], o_dr[V], o_di[V], o_dg[V];
+  #pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const float g = ev[s][v] + q[v];
+        q[v] = av[s][v] * g;
+        const float xx = LD::get(rx[s], v);
+        const float r = sigmoid_f(LD::get(rrl[s], v));
+        const float i = sigmoid_f(LD::get(ril[s], v));
+        const float a = av[s][v];
+        const float beta = hw_sqrt(one_minus_a2(kc[v] * r, a));
+        const float gb = g * beta;
+        const float dl = g * a * (hp[s][v] - (i * xx) * a * hw_rcp(beta));
+        o_dx[v] = gb * i;
+        o_di[v] = gb * xx * i * (1.0f - i);
+        o_dr[v] = dl * ca[v] * r * (1.0f - r);
+        if (s < nvalid) dal[v] = fmaf(dl * p.c, r, dal[v]);
+        if (GATE) o_dg[v] = LD::get(rdy[s], v) * fmaf(a, hp[s][v], bv[s][v]) * gelu_grad_f(LD::get(rg[GATE ? s : 0], v));
+      }
+      if (ch_ok && s < nvalid) {
+        const uint32_t ro = (uint32_t)(wave * kBSteps + s) * row_out;
+        ST::store(wdx, lane_out, ro, o_dx);
+        ST::store(wdr, lane_out, ro, o_dr);
+        ST::store(wdi, lane_out, ro, o_di);
+        if (GATE && p.dgate) ST::store(wdg, lane_out, ro, o_dg);
+      }
+    }
+    if (p.dh0 && ch_ok && c == 0 && wave == 0)
+  #pragma unroll
+      for (int v = 0; v < V; ++v) p.dh0[b * p.D + ch0 + v] = q[v];
+  #pragma unroll
+    for (int v = 0; v < V; ++v) s_dal[wave][lane * V + v] = ch_ok ? dal[v] : 0.0f;
+    __syncthreads();
+    if (wave < V) {
+      const int j = wave * 64 + lane;
+      const int64_t chj = k * TW + j;
+      if (chj < p.D) {
+        float acc = 0.0f;
+  #pragma unroll
+        for (int w = 0; w < kBWaves; ++w) acc += s_dal[w][j];
+        p.dalog_part[(b * p.n_chunks + c) * p.D + chj] = acc;
+      }
+    }
+    if (threadIdx.x == 0) s_tick[parity ^ 1] = take_end(p.ctl, n_seq, (uint32_t)p.n_chunks, xc, left, m_next);
+    __syncthreads();  // this unit's LDS is free; the next ticket is visible
+  }
+  if (threadIdx.x == 0) finish_launch(p.ctl, E);
 }
 
 // ------------------------------------------------------------------ MinMax backward
@@ -709,10 +830,20 @@ struct MmBwdParams {
 __device__ __forceinline__ float sel_lo(float u, float w) { return u == w ? 0.5f : (u > w ? 0.0f : 1.0f); }
 __device__ __forceinline__ float sel_hi(float u, float w) { return u == w ? 0.5f : (u < w ? 0.0f : 1.0f); }
 
+// The step weights are products of {0, 1/2, 1}, i.e. {0, 1/4, 1/2, 1}: four times a weight is a
+// byte, packed four to a register (one v_cvt_pk_u8_f32 to store, one v_cvt_f32_ubyte to read back).
+template <int N>
+struct Bytes4 {
+  uint32_t u[(N + 3) / 4] = {};
+  __device__ __forceinline__ void set(int i, float x4) { u[i >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(x4, i & 3, u[i >> 2]); }
+  __device__ __forceinline__ float get(int i) const { return (float)((u[i >> 2] >> (8 * (i & 3))) & 0xffu); }
+};
+
 template <typename Tin, typename Tout, int V, bool GATE>
-__global__ __launch_bounds__(kBWaves * 64) void minmax_bwd_kernel(MmBwdParams p) {
+__global__ __launch_bounds__(kBWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void minmax_bwd_kernel(MmBwdParams p) {
   constexpr int TW = 64 * V;  // channels per tile
-  __shared__ unsigned long long s_tick;
+  __shared__ unsigned long long s_tick[2];
+  __shared__ uint32_t s_epoch;
   __shared__ float s_fA[kBWaves][TW], s_fB[kBWaves][TW];  // forward wave aggregates
   __shared__ float s_rA[kBWaves][TW], s_rB[kBWaves][TW];  // reverse wave aggregates
   __shared__ float s_qin[TW];
@@ -720,159 +851,184 @@ __global__ __launch_bounds__(kBWaves * 64) void minmax_bwd_kernel(MmBwdParams p)
   using ST = win<Tout, V, kStreaming>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (threadIdx.x == 0) s_tick = atomicAdd(&p.ctl->tick, 1ull);
-  __syncthreads();
-  const uint32_t E = (uint32_t)(s_tick >> 32) + 1u;
-  const int64_t ticket = (int64_t)(s_tick & 0xffffffffull);  // the grid holds exactly one per unit
-  const int64_t per_round = p.B * p.n_tiles;
-  const int64_t cr = ticket / per_round;  // reverse chunk index
-  const int64_t c = p.n_chunks - 1 - cr;
-  const int64_t rr = ticket - cr * per_round;
-  const int64_t b = rr / p.n_tiles, k = rr - b * p.n_tiles;
-  const int rows = (int)min<int64_t>(kChunk, p.L - c * kChunk);
-  const int64_t ch0 = k * TW + (int64_t)lane * V;
-  const bool ch_ok = ch0 < p.D;  // V = 2 only when D is even
-  const int64_t chl = ch_ok ? ch0 : p.D - V;
-  const int64_t t0 = c * kChunk + (int64_t)wave * kBSteps;
-  const int nvalid = rows - wave * kBSteps;
-
-  // ---- loads of the unit's rows (rows past the chunk read its last row; results unused)
-  constexpr int es = sizeof(Tin);
-  auto window = [&](const void* a, int e) {
-    return make_window(static_cast<const char*>(a) + ((b * p.L + c * kChunk) * p.D) * e, (uint32_t)(rows * p.D * e));
-  };
-  const auto wr = window(p.r, es), ws = window(p.s, es), wd = window(p.dy, es);
-  const auto wg = window(GATE ? p.gate : p.r, es);
-  const uint32_t row_in = (uint32_t)(p.D * es), lane_in = (uint32_t)(chl * es);
-  typename LD::raw raw_r[kBSteps], raw_s[kBSteps], rdy[kBSteps], rg[GATE ? kBSteps : 1];
-#pragma unroll
-  for (int s = 0; s < kBSteps; ++s) {
-    const uint32_t ro = (uint32_t)min(wave * kBSteps + s, rows - 1) * row_in;
-    raw_r[s] = LD::load(wr, lane_in, ro);
-    raw_s[s] = LD::load(ws, lane_in, ro);
-    rdy[s] = LD::load(wd, lane_in, ro);
-    if (GATE) rg[GATE ? s : 0] = LD::load(wg, lane_in, ro);
+  int xc = (int)(blockIdx.x % kTicketClasses), left = kTicketClasses;  // ticket cursor (thread 0)
+  const uint32_t n_seq = (uint32_t)(p.B * p.n_tiles);
+  if (threadIdx.x == 0) {
+    s_epoch = launch_epoch(p.ctl);
+    s_tick[0] = take_unit(p.ctl, n_seq, (uint32_t)p.n_chunks, xc, left);
   }
-  float hc[V];
-#pragma unroll
-  for (int v = 0; v < V; ++v) hc[v] = p.carry[(b * p.n_chunks + c) * p.D + chl + v];
+  __syncthreads();
+  const uint32_t E = __builtin_amdgcn_readfirstlane(s_epoch);
+  for (int parity = 0;; parity ^= 1) {
+    const unsigned long long ticket = uniform_ticket(s_tick[parity]);
+    if (ticket == kNoUnit) break;
+    const SeqChunk sc = unit_seq_chunk(ticket, n_seq);
+    const int64_t cr = sc.chunk;  // reverse chunk index
+    const int64_t c = p.n_chunks - 1 - cr;
+    const int64_t b = sc.seq / p.n_tiles, k = sc.seq - b * p.n_tiles;
+    const int rows = (int)min<int64_t>(kChunk, p.L - c * kChunk);
+    const int64_t ch0 = k * TW + (int64_t)lane * V;
+    const bool ch_ok = ch0 < p.D;  // V = 2 only when D is even
+    const int64_t chl = ch_ok ? ch0 : p.D - V;
+    const int64_t t0 = c * kChunk + (int64_t)wave * kBSteps;
+    const int nvalid = rows - wave * kBSteps;
 
-  // ---- forward maps (identity past L and on idle lanes) and the wave's forward aggregate
-  float av[kBSteps][V], bv[kBSteps][V];
-  float fA[V], fB[V];
-#pragma unroll
-  for (int v = 0; v < V; ++v) { fA[v] = MinMaxOp::id_a(); fB[v] = MinMaxOp::id_b(); }
-#pragma unroll
-  for (int s = 0; s < kBSteps; ++s) {
-    const bool ok = ch_ok && (t0 + s < p.L);
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      av[s][v] = ok ? LD::get(raw_r[s], v) : MinMaxOp::id_a();
-      bv[s][v] = ok ? LD::get(raw_s[s], v) : MinMaxOp::id_b();
-      fB[v] = MinMaxOp::apply(av[s][v], bv[s][v], fB[v]);
-      fA[v] = MinMaxOp::fold_a(av[s][v], fA[v]);
+    // ---- loads of the unit's rows (rows past the chunk read its last row; results unused)
+    constexpr int es = sizeof(Tin);
+    auto window = [&](const void* a, int e) {
+      return make_window(static_cast<const char*>(a) + ((b * p.L + c * kChunk) * p.D) * e, (uint32_t)(rows * p.D * e));
+    };
+    const auto wr = window(p.r, es), ws = window(p.s, es), wd = window(p.dy, es);
+    const auto wg = window(GATE ? p.gate : p.r, es);
+    const uint32_t row_in = (uint32_t)(p.D * es), lane_in = (uint32_t)(chl * es);
+    typename LD::raw raw_r[kBSteps], raw_s[kBSteps], rdy[kBSteps], rg[GATE ? kBSteps : 1];
+  #pragma unroll
+    for (int s = 0; s < kBSteps; ++s) {
+      const uint32_t ro = (uint32_t)min(wave * kBSteps + s, rows - 1) * row_in;
+      raw_r[s] = LD::load(wr, lane_in, ro);
+      raw_s[s] = LD::load(ws, lane_in, ro);
+      rdy[s] = LD::load(wd, lane_in, ro);
     }
-  }
-#pragma unroll
-  for (int v = 0; v < V; ++v) {
-    s_fA[wave][lane * V + v] = fA[v];
-    s_fB[wave][lane * V + v] = fB[v];
-  }
-  __syncthreads();
+    uint32_t m_next = 0;  // next unit, one ahead (thread 0; resolved at the end of this unit)
+    if (threadIdx.x == 0) m_next = take_begin(p.ctl, xc, left);
+    float hc[V];
+  #pragma unroll
+    for (int v = 0; v < V; ++v) hc[v] = p.carry[(b * p.n_chunks + c) * p.D + chl + v];
 
-  // ---- forward states of this wave's steps, the reverse coefficients, the reverse aggregate
-  float ap[kBSteps][V], ev[kBSteps][V], kr[kBSteps][V], ks[kBSteps][V], xt[GATE ? kBSteps : 1][V];
-  float rA[V], rB[V];
-#pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const int j = lane * V + v;
-    float h = hc[v];
-    for (int w = 0; w < wave; ++w) h = MinMaxOp::apply(s_fA[w][j], s_fB[w][j], h);
-#pragma unroll
+    // ---- forward maps (identity past L and on idle lanes) and the wave's forward aggregate
+    float av[kBSteps][V], bv[kBSteps][V];
+    float fA[V], fB[V];
+  #pragma unroll
+    for (int v = 0; v < V; ++v) { fA[v] = MinMaxOp::id_a(); fB[v] = MinMaxOp::id_b(); }
+  #pragma unroll
     for (int s = 0; s < kBSteps; ++s) {
       const bool ok = ch_ok && (t0 + s < p.L);
-      const float r = av[s][v], sv = bv[s][v];
-      const float m = mm_min(r, h);
-      const float wm = sel_hi(m, sv);
-      ap[s][v] = ok ? wm * sel_lo(h, r) : 1.0f;
-      kr[s][v] = wm * sel_lo(r, h);
-      ks[s][v] = sel_hi(sv, m);
-      const float G = GATE ? LD::get(rg[GATE ? s : 0], v) : 1.0f;
-      ev[s][v] = ok ? LD::get(rdy[s], v) * G : 0.0f;
-      h = mm_max(m, sv);
-      if (GATE) xt[GATE ? s : 0][v] = h;
+  #pragma unroll
+      for (int v = 0; v < V; ++v) {
+        av[s][v] = ok ? LD::get(raw_r[s], v) : MinMaxOp::id_a();
+        bv[s][v] = ok ? LD::get(raw_s[s], v) : MinMaxOp::id_b();
+        fB[v] = MinMaxOp::apply(av[s][v], bv[s][v], fB[v]);
+        fA[v] = MinMaxOp::fold_a(av[s][v], fA[v]);
+      }
     }
-    rA[v] = 1.0f;
-    rB[v] = 0.0f;
-#pragma unroll
-    for (int s = kBSteps - 1; s >= 0; --s) {
-      rB[v] = fmaf(ap[s][v], rB[v], ap[s][v] * ev[s][v]);
-      rA[v] *= ap[s][v];
-    }
-    s_rA[wave][j] = rA[v];
-    s_rB[wave][j] = rB[v];
-  }
-  __syncthreads();
-
-  // ---- waves 0 .. V-1: chunk reverse aggregate, publish, reverse carry over later chunks
-  if (wave < V) {
-    const int j = wave * 64 + lane;
-    const int64_t seq_unit = (b * p.n_tiles + k) * p.n_chunks;
-    float Ac = 1.0f, Bc = 0.0f;
-#pragma unroll
-    for (int w = kBWaves - 1; w >= 0; --w) {
-      Bc = fmaf(s_rA[w][j], Bc, s_rB[w][j]);
-      Ac *= s_rA[w][j];
-    }
-    const int64_t chj = k * TW + j;
-    const float init = p.dx_last ? p.dx_last[b * p.D + (chj < p.D ? chj : p.D - 1)] : 0.0f;
-    float incl;
-    s_qin[j] = lookback_carry<AffineOp, TW>(p.ctl, p.words, seq_unit, cr, p.n_chunks, j, E, Ac, Bc, init, &incl);
-  }
-  __syncthreads();
-
-  // ---- per-step gradients, last step first
-  float q[V];
-#pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const int j = lane * V + v;
-    float qq = s_qin[j];
-    for (int w = kBWaves - 1; w > wave; --w) qq = fmaf(s_rA[w][j], qq, s_rB[w][j]);
-    q[v] = qq;
-  }
-  const auto wdr = window(p.dr, (int)sizeof(Tout)), wds = window(p.ds, (int)sizeof(Tout));
-  const auto wdg = window(GATE && p.dgate ? p.dgate : p.dr, (int)sizeof(Tout));
-  const uint32_t row_out = (uint32_t)(p.D * (int64_t)sizeof(Tout)), lane_out = (uint32_t)(chl * (int64_t)sizeof(Tout));
-#pragma unroll
-  for (int s = kBSteps - 1; s >= 0; --s) {
-    float o_dr[V], o_ds[V], o_dg[V];
-#pragma unroll
+  #pragma unroll
     for (int v = 0; v < V; ++v) {
-      const float g = ev[s][v] + q[v];
-      q[v] = ap[s][v] * g;
-      o_dr[v] = g * kr[s][v];
-      o_ds[v] = g * ks[s][v];
-      if (GATE) o_dg[v] = LD::get(rdy[s], v) * xt[GATE ? s : 0][v];
+      s_fA[wave][lane * V + v] = fA[v];
+      s_fB[wave][lane * V + v] = fB[v];
     }
-    if (ch_ok && s < nvalid) {
-      const uint32_t ro = (uint32_t)(wave * kBSteps + s) * row_out;
-      ST::store(wdr, lane_out, ro, o_dr);
-      ST::store(wds, lane_out, ro, o_ds);
-      if (GATE && p.dgate) ST::store(wdg, lane_out, ro, o_dg);
-    }
-  }
-  if (p.dx0 && ch_ok && c == 0 && wave == 0)
-#pragma unroll
-    for (int v = 0; v < V; ++v) p.dx0[b * p.D + ch0 + v] = q[v];
+    // the gate is first needed after the barrier: its loads are issued here, once r and s are spent
+    if (GATE)
+  #pragma unroll
+      for (int s = 0; s < kBSteps; ++s)
+        rg[GATE ? s : 0] = LD::load(wg, lane_in, (uint32_t)min(wave * kBSteps + s, rows - 1) * row_in);
+    __syncthreads();
 
-  // ---- last workgroup to finish resets the ticket and advances the epoch
-  if (threadIdx.x == 0) {
-    const unsigned int old = atomicAdd(&p.ctl->done, 1u);
-    if (old == gridDim.x - 1) {
-      __hip_atomic_store(&p.ctl->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&p.ctl->tick, (unsigned long long)E << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // ---- forward states of this wave's steps: the output-gate gradient (stored now, in step order),
+    //      the step weights, and the wave's reverse aggregate
+    const uint32_t row_out = (uint32_t)(p.D * (int64_t)sizeof(Tout)), lane_out = (uint32_t)(chl * (int64_t)sizeof(Tout));
+    const auto wdg = window(GATE && p.dgate ? p.dgate : p.dr, (int)sizeof(Tout));
+    // 4 a'_t = 4 wM wX, 4 wM wR and 4 wS of step s, channel v at bytes (k kBSteps + s) V + v, k = 0, 1, 2
+    Bytes4<3 * kBSteps * V> wt;
+    auto wi = [](int k, int s, int v) { return (k * kBSteps + s) * V + v; };
+    float ev[kBSteps][V];
+    {
+      float h[V];
+  #pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int j = lane * V + v;
+        h[v] = hc[v];
+        for (int w = 0; w < wave; ++w) h[v] = MinMaxOp::apply(s_fA[w][j], s_fB[w][j], h[v]);
+      }
+  #pragma unroll
+      for (int s = 0; s < kBSteps; ++s) {
+        const bool ok = ch_ok && (t0 + s < p.L);
+        float o_dg[V];
+  #pragma unroll
+        for (int v = 0; v < V; ++v) {
+          const float r = av[s][v], sv = bv[s][v];
+          const float m = mm_min(r, h[v]);
+          const float wm2 = 2.0f * sel_hi(m, sv);
+          wt.set(wi(0, s, v), ok ? wm2 * (2.0f * sel_lo(h[v], r)) : 4.0f);
+          wt.set(wi(1, s, v), wm2 * (2.0f * sel_lo(r, h[v])));
+          wt.set(wi(2, s, v), 4.0f * sel_hi(sv, m));
+          const float dy = LD::get(rdy[s], v);
+          ev[s][v] = ok ? (GATE ? dy * LD::get(rg[GATE ? s : 0], v) : dy) : 0.0f;
+          h[v] = mm_max(m, sv);
+          o_dg[v] = dy * h[v];
+        }
+        if (GATE && p.dgate && ch_ok && s < nvalid) ST::store(wdg, lane_out, (uint32_t)(wave * kBSteps + s) * row_out, o_dg);
+      }
     }
+    // the packed weights are final here: keep them packed (rather than their inputs) from now on
+  #pragma unroll
+    for (int i = 0; i < (3 * kBSteps * V + 3) / 4; ++i) asm volatile("" : "+v"(wt.u[i]));
+  #pragma unroll
+    for (int v = 0; v < V; ++v) {
+      float rA = 1.0f, rB = 0.0f;
+  #pragma unroll
+      for (int s = kBSteps - 1; s >= 0; --s) {
+        const float a = 0.25f * wt.get(wi(0, s, v));
+        rB = fmaf(a, rB, a * ev[s][v]);
+        rA *= a;
+      }
+      s_rA[wave][lane * V + v] = rA;
+      s_rB[wave][lane * V + v] = rB;
+    }
+    __syncthreads();
+
+    // ---- waves 0 .. V-1: chunk reverse aggregate, publish, reverse carry over later chunks
+    if (wave < V) {
+      const int j = wave * 64 + lane;
+      const int64_t seq_unit = (b * p.n_tiles + k) * p.n_chunks;
+      float Ac = 1.0f, Bc = 0.0f;
+  #pragma unroll
+      for (int w = kBWaves - 1; w >= 0; --w) {
+        Bc = fmaf(s_rA[w][j], Bc, s_rB[w][j]);
+        Ac *= s_rA[w][j];
+      }
+      const int64_t chj = k * TW + j;
+      const float init = p.dx_last ? p.dx_last[b * p.D + (chj < p.D ? chj : p.D - 1)] : 0.0f;
+      float incl;
+      s_qin[j] = lookback_carry<AffineOp, TW>(p.ctl, p.words, seq_unit, cr, p.n_chunks, j, E, Ac, Bc, init, &incl);
+    }
+    __syncthreads();
+
+    // ---- per-step gradients, last step first (the packed weights are decoded again here rather than
+    //      kept unpacked through the lookback: the empty asm hides the earlier decode)
+  #pragma unroll
+    for (int i = 0; i < (3 * kBSteps * V + 3) / 4; ++i) asm volatile("" : "+v"(wt.u[i]));
+    float q[V];
+  #pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int j = lane * V + v;
+      float qq = s_qin[j];
+      for (int w = kBWaves - 1; w > wave; --w) qq = fmaf(s_rA[w][j], qq, s_rB[w][j]);
+      q[v] = qq;
+    }
+    const auto wdr = window(p.dr, (int)sizeof(Tout)), wds = window(p.ds, (int)sizeof(Tout));
+  #pragma unroll
+    for (int s = kBSteps - 1; s >= 0; --s) {
+      float o_dr[V], o_ds[V];
+  #pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const float g4 = 0.25f * (ev[s][v] + q[v]);
+        q[v] = wt.get(wi(0, s, v)) * g4;
+        o_dr[v] = wt.get(wi(1, s, v)) * g4;
+        o_ds[v] = wt.get(wi(2, s, v)) * g4;
+      }
+      if (ch_ok && s < nvalid) {
+        const uint32_t ro = (uint32_t)(wave * kBSteps + s) * row_out;
+        ST::store(wdr, lane_out, ro, o_dr);
+        ST::store(wds, lane_out, ro, o_ds);
+      }
+    }
+    if (p.dx0 && ch_ok && c == 0 && wave == 0)
+  #pragma unroll
+      for (int v = 0; v < V; ++v) p.dx0[b * p.D + ch0 + v] = q[v];
+    if (threadIdx.x == 0) s_tick[parity ^ 1] = take_end(p.ctl, n_seq, (uint32_t)p.n_chunks, xc, left, m_next);
+    __syncthreads();  // this unit's LDS is free; the next ticket is visible
   }
+  if (threadIdx.x == 0) finish_launch(p.ctl, E);
 }
 
 // d a_log[d] = sum over (batch, chunk) of the unit partials, in a fixed order: slice s of
@@ -895,26 +1051,27 @@ __global__ __launch_bounds__(256) void dalog_final_kernel(const float* slices, i
 }
 
 // ------------------------------------------------------------------ launchers
-// Persistent grid: as many workgroups as stay resident together (by the kernel's own occupancy),
-// never more than there are work units.
+// Persistent grids: as many workgroups as stay resident together (by the kernel's own occupancy,
+// cached per kernel), never more than there are work units.
+int64_t resident_blocks(const void* kern, int threads) {
+  static std::mutex mu;
+  static std::unordered_map<const void*, int64_t> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto it = cache.find(kern);
+  if (it != cache.end()) return it->second;
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, 0) != hipSuccess || per_cu <= 0) per_cu = 1;
+  return cache[kern] = (int64_t)per_cu * cus;
+}
 template <class Op, typename Tin, typename Tout, int V, bool GATE, bool RECORD>
 hipError_t launch_scan_t(const Scan1Params& p, hipStream_t s) {
+  const auto kern = scan1_kernel<Op, Tin, Tout, V, GATE, RECORD>;
   const int64_t total = p.B * p.n_tiles * p.n_chunks;
-  static int per_cu = 0, cus = 0;
-  if (per_cu == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan1_kernel<Op, Tin, Tout, V, GATE, RECORD>,
-                                                     kWaves * 64, 0) != hipSuccess ||
-        per_cu <= 0)
-      per_cu = 1;
-  }
-  const int64_t grid = std::min<int64_t>(total, (int64_t)per_cu * cus);
-  Scan1Params q = p;
-  q.one_unit_each = grid == total;
-  hipLaunchKernelGGL((scan1_kernel<Op, Tin, Tout, V, GATE, RECORD>), dim3((unsigned)grid), dim3(kWaves * 64), 0, s, q);
+  const int64_t grid = std::min<int64_t>(total, resident_blocks(reinterpret_cast<const void*>(kern), kWaves * 64));
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kWaves * 64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -934,7 +1091,7 @@ void scan_geometry(Scan1Params& p, void* scratch) {
   p.n_tiles = (p.D + TW - 1) / TW;
   p.n_chunks = (p.L + kChunk - 1) / kChunk;
   p.ctl = static_cast<LookbackCtl*>(scratch);
-  p.words = reinterpret_cast<unsigned long long*>(static_cast<char*>(scratch) + 256);
+  p.words = reinterpret_cast<unsigned long long*>(static_cast<char*>(scratch) + kCtlBytes);
 }
 
 // The record pass of the backward: no outputs, the state entering each chunk to p.carry_out.
@@ -981,7 +1138,7 @@ size_t scan1_scratch_bytes(int64_t B, int64_t L, int64_t D) {
   const int64_t TW = 64 * V;
   const int64_t n_tiles = (D + TW - 1) / TW;
   const int64_t n_chunks = (L + kChunk - 1) / kChunk;
-  return 256 + (size_t)(B * n_tiles * n_chunks) * 3 * TW * sizeof(unsigned long long);
+  return (size_t)kCtlBytes + (size_t)(B * n_tiles * n_chunks) * 3 * TW * sizeof(unsigned long long);
 }
 
 hipError_t launch_rglru_scan(const RglruScanArgs& a, hipStream_t s) {
@@ -989,7 +1146,7 @@ hipError_t launch_rglru_scan(const RglruScanArgs& a, hipStream_t s) {
   p.B = a.B; p.L = a.L; p.D = a.D;
   p.in[0] = a.x; p.in[1] = a.r_logit; p.in[2] = a.i_logit;
   p.gate = a.gate;
-  p.a_log = a.a_log; p.c = a.c; p.h0 = a.h0; p.y = a.y; p.h_last = a.h_last;
+  p.a_log = a.a_log; p.c = a.c; p.h0 = a.h0; p.y = a.y; p.h_last = a.h_last; p.carry_out = a.chunk_states;
   return launch_scan_op<AffineOp>(p, a.in_bf16, a.out_bf16, a.scratch, s);
 }
 
@@ -998,21 +1155,25 @@ hipError_t launch_minmax_scan(const MinmaxScanArgs& a, hipStream_t s) {
   p.B = a.B; p.L = a.L; p.D = a.D;
   p.in[0] = a.r; p.in[1] = a.s;
   p.gate = a.gate;
-  p.h0 = a.x0; p.y = a.y; p.h_last = a.x_last;
+  p.h0 = a.x0; p.y = a.y; p.h_last = a.x_last; p.carry_out = a.chunk_states;
   return launch_scan_op<MinMaxOp>(p, a.in_bf16, a.out_bf16, a.scratch, s);
 }
 
-template <int V, bool G>
-hipError_t launch_bwd_g(const Bwd1Params& q, int in_bf16, int out_bf16, dim3 grid, hipStream_t s) {
-  const dim3 blk(kBWaves * 64);
-  if (!in_bf16) hipLaunchKernelGGL((rglru_bwd_kernel<float, float, V, G>), grid, blk, 0, s, q);
-  else if (out_bf16) hipLaunchKernelGGL((rglru_bwd_kernel<bf16_t, bf16_t, V, G>), grid, blk, 0, s, q);
-  else hipLaunchKernelGGL((rglru_bwd_kernel<bf16_t, float, V, G>), grid, blk, 0, s, q);
+template <typename Tin, typename Tout, int V, bool G>
+hipError_t launch_bwd_k(const Bwd1Params& q, int64_t units, hipStream_t s) {
+  const auto kern = rglru_bwd_kernel<Tin, Tout, V, G>;
+  const int64_t grid = std::min<int64_t>(units, resident_blocks(reinterpret_cast<const void*>(kern), kBWaves * 64));
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBWaves * 64), 0, s, q);
   return hipGetLastError();
 }
+template <int V, bool G>
+hipError_t launch_bwd_g(const Bwd1Params& q, int in_bf16, int out_bf16, int64_t units, hipStream_t s) {
+  if (!in_bf16) return launch_bwd_k<float, float, V, G>(q, units, s);
+  return out_bf16 ? launch_bwd_k<bf16_t, bf16_t, V, G>(q, units, s) : launch_bwd_k<bf16_t, float, V, G>(q, units, s);
+}
 template <int V>
-hipError_t launch_bwd_dt(const Bwd1Params& q, bool gate, int in_bf16, int out_bf16, dim3 grid, hipStream_t s) {
-  return gate ? launch_bwd_g<V, true>(q, in_bf16, out_bf16, grid, s) : launch_bwd_g<V, false>(q, in_bf16, out_bf16, grid, s);
+hipError_t launch_bwd_dt(const Bwd1Params& q, bool gate, int in_bf16, int out_bf16, int64_t units, hipStream_t s) {
+  return gate ? launch_bwd_g<V, true>(q, in_bf16, out_bf16, units, s) : launch_bwd_g<V, false>(q, in_bf16, out_bf16, units, s);
 }
 
 // Scratch of the backward call: lookback control block and words (sized for the larger of the
@@ -1021,29 +1182,34 @@ namespace {
 // The reverse pass uses the same tiling as the forward (64 V channels per tile, V = 2 for even D),
 // so one word layout serves both.
 int64_t bwd_words_bytes(int64_t B, int64_t L, int64_t D) {
-  return ((int64_t)scan1_scratch_bytes(B, L, D) - 256 + 255) / 256 * 256;
+  return ((int64_t)scan1_scratch_bytes(B, L, D) - kCtlBytes + 255) / 256 * 256;
 }
 }  // namespace
 
 size_t rglru_bwd_scratch_bytes(int64_t B, int64_t L, int64_t D) {
   const int64_t n_chunks = (L + kChunk - 1) / kChunk;
   const int64_t per = (B * n_chunks * D * 4 + 255) / 256 * 256;
-  return (size_t)(256 + bwd_words_bytes(B, L, D) + 2 * per + (int64_t)kDalSlices * D * 4);
+  return (size_t)(kCtlBytes + bwd_words_bytes(B, L, D) + 2 * per + (int64_t)kDalSlices * D * 4);
 }
 
 hipError_t launch_rglru_scan_backward(const RglruBwdArgs& a, hipStream_t s) {
   const int64_t n_chunks = (a.L + kChunk - 1) / kChunk;
   const int64_t per = (a.B * n_chunks * a.D * 4 + 255) / 256 * 256;
   char* base = static_cast<char*>(a.scratch);
-  float* carry = reinterpret_cast<float*>(base + 256 + bwd_words_bytes(a.B, a.L, a.D));
-  float* dal = reinterpret_cast<float*>(reinterpret_cast<char*>(carry) + per);
-  // 1. forward pass that records the state entering every chunk (no outputs)
-  Scan1Params f{};
-  f.B = a.B; f.L = a.L; f.D = a.D;
-  f.in[0] = a.x; f.in[1] = a.r_logit; f.in[2] = a.i_logit;
-  f.a_log = a.a_log; f.c = a.c; f.h0 = a.h0; f.y = nullptr; f.h_last = nullptr; f.carry_out = carry;
-  hipError_t e = launch_record_op<AffineOp>(f, a.in_bf16, a.scratch, s);
-  if (e != hipSuccess) return e;
+  float* rec = reinterpret_cast<float*>(base + kCtlBytes + bwd_words_bytes(a.B, a.L, a.D));
+  float* dal = reinterpret_cast<float*>(reinterpret_cast<char*>(rec) + per);
+  // 1. the state entering every chunk: the forward's, or a forward pass that records it (no outputs)
+  const float* carry = a.chunk_states;
+  hipError_t e = hipSuccess;
+  if (!carry) {
+    Scan1Params f{};
+    f.B = a.B; f.L = a.L; f.D = a.D;
+    f.in[0] = a.x; f.in[1] = a.r_logit; f.in[2] = a.i_logit;
+    f.a_log = a.a_log; f.c = a.c; f.h0 = a.h0; f.y = nullptr; f.h_last = nullptr; f.carry_out = rec;
+    e = launch_record_op<AffineOp>(f, a.in_bf16, a.scratch, s);
+    if (e != hipSuccess) return e;
+    carry = rec;
+  }
   // 2. reverse pass, one workgroup per (batch, 64-channel tile, chunk)
   const int V = vec_width(a.D);
   Bwd1Params q{};
@@ -1053,10 +1219,10 @@ hipError_t launch_rglru_scan_backward(const RglruBwdArgs& a, hipStream_t s) {
   q.a_log = a.a_log; q.c = a.c; q.carry = carry; q.dh_last = a.dh_last;
   q.dx = a.dx; q.dr = a.dr_logit; q.di = a.di_logit; q.dgate = a.dgate; q.dalog_part = dal; q.dh0 = a.dh0;
   q.ctl = static_cast<LookbackCtl*>(a.scratch);
-  q.words = reinterpret_cast<unsigned long long*>(base + 256);
-  const dim3 grid((unsigned)(a.B * q.n_tiles * n_chunks));
-  if (V == 2) e = launch_bwd_dt<2>(q, a.gate != nullptr, a.in_bf16, a.out_bf16, grid, s);
-  else e = launch_bwd_dt<1>(q, a.gate != nullptr, a.in_bf16, a.out_bf16, grid, s);
+  q.words = reinterpret_cast<unsigned long long*>(base + kCtlBytes);
+  const int64_t units = a.B * q.n_tiles * n_chunks;
+  if (V == 2) e = launch_bwd_dt<2>(q, a.gate != nullptr, a.in_bf16, a.out_bf16, units, s);
+  else e = launch_bwd_dt<1>(q, a.gate != nullptr, a.in_bf16, a.out_bf16, units, s);
   if (e != hipSuccess) return e;
   // 3. d a_log
   float* slices = reinterpret_cast<float*>(reinterpret_cast<char*>(dal) + per);
@@ -1067,36 +1233,44 @@ hipError_t launch_rglru_scan_backward(const RglruBwdArgs& a, hipStream_t s) {
 }
 
 namespace {
-template <int V, bool G>
-hipError_t launch_mm_bwd_g(const MmBwdParams& q, int in_bf16, int out_bf16, dim3 grid, hipStream_t s) {
-  const dim3 blk(kBWaves * 64);
-  if (!in_bf16) hipLaunchKernelGGL((minmax_bwd_kernel<float, float, V, G>), grid, blk, 0, s, q);
-  else if (out_bf16) hipLaunchKernelGGL((minmax_bwd_kernel<bf16_t, bf16_t, V, G>), grid, blk, 0, s, q);
-  else hipLaunchKernelGGL((minmax_bwd_kernel<bf16_t, float, V, G>), grid, blk, 0, s, q);
+template <typename Tin, typename Tout, int V, bool G>
+hipError_t launch_mm_bwd_k(const MmBwdParams& q, int64_t units, hipStream_t s) {
+  const auto kern = minmax_bwd_kernel<Tin, Tout, V, G>;
+  const int64_t grid = std::min<int64_t>(units, resident_blocks(reinterpret_cast<const void*>(kern), kBWaves * 64));
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBWaves * 64), 0, s, q);
   return hipGetLastError();
 }
+template <int V, bool G>
+hipError_t launch_mm_bwd_g(const MmBwdParams& q, int in_bf16, int out_bf16, int64_t units, hipStream_t s) {
+  if (!in_bf16) return launch_mm_bwd_k<float, float, V, G>(q, units, s);
+  return out_bf16 ? launch_mm_bwd_k<bf16_t, bf16_t, V, G>(q, units, s) : launch_mm_bwd_k<bf16_t, float, V, G>(q, units, s);
+}
 template <int V>
-hipError_t launch_mm_bwd_dt(const MmBwdParams& q, bool gate, int in_bf16, int out_bf16, dim3 grid, hipStream_t s) {
-  return gate ? launch_mm_bwd_g<V, true>(q, in_bf16, out_bf16, grid, s) : launch_mm_bwd_g<V, false>(q, in_bf16, out_bf16, grid, s);
+hipError_t launch_mm_bwd_dt(const MmBwdParams& q, bool gate, int in_bf16, int out_bf16, int64_t units, hipStream_t s) {
+  return gate ? launch_mm_bwd_g<V, true>(q, in_bf16, out_bf16, units, s) : launch_mm_bwd_g<V, false>(q, in_bf16, out_bf16, units, s);
 }
 }  // namespace
 
 size_t minmax_bwd_scratch_bytes(int64_t B, int64_t L, int64_t D) {
   const int64_t n_chunks = (L + kChunk - 1) / kChunk;
-  return (size_t)(256 + bwd_words_bytes(B, L, D) + B * n_chunks * D * 4);
+  return (size_t)(kCtlBytes + bwd_words_bytes(B, L, D) + B * n_chunks * D * 4);
 }
 
 hipError_t launch_minmax_scan_backward(const MinmaxBwdArgs& a, hipStream_t s) {
   const int64_t n_chunks = (a.L + kChunk - 1) / kChunk;
   char* base = static_cast<char*>(a.scratch);
-  float* carry = reinterpret_cast<float*>(base + 256 + bwd_words_bytes(a.B, a.L, a.D));
-  // 1. forward pass that records the state entering every chunk (no outputs)
-  Scan1Params f{};
-  f.B = a.B; f.L = a.L; f.D = a.D;
-  f.in[0] = a.r; f.in[1] = a.s;
-  f.h0 = a.x0; f.y = nullptr; f.h_last = nullptr; f.carry_out = carry;
-  hipError_t e = launch_record_op<MinMaxOp>(f, a.in_bf16, a.scratch, s);
-  if (e != hipSuccess) return e;
+  float* rec = reinterpret_cast<float*>(base + kCtlBytes + bwd_words_bytes(a.B, a.L, a.D));
+  // 1. the state entering every chunk: the forward's, or a forward pass that records it (no outputs)
+  const float* carry = a.chunk_states;
+  if (!carry) {
+    Scan1Params f{};
+    f.B = a.B; f.L = a.L; f.D = a.D;
+    f.in[0] = a.r; f.in[1] = a.s;
+    f.h0 = a.x0; f.y = nullptr; f.h_last = nullptr; f.carry_out = rec;
+    const hipError_t e = launch_record_op<MinMaxOp>(f, a.in_bf16, a.scratch, s);
+    if (e != hipSuccess) return e;
+    carry = rec;
+  }
   // 2. reverse pass, one workgroup per (batch, 64-channel tile, chunk)
   const int V = vec_width(a.D);
   MmBwdParams q{};
@@ -1105,10 +1279,10 @@ hipError_t launch_minmax_scan_backward(const MinmaxBwdArgs& a, hipStream_t s) {
   q.r = a.r; q.s = a.s; q.gate = a.gate; q.dy = a.dy; q.carry = carry; q.dx_last = a.dx_last;
   q.dr = a.dr; q.ds = a.ds; q.dgate = a.dgate; q.dx0 = a.dx0;
   q.ctl = static_cast<LookbackCtl*>(a.scratch);
-  q.words = reinterpret_cast<unsigned long long*>(base + 256);
-  const dim3 grid((unsigned)(a.B * q.n_tiles * n_chunks));
-  return V == 2 ? launch_mm_bwd_dt<2>(q, a.gate != nullptr, a.in_bf16, a.out_bf16, grid, s)
-                : launch_mm_bwd_dt<1>(q, a.gate != nullptr, a.in_bf16, a.out_bf16, grid, s);
+  q.words = reinterpret_cast<unsigned long long*>(base + kCtlBytes);
+  const int64_t units = a.B * q.n_tiles * n_chunks;
+  return V == 2 ? launch_mm_bwd_dt<2>(q, a.gate != nullptr, a.in_bf16, a.out_bf16, units, s)
+                : launch_mm_bwd_dt<1>(q, a.gate != nullptr, a.in_bf16, a.out_bf16, units, s);
 }
 
 hipError_t launch_rglru_update(const RglruUpdateArgs& a, hipStream_t s) {

@@ -55,9 +55,9 @@ def test_status_strings_and_version(L):
     assert L.ssd_status_str(99) == b"unknown status"
 
 
-def rglru(L, B=2, Lq=8, D=4, ind=F32, outd=F32, x=0, r=1, i=2, a=3, c=8.0, h0=None, g=None, y=4, hl=None):
+def rglru(L, B=2, Lq=8, D=4, ind=F32, outd=F32, x=0, r=1, i=2, a=3, c=8.0, h0=None, g=None, y=4, hl=None, cs=None):
     p = lambda k: None if k is None else ptr(k)
-    return L.ssd_rglru_scan(B, Lq, D, ind, outd, p(x), p(r), p(i), p(a), c, p(h0), p(g), p(y), p(hl), None)
+    return L.ssd_rglru_scan(B, Lq, D, ind, outd, p(x), p(r), p(i), p(a), c, p(h0), p(g), p(y), p(hl), p(cs), None)
 
 
 def test_rglru_scan_validation(L):
@@ -71,8 +71,11 @@ def test_rglru_scan_validation(L):
     assert rglru(L, y=0) == ALIAS                  # y on top of x
     assert rglru(L, h0=5, hl=5) == ALIAS           # h_last on top of h0
     assert rglru(L, g=6, y=6) == ALIAS             # y on top of the gate
+    assert rglru(L, cs=2) == ALIAS                 # chunk states on top of i_logit
     assert L.ssd_rglru_scan(2, 8, 4, F32, F32, ctypes.c_void_p(P + 8), ptr(1), ptr(2), ptr(3), 8.0, None, None,
-                            ptr(4), None, None) == ALIGN
+                            ptr(4), None, None, None) == ALIGN
+    assert L.ssd_rglru_scan(2, 8, 4, F32, F32, ptr(0), ptr(1), ptr(2), ptr(3), 8.0, None, None,
+                            ptr(4), None, ctypes.c_void_p(P + 5 * 64 * MB + 4), None) == ALIGN
     assert b"aligned" in L.ssd_last_error()
     # empty problem: nothing to do, no launch
     assert rglru(L, B=0) == OK
@@ -93,16 +96,17 @@ def test_rglru_update_validation(L):
 
 def test_minmax_validation(L):
     p = lambda k: None if k is None else ptr(k)
-    f = lambda B=2, Lq=8, D=4, ind=BF16, outd=F32, r=0, s=1, x0=None, g=None, y=4, xl=None: L.ssd_minmax_scan(
-        B, Lq, D, ind, outd, p(r), p(s), p(x0), p(g), p(y), p(xl), None)
+    f = lambda B=2, Lq=8, D=4, ind=BF16, outd=F32, r=0, s=1, x0=None, g=None, y=4, xl=None, cs=None: \
+        L.ssd_minmax_scan(B, Lq, D, ind, outd, p(r), p(s), p(x0), p(g), p(y), p(xl), p(cs), None)
     assert f(B=-1) == SHAPE
     assert f(ind=F32, outd=BF16) == DTYPE
     assert f(s=None) == NULL
     assert f(y=1) == ALIAS
     assert f(x0=5, xl=5) == ALIAS
     assert f(g=6, y=6) == ALIAS
+    assert f(cs=0) == ALIAS
     assert L.ssd_minmax_scan(2, 8, 4, BF16, F32, ptr(0), ctypes.c_void_p(P + 1), None, None, ptr(4), None,
-                             None) == ALIGN
+                             None, None) == ALIGN
     assert f(D=0) == OK
     u = lambda B=4, D=8, st=4, y=5, g=None: L.ssd_minmax_update(B, D, BF16, F32, ptr(0), ptr(1), p(g), p(st), p(y),
                                                                 None)

@@ -145,3 +145,51 @@ def test_minmax_backward_empty_sequence():
     g = ssd.minmax_scan_backward(r, r, r, dx_last=dxl)
     torch.cuda.synchronize()
     assert torch.equal(g["dx0"], dxl)
+
+
+# ----------------------------------------------------------------------------- saved chunk states
+@pytest.mark.parametrize("dtype,L,D", [(synth.F32, 64 * 3 + 7, 130), (synth.BF16, 64 * 5, 257)])
+def test_rglru_chunk_states_match_oracle_and_feed_backward(dtype, L, D):
+    import torch
+    import oracle
+    B = 2
+    inp = synth.rglru_inputs(B, L, D, dtype, 6000 + L, with_h0=True, with_gate=True)
+    x, r, i, g = (to_dev(inp.t[n]) for n in ("x", "r_logit", "i_logit", "gate"))
+    a_log, h0 = to_dev(inp.p["a_log"]), to_dev(inp.p["h0"])
+    cs = torch.full(ssd.chunk_states_shape(B, L, D), float("nan"), device="cuda")
+    ssd.rglru_scan(x, r, i, a_log, 8.0, h0=h0, gate=g, chunk_states=cs)
+    torch.cuda.synchronize()
+    # the state entering chunk k is h_{64k - 1} (h0 for k = 0): the ungated oracle's output there
+    y_ref, _ = oracle.rglru_scan(f64(inp.t["x"]), f64(inp.t["r_logit"]), f64(inp.t["i_logit"]), f64(inp.p["a_log"]),
+                                 8.0, h0=f64(inp.p["h0"]))
+    want = np.concatenate([f64(inp.p["h0"])[:, None, :], y_ref[:, 63:L - 1:64, :]], axis=1)
+    assert want.shape == tuple(cs.shape)
+    assert_close(host(cs), want, TOLB[dtype], "chunk_states")
+    dy = torch.randn((B, L, D), device="cuda").to(x.dtype)
+    args = (x, r, i, a_log, 8.0, dy)
+    g1 = ssd.rglru_scan_backward(*args, h0=h0, gate=g, chunk_states=cs)
+    g2 = ssd.rglru_scan_backward(*args, h0=h0, gate=g)
+    torch.cuda.synchronize()
+    for k in g2:
+        assert torch.equal(g1[k], g2[k]), k
+
+
+def test_minmax_chunk_states_exact_and_feed_backward():
+    import torch
+    import oracle
+    B, L, D = 2, 64 * 4 + 3, 96
+    inp = synth.minmax_inputs(B, L, D, synth.BF16, 6100, with_x0=True, with_gate=True, ties=True)
+    r, s, g = (to_dev(inp.t[n]) for n in ("r", "s", "gate"))
+    x0 = to_dev(inp.p["x0"])
+    cs = torch.full(ssd.chunk_states_shape(B, L, D), float("nan"), device="cuda")
+    ssd.minmax_scan(r, s, x0=x0, gate=g, chunk_states=cs)
+    torch.cuda.synchronize()
+    y_ref, _ = oracle.minmax_scan(f64(inp.t["r"]), f64(inp.t["s"]), x0=f64(inp.p["x0"]))
+    want = np.concatenate([f64(inp.p["x0"])[:, None, :], y_ref[:, 63:L - 1:64, :]], axis=1)
+    assert np.array_equal(host(cs), want)  # every MinMax state is one of the inputs
+    dy = torch.randn((B, L, D), device="cuda").to(torch.bfloat16)
+    g1 = ssd.minmax_scan_backward(r, s, dy, x0=x0, gate=g, chunk_states=cs)
+    g2 = ssd.minmax_scan_backward(r, s, dy, x0=x0, gate=g)
+    torch.cuda.synchronize()
+    for k in g2:
+        assert torch.equal(g1[k], g2[k]), k

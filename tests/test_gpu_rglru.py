@@ -72,7 +72,7 @@ def test_every_output_written_and_deterministic():
         hl = torch.full((2, 384), float("nan"), device="cuda")
         st = ssd.lib().ssd_rglru_scan(2, 333, 384, ssd.SSD_BF16, ssd.SSD_F32, x.data_ptr(), r.data_ptr(),
                                       i.data_ptr(), a_log.data_ptr(), 8.0, None, None, y.data_ptr(), hl.data_ptr(),
-                                      torch.cuda.current_stream().cuda_stream)
+                                      None, torch.cuda.current_stream().cuda_stream)
         assert st == 0
         torch.cuda.synchronize()
         assert not torch.isnan(y).any() and not torch.isnan(hl).any()
