@@ -667,8 +667,9 @@ __global__ __launch_bounds__(kBWaves * 64) void rglru_bwd_kernel(Bwd1Params p) {
   #pragma unroll
     for (int v = 0; v < V; ++v) kc[v] = p.c * p.a_log[chl + v] * kLog2e;
 
-    // ---- forward pairs, reverse pairs, and both wave aggregates
-    float av[kBSteps][V], bv[kBSteps][V], ev[kBSteps][V];
+    // ---- forward pairs (keeping the gates r, i and beta for the gradients), reverse pairs, and
+    //      both wave aggregates
+    float av[kBSteps][V], bv[kBSteps][V], ev[kBSteps][V], rv[kBSteps][V], iv[kBSteps][V], btv[kBSteps][V];
     float fA[V], fB[V], rA[V], rB[V];
   #pragma unroll
     for (int v = 0; v < V; ++v) { fA[v] = 1.0f; fB[v] = 0.0f; rA[v] = 1.0f; rB[v] = 0.0f; }
@@ -677,9 +678,16 @@ __global__ __launch_bounds__(kBWaves * 64) void rglru_bwd_kernel(Bwd1Params p) {
       const bool ok = ch_ok && (t0 + s < p.L);
   #pragma unroll
       for (int v = 0; v < V; ++v) {
-        const float in3[3] = {LD::get(rx[s], v), LD::get(rrl[s], v), LD::get(ril[s], v)};
-        float a, bb;
-        AffineOp::step(in3, AffineOp::Chan{kc[v]}, a, bb);
+        // AffineOp::step, with its intermediates kept
+        const float r = sigmoid_f(LD::get(rrl[s], v));
+        const float i = sigmoid_f(LD::get(ril[s], v));
+        const float l2 = kc[v] * r;
+        const float a = hw_exp2(l2);
+        const float beta = hw_sqrt(one_minus_a2(l2, a));
+        const float bb = beta * (i * LD::get(rx[s], v));
+        rv[s][v] = r;
+        iv[s][v] = i;
+        btv[s][v] = beta;
         const float G = GATE ? gelu_f(LD::get(rg[GATE ? s : 0], v)) : 1.0f;
         av[s][v] = ok ? a : 1.0f;
         bv[s][v] = ok ? bb : 0.0f;
@@ -753,10 +761,8 @@ __global__ __launch_bounds__(kBWaves * 64) void rglru_bwd_kernel(Bwd1Params p) {
         const float g = ev[s][v] + q[v];
         q[v] = av[s][v] * g;
         const float xx = LD::get(rx[s], v);
-        const float r = sigmoid_f(LD::get(rrl[s], v));
-        const float i = sigmoid_f(LD::get(ril[s], v));
+        const float r = rv[s][v], i = iv[s][v], beta = btv[s][v];
         const float a = av[s][v];
-        const float beta = hw_sqrt(one_minus_a2(kc[v] * r, a));
         const float gb = g * beta;
         const float dl = g * a * (hp[s][v] - (i * xx) * a * hw_rcp(beta));
         o_dx[v] = gb * i;
