@@ -14,6 +14,11 @@ forward loop written from the recurrence:
   MinMax (minmaxrnc package, MinMaxNeuron / minmax_operator): x_t = max(min(r_t, x_{t-1}), s_t),
       y_t = x_t or x_t g_t; torch's min / max split the gradient equally between equal operands.
 
+  Selective scan (cortexnet 3.2.1, cortexnet/ssm.py, MultiScaleSSM.forward / _selective_scan):
+      delta = softplus(dt + dt_bias) (or dt + dt_bias), abar = exp(clamp(delta A, max=20)),
+      h_t = abar h_{t-1} + (delta B_t) x_t,  y_t = (sum_n C_t,n h_t,n + Dskip x_t) silu(z_t);
+      the clamp passes the gradient where delta A <= 20 (torch.clamp).
+
 The loss whose gradient is returned is  sum(dy * y) + sum(dh_last * h_last) (x_last for MinMax).
 """
 from __future__ import annotations
@@ -82,3 +87,43 @@ def minmax_scan_grads(r, s, dy, x0=None, gate=None, dx_last=None):
     if gt is not None:
         out["dgate"] = z(grads[3], gt)
     return out
+
+
+def selective_scan_grads(x, dt, A, Bm, Cm, dy, Dskip=None, z=None, dt_bias=None, dt_softplus=True, h0=None,
+                         dh_last=None):
+    """Gradients of the batched selective scan for the loss sum(dy * y) + sum(dh_last * h_last).
+    Shapes: x, dt, z, dy [B,L,D]; A [D,N]; Bm, Cm [B,L,N]; Dskip, dt_bias [D]; h0, dh_last [B,D,N].
+    Returns a dict of float64 arrays: dx, ddt [B,L,D], dA [D,N], dBm, dCm [B,L,N], dh0 [B,D,N], and
+    dDskip, dz, ddt_bias for the optional inputs that are given."""
+    import torch
+    F = torch.nn.functional
+    xs, dts, As, Bs, Cs = _t(x), _t(dt), _t(A), _t(Bm), _t(Cm)
+    Ds, zs, dbs = _t(Dskip), _t(z), _t(dt_bias)
+    B, L, D = xs.shape
+    N = As.shape[1]
+    h = _t(h0) if h0 is not None else torch.zeros((B, D, N), dtype=torch.float64, requires_grad=True)
+    h_init = h
+    v = dts + dbs if dbs is not None else dts
+    delta = F.softplus(v) if dt_softplus else v
+    ys = []
+    for t in range(L):
+        abar = torch.exp((delta[:, t, :, None] * As[None]).clamp(max=20))
+        h = abar * h + (delta[:, t, :, None] * Bs[:, t, None, :]) * xs[:, t, :, None]
+        y_t = (h * Cs[:, t, None, :]).sum(-1)
+        if Ds is not None:
+            y_t = y_t + xs[:, t] * Ds
+        if zs is not None:
+            y_t = y_t * F.silu(zs[:, t])
+        ys.append(y_t)
+    y = torch.stack(ys, dim=1) if L > 0 else torch.zeros((B, 0, D), dtype=torch.float64)
+    loss = (y * torch.as_tensor(np.asarray(dy, dtype=np.float64))).sum()
+    if dh_last is not None:
+        loss = loss + (h * torch.as_tensor(np.asarray(dh_last, dtype=np.float64))).sum()
+    names = ["dx", "ddt", "dA", "dBm", "dCm", "dh0"]
+    inputs = [xs, dts, As, Bs, Cs, h_init]
+    for nm, tsr in (("dDskip", Ds), ("dz", zs), ("ddt_bias", dbs)):
+        if tsr is not None:
+            names.append(nm)
+            inputs.append(tsr)
+    grads = torch.autograd.grad(loss, inputs, allow_unused=True)
+    return {nm: (np.zeros(tsr.shape) if g is None else g.detach().numpy()) for nm, g, tsr in zip(names, grads, inputs)}

@@ -99,3 +99,79 @@ def test_minmax_grads_route_and_split_at_ties():
     assert G["dr"][0, 0, 0] == 0.5 and G["dx0"][0, 0] == 0.5
     G = og.minmax_scan_grads(one([1.0]), one([1.0]), one([1.0]), x0=np.array([[1.0]]))
     assert G["ds"][0, 0, 0] == 0.5 and G["dr"][0, 0, 0] == 0.25 and G["dx0"][0, 0] == 0.25
+
+
+def _selective_case(seed, softplus=True, clamp=False):
+    rng = np.random.default_rng(seed)
+    B, L, D, N = 2, 6, 3, 4
+    x, z, dy = (rng.standard_normal((B, L, D)) for _ in range(3))
+    dt = rng.standard_normal((B, L, D)) * 0.5 - (1.0 if softplus else -0.6)
+    A = -rng.uniform(0.5, 3.0, size=(D, N))
+    Bm, Cm = (rng.standard_normal((B, L, N)) * 0.5 for _ in range(2))
+    Dskip, dt_bias = rng.standard_normal(D), rng.standard_normal(D) * 0.3
+    if clamp:  # channel 0: positive A, small steps except one large step at t = 2, where the clamp at 20
+        A[0, :] = [30.0, 45.0, 0.3, 60.0]  # acts on states 0, 1, 3 (away from its edge) and the state
+        dt[:, :, 0] = 0.05 - dt_bias[0]    # grows by e^20 once
+        dt[:, 2, 0] = 1.0 - dt_bias[0]
+    h0, dhl = rng.standard_normal((B, D, N)), rng.standard_normal((B, D, N))
+    return dict(x=x, dt=dt, A=A, Bm=Bm, Cm=Cm, Dskip=Dskip, z=z, dt_bias=dt_bias, h0=h0), dy, dhl
+
+
+@pytest.mark.parametrize("softplus,clamp", [(True, False), (False, False)])
+def test_selective_grads_match_central_differences(softplus, clamp):
+    k, dy, dhl = _selective_case(31 + softplus + 2 * clamp, softplus, clamp)
+    G = og.selective_scan_grads(k["x"], k["dt"], k["A"], k["Bm"], k["Cm"], dy, Dskip=k["Dskip"], z=k["z"],
+                                dt_bias=k["dt_bias"], dt_softplus=softplus, h0=k["h0"], dh_last=dhl)
+
+    def F(**over):
+        a = dict(k, **over)
+        y, hl = oracle.selective_scan(a["x"], a["dt"], a["A"], a["Bm"], a["Cm"], Dskip=a["Dskip"], z=a["z"],
+                                      dt_bias=a["dt_bias"], dt_softplus=softplus, h0=a["h0"])
+        return _loss(y, hl, dy, dhl)
+
+    names = [("x", "dx"), ("dt", "ddt"), ("A", "dA"), ("Bm", "dBm"), ("Cm", "dCm"), ("h0", "dh0"),
+             ("Dskip", "dDskip"), ("z", "dz"), ("dt_bias", "ddt_bias")]
+    eps = 1e-6
+    for arg, gname in names:
+        base = k[arg]
+        num = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            p, m = base.copy(), base.copy()
+            p[idx] += eps
+            m[idx] -= eps
+            num[idx] = (F(**{arg: p}) - F(**{arg: m})) / (2 * eps)
+        err = np.max(np.abs(num - G[gname])) / max(np.max(np.abs(num)), 1e-12)
+        assert err < 2e-6, (gname, err)
+
+
+def test_selective_state_gradient_closed_form():
+    """One state, no input: h_L = prod_t abar_t h0, so dL/dh0 = prod_t exp(delta_t A) for L = sum h_L."""
+    B, L, D, N = 1, 5, 1, 1
+    dt = np.array([0.1, 0.2, 0.05, 0.3, 0.15]).reshape(B, L, D)
+    A = np.array([[-1.5]])
+    zero = np.zeros((B, L, D))
+    G = og.selective_scan_grads(zero, dt, A, np.zeros((B, L, N)), np.zeros((B, L, N)), zero, dt_softplus=False,
+                                h0=np.ones((B, D, N)), dh_last=np.ones((B, D, N)))
+    assert np.isclose(G["dh0"][0, 0, 0], np.exp(-1.5 * dt.sum()), rtol=1e-14, atol=0)
+    # and dL/dA = sum(dt) * that (the state is h0 times the product)
+    assert np.isclose(G["dA"][0, 0], dt.sum() * np.exp(-1.5 * dt.sum()), rtol=1e-13, atol=0)
+
+
+def test_selective_clamp_passes_no_gradient_closed_form():
+    """Two steps, one state, A > 0: the first exponent 0.1 A is below the clamp, the second 0.9 A = 27
+    is clamped to 20.  With y_t = C_t h_t and L = w1 y1 + w2 y2 + dhl h2 (written out by hand):
+    G2 = w2 C1 + dhl, G1 = w1 C0 + e^20 G2; dA = G1 d0 e^(d0 a) c (step 2 contributes nothing);
+    d delta1 = G2 B1 x1 (no term through the clamped exponent); d delta0 = G1 (a e^(d0 a) c + B0 x0)."""
+    a, c, d0, d1 = 30.0, 0.7, 0.1, 0.9
+    x0, x1, B0, B1, C0, C1, w1, w2, dhl = 0.3, -1.1, 0.8, 0.5, -0.4, 1.3, 0.6, -0.2, 0.9
+    G = og.selective_scan_grads(np.array([x0, x1]).reshape(1, 2, 1), np.array([d0, d1]).reshape(1, 2, 1),
+                                np.array([[a]]), np.array([B0, B1]).reshape(1, 2, 1),
+                                np.array([C0, C1]).reshape(1, 2, 1), np.array([w1, w2]).reshape(1, 2, 1),
+                                dt_softplus=False, h0=np.array([[[c]]]), dh_last=np.array([[[dhl]]]))
+    e0 = math.exp(d0 * a)
+    G2 = w2 * C1 + dhl
+    G1 = w1 * C0 + math.exp(20.0) * G2
+    assert np.isclose(G["dA"][0, 0], G1 * d0 * e0 * c, rtol=1e-12, atol=0)
+    assert np.isclose(G["ddt"][0, 1, 0], G2 * B1 * x1, rtol=1e-12, atol=0)
+    assert np.isclose(G["ddt"][0, 0, 0], G1 * (a * e0 * c + B0 * x0), rtol=1e-12, atol=0)
+    assert np.isclose(G["dh0"][0, 0, 0], G1 * e0, rtol=1e-12, atol=0)
