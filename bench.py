@@ -75,6 +75,12 @@ def minmax_bwd_bytes(B, L, D, in_b=2, out_b=4):
     return B * L * D * (3 * in_b + 2 * out_b)
 
 
+def selective_bwd_bytes(B, L, D, N, in_b=2, out_b=4):
+    # x, dt, z, dy read, dx, ddt, dz written; Bm, Cm read, dBm, dCm written; A, Dskip, dt_bias and
+    # their gradients
+    return B * L * D * (4 * in_b + 3 * out_b) + B * L * N * (2 * in_b + 2 * out_b) + D * N * 8 + D * 16
+
+
 def conv_bytes(B, L, D, W, in_b=2, out_b=4):
     return B * L * D * (in_b + out_b) + D * (W + 1) * 4
 
@@ -222,7 +228,12 @@ def forms(args, device):
     Dskip = torch.ones(D, device=device)
     ms = time_calls(lambda kk: ssd.selective_scan(x, dt, A, Bm, Cm, Dskip=Dskip, z=z), 1, 30, 3)[0]
     record("selective_unstructured_A_B4_L2048_D1536_N16", ms, B * L * D * N, selective_bytes(B, L, D, N))
-    del x, z, dt, Bm, Cm
+
+    # --- gradients of the selective scan on the headline shape (dy ~ N(0, 1), h0 and dh_last zero)
+    dy = randn((B, L, D))
+    ms = time_calls(lambda kk: ssd.selective_scan_backward(x, dt, A, Bm, Cm, dy, Dskip=Dskip, z=z), 1, 10, 2)[0]
+    record("selective_backward_bf16_B4_L2048_D1536_N16", ms, B * L * D * N, selective_bwd_bytes(B, L, D, N))
+    del x, z, dt, Bm, Cm, dy
 
     # --- RG-LRU fp32, B=2 L=128 D=64 (latency bound)
     B, L, D = 2, 128, 64

@@ -32,7 +32,8 @@ SCAN_CHUNK = 64  # SSD_SCAN_CHUNK of ssd.h
 EXPORTS = ("ssd_status_str", "ssd_last_error", "ssd_version", "ssd_rglru_scan", "ssd_rglru_scan_backward",
            "ssd_rglru_update",
            "ssd_selective_scan", "ssd_selective_update", "ssd_hgrn2_scan", "ssd_hgrn2_update", "ssd_minmax_scan",
-           "ssd_minmax_update", "ssd_minmax_scan_backward", "ssd_causal_conv1d", "ssd_causal_conv1d_update")
+           "ssd_minmax_update", "ssd_minmax_scan_backward", "ssd_causal_conv1d", "ssd_causal_conv1d_update",
+           "ssd_selective_scan_backward")
 
 
 class SSDError(RuntimeError):
@@ -81,6 +82,9 @@ def lib() -> ctypes.CDLL:
                                                _vp]
         L.ssd_selective_scan.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _fp, _vp, _vp,
                                          _fp, _vp, _fp, ctypes.c_int, _vp, _i64, _fp, _vp, _fp, _vp]
+        L.ssd_selective_scan_backward.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _fp,
+                                                  _vp, _vp, _fp, _vp, _fp, ctypes.c_int, _fp, _vp, _fp, _vp, _vp,
+                                                  _fp, _vp, _vp, _fp, _vp, _fp, _fp, _vp]
         L.ssd_selective_update.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _fp, _vp, _vp, _fp,
                                            _vp, _fp, ctypes.c_int, _fp, _vp, _vp]
         L.ssd_hgrn2_scan.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp,
@@ -388,6 +392,41 @@ def selective_update(x, dt, A, Bm, Cm, state, Dskip=None, z=None, dt_bias=None, 
     return y
 
 
+def selective_scan_backward(x, dt, A, Bm, Cm, dy, Dskip=None, z=None, dt_bias=None, dt_softplus: bool = True, h0=None,
+                            dh_last=None, out_dtype=None):
+    """Gradients of the batched ``selective_scan`` for the loss sum(dy * y) + sum(dh_last * h_last)
+    (see ``ssd_selective_scan_backward``).  Returns a dict: dx, ddt [B, L, D], dBm, dCm [B, L, N] (out
+    dtype), dA [D, N], dh0 [B, D, N] (fp32), and dDskip, ddt_bias [D] (fp32), dz [B, L, D] for the
+    optional inputs that are given."""
+    torch = _torch()
+    B, L, D = x.shape
+    N = int(A.shape[1])
+    code = _act([x, dt, Bm, Cm, z, dy], ["x", "dt", "Bm", "Cm", "z", "dy"])
+    oc = _out_code(out_dtype)
+    odt = torch.bfloat16 if oc == SSD_BF16 else torch.float32
+    dev = x.device
+    g = {"dx": torch.empty((B, L, D), device=dev, dtype=odt), "ddt": torch.empty((B, L, D), device=dev, dtype=odt),
+         "dA": torch.empty((D, N), device=dev, dtype=torch.float32),
+         "dBm": torch.empty((B, L, N), device=dev, dtype=odt), "dCm": torch.empty((B, L, N), device=dev, dtype=odt),
+         "dh0": torch.empty((B, D, N), device=dev, dtype=torch.float32)}
+    if Dskip is not None:
+        g["dDskip"] = torch.empty((D,), device=dev, dtype=torch.float32)
+    if z is not None:
+        g["dz"] = torch.empty((B, L, D), device=dev, dtype=odt)
+    if dt_bias is not None:
+        g["ddt_bias"] = torch.empty((D,), device=dev, dtype=torch.float32)
+    st = lib().ssd_selective_scan_backward(
+        B, L, D, N, code, oc, _dev(x, "x"), _dev(dt, "dt", x.shape), _dev(A, "A", (D, N), torch.float32),
+        _dev(Bm, "Bm", (B, L, N)), _dev(Cm, "Cm", (B, L, N)), _dev(Dskip, "Dskip", (D,), torch.float32),
+        _dev(z, "z", x.shape), _dev(dt_bias, "dt_bias", (D,), torch.float32), int(bool(dt_softplus)),
+        _dev(h0, "h0", (B, D, N), torch.float32), _dev(dy, "dy", x.shape),
+        _dev(dh_last, "dh_last", (B, D, N), torch.float32), _dev(g["dx"], "dx"), _dev(g["ddt"], "ddt"),
+        _dev(g["dA"], "dA"), _dev(g["dBm"], "dBm"), _dev(g["dCm"], "dCm"), _dev(g.get("dDskip"), "dDskip"),
+        _dev(g.get("dz"), "dz"), _dev(g.get("ddt_bias"), "ddt_bias"), _dev(g["dh0"], "dh0"), _stream(dev))
+    _raise(st, "selective_scan_backward")
+    return g
+
+
 # ----------------------------------------------------------------------------- HGRN2
 def hgrn2_scan(q, k, v, g_logit, lower_bound: float, S0=None, return_last_state: bool = False, out_dtype=None):
     """HGRN2 matrix-state scan over [B, L, H, d] (see ``ssd_hgrn2_scan``).  Returns o, or (o, S_last)."""
@@ -419,6 +458,6 @@ def hgrn2_update(q, k, v, g_logit, lower_bound: float, S, out_dtype=None):
     return o
 
 
-__all__ = ["chunk_states_shape", "SCAN_CHUNK", "rglru_scan", "rglru_scan_backward", "rglru_update", "selective_scan", "selective_update", "hgrn2_scan", "hgrn2_update",
+__all__ = ["chunk_states_shape", "SCAN_CHUNK", "rglru_scan", "rglru_scan_backward", "rglru_update", "selective_scan", "selective_scan_backward", "selective_update", "hgrn2_scan", "hgrn2_update",
            "minmax_scan", "minmax_update", "minmax_scan_backward", "causal_conv1d", "causal_conv1d_update", "lib", "LIB_PATH", "EXPORTS",
            "SSDError", "SSDValueError", "SSD_F32", "SSD_BF16"]

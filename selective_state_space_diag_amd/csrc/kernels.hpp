@@ -146,6 +146,32 @@ int64_t selective_segment_len(const SelectiveScanArgs& a);
 size_t selective_scan_scratch_bytes(const SelectiveScanArgs& a);
 hipError_t launch_selective_scan(const SelectiveScanArgs& a, hipStream_t s);
 
+// Gradients of the batched selective scan (no cu_seqlens).
+struct SelectiveBwdArgs {
+  int64_t B, L, D, N;
+  int in_bf16, out_bf16;
+  const void *x, *dt;
+  const float* A;
+  const void *Bm, *Cm;
+  const float* Dskip;   // or NULL
+  const void* z;        // or NULL
+  const float* dt_bias; // or NULL
+  int dt_softplus;
+  const float* h0;      // [B][D][N] or NULL
+  const void* dy;       // in dtype
+  const float* dh_last; // [B][D][N] or NULL
+  void *dx, *ddt;       // out dtype
+  float* dA;            // [D][N]
+  void *dBm, *dCm;      // out dtype [B][L][N]
+  float* dDskip;        // [D] or NULL
+  void* dz;             // out dtype, when z is given
+  float* ddt_bias;      // [D] or NULL
+  float* dh0;           // [B][D][N] or NULL
+  void* scratch;        // selective_scan_backward_scratch_bytes
+};
+size_t selective_scan_backward_scratch_bytes(const SelectiveBwdArgs& a);
+hipError_t launch_selective_scan_backward(const SelectiveBwdArgs& a, hipStream_t s);
+
 struct SelectiveUpdateArgs {
   int64_t B, D, N;
   int in_bf16, out_bf16;

@@ -565,6 +565,323 @@ Plan make_plan(const SelectiveScanArgs& a) {
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
+// ============================================================================= backward
+// Gradients of the batched scan for the loss sum dy y + sum dh_last h_last.  With s_t the readout
+// before the gate, ds_t = dy_t silu(z_t) (or dy_t) and the reverse state q (q_L = dh_last,
+// g_t = ds_t C_t + q_{t+1}, q_t = abar_t g_t):
+//   dh0 = q_0,  dz_t = dy_t s_t silu'(z_t),  dDskip = sum ds x,  dx_t = ds_t Dskip + delta_t sum_n g B,
+//   dC_tn = sum_d ds_t h_tn,  dB_tn = sum_d g_tn delta_t x_t,  and with m = [delta A <= 20] (the clamp
+//   passes no gradient above 20): d delta_t = x_t sum_n g B + sum_n m g h_{t-1} abar A_n,
+//   dA_n = sum m g h_{t-1} abar delta,  d dt = d delta softplus'(dt + bias),  d dt_bias = sum d dt.
+// Passes over segments of kBT rows, one lane per channel as in the forward:
+//   1. the forward's aggregate and carry passes (segment length kBT): the state entering each segment;
+//   2. reverse aggregates of segments >= 1: q at the segment's start from q = 0 at its end, prod abar;
+//   3. reverse carry: q at each segment's end;
+//   4. per segment: for one state at a time, forward through the rows keeping h_{t-1} and abar, then
+//      back, accumulating the row gradients; dB and dC are summed over the workgroup's channels by a
+//      lane butterfly and across its waves in LDS; dA, dDskip and d dt_bias leave per-segment sums;
+//   5. fixed-order sums of the partial results.
+constexpr int kBT = 16;  // rows per backward segment
+
+struct SelBwdParams {
+  int64_t L, D, nseg, nblk, BL;
+  const void* x;
+  const void* dt;
+  const float* A;
+  const void* Bm;
+  const void* Cm;
+  const float* Dskip;
+  const void* z;
+  const float* dt_bias;
+  const float* h0;
+  const void* dy;
+  const float* dh_last;
+  const float* carry;  // [unit][N][D] state entering segments >= 1 (pass 1)
+  float* aggP;         // [unit][N][D] prod abar of the segment (pass 2)
+  float* aggQ;         // [unit][N][D] q at the segment's start from 0 at its end (pass 2)
+  float* qend;         // [unit][N][D] q at the segment's end (pass 3)
+  void* dx;
+  void* ddt;
+  void* dz;
+  float* dBm_part;     // [nblk][B L][N] per channel block
+  float* dCm_part;
+  float* dA_part;      // [unit][N][D]
+  float* dD_part;      // [unit][D]
+  float* dbias_part;   // [unit][D]
+  float* dh0;          // [B][D][N] or NULL
+};
+
+// softplus'(v) as torch takes it: sigmoid(v), and 1 above the threshold 20.
+__device__ __forceinline__ float softplus_grad_f(float v) { return v > 20.0f ? 1.0f : sigmoid_f(v); }
+// silu'(z) = sigmoid(z) (1 + z (1 - sigmoid(z)))
+__device__ __forceinline__ float silu_grad_f(float z) {
+  const float sg = sigmoid_f(z);
+  return sg * fmaf(z, 1.0f - sg, 1.0f);
+}
+
+// Sum of v[j] over the 64 lanes of the wave, for 16 values j at once: each exchange step halves the
+// values a lane keeps (the half picked by one lane bit) and adds its partner's other half.  On return
+// lanes with (lane & 3) == 0 hold the total of value (lane >> 2) & 15 in v[0].
+__device__ __forceinline__ void wave_sum16(float (&v)[16], int lane) {
+#pragma unroll
+  for (int half = 8, bit = 32; half >= 1; half >>= 1, bit >>= 1) {
+    const bool hi = (lane & bit) != 0;
+#pragma unroll
+    for (int i = 0; i < half; ++i) {
+      const float send = hi ? v[i] : v[i + half];
+      const float keep = hi ? v[i + half] : v[i];
+      v[i] = keep + __shfl_xor(send, bit);
+    }
+  }
+  v[0] += __shfl_xor(v[0], 2);
+  v[0] += __shfl_xor(v[0], 1);
+}
+
+// Pass 2: reverse aggregates of segments >= 1 (a sequence's first segment needs none).
+template <typename Tin, int NS, bool SOFTPLUS, bool GATE>
+__global__ __launch_bounds__(kThreads) void selective_bwd_agg_kernel(SelBwdParams p) {
+  const int64_t u = blockIdx.x;
+  const int64_t seq = u / p.nseg, seg = u - seq * p.nseg;
+  if (seg == 0) return;
+  const int64_t row0 = seq * p.L + seg * kBT;
+  const int R = (int)min<int64_t>(kBT, (seq + 1) * p.L - row0);
+  const int64_t d = (int64_t)blockIdx.y * kThreads + threadIdx.x;
+  const bool active = d < p.D;
+  const int64_t dl = active ? d : p.D - 1;
+  __shared__ float sC[kBT * NS];
+  for (int e = threadIdx.x; e < kBT * NS; e += kThreads) {
+    const int t = e / NS;
+    sC[e] = t < R ? io<Tin>::load(p.Cm, (row0 + t) * NS + (e - t * NS)) : 0.0f;
+  }
+  float A2[NS];
+#pragma unroll
+  for (int n = 0; n < NS; ++n) A2[n] = p.A[dl * NS + n] * kLog2e;
+  const float bias = p.dt_bias ? p.dt_bias[dl] : 0.0f;
+  float delta[kBT], ds[kBT];
+#pragma unroll
+  for (int t = 0; t < kBT; ++t) {
+    const int64_t r = row0 + min(t, R - 1);
+    const float v = io<Tin>::load(p.dt, r * p.D + dl) + bias;
+    const float dyv = io<Tin>::load(p.dy, r * p.D + dl);
+    const float g = GATE ? silu_f(io<Tin>::load(p.z, r * p.D + dl)) : 1.0f;
+    delta[t] = t < R ? (SOFTPLUS ? softplus_f(v) : v) : 0.0f;  // rows past the sequence: identity
+    ds[t] = t < R ? dyv * g : 0.0f;
+  }
+  __syncthreads();
+  if (!active) return;
+#pragma unroll 1
+  for (int n = 0; n < NS; ++n) {
+    float q = 0.0f, e_sum = 0.0f;
+#pragma unroll
+    for (int t = kBT - 1; t >= 0; --t) {
+      float e = delta[t] * A2[n];
+      e = e > kClampLog2 ? kClampLog2 : e;
+      e_sum += e;
+      q = hw_exp2(e) * fmaf(ds[t], sC[t * NS + n], q);
+    }
+    p.aggQ[(u * NS + n) * p.D + d] = q;
+    p.aggP[(u * NS + n) * p.D + d] = hw_exp2(e_sum);
+  }
+}
+
+// Pass 3: one thread per (sequence, state, channel), segments from the last to the first.
+template <int NS>
+__global__ __launch_bounds__(kThreads) void selective_bwd_carry_kernel(SelBwdParams p, int64_t nseq) {
+  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t per_seq = NS * p.D;
+  const int64_t seq = gid / per_seq;
+  if (seq >= nseq) return;
+  const int64_t e = gid - seq * per_seq;  // n * D + d
+  const int64_t n = e / p.D, d = e - n * p.D;
+  float q = p.dh_last ? p.dh_last[(seq * p.D + d) * NS + n] : 0.0f;
+  for (int64_t s = p.nseg - 1; s >= 0; --s) {
+    const int64_t idx = ((seq * p.nseg + s) * NS + n) * p.D + d;
+    p.qend[idx] = q;
+    if (s > 0) q = fmaf(p.aggP[idx], q, p.aggQ[idx]);
+  }
+}
+
+// Pass 4.
+template <typename Tin, typename Tout, int NS, bool SOFTPLUS, bool GATE>
+__global__ __launch_bounds__(kThreads) void selective_bwd_kernel(SelBwdParams p) {
+  static_assert(kBT == 16, "the dB / dC butterfly sums 16 rows");
+  const int64_t u = blockIdx.x;
+  const int64_t seq = u / p.nseg, seg = u - seq * p.nseg;
+  const int64_t row0 = seq * p.L + seg * kBT;
+  const int R = (int)min<int64_t>(kBT, (seq + 1) * p.L - row0);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t d = (int64_t)blockIdx.y * kThreads + threadIdx.x;
+  const bool active = d < p.D;
+  const int64_t dl = active ? d : p.D - 1;  // lanes past D recompute channel D-1 and store nothing
+  __shared__ float sB[kBT * NS], sC[kBT * NS];
+  __shared__ float sRedB[NS][kThreads / 64][kBT], sRedC[NS][kThreads / 64][kBT];
+  for (int e = threadIdx.x; e < kBT * NS; e += kThreads) {
+    const int t = e / NS;
+    const int64_t idx = (row0 + min(t, R - 1)) * NS + (e - t * NS);
+    sB[e] = io<Tin>::load(p.Bm, idx);
+    sC[e] = io<Tin>::load(p.Cm, idx);
+  }
+  const float bias = p.dt_bias ? p.dt_bias[dl] : 0.0f;
+  const float dskip = p.Dskip ? p.Dskip[dl] : 0.0f;
+  // per row: delta, x, ds = dy silu(z); rows past the sequence are exact identities (delta = x = ds = 0).
+  // (dt, dy and z are read again for the row gradients at the end, from L2.)
+  float delta[kBT], xv[kBT], ds[kBT];
+#pragma unroll
+  for (int t = 0; t < kBT; ++t) {
+    const int64_t r = row0 + min(t, R - 1);
+    const bool ok = t < R;
+    const float v = io<Tin>::load(p.dt, r * p.D + dl) + bias;
+    const float xx = io<Tin>::load(p.x, r * p.D + dl);
+    const float dyv = io<Tin>::load(p.dy, r * p.D + dl);
+    const float g = GATE ? silu_f(io<Tin>::load(p.z, r * p.D + dl)) : 1.0f;
+    delta[t] = ok ? (SOFTPLUS ? softplus_f(v) : v) : 0.0f;
+    xv[t] = ok ? xx : 0.0f;
+    ds[t] = ok ? dyv * g : 0.0f;
+  }
+  float sacc[kBT], GB[kBT], MA[kBT];
+#pragma unroll
+  for (int t = 0; t < kBT; ++t) { sacc[t] = 0.0f; GB[t] = 0.0f; MA[t] = 0.0f; }
+  __syncthreads();
+
+#pragma unroll 1
+  for (int n = 0; n < NS; ++n) {
+    const float An = p.A[dl * NS + n];
+    const float A2 = An * kLog2e;
+    float h = seg == 0 ? (p.h0 ? p.h0[(seq * p.D + dl) * NS + n] : 0.0f) : p.carry[(u * NS + n) * p.D + dl];
+    float q = p.qend[(u * NS + n) * p.D + dl];
+    // forward through the rows
+    float ab[kBT], hp[kBT], v[16];
+    uint32_t live = 0;  // bit t: the clamp does not act at row t
+#pragma unroll
+    for (int t = 0; t < kBT; ++t) {
+      float e = delta[t] * A2;
+      live |= (e <= kClampLog2 ? 1u : 0u) << t;
+      e = e > kClampLog2 ? kClampLog2 : e;
+      ab[t] = hw_exp2(e);
+      hp[t] = h;
+      h = fmaf(ab[t], h, (delta[t] * xv[t]) * sB[t * NS + n]);
+      sacc[t] = fmaf(sC[t * NS + n], h, sacc[t]);
+      v[t] = active ? ds[t] * h : 0.0f;  // this lane's share of dC_tn (idle lanes add nothing)
+    }
+    wave_sum16(v, lane);
+    if ((lane & 3) == 0) sRedC[n][wave][(lane >> 2) & 15] = v[0];
+    // back through the rows
+    float dA = 0.0f;
+#pragma unroll
+    for (int t = kBT - 1; t >= 0; --t) {
+      const float g = fmaf(ds[t], sC[t * NS + n], q);
+      q = ab[t] * g;
+      const float mab = (live >> t) & 1u ? (g * hp[t]) * ab[t] : 0.0f;  // d abar times abar, unclamped rows
+      MA[t] = fmaf(mab, An, MA[t]);
+      dA = fmaf(mab, delta[t], dA);
+      GB[t] = fmaf(g, sB[t * NS + n], GB[t]);
+      v[t] = active ? g * (delta[t] * xv[t]) : 0.0f;  // this lane's share of dB_tn
+    }
+    wave_sum16(v, lane);
+    if ((lane & 3) == 0) sRedB[n][wave][(lane >> 2) & 15] = v[0];
+    if (active) {
+      p.dA_part[(u * NS + n) * p.D + d] = dA;
+      if (seg == 0 && p.dh0) p.dh0[(seq * p.D + d) * NS + n] = q;
+    }
+  }
+
+  // row gradients
+  const int64_t rowb = row0 * p.D;
+  float dsum = 0.0f, bsum = 0.0f;
+#pragma unroll
+  for (int t = 0; t < kBT; ++t) {
+    const int64_t r = row0 + min(t, R - 1);
+    const float ddelta = fmaf(xv[t], GB[t], MA[t]);
+    const float gdt = SOFTPLUS ? ddelta * softplus_grad_f(io<Tin>::load(p.dt, r * p.D + dl) + bias) : ddelta;
+    const float gx = fmaf(ds[t], dskip, delta[t] * GB[t]);
+    float gz = 0.0f;
+    if (GATE) gz = io<Tin>::load(p.dy, r * p.D + dl) * silu_grad_f(io<Tin>::load(p.z, r * p.D + dl)) *
+                   fmaf(dskip, xv[t], sacc[t]);
+    dsum = fmaf(ds[t], xv[t], dsum);
+    if (t < R) bsum += gdt;
+    if (active && t < R) {
+      io<Tout>::store(p.dx, rowb + t * p.D + d, gx);
+      io<Tout>::store(p.ddt, rowb + t * p.D + d, gdt);
+      if (GATE) io<Tout>::store(p.dz, rowb + t * p.D + d, gz);
+    }
+  }
+  if (active) {
+    p.dD_part[u * p.D + d] = dsum;
+    p.dbias_part[u * p.D + d] = bsum;
+  }
+  // dB / dC of this channel block: the waves' sums, in wave order
+  __syncthreads();
+  for (int e = threadIdx.x; e < NS * kBT; e += kThreads) {
+    const int n = e / kBT, t = e - n * kBT;
+    float sb = 0.0f, sc = 0.0f;
+#pragma unroll
+    for (int wv = 0; wv < kThreads / 64; ++wv) {
+      sb += sRedB[n][wv][t];
+      sc += sRedC[n][wv][t];
+    }
+    if (t < R) {
+      p.dBm_part[((int64_t)blockIdx.y * p.BL + row0 + t) * NS + n] = sb;
+      p.dCm_part[((int64_t)blockIdx.y * p.BL + row0 + t) * NS + n] = sc;
+    }
+  }
+}
+
+// Pass 5: fixed-order sums.  dBm, dCm: over channel blocks; dA [D][N], dDskip, d dt_bias: over units.
+template <typename Tout>
+__global__ __launch_bounds__(kThreads) void selective_bwd_bc_kernel(const float* PB, const float* PC, int64_t nblk,
+                                                                    int64_t total, void* dBm, void* dCm) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= total) return;
+  float sb = 0.0f, sc = 0.0f;
+  for (int64_t k = 0; k < nblk; ++k) {
+    sb += PB[k * total + i];
+    sc += PC[k * total + i];
+  }
+  io<Tout>::store(dBm, i, sb);
+  io<Tout>::store(dCm, i, sc);
+}
+
+__global__ __launch_bounds__(kThreads) void selective_bwd_sum_kernel(const float* part, int64_t units, int64_t width,
+                                                                     int64_t N, float* out) {
+  // column c = n * D + d of [units][N][D] (or d of [units][D] with N = 1) -> out[d * N + n]
+  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (c >= width) return;
+  float acc = 0.0f;
+  for (int64_t k = 0; k < units; ++k) acc += part[k * width + c];
+  const int64_t D = width / N, n = c / D, d = c - n * D;
+  out[d * N + n] = acc;
+}
+
+template <typename Tin, typename Tout, int NS, bool SOFTPLUS>
+void launch_bwd_n(const SelBwdParams& q, int64_t U, int64_t nseq, bool gate, hipStream_t s) {
+  const dim3 grid((unsigned)U, (unsigned)q.nblk), blk(kThreads);
+  if (gate) hipLaunchKernelGGL((selective_bwd_agg_kernel<Tin, NS, SOFTPLUS, true>), grid, blk, 0, s, q);
+  else hipLaunchKernelGGL((selective_bwd_agg_kernel<Tin, NS, SOFTPLUS, false>), grid, blk, 0, s, q);
+  const int64_t nthreads = nseq * NS * q.D;
+  hipLaunchKernelGGL((selective_bwd_carry_kernel<NS>), dim3((unsigned)((nthreads + kThreads - 1) / kThreads)), blk, 0,
+                     s, q, nseq);
+  if (gate) hipLaunchKernelGGL((selective_bwd_kernel<Tin, Tout, NS, SOFTPLUS, true>), grid, blk, 0, s, q);
+  else hipLaunchKernelGGL((selective_bwd_kernel<Tin, Tout, NS, SOFTPLUS, false>), grid, blk, 0, s, q);
+}
+
+template <typename Tin, typename Tout, int NS>
+void launch_bwd_sp(const SelBwdParams& q, int64_t U, int64_t nseq, bool softplus, bool gate, hipStream_t s) {
+  if (softplus) launch_bwd_n<Tin, Tout, NS, true>(q, U, nseq, gate, s);
+  else launch_bwd_n<Tin, Tout, NS, false>(q, U, nseq, gate, s);
+}
+
+template <typename Tin, typename Tout>
+void launch_bwd_t(const SelBwdParams& q, int64_t N, int64_t U, int64_t nseq, bool softplus, bool gate, hipStream_t s) {
+  switch (N) {
+    case 1: launch_bwd_sp<Tin, Tout, 1>(q, U, nseq, softplus, gate, s); break;
+    case 2: launch_bwd_sp<Tin, Tout, 2>(q, U, nseq, softplus, gate, s); break;
+    case 4: launch_bwd_sp<Tin, Tout, 4>(q, U, nseq, softplus, gate, s); break;
+    case 8: launch_bwd_sp<Tin, Tout, 8>(q, U, nseq, softplus, gate, s); break;
+    default: launch_bwd_sp<Tin, Tout, 16>(q, U, nseq, softplus, gate, s); break;
+  }
+}
+
 }  // namespace
 
 int64_t selective_segment_len(const SelectiveScanArgs& a) { return make_plan(a).T; }
@@ -604,6 +921,101 @@ hipError_t launch_selective_scan(const SelectiveScanArgs& a, hipStream_t s) {
   if (!a.in_bf16) return launch_by_n<float, float>(p, pl.U, a.dt_softplus != 0, s);
   return a.out_bf16 ? launch_by_n<bf16_t, bf16_t>(p, pl.U, a.dt_softplus != 0, s)
                     : launch_by_n<bf16_t, float>(p, pl.U, a.dt_softplus != 0, s);
+}
+
+namespace {
+struct BwdLayout {
+  int64_t nseg, U, nblk;
+  size_t state, row, bc;  // bytes of one [U][N][D], one [U][D], one [nblk][B L][N] buffer
+};
+BwdLayout bwd_layout(const SelectiveBwdArgs& a) {
+  BwdLayout l;
+  l.nseg = (a.L + kBT - 1) / kBT;
+  l.U = a.B * l.nseg;
+  l.nblk = (a.D + kThreads - 1) / kThreads;
+  l.state = align256((size_t)(l.U * a.N * a.D) * sizeof(float));
+  l.row = align256((size_t)(l.U * a.D) * sizeof(float));
+  l.bc = align256((size_t)(l.nblk * a.B * a.L * a.N) * sizeof(float));
+  return l;
+}
+
+template <typename Tin, int NS>
+void launch_fwd_carry(const SelParams& f, int64_t U, bool softplus, hipStream_t s) {
+  const dim3 grid((unsigned)U, (unsigned)((f.D + kThreads - 1) / kThreads));
+  if (softplus) hipLaunchKernelGGL((selective_aggregate_kernel<Tin, NS, true>), grid, dim3(kThreads), 0, s, f);
+  else hipLaunchKernelGGL((selective_aggregate_kernel<Tin, NS, false>), grid, dim3(kThreads), 0, s, f);
+  const int64_t nthreads = f.nseq * NS * f.D;
+  hipLaunchKernelGGL((selective_carry_kernel<NS>), dim3((unsigned)((nthreads + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, f);
+}
+template <typename Tin>
+void launch_fwd_carry_t(const SelParams& f, int64_t U, bool softplus, hipStream_t s) {
+  switch (f.N) {
+    case 1: launch_fwd_carry<Tin, 1>(f, U, softplus, s); break;
+    case 2: launch_fwd_carry<Tin, 2>(f, U, softplus, s); break;
+    case 4: launch_fwd_carry<Tin, 4>(f, U, softplus, s); break;
+    case 8: launch_fwd_carry<Tin, 8>(f, U, softplus, s); break;
+    default: launch_fwd_carry<Tin, 16>(f, U, softplus, s); break;
+  }
+}
+}  // namespace
+
+size_t selective_scan_backward_scratch_bytes(const SelectiveBwdArgs& a) {
+  const BwdLayout l = bwd_layout(a);
+  return 5 * l.state + 2 * l.row + 2 * l.bc;
+}
+
+hipError_t launch_selective_scan_backward(const SelectiveBwdArgs& a, hipStream_t s) {
+  const BwdLayout l = bwd_layout(a);
+  char* base = static_cast<char*>(a.scratch);
+  float* carry = reinterpret_cast<float*>(base);
+  float* aggP = reinterpret_cast<float*>(base + l.state);
+  float* aggQ = reinterpret_cast<float*>(base + 2 * l.state);
+  float* qend = reinterpret_cast<float*>(base + 3 * l.state);
+  float* dA_part = reinterpret_cast<float*>(base + 4 * l.state);
+  float* dD_part = reinterpret_cast<float*>(base + 5 * l.state);
+  float* dbias_part = reinterpret_cast<float*>(base + 5 * l.state + l.row);
+  float* PB = reinterpret_cast<float*>(base + 5 * l.state + 2 * l.row);
+  float* PC = reinterpret_cast<float*>(base + 5 * l.state + 2 * l.row + l.bc);
+  // 1. the state entering every segment: the forward's aggregate and carry passes at segment kBT
+  if (l.nseg > 1) {
+    SelParams f{};
+    f.L = a.L; f.D = a.D; f.N = a.N; f.nseq = a.B; f.T = kBT; f.nseg = l.nseg;
+    f.cu = nullptr; f.units = nullptr; f.n_units = nullptr; f.seq_units = nullptr;
+    f.x = a.x; f.dt = a.dt; f.A = a.A; f.Bm = a.Bm; f.Cm = a.Cm; f.dt_bias = a.dt_bias; f.h0 = a.h0;
+    f.aggP = aggP; f.aggH = aggQ; f.carry = carry;
+    if (a.in_bf16) launch_fwd_carry_t<bf16_t>(f, l.U, a.dt_softplus != 0, s);
+    else launch_fwd_carry_t<float>(f, l.U, a.dt_softplus != 0, s);
+  }
+  // 2.-4.
+  SelBwdParams q{};
+  q.L = a.L; q.D = a.D; q.nseg = l.nseg; q.nblk = l.nblk; q.BL = a.B * a.L;
+  q.x = a.x; q.dt = a.dt; q.A = a.A; q.Bm = a.Bm; q.Cm = a.Cm; q.Dskip = a.Dskip; q.z = a.z; q.dt_bias = a.dt_bias;
+  q.h0 = a.h0; q.dy = a.dy; q.dh_last = a.dh_last;
+  q.carry = carry; q.aggP = aggP; q.aggQ = aggQ; q.qend = qend;
+  q.dx = a.dx; q.ddt = a.ddt; q.dz = a.dz; q.dBm_part = PB; q.dCm_part = PC;
+  q.dA_part = dA_part; q.dD_part = dD_part; q.dbias_part = dbias_part; q.dh0 = a.dh0;
+  const bool sp = a.dt_softplus != 0, gate = a.z != nullptr;
+  if (!a.in_bf16) launch_bwd_t<float, float>(q, a.N, l.U, a.B, sp, gate, s);
+  else if (a.out_bf16) launch_bwd_t<bf16_t, bf16_t>(q, a.N, l.U, a.B, sp, gate, s);
+  else launch_bwd_t<bf16_t, float>(q, a.N, l.U, a.B, sp, gate, s);
+  // 5. fixed-order sums
+  const int64_t nbc = a.B * a.L * a.N;
+  const dim3 blk(kThreads);
+  if (a.out_bf16)
+    hipLaunchKernelGGL((selective_bwd_bc_kernel<bf16_t>), dim3((unsigned)((nbc + kThreads - 1) / kThreads)), blk, 0, s,
+                       PB, PC, l.nblk, nbc, a.dBm, a.dCm);
+  else
+    hipLaunchKernelGGL((selective_bwd_bc_kernel<float>), dim3((unsigned)((nbc + kThreads - 1) / kThreads)), blk, 0, s,
+                       PB, PC, l.nblk, nbc, a.dBm, a.dCm);
+  const int64_t wA = a.N * a.D;
+  hipLaunchKernelGGL(selective_bwd_sum_kernel, dim3((unsigned)((wA + kThreads - 1) / kThreads)), blk, 0, s, dA_part,
+                     l.U, wA, a.N, a.dA);
+  const dim3 gD((unsigned)((a.D + kThreads - 1) / kThreads));
+  if (a.dDskip) hipLaunchKernelGGL(selective_bwd_sum_kernel, gD, blk, 0, s, dD_part, l.U, a.D, (int64_t)1, a.dDskip);
+  if (a.ddt_bias)
+    hipLaunchKernelGGL(selective_bwd_sum_kernel, gD, blk, 0, s, dbias_part, l.U, a.D, (int64_t)1, a.ddt_bias);
+  return hipGetLastError();
 }
 
 hipError_t launch_selective_update(const SelectiveUpdateArgs& a, hipStream_t s) {

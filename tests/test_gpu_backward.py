@@ -193,3 +193,106 @@ def test_minmax_chunk_states_exact_and_feed_backward():
     torch.cuda.synchronize()
     for k in g2:
         assert torch.equal(g1[k], g2[k]), k
+
+
+# ----------------------------------------------------------------------------- selective scan
+def run_sel_bwd(B, L, D, N, dtype, seed, softplus=True, with_z=True, with_skip=True, with_bias=True, with_h0=True,
+                with_dhl=True, A=None, edit=None, tol=None):
+    import torch
+    inp = synth.selective_inputs(B, L, D, N, dtype, seed, dt_softplus=softplus, with_z=with_z, with_skip=with_skip,
+                                 with_h0=with_h0)
+    rng = np.random.default_rng(seed + 7)
+    if A is not None:
+        inp.p["A"] = A.astype(np.float32)
+    if edit is not None:
+        edit(inp)
+    bias = (rng.standard_normal(D) * 0.1).astype(np.float32) if with_bias else None
+    dy32 = rng.standard_normal((B, L, D)).astype(np.float32)
+    dy = synth.Tensor(dtype, synth.f32_to_bf16_bits(dy32)) if dtype == synth.BF16 else synth.Tensor(dtype, dy32)
+    dhl = rng.standard_normal((B, D, N)).astype(np.float32) if with_dhl else None
+    t = {n: to_dev(inp.t[n]) for n in inp.t}
+    G = ssd.selective_scan_backward(t["x"], t["dt"], to_dev(inp.p["A"]), t["Bm"], t["Cm"], to_dev(dy),
+                                    Dskip=to_dev(inp.p.get("Dskip")), z=t.get("z"), dt_bias=to_dev(bias),
+                                    dt_softplus=softplus, h0=to_dev(inp.p.get("h0")), dh_last=to_dev(dhl))
+    torch.cuda.synchronize()
+    R = og.selective_scan_grads(f64(inp.t["x"]), f64(inp.t["dt"]), f64(inp.p["A"]), f64(inp.t["Bm"]),
+                                f64(inp.t["Cm"]), f64(dy), Dskip=f64(inp.p.get("Dskip")),
+                                z=f64(inp.t["z"]) if with_z else None, dt_bias=f64(bias), dt_softplus=softplus,
+                                h0=f64(inp.p.get("h0")), dh_last=None if dhl is None else dhl.astype(np.float64))
+    for name in R:
+        assert_close(host(G[name]), R[name], TOLB[dtype] if tol is None else tol, name)
+    return G
+
+
+def test_selective_backward_fp32_ragged():
+    # 100 rows = 6 segments of 16 and a ragged one; 300 channels = two channel blocks, the second ragged
+    run_sel_bwd(2, 100, 300, 16, synth.F32, 7000)
+
+
+@pytest.mark.parametrize("N", [1, 2, 4, 8])
+def test_selective_backward_small_n(N):
+    run_sel_bwd(2, 37, 96, N, synth.F32, 7100 + N, with_bias=N % 2 == 0, with_h0=N > 2)
+
+
+@pytest.mark.parametrize("L", [1, 16, 17])
+def test_selective_backward_short_sequences(L):
+    run_sel_bwd(3, L, 64, 16, synth.F32, 7200 + L)
+
+
+def test_selective_backward_bf16_raw_dt_no_gate():
+    run_sel_bwd(2, 64 * 3, 256, 8, synth.BF16, 7300, softplus=False, with_z=False, with_skip=False, with_bias=False,
+                with_h0=False, with_dhl=False)
+
+
+def test_selective_backward_clamp_active():
+    """Channels with positive A and one large step, where delta A exceeds 20 on some states (clamped,
+    no gradient through the exponent) and not on another; elsewhere delta = 1e-3 keeps the growth small
+    (the state is multiplied by e^20 once).  Tolerance 1e-4 RMS: before the clamped step the gradient
+    terms of the states are e^20 larger than the sums they cancel into (each element is within a few
+    1e-6 of its own magnitude); a wrong clamp mask errs by O(1)."""
+    D, N, L = 64, 4, 40
+    A = -np.tile(np.arange(1, N + 1, dtype=np.float64), (D, 1))
+    hot = np.arange(0, D, 7)
+    A[hot, :] = [60.0, 30.0, 100.0, 2.0]
+
+    def edit(inp):
+        dt = inp.t["dt"].data  # raw delta (softplus off), fp32
+        dt[:, :, hot] = 1e-3
+        dt[:, 20, hot] = 0.8   # delta A = 48, 24, 80, 1.6: states 0, 1, 2 clamped, state 3 not
+
+    run_sel_bwd(1, L, D, N, synth.F32, 7400, softplus=False, with_bias=False, A=A, with_dhl=False, edit=edit,
+                tol=1e-4)
+
+
+def test_selective_backward_deterministic_and_bf16_output():
+    import torch
+    inp = synth.selective_inputs(2, 96, 320, 16, synth.BF16, 7500, with_h0=True)
+    t = {n: to_dev(inp.t[n]) for n in inp.t}
+    dy = torch.randn((2, 96, 320), device="cuda").to(torch.bfloat16)
+    args = (t["x"], t["dt"], to_dev(inp.p["A"]), t["Bm"], t["Cm"], dy)
+    kw = dict(Dskip=to_dev(inp.p["Dskip"]), z=t["z"], h0=to_dev(inp.p["h0"]))
+    g1 = ssd.selective_scan_backward(*args, **kw)
+    g2 = ssd.selective_scan_backward(*args, **kw)
+    g16 = ssd.selective_scan_backward(*args, out_dtype=torch.bfloat16, **kw)
+    torch.cuda.synchronize()
+    for k in g1:
+        assert torch.equal(g1[k], g2[k]), k
+    for k in ("dx", "ddt", "dz", "dBm", "dCm"):
+        assert torch.equal(g16[k], g1[k].to(torch.bfloat16)), k
+
+
+def test_selective_backward_empty_sequence():
+    import torch
+    x = torch.empty((2, 0, 8), device="cuda")
+    bm = torch.empty((2, 0, 4), device="cuda")
+    A = -torch.ones((8, 4), device="cuda")
+    dhl = torch.randn((2, 8, 4), device="cuda")
+    g = ssd.selective_scan_backward(x, x, A, bm, bm, x, Dskip=torch.ones(8, device="cuda"), dh_last=dhl)
+    torch.cuda.synchronize()
+    assert torch.equal(g["dh0"], dhl) and torch.all(g["dA"] == 0) and torch.all(g["dDskip"] == 0)
+
+
+def test_selective_backward_full_width_bf16():
+    """All 1536 channels of the headline workload (6 channel blocks summed for dB / dC), its multi-scale
+    A, softplus steps, gate and skip, over 256 steps."""
+    run_sel_bwd(2, 256, 1536, 16, synth.BF16, 7600)
