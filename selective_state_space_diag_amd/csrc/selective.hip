@@ -622,17 +622,22 @@ __device__ __forceinline__ float silu_grad_f(float z) {
 // Sum of v[j] over the 64 lanes of the wave, for 16 values j at once: each exchange step halves the
 // values a lane keeps (the half picked by one lane bit) and adds its partner's other half.  On return
 // lanes with (lane & 3) == 0 hold the total of value (lane >> 2) & 15 in v[0].
-__device__ __forceinline__ void wave_sum16(float (&v)[16], int lane) {
+template <int HALF>
+__device__ __forceinline__ void wave_sum_step(float (&v)[16], int lane) {
+  constexpr int kBit = HALF * 4;  // 32, 16, 8, 4 for HALF = 8, 4, 2, 1
+  const bool hi = (lane & kBit) != 0;
 #pragma unroll
-  for (int half = 8, bit = 32; half >= 1; half >>= 1, bit >>= 1) {
-    const bool hi = (lane & bit) != 0;
-#pragma unroll
-    for (int i = 0; i < half; ++i) {
-      const float send = hi ? v[i] : v[i + half];
-      const float keep = hi ? v[i + half] : v[i];
-      v[i] = keep + __shfl_xor(send, bit);
-    }
+  for (int i = 0; i < HALF; ++i) {
+    const float send = hi ? v[i] : v[i + HALF];
+    const float keep = hi ? v[i + HALF] : v[i];
+    v[i] = keep + __shfl_xor(send, kBit);
   }
+}
+__device__ __forceinline__ void wave_sum16(float (&v)[16], int lane) {
+  wave_sum_step<8>(v, lane);
+  wave_sum_step<4>(v, lane);
+  wave_sum_step<2>(v, lane);
+  wave_sum_step<1>(v, lane);
   v[0] += __shfl_xor(v[0], 2);
   v[0] += __shfl_xor(v[0], 1);
 }
@@ -657,13 +662,18 @@ __global__ __launch_bounds__(kThreads) void selective_bwd_agg_kernel(SelBwdParam
 #pragma unroll
   for (int n = 0; n < NS; ++n) A2[n] = p.A[dl * NS + n] * kLog2e;
   const float bias = p.dt_bias ? p.dt_bias[dl] : 0.0f;
+  using W = win<Tin, 1>;
+  constexpr int es = sizeof(Tin);
+  const auto wdt = unit_window(p.dt, row0, R, p.D, es), wdy = unit_window(p.dy, row0, R, p.D, es);
+  const auto wzz = unit_window(GATE ? p.z : p.dt, row0, R, p.D, es);
+  const uint32_t lane_in = (uint32_t)(dl * es), row_in = (uint32_t)(p.D * es);
   float delta[kBT], ds[kBT];
 #pragma unroll
   for (int t = 0; t < kBT; ++t) {
-    const int64_t r = row0 + min(t, R - 1);
-    const float v = io<Tin>::load(p.dt, r * p.D + dl) + bias;
-    const float dyv = io<Tin>::load(p.dy, r * p.D + dl);
-    const float g = GATE ? silu_f(io<Tin>::load(p.z, r * p.D + dl)) : 1.0f;
+    const uint32_t ro = (uint32_t)min(t, R - 1) * row_in;
+    const float v = W::get(W::load(wdt, lane_in, ro), 0) + bias;
+    const float dyv = W::get(W::load(wdy, lane_in, ro), 0);
+    const float g = GATE ? silu_f(W::get(W::load(wzz, lane_in, ro), 0)) : 1.0f;
     delta[t] = t < R ? (SOFTPLUS ? softplus_f(v) : v) : 0.0f;  // rows past the sequence: identity
     ds[t] = t < R ? dyv * g : 0.0f;
   }
@@ -716,6 +726,7 @@ __global__ __launch_bounds__(kThreads) void selective_bwd_kernel(SelBwdParams p)
   const int64_t dl = active ? d : p.D - 1;  // lanes past D recompute channel D-1 and store nothing
   __shared__ float sB[kBT * NS], sC[kBT * NS];
   __shared__ float sRedB[NS][kThreads / 64][kBT], sRedC[NS][kThreads / 64][kBT];
+  __shared__ float sAb[kBT][kThreads], sHp[kBT][kThreads];  // one state's abar and h_{t-1}, per thread
   for (int e = threadIdx.x; e < kBT * NS; e += kThreads) {
     const int t = e / NS;
     const int64_t idx = (row0 + min(t, R - 1)) * NS + (e - t * NS);
@@ -726,17 +737,24 @@ __global__ __launch_bounds__(kThreads) void selective_bwd_kernel(SelBwdParams p)
   const float dskip = p.Dskip ? p.Dskip[dl] : 0.0f;
   // per row: delta, x, ds = dy silu(z); rows past the sequence are exact identities (delta = x = ds = 0).
   // (dt, dy and z are read again for the row gradients at the end, from L2.)
-  float delta[kBT], xv[kBT], ds[kBT];
+  using W = win<Tin, 1>;
+  constexpr int es = sizeof(Tin);
+  const auto wdt = unit_window(p.dt, row0, R, p.D, es), wxx = unit_window(p.x, row0, R, p.D, es);
+  const auto wdy = unit_window(p.dy, row0, R, p.D, es), wzz = unit_window(GATE ? p.z : p.x, row0, R, p.D, es);
+  const uint32_t lane_in = (uint32_t)(dl * es), row_in = (uint32_t)(p.D * es);
+  auto ld = [&](const __amdgpu_buffer_rsrc_t& w, int t) {
+    return W::get(W::load(w, lane_in, (uint32_t)min(t, R - 1) * row_in), 0);
+  };
+  float delta[kBT], dx_[kBT], ds[kBT];  // dx_ = delta x
 #pragma unroll
   for (int t = 0; t < kBT; ++t) {
-    const int64_t r = row0 + min(t, R - 1);
     const bool ok = t < R;
-    const float v = io<Tin>::load(p.dt, r * p.D + dl) + bias;
-    const float xx = io<Tin>::load(p.x, r * p.D + dl);
-    const float dyv = io<Tin>::load(p.dy, r * p.D + dl);
-    const float g = GATE ? silu_f(io<Tin>::load(p.z, r * p.D + dl)) : 1.0f;
+    const float v = ld(wdt, t) + bias;
+    const float xx = ld(wxx, t);
+    const float dyv = ld(wdy, t);
+    const float g = GATE ? silu_f(ld(wzz, t)) : 1.0f;
     delta[t] = ok ? (SOFTPLUS ? softplus_f(v) : v) : 0.0f;
-    xv[t] = ok ? xx : 0.0f;
+    dx_[t] = delta[t] * (ok ? xx : 0.0f);
     ds[t] = ok ? dyv * g : 0.0f;
   }
   float sacc[kBT], GB[kBT], MA[kBT];
@@ -744,39 +762,53 @@ __global__ __launch_bounds__(kThreads) void selective_bwd_kernel(SelBwdParams p)
   for (int t = 0; t < kBT; ++t) { sacc[t] = 0.0f; GB[t] = 0.0f; MA[t] = 0.0f; }
   __syncthreads();
 
+  // the state's entering value, its value of q at the segment's end and its A, loaded one state ahead
+  auto h_in = [&](int n) {
+    return seg == 0 ? (p.h0 ? p.h0[(seq * p.D + dl) * NS + n] : 0.0f) : p.carry[(u * NS + n) * p.D + dl];
+  };
+  float nx_h = h_in(0), nx_q = p.qend[u * NS * p.D + dl], nx_A = p.A[dl * NS];
 #pragma unroll 1
   for (int n = 0; n < NS; ++n) {
-    const float An = p.A[dl * NS + n];
+    const float An = nx_A;
     const float A2 = An * kLog2e;
-    float h = seg == 0 ? (p.h0 ? p.h0[(seq * p.D + dl) * NS + n] : 0.0f) : p.carry[(u * NS + n) * p.D + dl];
-    float q = p.qend[(u * NS + n) * p.D + dl];
-    // forward through the rows
-    float ab[kBT], hp[kBT], v[16];
+    float h = nx_h;
+    float q = nx_q;
+    if (n + 1 < NS) {
+      nx_h = h_in(n + 1);
+      nx_q = p.qend[(u * NS + n + 1) * p.D + dl];
+      nx_A = p.A[dl * NS + n + 1];
+    }
+    // forward through the rows (abar and h_{t-1} of this state kept in LDS for the way back)
+    float v[16];
     uint32_t live = 0;  // bit t: the clamp does not act at row t
 #pragma unroll
     for (int t = 0; t < kBT; ++t) {
       float e = delta[t] * A2;
       live |= (e <= kClampLog2 ? 1u : 0u) << t;
       e = e > kClampLog2 ? kClampLog2 : e;
-      ab[t] = hw_exp2(e);
-      hp[t] = h;
-      h = fmaf(ab[t], h, (delta[t] * xv[t]) * sB[t * NS + n]);
+      const float ab = hw_exp2(e);
+      sAb[t][threadIdx.x] = ab;
+      sHp[t][threadIdx.x] = h;
+      h = fmaf(ab, h, dx_[t] * sB[t * NS + n]);
       sacc[t] = fmaf(sC[t * NS + n], h, sacc[t]);
       v[t] = active ? ds[t] * h : 0.0f;  // this lane's share of dC_tn (idle lanes add nothing)
     }
     wave_sum16(v, lane);
     if ((lane & 3) == 0) sRedC[n][wave][(lane >> 2) & 15] = v[0];
+    // (a compiler-only memory fence: abar and h_{t-1} are read back from LDS rather than kept live)
+    asm volatile("" ::: "memory");
     // back through the rows
     float dA = 0.0f;
 #pragma unroll
     for (int t = kBT - 1; t >= 0; --t) {
+      const float ab = sAb[t][threadIdx.x], hp = sHp[t][threadIdx.x];
       const float g = fmaf(ds[t], sC[t * NS + n], q);
-      q = ab[t] * g;
-      const float mab = (live >> t) & 1u ? (g * hp[t]) * ab[t] : 0.0f;  // d abar times abar, unclamped rows
+      q = ab * g;
+      const float mab = (live >> t) & 1u ? (g * hp) * ab : 0.0f;  // d abar times abar, unclamped rows
       MA[t] = fmaf(mab, An, MA[t]);
       dA = fmaf(mab, delta[t], dA);
       GB[t] = fmaf(g, sB[t * NS + n], GB[t]);
-      v[t] = active ? g * (delta[t] * xv[t]) : 0.0f;  // this lane's share of dB_tn
+      v[t] = active ? g * dx_[t] : 0.0f;  // this lane's share of dB_tn
     }
     wave_sum16(v, lane);
     if ((lane & 3) == 0) sRedB[n][wave][(lane >> 2) & 15] = v[0];
@@ -787,23 +819,25 @@ __global__ __launch_bounds__(kThreads) void selective_bwd_kernel(SelBwdParams p)
   }
 
   // row gradients
-  const int64_t rowb = row0 * p.D;
+  using WO = win<Tout, 1>;
+  const auto wox = unit_window(p.dx, row0, R, p.D, sizeof(Tout)), wot = unit_window(p.ddt, row0, R, p.D, sizeof(Tout));
+  const auto woz = unit_window(GATE ? p.dz : p.dx, row0, R, p.D, sizeof(Tout));
+  const uint32_t lane_out = (uint32_t)(dl * (int64_t)sizeof(Tout)), row_out = (uint32_t)(p.D * (int64_t)sizeof(Tout));
   float dsum = 0.0f, bsum = 0.0f;
 #pragma unroll
   for (int t = 0; t < kBT; ++t) {
-    const int64_t r = row0 + min(t, R - 1);
-    const float ddelta = fmaf(xv[t], GB[t], MA[t]);
-    const float gdt = SOFTPLUS ? ddelta * softplus_grad_f(io<Tin>::load(p.dt, r * p.D + dl) + bias) : ddelta;
+    const float xx = t < R ? ld(wxx, t) : 0.0f;
+    const float ddelta = fmaf(xx, GB[t], MA[t]);
+    const float gdt = SOFTPLUS ? ddelta * softplus_grad_f(ld(wdt, t) + bias) : ddelta;
     const float gx = fmaf(ds[t], dskip, delta[t] * GB[t]);
     float gz = 0.0f;
-    if (GATE) gz = io<Tin>::load(p.dy, r * p.D + dl) * silu_grad_f(io<Tin>::load(p.z, r * p.D + dl)) *
-                   fmaf(dskip, xv[t], sacc[t]);
-    dsum = fmaf(ds[t], xv[t], dsum);
+    if (GATE) gz = ld(wdy, t) * silu_grad_f(ld(wzz, t)) * fmaf(dskip, xx, sacc[t]);
+    dsum = fmaf(ds[t], xx, dsum);
     if (t < R) bsum += gdt;
     if (active && t < R) {
-      io<Tout>::store(p.dx, rowb + t * p.D + d, gx);
-      io<Tout>::store(p.ddt, rowb + t * p.D + d, gdt);
-      if (GATE) io<Tout>::store(p.dz, rowb + t * p.D + d, gz);
+      WO::store(wox, lane_out, (uint32_t)t * row_out, &gx);
+      WO::store(wot, lane_out, (uint32_t)t * row_out, &gdt);
+      if (GATE) WO::store(woz, lane_out, (uint32_t)t * row_out, &gz);
     }
   }
   if (active) {
@@ -842,13 +876,26 @@ __global__ __launch_bounds__(kThreads) void selective_bwd_bc_kernel(const float*
   io<Tout>::store(dCm, i, sc);
 }
 
-__global__ __launch_bounds__(kThreads) void selective_bwd_sum_kernel(const float* part, int64_t units, int64_t width,
-                                                                     int64_t N, float* out) {
-  // column c = n * D + d of [units][N][D] (or d of [units][D] with N = 1) -> out[d * N + n]
+// Sums over units in two fixed-order steps: slice k of kSumSlices adds units [k U / S, (k + 1) U / S),
+// then the slices are added in order.  Column c = n * D + d of [units][N][D] (or d of [units][D]
+// with N = 1) goes to out[d * N + n].
+constexpr int kSumSlices = 32;
+__global__ __launch_bounds__(kThreads) void selective_bwd_slice_kernel(const float* part, int64_t units,
+                                                                       int64_t width, float* slices) {
+  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (c >= width) return;
+  const int64_t k = blockIdx.y, u0 = k * units / kSumSlices, u1 = (k + 1) * units / kSumSlices;
+  float acc = 0.0f;
+  for (int64_t u = u0; u < u1; ++u) acc += part[u * width + c];
+  slices[k * width + c] = acc;
+}
+__global__ __launch_bounds__(kThreads) void selective_bwd_final_kernel(const float* slices, int64_t width, int64_t N,
+                                                                       float* out) {
   const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (c >= width) return;
   float acc = 0.0f;
-  for (int64_t k = 0; k < units; ++k) acc += part[k * width + c];
+#pragma unroll
+  for (int k = 0; k < kSumSlices; ++k) acc += slices[k * width + c];
   const int64_t D = width / N, n = c / D, d = c - n * D;
   out[d * N + n] = acc;
 }
@@ -926,7 +973,7 @@ hipError_t launch_selective_scan(const SelectiveScanArgs& a, hipStream_t s) {
 namespace {
 struct BwdLayout {
   int64_t nseg, U, nblk;
-  size_t state, row, bc;  // bytes of one [U][N][D], one [U][D], one [nblk][B L][N] buffer
+  size_t state, row, bc, slices;  // bytes of one [U][N][D], [U][D], [nblk][B L][N], [kSumSlices][N][D] buffer
 };
 BwdLayout bwd_layout(const SelectiveBwdArgs& a) {
   BwdLayout l;
@@ -936,6 +983,7 @@ BwdLayout bwd_layout(const SelectiveBwdArgs& a) {
   l.state = align256((size_t)(l.U * a.N * a.D) * sizeof(float));
   l.row = align256((size_t)(l.U * a.D) * sizeof(float));
   l.bc = align256((size_t)(l.nblk * a.B * a.L * a.N) * sizeof(float));
+  l.slices = align256((size_t)(kSumSlices * a.N * a.D) * sizeof(float));
   return l;
 }
 
@@ -962,7 +1010,7 @@ void launch_fwd_carry_t(const SelParams& f, int64_t U, bool softplus, hipStream_
 
 size_t selective_scan_backward_scratch_bytes(const SelectiveBwdArgs& a) {
   const BwdLayout l = bwd_layout(a);
-  return 5 * l.state + 2 * l.row + 2 * l.bc;
+  return 5 * l.state + 2 * l.row + 2 * l.bc + l.slices;
 }
 
 hipError_t launch_selective_scan_backward(const SelectiveBwdArgs& a, hipStream_t s) {
@@ -977,6 +1025,7 @@ hipError_t launch_selective_scan_backward(const SelectiveBwdArgs& a, hipStream_t
   float* dbias_part = reinterpret_cast<float*>(base + 5 * l.state + l.row);
   float* PB = reinterpret_cast<float*>(base + 5 * l.state + 2 * l.row);
   float* PC = reinterpret_cast<float*>(base + 5 * l.state + 2 * l.row + l.bc);
+  float* slices = reinterpret_cast<float*>(base + 5 * l.state + 2 * l.row + 2 * l.bc);  // kSumSlices x (N D)
   // 1. the state entering every segment: the forward's aggregate and carry passes at segment kBT
   if (l.nseg > 1) {
     SelParams f{};
@@ -1008,13 +1057,15 @@ hipError_t launch_selective_scan_backward(const SelectiveBwdArgs& a, hipStream_t
   else
     hipLaunchKernelGGL((selective_bwd_bc_kernel<float>), dim3((unsigned)((nbc + kThreads - 1) / kThreads)), blk, 0, s,
                        PB, PC, l.nblk, nbc, a.dBm, a.dCm);
-  const int64_t wA = a.N * a.D;
-  hipLaunchKernelGGL(selective_bwd_sum_kernel, dim3((unsigned)((wA + kThreads - 1) / kThreads)), blk, 0, s, dA_part,
-                     l.U, wA, a.N, a.dA);
-  const dim3 gD((unsigned)((a.D + kThreads - 1) / kThreads));
-  if (a.dDskip) hipLaunchKernelGGL(selective_bwd_sum_kernel, gD, blk, 0, s, dD_part, l.U, a.D, (int64_t)1, a.dDskip);
-  if (a.ddt_bias)
-    hipLaunchKernelGGL(selective_bwd_sum_kernel, gD, blk, 0, s, dbias_part, l.U, a.D, (int64_t)1, a.ddt_bias);
+  // (the three sums use the slice buffer in turn; width <= N D)
+  auto sum_units = [&](const float* part, int64_t width, int64_t n, float* out) {
+    const unsigned nb = (unsigned)((width + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL(selective_bwd_slice_kernel, dim3(nb, kSumSlices), blk, 0, s, part, l.U, width, slices);
+    hipLaunchKernelGGL(selective_bwd_final_kernel, dim3(nb), blk, 0, s, slices, width, n, out);
+  };
+  sum_units(dA_part, a.N * a.D, a.N, a.dA);
+  if (a.dDskip) sum_units(dD_part, a.D, 1, a.dDskip);
+  if (a.ddt_bias) sum_units(dbias_part, a.D, 1, a.ddt_bias);
   return hipGetLastError();
 }
 
