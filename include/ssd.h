@@ -250,7 +250,7 @@ int ssd_selective_scan(int64_t B, int64_t L, int64_t D, int64_t N, int in_dtype,
  *   dBm, dCm            : [B, L, N] (out dtype)
  *   dA                  : [D, N] fp32;  dDskip, ddt_bias : [D] fp32 or NULL;  dh0 : [B, D, N] fp32 or NULL
  * Every output is overwritten (not accumulated).  The forward states are recomputed (the scratch
- * holds per-16-row-segment states, 6 x B * ceil(L/16) * D * N fp32).  Reductions run in a fixed
+ * holds per-16-row-segment states, about 5 x B * ceil(L/16) * D * N fp32).  Reductions run in a fixed
  * order: results are deterministic.  Errors as ssd_selective_scan, plus SSD_ERR_NULL for missing
  * dy / dx / ddt / dBm / dCm / dA (or dz with z). */
 int ssd_selective_scan_backward(int64_t B, int64_t L, int64_t D, int64_t N, int in_dtype, int out_dtype,

@@ -343,7 +343,8 @@ __global__ __launch_bounds__(kThreads) void selective_scan_kernel(SelParams p) {
 // One thread per (sequence, state n, channel d): walks the sequence's segments in order,
 // carry[s] = h; h = P[s] h + H[s], starting from h0 (or zero).  The aggregate loads do not depend
 // on h, so they are issued ahead of the multiply-add chain.
-template <int NS>
+// (ROLE tells apart, by name, the forward's launches from the backward's at its own segment length)
+template <int NS, int ROLE = 0>
 __global__ __launch_bounds__(kThreads) void selective_carry_kernel(SelParams p) {
   const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const int64_t per_seq = NS * p.D;
@@ -993,7 +994,7 @@ void launch_fwd_carry(const SelParams& f, int64_t U, bool softplus, hipStream_t 
   if (softplus) hipLaunchKernelGGL((selective_aggregate_kernel<Tin, NS, true>), grid, dim3(kThreads), 0, s, f);
   else hipLaunchKernelGGL((selective_aggregate_kernel<Tin, NS, false>), grid, dim3(kThreads), 0, s, f);
   const int64_t nthreads = f.nseq * NS * f.D;
-  hipLaunchKernelGGL((selective_carry_kernel<NS>), dim3((unsigned)((nthreads + kThreads - 1) / kThreads)),
+  hipLaunchKernelGGL((selective_carry_kernel<NS, 1>), dim3((unsigned)((nthreads + kThreads - 1) / kThreads)),
                      dim3(kThreads), 0, s, f);
 }
 template <typename Tin>
