@@ -10,7 +10,7 @@
  *                 (gradients)                       ssd_minmax_scan_backward
  *   causal conv   depthwise, width W <= 4           ssd_causal_conv1d / ssd_causal_conv1d_update
  *   selective     N <= 16 states per channel        ssd_selective_scan / ssd_selective_update
- *                 (gradients, batched)              ssd_selective_scan_backward
+ *                 (gradients)                       ssd_selective_scan_backward
  *   HGRN2         d x d matrix state per head       ssd_hgrn2_scan / ssd_hgrn2_update
  *
  * Conventions (every entry point):
@@ -235,8 +235,8 @@ int ssd_selective_scan(int64_t B, int64_t L, int64_t D, int64_t N, int in_dtype,
                        const int32_t* cu_seqlens, int64_t nseq,
                        const float* h0, void* y, float* h_last, void* stream);
 
-/* Gradients of the batched ssd_selective_scan (cu_seqlens not supported here) for the loss
- *     sum_{b,t,d} dy * y  +  sum_{b,d,n} dh_last * h_last.
+/* Gradients of ssd_selective_scan (batched, or packed varlen sequences as there) for the loss
+ *     sum_{b,t,d} dy * y  +  sum_{sequence,d,n} dh_last * h_last.
  * The pages train through autograd and print no backward pass; this is the gradient of the forward
  * definition above, with the clamp at 20 passing no gradient where delta*A > 20 (torch.clamp).
  * With s_t the readout before the gate, ds_t = dy_t silu(z_t) and g_t = dL/dh_t:
@@ -244,11 +244,12 @@ int ssd_selective_scan(int64_t B, int64_t L, int64_t D, int64_t N, int in_dtype,
  *   d delta = x sum_n g B + sum_n g h_{t-1} abar A (unclamped entries),  ddt = d delta softplus'(dt + bias)
  *   (or d delta without softplus),  dA = sum_{b,t} g h_{t-1} abar delta,  dDskip = sum ds x,
  *   ddt_bias = sum ddt,  dh0 = abar_0 g_0.
- *   inputs              : as ssd_selective_scan (B sequences, no cu_seqlens), plus
- *   dy                  : [B, L, D] (in dtype);   dh_last : [B, D, N] fp32 or NULL (= 0)
+ *   inputs              : as ssd_selective_scan (cu_seqlens, nseq and the state shapes too), plus
+ *   dy                  : [B, L, D] (in dtype);   dh_last : [B or nseq, D, N] fp32 or NULL (= 0)
  *   dx, ddt             : [B, L, D] (out dtype);  dz : [B, L, D] (out dtype), required when z is given
  *   dBm, dCm            : [B, L, N] (out dtype)
- *   dA                  : [D, N] fp32;  dDskip, ddt_bias : [D] fp32 or NULL;  dh0 : [B, D, N] fp32 or NULL
+ *   dA                  : [D, N] fp32;  dDskip, ddt_bias : [D] fp32 or NULL;
+ *   dh0                 : [B or nseq, D, N] fp32 or NULL (a zero-length sequence gets its dh_last)
  * Every output is overwritten (not accumulated).  The forward states are recomputed (the scratch
  * holds per-16-row-segment states, about 5 x B * ceil(L/16) * D * N fp32).  Reductions run in a fixed
  * order: results are deterministic.  Errors as ssd_selective_scan, plus SSD_ERR_NULL for missing
@@ -256,7 +257,8 @@ int ssd_selective_scan(int64_t B, int64_t L, int64_t D, int64_t N, int in_dtype,
 int ssd_selective_scan_backward(int64_t B, int64_t L, int64_t D, int64_t N, int in_dtype, int out_dtype,
                                 const void* x, const void* dt, const float* A,
                                 const void* Bm, const void* Cm, const float* Dskip, const void* z,
-                                const float* dt_bias, int dt_softplus, const float* h0,
+                                const float* dt_bias, int dt_softplus,
+                                const int32_t* cu_seqlens, int64_t nseq, const float* h0,
                                 const void* dy, const float* dh_last,
                                 void* dx, void* ddt, float* dA, void* dBm, void* dCm,
                                 float* dDskip, void* dz, float* ddt_bias, float* dh0, void* stream);

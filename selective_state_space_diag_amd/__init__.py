@@ -83,8 +83,8 @@ def lib() -> ctypes.CDLL:
         L.ssd_selective_scan.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _fp, _vp, _vp,
                                          _fp, _vp, _fp, ctypes.c_int, _vp, _i64, _fp, _vp, _fp, _vp]
         L.ssd_selective_scan_backward.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _fp,
-                                                  _vp, _vp, _fp, _vp, _fp, ctypes.c_int, _fp, _vp, _fp, _vp, _vp,
-                                                  _fp, _vp, _vp, _fp, _vp, _fp, _fp, _vp]
+                                                  _vp, _vp, _fp, _vp, _fp, ctypes.c_int, _vp, _i64, _fp, _vp, _fp,
+                                                  _vp, _vp, _fp, _vp, _vp, _fp, _vp, _fp, _fp, _vp]
         L.ssd_selective_update.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _fp, _vp, _vp, _fp,
                                            _vp, _fp, ctypes.c_int, _fp, _vp, _vp]
         L.ssd_hgrn2_scan.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp,
@@ -393,22 +393,27 @@ def selective_update(x, dt, A, Bm, Cm, state, Dskip=None, z=None, dt_bias=None, 
 
 
 def selective_scan_backward(x, dt, A, Bm, Cm, dy, Dskip=None, z=None, dt_bias=None, dt_softplus: bool = True, h0=None,
-                            dh_last=None, out_dtype=None):
-    """Gradients of the batched ``selective_scan`` for the loss sum(dy * y) + sum(dh_last * h_last)
-    (see ``ssd_selective_scan_backward``).  Returns a dict: dx, ddt [B, L, D], dBm, dCm [B, L, N] (out
-    dtype), dA [D, N], dh0 [B, D, N] (fp32), and dDskip, ddt_bias [D] (fp32), dz [B, L, D] for the
-    optional inputs that are given."""
+                            dh_last=None, out_dtype=None, cu_seqlens=None, check_cu_seqlens: bool = True):
+    """Gradients of ``selective_scan`` for the loss sum(dy * y) + sum(dh_last * h_last) (see
+    ``ssd_selective_scan_backward``); ``cu_seqlens`` as for ``selective_scan``.  Returns a dict: dx,
+    ddt [B, L, D], dBm, dCm [B, L, N] (out dtype), dA [D, N], dh0 [B or nseq, D, N] (fp32), and dDskip,
+    ddt_bias [D] (fp32), dz [B, L, D] for the optional inputs that are given."""
     torch = _torch()
     B, L, D = x.shape
     N = int(A.shape[1])
     code = _act([x, dt, Bm, Cm, z, dy], ["x", "dt", "Bm", "Cm", "z", "dy"])
     oc = _out_code(out_dtype)
+    cu = None
+    nseq = B
+    if cu_seqlens is not None:
+        cu = _cu_seqlens_device(cu_seqlens, L, x.device, check_cu_seqlens)
+        nseq = cu.numel() - 1
     odt = torch.bfloat16 if oc == SSD_BF16 else torch.float32
     dev = x.device
     g = {"dx": torch.empty((B, L, D), device=dev, dtype=odt), "ddt": torch.empty((B, L, D), device=dev, dtype=odt),
          "dA": torch.empty((D, N), device=dev, dtype=torch.float32),
          "dBm": torch.empty((B, L, N), device=dev, dtype=odt), "dCm": torch.empty((B, L, N), device=dev, dtype=odt),
-         "dh0": torch.empty((B, D, N), device=dev, dtype=torch.float32)}
+         "dh0": torch.empty((nseq, D, N), device=dev, dtype=torch.float32)}
     if Dskip is not None:
         g["dDskip"] = torch.empty((D,), device=dev, dtype=torch.float32)
     if z is not None:
@@ -419,8 +424,8 @@ def selective_scan_backward(x, dt, A, Bm, Cm, dy, Dskip=None, z=None, dt_bias=No
         B, L, D, N, code, oc, _dev(x, "x"), _dev(dt, "dt", x.shape), _dev(A, "A", (D, N), torch.float32),
         _dev(Bm, "Bm", (B, L, N)), _dev(Cm, "Cm", (B, L, N)), _dev(Dskip, "Dskip", (D,), torch.float32),
         _dev(z, "z", x.shape), _dev(dt_bias, "dt_bias", (D,), torch.float32), int(bool(dt_softplus)),
-        _dev(h0, "h0", (B, D, N), torch.float32), _dev(dy, "dy", x.shape),
-        _dev(dh_last, "dh_last", (B, D, N), torch.float32), _dev(g["dx"], "dx"), _dev(g["ddt"], "ddt"),
+        _dev(cu, "cu_seqlens"), nseq, _dev(h0, "h0", (nseq, D, N), torch.float32), _dev(dy, "dy", x.shape),
+        _dev(dh_last, "dh_last", (nseq, D, N), torch.float32), _dev(g["dx"], "dx"), _dev(g["ddt"], "ddt"),
         _dev(g["dA"], "dA"), _dev(g["dBm"], "dBm"), _dev(g["dCm"], "dCm"), _dev(g.get("dDskip"), "dDskip"),
         _dev(g.get("dz"), "dz"), _dev(g.get("ddt_bias"), "ddt_bias"), _dev(g["dh0"], "dh0"), _stream(dev))
     _raise(st, "selective_scan_backward")

@@ -422,13 +422,23 @@ int ssd_selective_scan(int64_t B, int64_t L, int64_t D, int64_t N, int in_dtype,
 int ssd_selective_scan_backward(int64_t B, int64_t L, int64_t D, int64_t N, int in_dtype, int out_dtype,
                                 const void* x, const void* dt, const float* A, const void* Bm, const void* Cm,
                                 const float* Dskip, const void* z, const float* dt_bias, int dt_softplus,
-                                const float* h0, const void* dy, const float* dh_last, void* dx, void* ddt, float* dA,
+                                const int32_t* cu_seqlens, int64_t nseq, const float* h0, const void* dy,
+                                const float* dh_last, void* dx, void* ddt, float* dA,
                                 void* dBm, void* dCm, float* dDskip, void* dz, float* ddt_bias, float* dh0,
                                 void* stream) {
   SSD_TRY(check_dtypes(in_dtype, out_dtype));
   if (B < 0 || L < 0 || D < 0 || N < 0) return fail(SSD_ERR_SHAPE, "negative size");
   if (!supported_n(N)) return fail(SSD_ERR_SHAPE, "N must be 1, 2, 4, 8 or 16");
-  if (too_big({B, L, D}) || too_big({B, D, N}) || (D + 255) / 256 > 65535 || B * ((L + 15) / 16) >= (int64_t)1 << 31)
+  if (cu_seqlens) {
+    if (B != 1) return fail(SSD_ERR_SHAPE, "cu_seqlens requires B == 1");
+    if (nseq < 0) return fail(SSD_ERR_SHAPE, "nseq must be >= 0");
+    if (nseq == 0 && L != 0) return fail(SSD_ERR_SHAPE, "nseq == 0 requires L == 0");
+    if (L >= (int64_t)1 << 31 || nseq >= (int64_t)1 << 30) return fail(SSD_ERR_SHAPE, "packed length too large");
+  } else {
+    nseq = B;
+  }
+  if (too_big({B, L, D}) || too_big({nseq, D, N}) || (D + 255) / 256 > 65535 ||
+      B * ((L + 15) / 16) + nseq >= (int64_t)1 << 31)
     return fail(SSD_ERR_SHAPE, "problem too large");
   const int64_t nact = B * L * D;
   if (nact > 0 && (!x || !dt || !dy || !dx || !ddt)) return fail(SSD_ERR_NULL, "x, dt, dy, dx and ddt are required");
@@ -437,11 +447,12 @@ int ssd_selective_scan_backward(int64_t B, int64_t L, int64_t D, int64_t N, int 
   if (nact > 0 && z && !dz) return fail(SSD_ERR_NULL, "dz is required with z");
   const size_t ab = (size_t)nact * esize(in_dtype), ob = (size_t)nact * esize(out_dtype);
   const size_t bb = (size_t)(B * L * N) * esize(in_dtype), bo = (size_t)(B * L * N) * esize(out_dtype);
-  const size_t sb = (size_t)(B * D * N) * 4, db = (size_t)D * 4;
+  const size_t sb = (size_t)(nseq * D * N) * 4, db = (size_t)D * 4;
   std::vector<Span> ins = {{"x", x, ab},         {"dt", dt, ab},         {"A", A, (size_t)(D * N) * 4},
                            {"Bm", Bm, bb},       {"Cm", Cm, bb},         {"Dskip", Dskip, db},
                            {"z", z, ab},         {"dt_bias", dt_bias, db}, {"h0", h0, sb},
-                           {"dy", dy, ab},       {"dh_last", dh_last, sb}};
+                           {"dy", dy, ab},       {"dh_last", dh_last, sb},
+                           {"cu_seqlens", cu_seqlens, (size_t)(nseq + 1) * 4}};
   std::vector<Span> outs = {{"dx", dx, ob},      {"ddt", ddt, ob},       {"dA", dA, (size_t)(D * N) * 4},
                             {"dBm", dBm, bo},    {"dCm", dCm, bo},       {"dDskip", dDskip, db},
                             {"dz", z ? dz : nullptr, ob}, {"ddt_bias", ddt_bias, db}, {"dh0", dh0, sb}};
@@ -450,15 +461,15 @@ int ssd_selective_scan_backward(int64_t B, int64_t L, int64_t D, int64_t N, int 
   SSD_TRY(check_align(all));
   SSD_TRY(check_alias(outs, ins));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (D * N == 0 || B == 0) return ok();
+  if (D * N == 0 || nseq == 0) return ok();
   if (L == 0) {  // no steps: parameter gradients are zero, dh0 = dh_last
     SSD_TRY(hip_status(ssd::launch_copy_or_zero(dA, nullptr, D * N, s), "selective_scan_backward"));
     SSD_TRY(hip_status(ssd::launch_copy_or_zero(dDskip, nullptr, D, s), "selective_scan_backward"));
     SSD_TRY(hip_status(ssd::launch_copy_or_zero(ddt_bias, nullptr, D, s), "selective_scan_backward"));
-    return hip_status(ssd::launch_copy_or_zero(dh0, dh_last, B * D * N, s), "selective_scan_backward");
+    return hip_status(ssd::launch_copy_or_zero(dh0, dh_last, nseq * D * N, s), "selective_scan_backward");
   }
   ssd::SelectiveBwdArgs a{B, L, D, N, in_dtype == SSD_BF16, out_dtype == SSD_BF16, x, dt, A, Bm, Cm, Dskip, z,
-                          dt_bias, dt_softplus ? 1 : 0, h0, dy, dh_last, dx, ddt, dA, dBm, dCm, dDskip,
+                          dt_bias, dt_softplus ? 1 : 0, cu_seqlens, nseq, h0, dy, dh_last, dx, ddt, dA, dBm, dCm, dDskip,
                           z ? dz : nullptr, ddt_bias, dh0, nullptr};
   SSD_TRY(get_scratch(stream, kScratchSelectiveBwd, ssd::selective_scan_backward_scratch_bytes(a), &a.scratch));
   return hip_status(ssd::launch_selective_scan_backward(a, s), "selective_scan_backward launch");

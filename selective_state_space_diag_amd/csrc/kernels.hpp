@@ -146,7 +146,7 @@ int64_t selective_segment_len(const SelectiveScanArgs& a);
 size_t selective_scan_scratch_bytes(const SelectiveScanArgs& a);
 hipError_t launch_selective_scan(const SelectiveScanArgs& a, hipStream_t s);
 
-// Gradients of the batched selective scan (no cu_seqlens).
+// Gradients of the selective scan (batched, or packed varlen with B = 1).
 struct SelectiveBwdArgs {
   int64_t B, L, D, N;
   int in_bf16, out_bf16;
@@ -157,7 +157,9 @@ struct SelectiveBwdArgs {
   const void* z;        // or NULL
   const float* dt_bias; // or NULL
   int dt_softplus;
-  const float* h0;      // [B][D][N] or NULL
+  const int32_t* cu_seqlens;  // device [nseq + 1] or NULL
+  int64_t nseq;
+  const float* h0;      // [B or nseq][D][N] or NULL
   const void* dy;       // in dtype
   const float* dh_last; // [B][D][N] or NULL
   void *dx, *ddt;       // out dtype

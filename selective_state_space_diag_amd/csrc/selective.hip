@@ -585,7 +585,11 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 constexpr int kBT = 16;  // rows per backward segment
 
 struct SelBwdParams {
-  int64_t L, D, nseg, nblk, BL;
+  int64_t L, D, nseg, nblk, BL;  // batched: L rows per sequence, nseg segments each; BL rows in all
+  const int32_t* cu;             // packed varlen: boundaries, or NULL (then the fields below are unused)
+  const int2* units;             // (sequence, segment) per unit
+  const int* n_units;            // number of units (device)
+  const int2* seq_units;         // (first unit, unit count) per sequence
   const void* x;
   const void* dt;
   const float* A;
@@ -611,6 +615,34 @@ struct SelBwdParams {
   float* dbias_part;   // [unit][D]
   float* dh0;          // [B][D][N] or NULL
 };
+
+// Unit u of the backward passes: its sequence, segment, first row and row count.
+struct BUnit {
+  int64_t seq, seg, row0;
+  int R;
+  bool valid;
+};
+__device__ __forceinline__ BUnit bwd_unit(const SelBwdParams& p, int64_t u) {
+  BUnit r;
+  int64_t end;
+  if (p.cu == nullptr) {
+    r.seq = u / p.nseg;
+    r.seg = u - r.seq * p.nseg;
+    r.row0 = r.seq * p.L + r.seg * kBT;
+    end = (r.seq + 1) * p.L;
+    r.valid = true;
+  } else {
+    r.valid = u < (int64_t)(*p.n_units);
+    if (!r.valid) return r;
+    const int2 e = p.units[u];
+    r.seq = e.x;
+    r.seg = e.y;
+    r.row0 = (int64_t)p.cu[r.seq] + r.seg * kBT;
+    end = p.cu[r.seq + 1];
+  }
+  r.R = (int)min<int64_t>(kBT, end - r.row0);
+  return r;
+}
 
 // softplus'(v) as torch takes it: sigmoid(v), and 1 above the threshold 20.
 __device__ __forceinline__ float softplus_grad_f(float v) { return v > 20.0f ? 1.0f : sigmoid_f(v); }
@@ -647,10 +679,10 @@ __device__ __forceinline__ void wave_sum16(float (&v)[16], int lane) {
 template <typename Tin, int NS, bool SOFTPLUS, bool GATE>
 __global__ __launch_bounds__(kThreads) void selective_bwd_agg_kernel(SelBwdParams p) {
   const int64_t u = blockIdx.x;
-  const int64_t seq = u / p.nseg, seg = u - seq * p.nseg;
-  if (seg == 0) return;
-  const int64_t row0 = seq * p.L + seg * kBT;
-  const int R = (int)min<int64_t>(kBT, (seq + 1) * p.L - row0);
+  const BUnit U = bwd_unit(p, u);
+  if (!U.valid || U.seg == 0) return;
+  const int64_t row0 = U.row0;
+  const int R = U.R;
   const int64_t d = (int64_t)blockIdx.y * kThreads + threadIdx.x;
   const bool active = d < p.D;
   const int64_t dl = active ? d : p.D - 1;
@@ -704,9 +736,16 @@ __global__ __launch_bounds__(kThreads) void selective_bwd_carry_kernel(SelBwdPar
   if (seq >= nseq) return;
   const int64_t e = gid - seq * per_seq;  // n * D + d
   const int64_t n = e / p.D, d = e - n * p.D;
+  int64_t first = seq * p.nseg, count = p.nseg;
+  if (p.cu != nullptr) {
+    const int2 r = p.seq_units[seq];
+    first = r.x;
+    count = r.y;
+  }
   float q = p.dh_last ? p.dh_last[(seq * p.D + d) * NS + n] : 0.0f;
-  for (int64_t s = p.nseg - 1; s >= 0; --s) {
-    const int64_t idx = ((seq * p.nseg + s) * NS + n) * p.D + d;
+  if (count == 0 && p.dh0) p.dh0[(seq * p.D + d) * NS + n] = q;  // empty sequence: dh0 = dh_last
+  for (int64_t s = count - 1; s >= 0; --s) {
+    const int64_t idx = ((first + s) * NS + n) * p.D + d;
     p.qend[idx] = q;
     if (s > 0) q = fmaf(p.aggP[idx], q, p.aggQ[idx]);
   }
@@ -717,9 +756,10 @@ template <typename Tin, typename Tout, int NS, bool SOFTPLUS, bool GATE>
 __global__ __launch_bounds__(kThreads) void selective_bwd_kernel(SelBwdParams p) {
   static_assert(kBT == 16, "the dB / dC butterfly sums 16 rows");
   const int64_t u = blockIdx.x;
-  const int64_t seq = u / p.nseg, seg = u - seq * p.nseg;
-  const int64_t row0 = seq * p.L + seg * kBT;
-  const int R = (int)min<int64_t>(kBT, (seq + 1) * p.L - row0);
+  const BUnit U = bwd_unit(p, u);
+  if (!U.valid) return;
+  const int64_t seq = U.seq, seg = U.seg, row0 = U.row0;
+  const int R = U.R;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t d = (int64_t)blockIdx.y * kThreads + threadIdx.x;
@@ -882,9 +922,11 @@ __global__ __launch_bounds__(kThreads) void selective_bwd_bc_kernel(const float*
 // with N = 1) goes to out[d * N + n].
 constexpr int kSumSlices = 32;
 __global__ __launch_bounds__(kThreads) void selective_bwd_slice_kernel(const float* part, int64_t units,
-                                                                       int64_t width, float* slices) {
+                                                                       const int* n_units, int64_t width,
+                                                                       float* slices) {
   const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (c >= width) return;
+  if (n_units) units = *n_units;  // packed varlen: the units the planner made
   const int64_t k = blockIdx.y, u0 = k * units / kSumSlices, u1 = (k + 1) * units / kSumSlices;
   float acc = 0.0f;
   for (int64_t u = u0; u < u1; ++u) acc += part[u * width + c];
@@ -973,13 +1015,22 @@ hipError_t launch_selective_scan(const SelectiveScanArgs& a, hipStream_t s) {
 
 namespace {
 struct BwdLayout {
-  int64_t nseg, U, nblk;
+  int64_t nseg, U, nblk;          // U: units (packed varlen: an upper bound)
   size_t state, row, bc, slices;  // bytes of one [U][N][D], [U][D], [nblk][B L][N], [kSumSlices][N][D] buffer
+  size_t tbl, seqtbl;             // packed varlen: unit table (after a 256-byte count), per-sequence table
 };
 BwdLayout bwd_layout(const SelectiveBwdArgs& a) {
   BwdLayout l;
-  l.nseg = (a.L + kBT - 1) / kBT;
-  l.U = a.B * l.nseg;
+  if (a.cu_seqlens == nullptr) {
+    l.nseg = (a.L + kBT - 1) / kBT;
+    l.U = a.B * l.nseg;
+    l.tbl = l.seqtbl = 0;
+  } else {
+    l.nseg = 0;
+    l.U = (a.L + kBT - 1) / kBT + a.nseq;  // sum over sequences of ceil(len / kBT)
+    l.tbl = align256(256 + (size_t)l.U * sizeof(int2));
+    l.seqtbl = align256((size_t)a.nseq * sizeof(int2));
+  }
   l.nblk = (a.D + kThreads - 1) / kThreads;
   l.state = align256((size_t)(l.U * a.N * a.D) * sizeof(float));
   l.row = align256((size_t)(l.U * a.D) * sizeof(float));
@@ -1011,7 +1062,7 @@ void launch_fwd_carry_t(const SelParams& f, int64_t U, bool softplus, hipStream_
 
 size_t selective_scan_backward_scratch_bytes(const SelectiveBwdArgs& a) {
   const BwdLayout l = bwd_layout(a);
-  return 5 * l.state + 2 * l.row + 2 * l.bc + l.slices;
+  return 5 * l.state + 2 * l.row + 2 * l.bc + l.slices + l.tbl + l.seqtbl;
 }
 
 hipError_t launch_selective_scan_backward(const SelectiveBwdArgs& a, hipStream_t s) {
@@ -1027,11 +1078,22 @@ hipError_t launch_selective_scan_backward(const SelectiveBwdArgs& a, hipStream_t
   float* PB = reinterpret_cast<float*>(base + 5 * l.state + 2 * l.row);
   float* PC = reinterpret_cast<float*>(base + 5 * l.state + 2 * l.row + l.bc);
   float* slices = reinterpret_cast<float*>(base + 5 * l.state + 2 * l.row + 2 * l.bc);  // kSumSlices x (N D)
+  char* tbl = base + 5 * l.state + 2 * l.row + 2 * l.bc + l.slices;
+  int* n_units = nullptr;
+  int2 *units = nullptr, *seq_units = nullptr;
+  const int64_t nseq = a.cu_seqlens ? a.nseq : a.B;
+  if (a.cu_seqlens) {  // the forward's planner at segment kBT (no h_last to fill)
+    n_units = reinterpret_cast<int*>(tbl);
+    units = reinterpret_cast<int2*>(tbl + 256);
+    seq_units = reinterpret_cast<int2*>(tbl + l.tbl);
+    hipLaunchKernelGGL(selective_plan_kernel, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.nseq, (int64_t)kBT, units,
+                       n_units, seq_units, a.D, a.N, a.h0, (float*)nullptr);
+  }
   // 1. the state entering every segment: the forward's aggregate and carry passes at segment kBT
-  if (l.nseg > 1) {
+  if (a.cu_seqlens || l.nseg > 1) {
     SelParams f{};
-    f.L = a.L; f.D = a.D; f.N = a.N; f.nseq = a.B; f.T = kBT; f.nseg = l.nseg;
-    f.cu = nullptr; f.units = nullptr; f.n_units = nullptr; f.seq_units = nullptr;
+    f.L = a.L; f.D = a.D; f.N = a.N; f.nseq = nseq; f.T = kBT; f.nseg = l.nseg;
+    f.cu = a.cu_seqlens; f.units = units; f.n_units = n_units; f.seq_units = seq_units;
     f.x = a.x; f.dt = a.dt; f.A = a.A; f.Bm = a.Bm; f.Cm = a.Cm; f.dt_bias = a.dt_bias; f.h0 = a.h0;
     f.aggP = aggP; f.aggH = aggQ; f.carry = carry;
     if (a.in_bf16) launch_fwd_carry_t<bf16_t>(f, l.U, a.dt_softplus != 0, s);
@@ -1040,15 +1102,16 @@ hipError_t launch_selective_scan_backward(const SelectiveBwdArgs& a, hipStream_t
   // 2.-4.
   SelBwdParams q{};
   q.L = a.L; q.D = a.D; q.nseg = l.nseg; q.nblk = l.nblk; q.BL = a.B * a.L;
+  q.cu = a.cu_seqlens; q.units = units; q.n_units = n_units; q.seq_units = seq_units;
   q.x = a.x; q.dt = a.dt; q.A = a.A; q.Bm = a.Bm; q.Cm = a.Cm; q.Dskip = a.Dskip; q.z = a.z; q.dt_bias = a.dt_bias;
   q.h0 = a.h0; q.dy = a.dy; q.dh_last = a.dh_last;
   q.carry = carry; q.aggP = aggP; q.aggQ = aggQ; q.qend = qend;
   q.dx = a.dx; q.ddt = a.ddt; q.dz = a.dz; q.dBm_part = PB; q.dCm_part = PC;
   q.dA_part = dA_part; q.dD_part = dD_part; q.dbias_part = dbias_part; q.dh0 = a.dh0;
   const bool sp = a.dt_softplus != 0, gate = a.z != nullptr;
-  if (!a.in_bf16) launch_bwd_t<float, float>(q, a.N, l.U, a.B, sp, gate, s);
-  else if (a.out_bf16) launch_bwd_t<bf16_t, bf16_t>(q, a.N, l.U, a.B, sp, gate, s);
-  else launch_bwd_t<bf16_t, float>(q, a.N, l.U, a.B, sp, gate, s);
+  if (!a.in_bf16) launch_bwd_t<float, float>(q, a.N, l.U, nseq, sp, gate, s);
+  else if (a.out_bf16) launch_bwd_t<bf16_t, bf16_t>(q, a.N, l.U, nseq, sp, gate, s);
+  else launch_bwd_t<bf16_t, float>(q, a.N, l.U, nseq, sp, gate, s);
   // 5. fixed-order sums
   const int64_t nbc = a.B * a.L * a.N;
   const dim3 blk(kThreads);
@@ -1061,7 +1124,8 @@ hipError_t launch_selective_scan_backward(const SelectiveBwdArgs& a, hipStream_t
   // (the three sums use the slice buffer in turn; width <= N D)
   auto sum_units = [&](const float* part, int64_t width, int64_t n, float* out) {
     const unsigned nb = (unsigned)((width + kThreads - 1) / kThreads);
-    hipLaunchKernelGGL(selective_bwd_slice_kernel, dim3(nb, kSumSlices), blk, 0, s, part, l.U, width, slices);
+    hipLaunchKernelGGL(selective_bwd_slice_kernel, dim3(nb, kSumSlices), blk, 0, s, part, l.U,
+                       (const int*)n_units, width, slices);
     hipLaunchKernelGGL(selective_bwd_final_kernel, dim3(nb), blk, 0, s, slices, width, n, out);
   };
   sum_units(dA_part, a.N * a.D, a.N, a.dA);

@@ -296,3 +296,44 @@ def test_selective_backward_full_width_bf16():
     """All 1536 channels of the headline workload (6 channel blocks summed for dB / dC), its multi-scale
     A, softplus steps, gate and skip, over 256 steps."""
     run_sel_bwd(2, 256, 1536, 16, synth.BF16, 7600)
+
+
+
+def test_selective_backward_varlen_matches_per_sequence_oracle():
+    """Packed sequences (incl. empty and single-row ones) are independent (reading R7): the reference is
+    the gradient oracle run on each sequence alone, compared per sequence (against that sequence's RMS:
+    a one-row sequence's gradients are ~100x the others'); dA, dDskip and ddt_bias add over the
+    sequences."""
+    import torch
+    lengths = [37, 0, 1, 64, 100, 16, 17]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    L, D, N = int(cu[-1]), 96, 16
+    inp = synth.selective_inputs(1, L, D, N, synth.F32, 7700, cu_seqlens=cu, with_h0=True)
+    rng = np.random.default_rng(7707)
+    bias = (rng.standard_normal(D) * 0.1).astype(np.float32)
+    dy = rng.standard_normal((1, L, D)).astype(np.float32)
+    nseq = len(lengths)
+    dhl = rng.standard_normal((nseq, D, N)).astype(np.float32)
+    t = {n: to_dev(inp.t[n]) for n in inp.t}
+    G = ssd.selective_scan_backward(t["x"], t["dt"], to_dev(inp.p["A"]), t["Bm"], t["Cm"], to_dev(dy),
+                                    Dskip=to_dev(inp.p["Dskip"]), z=t["z"], dt_bias=to_dev(bias),
+                                    h0=to_dev(inp.p["h0"]), dh_last=to_dev(dhl), cu_seqlens=cu)
+    torch.cuda.synchronize()
+    pooled = {k: 0.0 for k in ("dA", "dDskip", "ddt_bias")}
+    for sq in range(nseq):
+        a, b = int(cu[sq]), int(cu[sq + 1])
+        if b == a:
+            assert np.array_equal(host(G["dh0"])[sq], dhl[sq].astype(np.float64)), "empty sequence: dh0 = dh_last"
+            continue
+        sl = lambda arr: f64(arr)[:, a:b]
+        R = og.selective_scan_grads(sl(inp.t["x"]), sl(inp.t["dt"]), f64(inp.p["A"]), sl(inp.t["Bm"]),
+                                    sl(inp.t["Cm"]), dy[:, a:b].astype(np.float64), Dskip=f64(inp.p["Dskip"]),
+                                    z=sl(inp.t["z"]), dt_bias=bias.astype(np.float64), h0=f64(inp.p["h0"])[sq:sq + 1],
+                                    dh_last=dhl[sq:sq + 1].astype(np.float64))
+        for k in ("dx", "ddt", "dBm", "dCm", "dz"):
+            assert_close(host(G[k])[:, a:b], R[k], TOLB[synth.F32], f"{k} of sequence {sq}")
+        assert_close(host(G["dh0"])[sq], R["dh0"][0], TOLB[synth.F32], f"dh0 of sequence {sq}")
+        for k in pooled:
+            pooled[k] = pooled[k] + R[k]
+    for k, v in pooled.items():
+        assert_close(host(G[k]), v, TOLB[synth.F32], k)
