@@ -19,7 +19,11 @@ forward loop written from the recurrence:
       h_t = abar h_{t-1} + (delta B_t) x_t,  y_t = (sum_n C_t,n h_t,n + Dskip x_t) silu(z_t);
       the clamp passes the gradient where delta A <= 20 (torch.clamp).
 
-The loss whose gradient is returned is  sum(dy * y) + sum(dh_last * h_last) (x_last for MinMax).
+  HGRN2 (frankenstein-transformer documentation, "HGRN2 Attention", state update and gate):
+      g = lb + (1 - lb) sigmoid(g_logit),  S[i][j] = g_i S[i][j] + v_i k_j,  o_i = sum_j S[i][j] q_j.
+
+The loss whose gradient is returned is  sum(dy * y) + sum(dh_last * h_last) (x_last for MinMax;
+do and dS_last for HGRN2).
 """
 from __future__ import annotations
 
@@ -126,4 +130,31 @@ def selective_scan_grads(x, dt, A, Bm, Cm, dy, Dskip=None, z=None, dt_bias=None,
             names.append(nm)
             inputs.append(tsr)
     grads = torch.autograd.grad(loss, inputs, allow_unused=True)
+    return {nm: (np.zeros(tsr.shape) if g is None else g.detach().numpy()) for nm, g, tsr in zip(names, grads, inputs)}
+
+
+def hgrn2_scan_grads(q, k, v, g_logit, lower_bound, do, S0=None, dS_last=None):
+    """Gradients of the HGRN2 scan (frankenstein-transformer documentation, "HGRN2 Attention": the gate
+    g = lb + (1 - lb) sigmoid(g_logit) scales row i of the state, S[i][j] = g_i S[i][j] + v_i k_j, and
+    the readout is o_i = sum_j S[i][j] q_j including the current token) for the loss
+    sum(do * o) + sum(dS_last * S_last).  Shapes: q, k, v, g_logit, do [B,L,H,d]; S0, dS_last [B,H,d,d].
+    Returns float64 dq, dk, dv, dg_logit [B,L,H,d] and dS0 [B,H,d,d] (of a zero state when S0 is None)."""
+    import torch
+    qs, ks, vs, gs = _t(q), _t(k), _t(v), _t(g_logit)
+    B, L, H, d = qs.shape
+    S = _t(S0) if S0 is not None else torch.zeros((B, H, d, d), dtype=torch.float64, requires_grad=True)
+    S_init = S
+    lb = float(lower_bound)
+    os_ = []
+    for t in range(L):
+        g = lb + (1.0 - lb) * torch.sigmoid(gs[:, t])                          # [B,H,d] over rows i
+        S = g[..., :, None] * S + vs[:, t, :, :, None] * ks[:, t, :, None, :]  # row i scaled, v_i k_j added
+        os_.append((S * qs[:, t, :, None, :]).sum(-1))                        # o_i = sum_j S[i][j] q_j
+    o = torch.stack(os_, dim=1) if L > 0 else torch.zeros((B, 0, H, d), dtype=torch.float64)
+    loss = (o * torch.as_tensor(np.asarray(do, dtype=np.float64))).sum()
+    if dS_last is not None:
+        loss = loss + (S * torch.as_tensor(np.asarray(dS_last, dtype=np.float64))).sum()
+    inputs = [qs, ks, vs, gs, S_init]
+    grads = torch.autograd.grad(loss, inputs, allow_unused=True)
+    names = ["dq", "dk", "dv", "dg_logit", "dS0"]
     return {nm: (np.zeros(tsr.shape) if g is None else g.detach().numpy()) for nm, g, tsr in zip(names, grads, inputs)}

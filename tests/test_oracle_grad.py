@@ -175,3 +175,70 @@ def test_selective_clamp_passes_no_gradient_closed_form():
     assert np.isclose(G["ddt"][0, 1, 0], G2 * B1 * x1, rtol=1e-12, atol=0)
     assert np.isclose(G["ddt"][0, 0, 0], G1 * (a * e0 * c + B0 * x0), rtol=1e-12, atol=0)
     assert np.isclose(G["dh0"][0, 0, 0], G1 * e0, rtol=1e-12, atol=0)
+
+
+def _hgrn2_case(seed, B=1, L=5, H=2, d=3, lb=0.3):
+    rng = np.random.default_rng(seed)
+    q, k, v, gl, do = (rng.standard_normal((B, L, H, d)) for _ in range(5))
+    S0, dSl = rng.standard_normal((B, H, d, d)), rng.standard_normal((B, H, d, d))
+    return dict(q=q, k=k, v=v, g_logit=gl, S0=S0), do, dSl, lb
+
+
+def test_hgrn2_grads_match_central_differences():
+    k, do, dSl, lb = _hgrn2_case(41)
+    G = og.hgrn2_scan_grads(k["q"], k["k"], k["v"], k["g_logit"], lb, do, S0=k["S0"], dS_last=dSl)
+
+    def F(**over):
+        a = dict(k, **over)
+        o, Sl = oracle.hgrn2_scan(a["q"], a["k"], a["v"], a["g_logit"], lb, S0=a["S0"])
+        return float(np.sum(o * do) + np.sum(Sl * dSl))
+
+    eps = 1e-6
+    for arg, gname in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("g_logit", "dg_logit"), ("S0", "dS0")):
+        base = k[arg]
+        num = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            p, m = base.copy(), base.copy()
+            p[idx] += eps
+            m[idx] -= eps
+            num[idx] = (F(**{arg: p}) - F(**{arg: m})) / (2 * eps)
+        err = np.max(np.abs(num - G[gname])) / max(np.max(np.abs(num)), 1e-12)
+        assert err < 1e-6, (gname, err)
+
+
+def test_hgrn2_grads_without_decay_are_linear_attention_closed_form():
+    """lb = 1 makes g = 1: o_t = S0 q_t + sum_{s<=t} v_s (k_s . q_t) (causal linear attention), so, by hand,
+    dq_t = S0^T do_t + sum_{s<=t} k_s (v_s . do_t), dk_s = sum_{t>=s} q_t (v_s . do_t) + dS_last^T v_s,
+    dv_s = sum_{t>=s} do_t (k_s . q_t) + dS_last k_s, dS0 = sum_t do_t q_t^T + dS_last, dg_logit = 0."""
+    k, do, dSl, _ = _hgrn2_case(43, B=1, L=6, H=1, d=4)
+    q, kk, v, S0 = k["q"][0, :, 0], k["k"][0, :, 0], k["v"][0, :, 0], k["S0"][0, 0]
+    dO, dS = do[0, :, 0], dSl[0, 0]
+    G = og.hgrn2_scan_grads(k["q"], k["k"], k["v"], k["g_logit"], 1.0, do, S0=k["S0"], dS_last=dSl)
+    L = q.shape[0]
+    dq = np.array([S0.T @ dO[t] + sum(kk[s] * (v[s] @ dO[t]) for s in range(t + 1)) for t in range(L)])
+    dk = np.array([sum(q[t] * (v[s] @ dO[t]) for t in range(s, L)) + dS.T @ v[s] for s in range(L)])
+    dv = np.array([sum(dO[t] * (kk[s] @ q[t]) for t in range(s, L)) + dS @ kk[s] for s in range(L)])
+    dS0 = sum(np.outer(dO[t], q[t]) for t in range(L)) + dS
+    assert np.allclose(G["dq"][0, :, 0], dq, rtol=1e-12, atol=1e-12)
+    assert np.allclose(G["dk"][0, :, 0], dk, rtol=1e-12, atol=1e-12)
+    assert np.allclose(G["dv"][0, :, 0], dv, rtol=1e-12, atol=1e-12)
+    assert np.allclose(G["dS0"][0, 0], dS0, rtol=1e-12, atol=1e-12)
+    assert np.all(G["dg_logit"] == 0.0)
+
+
+def test_hgrn2_decay_only_closed_form():
+    """v = 0 and do = 0: S_L = diag(prod_t g_t) S0, so with L = sum(dS_last * S_L):
+    dS0 = diag(prod g) dS_last and dg_logit_t[i] = c_i (1 - lb) sigmoid'(x_t[i]) / g_t[i] with
+    c_i = sum_j dS_last[i][j] S_L[i][j]; q and k get no gradient."""
+    k, _, dSl, lb = _hgrn2_case(47, B=1, L=4, H=1, d=3, lb=0.25)
+    z = np.zeros_like(k["v"])
+    G = og.hgrn2_scan_grads(k["q"], k["k"], z, k["g_logit"], lb, z, S0=k["S0"], dS_last=dSl)
+    x = k["g_logit"][0, :, 0]
+    sig = 1.0 / (1.0 + np.exp(-x))
+    g = lb + (1 - lb) * sig
+    P = np.prod(g, axis=0)
+    SL = P[:, None] * k["S0"][0, 0]
+    c = np.sum(dSl[0, 0] * SL, axis=1)
+    assert np.allclose(G["dS0"][0, 0], P[:, None] * dSl[0, 0], rtol=1e-13, atol=0)
+    assert np.allclose(G["dg_logit"][0, :, 0], c[None, :] * (1 - lb) * sig * (1 - sig) / g, rtol=1e-12, atol=0)
+    assert np.all(G["dq"] == 0.0) and np.all(G["dk"] == 0.0)
