@@ -12,6 +12,7 @@
  *   selective     N <= 16 states per channel        ssd_selective_scan / ssd_selective_update
  *                 (gradients)                       ssd_selective_scan_backward
  *   HGRN2         d x d matrix state per head       ssd_hgrn2_scan / ssd_hgrn2_update
+ *                 (gradients)                       ssd_hgrn2_scan_backward
  *
  * Conventions (every entry point):
  *   - Sizes are int64_t element counts; every pointer is DEVICE memory owned by
@@ -288,6 +289,28 @@ int ssd_selective_update(int64_t B, int64_t D, int64_t N, int in_dtype, int out_
 int ssd_hgrn2_scan(int64_t B, int64_t L, int64_t H, int64_t d, int in_dtype, int out_dtype,
                    const void* q, const void* k, const void* v, const void* g_logit,
                    float lower_bound, const float* S0, void* o, float* S_last, void* stream);
+
+/* Gradients of ssd_hgrn2_scan for the loss  sum do * o + sum dS_last * S_last.  The page trains
+ * through autograd and prints no backward pass; this is the gradient of the definition above.  With
+ * R_t = dL/dS_t (R_t = do_t q_t^T + diag(g_{t+1}) R_{t+1}, R_{L-1} = do_{L-1} q_{L-1}^T + dS_last):
+ *   dq_t = S_t^T do_t,   dk_t = R_t^T v_t,   dv_t = R_t k_t,   dS0 = diag(g_0) R_0,
+ *   dg_logit_t = c_t (1 - lower_bound) sigmoid'(g_logit_t) / g_t  with
+ *   c_t[i] = sum_{u >= t} (do_u[i] o_u[i] - v_u[i] dv_u[i]) + sum_j dS_last[i][j] S_last[i][j]
+ *   (c_t is the derivative with respect to log g_t; 0 where sigmoid(g_logit) is 0).
+ *   inputs            : as ssd_hgrn2_scan (S0 [B, H, d, d] fp32 or NULL), plus
+ *   o                 : [B, L, H, d] fp32, the forward output for these inputs, or NULL (then it is
+ *                       recomputed into the scratch buffer: B * L * H * d fp32 more)
+ *   dO                : [B, L, H, d] (in dtype);  dS_last : [B, H, d, d] fp32 or NULL (= 0)
+ *   dq, dk, dv, dg_logit : [B, L, H, d] (out dtype);  dS0 : [B, H, d, d] fp32 or NULL
+ * Any lower_bound in [0, 1] (no decay ratios are formed).  Every output is overwritten.  The scratch
+ * holds S_last (B * H * d * d fp32) and, for fp32 inputs, the state after every 32nd token (from
+ * which the running sum c_t is restarted exactly: B * H * floor((L - 1) / 32) * d * d fp32).  Errors as ssd_hgrn2_scan, plus SSD_ERR_NULL for missing dO, dq,
+ * dk, dv or dg_logit. */
+int ssd_hgrn2_scan_backward(int64_t B, int64_t L, int64_t H, int64_t d, int in_dtype, int out_dtype,
+                            const void* q, const void* k, const void* v, const void* g_logit,
+                            float lower_bound, const float* S0, const float* o, const void* dO,
+                            const float* dS_last, void* dq, void* dk, void* dv, void* dg_logit,
+                            float* dS0, void* stream);
 
 /* One HGRN2 decode step.  q, k, v, g_logit, o : [B, H, d];  S : [B, H, d, d] fp32 in place.
  * Errors as ssd_hgrn2_scan. */

@@ -33,7 +33,7 @@ EXPORTS = ("ssd_status_str", "ssd_last_error", "ssd_version", "ssd_rglru_scan", 
            "ssd_rglru_update",
            "ssd_selective_scan", "ssd_selective_update", "ssd_hgrn2_scan", "ssd_hgrn2_update", "ssd_minmax_scan",
            "ssd_minmax_update", "ssd_minmax_scan_backward", "ssd_causal_conv1d", "ssd_causal_conv1d_update",
-           "ssd_selective_scan_backward")
+           "ssd_selective_scan_backward", "ssd_hgrn2_scan_backward")
 
 
 class SSDError(RuntimeError):
@@ -91,6 +91,8 @@ def lib() -> ctypes.CDLL:
                                      ctypes.c_float, _fp, _vp, _fp, _vp]
         L.ssd_hgrn2_update.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp,
                                        ctypes.c_float, _fp, _vp, _vp]
+        L.ssd_hgrn2_scan_backward.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                              ctypes.c_float, _fp, _fp, _vp, _fp, _vp, _vp, _vp, _vp, _fp, _vp]
         for name in EXPORTS[3:]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -447,6 +449,28 @@ def hgrn2_scan(q, k, v, g_logit, lower_bound: float, S0=None, return_last_state:
                               _stream(q.device))
     _raise(st, "hgrn2_scan")
     return (o, S_last) if return_last_state else o
+
+
+def hgrn2_scan_backward(q, k, v, g_logit, lower_bound: float, do, S0=None, dS_last=None, o=None, out_dtype=None):
+    """Gradients of ``hgrn2_scan`` for the loss sum(do * o) + sum(dS_last * S_last) (see
+    ``ssd_hgrn2_scan_backward``).  ``o`` may pass the forward's fp32 output to save recomputing it.
+    Returns a dict: dq, dk, dv, dg_logit [B, L, H, d] (out dtype) and dS0 [B, H, d, d] (fp32)."""
+    torch = _torch()
+    B, L, H, d = q.shape
+    code = _act([q, k, v, g_logit, do], ["q", "k", "v", "g_logit", "do"])
+    oc = _out_code(out_dtype)
+    odt = torch.bfloat16 if oc == SSD_BF16 else torch.float32
+    dev = q.device
+    g = {n: torch.empty((B, L, H, d), device=dev, dtype=odt) for n in ("dq", "dk", "dv", "dg_logit")}
+    g["dS0"] = torch.empty((B, H, d, d), device=dev, dtype=torch.float32)
+    st = lib().ssd_hgrn2_scan_backward(
+        B, L, H, d, code, oc, _dev(q, "q"), _dev(k, "k", q.shape), _dev(v, "v", q.shape),
+        _dev(g_logit, "g_logit", q.shape), float(lower_bound), _dev(S0, "S0", (B, H, d, d), torch.float32),
+        _dev(o, "o", q.shape, torch.float32), _dev(do, "do", q.shape),
+        _dev(dS_last, "dS_last", (B, H, d, d), torch.float32), _dev(g["dq"], "dq"), _dev(g["dk"], "dk"),
+        _dev(g["dv"], "dv"), _dev(g["dg_logit"], "dg_logit"), _dev(g["dS0"], "dS0"), _stream(dev))
+    _raise(st, "hgrn2_scan_backward")
+    return g
 
 
 def hgrn2_update(q, k, v, g_logit, lower_bound: float, S, out_dtype=None):

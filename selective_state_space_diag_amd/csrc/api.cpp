@@ -35,7 +35,8 @@ int ok() {
 // process exit.  Purposes are kept apart so that one kernel family never reads another's data.
 // RG-LRU and MinMax share a kind: their launches use the same epoch-tagged lookback protocol, so
 // words left by one never validate for the next launch on the stream.
-enum ScratchKind { kScratchScan1 = 0, kScratchSelective = 1, kScratchScan1Bwd = 2, kScratchSelectiveBwd = 3 };
+enum ScratchKind { kScratchScan1 = 0, kScratchSelective = 1, kScratchScan1Bwd = 2, kScratchSelectiveBwd = 3,
+                   kScratchHgrn2Bwd = 4 };
 
 struct ScratchBuf {
   void* ptr = nullptr;
@@ -549,6 +550,40 @@ int ssd_hgrn2_update(int64_t B, int64_t H, int64_t d, int in_dtype, int out_dtyp
   if (n == 0) return ok();
   ssd::Hgrn2UpdateArgs a{B, H, d, in_dtype == SSD_BF16, out_dtype == SSD_BF16, q, k, v, g_logit, lower_bound, S, o};
   return hip_status(ssd::launch_hgrn2_update(a, static_cast<hipStream_t>(stream)), "hgrn2_update launch");
+}
+
+int ssd_hgrn2_scan_backward(int64_t B, int64_t L, int64_t H, int64_t d, int in_dtype, int out_dtype, const void* q,
+                            const void* k, const void* v, const void* g_logit, float lower_bound, const float* S0,
+                            const float* o, const void* dO, const float* dS_last, void* dq, void* dk, void* dv,
+                            void* dg_logit, float* dS0, void* stream) {
+  SSD_TRY(check_dtypes(in_dtype, out_dtype));
+  if (B < 0 || L < 0 || H < 0 || d < 0) return fail(SSD_ERR_SHAPE, "negative size");
+  if (!supported_d(d)) return fail(SSD_ERR_SHAPE, "head dim d must be 16, 32, 64 or 128");
+  if (too_big({B, L, H, d}) || B * H >= (int64_t)1 << 30) return fail(SSD_ERR_SHAPE, "problem too large");
+  if (!(lower_bound >= 0.0f && lower_bound <= 1.0f)) return fail(SSD_ERR_VALUE, "lower_bound must be in [0, 1]");
+  const int64_t nact = B * L * H * d;
+  if (nact > 0 && (!q || !k || !v || !g_logit || !dO))
+    return fail(SSD_ERR_NULL, "q, k, v, g_logit and dO are required");
+  if (nact > 0 && (!dq || !dk || !dv || !dg_logit))
+    return fail(SSD_ERR_NULL, "dq, dk, dv and dg_logit are required");
+  const size_t ab = (size_t)nact * esize(in_dtype), ob = (size_t)nact * esize(out_dtype);
+  const size_t sb = (size_t)(B * H * d * d) * 4;
+  std::vector<Span> ins = {{"q", q, ab},           {"k", k, ab},   {"v", v, ab},
+                           {"g_logit", g_logit, ab}, {"S0", S0, sb}, {"o", o, (size_t)nact * 4},
+                           {"dO", dO, ab},         {"dS_last", dS_last, sb}};
+  std::vector<Span> outs = {{"dq", dq, ob}, {"dk", dk, ob}, {"dv", dv, ob}, {"dg_logit", dg_logit, ob},
+                            {"dS0", dS0, sb}};
+  std::vector<Span> all = ins;
+  all.insert(all.end(), outs.begin(), outs.end());
+  SSD_TRY(check_align(all));
+  SSD_TRY(check_alias(outs, ins));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (B * H == 0) return ok();
+  if (L == 0) return hip_status(ssd::launch_copy_or_zero(dS0, dS_last, B * H * d * d, s), "hgrn2_scan_backward");
+  ssd::Hgrn2BwdArgs a{B,  L,  H,  d,  in_dtype == SSD_BF16, out_dtype == SSD_BF16, q, k, v, g_logit, lower_bound,
+                      S0, o,  dO, dS_last, dq, dk, dv, dg_logit, dS0, nullptr};
+  SSD_TRY(get_scratch(stream, kScratchHgrn2Bwd, ssd::hgrn2_scan_backward_scratch_bytes(a), &a.scratch));
+  return hip_status(ssd::launch_hgrn2_scan_backward(a, s), "hgrn2_scan_backward launch");
 }
 
 }  // extern "C"

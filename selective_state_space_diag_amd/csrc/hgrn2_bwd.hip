@@ -1,0 +1,444 @@
+// hgrn2_bwd.hip -- backward of the HGRN2 matrix-state scan for gfx950.
+//
+// Forward (frankenstein-transformer documentation, "HGRN2 Attention", state update and gate):
+//   g_t = lb + (1 - lb) sigmoid(x_t),  S_t[i][j] = g_t[i] S_{t-1}[i][j] + v_t[i] k_t[j],
+//   o_t[i] = sum_j S_t[i][j] q_t[j]          (the gate scales row i, the value index).
+// For the loss sum(do . o) + sum(dS_last . S_L), the adjoint of S_t is
+//   R_t = do_t q_t^T + diag(g_{t+1}) R_{t+1},   R_{L-1} = do_{L-1} q_{L-1}^T + dS_last,
+// and the gradients are
+//   dq_t = S_t^T do_t,   dk_t = R_t^T v_t,   dv_t = R_t k_t,   dS0 = diag(g_0) R_0,
+//   dlog g_t[i] = sum_{u >= t} (do_u[i] o_u[i] - v_u[i] dv_u[i]) + sum_j dS_last[i][j] S_L[i][j].
+// The last line: with beta_t = sum_{w <= t} log g_w, every term of o_u[i] and of S_L[i][:] carries
+// exp(beta_u[i]) (exp(beta_{L-1}[i])) and every input v_s[i] carries exp(-beta_s[i]); the
+// derivative with respect to beta_t is therefore do_t o_t - v_t dv_t (plus the S_L term at the
+// last token), and log g_w enters every beta_t with t >= w.  Then
+//   dx_t = dlog g_t (1 - lb) sigmoid(x_t) (1 - sigmoid(x_t)) / g_t.
+//
+// The suffix sum adds one rounded term per token and nothing makes old errors decay, so for fp32
+// inputs (1e-5 error budget) the sum is restarted exactly every kAnchor tokens: dlog g_t equals
+// g_t sum_j R_t[i][j] S_{t-1}[i][j] = sum_j R_t[i][j] S_t[i][j] - v_t[i] dv_t[i], with S_t taken from
+// checkpoints that kDQ writes.  bf16 inputs (2e-2 budget) skip the checkpoints.  The first token
+// is always exact: dlog g_0 = g_0 sum_j R_0[i][j] S0[i][j] (0 without an initial state).
+//
+// Three sweeps, each a sequential pass over the tokens of one head that keeps a d x d matrix in
+// registers and needs no cross-row sums beyond 16 lanes:
+//   kDQ  forward, S column-owned:  S[i][j] update, dq_t[j] = sum_i do_t[i] S_t[i][j]; writes S_L;
+//   kDK  reverse, R column-owned:  R[i][j] update, dk_t[j] = sum_i v_t[i] R_t[i][j];
+//   kDV  reverse, R row-owned:     R[i][j] update, dv_t[i] = sum_j R_t[i][j] k_t[j], the running
+//        dlog g (from o, dv and S_L), dx_t and dS0.
+// Thread layout: a thread owns AB consecutive "a" indices (the owned axis: j for kDQ/kDK, i for
+// kDV) and the d/16 "m" indices of its part p = lane % 16 (the summed axis), so the sum over m is
+// a sum over the 16 lanes of a row group.  The per-token vectors of the head (gates, q, k, v, do,
+// o) are staged in LDS, eight tokens per stage, double-buffered: the next stage's loads are
+// issued before the current stage is computed and written to LDS after it.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ssd {
+namespace {
+
+enum { kDQ = 0, kDK = 1, kDV = 2 };
+constexpr int kTS = 8;     // tokens per stage
+constexpr int kParts = 16; // lanes that share the summed axis
+constexpr int kAnchor = 32; // tokens between exact restarts of the running dlog g (checkpointed states)
+
+struct H2BwdParams {
+  int64_t B, L, H;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* x;   // gate logits
+  const void* dO;
+  const float* o;  // forward output, fp32
+  float lb;
+  const float* S0;
+  const float* dS_last;
+  float* S_L;      // final state (written by kDQ, read by kDV)
+  float* ckpt;     // states after tokens kAnchor - 1, 2 kAnchor - 1, ... before the last, or NULL
+  void* dq;
+  void* dk;
+  void* dv;
+  void* dx;
+  float* dS0;
+};
+
+// What slot s of the staged vectors holds, per sweep.
+enum SlotKind { kAct = 0, kOut = 1, kGate = 2, kRatio = 3 };
+template <int MODE> struct Slots;
+template <> struct Slots<kDQ> {  // m = i: gate(t), v, do; a = j: k
+  static constexpr int n = 4;
+  static __device__ __forceinline__ int kind(int s) { return s == 0 ? kGate : kAct; }
+  static __device__ __forceinline__ int shift(int) { return 0; }
+  static __device__ __forceinline__ const void* src(const H2BwdParams& p, int s) {
+    return s == 0 ? p.x : s == 1 ? p.v : s == 2 ? p.dO : p.k;
+  }
+};
+template <> struct Slots<kDK> {  // m = i: gate(t+1), do, v; a = j: q
+  static constexpr int n = 4;
+  static __device__ __forceinline__ int kind(int s) { return s == 0 ? kGate : kAct; }
+  static __device__ __forceinline__ int shift(int s) { return s == 0 ? 1 : 0; }
+  static __device__ __forceinline__ const void* src(const H2BwdParams& p, int s) {
+    return s == 0 ? p.x : s == 1 ? p.dO : s == 2 ? p.v : p.q;
+  }
+};
+template <> struct Slots<kDV> {  // m = j: q, k; a = i: do, o, v, gate(t+1), ratio(t)
+  static constexpr int n = 7;
+  static __device__ __forceinline__ int kind(int s) {
+    return s == 3 ? kOut : s == 5 ? kGate : s == 6 ? kRatio : kAct;
+  }
+  static __device__ __forceinline__ int shift(int s) { return s == 5 ? 1 : 0; }
+  static __device__ __forceinline__ const void* src(const H2BwdParams& p, int s) {
+    return s == 0 ? p.q : s == 1 ? p.k : s == 2 ? p.dO : s == 3 ? (const void*)p.o : s == 4 ? p.v : p.x;
+  }
+};
+
+__device__ __forceinline__ float gate_of(float x, float lb) { return fmaf(1.0f - lb, sigmoid_f(x), lb); }
+// (1 - lb) sigmoid'(x) / g: the factor from dlog g to dx (0 where sigmoid(x) is 0, as in the
+// chain rule through sigmoid).
+__device__ __forceinline__ float ratio_of(float x, float lb) {
+  const float s = sigmoid_f(x);
+  const float g = fmaf(1.0f - lb, s, lb);
+  return s == 0.0f ? 0.0f : (1.0f - lb) * s * (1.0f - s) / g;
+}
+
+// Sum over the 16 lanes of a row group of AB per-lane values; lane p returns the total of value
+// p / (16 / AB) (every lane of that sub-group holds it).
+template <int AB>
+__device__ __forceinline__ float part_reduce(const float (&acc)[AB], int p) {
+  float v;
+  if constexpr (AB == 4) {
+    const bool lo8 = p < 8;
+    const float k0 = lo8 ? acc[0] : acc[2], k1 = lo8 ? acc[1] : acc[3];
+    const float s0 = lo8 ? acc[2] : acc[0], s1 = lo8 ? acc[3] : acc[1];
+    const float r0 = k0 + __shfl_xor(s0, 8), r1 = k1 + __shfl_xor(s1, 8);
+    const bool lo4 = (p & 4) == 0;
+    v = (lo4 ? r0 : r1) + __shfl_xor(lo4 ? r1 : r0, 4);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 1);
+  } else {
+    static_assert(AB == 2, "AB must be 2 or 4");
+    const bool lo8 = p < 8;
+    v = (lo8 ? acc[0] : acc[1]) + __shfl_xor(lo8 ? acc[1] : acc[0], 8);
+    v += __shfl_xor(v, 4);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 1);
+  }
+  return v;
+}
+
+template <int MP>
+__device__ __forceinline__ void lds_vec(const float* p, float (&r)[MP]) {
+  if constexpr (MP % 4 == 0) {
+#pragma unroll
+    for (int e = 0; e < MP; e += 4) {
+      const float4 f = *reinterpret_cast<const float4*>(p + e);
+      r[e] = f.x; r[e + 1] = f.y; r[e + 2] = f.z; r[e + 3] = f.w;
+    }
+  } else if constexpr (MP == 2) {
+    const float2 f = *reinterpret_cast<const float2*>(p);
+    r[0] = f.x; r[1] = f.y;
+  } else {
+#pragma unroll
+    for (int e = 0; e < MP; ++e) r[e] = p[e];
+  }
+}
+
+template <int DH, int AB> struct SweepShape {
+  static constexpr int MP = DH / kParts;          // summed-axis entries per thread
+  static constexpr int TH = DH / AB * kParts;     // threads per head
+  static constexpr int NT = TH < 256 ? TH : 256;  // threads per workgroup
+  static constexpr int W = TH / NT;               // workgroups per head
+  static constexpr int PER = kTS * DH / NT;       // staged elements per thread and slot
+  static_assert(DH % kParts == 0 && TH % NT == 0 && (kTS * DH) % NT == 0, "sweep shape");
+};
+
+template <int MODE, typename Tin, typename Tout, int DH, int AB>
+__global__ __launch_bounds__((SweepShape<DH, AB>::NT)) void hgrn2_bwd_sweep_kernel(H2BwdParams p) {
+  using SS = SweepShape<DH, AB>;
+  using SL = Slots<MODE>;
+  constexpr int MP = SS::MP, NT = SS::NT, PER = SS::PER, NV = SL::n;
+  constexpr bool REV = MODE != kDQ;
+  __shared__ __align__(16) float stg[2][NV][kTS][DH];
+
+  const int tid = threadIdx.x;
+  const int64_t head = blockIdx.x / SS::W;
+  const int wsub = (int)(blockIdx.x - head * SS::W);
+  const int64_t b = head / p.H, hh = head - b * p.H;
+  const int pp = tid & (kParts - 1);
+  const int a0 = ((wsub * NT + tid) / kParts) * AB;  // owned indices a0 .. a0 + AB - 1
+  const int m0 = pp * MP;                             // summed-axis indices m0 .. m0 + MP - 1
+  constexpr int SUB = kParts / AB;                    // lanes per owned index after the reduction
+  const int ustar = pp / SUB;                         // owned index whose total this lane receives
+  const bool writer = (pp % SUB) == 0;
+  const int64_t L = p.L;
+  const int64_t nstage = (L + kTS - 1) / kTS;
+  const int64_t row_stride = p.H * DH;                // elements between consecutive tokens
+  const int64_t head_base = (b * L * p.H + hh) * DH;  // token 0 of this head
+  const float lb = p.lb;
+  const int64_t nanch = (L - 1) / kAnchor;            // checkpointed states per head
+
+  // ---- staging: stage s covers tokens t0 .. t0 + kTS - 1 with t0 = s kTS (forward) or
+  // L - (s + 1) kTS (reverse; tokens below 0 are skipped)
+  float raw[NV][PER];
+  auto stage_t0 = [&](int64_t s) -> int64_t { return REV ? L - (s + 1) * kTS : s * kTS; };
+  auto fetch = [&](int64_t s) {
+    const int64_t t0 = stage_t0(s);
+#pragma unroll
+    for (int sl = 0; sl < NV; ++sl) {
+      const void* src = SL::src(p, sl);
+      const int kd = SL::kind(sl);
+#pragma unroll
+      for (int r = 0; r < PER; ++r) {
+        const int idx = tid + r * NT;
+        const int tau = idx / DH, c = idx - (idx / DH) * DH;
+        const int64_t t = t0 + tau + SL::shift(sl);
+        float val = 0.0f;
+        if (t >= 0 && t < L) {
+          const int64_t off = head_base + t * row_stride + c;
+          val = kd == kOut ? static_cast<const float*>(src)[off] : io<Tin>::load(src, off);
+        }
+        raw[sl][r] = val;
+      }
+    }
+  };
+  auto publish = [&](int64_t s, int buf) {
+    const int64_t t0 = stage_t0(s);
+#pragma unroll
+    for (int sl = 0; sl < NV; ++sl) {
+      const int kd = SL::kind(sl);
+#pragma unroll
+      for (int r = 0; r < PER; ++r) {
+        const int idx = tid + r * NT;
+        const int tau = idx / DH, c = idx - (idx / DH) * DH;
+        const int64_t t = t0 + tau + SL::shift(sl);
+        const bool in = t >= 0 && t < L;
+        float val = raw[sl][r];
+        if (kd == kGate) val = in ? gate_of(val, lb) : 1.0f;  // no gate past the ends
+        if (kd == kRatio) val = in ? ratio_of(val, lb) : 0.0f;
+        stg[buf][sl][tau][c] = val;
+      }
+    }
+  };
+
+  // ---- the matrix: M[x][y] with x over the rows this thread holds: for kDQ / kDK M[e][u] =
+  // matrix[m0 + e][a0 + u]; for kDV M[u][e] = R[a0 + u][m0 + e]; stored as mat[u][e] either way.
+  float mat[AB][MP];
+  const int64_t mbase = head * DH * DH;
+  // kDV: running dlog g of row a0 + ustar, a sum over all later tokens whose terms largely cancel:
+  // it is accumulated in fp64 so that its rounding does not grow with the sequence length
+  double cum = 0.0;
+  if constexpr (MODE == kDV) {
+    float part[AB];
+#pragma unroll
+    for (int u = 0; u < AB; ++u) {
+      part[u] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < MP; ++e) {
+        const int64_t off = mbase + (int64_t)(a0 + u) * DH + m0 + e;
+        const float ds = p.dS_last ? p.dS_last[off] : 0.0f;
+        mat[u][e] = ds;
+        part[u] = fmaf(ds, p.S_L[off], part[u]);
+      }
+    }
+    cum = (double)part_reduce<AB>(part, pp);
+  } else {
+    const float* init = MODE == kDQ ? p.S0 : p.dS_last;
+#pragma unroll
+    for (int u = 0; u < AB; ++u)
+#pragma unroll
+      for (int e = 0; e < MP; ++e)
+        mat[u][e] = init ? init[mbase + (int64_t)(m0 + e) * DH + a0 + u] : 0.0f;
+  }
+
+  if (nstage > 0) {
+    fetch(0);
+    publish(0, 0);
+  }
+  __syncthreads();
+  for (int64_t s = 0; s < nstage; ++s) {
+    const int buf = (int)(s & 1);
+    if (s + 1 < nstage) fetch(s + 1);
+    const int64_t t0 = stage_t0(s);
+#pragma unroll
+    for (int step = 0; step < kTS; ++step) {
+      const int tau = REV ? kTS - 1 - step : step;
+      const int64_t t = t0 + tau;
+      if (t < 0 || t >= L) continue;  // uniform across the workgroup
+      const int64_t out_off = head_base + t * row_stride;
+      float acc[AB];
+      if constexpr (MODE == kDV) {
+        float qv[MP], kv[MP], dov[AB], gn[AB];
+        lds_vec<MP>(&stg[buf][0][tau][m0], qv);
+        lds_vec<MP>(&stg[buf][1][tau][m0], kv);
+        lds_vec<AB>(&stg[buf][2][tau][a0], dov);
+        lds_vec<AB>(&stg[buf][5][tau][a0], gn);
+#pragma unroll
+        for (int u = 0; u < AB; ++u) {
+          acc[u] = 0.0f;
+#pragma unroll
+          for (int e = 0; e < MP; ++e) {
+            mat[u][e] = fmaf(gn[u], mat[u][e], dov[u] * qv[e]);
+            acc[u] = fmaf(mat[u][e], kv[e], acc[u]);
+          }
+        }
+        const float dvt = part_reduce<AB>(acc, pp);
+        const int ia = a0 + ustar;
+        const float dos = stg[buf][2][tau][ia], os = stg[buf][3][tau][ia], vs = stg[buf][4][tau][ia];
+        const float rt = stg[buf][6][tau][ia];
+        if (t == 0) {  // uniform: dlog g_0 = g_0 sum_j R_0[i][j] S0[i][j], exactly 0 without S0
+          float part[AB];
+#pragma unroll
+          for (int u = 0; u < AB; ++u) {
+            part[u] = 0.0f;
+#pragma unroll
+            for (int e = 0; e < MP; ++e)
+              part[u] = fmaf(mat[u][e], p.S0 ? p.S0[mbase + (a0 + u) * DH + m0 + e] : 0.0f, part[u]);
+          }
+          const float tot = part_reduce<AB>(part, pp);
+          cum = (double)(gate_of(io<Tin>::load(p.x, head_base + ia), lb) * tot);
+        } else if (p.ckpt && (t + 1) % kAnchor == 0 && t + 1 < L) {  // uniform
+          // restart the suffix sum exactly: dlog g_t = sum_j R_t[i][j] S_t[i][j] - v_t dv_t
+          const float* St = p.ckpt + (head * nanch + (t + 1) / kAnchor - 1) * DH * DH;
+          float part[AB];
+#pragma unroll
+          for (int u = 0; u < AB; ++u) {
+            part[u] = 0.0f;
+#pragma unroll
+            for (int e = 0; e < MP; ++e) part[u] = fmaf(mat[u][e], St[(a0 + u) * DH + m0 + e], part[u]);
+          }
+          cum = (double)fmaf(-vs, dvt, part_reduce<AB>(part, pp));
+        } else {
+          cum += (double)fmaf(dos, os, -vs * dvt);
+        }
+        if (writer) {
+          io<Tout>::store(p.dv, out_off + ia, dvt);
+          io<Tout>::store(p.dx, out_off + ia, (float)cum * rt);
+        }
+      } else {
+        float gv[MP], xv[MP], yv[MP], av[AB];
+        // kDQ: g(t), v, do over i and k over j:  S = g S + v k^T, dq = S^T do
+        // kDK: g(t+1), do, v over i and q over j: R = g R + do q^T, dk = R^T v
+        lds_vec<MP>(&stg[buf][0][tau][m0], gv);
+        lds_vec<MP>(&stg[buf][1][tau][m0], xv);
+        lds_vec<MP>(&stg[buf][2][tau][m0], yv);
+        lds_vec<AB>(&stg[buf][3][tau][a0], av);
+#pragma unroll
+        for (int u = 0; u < AB; ++u) {
+          acc[u] = 0.0f;
+#pragma unroll
+          for (int e = 0; e < MP; ++e) {
+            mat[u][e] = fmaf(gv[e], mat[u][e], xv[e] * av[u]);
+            acc[u] = fmaf(yv[e], mat[u][e], acc[u]);
+          }
+        }
+        const float tot = part_reduce<AB>(acc, pp);
+        if (writer) io<Tout>::store(MODE == kDQ ? p.dq : p.dk, out_off + a0 + ustar, tot);
+        if constexpr (MODE == kDQ) {
+          if (p.ckpt && (t + 1) % kAnchor == 0 && t + 1 < L) {  // uniform: state after token t
+            float* St = p.ckpt + (head * nanch + (t + 1) / kAnchor - 1) * DH * DH;
+#pragma unroll
+            for (int u = 0; u < AB; ++u)
+#pragma unroll
+              for (int e = 0; e < MP; ++e) St[(m0 + e) * DH + a0 + u] = mat[u][e];
+          }
+        }
+      }
+    }
+    if (s + 1 < nstage) publish(s + 1, buf ^ 1);
+    __syncthreads();
+  }
+
+  if constexpr (MODE == kDQ) {
+#pragma unroll
+    for (int u = 0; u < AB; ++u)
+#pragma unroll
+      for (int e = 0; e < MP; ++e) p.S_L[mbase + (int64_t)(m0 + e) * DH + a0 + u] = mat[u][e];
+  }
+  if constexpr (MODE == kDV) {
+    if (p.dS0) {
+      float g0[AB];
+#pragma unroll
+      for (int u = 0; u < AB; ++u)
+        g0[u] = L > 0 ? gate_of(io<Tin>::load(p.x, head_base + a0 + u), lb) : 1.0f;
+#pragma unroll
+      for (int u = 0; u < AB; ++u)
+#pragma unroll
+        for (int e = 0; e < MP; ++e) p.dS0[mbase + (int64_t)(a0 + u) * DH + m0 + e] = g0[u] * mat[u][e];
+    }
+  }
+}
+
+template <int MODE, typename Tin, typename Tout, int DH>
+void launch_sweep(const H2BwdParams& p, hipStream_t s) {
+  constexpr int AB = 4;
+  using SS = SweepShape<DH, AB>;
+  const dim3 grid((unsigned)(p.B * p.H * SS::W));
+  hipLaunchKernelGGL((hgrn2_bwd_sweep_kernel<MODE, Tin, Tout, DH, AB>), grid, dim3(SS::NT), 0, s, p);
+}
+
+template <int MODE, typename Tin, typename Tout>
+void launch_sweep_d(const H2BwdParams& p, int64_t d, hipStream_t s) {
+  switch (d) {
+    case 16: launch_sweep<MODE, Tin, Tout, 16>(p, s); break;
+    case 32: launch_sweep<MODE, Tin, Tout, 32>(p, s); break;
+    case 64: launch_sweep<MODE, Tin, Tout, 64>(p, s); break;
+    default: launch_sweep<MODE, Tin, Tout, 128>(p, s); break;
+  }
+}
+
+template <typename Tin, typename Tout>
+void launch_all(const H2BwdParams& p, int64_t d, hipStream_t s) {
+  launch_sweep_d<kDQ, Tin, Tout>(p, d, s);
+  launch_sweep_d<kDK, Tin, Tout>(p, d, s);
+  launch_sweep_d<kDV, Tin, Tout>(p, d, s);
+}
+
+}  // namespace
+
+namespace {
+// Scratch: [S_last][checkpoints (fp32 inputs)][recomputed o (when not given)], 256-byte aligned.
+struct BwdLayout {
+  size_t state, ckpt, outs;
+  explicit BwdLayout(const Hgrn2BwdArgs& a) {
+    const size_t dd = (size_t)(a.B * a.H * a.d * a.d) * 4;
+    state = (dd + 255) / 256 * 256;
+    // bf16 inputs carry a 2e-2 error budget, far above the suffix sum's rounding: no restarts
+    ckpt = a.in_bf16 ? 0 : ((size_t)((a.L - 1) / kAnchor) * dd + 255) / 256 * 256;
+    outs = a.o ? 0 : (size_t)(a.B * a.L * a.H * a.d) * 4;
+  }
+};
+}  // namespace
+
+size_t hgrn2_scan_backward_scratch_bytes(const Hgrn2BwdArgs& a) {
+  const BwdLayout lay(a);
+  return lay.state + lay.ckpt + lay.outs;
+}
+
+hipError_t launch_hgrn2_scan_backward(const Hgrn2BwdArgs& a, hipStream_t s) {
+  char* scratch = static_cast<char*>(a.scratch);
+  const BwdLayout lay(a);
+  float* S_L = reinterpret_cast<float*>(scratch);
+  float* ckpt = lay.ckpt ? reinterpret_cast<float*>(scratch + lay.state) : nullptr;
+  const float* o = a.o;
+  if (!o) {  // recompute the forward output in fp32
+    float* o_tmp = reinterpret_cast<float*>(scratch + lay.state + lay.ckpt);
+    Hgrn2ScanArgs f{a.B, a.L, a.H, a.d, a.in_bf16, 0, a.q, a.k, a.v, a.g_logit, a.lower_bound, a.S0, o_tmp, nullptr};
+    const hipError_t e = launch_hgrn2_scan(f, s);
+    if (e != hipSuccess) return e;
+    o = o_tmp;
+  }
+  H2BwdParams p;
+  p.B = a.B; p.L = a.L; p.H = a.H;
+  p.q = a.q; p.k = a.k; p.v = a.v; p.x = a.g_logit; p.dO = a.dO; p.o = o; p.lb = a.lower_bound;
+  p.S0 = a.S0; p.dS_last = a.dS_last; p.S_L = S_L; p.ckpt = ckpt;
+  p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.dx = a.dg_logit; p.dS0 = a.dS0;
+  if (!a.in_bf16)
+    launch_all<float, float>(p, a.d, s);
+  else if (a.out_bf16)
+    launch_all<bf16_t, bf16_t>(p, a.d, s);
+  else
+    launch_all<bf16_t, float>(p, a.d, s);
+  return hipGetLastError();
+}
+
+}  // namespace ssd

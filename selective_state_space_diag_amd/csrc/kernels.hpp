@@ -211,6 +211,23 @@ struct Hgrn2UpdateArgs {
 };
 hipError_t launch_hgrn2_update(const Hgrn2UpdateArgs& a, hipStream_t s);
 
+// Backward of the HGRN2 scan: o is the forward output in fp32 (NULL: recomputed into scratch).
+struct Hgrn2BwdArgs {
+  int64_t B, L, H, d;
+  int in_bf16, out_bf16;
+  const void *q, *k, *v, *g_logit;
+  float lower_bound;
+  const float* S0;
+  const float* o;
+  const void* dO;
+  const float* dS_last;
+  void *dq, *dk, *dv, *dg_logit;
+  float* dS0;
+  void* scratch;
+};
+size_t hgrn2_scan_backward_scratch_bytes(const Hgrn2BwdArgs& a);
+hipError_t launch_hgrn2_scan_backward(const Hgrn2BwdArgs& a, hipStream_t s);
+
 // ------------------------------------------------------------------ utilities
 // dst[i] = src ? src[i] : 0 for i < n (used for empty problems: final state = initial state).
 hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t s);

@@ -187,6 +187,24 @@ def test_hgrn2_validation(L):
     assert f(lb=2.0) == VALUE
 
 
+def test_hgrn2_backward_validation(L):
+    p = lambda k: None if k is None else ptr(k)
+    f = lambda B=2, d=64, lb=0.5, do=5, o=None, dq=6, dS0=None, S0=None: L.ssd_hgrn2_scan_backward(
+        B, 16, 4, d, BF16, F32, ptr(0), ptr(1), ptr(2), ptr(3), lb, p(S0), p(o), p(do), None, p(dq), ptr(7), ptr(8),
+        ptr(9), p(dS0), None)
+    assert f(d=48) == SHAPE
+    assert f(lb=1.5) == VALUE
+    assert f(do=None) == NULL
+    assert f(dq=None) == NULL
+    assert f(dq=0) == ALIAS           # dq on top of q
+    assert f(o=10, dq=10) == ALIAS    # dq on top of the given forward output
+    assert f(S0=11, dS0=11) == ALIAS
+    assert L.ssd_hgrn2_scan_backward(2, 16, 4, 64, BF16, F32, ptr(0), ptr(1), ptr(2), ptr(3), 0.5, None,
+                                     ctypes.c_void_p(P + 10 * 64 * MB + 8), ptr(5), None, ptr(6), ptr(7), ptr(8),
+                                     ptr(9), None, None) == ALIGN
+    assert f(B=0) == OK
+
+
 def test_python_layer_requires_gpu_tensors():
     torch = pytest.importorskip("torch")
     x = torch.zeros(1, 4, 8)
