@@ -89,6 +89,11 @@ def hgrn2_bytes(B, L, H, d, in_b=2, out_b=4):
     return B * L * H * d * (4 * in_b + out_b)
 
 
+def hgrn2_bwd_bytes(B, L, H, d, in_b=2, out_b=4):
+    # q, k, v, g_logit, do read (in dtype) and the forward's fp32 o; dq, dk, dv, dg_logit written
+    return B * L * H * d * (5 * in_b + 4 + 4 * out_b)
+
+
 def profiled_traffic(profile, sources):
     """HBM bytes per call recorded by rocprofv3 counter runs in profiles/<profile>, if the kernel
     sources are unchanged since (their sha256 is stored with the figure); else None."""
@@ -328,7 +333,17 @@ def forms(args, device):
     record("hgrn2_bf16_B8_H16_d128_L4096", ms, B * L * H * dd * dd, hgrn2_bytes(B, L, H, dd),
            dict(mfma_equiv_tflops=flops / (ms * 1e-3) / 1e12,
                 mfma_util=flops / (ms * 1e-3) / 1e12 / BF16_MFMA_TFLOPS))
-    del q, k, v, g
+
+    # --- gradients of the HGRN2 scan on the same shape (do ~ N(0, 1/d)), given the forward's fp32
+    #     output; the three sweeps execute 15 d^2 fp32 flops per token and head (two state updates of
+    #     3 d^2, the adjoint update twice, three d^2 matrix-vector products)
+    do = randn((B, L, H, dd), std=dd ** -0.5)
+    o = ssd.hgrn2_scan(q, k, v, g, 0.5)
+    ms = time_calls(lambda kk: ssd.hgrn2_scan_backward(q, k, v, g, 0.5, do, o=o), 1, 3, 1)[0]
+    vflops = 15 * B * L * H * dd * dd
+    record("hgrn2_backward_bf16_B8_H16_d128_L4096", ms, B * L * H * dd * dd, hgrn2_bwd_bytes(B, L, H, dd),
+           dict(valu_tflops=vflops / (ms * 1e-3) / 1e12, valu_frac=vflops / (ms * 1e-3) / 1e12 / FP32_SCALAR_FMA_TFLOPS))
+    del q, k, v, g, do, o
 
     # --- packed varlen selective, L=131072, 32 sequences, D=4096, N=16
     Lt, D, N, ns = 131072, 4096, 16, 32

@@ -559,7 +559,8 @@ int ssd_hgrn2_scan_backward(int64_t B, int64_t L, int64_t H, int64_t d, int in_d
   SSD_TRY(check_dtypes(in_dtype, out_dtype));
   if (B < 0 || L < 0 || H < 0 || d < 0) return fail(SSD_ERR_SHAPE, "negative size");
   if (!supported_d(d)) return fail(SSD_ERR_SHAPE, "head dim d must be 16, 32, 64 or 128");
-  if (too_big({B, L, H, d}) || B * H >= (int64_t)1 << 30) return fail(SSD_ERR_SHAPE, "problem too large");
+  if (too_big({B, L, H, d}) || B * H >= (int64_t)1 << 30 || (L + 16) * H * d * 4 >= (int64_t)1 << 32)
+    return fail(SSD_ERR_SHAPE, "problem too large");
   if (!(lower_bound >= 0.0f && lower_bound <= 1.0f)) return fail(SSD_ERR_VALUE, "lower_bound must be in [0, 1]");
   const int64_t nact = B * L * H * d;
   if (nact > 0 && (!q || !k || !v || !g_logit || !dO))

@@ -101,28 +101,34 @@ __device__ __forceinline__ float ratio_of(float x, float lb) {
   return s == 0.0f ? 0.0f : (1.0f - lb) * s * (1.0f - s) / g;
 }
 
+// Cross-lane moves inside a row of 16 lanes (DPP): lane p reads lane 15 - p (mirror), lane
+// (p & 8) | (7 - (p & 7)) (half mirror), p ^ 2 and p ^ 1 (quad permutations).
+constexpr int kDppMirror = 0x140, kDppHalfMirror = 0x141, kDppXor2 = 0x4E, kDppXor1 = 0xB1;
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
 // Sum over the 16 lanes of a row group of AB per-lane values; lane p returns the total of value
-// p / (16 / AB) (every lane of that sub-group holds it).
+// p / (16 / AB) (every lane of that sub-group holds it).  Each step pairs lanes across one bit of
+// the lane index (mirror: bit 3, half mirror: bit 2, then bits 1 and 0), so after the four steps
+// every kept value has been summed over all 16 lanes.
 template <int AB>
 __device__ __forceinline__ float part_reduce(const float (&acc)[AB], int p) {
   float v;
+  const bool lo8 = p < 8, lo4 = (p & 4) == 0;
   if constexpr (AB == 4) {
-    const bool lo8 = p < 8;
     const float k0 = lo8 ? acc[0] : acc[2], k1 = lo8 ? acc[1] : acc[3];
     const float s0 = lo8 ? acc[2] : acc[0], s1 = lo8 ? acc[3] : acc[1];
-    const float r0 = k0 + __shfl_xor(s0, 8), r1 = k1 + __shfl_xor(s1, 8);
-    const bool lo4 = (p & 4) == 0;
-    v = (lo4 ? r0 : r1) + __shfl_xor(lo4 ? r1 : r0, 4);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 1);
+    const float r0 = k0 + dpp_f<kDppMirror>(s0), r1 = k1 + dpp_f<kDppMirror>(s1);
+    v = (lo4 ? r0 : r1) + dpp_f<kDppHalfMirror>(lo4 ? r1 : r0);
   } else {
     static_assert(AB == 2, "AB must be 2 or 4");
-    const bool lo8 = p < 8;
-    v = (lo8 ? acc[0] : acc[1]) + __shfl_xor(lo8 ? acc[1] : acc[0], 8);
-    v += __shfl_xor(v, 4);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 1);
+    v = (lo8 ? acc[0] : acc[1]) + dpp_f<kDppMirror>(lo8 ? acc[1] : acc[0]);
+    v += dpp_f<kDppHalfMirror>(v);
   }
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppXor1>(v);
   return v;
 }
 
@@ -158,46 +164,71 @@ __global__ __launch_bounds__((SweepShape<DH, AB>::NT)) void hgrn2_bwd_sweep_kern
   using SL = Slots<MODE>;
   constexpr int MP = SS::MP, NT = SS::NT, PER = SS::PER, NV = SL::n;
   constexpr bool REV = MODE != kDQ;
+  constexpr int ES = (int)sizeof(Tout);
   __shared__ __align__(16) float stg[2][NV][kTS][DH];
 
   const int tid = threadIdx.x;
-  const int64_t head = blockIdx.x / SS::W;
-  const int wsub = (int)(blockIdx.x - head * SS::W);
+  // the W workgroups of a head take block ids 8 apart, so that they share one XCD's L2 (block ids
+  // are dealt to the XCDs in turn)
+  int64_t head;
+  int wsub;
+  if (SS::W == 2 && gridDim.x % 16 == 0) {
+    head = (int64_t)(blockIdx.x / 16) * 8 + (blockIdx.x % 8);
+    wsub = (int)((blockIdx.x / 8) % 2);
+  } else {
+    head = blockIdx.x / SS::W;
+    wsub = (int)(blockIdx.x - head * SS::W);
+  }
   const int64_t b = head / p.H, hh = head - b * p.H;
   const int pp = tid & (kParts - 1);
   const int a0 = ((wsub * NT + tid) / kParts) * AB;  // owned indices a0 .. a0 + AB - 1
   const int m0 = pp * MP;                             // summed-axis indices m0 .. m0 + MP - 1
   constexpr int SUB = kParts / AB;                    // lanes per owned index after the reduction
   const int ustar = pp / SUB;                         // owned index whose total this lane receives
-  const bool writer = (pp % SUB) == 0;
+  const int ia = a0 + ustar;
   const int64_t L = p.L;
   const int64_t nstage = (L + kTS - 1) / kTS;
   const int64_t row_stride = p.H * DH;                // elements between consecutive tokens
   const int64_t head_base = (b * L * p.H + hh) * DH;  // token 0 of this head
   const float lb = p.lb;
   const int64_t nanch = (L - 1) / kAnchor;            // checkpointed states per head
+  // outputs of this head: token t, column c at byte (t * row_stride + c) * ES.  The whole byte
+  // offset goes into the range-checked per-lane offset: stores to tokens outside [0, L) (whose
+  // offsets stay below 2^32: the host bounds (L + 16) H d 4 < 2^32)
+  // and stores of the lanes that do not write (offset kDrop) fall outside the window and are dropped.
+  const bool writer = (pp % SUB) == 0;
+  constexpr uint32_t kDrop = 0xFFFFFF00u;
+  const uint32_t out_bytes = (uint32_t)(((L - 1) * row_stride + DH) * ES);
+  const auto wo0 = make_window(static_cast<char*>(MODE == kDQ ? p.dq : MODE == kDK ? p.dk : p.dv) + head_base * ES,
+                               out_bytes);
+  const auto wo1 = make_window(static_cast<char*>(p.dx) + head_base * ES, out_bytes);
 
-  // ---- staging: stage s covers tokens t0 .. t0 + kTS - 1 with t0 = s kTS (forward) or
-  // L - (s + 1) kTS (reverse; tokens below 0 are skipped)
-  float raw[NV][PER];
-  auto stage_t0 = [&](int64_t s) -> int64_t { return REV ? L - (s + 1) * kTS : s * kTS; };
+  // ---- staging: the stages are the token blocks [c kTS, c kTS + kTS), taken in increasing c
+  // (forward) or decreasing c (reverse); tokens at or past L are staged as exact no-ops for the
+  // matrix update (gate 1, activations 0).
+  // Loads go through windows over the head's valid tokens (offsets past the last token read 0),
+  // so that they need no per-lane branch and stay in flight while the current stage computes.
+  uint32_t raw[NV][PER];  // raw bits: bf16 in the low half, or fp32
+  auto stage_t0 = [&](int64_t s) -> int64_t { return (REV ? nstage - 1 - s : s) * kTS; };
+  __amdgpu_buffer_rsrc_t wsrc[NV];
+#pragma unroll
+  for (int sl = 0; sl < NV; ++sl) {
+    const int es = SL::kind(sl) == kOut ? 4 : (int)sizeof(Tin);
+    wsrc[sl] = make_window(static_cast<const char*>(SL::src(p, sl)) + head_base * es,
+                           (uint32_t)(((L - 1) * row_stride + DH) * es));
+  }
   auto fetch = [&](int64_t s) {
     const int64_t t0 = stage_t0(s);
 #pragma unroll
     for (int sl = 0; sl < NV; ++sl) {
-      const void* src = SL::src(p, sl);
-      const int kd = SL::kind(sl);
+      const bool f32 = SL::kind(sl) == kOut || sizeof(Tin) == 4;
 #pragma unroll
       for (int r = 0; r < PER; ++r) {
         const int idx = tid + r * NT;
         const int tau = idx / DH, c = idx - (idx / DH) * DH;
-        const int64_t t = t0 + tau + SL::shift(sl);
-        float val = 0.0f;
-        if (t >= 0 && t < L) {
-          const int64_t off = head_base + t * row_stride + c;
-          val = kd == kOut ? static_cast<const float*>(src)[off] : io<Tin>::load(src, off);
-        }
-        raw[sl][r] = val;
+        const uint32_t off = (uint32_t)((t0 + tau + SL::shift(sl)) * row_stride + c);
+        raw[sl][r] = f32 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(wsrc[sl], (int)(off * 4), 0, 0)
+                         : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wsrc[sl], (int)(off * 2), 0, 0);
       }
     }
   };
@@ -210,9 +241,10 @@ __global__ __launch_bounds__((SweepShape<DH, AB>::NT)) void hgrn2_bwd_sweep_kern
       for (int r = 0; r < PER; ++r) {
         const int idx = tid + r * NT;
         const int tau = idx / DH, c = idx - (idx / DH) * DH;
-        const int64_t t = t0 + tau + SL::shift(sl);
-        const bool in = t >= 0 && t < L;
-        float val = raw[sl][r];
+        const int64_t tok = t0 + tau, t = tok + SL::shift(sl);
+        const bool in = t >= 0 && t < L && tok >= 0 && tok < L;
+        const bool f32 = kd == kOut || sizeof(Tin) == 4;
+        float val = f32 ? __uint_as_float(raw[sl][r]) : __uint_as_float(raw[sl][r] << 16);
         if (kd == kGate) val = in ? gate_of(val, lb) : 1.0f;  // no gate past the ends
         if (kd == kRatio) val = in ? ratio_of(val, lb) : 0.0f;
         stg[buf][sl][tau][c] = val;
@@ -220,12 +252,12 @@ __global__ __launch_bounds__((SweepShape<DH, AB>::NT)) void hgrn2_bwd_sweep_kern
     }
   };
 
-  // ---- the matrix: M[x][y] with x over the rows this thread holds: for kDQ / kDK M[e][u] =
-  // matrix[m0 + e][a0 + u]; for kDV M[u][e] = R[a0 + u][m0 + e]; stored as mat[u][e] either way.
+  // ---- the matrix: for kDQ / kDK mat[u][e] = matrix[m0 + e][a0 + u]; for kDV mat[u][e] =
+  // R[a0 + u][m0 + e]
   float mat[AB][MP];
   const int64_t mbase = head * DH * DH;
-  // kDV: running dlog g of row a0 + ustar, a sum over all later tokens whose terms largely cancel:
-  // it is accumulated in fp64 so that its rounding does not grow with the sequence length
+  // kDV: running dlog g of row ia, a sum over all later tokens whose terms largely cancel: it is
+  // accumulated in fp64 so that its rounding does not grow with the sequence length
   double cum = 0.0;
   if constexpr (MODE == kDV) {
     float part[AB];
@@ -250,6 +282,26 @@ __global__ __launch_bounds__((SweepShape<DH, AB>::NT)) void hgrn2_bwd_sweep_kern
         mat[u][e] = init ? init[mbase + (int64_t)(m0 + e) * DH + a0 + u] : 0.0f;
   }
 
+  // The matrix is loop-carried through the token loop: take its initial loads to completion here
+  // (the empty asm reads and redefines each register), so that no wait for them lands inside the
+  // loop, where it would also wait for the next stage's prefetch.
+#pragma unroll
+  for (int u = 0; u < AB; ++u)
+#pragma unroll
+    for (int e = 0; e < MP; ++e) asm volatile("" : "+v"(mat[u][e]));
+
+  // sum_j R[ia][j] X[ia][j] over this thread's rows (kDV), X a d x d fp32 matrix of the head
+  auto row_dot = [&](const float* X) -> float {
+    float part[AB];
+#pragma unroll
+    for (int u = 0; u < AB; ++u) {
+      part[u] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < MP; ++e) part[u] = fmaf(mat[u][e], X[(a0 + u) * DH + m0 + e], part[u]);
+    }
+    return part_reduce<AB>(part, pp);
+  };
+
   if (nstage > 0) {
     fetch(0);
     publish(0, 0);
@@ -259,12 +311,13 @@ __global__ __launch_bounds__((SweepShape<DH, AB>::NT)) void hgrn2_bwd_sweep_kern
     const int buf = (int)(s & 1);
     if (s + 1 < nstage) fetch(s + 1);
     const int64_t t0 = stage_t0(s);
+    // checkpoint / exact restart at the stage's last token in time order (uniform)
+    const bool anchor = p.ckpt && (t0 + kTS) % kAnchor == 0 && t0 + kTS < L;
 #pragma unroll
     for (int step = 0; step < kTS; ++step) {
       const int tau = REV ? kTS - 1 - step : step;
       const int64_t t = t0 + tau;
-      if (t < 0 || t >= L) continue;  // uniform across the workgroup
-      const int64_t out_off = head_base + t * row_stride;
+      const uint32_t lo = writer ? (uint32_t)((t * row_stride + ia) * ES) : kDrop;
       float acc[AB];
       if constexpr (MODE == kDV) {
         float qv[MP], kv[MP], dov[AB], gn[AB];
@@ -282,38 +335,17 @@ __global__ __launch_bounds__((SweepShape<DH, AB>::NT)) void hgrn2_bwd_sweep_kern
           }
         }
         const float dvt = part_reduce<AB>(acc, pp);
-        const int ia = a0 + ustar;
         const float dos = stg[buf][2][tau][ia], os = stg[buf][3][tau][ia], vs = stg[buf][4][tau][ia];
         const float rt = stg[buf][6][tau][ia];
-        if (t == 0) {  // uniform: dlog g_0 = g_0 sum_j R_0[i][j] S0[i][j], exactly 0 without S0
-          float part[AB];
-#pragma unroll
-          for (int u = 0; u < AB; ++u) {
-            part[u] = 0.0f;
-#pragma unroll
-            for (int e = 0; e < MP; ++e)
-              part[u] = fmaf(mat[u][e], p.S0 ? p.S0[mbase + (a0 + u) * DH + m0 + e] : 0.0f, part[u]);
-          }
-          const float tot = part_reduce<AB>(part, pp);
-          cum = (double)(gate_of(io<Tin>::load(p.x, head_base + ia), lb) * tot);
-        } else if (p.ckpt && (t + 1) % kAnchor == 0 && t + 1 < L) {  // uniform
-          // restart the suffix sum exactly: dlog g_t = sum_j R_t[i][j] S_t[i][j] - v_t dv_t
-          const float* St = p.ckpt + (head * nanch + (t + 1) / kAnchor - 1) * DH * DH;
-          float part[AB];
-#pragma unroll
-          for (int u = 0; u < AB; ++u) {
-            part[u] = 0.0f;
-#pragma unroll
-            for (int e = 0; e < MP; ++e) part[u] = fmaf(mat[u][e], St[(a0 + u) * DH + m0 + e], part[u]);
-          }
-          cum = (double)fmaf(-vs, dvt, part_reduce<AB>(part, pp));
-        } else {
-          cum += (double)fmaf(dos, os, -vs * dvt);
+        cum += (double)fmaf(dos, os, -vs * dvt);  // tokens outside [0, L) add exactly 0
+        if (step == 0 && anchor) {
+          // restart the suffix sum exactly: dlog g_t = sum_j R_t[ia][j] S_t[ia][j] - v_t dv_t
+          const float P = row_dot(p.ckpt + (head * nanch + (t0 + kTS) / kAnchor - 1) * DH * DH);
+          cum = (double)fmaf(-vs, dvt, P);
         }
-        if (writer) {
-          io<Tout>::store(p.dv, out_off + ia, dvt);
-          io<Tout>::store(p.dx, out_off + ia, (float)cum * rt);
-        }
+        const float dg = (float)cum * rt;
+        win<Tout, 1>::store(wo0, lo, 0u, &dvt);
+        win<Tout, 1>::store(wo1, lo, 0u, &dg);
       } else {
         float gv[MP], xv[MP], yv[MP], av[AB];
         // kDQ: g(t), v, do over i and k over j:  S = g S + v k^T, dq = S^T do
@@ -332,16 +364,16 @@ __global__ __launch_bounds__((SweepShape<DH, AB>::NT)) void hgrn2_bwd_sweep_kern
           }
         }
         const float tot = part_reduce<AB>(acc, pp);
-        if (writer) io<Tout>::store(MODE == kDQ ? p.dq : p.dk, out_off + a0 + ustar, tot);
-        if constexpr (MODE == kDQ) {
-          if (p.ckpt && (t + 1) % kAnchor == 0 && t + 1 < L) {  // uniform: state after token t
-            float* St = p.ckpt + (head * nanch + (t + 1) / kAnchor - 1) * DH * DH;
+        win<Tout, 1>::store(wo0, lo, 0u, &tot);
+      }
+    }
+    if constexpr (MODE == kDQ) {
+      if (anchor) {  // state after the stage's last token
+        float* St = p.ckpt + (head * nanch + (t0 + kTS) / kAnchor - 1) * DH * DH;
 #pragma unroll
-            for (int u = 0; u < AB; ++u)
+        for (int u = 0; u < AB; ++u)
 #pragma unroll
-              for (int e = 0; e < MP; ++e) St[(m0 + e) * DH + a0 + u] = mat[u][e];
-          }
-        }
+          for (int e = 0; e < MP; ++e) St[(m0 + e) * DH + a0 + u] = mat[u][e];
       }
     }
     if (s + 1 < nstage) publish(s + 1, buf ^ 1);
@@ -355,15 +387,22 @@ __global__ __launch_bounds__((SweepShape<DH, AB>::NT)) void hgrn2_bwd_sweep_kern
       for (int e = 0; e < MP; ++e) p.S_L[mbase + (int64_t)(m0 + e) * DH + a0 + u] = mat[u][e];
   }
   if constexpr (MODE == kDV) {
-    if (p.dS0) {
-      float g0[AB];
+    if (L > 0) {
+      // mat = R_0 (tokens before 0 were no-ops): the first token's dlog g is exact,
+      // g_0 sum_j R_0[ia][j] S0[ia][j] (0 without an initial state); its dg_logit is rewritten
+      const float rs0 = p.S0 ? row_dot(p.S0 + mbase) : 0.0f;
+      const float g0 = gate_of(io<Tin>::load(p.x, head_base + ia), lb);
+      const float dg0 = g0 * rs0 * ratio_of(io<Tin>::load(p.x, head_base + ia), lb);
+      win<Tout, 1>::store(wo1, writer ? (uint32_t)(ia * ES) : kDrop, 0u, &dg0);
+      if (p.dS0) {
+        float gr[AB];
 #pragma unroll
-      for (int u = 0; u < AB; ++u)
-        g0[u] = L > 0 ? gate_of(io<Tin>::load(p.x, head_base + a0 + u), lb) : 1.0f;
+        for (int u = 0; u < AB; ++u) gr[u] = gate_of(io<Tin>::load(p.x, head_base + a0 + u), lb);
 #pragma unroll
-      for (int u = 0; u < AB; ++u)
+        for (int u = 0; u < AB; ++u)
 #pragma unroll
-        for (int e = 0; e < MP; ++e) p.dS0[mbase + (int64_t)(a0 + u) * DH + m0 + e] = g0[u] * mat[u][e];
+          for (int e = 0; e < MP; ++e) p.dS0[mbase + (int64_t)(a0 + u) * DH + m0 + e] = gr[u] * mat[u][e];
+      }
     }
   }
 }
