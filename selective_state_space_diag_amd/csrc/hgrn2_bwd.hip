@@ -37,6 +37,8 @@
 namespace ssd {
 namespace {
 
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+
 enum { kDQ = 0, kDK = 1, kDV = 2 };
 constexpr int kTS = 8;     // tokens per stage
 constexpr int kParts = 16; // lanes that share the summed axis
@@ -155,7 +157,8 @@ template <int DH, int AB> struct SweepShape {
   static constexpr int NT = TH < 256 ? TH : 256;  // threads per workgroup
   static constexpr int W = TH / NT;               // workgroups per head
   static constexpr int PER = kTS * DH / NT;       // staged elements per thread and slot
-  static_assert(DH % kParts == 0 && TH % NT == 0 && (kTS * DH) % NT == 0, "sweep shape");
+  static_assert(DH % kParts == 0 && TH % NT == 0 && (kTS * DH) % NT == 0 && PER <= 4 && DH % PER == 0,
+                "sweep shape");
 };
 
 template <int MODE, typename Tin, typename Tout, int DH, int AB>
@@ -207,8 +210,9 @@ __global__ __launch_bounds__((SweepShape<DH, AB>::NT)) void hgrn2_bwd_sweep_kern
   // (forward) or decreasing c (reverse); tokens at or past L are staged as exact no-ops for the
   // matrix update (gate 1, activations 0).
   // Loads go through windows over the head's valid tokens (offsets past the last token read 0),
-  // so that they need no per-lane branch and stay in flight while the current stage computes.
-  uint32_t raw[NV][PER];  // raw bits: bf16 in the low half, or fp32
+  // so that they need no per-lane branch and stay in flight while the current stage computes.  A
+  // thread loads PER consecutive elements of one token row per slot (one 4- to 16-byte load).
+  uint32_t raw[NV][4];  // raw bits: bf16 pairs, or fp32
   auto stage_t0 = [&](int64_t s) -> int64_t { return (REV ? nstage - 1 - s : s) * kTS; };
   __amdgpu_buffer_rsrc_t wsrc[NV];
 #pragma unroll
@@ -217,37 +221,51 @@ __global__ __launch_bounds__((SweepShape<DH, AB>::NT)) void hgrn2_bwd_sweep_kern
     wsrc[sl] = make_window(static_cast<const char*>(SL::src(p, sl)) + head_base * es,
                            (uint32_t)(((L - 1) * row_stride + DH) * es));
   }
+  const int tau_ld = (tid * PER) / DH, c_ld = (tid * PER) % DH;  // this thread's staged elements
   auto fetch = [&](int64_t s) {
     const int64_t t0 = stage_t0(s);
 #pragma unroll
     for (int sl = 0; sl < NV; ++sl) {
-      const bool f32 = SL::kind(sl) == kOut || sizeof(Tin) == 4;
-#pragma unroll
-      for (int r = 0; r < PER; ++r) {
-        const int idx = tid + r * NT;
-        const int tau = idx / DH, c = idx - (idx / DH) * DH;
-        const uint32_t off = (uint32_t)((t0 + tau + SL::shift(sl)) * row_stride + c);
-        raw[sl][r] = f32 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(wsrc[sl], (int)(off * 4), 0, 0)
-                         : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wsrc[sl], (int)(off * 2), 0, 0);
+      const int es = SL::kind(sl) == kOut ? 4 : (int)sizeof(Tin);
+      const uint32_t off = (uint32_t)(((t0 + tau_ld + SL::shift(sl)) * row_stride + c_ld) * es);
+      const int bytes = PER * es;
+      if (bytes == 16) {
+        const v4i_t d = __builtin_amdgcn_raw_buffer_load_b128(wsrc[sl], (int)off, 0, 0);
+        raw[sl][0] = d.x; raw[sl][1] = d.y; raw[sl][2] = d.z; raw[sl][3] = d.w;
+      } else if (bytes == 8) {
+        const u32x2_t d = __builtin_amdgcn_raw_buffer_load_b64(wsrc[sl], (int)off, 0, 0);
+        raw[sl][0] = d.x; raw[sl][1] = d.y;
+      } else if (bytes == 4) {
+        raw[sl][0] = __builtin_amdgcn_raw_buffer_load_b32(wsrc[sl], (int)off, 0, 0);
+      } else {
+        raw[sl][0] = __builtin_amdgcn_raw_buffer_load_b16(wsrc[sl], (int)off, 0, 0);
       }
     }
   };
   auto publish = [&](int64_t s, int buf) {
     const int64_t t0 = stage_t0(s);
+    const int64_t tok = t0 + tau_ld;
 #pragma unroll
     for (int sl = 0; sl < NV; ++sl) {
       const int kd = SL::kind(sl);
+      const bool f32 = kd == kOut || sizeof(Tin) == 4;
+      const int64_t t = tok + SL::shift(sl);
+      const bool in = t < L && tok < L;
+      float val[PER];
 #pragma unroll
-      for (int r = 0; r < PER; ++r) {
-        const int idx = tid + r * NT;
-        const int tau = idx / DH, c = idx - (idx / DH) * DH;
-        const int64_t tok = t0 + tau, t = tok + SL::shift(sl);
-        const bool in = t >= 0 && t < L && tok >= 0 && tok < L;
-        const bool f32 = kd == kOut || sizeof(Tin) == 4;
-        float val = f32 ? __uint_as_float(raw[sl][r]) : __uint_as_float(raw[sl][r] << 16);
-        if (kd == kGate) val = in ? gate_of(val, lb) : 1.0f;  // no gate past the ends
-        if (kd == kRatio) val = in ? ratio_of(val, lb) : 0.0f;
-        stg[buf][sl][tau][c] = val;
+      for (int k = 0; k < PER; ++k) {
+        val[k] = f32 ? __uint_as_float(raw[sl][k]) : ((k & 1) ? bf16_hi(raw[sl][k >> 1]) : bf16_lo(raw[sl][k >> 1]));
+        if (kd == kGate) val[k] = in ? gate_of(val[k], lb) : 1.0f;  // no gate past the end
+        if (kd == kRatio) val[k] = in ? ratio_of(val[k], lb) : 0.0f;
+      }
+      float* dst = &stg[buf][sl][tau_ld][c_ld];
+      if constexpr (PER == 4) {
+        *reinterpret_cast<float4*>(dst) = make_float4(val[0], val[1], val[2], val[3]);
+      } else if constexpr (PER == 2) {
+        *reinterpret_cast<float2*>(dst) = make_float2(val[0], val[1]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < PER; ++k) dst[k] = val[k];
       }
     }
   };
@@ -313,59 +331,76 @@ __global__ __launch_bounds__((SweepShape<DH, AB>::NT)) void hgrn2_bwd_sweep_kern
     const int64_t t0 = stage_t0(s);
     // checkpoint / exact restart at the stage's last token in time order (uniform)
     const bool anchor = p.ckpt && (t0 + kTS) % kAnchor == 0 && t0 + kTS < L;
+    // operands of one token, read from LDS one token ahead of their use
+    struct Tok {
+      float m[3][MP];  // summed-axis vectors (kDV: q, k; others: gate, x, y)
+      float a[2][AB];  // owned-axis vectors (kDV: do, gate(t+1); others: k or q)
+      float sc[4];     // kDV: do, o, v, ratio of row ia
+    };
+    auto read_tok = [&](int tau, Tok& o) {
+      if constexpr (MODE == kDV) {
+        lds_vec<MP>(&stg[buf][0][tau][m0], o.m[0]);
+        lds_vec<MP>(&stg[buf][1][tau][m0], o.m[1]);
+        lds_vec<AB>(&stg[buf][2][tau][a0], o.a[0]);
+        lds_vec<AB>(&stg[buf][5][tau][a0], o.a[1]);
+        o.sc[0] = stg[buf][2][tau][ia];
+        o.sc[1] = stg[buf][3][tau][ia];
+        o.sc[2] = stg[buf][4][tau][ia];
+        o.sc[3] = stg[buf][6][tau][ia];
+      } else {
+        lds_vec<MP>(&stg[buf][0][tau][m0], o.m[0]);
+        lds_vec<MP>(&stg[buf][1][tau][m0], o.m[1]);
+        lds_vec<MP>(&stg[buf][2][tau][m0], o.m[2]);
+        lds_vec<AB>(&stg[buf][3][tau][a0], o.a[0]);
+      }
+    };
+    Tok cur, nxt;
+    read_tok(REV ? kTS - 1 : 0, cur);
 #pragma unroll
     for (int step = 0; step < kTS; ++step) {
       const int tau = REV ? kTS - 1 - step : step;
+      if (step + 1 < kTS) read_tok(REV ? tau - 1 : tau + 1, nxt);
       const int64_t t = t0 + tau;
       const uint32_t lo = writer ? (uint32_t)((t * row_stride + ia) * ES) : kDrop;
       float acc[AB];
       if constexpr (MODE == kDV) {
-        float qv[MP], kv[MP], dov[AB], gn[AB];
-        lds_vec<MP>(&stg[buf][0][tau][m0], qv);
-        lds_vec<MP>(&stg[buf][1][tau][m0], kv);
-        lds_vec<AB>(&stg[buf][2][tau][a0], dov);
-        lds_vec<AB>(&stg[buf][5][tau][a0], gn);
+        // R = diag(g(t+1)) R + do q^T,  dv = R k
 #pragma unroll
         for (int u = 0; u < AB; ++u) {
           acc[u] = 0.0f;
 #pragma unroll
           for (int e = 0; e < MP; ++e) {
-            mat[u][e] = fmaf(gn[u], mat[u][e], dov[u] * qv[e]);
-            acc[u] = fmaf(mat[u][e], kv[e], acc[u]);
+            mat[u][e] = fmaf(cur.a[1][u], mat[u][e], cur.a[0][u] * cur.m[0][e]);
+            acc[u] = fmaf(mat[u][e], cur.m[1][e], acc[u]);
           }
         }
         const float dvt = part_reduce<AB>(acc, pp);
-        const float dos = stg[buf][2][tau][ia], os = stg[buf][3][tau][ia], vs = stg[buf][4][tau][ia];
-        const float rt = stg[buf][6][tau][ia];
-        cum += (double)fmaf(dos, os, -vs * dvt);  // tokens outside [0, L) add exactly 0
+        const float vs = cur.sc[2];
+        cum += (double)fmaf(cur.sc[0], cur.sc[1], -vs * dvt);  // tokens past L add exactly 0
         if (step == 0 && anchor) {
           // restart the suffix sum exactly: dlog g_t = sum_j R_t[ia][j] S_t[ia][j] - v_t dv_t
           const float P = row_dot(p.ckpt + (head * nanch + (t0 + kTS) / kAnchor - 1) * DH * DH);
           cum = (double)fmaf(-vs, dvt, P);
         }
-        const float dg = (float)cum * rt;
+        const float dg = (float)cum * cur.sc[3];
         win<Tout, 1>::store(wo0, lo, 0u, &dvt);
         win<Tout, 1>::store(wo1, lo, 0u, &dg);
       } else {
-        float gv[MP], xv[MP], yv[MP], av[AB];
         // kDQ: g(t), v, do over i and k over j:  S = g S + v k^T, dq = S^T do
         // kDK: g(t+1), do, v over i and q over j: R = g R + do q^T, dk = R^T v
-        lds_vec<MP>(&stg[buf][0][tau][m0], gv);
-        lds_vec<MP>(&stg[buf][1][tau][m0], xv);
-        lds_vec<MP>(&stg[buf][2][tau][m0], yv);
-        lds_vec<AB>(&stg[buf][3][tau][a0], av);
 #pragma unroll
         for (int u = 0; u < AB; ++u) {
           acc[u] = 0.0f;
 #pragma unroll
           for (int e = 0; e < MP; ++e) {
-            mat[u][e] = fmaf(gv[e], mat[u][e], xv[e] * av[u]);
-            acc[u] = fmaf(yv[e], mat[u][e], acc[u]);
+            mat[u][e] = fmaf(cur.m[0][e], mat[u][e], cur.m[1][e] * cur.a[0][u]);
+            acc[u] = fmaf(cur.m[2][e], mat[u][e], acc[u]);
           }
         }
         const float tot = part_reduce<AB>(acc, pp);
         win<Tout, 1>::store(wo0, lo, 0u, &tot);
       }
+      if (step + 1 < kTS) cur = nxt;
     }
     if constexpr (MODE == kDQ) {
       if (anchor) {  // state after the stage's last token
