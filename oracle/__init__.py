@@ -58,9 +58,14 @@ def lib():
                                               ctypes.c_int, _dp, _dp]
         L.oracle_hgrn2_scan.argtypes = [_i64, _i64, _i64, _i64, _dp, _dp, _dp, _dp, ctypes.c_double, _dp, _dp, _dp]
         L.oracle_hgrn2_update.argtypes = [_i64, _i64, _i64, _dp, _dp, _dp, _dp, ctypes.c_double, _dp, _dp]
+        L.oracle_hgrn2_key_scan.argtypes = [_i64, _i64, _i64, _i64, _dp, _dp, _dp, _dp, ctypes.c_double, _dp, _dp,
+                                            _dp]
+        L.oracle_hgrn2_key_update.argtypes = [_i64, _i64, _i64, _dp, _dp, _dp, _dp, ctypes.c_double, _dp, _dp]
+        L.oracle_readout_norm.argtypes = [_i64, _i64, _dp, _dp, _dp, _dp, ctypes.c_double, _dp]
         for fn in ("oracle_affine_scan", "oracle_rglru_scan", "oracle_rglru_update", "oracle_selective_scan",
                    "oracle_selective_update", "oracle_hgrn2_scan", "oracle_hgrn2_update", "oracle_minmax_scan",
-                   "oracle_minmax_update", "oracle_causal_conv1d", "oracle_causal_conv1d_update"):
+                   "oracle_minmax_update", "oracle_causal_conv1d", "oracle_causal_conv1d_update",
+                   "oracle_hgrn2_key_scan", "oracle_hgrn2_key_update", "oracle_readout_norm"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -169,6 +174,39 @@ def hgrn2_update(q, k, v, g_logit, lower_bound, S):
     _check(lib().oracle_hgrn2_update(B, H, d, _p(q), _p(k), _p(v), _p(g_logit), float(lower_bound), _p(St), _p(o)),
            "hgrn2_update")
     return o, St
+
+
+def hgrn2_key_scan(q, k, v, g_logit, lower_bound, S0=None):
+    """Key-axis gating (S[i][j] = g_j S[i][j] + v_i k_j).  Returns (o [B,L,H,d], S_last [B,H,d,d])."""
+    q, k, v, g_logit, S0 = map(_f64, (q, k, v, g_logit, S0))
+    B, L, H, d = q.shape
+    o = np.empty((B, L, H, d))
+    S_last = np.empty((B, H, d, d))
+    _check(lib().oracle_hgrn2_key_scan(B, L, H, d, _p(q), _p(k), _p(v), _p(g_logit), float(lower_bound), _p(S0),
+                                       _p(o), _p(S_last)), "hgrn2_key_scan")
+    return o, S_last
+
+
+def hgrn2_key_update(q, k, v, g_logit, lower_bound, S):
+    """Returns (o [B,H,d], new_S [B,H,d,d]); the input state is not modified."""
+    q, k, v, g_logit = map(_f64, (q, k, v, g_logit))
+    St = np.array(S, dtype=np.float64, copy=True, order="C")
+    B, H, d = q.shape
+    o = np.empty((B, H, d))
+    _check(lib().oracle_hgrn2_key_update(B, H, d, _p(q), _p(k), _p(v), _p(g_logit), float(lower_bound), _p(St),
+                                         _p(o)), "hgrn2_key_update")
+    return o, St
+
+
+def readout_norm(o, gate=None, weight=None, bias=None, eps=1e-5):
+    """LayerNorm over the last axis of ``o`` (biased variance), affine, times silu(gate)."""
+    o, gate, weight, bias = map(_f64, (o, gate, weight, bias))
+    width = o.shape[-1]
+    rows = o.size // width if width else 0
+    y = np.empty(o.shape)
+    _check(lib().oracle_readout_norm(rows, width, _p(o), _p(gate), _p(weight), _p(bias), float(eps), _p(y)),
+           "readout_norm")
+    return y
 
 
 def minmax_scan(r, s, x0=None, gate=None):

@@ -233,6 +233,90 @@ int oracle_hgrn2_update(int64_t B, int64_t H, int64_t d,
   return 0;
 }
 
+/* [HGRN2-KEY] the key-axis reading of the gate (the convention of the HGRN2 paper the page cites,
+ * not printed there): the gate scales column j, S[i][j] = g_j S[i][j] + v_i k_j, i.e.
+ * S_t = S_{t-1} diag(g_t) + v_t k_t^T; the readout is the same o_i = sum_j S[i][j] q_j. */
+static void hgrn2_key_step(double* S, int64_t d, const double* q, const double* k, const double* v,
+                           const double* g_logit, double lb, double* o) {
+  for (int64_t i = 0; i < d; ++i) {
+    double* row = S + i * d;
+    for (int64_t j = 0; j < d; ++j) {
+      double g = lb + (1.0 - lb) * sigmoid(g_logit[j]);
+      row[j] = g * row[j] + v[i] * k[j];
+    }
+  }
+  for (int64_t i = 0; i < d; ++i) {
+    const double* row = S + i * d;
+    double acc = 0.0;
+    for (int64_t j = 0; j < d; ++j) acc += row[j] * q[j];
+    o[i] = acc;
+  }
+}
+
+int oracle_hgrn2_key_scan(int64_t B, int64_t L, int64_t H, int64_t d,
+                          const double* q, const double* k, const double* v,
+                          const double* g_logit, double lower_bound, const double* S0,
+                          double* o, double* S_last) {
+  if (B < 0 || L < 0 || H < 0 || d < 0) return 1;
+  if (B * L * H * d > 0 && (!q || !k || !v || !g_logit || !o)) return 1;
+  double* S = (double*)malloc(sizeof(double) * (size_t)(d > 0 ? d * d : 1));
+  if (!S) return 1;
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t hh = 0; hh < H; ++hh) {
+      const int64_t sbase = (b * H + hh) * d * d;
+      for (int64_t e = 0; e < d * d; ++e) S[e] = S0 ? S0[sbase + e] : 0.0;
+      for (int64_t t = 0; t < L; ++t) {
+        int64_t base = ((b * L + t) * H + hh) * d;
+        hgrn2_key_step(S, d, q + base, k + base, v + base, g_logit + base, lower_bound, o + base);
+      }
+      if (S_last)
+        for (int64_t e = 0; e < d * d; ++e) S_last[sbase + e] = S[e];
+    }
+  }
+  free(S);
+  return 0;
+}
+
+int oracle_hgrn2_key_update(int64_t B, int64_t H, int64_t d,
+                            const double* q, const double* k, const double* v,
+                            const double* g_logit, double lower_bound, double* S, double* o) {
+  if (B < 0 || H < 0 || d < 0) return 1;
+  if (B * H * d > 0 && (!q || !k || !v || !g_logit || !S || !o)) return 1;
+  for (int64_t bh = 0; bh < B * H; ++bh) {
+    hgrn2_key_step(S + bh * d * d, d, q + bh * d, k + bh * d, v + bh * d, g_logit + bh * d,
+                   lower_bound, o + bh * d);
+  }
+  return 0;
+}
+
+/* [NORM] the HGRN2 layer's readout normalisation and output gate (frankenstein-transformer
+ * documentation, "HGRN2 Attention": a LayerNorm applied to the recurrent readout before the
+ * silu-gated output): per row of `width` features,
+ *   y = ((o - mean) / sqrt(var + eps) * weight + bias) * silu(gate),
+ * mean and (biased) variance over the row, as torch.nn.LayerNorm computes them; weight / bias NULL
+ * mean 1 / 0, gate NULL means no gate. */
+int oracle_readout_norm(int64_t rows, int64_t width, const double* o, const double* gate,
+                        const double* weight, const double* bias, double eps, double* y) {
+  if (rows < 0 || width < 0) return 1;
+  if (rows * width > 0 && (!o || !y)) return 1;
+  for (int64_t r = 0; r < rows; ++r) {
+    const double* x = o + r * width;
+    double mean = 0.0;
+    for (int64_t c = 0; c < width; ++c) mean += x[c];
+    mean /= (double)width;
+    double var = 0.0;
+    for (int64_t c = 0; c < width; ++c) var += (x[c] - mean) * (x[c] - mean);
+    var /= (double)width;
+    const double inv = 1.0 / sqrt(var + eps);
+    for (int64_t c = 0; c < width; ++c) {
+      double v = (x[c] - mean) * inv * (weight ? weight[c] : 1.0) + (bias ? bias[c] : 0.0);
+      if (gate) v *= gate[r * width + c] * sigmoid(gate[r * width + c]);
+      y[r * width + c] = v;
+    }
+  }
+  return 0;
+}
+
 /* [MINMAX] min and max on the order of the real numbers with -0 placed below +0 (so that every
  * result is one definite input value); a NaN operand gives NaN. */
 static double mm_min(double a, double b) {

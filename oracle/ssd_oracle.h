@@ -94,6 +94,15 @@ int oracle_hgrn2_scan(int64_t B, int64_t L, int64_t H, int64_t d,
 int oracle_hgrn2_update(int64_t B, int64_t H, int64_t d,
                         const double* q, const double* k, const double* v,
                         const double* g_logit, double lower_bound, double* S, double* o);
+int oracle_hgrn2_key_scan(int64_t B, int64_t L, int64_t H, int64_t d,
+                          const double* q, const double* k, const double* v,
+                          const double* g_logit, double lower_bound, const double* S0,
+                          double* o, double* S_last);
+int oracle_hgrn2_key_update(int64_t B, int64_t H, int64_t d,
+                            const double* q, const double* k, const double* v,
+                            const double* g_logit, double lower_bound, double* S, double* o);
+int oracle_readout_norm(int64_t rows, int64_t width, const double* o, const double* gate,
+                        const double* weight, const double* bias, double eps, double* y);
 
 /* MinMax recurrence (minmaxrnc MinMaxNeuron): x_t = max(min(r_t, x_{t-1}), s_t)
  * from x0 (NULL = zero).  min / max order -0 below +0 and return NaN when an
