@@ -13,6 +13,8 @@
  *                 (gradients)                       ssd_selective_scan_backward
  *   HGRN2         d x d matrix state per head       ssd_hgrn2_scan / ssd_hgrn2_update
  *                 (gradients)                       ssd_hgrn2_scan_backward
+ *                 (gate on the key axis)            ssd_hgrn2_key_scan / ssd_hgrn2_key_update
+ *                 (readout LayerNorm, silu gate)    ssd_readout_norm
  *
  * Conventions (every entry point):
  *   - Sizes are int64_t element counts; every pointer is DEVICE memory owned by
@@ -317,6 +319,39 @@ int ssd_hgrn2_scan_backward(int64_t B, int64_t L, int64_t H, int64_t d, int in_d
 int ssd_hgrn2_update(int64_t B, int64_t H, int64_t d, int in_dtype, int out_dtype,
                      const void* q, const void* k, const void* v, const void* g_logit,
                      float lower_bound, float* S, void* o, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * HGRN2 with the gate on the key axis.  The page defines the state update with the gate scaling
+ * the state "per channel" and cites the HGRN2 paper, whose convention (the gate on the key
+ * dimension) it does not print; this is that reading:
+ *     g_j = lower_bound + (1 - lower_bound) * sigmoid(g_logit_j),
+ *     S[i][j] = g_j * S[i][j] + v_i * k_j,        o_i = sum_j S[i][j] * q_j,
+ * i.e. S_t = S_{t-1} diag(g_t) + v_t k_t^T.  Arguments, layouts and errors as ssd_hgrn2_scan /
+ * ssd_hgrn2_update; additionally (L + 16) * H * d * 4 must stay below 2^32 for the scan.
+ * ------------------------------------------------------------------------------------------- */
+int ssd_hgrn2_key_scan(int64_t B, int64_t L, int64_t H, int64_t d, int in_dtype, int out_dtype,
+                       const void* q, const void* k, const void* v, const void* g_logit,
+                       float lower_bound, const float* S0, void* o, float* S_last, void* stream);
+int ssd_hgrn2_key_update(int64_t B, int64_t H, int64_t d, int in_dtype, int out_dtype,
+                         const void* q, const void* k, const void* v, const void* g_logit,
+                         float lower_bound, float* S, void* o, void* stream);
+
+/* The HGRN2 layer's readout normalisation and output gate (frankenstein-transformer documentation,
+ * "HGRN2 Attention": a LayerNorm on the recurrent readout, before the silu-gated output).  Per row of
+ * `width` contiguous features:
+ *     y = ((o - mean) / sqrt(var + eps) * weight + bias) * silu(gate),
+ * mean and biased variance over the row (torch.nn.LayerNorm).  For the layer's norm over its hidden
+ * size, rows = B * L and width = H * d of the scan output [B, L, H, d]; width = d normalises each head.
+ *   o      : [rows, width] fp32 (the scan output)
+ *   gate   : [rows, width] (in dtype) or NULL (no gate)
+ *   weight, bias : [width] fp32 or NULL (1 / 0)
+ *   y      : [rows, width] (out dtype)
+ *   eps    : finite, >= 0 (torch's default is 1e-5)
+ * Errors: SSD_ERR_NULL, SSD_ERR_SHAPE (negative size, width > 8192), SSD_ERR_DTYPE, SSD_ERR_ALIGN,
+ * SSD_ERR_VALUE (eps), SSD_ERR_ALIAS. */
+int ssd_readout_norm(int64_t rows, int64_t width, int in_dtype, int out_dtype, const float* o,
+                     const void* gate, const float* weight, const float* bias, float eps, void* y,
+                     void* stream);
 
 #ifdef __cplusplus
 }

@@ -33,7 +33,8 @@ EXPORTS = ("ssd_status_str", "ssd_last_error", "ssd_version", "ssd_rglru_scan", 
            "ssd_rglru_update",
            "ssd_selective_scan", "ssd_selective_update", "ssd_hgrn2_scan", "ssd_hgrn2_update", "ssd_minmax_scan",
            "ssd_minmax_update", "ssd_minmax_scan_backward", "ssd_causal_conv1d", "ssd_causal_conv1d_update",
-           "ssd_selective_scan_backward", "ssd_hgrn2_scan_backward")
+           "ssd_selective_scan_backward", "ssd_hgrn2_scan_backward", "ssd_hgrn2_key_scan", "ssd_hgrn2_key_update",
+           "ssd_readout_norm")
 
 
 class SSDError(RuntimeError):
@@ -91,6 +92,10 @@ def lib() -> ctypes.CDLL:
                                      ctypes.c_float, _fp, _vp, _fp, _vp]
         L.ssd_hgrn2_update.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp,
                                        ctypes.c_float, _fp, _vp, _vp]
+        L.ssd_hgrn2_key_scan.argtypes = L.ssd_hgrn2_scan.argtypes
+        L.ssd_hgrn2_key_update.argtypes = L.ssd_hgrn2_update.argtypes
+        L.ssd_readout_norm.argtypes = [_i64, _i64, ctypes.c_int, ctypes.c_int, _fp, _vp, _fp, _fp, ctypes.c_float, _vp,
+                                       _vp]
         L.ssd_hgrn2_scan_backward.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp,
                                               ctypes.c_float, _fp, _fp, _vp, _fp, _vp, _vp, _vp, _vp, _fp, _vp]
         for name in EXPORTS[3:]:
@@ -435,18 +440,20 @@ def selective_scan_backward(x, dt, A, Bm, Cm, dy, Dskip=None, z=None, dt_bias=No
 
 
 # ----------------------------------------------------------------------------- HGRN2
-def hgrn2_scan(q, k, v, g_logit, lower_bound: float, S0=None, return_last_state: bool = False, out_dtype=None):
-    """HGRN2 matrix-state scan over [B, L, H, d] (see ``ssd_hgrn2_scan``).  Returns o, or (o, S_last)."""
+def hgrn2_scan(q, k, v, g_logit, lower_bound: float, S0=None, return_last_state: bool = False, out_dtype=None,
+               gate_axis: str = "value"):
+    """HGRN2 matrix-state scan over [B, L, H, d] (see ``ssd_hgrn2_scan``; ``gate_axis="key"`` takes
+    ``ssd_hgrn2_key_scan``).  Returns o, or (o, S_last)."""
     torch = _torch()
     B, L, H, d = q.shape
     code = _act([q, k, v, g_logit], ["q", "k", "v", "g_logit"])
     oc = _out_code(out_dtype)
     o = torch.empty((B, L, H, d), device=q.device, dtype=torch.bfloat16 if oc == SSD_BF16 else torch.float32)
     S_last = torch.empty((B, H, d, d), device=q.device, dtype=torch.float32) if return_last_state else None
-    st = lib().ssd_hgrn2_scan(B, L, H, d, code, oc, _dev(q, "q"), _dev(k, "k", q.shape), _dev(v, "v", q.shape),
-                              _dev(g_logit, "g_logit", q.shape), float(lower_bound),
-                              _dev(S0, "S0", (B, H, d, d), torch.float32), _dev(o, "o"), _dev(S_last, "S_last"),
-                              _stream(q.device))
+    fn = _gate_axis_fn(gate_axis, lib().ssd_hgrn2_scan, lib().ssd_hgrn2_key_scan)
+    st = fn(B, L, H, d, code, oc, _dev(q, "q"), _dev(k, "k", q.shape), _dev(v, "v", q.shape),
+            _dev(g_logit, "g_logit", q.shape), float(lower_bound), _dev(S0, "S0", (B, H, d, d), torch.float32),
+            _dev(o, "o"), _dev(S_last, "S_last"), _stream(q.device))
     _raise(st, "hgrn2_scan")
     return (o, S_last) if return_last_state else o
 
@@ -473,18 +480,44 @@ def hgrn2_scan_backward(q, k, v, g_logit, lower_bound: float, do, S0=None, dS_la
     return g
 
 
-def hgrn2_update(q, k, v, g_logit, lower_bound: float, S, out_dtype=None):
+def _gate_axis_fn(gate_axis, value_fn, key_fn):
+    if gate_axis == "value":
+        return value_fn
+    if gate_axis == "key":
+        return key_fn
+    raise ValueError('gate_axis must be "value" or "key"')
+
+
+def hgrn2_update(q, k, v, g_logit, lower_bound: float, S, out_dtype=None, gate_axis: str = "value"):
     """One decode step; ``S`` [B, H, d, d] fp32 is updated in place.  Returns o [B, H, d]."""
     torch = _torch()
     B, H, d = q.shape
     code = _act([q, k, v, g_logit], ["q", "k", "v", "g_logit"])
     oc = _out_code(out_dtype)
     o = torch.empty((B, H, d), device=q.device, dtype=torch.bfloat16 if oc == SSD_BF16 else torch.float32)
-    st = lib().ssd_hgrn2_update(B, H, d, code, oc, _dev(q, "q"), _dev(k, "k", q.shape), _dev(v, "v", q.shape),
-                                _dev(g_logit, "g_logit", q.shape), float(lower_bound),
-                                _dev(S, "S", (B, H, d, d), torch.float32), _dev(o, "o"), _stream(q.device))
+    fn = _gate_axis_fn(gate_axis, lib().ssd_hgrn2_update, lib().ssd_hgrn2_key_update)
+    st = fn(B, H, d, code, oc, _dev(q, "q"), _dev(k, "k", q.shape), _dev(v, "v", q.shape),
+            _dev(g_logit, "g_logit", q.shape), float(lower_bound), _dev(S, "S", (B, H, d, d), torch.float32),
+            _dev(o, "o"), _stream(q.device))
     _raise(st, "hgrn2_update")
     return o
+
+
+def readout_norm(o, gate=None, weight=None, bias=None, eps: float = 1e-5, out_dtype=None):
+    """LayerNorm over the last axis of the fp32 ``o`` (biased variance), affine, times silu(gate) (see
+    ``ssd_readout_norm``).  For the layer's norm over its hidden size pass o as [B, L, H * d]."""
+    torch = _torch()
+    width = int(o.shape[-1])
+    rows = o.numel() // width if width else 0
+    code = _act([gate], ["gate"]) if gate is not None else SSD_BF16 if out_dtype == torch.bfloat16 else SSD_F32
+    oc = _out_code(out_dtype)
+    y = torch.empty(o.shape, device=o.device, dtype=torch.bfloat16 if oc == SSD_BF16 else torch.float32)
+    st = lib().ssd_readout_norm(rows, width, code, oc, _dev(o, "o", None, torch.float32), _dev(gate, "gate", o.shape),
+                                _dev(weight, "weight", (width,), torch.float32),
+                                _dev(bias, "bias", (width,), torch.float32), float(eps), _dev(y, "y"),
+                                _stream(o.device))
+    _raise(st, "readout_norm")
+    return y
 
 
 __all__ = ["chunk_states_shape", "SCAN_CHUNK", "rglru_scan", "rglru_scan_backward", "rglru_update", "selective_scan", "selective_scan_backward", "selective_update", "hgrn2_scan", "hgrn2_update",

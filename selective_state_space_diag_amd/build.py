@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libssd.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "scan1.hip", "conv1d.hip", "selective.hip", "hgrn2.hip", "hgrn2_bwd.hip"]
+SOURCES = ["api.cpp", "scan1.hip", "conv1d.hip", "selective.hip", "hgrn2.hip", "hgrn2_sweep.hip", "norm.hip"]
 ARCH = "gfx950"
 # Packed fp32 VALU instructions are disabled for all device code.
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,

@@ -505,9 +505,9 @@ int ssd_selective_update(int64_t B, int64_t D, int64_t N, int in_dtype, int out_
 // ============================================================================ HGRN2
 static bool supported_d(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
-int ssd_hgrn2_scan(int64_t B, int64_t L, int64_t H, int64_t d, int in_dtype, int out_dtype, const void* q,
-                   const void* k, const void* v, const void* g_logit, float lower_bound, const float* S0, void* o,
-                   float* S_last, void* stream) {
+static int hgrn2_scan_common(bool key, int64_t B, int64_t L, int64_t H, int64_t d, int in_dtype, int out_dtype,
+                             const void* q, const void* k, const void* v, const void* g_logit, float lower_bound,
+                             const float* S0, void* o, float* S_last, void* stream) {
   SSD_TRY(check_dtypes(in_dtype, out_dtype));
   if (B < 0 || L < 0 || H < 0 || d < 0) return fail(SSD_ERR_SHAPE, "negative size");
   if (!supported_d(d)) return fail(SSD_ERR_SHAPE, "head dim d must be 16, 32, 64 or 128");
@@ -528,11 +528,31 @@ int ssd_hgrn2_scan(int64_t B, int64_t L, int64_t H, int64_t d, int in_dtype, int
   if (L == 0) return hip_status(ssd::launch_copy_or_zero(S_last, S0, B * H * d * d, s), "hgrn2_scan");
   ssd::Hgrn2ScanArgs a{B, L, H, d, in_dtype == SSD_BF16, out_dtype == SSD_BF16, q, k, v, g_logit, lower_bound, S0, o,
                        S_last};
+  if (key) {
+    // the key-axis sweep addresses a head's rows with 32-bit offsets (as the backward sweeps)
+    if ((L + 16) * H * d * 4 >= (int64_t)1 << 32) return fail(SSD_ERR_SHAPE, "problem too large");
+    return hip_status(ssd::launch_hgrn2_key_scan(a, s), "hgrn2_key_scan launch");
+  }
   return hip_status(ssd::launch_hgrn2_scan(a, s), "hgrn2_scan launch");
 }
 
-int ssd_hgrn2_update(int64_t B, int64_t H, int64_t d, int in_dtype, int out_dtype, const void* q, const void* k,
-                     const void* v, const void* g_logit, float lower_bound, float* S, void* o, void* stream) {
+int ssd_hgrn2_scan(int64_t B, int64_t L, int64_t H, int64_t d, int in_dtype, int out_dtype, const void* q,
+                   const void* k, const void* v, const void* g_logit, float lower_bound, const float* S0, void* o,
+                   float* S_last, void* stream) {
+  return hgrn2_scan_common(false, B, L, H, d, in_dtype, out_dtype, q, k, v, g_logit, lower_bound, S0, o, S_last,
+                           stream);
+}
+
+int ssd_hgrn2_key_scan(int64_t B, int64_t L, int64_t H, int64_t d, int in_dtype, int out_dtype, const void* q,
+                       const void* k, const void* v, const void* g_logit, float lower_bound, const float* S0, void* o,
+                       float* S_last, void* stream) {
+  return hgrn2_scan_common(true, B, L, H, d, in_dtype, out_dtype, q, k, v, g_logit, lower_bound, S0, o, S_last,
+                           stream);
+}
+
+static int hgrn2_update_common(bool key, int64_t B, int64_t H, int64_t d, int in_dtype, int out_dtype,
+                               const void* q, const void* k, const void* v, const void* g_logit, float lower_bound,
+                               float* S, void* o, void* stream) {
   SSD_TRY(check_dtypes(in_dtype, out_dtype));
   if (B < 0 || H < 0 || d < 0) return fail(SSD_ERR_SHAPE, "negative size");
   if (!supported_d(d)) return fail(SSD_ERR_SHAPE, "head dim d must be 16, 32, 64 or 128");
@@ -549,7 +569,42 @@ int ssd_hgrn2_update(int64_t B, int64_t H, int64_t d, int in_dtype, int out_dtyp
   SSD_TRY(check_alias(outs, ins));
   if (n == 0) return ok();
   ssd::Hgrn2UpdateArgs a{B, H, d, in_dtype == SSD_BF16, out_dtype == SSD_BF16, q, k, v, g_logit, lower_bound, S, o};
-  return hip_status(ssd::launch_hgrn2_update(a, static_cast<hipStream_t>(stream)), "hgrn2_update launch");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (key) return hip_status(ssd::launch_hgrn2_key_update(a, s), "hgrn2_key_update launch");
+  return hip_status(ssd::launch_hgrn2_update(a, s), "hgrn2_update launch");
+}
+
+int ssd_hgrn2_update(int64_t B, int64_t H, int64_t d, int in_dtype, int out_dtype, const void* q, const void* k,
+                     const void* v, const void* g_logit, float lower_bound, float* S, void* o, void* stream) {
+  return hgrn2_update_common(false, B, H, d, in_dtype, out_dtype, q, k, v, g_logit, lower_bound, S, o, stream);
+}
+
+int ssd_hgrn2_key_update(int64_t B, int64_t H, int64_t d, int in_dtype, int out_dtype, const void* q, const void* k,
+                         const void* v, const void* g_logit, float lower_bound, float* S, void* o, void* stream) {
+  return hgrn2_update_common(true, B, H, d, in_dtype, out_dtype, q, k, v, g_logit, lower_bound, S, o, stream);
+}
+
+int ssd_readout_norm(int64_t rows, int64_t width, int in_dtype, int out_dtype, const float* o, const void* gate,
+                     const float* weight, const float* bias, float eps, void* y, void* stream) {
+  SSD_TRY(check_dtypes(in_dtype, out_dtype));
+  if (rows < 0 || width < 0) return fail(SSD_ERR_SHAPE, "negative size");
+  if (width > 8192) return fail(SSD_ERR_SHAPE, "width must be at most 8192");
+  if (rows >= (int64_t)1 << 31 || too_big({rows, width})) return fail(SSD_ERR_SHAPE, "problem too large");
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(SSD_ERR_VALUE, "eps must be finite and >= 0");
+  const int64_t n = rows * width;
+  if (n > 0 && (!o || !y)) return fail(SSD_ERR_NULL, "o and y are required");
+  std::vector<Span> ins = {{"o", o, (size_t)n * 4},
+                           {"gate", gate, (size_t)n * esize(in_dtype)},
+                           {"weight", weight, (size_t)width * 4},
+                           {"bias", bias, (size_t)width * 4}};
+  std::vector<Span> outs = {{"y", y, (size_t)n * esize(out_dtype)}};
+  std::vector<Span> all = ins;
+  all.insert(all.end(), outs.begin(), outs.end());
+  SSD_TRY(check_align(all));
+  SSD_TRY(check_alias(outs, ins));
+  if (n == 0) return ok();
+  ssd::ReadoutNormArgs a{rows, width, in_dtype == SSD_BF16, out_dtype == SSD_BF16, o, gate, weight, bias, eps, y};
+  return hip_status(ssd::launch_readout_norm(a, static_cast<hipStream_t>(stream)), "readout_norm launch");
 }
 
 int ssd_hgrn2_scan_backward(int64_t B, int64_t L, int64_t H, int64_t d, int in_dtype, int out_dtype, const void* q,

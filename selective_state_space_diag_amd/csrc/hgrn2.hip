@@ -65,8 +65,9 @@ __global__ __launch_bounds__(DH < 64 ? 64 : DH) void hgrn2_recurrent_kernel(H2Pa
   }
 }
 
-// Decode step: one wave per value row; o_i reduced across the wave.
-template <typename Tin, typename Tout>
+// Decode step: one wave per value row; o_i reduced across the wave.  KEY: the gate scales the key
+// columns, S[i][j] = g_j S[i][j] + v_i k_j (the key-axis reading), instead of the value rows.
+template <typename Tin, typename Tout, bool KEY>
 __global__ __launch_bounds__(256) void hgrn2_update_kernel(int64_t rows, int64_t d, const void* q, const void* k,
                                                            const void* v, const void* g, float lb, float* S,
                                                            void* o) {
@@ -75,12 +76,13 @@ __global__ __launch_bounds__(256) void hgrn2_update_kernel(int64_t rows, int64_t
   if (r >= rows) return;
   const int64_t bh = r / d;
   const int64_t i = r - bh * d;
-  const float gi = fmaf(1.0f - lb, sigmoid_f(io<Tin>::load(g, bh * d + i)), lb);
+  const float gi = KEY ? 0.0f : fmaf(1.0f - lb, sigmoid_f(io<Tin>::load(g, bh * d + i)), lb);
   const float vi = io<Tin>::load(v, bh * d + i);
   float acc = 0.0f;
   for (int64_t j = lane; j < d; j += 64) {
     const int64_t e = r * d + j;
-    const float s = fmaf(gi, S[e], vi * io<Tin>::load(k, bh * d + j));
+    const float gg = KEY ? fmaf(1.0f - lb, sigmoid_f(io<Tin>::load(g, bh * d + j)), lb) : gi;
+    const float s = fmaf(gg, S[e], vi * io<Tin>::load(k, bh * d + j));
     S[e] = s;
     acc = fmaf(s, io<Tin>::load(q, bh * d + j), acc);
   }
@@ -612,20 +614,26 @@ hipError_t launch_hgrn2_scan(const Hgrn2ScanArgs& a, hipStream_t s) {
   return a.out_bf16 ? launch_recurrent_t<bf16_t, bf16_t>(p, s) : launch_recurrent_t<bf16_t, float>(p, s);
 }
 
-hipError_t launch_hgrn2_update(const Hgrn2UpdateArgs& a, hipStream_t s) {
+namespace {
+template <bool KEY>
+hipError_t launch_update_t(const Hgrn2UpdateArgs& a, hipStream_t s) {
   const int64_t rows = a.B * a.H * a.d;
   const dim3 grid((unsigned)((rows + 3) / 4));
   if (!a.in_bf16)
-    hipLaunchKernelGGL((hgrn2_update_kernel<float, float>), grid, dim3(256), 0, s, rows, a.d, a.q, a.k, a.v,
+    hipLaunchKernelGGL((hgrn2_update_kernel<float, float, KEY>), grid, dim3(256), 0, s, rows, a.d, a.q, a.k, a.v,
                        a.g_logit, a.lower_bound, a.S, a.o);
   else if (a.out_bf16)
-    hipLaunchKernelGGL((hgrn2_update_kernel<bf16_t, bf16_t>), grid, dim3(256), 0, s, rows, a.d, a.q, a.k, a.v,
+    hipLaunchKernelGGL((hgrn2_update_kernel<bf16_t, bf16_t, KEY>), grid, dim3(256), 0, s, rows, a.d, a.q, a.k, a.v,
                        a.g_logit, a.lower_bound, a.S, a.o);
   else
-    hipLaunchKernelGGL((hgrn2_update_kernel<bf16_t, float>), grid, dim3(256), 0, s, rows, a.d, a.q, a.k, a.v,
+    hipLaunchKernelGGL((hgrn2_update_kernel<bf16_t, float, KEY>), grid, dim3(256), 0, s, rows, a.d, a.q, a.k, a.v,
                        a.g_logit, a.lower_bound, a.S, a.o);
   return hipGetLastError();
 }
+}  // namespace
+
+hipError_t launch_hgrn2_update(const Hgrn2UpdateArgs& a, hipStream_t s) { return launch_update_t<false>(a, s); }
+hipError_t launch_hgrn2_key_update(const Hgrn2UpdateArgs& a, hipStream_t s) { return launch_update_t<true>(a, s); }
 
 namespace {
 __global__ __launch_bounds__(256) void copy_or_zero_kernel(float* dst, const float* src, int64_t n) {

@@ -1,4 +1,5 @@
-// hgrn2_bwd.hip -- backward of the HGRN2 matrix-state scan for gfx950.
+// hgrn2_sweep.hip -- register-resident token sweeps over HGRN2 heads for gfx950: the backward of the
+// matrix-state scan, and the key-axis-gated forward.
 //
 // Forward (frankenstein-transformer documentation, "HGRN2 Attention", state update and gate):
 //   g_t = lb + (1 - lb) sigmoid(x_t),  S_t[i][j] = g_t[i] S_{t-1}[i][j] + v_t[i] k_t[j],
@@ -20,14 +21,17 @@
 // checkpoints that kDQ writes.  bf16 inputs (2e-2 budget) skip the checkpoints.  The first token
 // is always exact: dlog g_0 = g_0 sum_j R_0[i][j] S0[i][j] (0 without an initial state).
 //
-// Three sweeps, each a sequential pass over the tokens of one head that keeps a d x d matrix in
-// registers and needs no cross-row sums beyond 16 lanes:
+// Four sweeps, each a sequential pass over the tokens of one head that keeps a d x d matrix in
+// registers and needs no cross-row sums beyond 16 lanes; three make the backward:
 //   kDQ  forward, S column-owned:  S[i][j] update, dq_t[j] = sum_i do_t[i] S_t[i][j]; writes S_L;
 //   kDK  reverse, R column-owned:  R[i][j] update, dk_t[j] = sum_i v_t[i] R_t[i][j];
 //   kDV  reverse, R row-owned:     R[i][j] update, dv_t[i] = sum_j R_t[i][j] k_t[j], the running
-//        dlog g (from o, dv and S_L), dx_t and dS0.
+//        dlog g (from o, dv and S_L), dx_t and dS0;
+// and one is the forward under the key-axis reading of the gate (the convention of the HGRN2 paper
+// the page cites, not printed there), S_t[i][j] = g_t[j] S_{t-1}[i][j] + v_t[i] k_t[j]:
+//   kFK  forward, S row-owned:       S[i][j] update, o_t[i] = sum_j S_t[i][j] q_t[j]; writes S_last.
 // Thread layout: a thread owns AB consecutive "a" indices (the owned axis: j for kDQ/kDK, i for
-// kDV) and the d/16 "m" indices of its part p = lane % 16 (the summed axis), so the sum over m is
+// kDV/kFK) and the d/16 "m" indices of its part p = lane % 16 (the summed axis), so the sum over m is
 // a sum over the 16 lanes of a row group.  The per-token vectors of the head (gates, q, k, v, do,
 // o) are staged in LDS, eight tokens per stage, double-buffered: the next stage's loads are
 // issued before the current stage is computed and written to LDS after it.
@@ -39,12 +43,12 @@ namespace {
 
 typedef int v4i_t __attribute__((ext_vector_type(4)));
 
-enum { kDQ = 0, kDK = 1, kDV = 2 };
+enum { kDQ = 0, kDK = 1, kDV = 2, kFK = 3 };
 constexpr int kTS = 8;     // tokens per stage
 constexpr int kParts = 16; // lanes that share the summed axis
 constexpr int kAnchor = 32; // tokens between exact restarts of the running dlog g (checkpointed states)
 
-struct H2BwdParams {
+struct H2SweepParams {
   int64_t B, L, H;
   const void* q;
   const void* k;
@@ -62,6 +66,8 @@ struct H2BwdParams {
   void* dv;
   void* dx;
   float* dS0;
+  void* y;         // kFK: output o
+  float* S_last;   // kFK: final state, or NULL
 };
 
 // What slot s of the staged vectors holds, per sweep.
@@ -71,7 +77,7 @@ template <> struct Slots<kDQ> {  // m = i: gate(t), v, do; a = j: k
   static constexpr int n = 4;
   static __device__ __forceinline__ int kind(int s) { return s == 0 ? kGate : kAct; }
   static __device__ __forceinline__ int shift(int) { return 0; }
-  static __device__ __forceinline__ const void* src(const H2BwdParams& p, int s) {
+  static __device__ __forceinline__ const void* src(const H2SweepParams& p, int s) {
     return s == 0 ? p.x : s == 1 ? p.v : s == 2 ? p.dO : p.k;
   }
 };
@@ -79,8 +85,16 @@ template <> struct Slots<kDK> {  // m = i: gate(t+1), do, v; a = j: q
   static constexpr int n = 4;
   static __device__ __forceinline__ int kind(int s) { return s == 0 ? kGate : kAct; }
   static __device__ __forceinline__ int shift(int s) { return s == 0 ? 1 : 0; }
-  static __device__ __forceinline__ const void* src(const H2BwdParams& p, int s) {
+  static __device__ __forceinline__ const void* src(const H2SweepParams& p, int s) {
     return s == 0 ? p.x : s == 1 ? p.dO : s == 2 ? p.v : p.q;
+  }
+};
+template <> struct Slots<kFK> {  // m = j: gate(t), k, q; a = i: v
+  static constexpr int n = 4;
+  static __device__ __forceinline__ int kind(int s) { return s == 0 ? kGate : kAct; }
+  static __device__ __forceinline__ int shift(int) { return 0; }
+  static __device__ __forceinline__ const void* src(const H2SweepParams& p, int s) {
+    return s == 0 ? p.x : s == 1 ? p.k : s == 2 ? p.q : p.v;
   }
 };
 template <> struct Slots<kDV> {  // m = j: q, k; a = i: do, o, v, gate(t+1), ratio(t)
@@ -89,7 +103,7 @@ template <> struct Slots<kDV> {  // m = j: q, k; a = i: do, o, v, gate(t+1), rat
     return s == 3 ? kOut : s == 5 ? kGate : s == 6 ? kRatio : kAct;
   }
   static __device__ __forceinline__ int shift(int s) { return s == 5 ? 1 : 0; }
-  static __device__ __forceinline__ const void* src(const H2BwdParams& p, int s) {
+  static __device__ __forceinline__ const void* src(const H2SweepParams& p, int s) {
     return s == 0 ? p.q : s == 1 ? p.k : s == 2 ? p.dO : s == 3 ? (const void*)p.o : s == 4 ? p.v : p.x;
   }
 };
@@ -162,11 +176,11 @@ template <int DH, int AB> struct SweepShape {
 };
 
 template <int MODE, typename Tin, typename Tout, int DH, int AB>
-__global__ __launch_bounds__((SweepShape<DH, AB>::NT)) void hgrn2_bwd_sweep_kernel(H2BwdParams p) {
+__global__ __launch_bounds__((SweepShape<DH, AB>::NT)) void hgrn2_sweep_kernel(H2SweepParams p) {
   using SS = SweepShape<DH, AB>;
   using SL = Slots<MODE>;
   constexpr int MP = SS::MP, NT = SS::NT, PER = SS::PER, NV = SL::n;
-  constexpr bool REV = MODE != kDQ;
+  constexpr bool REV = MODE == kDK || MODE == kDV;
   constexpr int ES = (int)sizeof(Tout);
   __shared__ __align__(16) float stg[2][NV][kTS][DH];
 
@@ -202,9 +216,9 @@ __global__ __launch_bounds__((SweepShape<DH, AB>::NT)) void hgrn2_bwd_sweep_kern
   const bool writer = (pp % SUB) == 0;
   constexpr uint32_t kDrop = 0xFFFFFF00u;
   const uint32_t out_bytes = (uint32_t)(((L - 1) * row_stride + DH) * ES);
-  const auto wo0 = make_window(static_cast<char*>(MODE == kDQ ? p.dq : MODE == kDK ? p.dk : p.dv) + head_base * ES,
-                               out_bytes);
-  const auto wo1 = make_window(static_cast<char*>(p.dx) + head_base * ES, out_bytes);
+  void* out0 = MODE == kDQ ? p.dq : MODE == kDK ? p.dk : MODE == kDV ? p.dv : p.y;
+  const auto wo0 = make_window(static_cast<char*>(out0) + head_base * ES, out_bytes);
+  const auto wo1 = make_window(static_cast<char*>(MODE == kDV ? p.dx : out0) + head_base * ES, out_bytes);
 
   // ---- staging: the stages are the token blocks [c kTS, c kTS + kTS), taken in increasing c
   // (forward) or decreasing c (reverse); tokens at or past L are staged as exact no-ops for the
@@ -291,6 +305,11 @@ __global__ __launch_bounds__((SweepShape<DH, AB>::NT)) void hgrn2_bwd_sweep_kern
       }
     }
     cum = (double)part_reduce<AB>(part, pp);
+  } else if constexpr (MODE == kFK) {  // mat[u][e] = S[a0 + u][m0 + e]
+#pragma unroll
+    for (int u = 0; u < AB; ++u)
+#pragma unroll
+      for (int e = 0; e < MP; ++e) mat[u][e] = p.S0 ? p.S0[mbase + (int64_t)(a0 + u) * DH + m0 + e] : 0.0f;
   } else {
     const float* init = MODE == kDQ ? p.S0 : p.dS_last;
 #pragma unroll
@@ -347,7 +366,7 @@ __global__ __launch_bounds__((SweepShape<DH, AB>::NT)) void hgrn2_bwd_sweep_kern
         o.sc[1] = stg[buf][3][tau][ia];
         o.sc[2] = stg[buf][4][tau][ia];
         o.sc[3] = stg[buf][6][tau][ia];
-      } else {
+      } else {  // kFK: m = gate, k, q; a = v.  Others: m = gate, x, y; a = k or q.
         lds_vec<MP>(&stg[buf][0][tau][m0], o.m[0]);
         lds_vec<MP>(&stg[buf][1][tau][m0], o.m[1]);
         lds_vec<MP>(&stg[buf][2][tau][m0], o.m[2]);
@@ -385,6 +404,19 @@ __global__ __launch_bounds__((SweepShape<DH, AB>::NT)) void hgrn2_bwd_sweep_kern
         const float dg = (float)cum * cur.sc[3];
         win<Tout, 1>::store(wo0, lo, 0u, &dvt);
         win<Tout, 1>::store(wo1, lo, 0u, &dg);
+      } else if constexpr (MODE == kFK) {
+        // S = S diag(g) + v k^T,  o = S q
+#pragma unroll
+        for (int u = 0; u < AB; ++u) {
+          acc[u] = 0.0f;
+#pragma unroll
+          for (int e = 0; e < MP; ++e) {
+            mat[u][e] = fmaf(cur.m[0][e], mat[u][e], cur.a[0][u] * cur.m[1][e]);
+            acc[u] = fmaf(mat[u][e], cur.m[2][e], acc[u]);
+          }
+        }
+        const float ot = part_reduce<AB>(acc, pp);
+        win<Tout, 1>::store(wo0, lo, 0u, &ot);
       } else {
         // kDQ: g(t), v, do over i and k over j:  S = g S + v k^T, dq = S^T do
         // kDK: g(t+1), do, v over i and q over j: R = g R + do q^T, dk = R^T v
@@ -421,6 +453,14 @@ __global__ __launch_bounds__((SweepShape<DH, AB>::NT)) void hgrn2_bwd_sweep_kern
 #pragma unroll
       for (int e = 0; e < MP; ++e) p.S_L[mbase + (int64_t)(m0 + e) * DH + a0 + u] = mat[u][e];
   }
+  if constexpr (MODE == kFK) {
+    if (p.S_last) {
+#pragma unroll
+      for (int u = 0; u < AB; ++u)
+#pragma unroll
+        for (int e = 0; e < MP; ++e) p.S_last[mbase + (int64_t)(a0 + u) * DH + m0 + e] = mat[u][e];
+    }
+  }
   if constexpr (MODE == kDV) {
     if (L > 0) {
       // mat = R_0 (tokens before 0 were no-ops): the first token's dlog g is exact,
@@ -443,15 +483,15 @@ __global__ __launch_bounds__((SweepShape<DH, AB>::NT)) void hgrn2_bwd_sweep_kern
 }
 
 template <int MODE, typename Tin, typename Tout, int DH>
-void launch_sweep(const H2BwdParams& p, hipStream_t s) {
+void launch_sweep(const H2SweepParams& p, hipStream_t s) {
   constexpr int AB = 4;
   using SS = SweepShape<DH, AB>;
   const dim3 grid((unsigned)(p.B * p.H * SS::W));
-  hipLaunchKernelGGL((hgrn2_bwd_sweep_kernel<MODE, Tin, Tout, DH, AB>), grid, dim3(SS::NT), 0, s, p);
+  hipLaunchKernelGGL((hgrn2_sweep_kernel<MODE, Tin, Tout, DH, AB>), grid, dim3(SS::NT), 0, s, p);
 }
 
 template <int MODE, typename Tin, typename Tout>
-void launch_sweep_d(const H2BwdParams& p, int64_t d, hipStream_t s) {
+void launch_sweep_d(const H2SweepParams& p, int64_t d, hipStream_t s) {
   switch (d) {
     case 16: launch_sweep<MODE, Tin, Tout, 16>(p, s); break;
     case 32: launch_sweep<MODE, Tin, Tout, 32>(p, s); break;
@@ -461,7 +501,7 @@ void launch_sweep_d(const H2BwdParams& p, int64_t d, hipStream_t s) {
 }
 
 template <typename Tin, typename Tout>
-void launch_all(const H2BwdParams& p, int64_t d, hipStream_t s) {
+void launch_all(const H2SweepParams& p, int64_t d, hipStream_t s) {
   launch_sweep_d<kDQ, Tin, Tout>(p, d, s);
   launch_sweep_d<kDK, Tin, Tout>(p, d, s);
   launch_sweep_d<kDV, Tin, Tout>(p, d, s);
@@ -488,6 +528,20 @@ size_t hgrn2_scan_backward_scratch_bytes(const Hgrn2BwdArgs& a) {
   return lay.state + lay.ckpt + lay.outs;
 }
 
+hipError_t launch_hgrn2_key_scan(const Hgrn2ScanArgs& a, hipStream_t s) {
+  H2SweepParams p{};
+  p.B = a.B; p.L = a.L; p.H = a.H;
+  p.q = a.q; p.k = a.k; p.v = a.v; p.x = a.g_logit; p.lb = a.lower_bound;
+  p.S0 = a.S0; p.y = a.o; p.S_last = a.S_last;
+  if (!a.in_bf16)
+    launch_sweep_d<kFK, float, float>(p, a.d, s);
+  else if (a.out_bf16)
+    launch_sweep_d<kFK, bf16_t, bf16_t>(p, a.d, s);
+  else
+    launch_sweep_d<kFK, bf16_t, float>(p, a.d, s);
+  return hipGetLastError();
+}
+
 hipError_t launch_hgrn2_scan_backward(const Hgrn2BwdArgs& a, hipStream_t s) {
   char* scratch = static_cast<char*>(a.scratch);
   const BwdLayout lay(a);
@@ -501,7 +555,7 @@ hipError_t launch_hgrn2_scan_backward(const Hgrn2BwdArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     o = o_tmp;
   }
-  H2BwdParams p;
+  H2SweepParams p{};
   p.B = a.B; p.L = a.L; p.H = a.H;
   p.q = a.q; p.k = a.k; p.v = a.v; p.x = a.g_logit; p.dO = a.dO; p.o = o; p.lb = a.lower_bound;
   p.S0 = a.S0; p.dS_last = a.dS_last; p.S_L = S_L; p.ckpt = ckpt;

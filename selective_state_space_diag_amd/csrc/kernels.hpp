@@ -210,6 +210,22 @@ struct Hgrn2UpdateArgs {
   void* o;
 };
 hipError_t launch_hgrn2_update(const Hgrn2UpdateArgs& a, hipStream_t s);
+// Key-axis gating (S[i][j] = g_j S[i][j] + v_i k_j): the same arguments.
+hipError_t launch_hgrn2_key_scan(const Hgrn2ScanArgs& a, hipStream_t s);
+hipError_t launch_hgrn2_key_update(const Hgrn2UpdateArgs& a, hipStream_t s);
+
+// Readout LayerNorm over rows of `width` features (fp32 o), affine, times silu(gate).
+struct ReadoutNormArgs {
+  int64_t rows, width;
+  int in_bf16, out_bf16;  // gate dtype, output dtype
+  const float* o;
+  const void* gate;
+  const float* weight;
+  const float* bias;
+  float eps;
+  void* y;
+};
+hipError_t launch_readout_norm(const ReadoutNormArgs& a, hipStream_t s);
 
 // Backward of the HGRN2 scan: o is the forward output in fp32 (NULL: recomputed into scratch).
 struct Hgrn2BwdArgs {

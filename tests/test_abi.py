@@ -205,6 +205,36 @@ def test_hgrn2_backward_validation(L):
     assert f(B=0) == OK
 
 
+def test_hgrn2_key_and_readout_norm_validation(L):
+    p = lambda k: None if k is None else ptr(k)
+    f = lambda B=2, Lq=16, d=64, lb=0.5, o=5, S0=None, SL=None: L.ssd_hgrn2_key_scan(
+        B, Lq, 4, d, BF16, F32, ptr(0), ptr(1), ptr(2), ptr(3), lb, p(S0), p(o), p(SL), None)
+    assert f(d=48) == SHAPE
+    assert f(lb=-1.0) == VALUE
+    assert f(o=None) == NULL
+    assert f(o=1) == ALIAS
+    assert f(S0=6, SL=6) == ALIAS
+    assert f(B=0) == OK
+    u = lambda d=64, S=4, o=5: L.ssd_hgrn2_key_update(2, 4, d, BF16, F32, ptr(0), ptr(1), ptr(2), ptr(3), 0.5, p(S),
+                                                      p(o), None)
+    assert u(d=100) == SHAPE
+    assert u(S=None) == NULL
+    assert u(o=4) == ALIAS
+    n = lambda rows=8, width=64, ind=BF16, outd=F32, o=0, g=1, w=None, b=None, eps=1e-5, y=4: L.ssd_readout_norm(
+        rows, width, ind, outd, p(o), p(g), p(w), p(b), eps, p(y), None)
+    assert n(width=8193) == SHAPE
+    assert n(rows=-1) == SHAPE
+    assert n(ind=F32, outd=BF16) == DTYPE
+    assert n(eps=-1.0) == VALUE
+    assert n(eps=float("nan")) == VALUE
+    assert n(o=None) == NULL
+    assert n(y=0) == ALIAS
+    assert n(y=1) == ALIAS
+    assert n(w=4, y=4) == ALIAS
+    assert L.ssd_readout_norm(8, 64, BF16, F32, ctypes.c_void_p(P + 4), None, None, None, 1e-5, ptr(4), None) == ALIGN
+    assert n(rows=0) == OK
+
+
 def test_python_layer_requires_gpu_tensors():
     torch = pytest.importorskip("torch")
     x = torch.zeros(1, 4, 8)
