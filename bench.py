@@ -343,7 +343,23 @@ def forms(args, device):
     vflops = 15 * B * L * H * dd * dd
     record("hgrn2_backward_bf16_B8_H16_d128_L4096", ms, B * L * H * dd * dd, hgrn2_bwd_bytes(B, L, H, dd),
            dict(valu_tflops=vflops / (ms * 1e-3) / 1e12, valu_frac=vflops / (ms * 1e-3) / 1e12 / FP32_SCALAR_FMA_TFLOPS))
-    del q, k, v, g, do, o
+    del do
+
+    # --- the key-axis gate reading on the same inputs (a register sweep: 5 d^2 fp32 flops per token
+    #     and head, the state update and the readout)
+    ms = time_calls(lambda kk: ssd.hgrn2_scan(q, k, v, g, 0.5, gate_axis="key"), 1, 3, 1)[0]
+    kflops = 5 * B * L * H * dd * dd
+    record("hgrn2_key_gate_bf16_B8_H16_d128_L4096", ms, B * L * H * dd * dd, hgrn2_bytes(B, L, H, dd),
+           dict(valu_tflops=kflops / (ms * 1e-3) / 1e12, valu_frac=kflops / (ms * 1e-3) / 1e12 / FP32_SCALAR_FMA_TFLOPS))
+
+    # --- readout LayerNorm over the hidden size (H d = 2048) with the silu output gate, on the scan's
+    #     fp32 output: o read (fp32), gate read (bf16), y written (fp32)
+    ogate = randn((B, L, H * dd))
+    wn, bn = torch.ones(H * dd, device=device), torch.zeros(H * dd, device=device)
+    o2 = o.view(B, L, H * dd)
+    ms = time_calls(lambda kk: ssd.readout_norm(o2, gate=ogate, weight=wn, bias=bn), 1, 10, 2)[0]
+    record("readout_norm_B8_L4096_width2048", ms, B * L * H * dd, B * L * H * dd * (4 + 2 + 4) + H * dd * 8)
+    del q, k, v, g, o, o2, ogate
 
     # --- packed varlen selective, L=131072, 32 sequences, D=4096, N=16
     Lt, D, N, ns = 131072, 4096, 16, 32
