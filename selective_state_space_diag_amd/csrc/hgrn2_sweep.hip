@@ -175,26 +175,28 @@ template <int DH, int AB> struct SweepShape {
                 "sweep shape");
 };
 
+// One sweep of mode MODE for workgroup `bid` of the `nb` that the mode uses; `lds` holds the
+// staging buffers (2 x the mode's slots x kTS x DH floats).
 template <int MODE, typename Tin, typename Tout, int DH, int AB>
-__global__ __launch_bounds__((SweepShape<DH, AB>::NT)) void hgrn2_sweep_kernel(H2SweepParams p) {
+__device__ __forceinline__ void sweep_body(const H2SweepParams& p, int64_t bid, int64_t nb, float* lds) {
   using SS = SweepShape<DH, AB>;
   using SL = Slots<MODE>;
   constexpr int MP = SS::MP, NT = SS::NT, PER = SS::PER, NV = SL::n;
   constexpr bool REV = MODE == kDK || MODE == kDV;
   constexpr int ES = (int)sizeof(Tout);
-  __shared__ __align__(16) float stg[2][NV][kTS][DH];
+  float(*stg)[NV][kTS][DH] = reinterpret_cast<float(*)[NV][kTS][DH]>(lds);
 
   const int tid = threadIdx.x;
   // the W workgroups of a head take block ids 8 apart, so that they share one XCD's L2 (block ids
   // are dealt to the XCDs in turn)
   int64_t head;
   int wsub;
-  if (SS::W == 2 && gridDim.x % 16 == 0) {
-    head = (int64_t)(blockIdx.x / 16) * 8 + (blockIdx.x % 8);
-    wsub = (int)((blockIdx.x / 8) % 2);
+  if (SS::W == 2 && nb % 16 == 0) {
+    head = (bid / 16) * 8 + (bid % 8);
+    wsub = (int)((bid / 8) % 2);
   } else {
-    head = blockIdx.x / SS::W;
-    wsub = (int)(blockIdx.x - head * SS::W);
+    head = bid / SS::W;
+    wsub = (int)(bid - head * SS::W);
   }
   const int64_t b = head / p.H, hh = head - b * p.H;
   const int pp = tid & (kParts - 1);
@@ -301,7 +303,7 @@ __global__ __launch_bounds__((SweepShape<DH, AB>::NT)) void hgrn2_sweep_kernel(H
         const int64_t off = mbase + (int64_t)(a0 + u) * DH + m0 + e;
         const float ds = p.dS_last ? p.dS_last[off] : 0.0f;
         mat[u][e] = ds;
-        part[u] = fmaf(ds, p.S_L[off], part[u]);
+        part[u] = p.dS_last ? fmaf(ds, p.S_L[off], part[u]) : 0.0f;
       }
     }
     cum = (double)part_reduce<AB>(part, pp);
@@ -482,29 +484,56 @@ __global__ __launch_bounds__((SweepShape<DH, AB>::NT)) void hgrn2_sweep_kernel(H
   }
 }
 
-template <int MODE, typename Tin, typename Tout, int DH>
-void launch_sweep(const H2SweepParams& p, hipStream_t s) {
-  constexpr int AB = 4;
-  using SS = SweepShape<DH, AB>;
-  const dim3 grid((unsigned)(p.B * p.H * SS::W));
-  hipLaunchKernelGGL((hgrn2_sweep_kernel<MODE, Tin, Tout, DH, AB>), grid, dim3(SS::NT), 0, s, p);
+constexpr int kNoMode = -1;
+// owned indices per thread of the key-axis forward (2 doubles the workgroups but measured slower)
+constexpr int kKeyAB = 4;
+template <int MODE> struct SlotCount { static constexpr int n = MODE < 0 ? 0 : Slots<(MODE < 0 ? 0 : MODE)>::n; };
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+// Up to three sweeps in one launch, their workgroups interleaved (block b runs mode b % NM), so
+// that independent sweeps share the CUs; the staging buffer is one array sized for the largest.
+template <typename Tin, typename Tout, int DH, int AB, int M0, int M1, int M2>
+__global__ __launch_bounds__((SweepShape<DH, AB>::NT)) void hgrn2_sweep_kernel(H2SweepParams p, int64_t nb) {
+  constexpr int NM = 1 + (M1 != kNoMode) + (M2 != kNoMode);
+  constexpr int NVMAX = cmax(SlotCount<M0>::n, cmax(SlotCount<M1>::n, SlotCount<M2>::n));
+  __shared__ __align__(16) float lds[2 * NVMAX * kTS * DH];
+  const int64_t bid = blockIdx.x / NM;
+  const int m = (int)(blockIdx.x % NM);
+  if (m == 0) sweep_body<M0, Tin, Tout, DH, AB>(p, bid, nb, lds);
+  if constexpr (M1 != kNoMode)
+    if (m == 1) sweep_body<(M1 < 0 ? 0 : M1), Tin, Tout, DH, AB>(p, bid, nb, lds);
+  if constexpr (M2 != kNoMode)
+    if (m == 2) sweep_body<(M2 < 0 ? 0 : M2), Tin, Tout, DH, AB>(p, bid, nb, lds);
 }
 
-template <int MODE, typename Tin, typename Tout>
+template <typename Tin, typename Tout, int DH, int AB, int M0, int M1, int M2>
+void launch_sweep(const H2SweepParams& p, hipStream_t s) {
+  constexpr int NM = 1 + (M1 != kNoMode) + (M2 != kNoMode);
+  using SS = SweepShape<DH, AB>;
+  const int64_t nb = p.B * p.H * SS::W;
+  hipLaunchKernelGGL((hgrn2_sweep_kernel<Tin, Tout, DH, AB, M0, M1, M2>), dim3((unsigned)(nb * NM)), dim3(SS::NT), 0,
+                     s, p, nb);
+}
+
+template <typename Tin, typename Tout, int M0, int M1 = kNoMode, int M2 = kNoMode, int AB = 4>
 void launch_sweep_d(const H2SweepParams& p, int64_t d, hipStream_t s) {
   switch (d) {
-    case 16: launch_sweep<MODE, Tin, Tout, 16>(p, s); break;
-    case 32: launch_sweep<MODE, Tin, Tout, 32>(p, s); break;
-    case 64: launch_sweep<MODE, Tin, Tout, 64>(p, s); break;
-    default: launch_sweep<MODE, Tin, Tout, 128>(p, s); break;
+    case 16: launch_sweep<Tin, Tout, 16, AB, M0, M1, M2>(p, s); break;
+    case 32: launch_sweep<Tin, Tout, 32, AB, M0, M1, M2>(p, s); break;
+    case 64: launch_sweep<Tin, Tout, 64, AB, M0, M1, M2>(p, s); break;
+    default: launch_sweep<Tin, Tout, 128, AB, M0, M1, M2>(p, s); break;
   }
 }
 
+// kDV needs kDQ's final state (for dS_last) and checkpoints (fp32 inputs); kDK depends on neither.
 template <typename Tin, typename Tout>
 void launch_all(const H2SweepParams& p, int64_t d, hipStream_t s) {
-  launch_sweep_d<kDQ, Tin, Tout>(p, d, s);
-  launch_sweep_d<kDK, Tin, Tout>(p, d, s);
-  launch_sweep_d<kDV, Tin, Tout>(p, d, s);
+  if (!p.dS_last && !p.ckpt) {
+    launch_sweep_d<Tin, Tout, kDV, kDQ, kDK>(p, d, s);
+  } else {
+    launch_sweep_d<Tin, Tout, kDQ>(p, d, s);
+    launch_sweep_d<Tin, Tout, kDV, kDK>(p, d, s);
+  }
 }
 
 }  // namespace
@@ -534,11 +563,11 @@ hipError_t launch_hgrn2_key_scan(const Hgrn2ScanArgs& a, hipStream_t s) {
   p.q = a.q; p.k = a.k; p.v = a.v; p.x = a.g_logit; p.lb = a.lower_bound;
   p.S0 = a.S0; p.y = a.o; p.S_last = a.S_last;
   if (!a.in_bf16)
-    launch_sweep_d<kFK, float, float>(p, a.d, s);
+    launch_sweep_d<float, float, kFK, kNoMode, kNoMode, kKeyAB>(p, a.d, s);
   else if (a.out_bf16)
-    launch_sweep_d<kFK, bf16_t, bf16_t>(p, a.d, s);
+    launch_sweep_d<bf16_t, bf16_t, kFK, kNoMode, kNoMode, kKeyAB>(p, a.d, s);
   else
-    launch_sweep_d<kFK, bf16_t, float>(p, a.d, s);
+    launch_sweep_d<bf16_t, float, kFK, kNoMode, kNoMode, kKeyAB>(p, a.d, s);
   return hipGetLastError();
 }
 
