@@ -44,7 +44,9 @@ namespace {
 typedef int v4i_t __attribute__((ext_vector_type(4)));
 
 enum { kDQ = 0, kDK = 1, kDV = 2, kFK = 3 };
-constexpr int kTS = 8;     // tokens per stage
+// tokens per stage: 8, or 4 for kDV, whose seven staged vectors would otherwise hold 56 KB of LDS
+// per workgroup (two workgroups per CU instead of three when it shares a launch)
+template <int MODE> struct StageLen { static constexpr int v = MODE == kDV ? 4 : 8; };
 constexpr int kParts = 16; // lanes that share the summed axis
 constexpr int kAnchor = 32; // tokens between exact restarts of the running dlog g (checkpointed states)
 
@@ -165,21 +167,22 @@ __device__ __forceinline__ void lds_vec(const float* p, float (&r)[MP]) {
   }
 }
 
-template <int DH, int AB> struct SweepShape {
+template <int DH, int AB, int TS> struct SweepShape {
   static constexpr int MP = DH / kParts;          // summed-axis entries per thread
   static constexpr int TH = DH / AB * kParts;     // threads per head
   static constexpr int NT = TH < 256 ? TH : 256;  // threads per workgroup
   static constexpr int W = TH / NT;               // workgroups per head
-  static constexpr int PER = kTS * DH / NT;       // staged elements per thread and slot
-  static_assert(DH % kParts == 0 && TH % NT == 0 && (kTS * DH) % NT == 0 && PER <= 4 && DH % PER == 0,
+  static constexpr int PER = TS * DH / NT;        // staged elements per thread and slot
+  static_assert(DH % kParts == 0 && TH % NT == 0 && (TS * DH) % NT == 0 && PER >= 1 && PER <= 4 && DH % PER == 0,
                 "sweep shape");
 };
 
 // One sweep of mode MODE for workgroup `bid` of the `nb` that the mode uses; `lds` holds the
-// staging buffers (2 x the mode's slots x kTS x DH floats).
+// staging buffers (2 x the mode's slots x its stage length x DH floats).
 template <int MODE, typename Tin, typename Tout, int DH, int AB>
 __device__ __forceinline__ void sweep_body(const H2SweepParams& p, int64_t bid, int64_t nb, float* lds) {
-  using SS = SweepShape<DH, AB>;
+  constexpr int kTS = StageLen<MODE>::v;
+  using SS = SweepShape<DH, AB, kTS>;
   using SL = Slots<MODE>;
   constexpr int MP = SS::MP, NT = SS::NT, PER = SS::PER, NV = SL::n;
   constexpr bool REV = MODE == kDK || MODE == kDV;
@@ -487,16 +490,18 @@ __device__ __forceinline__ void sweep_body(const H2SweepParams& p, int64_t bid, 
 constexpr int kNoMode = -1;
 // owned indices per thread of the key-axis forward (2 doubles the workgroups but measured slower)
 constexpr int kKeyAB = 4;
-template <int MODE> struct SlotCount { static constexpr int n = MODE < 0 ? 0 : Slots<(MODE < 0 ? 0 : MODE)>::n; };
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 // Up to three sweeps in one launch, their workgroups interleaved (block b runs mode b % NM), so
 // that independent sweeps share the CUs; the staging buffer is one array sized for the largest.
+template <int MODE> struct StageFloats {
+  static constexpr int v = MODE < 0 ? 0 : 2 * Slots<(MODE < 0 ? 0 : MODE)>::n * StageLen<MODE>::v;
+};
 template <typename Tin, typename Tout, int DH, int AB, int M0, int M1, int M2>
-__global__ __launch_bounds__((SweepShape<DH, AB>::NT)) void hgrn2_sweep_kernel(H2SweepParams p, int64_t nb) {
+__global__ __launch_bounds__((SweepShape<DH, AB, 8>::NT)) void hgrn2_sweep_kernel(H2SweepParams p, int64_t nb) {
   constexpr int NM = 1 + (M1 != kNoMode) + (M2 != kNoMode);
-  constexpr int NVMAX = cmax(SlotCount<M0>::n, cmax(SlotCount<M1>::n, SlotCount<M2>::n));
-  __shared__ __align__(16) float lds[2 * NVMAX * kTS * DH];
+  constexpr int PERDH = cmax(StageFloats<M0>::v, cmax(StageFloats<M1>::v, StageFloats<M2>::v));
+  __shared__ __align__(16) float lds[PERDH * DH];
   const int64_t bid = blockIdx.x / NM;
   const int m = (int)(blockIdx.x % NM);
   if (m == 0) sweep_body<M0, Tin, Tout, DH, AB>(p, bid, nb, lds);
@@ -509,7 +514,7 @@ __global__ __launch_bounds__((SweepShape<DH, AB>::NT)) void hgrn2_sweep_kernel(H
 template <typename Tin, typename Tout, int DH, int AB, int M0, int M1, int M2>
 void launch_sweep(const H2SweepParams& p, hipStream_t s) {
   constexpr int NM = 1 + (M1 != kNoMode) + (M2 != kNoMode);
-  using SS = SweepShape<DH, AB>;
+  using SS = SweepShape<DH, AB, 8>;
   const int64_t nb = p.B * p.H * SS::W;
   hipLaunchKernelGGL((hgrn2_sweep_kernel<Tin, Tout, DH, AB, M0, M1, M2>), dim3((unsigned)(nb * NM)), dim3(SS::NT), 0,
                      s, p, nb);
