@@ -327,7 +327,7 @@ int ssd_hgrn2_update(int64_t B, int64_t H, int64_t d, int in_dtype, int out_dtyp
  *     g_j = lower_bound + (1 - lower_bound) * sigmoid(g_logit_j),
  *     S[i][j] = g_j * S[i][j] + v_i * k_j,        o_i = sum_j S[i][j] * q_j,
  * i.e. S_t = S_{t-1} diag(g_t) + v_t k_t^T.  Arguments, layouts and errors as ssd_hgrn2_scan /
- * ssd_hgrn2_update; additionally (L + 16) * H * d * 4 must stay below 2^32 for the scan.
+ * ssd_hgrn2_update.
  * ------------------------------------------------------------------------------------------- */
 int ssd_hgrn2_key_scan(int64_t B, int64_t L, int64_t H, int64_t d, int in_dtype, int out_dtype,
                        const void* q, const void* k, const void* v, const void* g_logit,

@@ -511,7 +511,9 @@ static int hgrn2_scan_common(bool key, int64_t B, int64_t L, int64_t H, int64_t 
   SSD_TRY(check_dtypes(in_dtype, out_dtype));
   if (B < 0 || L < 0 || H < 0 || d < 0) return fail(SSD_ERR_SHAPE, "negative size");
   if (!supported_d(d)) return fail(SSD_ERR_SHAPE, "head dim d must be 16, 32, 64 or 128");
-  if (too_big({B, L, H, d}) || B * H >= (int64_t)1 << 31) return fail(SSD_ERR_SHAPE, "problem too large");
+  // (the register sweeps address a stage of a head's rows with 32-bit offsets: H d < 2^24 keeps them small)
+  if (too_big({B, L, H, d}) || B * H >= (int64_t)1 << 30 || H * d >= (int64_t)1 << 24)
+    return fail(SSD_ERR_SHAPE, "problem too large");
   if (!(lower_bound >= 0.0f && lower_bound <= 1.0f)) return fail(SSD_ERR_VALUE, "lower_bound must be in [0, 1]");
   const int64_t nact = B * L * H * d;
   if (nact > 0 && (!q || !k || !v || !g_logit || !o)) return fail(SSD_ERR_NULL, "q, k, v, g_logit and o are required");
@@ -528,11 +530,7 @@ static int hgrn2_scan_common(bool key, int64_t B, int64_t L, int64_t H, int64_t 
   if (L == 0) return hip_status(ssd::launch_copy_or_zero(S_last, S0, B * H * d * d, s), "hgrn2_scan");
   ssd::Hgrn2ScanArgs a{B, L, H, d, in_dtype == SSD_BF16, out_dtype == SSD_BF16, q, k, v, g_logit, lower_bound, S0, o,
                        S_last};
-  if (key) {
-    // the key-axis sweep addresses a head's rows with 32-bit offsets (as the backward sweeps)
-    if ((L + 16) * H * d * 4 >= (int64_t)1 << 32) return fail(SSD_ERR_SHAPE, "problem too large");
-    return hip_status(ssd::launch_hgrn2_key_scan(a, s), "hgrn2_key_scan launch");
-  }
+  if (key) return hip_status(ssd::launch_hgrn2_key_scan(a, s), "hgrn2_key_scan launch");
   return hip_status(ssd::launch_hgrn2_scan(a, s), "hgrn2_scan launch");
 }
 
@@ -614,7 +612,7 @@ int ssd_hgrn2_scan_backward(int64_t B, int64_t L, int64_t H, int64_t d, int in_d
   SSD_TRY(check_dtypes(in_dtype, out_dtype));
   if (B < 0 || L < 0 || H < 0 || d < 0) return fail(SSD_ERR_SHAPE, "negative size");
   if (!supported_d(d)) return fail(SSD_ERR_SHAPE, "head dim d must be 16, 32, 64 or 128");
-  if (too_big({B, L, H, d}) || B * H >= (int64_t)1 << 30 || (L + 16) * H * d * 4 >= (int64_t)1 << 32)
+  if (too_big({B, L, H, d}) || B * H >= (int64_t)1 << 30 || H * d >= (int64_t)1 << 24)
     return fail(SSD_ERR_SHAPE, "problem too large");
   if (!(lower_bound >= 0.0f && lower_bound <= 1.0f)) return fail(SSD_ERR_VALUE, "lower_bound must be in [0, 1]");
   const int64_t nact = B * L * H * d;

@@ -4,8 +4,8 @@
 //   g_i = lb + (1 - lb) sigmoid(g_logit_i),  S[i][j] = g_i S[i][j] + v_i k_j,  o_i = sum_j S[i][j] q_j.
 // The gate scales row i of S (the value index); rows evolve independently of each other.
 //
-// Recurrent scan: one workgroup per (batch, head), one lane per value row i holding S[i][:] in
-// registers; k_t and q_t of each step are staged in LDS (double-buffered) and read as broadcasts.
+// The chunked MFMA form below takes bf16 inputs with d = 128 and lower bounds >= 2^-1.5; the other
+// cases run the row-gated register sweep of hgrn2_sweep.hip.
 #include "common.hpp"
 #include "h2_layout.hpp"
 #include "kernels.hpp"
@@ -24,46 +24,6 @@ struct H2Params {
   void* o;
   float* S_last;
 };
-
-template <typename Tin, typename Tout, int DH>
-__global__ __launch_bounds__(DH < 64 ? 64 : DH) void hgrn2_recurrent_kernel(H2Params p) {
-  __shared__ float sk[2][DH];
-  __shared__ float sq[2][DH];
-  const int i = threadIdx.x;
-  const bool row_ok = i < DH;
-  const int64_t bh = blockIdx.x;
-  const int64_t b = bh / p.H;
-  const int64_t hh = bh - b * p.H;
-  float S[DH];
-  const int64_t sbase = (bh * DH + (row_ok ? i : 0)) * DH;
-#pragma unroll
-  for (int j = 0; j < DH; ++j) S[j] = (p.S0 && row_ok) ? p.S0[sbase + j] : 0.0f;
-  const float one_m_lb = 1.0f - p.lb;
-  for (int64_t t = 0; t < p.L; ++t) {
-    const int buf = (int)(t & 1);
-    const int64_t base = ((b * p.L + t) * p.H + hh) * DH;
-    float vi = 0.0f, gl = 0.0f;
-    if (row_ok) {
-      sk[buf][i] = io<Tin>::load(p.k, base + i);
-      sq[buf][i] = io<Tin>::load(p.q, base + i);
-      vi = io<Tin>::load(p.v, base + i);
-      gl = io<Tin>::load(p.g, base + i);
-    }
-    __syncthreads();
-    const float g = fmaf(one_m_lb, sigmoid_f(gl), p.lb);
-    float acc = 0.0f;
-#pragma unroll
-    for (int j = 0; j < DH; ++j) {
-      S[j] = fmaf(g, S[j], vi * sk[buf][j]);
-      acc = fmaf(S[j], sq[buf][j], acc);
-    }
-    if (row_ok) io<Tout>::store(p.o, base + i, acc);
-  }
-  if (p.S_last && row_ok) {
-#pragma unroll
-    for (int j = 0; j < DH; ++j) p.S_last[sbase + j] = S[j];
-  }
-}
 
 // Decode step: one wave per value row; o_i reduced across the wave.  KEY: the gate scales the key
 // columns, S[i][j] = g_j S[i][j] + v_i k_j (the key-axis reading), instead of the value rows.
@@ -102,7 +62,7 @@ __global__ __launch_bounds__(256) void hgrn2_update_kernel(int64_t rows, int64_t
 // copy) is split into a bf16 pair hi + lo, so its products carry about 16 significant bits instead
 // of 8; the state S itself stays in fp32 accumulators for the whole sequence.
 // Gamma_C >= lower_bound^64 must stay far from underflow: the launcher uses this form only for
-// lower_bound >= 2^-1.5 (Gamma_C >= 2^-96); smaller bounds take the recurrent kernel.
+// lower_bound >= 2^-1.5 (Gamma_C >= 2^-96); smaller bounds take the register sweep.
 //
 // Workgroup = (batch, head, half of the 128 value rows), 8 waves.  Wave (r, h) (r = wave % 4,
 // h = wave / 4) owns value rows i in [16r, 16r+16) of the half, the state columns j of tiles
@@ -581,18 +541,6 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
   }
 }
 
-template <typename Tin, typename Tout>
-hipError_t launch_recurrent_t(const H2Params& p, hipStream_t s) {
-  const dim3 grid((unsigned)(p.B * p.H));
-  switch (p.d) {
-    case 16: hipLaunchKernelGGL((hgrn2_recurrent_kernel<Tin, Tout, 16>), grid, dim3(64), 0, s, p); break;
-    case 32: hipLaunchKernelGGL((hgrn2_recurrent_kernel<Tin, Tout, 32>), grid, dim3(64), 0, s, p); break;
-    case 64: hipLaunchKernelGGL((hgrn2_recurrent_kernel<Tin, Tout, 64>), grid, dim3(64), 0, s, p); break;
-    default: hipLaunchKernelGGL((hgrn2_recurrent_kernel<Tin, Tout, 128>), grid, dim3(128), 0, s, p); break;
-  }
-  return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t launch_hgrn2_scan(const Hgrn2ScanArgs& a, hipStream_t s) {
@@ -610,8 +558,8 @@ hipError_t launch_hgrn2_scan(const Hgrn2ScanArgs& a, hipStream_t s) {
       hipLaunchKernelGGL((hgrn2_chunk_kernel<float>), grid, dim3(kWaves * 64), 0, s, p);
     return hipGetLastError();
   }
-  if (!a.in_bf16) return launch_recurrent_t<float, float>(p, s);
-  return a.out_bf16 ? launch_recurrent_t<bf16_t, bf16_t>(p, s) : launch_recurrent_t<bf16_t, float>(p, s);
+  // other cases (smaller lower bounds, fp32 inputs, other head dims): the register sweep
+  return launch_hgrn2_row_sweep(a, s);
 }
 
 namespace {

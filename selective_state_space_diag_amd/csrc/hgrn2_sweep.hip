@@ -29,7 +29,10 @@
 //        dlog g (from o, dv and S_L), dx_t and dS0;
 // and one is the forward under the key-axis reading of the gate (the convention of the HGRN2 paper
 // the page cites, not printed there), S_t[i][j] = g_t[j] S_{t-1}[i][j] + v_t[i] k_t[j]:
-//   kFK  forward, S row-owned:       S[i][j] update, o_t[i] = sum_j S_t[i][j] q_t[j]; writes S_last.
+//   kFK  forward, S row-owned:       S[i][j] update, o_t[i] = sum_j S_t[i][j] q_t[j]; writes S_last;
+// and one the forward of the page's row-gated recurrence, for the cases the chunked MFMA kernel
+// does not take (small lower bounds, fp32 inputs, head dims below 128):
+//   kFR  forward, S row-owned, gate on the row index; otherwise as kFK.
 // Thread layout: a thread owns AB consecutive "a" indices (the owned axis: j for kDQ/kDK, i for
 // kDV/kFK) and the d/16 "m" indices of its part p = lane % 16 (the summed axis), so the sum over m is
 // a sum over the 16 lanes of a row group.  The per-token vectors of the head (gates, q, k, v, do,
@@ -43,7 +46,7 @@ namespace {
 
 typedef int v4i_t __attribute__((ext_vector_type(4)));
 
-enum { kDQ = 0, kDK = 1, kDV = 2, kFK = 3 };
+enum { kDQ = 0, kDK = 1, kDV = 2, kFK = 3, kFR = 4 };
 // tokens per stage: 8, or 4 for kDV, whose seven staged vectors would otherwise hold 56 KB of LDS
 // per workgroup (two workgroups per CU instead of three when it shares a launch)
 template <int MODE> struct StageLen { static constexpr int v = MODE == kDV ? 4 : 8; };
@@ -97,6 +100,14 @@ template <> struct Slots<kFK> {  // m = j: gate(t), k, q; a = i: v
   static __device__ __forceinline__ int shift(int) { return 0; }
   static __device__ __forceinline__ const void* src(const H2SweepParams& p, int s) {
     return s == 0 ? p.x : s == 1 ? p.k : s == 2 ? p.q : p.v;
+  }
+};
+template <> struct Slots<kFR> {  // m = j: k, q; a = i: gate(t), v
+  static constexpr int n = 4;
+  static __device__ __forceinline__ int kind(int s) { return s == 2 ? kGate : kAct; }
+  static __device__ __forceinline__ int shift(int) { return 0; }
+  static __device__ __forceinline__ const void* src(const H2SweepParams& p, int s) {
+    return s == 0 ? p.k : s == 1 ? p.q : s == 2 ? p.x : p.v;
   }
 };
 template <> struct Slots<kDV> {  // m = j: q, k; a = i: do, o, v, gate(t+1), ratio(t)
@@ -214,50 +225,52 @@ __device__ __forceinline__ void sweep_body(const H2SweepParams& p, int64_t bid, 
   const int64_t head_base = (b * L * p.H + hh) * DH;  // token 0 of this head
   const float lb = p.lb;
   const int64_t nanch = (L - 1) / kAnchor;            // checkpointed states per head
-  // outputs of this head: token t, column c at byte (t * row_stride + c) * ES.  The whole byte
-  // offset goes into the range-checked per-lane offset: stores to tokens outside [0, L) (whose
-  // offsets stay below 2^32: the host bounds (L + 16) H d 4 < 2^32)
-  // and stores of the lanes that do not write (offset kDrop) fall outside the window and are dropped.
+  // Every activation access goes through a window over the rows of this head from a stage's first
+  // token t0 to min(t0 + kTS, L - 1) (so its byte offsets stay small for any L): rows past the last
+  // token read 0 and stores to them are dropped, as are the stores of the lanes that do not write
+  // (offset kDrop).  Token t0 + tau, column c is at byte (tau * row_stride + c) * element size.
   const bool writer = (pp % SUB) == 0;
   constexpr uint32_t kDrop = 0xFFFFFF00u;
-  const uint32_t out_bytes = (uint32_t)(((L - 1) * row_stride + DH) * ES);
-  void* out0 = MODE == kDQ ? p.dq : MODE == kDK ? p.dk : MODE == kDV ? p.dv : p.y;
-  const auto wo0 = make_window(static_cast<char*>(out0) + head_base * ES, out_bytes);
-  const auto wo1 = make_window(static_cast<char*>(MODE == kDV ? p.dx : out0) + head_base * ES, out_bytes);
+  auto stage_window = [&](const void* a, int es, int64_t t0) {
+    const int64_t last = min<int64_t>(L - 1 - t0, kTS);  // rows t0 .. t0 + last exist (t0 < L)
+    // the values are the same on every lane; readfirstlane says so to the compiler, which would
+    // otherwise keep the descriptor in vector registers and loop over its distinct values
+    const uint64_t base = (uint64_t)(static_cast<const char*>(a) + (head_base + t0 * row_stride) * es);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+    const uint32_t bytes = __builtin_amdgcn_readfirstlane((uint32_t)((last * row_stride + DH) * es));
+    return make_window(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), bytes);
+  };
+  void* out0 = MODE == kDQ ? p.dq : MODE == kDK ? p.dk : MODE == kDV ? p.dv : p.y;  // kFK, kFR: y
+  void* out1 = MODE == kDV ? p.dx : out0;
 
   // ---- staging: the stages are the token blocks [c kTS, c kTS + kTS), taken in increasing c
   // (forward) or decreasing c (reverse); tokens at or past L are staged as exact no-ops for the
   // matrix update (gate 1, activations 0).
-  // Loads go through windows over the head's valid tokens (offsets past the last token read 0),
-  // so that they need no per-lane branch and stay in flight while the current stage computes.  A
-  // thread loads PER consecutive elements of one token row per slot (one 4- to 16-byte load).
+  // Loads go through the stage windows, so that they need no per-lane branch and stay in flight
+  // while the current stage computes.  A thread loads PER consecutive elements of one token row per
+  // slot (one 4- to 16-byte load).
   uint32_t raw[NV][4];  // raw bits: bf16 pairs, or fp32
   auto stage_t0 = [&](int64_t s) -> int64_t { return (REV ? nstage - 1 - s : s) * kTS; };
-  __amdgpu_buffer_rsrc_t wsrc[NV];
-#pragma unroll
-  for (int sl = 0; sl < NV; ++sl) {
-    const int es = SL::kind(sl) == kOut ? 4 : (int)sizeof(Tin);
-    wsrc[sl] = make_window(static_cast<const char*>(SL::src(p, sl)) + head_base * es,
-                           (uint32_t)(((L - 1) * row_stride + DH) * es));
-  }
   const int tau_ld = (tid * PER) / DH, c_ld = (tid * PER) % DH;  // this thread's staged elements
   auto fetch = [&](int64_t s) {
     const int64_t t0 = stage_t0(s);
 #pragma unroll
     for (int sl = 0; sl < NV; ++sl) {
       const int es = SL::kind(sl) == kOut ? 4 : (int)sizeof(Tin);
-      const uint32_t off = (uint32_t)(((t0 + tau_ld + SL::shift(sl)) * row_stride + c_ld) * es);
+      const auto wsrc = stage_window(SL::src(p, sl), es, t0);
+      const uint32_t off = (uint32_t)(((tau_ld + SL::shift(sl)) * row_stride + c_ld) * es);
       const int bytes = PER * es;
       if (bytes == 16) {
-        const v4i_t d = __builtin_amdgcn_raw_buffer_load_b128(wsrc[sl], (int)off, 0, 0);
+        const v4i_t d = __builtin_amdgcn_raw_buffer_load_b128(wsrc, (int)off, 0, 0);
         raw[sl][0] = d.x; raw[sl][1] = d.y; raw[sl][2] = d.z; raw[sl][3] = d.w;
       } else if (bytes == 8) {
-        const u32x2_t d = __builtin_amdgcn_raw_buffer_load_b64(wsrc[sl], (int)off, 0, 0);
+        const u32x2_t d = __builtin_amdgcn_raw_buffer_load_b64(wsrc, (int)off, 0, 0);
         raw[sl][0] = d.x; raw[sl][1] = d.y;
       } else if (bytes == 4) {
-        raw[sl][0] = __builtin_amdgcn_raw_buffer_load_b32(wsrc[sl], (int)off, 0, 0);
+        raw[sl][0] = __builtin_amdgcn_raw_buffer_load_b32(wsrc, (int)off, 0, 0);
       } else {
-        raw[sl][0] = __builtin_amdgcn_raw_buffer_load_b16(wsrc[sl], (int)off, 0, 0);
+        raw[sl][0] = __builtin_amdgcn_raw_buffer_load_b16(wsrc, (int)off, 0, 0);
       }
     }
   };
@@ -310,7 +323,7 @@ __device__ __forceinline__ void sweep_body(const H2SweepParams& p, int64_t bid, 
       }
     }
     cum = (double)part_reduce<AB>(part, pp);
-  } else if constexpr (MODE == kFK) {  // mat[u][e] = S[a0 + u][m0 + e]
+  } else if constexpr (MODE == kFK || MODE == kFR) {  // mat[u][e] = S[a0 + u][m0 + e]
 #pragma unroll
     for (int u = 0; u < AB; ++u)
 #pragma unroll
@@ -371,6 +384,11 @@ __device__ __forceinline__ void sweep_body(const H2SweepParams& p, int64_t bid, 
         o.sc[1] = stg[buf][3][tau][ia];
         o.sc[2] = stg[buf][4][tau][ia];
         o.sc[3] = stg[buf][6][tau][ia];
+      } else if constexpr (MODE == kFR) {  // m = k, q; a = gate, v
+        lds_vec<MP>(&stg[buf][0][tau][m0], o.m[0]);
+        lds_vec<MP>(&stg[buf][1][tau][m0], o.m[1]);
+        lds_vec<AB>(&stg[buf][2][tau][a0], o.a[0]);
+        lds_vec<AB>(&stg[buf][3][tau][a0], o.a[1]);
       } else {  // kFK: m = gate, k, q; a = v.  Others: m = gate, x, y; a = k or q.
         lds_vec<MP>(&stg[buf][0][tau][m0], o.m[0]);
         lds_vec<MP>(&stg[buf][1][tau][m0], o.m[1]);
@@ -380,12 +398,12 @@ __device__ __forceinline__ void sweep_body(const H2SweepParams& p, int64_t bid, 
     };
     Tok cur, nxt;
     read_tok(REV ? kTS - 1 : 0, cur);
+    const auto wo0 = stage_window(out0, ES, t0), wo1 = stage_window(out1, ES, t0);
 #pragma unroll
     for (int step = 0; step < kTS; ++step) {
       const int tau = REV ? kTS - 1 - step : step;
       if (step + 1 < kTS) read_tok(REV ? tau - 1 : tau + 1, nxt);
-      const int64_t t = t0 + tau;
-      const uint32_t lo = writer ? (uint32_t)((t * row_stride + ia) * ES) : kDrop;
+      const uint32_t lo = writer ? (uint32_t)((tau * row_stride + ia) * ES) : kDrop;
       float acc[AB];
       if constexpr (MODE == kDV) {
         // R = diag(g(t+1)) R + do q^T,  dv = R k
@@ -409,6 +427,19 @@ __device__ __forceinline__ void sweep_body(const H2SweepParams& p, int64_t bid, 
         const float dg = (float)cum * cur.sc[3];
         win<Tout, 1>::store(wo0, lo, 0u, &dvt);
         win<Tout, 1>::store(wo1, lo, 0u, &dg);
+      } else if constexpr (MODE == kFR) {
+        // S = diag(g) S + v k^T,  o = S q
+#pragma unroll
+        for (int u = 0; u < AB; ++u) {
+          acc[u] = 0.0f;
+#pragma unroll
+          for (int e = 0; e < MP; ++e) {
+            mat[u][e] = fmaf(cur.a[0][u], mat[u][e], cur.a[1][u] * cur.m[0][e]);
+            acc[u] = fmaf(mat[u][e], cur.m[1][e], acc[u]);
+          }
+        }
+        const float ot = part_reduce<AB>(acc, pp);
+        win<Tout, 1>::store(wo0, lo, 0u, &ot);
       } else if constexpr (MODE == kFK) {
         // S = S diag(g) + v k^T,  o = S q
 #pragma unroll
@@ -458,7 +489,7 @@ __device__ __forceinline__ void sweep_body(const H2SweepParams& p, int64_t bid, 
 #pragma unroll
       for (int e = 0; e < MP; ++e) p.S_L[mbase + (int64_t)(m0 + e) * DH + a0 + u] = mat[u][e];
   }
-  if constexpr (MODE == kFK) {
+  if constexpr (MODE == kFK || MODE == kFR) {
     if (p.S_last) {
 #pragma unroll
       for (int u = 0; u < AB; ++u)
@@ -473,7 +504,7 @@ __device__ __forceinline__ void sweep_body(const H2SweepParams& p, int64_t bid, 
       const float rs0 = p.S0 ? row_dot(p.S0 + mbase) : 0.0f;
       const float g0 = gate_of(io<Tin>::load(p.x, head_base + ia), lb);
       const float dg0 = g0 * rs0 * ratio_of(io<Tin>::load(p.x, head_base + ia), lb);
-      win<Tout, 1>::store(wo1, writer ? (uint32_t)(ia * ES) : kDrop, 0u, &dg0);
+      win<Tout, 1>::store(stage_window(out1, ES, 0), writer ? (uint32_t)(ia * ES) : kDrop, 0u, &dg0);
       if (p.dS0) {
         float gr[AB];
 #pragma unroll
@@ -560,6 +591,20 @@ struct BwdLayout {
 size_t hgrn2_scan_backward_scratch_bytes(const Hgrn2BwdArgs& a) {
   const BwdLayout lay(a);
   return lay.state + lay.ckpt + lay.outs;
+}
+
+hipError_t launch_hgrn2_row_sweep(const Hgrn2ScanArgs& a, hipStream_t s) {
+  H2SweepParams p{};
+  p.B = a.B; p.L = a.L; p.H = a.H;
+  p.q = a.q; p.k = a.k; p.v = a.v; p.x = a.g_logit; p.lb = a.lower_bound;
+  p.S0 = a.S0; p.y = a.o; p.S_last = a.S_last;
+  if (!a.in_bf16)
+    launch_sweep_d<float, float, kFR>(p, a.d, s);
+  else if (a.out_bf16)
+    launch_sweep_d<bf16_t, bf16_t, kFR>(p, a.d, s);
+  else
+    launch_sweep_d<bf16_t, float, kFR>(p, a.d, s);
+  return hipGetLastError();
 }
 
 hipError_t launch_hgrn2_key_scan(const Hgrn2ScanArgs& a, hipStream_t s) {

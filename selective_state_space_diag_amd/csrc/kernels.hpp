@@ -212,6 +212,8 @@ struct Hgrn2UpdateArgs {
 hipError_t launch_hgrn2_update(const Hgrn2UpdateArgs& a, hipStream_t s);
 // Key-axis gating (S[i][j] = g_j S[i][j] + v_i k_j): the same arguments.
 hipError_t launch_hgrn2_key_scan(const Hgrn2ScanArgs& a, hipStream_t s);
+// The row-gated scan as a register sweep (the cases the chunked MFMA kernel does not take).
+hipError_t launch_hgrn2_row_sweep(const Hgrn2ScanArgs& a, hipStream_t s);
 hipError_t launch_hgrn2_key_update(const Hgrn2UpdateArgs& a, hipStream_t s);
 
 // Readout LayerNorm over rows of `width` features (fp32 o), affine, times silu(gate).
