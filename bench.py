@@ -334,6 +334,13 @@ def forms(args, device):
            dict(mfma_equiv_tflops=flops / (ms * 1e-3) / 1e12,
                 mfma_util=flops / (ms * 1e-3) / 1e12 / BF16_MFMA_TFLOPS))
 
+    # --- the same scan at the page's default lower bound 0 (the register sweep: 5 d^2 fp32 flops per
+    #     token and head; the chunked MFMA form needs lower bounds >= 2^-1.5)
+    ms = time_calls(lambda kk: ssd.hgrn2_scan(q, k, v, g, 0.0), 1, 3, 1)[0]
+    rflops = 5 * B * L * H * dd * dd
+    record("hgrn2_lb0_bf16_B8_H16_d128_L4096", ms, B * L * H * dd * dd, hgrn2_bytes(B, L, H, dd),
+           dict(valu_tflops=rflops / (ms * 1e-3) / 1e12, valu_frac=rflops / (ms * 1e-3) / 1e12 / FP32_SCALAR_FMA_TFLOPS))
+
     # --- gradients of the HGRN2 scan on the same shape (do ~ N(0, 1/d)), given the forward's fp32
     #     output; the three sweeps execute 15 d^2 fp32 flops per token and head (two state updates of
     #     3 d^2, the adjoint update twice, three d^2 matrix-vector products)

@@ -96,3 +96,22 @@ def test_config3_full_size_sampled_heads():
         assert_close(host(o[b:b + 1, :, h:h + 1]), orf, TOL[synth.BF16], f"o head {b},{h}")
         assert_close(host(S[b:b + 1, h:h + 1]), Sr, TOL[synth.BF16], f"S head {b},{h}")
     assert torch.isfinite(o).all()
+
+
+def test_full_size_default_lower_bound_sampled_heads():
+    """The same workload with the page's default lower bound 0 (the register-sweep path): every
+    output of 3 sampled heads and their final states vs the oracle."""
+    import torch
+    inp = synth.config_inputs(3)
+    inp.s["lower_bound"] = 0.0
+    o, S = gpu_run(inp)
+    torch.cuda.synchronize()
+    B, L, H, d = inp.t["q"].shape
+    rng = np.random.default_rng(4)
+    for _ in range(3):
+        b, h = int(rng.integers(B)), int(rng.integers(H))
+        g = lambda n: synth.bf16_to_f64(inp.t[n].data[b:b + 1, :, h:h + 1])
+        orf, Sr = oracle.hgrn2_scan(g("q"), g("k"), g("v"), g("g_logit"), 0.0)
+        assert_close(host(o[b:b + 1, :, h:h + 1]), orf, TOL[synth.BF16], f"o head {b},{h}")
+        assert_close(host(S[b:b + 1, h:h + 1]), Sr, TOL[synth.BF16], f"S head {b},{h}")
+    assert torch.isfinite(o).all()
