@@ -152,13 +152,13 @@ def headline(args, device):
     import selective_state_space_diag_amd as ssd
     from selective_state_space_diag_amd import synth
 
-    cfg = synth.CONFIGS[1]
+    cfg = synth.WORKLOADS["selective"]
     B, L, D, N = cfg["B"], cfg["L"], cfg["D"], cfg["N"]
     n_sets = 3
     sets = []
     host_inputs = None
     for k in range(n_sets):
-        inp = synth.config_inputs(1, seed=1001 + 100 * k)
+        inp = synth.workload_inputs("selective", seed=1001 + 100 * k)
         if k == 0:
             host_inputs = inp
         t = {n: dev_bf16(v.data, device) for n, v in inp.t.items()}

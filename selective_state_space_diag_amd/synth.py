@@ -246,20 +246,21 @@ def hgrn2_inputs(B: int, L: int, H: int, d: int, dtype: str = BF16, seed: int = 
 
 
 # ----------------------------------------------------------------------------- the five workloads
-CONFIGS = {
-    0: dict(kind="rglru", B=2, L=128, D=64, dtype=F32, c=8.0),
-    1: dict(kind="selective", B=4, L=2048, D=1536, N=16, dtype=BF16, scales=4),
-    2: dict(kind="rglru", B=8, L=8192, D=2560, dtype=BF16, c=8.0, decode_B=256, decode_steps=256),
-    3: dict(kind="hgrn2", B=8, L=4096, H=16, d=128, dtype=BF16, lower_bound=0.5, chunk=64),
-    4: dict(kind="varlen", L=131072, nseq=32, D=4096, N=16, dtype=BF16, scales=4),
+# Named workloads with the shapes and distributions described above; each has a fixed seed.
+WORKLOADS = {
+    "rglru_small": dict(kind="rglru", B=2, L=128, D=64, dtype=F32, c=8.0, seed=1000),
+    "selective": dict(kind="selective", B=4, L=2048, D=1536, N=16, dtype=BF16, scales=4, seed=1001),
+    "rglru": dict(kind="rglru", B=8, L=8192, D=2560, dtype=BF16, c=8.0, decode_B=256, decode_steps=256, seed=1002),
+    "hgrn2": dict(kind="hgrn2", B=8, L=4096, H=16, d=128, dtype=BF16, lower_bound=0.5, chunk=64, seed=1003),
+    "selective_varlen": dict(kind="varlen", L=131072, nseq=32, D=4096, N=16, dtype=BF16, scales=4, seed=1004),
 }
 
 
-def config_inputs(i: int, seed: Optional[int] = None, **overrides) -> Inputs:
-    """Inputs of benchmark configuration ``i`` (seed defaults to 1000 + i)."""
-    cfg = dict(CONFIGS[i])
+def workload_inputs(name: str, seed: Optional[int] = None, **overrides) -> Inputs:
+    """Inputs of the named workload (seed defaults to the workload's own)."""
+    cfg = dict(WORKLOADS[name])
     cfg.update(overrides)
-    seed = 1000 + i if seed is None else seed
+    seed = cfg["seed"] if seed is None else seed
     k = cfg["kind"]
     if k == "rglru":
         return rglru_inputs(cfg["B"], cfg["L"], cfg["D"], cfg["dtype"], seed, cfg["c"])

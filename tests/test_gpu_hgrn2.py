@@ -84,7 +84,7 @@ def test_bf16_output():
 def test_config3_full_size_sampled_heads():
     """B=8, H=16, d=128, L=4096 bf16 at full size; every output of 4 sampled heads vs the oracle."""
     import torch
-    inp = synth.config_inputs(3)
+    inp = synth.workload_inputs("hgrn2")
     o, S = gpu_run(inp)
     torch.cuda.synchronize()
     B, L, H, d = inp.t["q"].shape
@@ -102,7 +102,7 @@ def test_full_size_default_lower_bound_sampled_heads():
     """The same workload with the page's default lower bound 0 (the register-sweep path): every
     output of 3 sampled heads and their final states vs the oracle."""
     import torch
-    inp = synth.config_inputs(3)
+    inp = synth.workload_inputs("hgrn2")
     inp.s["lower_bound"] = 0.0
     o, S = gpu_run(inp)
     torch.cuda.synchronize()

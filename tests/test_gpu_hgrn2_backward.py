@@ -106,7 +106,7 @@ def test_full_workload_sampled_heads():
     """B=8, L=4096, H=16, d=128 (bf16, lb = 0.5), the benchmark shape: every head is computed on the
     GPU; two heads (independent of the others) are checked against the oracle run on them alone."""
     B, L, H, d = 8, 4096, 16, 128
-    inp = synth.config_inputs(3)
+    inp = synth.workload_inputs("hgrn2")
     rng = np.random.default_rng(7700)
     do32 = (rng.standard_normal((B, L, H, d)) / np.sqrt(d)).astype(np.float32)
     do = synth.Tensor(synth.BF16, synth.f32_to_bf16_bits(do32))

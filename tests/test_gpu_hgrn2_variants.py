@@ -75,7 +75,7 @@ def test_key_gated_decode_steps_equal_scan():
 def test_key_gated_full_workload_sampled_heads():
     """B=8, L=4096, H=16, d=128 bf16: every head on the GPU, two checked against the oracle alone."""
     import torch
-    inp = synth.config_inputs(3)
+    inp = synth.workload_inputs("hgrn2")
     t = inp.t
     o = ssd.hgrn2_scan(to_dev(t["q"]), to_dev(t["k"]), to_dev(t["v"]), to_dev(t["g_logit"]), 0.5, gate_axis="key")
     torch.cuda.synchronize()

@@ -158,8 +158,8 @@ def test_empty_sequence_copies_h0():
 def test_config2_full_size_sampled_channels():
     """B=8, L=8192, D=2560 bf16 at full size; every output of 64 sampled (b, d) channels vs the oracle."""
     import torch
-    cfg = synth.CONFIGS[2]
-    inp = synth.config_inputs(2)
+    cfg = synth.WORKLOADS["rglru"]
+    inp = synth.workload_inputs("rglru")
     B, L, D = cfg["B"], cfg["L"], cfg["D"]
     x, r, i = (to_dev(inp.t[n]) for n in ("x", "r_logit", "i_logit"))
     a_log = to_dev(inp.p["a_log"])

@@ -184,7 +184,7 @@ def _sampled_check(inp, nsample, seed, tol):
 
 
 def test_config1_full_size_sampled_channels():
-    inp = synth.config_inputs(1)
+    inp = synth.workload_inputs("selective")
     _sampled_check(inp, 16, 1, TOL[synth.BF16])
     inp.t.pop("z")
     inp.p.pop("Dskip")
@@ -192,5 +192,5 @@ def test_config1_full_size_sampled_channels():
 
 
 def test_config4_varlen_full_size_sampled_channels():
-    inp = synth.config_inputs(4)
+    inp = synth.workload_inputs("selective_varlen")
     _sampled_check(inp, 8, 3, TOL[synth.BF16])
