@@ -122,3 +122,42 @@ def test_readout_norm_over_hidden_of_scan_output():
     # bf16 output: the fp32 result rounded, within 1 ulp
     diff = (y16.float() - y.to(torch.bfloat16).float()).abs()
     assert bool((diff <= y.abs().clamp_min(1e-30) * 2.0 ** -7).all())
+
+
+@pytest.mark.parametrize("width", [64, 100, 2048])
+def test_readout_norm_fp32_gate_without_affine(width):
+    import torch
+    rng = np.random.default_rng(8700 + width)
+    rows = 20
+    o = (rng.standard_normal((rows, width)) * 0.5 - 3.0).astype(np.float32)
+    g = rng.standard_normal((rows, width)).astype(np.float32)
+    y = ssd.readout_norm(to_dev(o), gate=to_dev(g), eps=1e-3)
+    y0 = ssd.readout_norm(to_dev(o), eps=1e-3)
+    torch.cuda.synchronize()
+    assert_close(host(y), oracle.readout_norm(o.astype(np.float64), gate=g.astype(np.float64), eps=1e-3), 1e-5, "y")
+    assert_close(host(y0), oracle.readout_norm(o.astype(np.float64), eps=1e-3), 1e-5, "y0")
+
+
+def test_variants_deterministic_and_nan_propagating():
+    """Runs repeat bit for bit; a NaN in one head's input stays in that head (key gate) or row (norm)."""
+    import torch
+    inp = synth.hgrn2_inputs(2, 40, 3, 64, synth.BF16, 8800, with_S0=True)
+    t = {n: to_dev(v) for n, v in inp.t.items()}
+    S0 = to_dev(inp.p["S0"])
+    o1 = ssd.hgrn2_scan(t["q"], t["k"], t["v"], t["g_logit"], 0.5, S0=S0, gate_axis="key")
+    o2 = ssd.hgrn2_scan(t["q"], t["k"], t["v"], t["g_logit"], 0.5, S0=S0, gate_axis="key")
+    assert torch.equal(o1, o2)
+    v = t["v"].clone()
+    v[1, 5, 2, 7] = float("nan")
+    o3 = ssd.hgrn2_scan(t["q"], t["k"], v, t["g_logit"], 0.5, S0=S0, gate_axis="key")
+    torch.cuda.synchronize()
+    bad = torch.isnan(o3)
+    assert bool(bad[1, 5:, 2, 7].all())          # row 7 of head (1, 2) from token 5 on
+    assert not bool(bad[0].any()) and not bool(bad[1, :, :2].any())  # other heads untouched
+    assert torch.equal(o3[0], o1[0])
+    x = torch.randn((6, 256), device="cuda")
+    n1, n2 = ssd.readout_norm(x), ssd.readout_norm(x)
+    assert torch.equal(n1, n2)
+    x[3, 10] = float("nan")
+    n3 = ssd.readout_norm(x)
+    assert bool(torch.isnan(n3[3]).all()) and not bool(torch.isnan(n3[[0, 1, 2, 4, 5]]).any())
