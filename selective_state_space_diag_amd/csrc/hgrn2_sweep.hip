@@ -469,6 +469,9 @@ __device__ __forceinline__ void sweep_body(const H2SweepParams& p, int64_t bid, 
         win<Tout, 1>::store(wo0, lo, 0u, &tot);
       }
       if (step + 1 < kTS) cur = nxt;
+      // keep tokens in program order: otherwise the scheduler starts the next token's arithmetic
+      // right after issuing its operand reads and waits for them, exposing the LDS latency
+      __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (MODE == kDQ) {
       if (anchor) {  // state after the stage's last token
