@@ -383,6 +383,12 @@ def forms(args, device):
     ms = time_calls(lambda kk: ssd.selective_scan(x, dt, A, Bm, Cm, Dskip=Dskip, z=z, cu_seqlens=cu,
                                                   check_cu_seqlens=False), 1, 5, 1)[0]
     record("selective_varlen_L131072_D4096_N16_32seq", ms, Lt * D * N, selective_bytes(1, Lt, D, N, nseq=ns))
+
+    # --- gradients of the packed varlen scan (dy ~ N(0, 1))
+    dy = randn((1, Lt, D))
+    ms = time_calls(lambda kk: ssd.selective_scan_backward(x, dt, A, Bm, Cm, dy, Dskip=Dskip, z=z, cu_seqlens=cu,
+                                                           check_cu_seqlens=False), 1, 2, 1)[0]
+    record("selective_backward_varlen_L131072_D4096_N16_32seq", ms, Lt * D * N, selective_bwd_bytes(1, Lt, D, N))
     return out
 
 
