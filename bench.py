@@ -178,23 +178,27 @@ def headline(args, device):
     return res, host_inputs
 
 
-def cpu_baseline(host_inputs):
-    """The fp64 oracle on the first batch row of the headline workload (1 x 2048 x 1536 x 16)."""
+def cpu_baseline(host_inputs, min_seconds: float = 10.0):
+    """The fp64 oracle on the whole headline workload (4 x 2048 x 1536 x 16), run back to back until
+    at least ``min_seconds`` have passed (one pass takes about a second)."""
     import oracle
     t = host_inputs.t
-    sl = slice(0, 1)
-    g = lambda n: t[n].f64()[sl]
-    x, dt, z, Bm, Cm = g("x"), g("dt"), g("z"), g("Bm"), g("Cm")
+    x, dt, z, Bm, Cm = (t[n].f64() for n in ("x", "dt", "z", "Bm", "Cm"))
     A = host_inputs.p["A"].astype(np.float64)
     Dskip = host_inputs.p["Dskip"].astype(np.float64)
     oracle.lib()
+    reps = 0
     t0 = time.perf_counter()
-    oracle.selective_scan(x, dt, A, Bm, Cm, Dskip=Dskip, z=z, dt_softplus=True)
-    sec = time.perf_counter() - t0
-    updates = x.shape[0] * x.shape[1] * x.shape[2] * A.shape[1]
+    while True:
+        oracle.selective_scan(x, dt, A, Bm, Cm, Dskip=Dskip, z=z, dt_softplus=True)
+        reps += 1
+        sec = time.perf_counter() - t0
+        if sec >= min_seconds:
+            break
+    updates = reps * x.shape[0] * x.shape[1] * x.shape[2] * A.shape[1]
     return dict(value=updates / sec, unit="state-updates/s", cores=1, kind="oracle",
-                sample=f"batch row 0 of the headline workload: 1x2048x1536 channels x 16 states "
-                       f"({updates} updates) in {sec:.2f} s, single-threaded fp64")
+                sample=f"the whole headline workload (4x2048x1536 channels x 16 states) {reps} times back to back, "
+                       f"{updates} updates in {sec:.1f} s, single-threaded fp64")
 
 
 # ----------------------------------------------------------------------------- other workloads
