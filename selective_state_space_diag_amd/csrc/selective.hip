@@ -551,7 +551,11 @@ Plan make_plan(const SelectiveScanArgs& a) {
     pl.nseg = (a.L + T - 1) / T;
     pl.U = a.B * pl.nseg;
   } else {
-    int64_t want = (kTargetWaves + waves_per_row - 1) / waves_per_row;  // units over the packed rows
+    // Packed sequences end in partial segments of uneven length; spreading the rows over about
+    // eight resident rounds of workgroups lets the hardware keep the CUs busy while those finish
+    // (measured 4.8 -> 3.3 ms for 32 sequences of 600 to 15500 rows at D = 4096; 16 rounds: no gain).
+    constexpr int64_t kVarlenRounds = 8;
+    int64_t want = (kVarlenRounds * kTargetWaves + waves_per_row - 1) / waves_per_row;  // units over the packed rows
     if (want < 1) want = 1;
     int64_t T = (a.L + want - 1) / want;
     T = ((T + 15) / 16) * 16;
