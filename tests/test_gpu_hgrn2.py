@@ -81,7 +81,7 @@ def test_bf16_output():
     assert bool((diff <= o32.abs().clamp_min(1e-30) * 2.0 ** -7).all())
 
 
-def test_config3_full_size_sampled_heads():
+def test_hgrn2_workload_full_size_sampled_heads():
     """B=8, H=16, d=128, L=4096 bf16 at full size; every output of 4 sampled heads vs the oracle."""
     import torch
     inp = synth.workload_inputs("hgrn2")

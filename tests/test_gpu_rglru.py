@@ -28,7 +28,7 @@ def run_case(B, L, D, dtype, seed, with_h0=True, c=8.0):
     return inp, y
 
 
-def test_config0_fp32():
+def test_rglru_small_workload_fp32():
     run_case(2, 128, 64, synth.F32, 1000, with_h0=False)
 
 
@@ -155,7 +155,7 @@ def test_empty_sequence_copies_h0():
     assert y.shape == (3, 0, 64) and torch.equal(hl, h0)
 
 
-def test_config2_full_size_sampled_channels():
+def test_rglru_workload_full_size_sampled_channels():
     """B=8, L=8192, D=2560 bf16 at full size; every output of 64 sampled (b, d) channels vs the oracle."""
     import torch
     cfg = synth.WORKLOADS["rglru"]

@@ -183,7 +183,7 @@ def _sampled_check(inp, nsample, seed, tol):
     return worst
 
 
-def test_config1_full_size_sampled_channels():
+def test_selective_workload_full_size_sampled_channels():
     inp = synth.workload_inputs("selective")
     _sampled_check(inp, 16, 1, TOL[synth.BF16])
     inp.t.pop("z")
@@ -191,6 +191,10 @@ def test_config1_full_size_sampled_channels():
     _sampled_check(inp, 16, 2, TOL[synth.BF16])
 
 
-def test_config4_varlen_full_size_sampled_channels():
+def test_varlen_workload_full_size_sampled_channels():
     inp = synth.workload_inputs("selective_varlen")
     _sampled_check(inp, 8, 3, TOL[synth.BF16])
+    # and the scan term alone (the skip term dominates the output otherwise)
+    inp.t.pop("z")
+    inp.p.pop("Dskip")
+    _sampled_check(inp, 8, 4, TOL[synth.BF16])
