@@ -158,16 +158,38 @@ __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf
 __device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float hw_sqrt(float x) { return __builtin_amdgcn_sqrtf(x); }
 
-// sigmoid(v) = 1 / (1 + e^-v); saturates cleanly to 0 / 1 for large |v|.
+// e^v with the argument carried past fp32: t = v log2(e) rounds with an absolute error of up to
+// half an ulp of |t|, which moves 2^t by that much times ln 2 in relative terms (several ulp once
+// |v| is a few units).  The exact rounding error of the product (an fma) and the tail of log2(e)
+// beyond fp32 form tl, and 2^(t + tl) = 2^t (1 + tl ln 2) to first order (|tl| < 2^-23 |t|).
+constexpr float kLog2eLo = 1.9259629911e-08f;  // log2(e) - (float)log2(e)
+// Where the correction is not finite (v = +-inf, or 2^t overflowed) 2^t alone is the answer.
+__device__ __forceinline__ float exp_split(float v) {
+  const float t = v * kLog2e;
+  const float tl = fmaf(v, kLog2eLo, fmaf(v, kLog2e, -t));
+  const float e = hw_exp2(t);
+  const float c = e * tl;
+  return __builtin_isfinite(c) ? fmaf(c, kLn2, e) : e;
+}
+
+// sigmoid(v) = 1 / (1 + e^-v); saturates cleanly to 0 / 1 for large |v|.  The plain form rounds
+// the exponent (several ulp for |v| of a few units), which the forward gates can afford.
 __device__ __forceinline__ float sigmoid_f(float v) { return hw_rcp(1.0f + hw_exp2(-v * kLog2e)); }
 
 // silu(z) = z * sigmoid(z)
 __device__ __forceinline__ float silu_f(float z) { return z * sigmoid_f(z); }
 
+// The same with e^-v through exp_split (about 1 ulp): for derivatives that scale a whole gradient,
+// such as softplus'(v) = sigmoid(v) in d dt.
+__device__ __forceinline__ float sigmoid_acc_f(float v) { return hw_rcp(1.0f + exp_split(-v)); }
+__device__ __forceinline__ float silu_acc_f(float z) { return z * sigmoid_acc_f(z); }
+
 // softplus with the usual threshold: v for v > 20, else log(1 + e^v).  log1p is kept accurate
 // for small e^v by the correction log1p(e) = log(u) * e / (u - 1), u = 1 + e (u - 1 is exact).
+// e^v is formed with exp_split: delta scales every input term and every decay exponent of the scan,
+// so its relative error passes straight into the states.
 __device__ __forceinline__ float softplus_f(float v) {
-  float e = hw_exp2(v * kLog2e);
+  float e = exp_split(v);
   float u = 1.0f + e;
   float um1 = u - 1.0f;
   float lg = hw_log2(u) * kLn2;

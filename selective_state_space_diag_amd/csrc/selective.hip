@@ -649,10 +649,10 @@ __device__ __forceinline__ BUnit bwd_unit(const SelBwdParams& p, int64_t u) {
 }
 
 // softplus'(v) as torch takes it: sigmoid(v), and 1 above the threshold 20.
-__device__ __forceinline__ float softplus_grad_f(float v) { return v > 20.0f ? 1.0f : sigmoid_f(v); }
+__device__ __forceinline__ float softplus_grad_f(float v) { return v > 20.0f ? 1.0f : sigmoid_acc_f(v); }
 // silu'(z) = sigmoid(z) (1 + z (1 - sigmoid(z)))
 __device__ __forceinline__ float silu_grad_f(float z) {
-  const float sg = sigmoid_f(z);
+  const float sg = sigmoid_acc_f(z);
   return sg * fmaf(z, 1.0f - sg, 1.0f);
 }
 
@@ -710,7 +710,7 @@ __global__ __launch_bounds__(kThreads) void selective_bwd_agg_kernel(SelBwdParam
     const uint32_t ro = (uint32_t)min(t, R - 1) * row_in;
     const float v = W::get(W::load(wdt, lane_in, ro), 0) + bias;
     const float dyv = W::get(W::load(wdy, lane_in, ro), 0);
-    const float g = GATE ? silu_f(W::get(W::load(wzz, lane_in, ro), 0)) : 1.0f;
+    const float g = GATE ? silu_acc_f(W::get(W::load(wzz, lane_in, ro), 0)) : 1.0f;
     delta[t] = t < R ? (SOFTPLUS ? softplus_f(v) : v) : 0.0f;  // rows past the sequence: identity
     ds[t] = t < R ? dyv * g : 0.0f;
   }
@@ -797,7 +797,7 @@ __global__ __launch_bounds__(kThreads) void selective_bwd_kernel(SelBwdParams p)
     const float v = ld(wdt, t) + bias;
     const float xx = ld(wxx, t);
     const float dyv = ld(wdy, t);
-    const float g = GATE ? silu_f(ld(wzz, t)) : 1.0f;
+    const float g = GATE ? silu_acc_f(ld(wzz, t)) : 1.0f;
     delta[t] = ok ? (SOFTPLUS ? softplus_f(v) : v) : 0.0f;
     dx_[t] = delta[t] * (ok ? xx : 0.0f);
     ds[t] = ok ? dyv * g : 0.0f;

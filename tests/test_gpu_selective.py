@@ -74,6 +74,20 @@ def test_unstructured_A_mixed_with_multiscale_A(dtype):
     check(inp, TOL[dtype])
 
 
+def test_heavy_tailed_gated_output_fp32():
+    # a gated output whose largest element is about 45 times its RMS: the bound then asks for a few
+    # ulp on that element, so the error of delta (softplus of dt in about -7..-2) must stay near 1 ulp
+    inp = synth.selective_inputs(3, 203, 79, 4, synth.F32, 939316136, with_z=True, with_skip=False)
+    check(inp, TOL[synth.F32])
+
+
+def test_softplus_at_minus_infinity_gives_zero_step():
+    # dt = -inf: delta = softplus(-inf) = 0, so the row leaves the states unchanged
+    inp = synth.selective_inputs(2, 40, 64, 16, synth.F32, 36, with_h0=True)
+    inp.t["dt"].data[:, 5:9, :7] = -np.inf
+    check(inp, TOL[synth.F32])
+
+
 def test_long_memory_fp32():
     # one scale (A_n = -(n+1)) over 2048 steps: the longest-lived states accumulate the most rounding
     inp = synth.selective_inputs(1, 2048, 64, 16, synth.F32, 32, num_scales=1, with_h0=True)
