@@ -33,10 +33,10 @@
  *   - Base pointers must be 16-byte aligned.  Outputs must not overlap inputs.
  *   - Empty problems (a zero size) launch nothing except copying the initial
  *     state to the final-state output (or zero-filling it).
- *   - The scans use a device scratch buffer that the library allocates on first
- *     use per (device, stream) and keeps until the process ends (it grows when a
- *     larger problem needs it).  Calls on one stream are serialised by the
- *     stream; calls on different streams use different scratch buffers.
+ *   - The library allocates no memory and keeps no state between calls.  Scans
+ *     that pass partial results between workgroups take a caller-owned device
+ *     `workspace` (see "Workspaces" below).  The library is reentrant and
+ *     thread-safe: calls share nothing but the memory the caller passes.
  *   - NaN / Inf inputs propagate by IEEE rules; nothing is trapped.
  */
 #ifndef SSD_H
@@ -59,7 +59,8 @@ enum {
   SSD_ERR_ALIGN = 4,  /* a base pointer is not 16-byte aligned                    */
   SSD_ERR_VALUE = 5,  /* a scalar argument is out of range (c, lower_bound, ...)  */
   SSD_ERR_ALIAS = 6,  /* an output overlaps an input                              */
-  SSD_ERR_HIP = 7     /* the HIP runtime reported an error (allocation, launch)   */
+  SSD_ERR_HIP = 7,    /* the HIP runtime reported an error (launch, copy)         */
+  SSD_ERR_TIMEOUT = 8 /* a bounded wait between workgroups expired (ssd_workspace_check) */
 };
 
 /* Static description of a status code. */
@@ -68,6 +69,40 @@ const char* ssd_status_str(int status);
 const char* ssd_last_error(void);
 /* Library ABI version (major * 10000 + minor * 100 + patch). */
 int ssd_version(void);
+
+/* ---------------------------------------------------------------------------------------------
+ * Workspaces.  The scans that split one sequence over several workgroups (RG-LRU, MinMax and
+ * selective scans and the gradients of those and of HGRN2) hand partial results and work tickets
+ * from workgroup to workgroup through device memory the caller owns: the `workspace` argument, of
+ * at least the size the matching ssd_*_workspace_bytes query reports for the same sizes on the
+ * current device, 256-byte aligned.
+ *   - A workspace belongs to one entry point.  It must be zero-filled before its first use; each call
+ *     leaves it ready for the next call of the same entry point (it keeps a launch counter, so the
+ *     words one launch publishes never validate for another), so it is reused without clearing for
+ *     any later sizes.  Passed to a different entry point, it must be zero-filled again first.
+ *   - Calls whose work may run at the same time (on different streams, or from threads that do not
+ *     order their calls) need distinct workspaces.
+ *   - A call that needs no workspace (an empty problem) accepts NULL.
+ * Workspace errors: SSD_ERR_NULL (NULL when one is needed), SSD_ERR_SHAPE (workspace_bytes below the
+ * query's size), SSD_ERR_ALIGN (not 256-byte aligned), SSD_ERR_ALIAS (overlaps another argument).
+ *
+ * The workgroups of these scans wait on one another with bounded waits (about a second).  A wait
+ * that expires, which a correct launch never sees, does not hang the GPU: the waiting workgroup
+ * takes NaN as its incoming state (so every output that depends on it reads NaN) and records the
+ * event in the workspace.  ssd_workspace_check reports it.
+ * ------------------------------------------------------------------------------------------- */
+
+/* Waits for `stream` to finish its work, then reports whether any launch that used `workspace` since
+ * the last check had a bounded wait expire: SSD_ERR_TIMEOUT (and the record is cleared) or SSD_OK.
+ * The workspace is one passed to any of the calls that take one.  SSD_ERR_NULL for a NULL workspace,
+ * SSD_ERR_HIP if the runtime fails. */
+int ssd_workspace_check(const void* workspace, void* stream);
+
+/* Test hook for the timeout path, process-wide: the bounded waits of later launches give up after
+ * `spin_limit` polls (0 restores the default), and with `never_ready` nonzero they wait for words no
+ * launch ever writes, so every wait expires (then outputs read NaN as described above and
+ * ssd_workspace_check reports SSD_ERR_TIMEOUT).  Every kernel still runs to its end. */
+void ssd_testing_lookback(unsigned int spin_limit, int never_ready);
 
 /* Steps per chunk of the state-size-1 scans (RG-LRU, MinMax).  Their optional `chunk_states`
  * buffers are [B, ceil(L / SSD_SCAN_CHUNK), D] fp32, entry [b, k, d] being the state entering step
@@ -91,14 +126,19 @@ int ssd_version(void);
  *   h_last              : [B, D] fp32 or NULL; receives h_{L-1} (h0 when L = 0), never gated
  *   chunk_states        : [B, ceil(L/64), D] fp32 or NULL; receives the state entering each 64-step
  *                         chunk (see SSD_SCAN_CHUNK), the same bits ssd_rglru_scan_backward recomputes
+ *   workspace           : see "Workspaces"; size from ssd_rglru_scan_workspace_bytes(B, L, D)
  * Errors: SSD_ERR_NULL (x, r_logit, i_logit, a_log, y when B*L*D > 0), SSD_ERR_SHAPE (negative
  * size, D >= 2^22, or B * ceil(L/64) * ceil(D/64) >= 2^31), SSD_ERR_DTYPE, SSD_ERR_ALIGN,
- * SSD_ERR_VALUE (c not finite), SSD_ERR_ALIAS.
+ * SSD_ERR_VALUE (c not finite), SSD_ERR_ALIAS, and the workspace errors.
  * ------------------------------------------------------------------------------------------- */
 int ssd_rglru_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype,
                    const void* x, const void* r_logit, const void* i_logit,
                    const float* a_log, float c, const float* h0, const void* gate,
-                   void* y, float* h_last, float* chunk_states, void* stream);
+                   void* y, float* h_last, float* chunk_states,
+                   void* workspace, size_t workspace_bytes, void* stream);
+/* Workspace size of ssd_rglru_scan for these sizes, in *bytes.  SSD_ERR_NULL (bytes NULL) or
+ * SSD_ERR_SHAPE (sizes the scan rejects).  The other queries below follow the same convention. */
+int ssd_rglru_scan_workspace_bytes(int64_t B, int64_t L, int64_t D, size_t* bytes);
 
 /* Gradients of ssd_rglru_scan (reverse-time adjoint; the pages train through autograd and print no
  * backward pass, so this is the gradient of the forward definition above) for the loss
@@ -116,15 +156,17 @@ int ssd_rglru_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype,
  *   dh0                 : [B, D] fp32 or NULL
  * The per-step forward states are rebuilt inside each 64-step chunk from the chunk's incoming state:
  * the forward's chunk_states when given, else a forward pass first records them in the library's
- * scratch (then the call needs no saved activations).  Results are deterministic, and identical
+ * workspace (then the call needs no saved activations).  Results are deterministic, and identical
  * with and without chunk_states.
+ * workspace: see "Workspaces"; size from ssd_rglru_scan_backward_workspace_bytes(B, L, D).
  * Errors as ssd_rglru_scan, plus SSD_ERR_NULL for missing dy / dx / dr_logit / di_logit / da_log. */
 int ssd_rglru_scan_backward(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype,
                             const void* x, const void* r_logit, const void* i_logit,
                             const float* a_log, float c, const float* h0, const void* gate,
                             const float* chunk_states, const void* dy, const float* dh_last,
                             void* dx, void* dr_logit, void* di_logit, float* da_log, float* dh0,
-                            void* dgate, void* stream);
+                            void* dgate, void* workspace, size_t workspace_bytes, void* stream);
+int ssd_rglru_scan_backward_workspace_bytes(int64_t B, int64_t L, int64_t D, size_t* bytes);
 
 /* One RG-LRU decode step (RGLRU.step: single token, state carried by the caller).
  *   x, r_logit, i_logit : [B, D] (in dtype);  a_log : [D] fp32;  gate : [B, D] or NULL
@@ -150,11 +192,14 @@ int ssd_rglru_update(int64_t B, int64_t D, int in_dtype, int out_dtype,
  *   y                   : [B, L, D] (out dtype)
  *   x_last              : [B, D] fp32 or NULL; receives x_{L-1} (x0 when L = 0), never gated
  *   chunk_states        : [B, ceil(L/64), D] fp32 or NULL, as for ssd_rglru_scan
+ *   workspace           : see "Workspaces"; size from ssd_minmax_scan_workspace_bytes(B, L, D)
  * Errors: as ssd_rglru_scan (no scalar arguments).
  * ------------------------------------------------------------------------------------------- */
 int ssd_minmax_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype,
                     const void* r, const void* s, const float* x0, const void* gate,
-                    void* y, float* x_last, float* chunk_states, void* stream);
+                    void* y, float* x_last, float* chunk_states,
+                    void* workspace, size_t workspace_bytes, void* stream);
+int ssd_minmax_scan_workspace_bytes(int64_t B, int64_t L, int64_t D, size_t* bytes);
 
 /* Gradients of ssd_minmax_scan for the loss  sum dy * y + sum dx_last * x_last.  The package trains
  * the neuron through torch autograd, so the derivative of min and max is torch's: the selected operand
@@ -173,11 +218,13 @@ int ssd_minmax_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype
  * The forward states are rebuilt from each 64-step chunk's incoming state (the forward's
  * chunk_states, else recorded by a forward pass first).  Results are deterministic, and identical
  * with and without chunk_states.
+ * workspace: see "Workspaces"; size from ssd_minmax_scan_backward_workspace_bytes(B, L, D).
  * Errors as ssd_minmax_scan, plus SSD_ERR_NULL for missing dy / dr / ds. */
 int ssd_minmax_scan_backward(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype,
                              const void* r, const void* s, const float* x0, const void* gate,
                              const float* chunk_states, const void* dy, const float* dx_last, void* dr, void* ds,
-                             float* dx0, void* dgate, void* stream);
+                             float* dx0, void* dgate, void* workspace, size_t workspace_bytes, void* stream);
+int ssd_minmax_scan_backward_workspace_bytes(int64_t B, int64_t L, int64_t D, size_t* bytes);
 
 /* One MinMax decode step.  r, s, gate : [B, D] (gate may be NULL); state : [B, D] fp32 in/out;
  * y : [B, D].  Errors as ssd_minmax_scan; y must not overlap state. */
@@ -228,15 +275,20 @@ int ssd_causal_conv1d_update(int64_t B, int64_t D, int64_t W, int in_dtype, int 
  *                  and is not read on the host).  Zero-length sequences are allowed.
  *   h0, h_last   : [B or nseq, D, N] fp32 or NULL.
  *   Supported N : 1, 2, 4, 8, 16.
+ *   workspace    : see "Workspaces"; size from ssd_selective_scan_workspace_bytes(B, L, D, N, nseq,
+ *                  packed) with packed = (cu_seqlens != NULL) (nseq is ignored when not packed)
  * Errors: SSD_ERR_NULL, SSD_ERR_SHAPE (negative size, unsupported N, cu_seqlens with B != 1,
- * nseq < 0), SSD_ERR_DTYPE, SSD_ERR_ALIGN, SSD_ERR_ALIAS.
+ * nseq < 0), SSD_ERR_DTYPE, SSD_ERR_ALIGN, SSD_ERR_ALIAS, and the workspace errors.
  * ------------------------------------------------------------------------------------------- */
 int ssd_selective_scan(int64_t B, int64_t L, int64_t D, int64_t N, int in_dtype, int out_dtype,
                        const void* x, const void* dt, const float* A,
                        const void* Bm, const void* Cm, const float* Dskip, const void* z,
                        const float* dt_bias, int dt_softplus,
                        const int32_t* cu_seqlens, int64_t nseq,
-                       const float* h0, void* y, float* h_last, void* stream);
+                       const float* h0, void* y, float* h_last,
+                       void* workspace, size_t workspace_bytes, void* stream);
+int ssd_selective_scan_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int64_t nseq, int packed,
+                                       size_t* bytes);
 
 /* Gradients of ssd_selective_scan (batched, or packed varlen sequences as there) for the loss
  *     sum_{b,t,d} dy * y  +  sum_{sequence,d,n} dh_last * h_last.
@@ -253,10 +305,11 @@ int ssd_selective_scan(int64_t B, int64_t L, int64_t D, int64_t N, int in_dtype,
  *   dBm, dCm            : [B, L, N] (out dtype)
  *   dA                  : [D, N] fp32;  dDskip, ddt_bias : [D] fp32 or NULL;
  *   dh0                 : [B or nseq, D, N] fp32 or NULL (a zero-length sequence gets its dh_last)
- * Every output is overwritten (not accumulated).  The forward states are recomputed (the scratch
- * holds per-16-row-segment states, about 5 x B * ceil(L/16) * D * N fp32).  Reductions run in a fixed
- * order: results are deterministic.  Errors as ssd_selective_scan, plus SSD_ERR_NULL for missing
- * dy / dx / ddt / dBm / dCm / dA (or dz with z). */
+ * Every output is overwritten (not accumulated).  The forward states are recomputed (the workspace
+ * holds per-16-row-segment states, about 5 x B * ceil(L/16) * D * N fp32; see "Workspaces", size
+ * from ssd_selective_scan_backward_workspace_bytes).  Reductions run in a fixed order: results are
+ * deterministic.  Errors as ssd_selective_scan, plus SSD_ERR_NULL for missing dy / dx / ddt / dBm /
+ * dCm / dA (or dz with z). */
 int ssd_selective_scan_backward(int64_t B, int64_t L, int64_t D, int64_t N, int in_dtype, int out_dtype,
                                 const void* x, const void* dt, const float* A,
                                 const void* Bm, const void* Cm, const float* Dskip, const void* z,
@@ -264,7 +317,10 @@ int ssd_selective_scan_backward(int64_t B, int64_t L, int64_t D, int64_t N, int 
                                 const int32_t* cu_seqlens, int64_t nseq, const float* h0,
                                 const void* dy, const float* dh_last,
                                 void* dx, void* ddt, float* dA, void* dBm, void* dCm,
-                                float* dDskip, void* dz, float* ddt_bias, float* dh0, void* stream);
+                                float* dDskip, void* dz, float* ddt_bias, float* dh0,
+                                void* workspace, size_t workspace_bytes, void* stream);
+int ssd_selective_scan_backward_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int64_t nseq,
+                                                int packed, size_t* bytes);
 
 /* One selective decode step (the L == 1 path of MultiScaleSSM.forward with past_state).
  *   x, dt, z, y : [B, D];  Bm, Cm : [B, N];  A : [D, N] fp32;  state : [B, D, N] fp32 in place.
@@ -301,18 +357,23 @@ int ssd_hgrn2_scan(int64_t B, int64_t L, int64_t H, int64_t d, int in_dtype, int
  *   (c_t is the derivative with respect to log g_t; 0 where sigmoid(g_logit) is 0).
  *   inputs            : as ssd_hgrn2_scan (S0 [B, H, d, d] fp32 or NULL), plus
  *   o                 : [B, L, H, d] fp32, the forward output for these inputs, or NULL (then it is
- *                       recomputed into the scratch buffer: B * L * H * d fp32 more)
+ *                       recomputed into the workspace: B * L * H * d fp32 more)
  *   dO                : [B, L, H, d] (in dtype);  dS_last : [B, H, d, d] fp32 or NULL (= 0)
  *   dq, dk, dv, dg_logit : [B, L, H, d] (out dtype);  dS0 : [B, H, d, d] fp32 or NULL
- * Any lower_bound in [0, 1] (no decay ratios are formed).  Every output is overwritten.  The scratch
+ *   workspace         : see "Workspaces"; size from ssd_hgrn2_scan_backward_workspace_bytes(B, L, H,
+ *                       d, in_dtype, have_o) with have_o = (o != NULL)
+ * Any lower_bound in [0, 1] (no decay ratios are formed).  Every output is overwritten.  The workspace
  * holds S_last (B * H * d * d fp32) and, for fp32 inputs, the state after every 32nd token (from
- * which the running sum c_t is restarted exactly: B * H * floor((L - 1) / 32) * d * d fp32).  Errors as ssd_hgrn2_scan, plus SSD_ERR_NULL for missing dO, dq,
- * dk, dv or dg_logit. */
+ * which the running sum c_t is restarted exactly: B * H * floor((L - 1) / 32) * d * d fp32).
+ * Errors as ssd_hgrn2_scan, plus SSD_ERR_NULL for missing dO, dq, dk, dv or dg_logit, and the
+ * workspace errors. */
 int ssd_hgrn2_scan_backward(int64_t B, int64_t L, int64_t H, int64_t d, int in_dtype, int out_dtype,
                             const void* q, const void* k, const void* v, const void* g_logit,
                             float lower_bound, const float* S0, const float* o, const void* dO,
                             const float* dS_last, void* dq, void* dk, void* dv, void* dg_logit,
-                            float* dS0, void* stream);
+                            float* dS0, void* workspace, size_t workspace_bytes, void* stream);
+int ssd_hgrn2_scan_backward_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t d, int in_dtype, int have_o,
+                                            size_t* bytes);
 
 /* One HGRN2 decode step.  q, k, v, g_logit, o : [B, H, d];  S : [B, H, d, d] fp32 in place.
  * Errors as ssd_hgrn2_scan. */

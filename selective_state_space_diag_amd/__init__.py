@@ -2,14 +2,23 @@
 
 A thin ctypes layer over ``libssd.so`` (the C ABI declared in ``include/ssd.h``).
 It only marshals arguments: checks tensor placement, dtype, shape and contiguity,
-allocates outputs with torch, and passes raw device pointers plus torch's current
-HIP stream.  Every step of every scan runs in the HIP kernels.  There is no CPU
-or eager fallback: importing works without a GPU, but each call raises if the
-library is not built or no GPU is present.
+allocates outputs (and the scans' workspaces) with torch, and passes raw device
+pointers plus torch's current HIP stream.  Every step of every scan runs in the
+HIP kernels.  There is no CPU or eager fallback: importing works without a GPU,
+but each call raises if the library is not built or no GPU is present.
 
 Entry points (same names as the C ABI without the ``ssd_`` prefix):
-    rglru_scan, rglru_scan_backward, rglru_update, selective_scan, selective_update, hgrn2_scan, hgrn2_update,
-    minmax_scan, minmax_update, causal_conv1d, causal_conv1d_update
+    rglru_scan, rglru_scan_backward, rglru_update,
+    minmax_scan, minmax_scan_backward, minmax_update,
+    causal_conv1d, causal_conv1d_update,
+    selective_scan, selective_scan_backward, selective_update,
+    hgrn2_scan, hgrn2_scan_backward, hgrn2_update (gate_axis="value" or "key"), readout_norm,
+    workspace_check, testing_lookback
+
+Workspaces: the scans that pass partial results between workgroups take a caller-owned device
+workspace (``ssd_*_workspace_bytes`` gives its size).  By default this module keeps one zero-filled
+workspace per (device, stream, entry point), allocated through torch and grown on demand; a call may
+instead pass its own zero-filled uint8 tensor as ``workspace=`` (used by that entry point only).
 """
 from __future__ import annotations
 
@@ -24,17 +33,22 @@ LIB_PATH = os.path.join(_PKG, "libssd.so")
 
 SSD_F32, SSD_BF16 = 0, 1
 STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_DTYPE", 4: "SSD_ERR_ALIGN",
-                5: "SSD_ERR_VALUE", 6: "SSD_ERR_ALIAS", 7: "SSD_ERR_HIP"}
+                5: "SSD_ERR_VALUE", 6: "SSD_ERR_ALIAS", 7: "SSD_ERR_HIP", 8: "SSD_ERR_TIMEOUT"}
+SSD_ERR_HIP, SSD_ERR_TIMEOUT = 7, 8
 
 # Every symbol include/ssd.h declares.
 SCAN_CHUNK = 64  # SSD_SCAN_CHUNK of ssd.h
 
-EXPORTS = ("ssd_status_str", "ssd_last_error", "ssd_version", "ssd_rglru_scan", "ssd_rglru_scan_backward",
+EXPORTS = ("ssd_status_str", "ssd_last_error", "ssd_version", "ssd_testing_lookback", "ssd_workspace_check",
+           "ssd_rglru_scan", "ssd_rglru_scan_backward",
            "ssd_rglru_update",
            "ssd_selective_scan", "ssd_selective_update", "ssd_hgrn2_scan", "ssd_hgrn2_update", "ssd_minmax_scan",
            "ssd_minmax_update", "ssd_minmax_scan_backward", "ssd_causal_conv1d", "ssd_causal_conv1d_update",
            "ssd_selective_scan_backward", "ssd_hgrn2_scan_backward", "ssd_hgrn2_key_scan", "ssd_hgrn2_key_update",
-           "ssd_readout_norm")
+           "ssd_readout_norm", "ssd_rglru_scan_workspace_bytes", "ssd_rglru_scan_backward_workspace_bytes",
+           "ssd_minmax_scan_workspace_bytes", "ssd_minmax_scan_backward_workspace_bytes",
+           "ssd_selective_scan_workspace_bytes", "ssd_selective_scan_backward_workspace_bytes",
+           "ssd_hgrn2_scan_backward_workspace_bytes")
 
 
 class SSDError(RuntimeError):
@@ -51,6 +65,8 @@ _lib = None
 _i64 = ctypes.c_int64
 _vp = ctypes.c_void_p
 _fp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+_szp = ctypes.POINTER(ctypes.c_size_t)
 
 
 def lib() -> ctypes.CDLL:
@@ -65,27 +81,30 @@ def lib() -> ctypes.CDLL:
         L.ssd_last_error.restype = ctypes.c_char_p
         L.ssd_last_error.argtypes = []
         L.ssd_version.restype = ctypes.c_int
+        L.ssd_testing_lookback.argtypes = [ctypes.c_uint, ctypes.c_int]
+        L.ssd_testing_lookback.restype = None
+        L.ssd_workspace_check.argtypes = [_vp, _vp]
         L.ssd_rglru_scan.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _fp, ctypes.c_float,
-                                     _fp, _vp, _vp, _fp, _fp, _vp]
+                                     _fp, _vp, _vp, _fp, _fp, _vp, _sz, _vp]
         L.ssd_rglru_update.argtypes = [_i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _fp, ctypes.c_float, _vp,
                                        _fp, _vp, _vp]
         L.ssd_rglru_scan_backward.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _fp,
                                               ctypes.c_float, _fp, _vp, _fp, _vp, _fp, _vp, _vp, _vp, _fp, _fp, _vp,
-                                              _vp]
+                                              _vp, _sz, _vp]
         L.ssd_minmax_scan.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _fp, _vp, _vp, _fp, _fp,
-                                      _vp]
+                                      _vp, _sz, _vp]
         L.ssd_minmax_update.argtypes = [_i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _fp, _vp, _vp]
         L.ssd_minmax_scan_backward.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _fp, _vp, _fp,
-                                               _vp, _fp, _vp, _vp, _fp, _vp, _vp]
+                                               _vp, _fp, _vp, _vp, _fp, _vp, _vp, _sz, _vp]
         L.ssd_causal_conv1d.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _fp, _fp, _fp, _vp,
                                         _fp, _vp]
         L.ssd_causal_conv1d_update.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _fp, _fp, _fp, _vp,
                                                _vp]
         L.ssd_selective_scan.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _fp, _vp, _vp,
-                                         _fp, _vp, _fp, ctypes.c_int, _vp, _i64, _fp, _vp, _fp, _vp]
+                                         _fp, _vp, _fp, ctypes.c_int, _vp, _i64, _fp, _vp, _fp, _vp, _sz, _vp]
         L.ssd_selective_scan_backward.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _fp,
                                                   _vp, _vp, _fp, _vp, _fp, ctypes.c_int, _vp, _i64, _fp, _vp, _fp,
-                                                  _vp, _vp, _fp, _vp, _vp, _fp, _vp, _fp, _fp, _vp]
+                                                  _vp, _vp, _fp, _vp, _vp, _fp, _vp, _fp, _fp, _vp, _sz, _vp]
         L.ssd_selective_update.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _fp, _vp, _vp, _fp,
                                            _vp, _fp, ctypes.c_int, _fp, _vp, _vp]
         L.ssd_hgrn2_scan.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp,
@@ -97,8 +116,14 @@ def lib() -> ctypes.CDLL:
         L.ssd_readout_norm.argtypes = [_i64, _i64, ctypes.c_int, ctypes.c_int, _fp, _vp, _fp, _fp, ctypes.c_float, _vp,
                                        _vp]
         L.ssd_hgrn2_scan_backward.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp,
-                                              ctypes.c_float, _fp, _fp, _vp, _fp, _vp, _vp, _vp, _vp, _fp, _vp]
-        for name in EXPORTS[3:]:
+                                              ctypes.c_float, _fp, _fp, _vp, _fp, _vp, _vp, _vp, _vp, _fp, _vp, _sz,
+                                              _vp]
+        for q in ("rglru_scan", "rglru_scan_backward", "minmax_scan", "minmax_scan_backward"):
+            getattr(L, f"ssd_{q}_workspace_bytes").argtypes = [_i64, _i64, _i64, _szp]
+        L.ssd_selective_scan_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64, ctypes.c_int, _szp]
+        L.ssd_selective_scan_backward_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64, ctypes.c_int, _szp]
+        L.ssd_hgrn2_scan_backward_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _szp]
+        for name in EXPORTS[4:]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -160,6 +185,59 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+# ----------------------------------------------------------------------------- workspaces
+# One zero-filled workspace per (device, stream, entry point), grown on demand.  torch allocates it on
+# the current stream, so the zero fill is ordered before the call that first uses it; a replaced
+# (smaller) one is freed to torch's caching allocator, which hands its memory only to later work on
+# the same stream.
+_workspaces = {}
+
+
+def _workspace(entry: str, nbytes: int, device, workspace=None):
+    """(pointer, size) of the workspace for one call of ``entry`` needing ``nbytes``."""
+    if getattr(device, "type", None) != "cuda":
+        raise ValueError("the inputs must be on the GPU")
+    if nbytes == 0:
+        return None, 0
+    torch = _torch()
+    if workspace is not None:
+        if workspace.dtype != torch.uint8 or workspace.device.type != "cuda" or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 tensor on the GPU")
+        return workspace.data_ptr(), workspace.numel()
+    stream = torch.cuda.current_stream(device)
+    key = (stream.device_index, stream.cuda_stream, entry)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        size = max(nbytes, 1 << 20)
+        size = (size + 4095) // 4096 * 4096
+        ws = torch.zeros(size, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws.data_ptr(), ws.numel()
+
+
+def _ws_bytes(query: str, *args) -> int:
+    n = ctypes.c_size_t(0)
+    _raise(getattr(lib(), f"ssd_{query}_workspace_bytes")(*args, ctypes.byref(n)), f"{query}_workspace_bytes")
+    return int(n.value)
+
+
+def workspace_check(device=None):
+    """Check every workspace this module keeps for ``device``'s current stream (waiting for the stream):
+    raises SSDError with status SSD_ERR_TIMEOUT if a launch had a bounded wait between workgroups expire
+    since the last check (the outputs that depended on it hold NaN)."""
+    torch = _torch()
+    stream = torch.cuda.current_stream(device)
+    for (dev, sptr, entry), ws in list(_workspaces.items()):
+        if dev == stream.device_index and sptr == stream.cuda_stream:
+            _raise(lib().ssd_workspace_check(ws.data_ptr(), ctypes.c_void_p(sptr)), f"workspace_check({entry})")
+
+
+def testing_lookback(spin_limit: int = 0, never_ready: bool = False):
+    """Test hook of the timeout path (``ssd_testing_lookback``): later launches give up their bounded waits
+    after ``spin_limit`` polls (0 = default), and with ``never_ready`` every wait expires."""
+    lib().ssd_testing_lookback(int(spin_limit), int(bool(never_ready)))
+
+
 def _act(ts, names):
     """All activation tensors share one dtype; returns its code."""
     code = None
@@ -182,7 +260,7 @@ def chunk_states_shape(B: int, L: int, D: int):
 
 
 def rglru_scan(x, r_logit, i_logit, a_log, c: float = 8.0, h0=None, return_last_state: bool = False,
-               out_dtype=None, gate=None, chunk_states=None):
+               out_dtype=None, gate=None, chunk_states=None, workspace=None):
     """RG-LRU scan over [B, L, D] (see ``ssd_rglru_scan``); with ``gate``, y = gelu(gate) * h.
     ``chunk_states`` (fp32, ``chunk_states_shape``) receives the state entering each chunk, for
     ``rglru_scan_backward``.  Returns y, or (y, h_last)."""
@@ -192,12 +270,13 @@ def rglru_scan(x, r_logit, i_logit, a_log, c: float = 8.0, h0=None, return_last_
     oc = _out_code(out_dtype)
     y = torch.empty((B, L, D), device=x.device, dtype=torch.bfloat16 if oc == SSD_BF16 else torch.float32)
     h_last = torch.empty((B, D), device=x.device, dtype=torch.float32) if return_last_state else None
+    wp, wn = _workspace("rglru_scan", _ws_bytes("rglru_scan", B, L, D), x.device, workspace)
     st = lib().ssd_rglru_scan(B, L, D, code, oc, _dev(x, "x"), _dev(r_logit, "r_logit", x.shape),
                               _dev(i_logit, "i_logit", x.shape), _dev(a_log, "a_log", (D,), torch.float32),
                               float(c), _dev(h0, "h0", (B, D), torch.float32), _dev(gate, "gate", x.shape),
                               _dev(y, "y"), _dev(h_last, "h_last"),
                               _dev(chunk_states, "chunk_states", chunk_states_shape(B, L, D), torch.float32),
-                              _stream(x.device))
+                              wp, wn, _stream(x.device))
     _raise(st, "rglru_scan")
     return (y, h_last) if return_last_state else y
 
@@ -219,7 +298,7 @@ def rglru_update(x, r_logit, i_logit, a_log, c: float, state, out_dtype=None, ga
 
 
 def rglru_scan_backward(x, r_logit, i_logit, a_log, c, dy, h0=None, gate=None, dh_last=None, out_dtype=None,
-                        chunk_states=None):
+                        chunk_states=None, workspace=None):
     """Gradients of ``rglru_scan`` for the loss sum(dy * y) + sum(dh_last * h_last) (see
     ``ssd_rglru_scan_backward``); ``chunk_states`` from the forward call saves recomputing them.
     Returns a dict: dx, dr_logit, di_logit [B, L, D] (out dtype), da_log [D], dh0 [B, D] (fp32), and
@@ -234,19 +313,22 @@ def rglru_scan_backward(x, r_logit, i_logit, a_log, c, dy, h0=None, gate=None, d
         g["dgate"] = torch.empty((B, L, D), device=x.device, dtype=odt)
     g["da_log"] = torch.empty((D,), device=x.device, dtype=torch.float32)
     g["dh0"] = torch.empty((B, D), device=x.device, dtype=torch.float32)
+    wp, wn = _workspace("rglru_scan_backward", _ws_bytes("rglru_scan_backward", B, L, D), x.device, workspace)
     st = lib().ssd_rglru_scan_backward(
         B, L, D, code, oc, _dev(x, "x"), _dev(r_logit, "r_logit", x.shape), _dev(i_logit, "i_logit", x.shape),
         _dev(a_log, "a_log", (D,), torch.float32), float(c), _dev(h0, "h0", (B, D), torch.float32),
         _dev(gate, "gate", x.shape), _dev(chunk_states, "chunk_states", chunk_states_shape(B, L, D), torch.float32),
         _dev(dy, "dy", x.shape), _dev(dh_last, "dh_last", (B, D), torch.float32),
         _dev(g["dx"], "dx"), _dev(g["dr_logit"], "dr_logit"), _dev(g["di_logit"], "di_logit"),
-        _dev(g["da_log"], "da_log"), _dev(g["dh0"], "dh0"), _dev(g.get("dgate"), "dgate"), _stream(x.device))
+        _dev(g["da_log"], "da_log"), _dev(g["dh0"], "dh0"), _dev(g.get("dgate"), "dgate"), wp, wn,
+        _stream(x.device))
     _raise(st, "rglru_scan_backward")
     return g
 
 
 # ----------------------------------------------------------------------------- MinMax
-def minmax_scan(r, s, x0=None, gate=None, return_last_state: bool = False, out_dtype=None, chunk_states=None):
+def minmax_scan(r, s, x0=None, gate=None, return_last_state: bool = False, out_dtype=None, chunk_states=None,
+                workspace=None):
     """MinMax scan x_t = max(min(r_t, x_{t-1}), s_t) over [B, L, D] (see ``ssd_minmax_scan``);
     with ``gate``, y = x * gate; ``chunk_states`` as for ``rglru_scan``.  Returns y, or (y, x_last)."""
     torch = _torch()
@@ -255,11 +337,12 @@ def minmax_scan(r, s, x0=None, gate=None, return_last_state: bool = False, out_d
     oc = _out_code(out_dtype)
     y = torch.empty((B, L, D), device=r.device, dtype=torch.bfloat16 if oc == SSD_BF16 else torch.float32)
     x_last = torch.empty((B, D), device=r.device, dtype=torch.float32) if return_last_state else None
+    wp, wn = _workspace("minmax_scan", _ws_bytes("minmax_scan", B, L, D), r.device, workspace)
     st = lib().ssd_minmax_scan(B, L, D, code, oc, _dev(r, "r"), _dev(s, "s", r.shape),
                                _dev(x0, "x0", (B, D), torch.float32), _dev(gate, "gate", r.shape), _dev(y, "y"),
                                _dev(x_last, "x_last"),
                                _dev(chunk_states, "chunk_states", chunk_states_shape(B, L, D), torch.float32),
-                               _stream(r.device))
+                               wp, wn, _stream(r.device))
     _raise(st, "minmax_scan")
     return (y, x_last) if return_last_state else y
 
@@ -277,7 +360,8 @@ def minmax_update(r, s, state, gate=None, out_dtype=None):
     return y
 
 
-def minmax_scan_backward(r, s, dy, x0=None, gate=None, dx_last=None, out_dtype=None, chunk_states=None):
+def minmax_scan_backward(r, s, dy, x0=None, gate=None, dx_last=None, out_dtype=None, chunk_states=None,
+                         workspace=None):
     """Gradients of ``minmax_scan`` for the loss sum(dy * y) + sum(dx_last * x_last) (see
     ``ssd_minmax_scan_backward``).  Returns a dict: dr, ds [B, L, D] (out dtype), dx0 [B, D] (fp32),
     and dgate when a gate is given."""
@@ -290,11 +374,12 @@ def minmax_scan_backward(r, s, dy, x0=None, gate=None, dx_last=None, out_dtype=N
     if gate is not None:
         g["dgate"] = torch.empty((B, L, D), device=r.device, dtype=odt)
     g["dx0"] = torch.empty((B, D), device=r.device, dtype=torch.float32)
+    wp, wn = _workspace("minmax_scan_backward", _ws_bytes("minmax_scan_backward", B, L, D), r.device, workspace)
     st = lib().ssd_minmax_scan_backward(
         B, L, D, code, oc, _dev(r, "r"), _dev(s, "s", r.shape), _dev(x0, "x0", (B, D), torch.float32),
         _dev(gate, "gate", r.shape), _dev(chunk_states, "chunk_states", chunk_states_shape(B, L, D), torch.float32),
         _dev(dy, "dy", r.shape), _dev(dx_last, "dx_last", (B, D), torch.float32),
-        _dev(g["dr"], "dr"), _dev(g["ds"], "ds"), _dev(g["dx0"], "dx0"), _dev(g.get("dgate"), "dgate"),
+        _dev(g["dr"], "dr"), _dev(g["ds"], "ds"), _dev(g["dx0"], "dx0"), _dev(g.get("dgate"), "dgate"), wp, wn,
         _stream(r.device))
     _raise(st, "minmax_scan_backward")
     return g
@@ -354,7 +439,7 @@ def _cu_seqlens_device(cu_seqlens, L, device, check: bool):
 
 def selective_scan(x, dt, A, Bm, Cm, Dskip=None, z=None, dt_bias=None, dt_softplus: bool = True,
                    cu_seqlens=None, h0=None, return_last_state: bool = False, out_dtype=None,
-                   check_cu_seqlens: bool = True):
+                   check_cu_seqlens: bool = True, workspace=None):
     """Multi-scale selective scan over [B, L, D] with N states (see ``ssd_selective_scan``).
 
     ``cu_seqlens`` (int32 [nseq + 1], host or device) packs nseq sequences into B = 1.
@@ -371,12 +456,14 @@ def selective_scan(x, dt, A, Bm, Cm, Dskip=None, z=None, dt_bias=None, dt_softpl
         nseq = cu.numel() - 1
     y = torch.empty((B, L, D), device=x.device, dtype=torch.bfloat16 if oc == SSD_BF16 else torch.float32)
     h_last = torch.empty((nseq, D, N), device=x.device, dtype=torch.float32) if return_last_state else None
+    wp, wn = _workspace("selective_scan", _ws_bytes("selective_scan", B, L, D, N, nseq, int(cu is not None)),
+                        x.device, workspace)
     st = lib().ssd_selective_scan(
         B, L, D, N, code, oc, _dev(x, "x"), _dev(dt, "dt", x.shape), _dev(A, "A", (D, N), torch.float32),
         _dev(Bm, "Bm", (B, L, N)), _dev(Cm, "Cm", (B, L, N)), _dev(Dskip, "Dskip", (D,), torch.float32),
         _dev(z, "z", x.shape), _dev(dt_bias, "dt_bias", (D,), torch.float32), int(bool(dt_softplus)),
         _dev(cu, "cu_seqlens"), nseq, _dev(h0, "h0", (nseq, D, N), torch.float32), _dev(y, "y"),
-        _dev(h_last, "h_last"), _stream(x.device))
+        _dev(h_last, "h_last"), wp, wn, _stream(x.device))
     _raise(st, "selective_scan")
     return (y, h_last) if return_last_state else y
 
@@ -400,7 +487,8 @@ def selective_update(x, dt, A, Bm, Cm, state, Dskip=None, z=None, dt_bias=None, 
 
 
 def selective_scan_backward(x, dt, A, Bm, Cm, dy, Dskip=None, z=None, dt_bias=None, dt_softplus: bool = True, h0=None,
-                            dh_last=None, out_dtype=None, cu_seqlens=None, check_cu_seqlens: bool = True):
+                            dh_last=None, out_dtype=None, cu_seqlens=None, check_cu_seqlens: bool = True,
+                            workspace=None):
     """Gradients of ``selective_scan`` for the loss sum(dy * y) + sum(dh_last * h_last) (see
     ``ssd_selective_scan_backward``); ``cu_seqlens`` as for ``selective_scan``.  Returns a dict: dx,
     ddt [B, L, D], dBm, dCm [B, L, N] (out dtype), dA [D, N], dh0 [B or nseq, D, N] (fp32), and dDskip,
@@ -427,6 +515,8 @@ def selective_scan_backward(x, dt, A, Bm, Cm, dy, Dskip=None, z=None, dt_bias=No
         g["dz"] = torch.empty((B, L, D), device=dev, dtype=odt)
     if dt_bias is not None:
         g["ddt_bias"] = torch.empty((D,), device=dev, dtype=torch.float32)
+    wp, wn = _workspace("selective_scan_backward",
+                        _ws_bytes("selective_scan_backward", B, L, D, N, nseq, int(cu is not None)), dev, workspace)
     st = lib().ssd_selective_scan_backward(
         B, L, D, N, code, oc, _dev(x, "x"), _dev(dt, "dt", x.shape), _dev(A, "A", (D, N), torch.float32),
         _dev(Bm, "Bm", (B, L, N)), _dev(Cm, "Cm", (B, L, N)), _dev(Dskip, "Dskip", (D,), torch.float32),
@@ -434,7 +524,7 @@ def selective_scan_backward(x, dt, A, Bm, Cm, dy, Dskip=None, z=None, dt_bias=No
         _dev(cu, "cu_seqlens"), nseq, _dev(h0, "h0", (nseq, D, N), torch.float32), _dev(dy, "dy", x.shape),
         _dev(dh_last, "dh_last", (nseq, D, N), torch.float32), _dev(g["dx"], "dx"), _dev(g["ddt"], "ddt"),
         _dev(g["dA"], "dA"), _dev(g["dBm"], "dBm"), _dev(g["dCm"], "dCm"), _dev(g.get("dDskip"), "dDskip"),
-        _dev(g.get("dz"), "dz"), _dev(g.get("ddt_bias"), "ddt_bias"), _dev(g["dh0"], "dh0"), _stream(dev))
+        _dev(g.get("dz"), "dz"), _dev(g.get("ddt_bias"), "ddt_bias"), _dev(g["dh0"], "dh0"), wp, wn, _stream(dev))
     _raise(st, "selective_scan_backward")
     return g
 
@@ -458,7 +548,8 @@ def hgrn2_scan(q, k, v, g_logit, lower_bound: float, S0=None, return_last_state:
     return (o, S_last) if return_last_state else o
 
 
-def hgrn2_scan_backward(q, k, v, g_logit, lower_bound: float, do, S0=None, dS_last=None, o=None, out_dtype=None):
+def hgrn2_scan_backward(q, k, v, g_logit, lower_bound: float, do, S0=None, dS_last=None, o=None, out_dtype=None,
+                        workspace=None):
     """Gradients of ``hgrn2_scan`` for the loss sum(do * o) + sum(dS_last * S_last) (see
     ``ssd_hgrn2_scan_backward``).  ``o`` may pass the forward's fp32 output to save recomputing it.
     Returns a dict: dq, dk, dv, dg_logit [B, L, H, d] (out dtype) and dS0 [B, H, d, d] (fp32)."""
@@ -470,12 +561,14 @@ def hgrn2_scan_backward(q, k, v, g_logit, lower_bound: float, do, S0=None, dS_la
     dev = q.device
     g = {n: torch.empty((B, L, H, d), device=dev, dtype=odt) for n in ("dq", "dk", "dv", "dg_logit")}
     g["dS0"] = torch.empty((B, H, d, d), device=dev, dtype=torch.float32)
+    wp, wn = _workspace("hgrn2_scan_backward",
+                        _ws_bytes("hgrn2_scan_backward", B, L, H, d, code, int(o is not None)), dev, workspace)
     st = lib().ssd_hgrn2_scan_backward(
         B, L, H, d, code, oc, _dev(q, "q"), _dev(k, "k", q.shape), _dev(v, "v", q.shape),
         _dev(g_logit, "g_logit", q.shape), float(lower_bound), _dev(S0, "S0", (B, H, d, d), torch.float32),
         _dev(o, "o", q.shape, torch.float32), _dev(do, "do", q.shape),
         _dev(dS_last, "dS_last", (B, H, d, d), torch.float32), _dev(g["dq"], "dq"), _dev(g["dk"], "dk"),
-        _dev(g["dv"], "dv"), _dev(g["dg_logit"], "dg_logit"), _dev(g["dS0"], "dS0"), _stream(dev))
+        _dev(g["dv"], "dv"), _dev(g["dg_logit"], "dg_logit"), _dev(g["dS0"], "dS0"), wp, wn, _stream(dev))
     _raise(st, "hgrn2_scan_backward")
     return g
 
@@ -520,6 +613,8 @@ def readout_norm(o, gate=None, weight=None, bias=None, eps: float = 1e-5, out_dt
     return y
 
 
-__all__ = ["chunk_states_shape", "SCAN_CHUNK", "rglru_scan", "rglru_scan_backward", "rglru_update", "selective_scan", "selective_scan_backward", "selective_update", "hgrn2_scan", "hgrn2_update",
-           "minmax_scan", "minmax_update", "minmax_scan_backward", "causal_conv1d", "causal_conv1d_update", "lib", "LIB_PATH", "EXPORTS",
-           "SSDError", "SSDValueError", "SSD_F32", "SSD_BF16"]
+__all__ = ["chunk_states_shape", "SCAN_CHUNK", "rglru_scan", "rglru_scan_backward", "rglru_update", "selective_scan",
+           "selective_scan_backward", "selective_update", "hgrn2_scan", "hgrn2_scan_backward", "hgrn2_update",
+           "readout_norm", "minmax_scan", "minmax_update", "minmax_scan_backward", "causal_conv1d",
+           "causal_conv1d_update", "workspace_check", "testing_lookback", "lib", "LIB_PATH", "EXPORTS", "SSDError",
+           "SSDValueError", "SSD_F32", "SSD_BF16", "SSD_ERR_HIP", "SSD_ERR_TIMEOUT"]

@@ -1,16 +1,16 @@
-// api.cpp -- the C ABI declared in include/ssd.h: host-side validation, scratch management and
-// dispatch to the kernel launchers.  Nothing is enqueued unless every check passes.
+// api.cpp -- the C ABI declared in include/ssd.h: host-side validation (arguments and the caller's
+// workspace) and dispatch to the kernel launchers.  Nothing is enqueued unless every check passes.
+// The library allocates nothing and keeps no state between calls besides the process-wide settings
+// of the timeout test hook.
 #include "ssd.h"
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
-#include <map>
-#include <mutex>
 #include <string>
-#include <tuple>
 #include <utility>
 #include <vector>
 
@@ -27,51 +27,6 @@ int fail(int status, const std::string& msg) {
 
 int ok() {
   g_last_error.clear();
-  return SSD_OK;
-}
-
-// ------------------------------------------------------------------ scratch buffers
-// One buffer per (device, stream, purpose), allocated zero-filled, grown on demand, kept until
-// process exit.  Purposes are kept apart so that one kernel family never reads another's data.
-// RG-LRU and MinMax share a kind: their launches use the same epoch-tagged lookback protocol, so
-// words left by one never validate for the next launch on the stream.
-enum ScratchKind { kScratchScan1 = 0, kScratchSelective = 1, kScratchScan1Bwd = 2, kScratchSelectiveBwd = 3,
-                   kScratchHgrn2Bwd = 4 };
-
-struct ScratchBuf {
-  void* ptr = nullptr;
-  size_t bytes = 0;
-};
-
-std::mutex g_scratch_mu;
-std::map<std::tuple<int, void*, int>, ScratchBuf> g_scratch;
-
-int get_scratch(void* stream, int kind, size_t need, void** out) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return fail(SSD_ERR_HIP, "hipGetDevice failed");
-  std::lock_guard<std::mutex> lock(g_scratch_mu);
-  ScratchBuf& sb = g_scratch[std::make_tuple(dev, stream, kind)];
-  if (sb.bytes < need) {
-    if (sb.ptr) {
-      // the stream may still be using the old buffer
-      if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)
-        return fail(SSD_ERR_HIP, "hipStreamSynchronize failed while growing scratch");
-      (void)hipFree(sb.ptr);
-      sb.ptr = nullptr;
-      sb.bytes = 0;
-    }
-    size_t bytes = need < (1u << 20) ? (1u << 20) : need;
-    bytes = (bytes + 4095) / 4096 * 4096;
-    void* p = nullptr;
-    if (hipMalloc(&p, bytes) != hipSuccess) return fail(SSD_ERR_HIP, "hipMalloc of scratch failed");
-    if (hipMemset(p, 0, bytes) != hipSuccess) {
-      (void)hipFree(p);
-      return fail(SSD_ERR_HIP, "hipMemset of scratch failed");
-    }
-    sb.ptr = p;
-    sb.bytes = bytes;
-  }
-  *out = sb.ptr;
   return SSD_OK;
 }
 
@@ -129,6 +84,48 @@ bool too_big(std::initializer_list<int64_t> dims) {
   return prod > 9.0e15;
 }
 
+// ------------------------------------------------------------------ workspaces
+// The timeout test hook (ssd_testing_lookback): 0 = default spin limit; never_ready shifts the epoch
+// the waits accept to one no launch writes.
+std::atomic<unsigned int> g_spin_limit{0};
+std::atomic<int> g_never_ready{0};
+
+ssd::WaitCfg wait_cfg() {
+  ssd::WaitCfg w;
+  const unsigned int lim = g_spin_limit.load(std::memory_order_relaxed);
+  if (lim) w.spin_limit = lim;
+  if (g_never_ready.load(std::memory_order_relaxed)) w.skew = 0x80000000u;
+  return w;
+}
+
+// The caller's workspace against what the call needs; it must not overlap the call's other buffers.
+int check_workspace(void* ws, size_t ws_bytes, size_t need, const std::vector<Span>& others) {
+  if (need == 0) return SSD_OK;
+  if (!ws) return fail(SSD_ERR_NULL, "workspace is required: " + std::to_string(need) + " bytes (see the *_workspace_bytes query)");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(SSD_ERR_ALIGN, "workspace is not 256-byte aligned");
+  if (ws_bytes < need)
+    return fail(SSD_ERR_SHAPE, "workspace_bytes = " + std::to_string(ws_bytes) + " is below the " +
+                                   std::to_string(need) + " bytes this call needs");
+  const Span w{"workspace", ws, ws_bytes};
+  for (const Span& o : others)
+    if (overlap(w, o)) return fail(SSD_ERR_ALIAS, std::string("workspace overlaps ") + o.name);
+  return SSD_OK;
+}
+
+int ws_query(size_t* out, size_t bytes) {
+  if (!out) return fail(SSD_ERR_NULL, "bytes is NULL");
+  *out = bytes;
+  return ok();
+}
+
+// Shape limits shared by each scan and its workspace query.
+int scan1_shape(int64_t B, int64_t L, int64_t D) {
+  if (B < 0 || L < 0 || D < 0) return fail(SSD_ERR_SHAPE, "negative size");
+  if (too_big({B, L, D}) || D >= (int64_t)1 << 22 || B * ((L + 63) / 64) * ((D + 63) / 64) >= (int64_t)1 << 31)
+    return fail(SSD_ERR_SHAPE, "problem too large");
+  return SSD_OK;
+}
+
 int hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(SSD_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
   return ok();
@@ -154,22 +151,47 @@ const char* ssd_status_str(int status) {
     case SSD_ERR_VALUE: return "scalar argument out of range";
     case SSD_ERR_ALIAS: return "output overlaps another buffer";
     case SSD_ERR_HIP: return "HIP runtime error";
+    case SSD_ERR_TIMEOUT: return "a bounded wait between workgroups expired";
     default: return "unknown status";
   }
 }
 
 const char* ssd_last_error(void) { return g_last_error.c_str(); }
 
-int ssd_version(void) { return 200; }
+int ssd_version(void) { return 300; }
+
+int ssd_workspace_check(const void* workspace, void* stream) {
+  if (!workspace) return fail(SSD_ERR_NULL, "workspace is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* word = static_cast<char*>(const_cast<void*>(workspace)) + ssd::workspace_error_offset();
+  unsigned int err = 0;
+  if (hipMemcpyAsync(&err, word, sizeof(err), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return fail(SSD_ERR_HIP, "reading the workspace's wait record failed");
+  if (err == 0) return ok();
+  static const unsigned int kZero = 0;
+  if (hipMemcpyAsync(word, &kZero, sizeof(kZero), hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return fail(SSD_ERR_HIP, "clearing the workspace's wait record failed");
+  return fail(SSD_ERR_TIMEOUT, "a bounded wait between workgroups expired; the outputs that depend on it are NaN");
+}
+
+void ssd_testing_lookback(unsigned int spin_limit, int never_ready) {
+  g_spin_limit.store(spin_limit, std::memory_order_relaxed);
+  g_never_ready.store(never_ready ? 1 : 0, std::memory_order_relaxed);
+}
 
 // ============================================================================ RG-LRU
+int ssd_rglru_scan_workspace_bytes(int64_t B, int64_t L, int64_t D, size_t* bytes) {
+  SSD_TRY(scan1_shape(B, L, D));
+  return ws_query(bytes, B * L * D > 0 ? ssd::scan1_scratch_bytes(B, L, D) : 0);
+}
+
 int ssd_rglru_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype, const void* x, const void* r_logit,
                    const void* i_logit, const float* a_log, float c, const float* h0, const void* gate, void* y,
-                   float* h_last, float* chunk_states, void* stream) {
+                   float* h_last, float* chunk_states, void* workspace, size_t workspace_bytes, void* stream) {
   SSD_TRY(check_dtypes(in_dtype, out_dtype));
-  if (B < 0 || L < 0 || D < 0) return fail(SSD_ERR_SHAPE, "negative size");
-  if (too_big({B, L, D}) || D >= (int64_t)1 << 22 || B * ((L + 63) / 64) * ((D + 63) / 64) >= (int64_t)1 << 31)
-    return fail(SSD_ERR_SHAPE, "problem too large");
+  SSD_TRY(scan1_shape(B, L, D));
   if (!std::isfinite(c)) return fail(SSD_ERR_VALUE, "c must be finite");
   const int64_t nact = B * L * D;
   if (nact > 0 && (!x || !r_logit || !i_logit || !y)) return fail(SSD_ERR_NULL, "x, r_logit, i_logit and y are required");
@@ -186,9 +208,9 @@ int ssd_rglru_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype,
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (B * D == 0) return ok();
   if (L == 0) return hip_status(ssd::launch_copy_or_zero(h_last, h0, B * D, s), "rglru_scan");
+  SSD_TRY(check_workspace(workspace, workspace_bytes, ssd::scan1_scratch_bytes(B, L, D), all));
   ssd::RglruScanArgs a{B, L, D, in_dtype == SSD_BF16, out_dtype == SSD_BF16, x, r_logit, i_logit, a_log, c, h0, gate,
-                       y, h_last, chunk_states, nullptr};
-  SSD_TRY(get_scratch(stream, kScratchScan1, ssd::scan1_scratch_bytes(B, L, D), &a.scratch));
+                       y, h_last, chunk_states, workspace, wait_cfg()};
   return hip_status(ssd::launch_rglru_scan(a, s), "rglru_scan launch");
 }
 
@@ -215,15 +237,18 @@ int ssd_rglru_update(int64_t B, int64_t D, int in_dtype, int out_dtype, const vo
   return hip_status(ssd::launch_rglru_update(a, static_cast<hipStream_t>(stream)), "rglru_update launch");
 }
 
+int ssd_rglru_scan_backward_workspace_bytes(int64_t B, int64_t L, int64_t D, size_t* bytes) {
+  SSD_TRY(scan1_shape(B, L, D));
+  return ws_query(bytes, B * L * D > 0 ? ssd::rglru_bwd_scratch_bytes(B, L, D) : 0);
+}
+
 int ssd_rglru_scan_backward(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype, const void* x,
                             const void* r_logit, const void* i_logit, const float* a_log, float c, const float* h0,
                             const void* gate, const float* chunk_states, const void* dy, const float* dh_last,
-                            void* dx, void* dr_logit,
-                            void* di_logit, float* da_log, float* dh0, void* dgate, void* stream) {
+                            void* dx, void* dr_logit, void* di_logit, float* da_log, float* dh0, void* dgate,
+                            void* workspace, size_t workspace_bytes, void* stream) {
   SSD_TRY(check_dtypes(in_dtype, out_dtype));
-  if (B < 0 || L < 0 || D < 0) return fail(SSD_ERR_SHAPE, "negative size");
-  if (too_big({B, L, D}) || D >= (int64_t)1 << 22 || B * ((L + 63) / 64) * ((D + 63) / 64) >= (int64_t)1 << 31)
-    return fail(SSD_ERR_SHAPE, "problem too large");
+  SSD_TRY(scan1_shape(B, L, D));
   if (!std::isfinite(c)) return fail(SSD_ERR_VALUE, "c must be finite");
   const int64_t nact = B * L * D;
   if (nact > 0 && (!x || !r_logit || !i_logit || !dy || !dx || !dr_logit || !di_logit))
@@ -247,19 +272,24 @@ int ssd_rglru_scan_backward(int64_t B, int64_t L, int64_t D, int in_dtype, int o
     SSD_TRY(hip_status(ssd::launch_copy_or_zero(da_log, nullptr, D, s), "rglru_scan_backward"));
     return hip_status(ssd::launch_copy_or_zero(dh0, dh_last, B * D, s), "rglru_scan_backward");
   }
+  SSD_TRY(check_workspace(workspace, workspace_bytes, ssd::rglru_bwd_scratch_bytes(B, L, D), all));
   ssd::RglruBwdArgs a{B, L, D, in_dtype == SSD_BF16, out_dtype == SSD_BF16, x, r_logit, i_logit, a_log, c, h0, gate,
-                      chunk_states, dy, dh_last, dx, dr_logit, di_logit, gate ? dgate : nullptr, da_log, dh0, nullptr};
-  SSD_TRY(get_scratch(stream, kScratchScan1Bwd, ssd::rglru_bwd_scratch_bytes(B, L, D), &a.scratch));
+                      chunk_states, dy, dh_last, dx, dr_logit, di_logit, gate ? dgate : nullptr, da_log, dh0,
+                      workspace, wait_cfg()};
   return hip_status(ssd::launch_rglru_scan_backward(a, s), "rglru_scan_backward launch");
 }
 
 // ============================================================================ MinMax
+int ssd_minmax_scan_workspace_bytes(int64_t B, int64_t L, int64_t D, size_t* bytes) {
+  SSD_TRY(scan1_shape(B, L, D));
+  return ws_query(bytes, B * L * D > 0 ? ssd::scan1_scratch_bytes(B, L, D) : 0);
+}
+
 int ssd_minmax_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype, const void* r, const void* s_in,
-                    const float* x0, const void* gate, void* y, float* x_last, float* chunk_states, void* stream) {
+                    const float* x0, const void* gate, void* y, float* x_last, float* chunk_states, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   SSD_TRY(check_dtypes(in_dtype, out_dtype));
-  if (B < 0 || L < 0 || D < 0) return fail(SSD_ERR_SHAPE, "negative size");
-  if (too_big({B, L, D}) || D >= (int64_t)1 << 22 || B * ((L + 63) / 64) * ((D + 63) / 64) >= (int64_t)1 << 31)
-    return fail(SSD_ERR_SHAPE, "problem too large");
+  SSD_TRY(scan1_shape(B, L, D));
   const int64_t nact = B * L * D;
   if (nact > 0 && (!r || !s_in || !y)) return fail(SSD_ERR_NULL, "r, s and y are required");
   const size_t ab = (size_t)nact * esize(in_dtype), yb = (size_t)nact * esize(out_dtype);
@@ -273,9 +303,9 @@ int ssd_minmax_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (B * D == 0) return ok();
   if (L == 0) return hip_status(ssd::launch_copy_or_zero(x_last, x0, B * D, st), "minmax_scan");
+  SSD_TRY(check_workspace(workspace, workspace_bytes, ssd::scan1_scratch_bytes(B, L, D), all));
   ssd::MinmaxScanArgs a{B, L, D, in_dtype == SSD_BF16, out_dtype == SSD_BF16, r, s_in, x0, gate, y, x_last,
-                        chunk_states, nullptr};
-  SSD_TRY(get_scratch(stream, kScratchScan1, ssd::scan1_scratch_bytes(B, L, D), &a.scratch));
+                        chunk_states, workspace, wait_cfg()};
   return hip_status(ssd::launch_minmax_scan(a, st), "minmax_scan launch");
 }
 
@@ -298,14 +328,17 @@ int ssd_minmax_update(int64_t B, int64_t D, int in_dtype, int out_dtype, const v
   return hip_status(ssd::launch_minmax_update(a, static_cast<hipStream_t>(stream)), "minmax_update launch");
 }
 
+int ssd_minmax_scan_backward_workspace_bytes(int64_t B, int64_t L, int64_t D, size_t* bytes) {
+  SSD_TRY(scan1_shape(B, L, D));
+  return ws_query(bytes, B * L * D > 0 ? ssd::minmax_bwd_scratch_bytes(B, L, D) : 0);
+}
+
 int ssd_minmax_scan_backward(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype, const void* r,
                              const void* s_in, const float* x0, const void* gate, const float* chunk_states,
                              const void* dy, const float* dx_last, void* dr, void* ds, float* dx0, void* dgate,
-                             void* stream) {
+                             void* workspace, size_t workspace_bytes, void* stream) {
   SSD_TRY(check_dtypes(in_dtype, out_dtype));
-  if (B < 0 || L < 0 || D < 0) return fail(SSD_ERR_SHAPE, "negative size");
-  if (too_big({B, L, D}) || D >= (int64_t)1 << 22 || B * ((L + 63) / 64) * ((D + 63) / 64) >= (int64_t)1 << 31)
-    return fail(SSD_ERR_SHAPE, "problem too large");
+  SSD_TRY(scan1_shape(B, L, D));
   const int64_t nact = B * L * D;
   if (nact > 0 && (!r || !s_in || !dy || !dr || !ds)) return fail(SSD_ERR_NULL, "r, s, dy, dr and ds are required");
   const size_t ab = (size_t)nact * esize(in_dtype), ob = (size_t)nact * esize(out_dtype);
@@ -321,10 +354,9 @@ int ssd_minmax_scan_backward(int64_t B, int64_t L, int64_t D, int in_dtype, int 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (B * D == 0) return ok();
   if (L == 0) return hip_status(ssd::launch_copy_or_zero(dx0, dx_last, B * D, st), "minmax_scan_backward");
+  SSD_TRY(check_workspace(workspace, workspace_bytes, ssd::minmax_bwd_scratch_bytes(B, L, D), all));
   ssd::MinmaxBwdArgs a{B, L, D, in_dtype == SSD_BF16, out_dtype == SSD_BF16, r, s_in, x0, gate, chunk_states, dy,
-                       dx_last,
-                       dr, ds, gate ? dgate : nullptr, dx0, nullptr};
-  SSD_TRY(get_scratch(stream, kScratchScan1Bwd, ssd::minmax_bwd_scratch_bytes(B, L, D), &a.scratch));
+                       dx_last, dr, ds, gate ? dgate : nullptr, dx0, workspace, wait_cfg()};
   return hip_status(ssd::launch_minmax_scan_backward(a, st), "minmax_scan_backward launch");
 }
 
@@ -379,23 +411,60 @@ int ssd_causal_conv1d_update(int64_t B, int64_t D, int64_t W, int in_dtype, int 
 // ============================================================================ selective
 static bool supported_n(int64_t N) { return N == 1 || N == 2 || N == 4 || N == 8 || N == 16; }
 
+// Shape limits shared by the selective scans and their workspace queries; *nseq becomes B unless packed.
+static int selective_shape(int64_t B, int64_t L, int64_t D, int64_t N, bool packed, int64_t* nseq, bool bwd) {
+  if (B < 0 || L < 0 || D < 0 || N < 0) return fail(SSD_ERR_SHAPE, "negative size");
+  if (!supported_n(N)) return fail(SSD_ERR_SHAPE, "N must be 1, 2, 4, 8 or 16");
+  if (packed) {
+    if (B != 1) return fail(SSD_ERR_SHAPE, "cu_seqlens requires B == 1");
+    if (*nseq < 0) return fail(SSD_ERR_SHAPE, "nseq must be >= 0");
+    if (*nseq == 0 && L != 0) return fail(SSD_ERR_SHAPE, "nseq == 0 requires L == 0");
+    if (L >= (int64_t)1 << 31 || *nseq >= (int64_t)1 << 30) return fail(SSD_ERR_SHAPE, "packed length too large");
+  } else {
+    *nseq = B;
+  }
+  if (too_big({B, L, D}) || too_big({*nseq, D, N}) || (D + 255) / 256 > 65535 ||
+      (bwd && B * ((L + 15) / 16) + *nseq >= (int64_t)1 << 31))
+    return fail(SSD_ERR_SHAPE, "problem too large");
+  return SSD_OK;
+}
+
+// Workspace of a selective scan with these sizes (0 when the call launches no scan).  The packed plan
+// reads only whether a cu_seqlens table is given, never the table itself.
+static size_t selective_ws(int64_t B, int64_t L, int64_t D, int64_t N, bool packed, int64_t nseq) {
+  if (D * N == 0 || nseq == 0 || L == 0) return 0;
+  ssd::SelectiveScanArgs a{};
+  a.B = B; a.L = L; a.D = D; a.N = N; a.nseq = nseq;
+  a.cu_seqlens = packed ? reinterpret_cast<const int32_t*>(&a) : nullptr;
+  return ssd::selective_scan_scratch_bytes(a);
+}
+static size_t selective_bwd_ws(int64_t B, int64_t L, int64_t D, int64_t N, bool packed, int64_t nseq) {
+  if (D * N == 0 || nseq == 0 || L == 0) return 0;
+  ssd::SelectiveBwdArgs a{};
+  a.B = B; a.L = L; a.D = D; a.N = N; a.nseq = nseq;
+  a.cu_seqlens = packed ? reinterpret_cast<const int32_t*>(&a) : nullptr;
+  return ssd::selective_scan_backward_scratch_bytes(a);
+}
+
+extern "C" int ssd_selective_scan_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int64_t nseq, int packed,
+                                                  size_t* bytes) {
+  SSD_TRY(selective_shape(B, L, D, N, packed != 0, &nseq, false));
+  return ws_query(bytes, selective_ws(B, L, D, N, packed != 0, nseq));
+}
+
+extern "C" int ssd_selective_scan_backward_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int64_t nseq,
+                                                           int packed, size_t* bytes) {
+  SSD_TRY(selective_shape(B, L, D, N, packed != 0, &nseq, true));
+  return ws_query(bytes, selective_bwd_ws(B, L, D, N, packed != 0, nseq));
+}
+
 int ssd_selective_scan(int64_t B, int64_t L, int64_t D, int64_t N, int in_dtype, int out_dtype, const void* x,
                        const void* dt, const float* A, const void* Bm, const void* Cm, const float* Dskip,
                        const void* z, const float* dt_bias, int dt_softplus, const int32_t* cu_seqlens, int64_t nseq,
-                       const float* h0, void* y, float* h_last, void* stream) {
+                       const float* h0, void* y, float* h_last, void* workspace, size_t workspace_bytes,
+                       void* stream) {
   SSD_TRY(check_dtypes(in_dtype, out_dtype));
-  if (B < 0 || L < 0 || D < 0 || N < 0) return fail(SSD_ERR_SHAPE, "negative size");
-  if (!supported_n(N)) return fail(SSD_ERR_SHAPE, "N must be 1, 2, 4, 8 or 16");
-  if (cu_seqlens) {
-    if (B != 1) return fail(SSD_ERR_SHAPE, "cu_seqlens requires B == 1");
-    if (nseq < 0) return fail(SSD_ERR_SHAPE, "nseq must be >= 0");
-    if (nseq == 0 && L != 0) return fail(SSD_ERR_SHAPE, "nseq == 0 requires L == 0");
-    if (L >= (int64_t)1 << 31 || nseq >= (int64_t)1 << 30) return fail(SSD_ERR_SHAPE, "packed length too large");
-  } else {
-    nseq = B;
-  }
-  if (too_big({B, L, D}) || too_big({nseq, D, N}) || (D + 255) / 256 > 65535)
-    return fail(SSD_ERR_SHAPE, "problem too large");
+  SSD_TRY(selective_shape(B, L, D, N, cu_seqlens != nullptr, &nseq, false));
   const int64_t nact = B * L * D;
   if (nact > 0 && (!x || !dt || !y)) return fail(SSD_ERR_NULL, "x, dt and y are required");
   if (B * L * N > 0 && (!Bm || !Cm)) return fail(SSD_ERR_NULL, "Bm and Cm are required");
@@ -414,9 +483,9 @@ int ssd_selective_scan(int64_t B, int64_t L, int64_t D, int64_t N, int in_dtype,
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (D * N == 0 || nseq == 0) return ok();
   if (L == 0) return hip_status(ssd::launch_copy_or_zero(h_last, h0, nseq * D * N, s), "selective_scan");
+  SSD_TRY(check_workspace(workspace, workspace_bytes, selective_ws(B, L, D, N, cu_seqlens != nullptr, nseq), all));
   ssd::SelectiveScanArgs a{B, L, D, N, in_dtype == SSD_BF16, out_dtype == SSD_BF16, x, dt, A, Bm, Cm, Dskip, z,
-                           dt_bias, dt_softplus ? 1 : 0, cu_seqlens, nseq, h0, y, h_last, nullptr};
-  SSD_TRY(get_scratch(stream, kScratchSelective, ssd::selective_scan_scratch_bytes(a), &a.scratch));
+                           dt_bias, dt_softplus ? 1 : 0, cu_seqlens, nseq, h0, y, h_last, workspace};
   return hip_status(ssd::launch_selective_scan(a, s), "selective_scan launch");
 }
 
@@ -426,21 +495,9 @@ int ssd_selective_scan_backward(int64_t B, int64_t L, int64_t D, int64_t N, int 
                                 const int32_t* cu_seqlens, int64_t nseq, const float* h0, const void* dy,
                                 const float* dh_last, void* dx, void* ddt, float* dA,
                                 void* dBm, void* dCm, float* dDskip, void* dz, float* ddt_bias, float* dh0,
-                                void* stream) {
+                                void* workspace, size_t workspace_bytes, void* stream) {
   SSD_TRY(check_dtypes(in_dtype, out_dtype));
-  if (B < 0 || L < 0 || D < 0 || N < 0) return fail(SSD_ERR_SHAPE, "negative size");
-  if (!supported_n(N)) return fail(SSD_ERR_SHAPE, "N must be 1, 2, 4, 8 or 16");
-  if (cu_seqlens) {
-    if (B != 1) return fail(SSD_ERR_SHAPE, "cu_seqlens requires B == 1");
-    if (nseq < 0) return fail(SSD_ERR_SHAPE, "nseq must be >= 0");
-    if (nseq == 0 && L != 0) return fail(SSD_ERR_SHAPE, "nseq == 0 requires L == 0");
-    if (L >= (int64_t)1 << 31 || nseq >= (int64_t)1 << 30) return fail(SSD_ERR_SHAPE, "packed length too large");
-  } else {
-    nseq = B;
-  }
-  if (too_big({B, L, D}) || too_big({nseq, D, N}) || (D + 255) / 256 > 65535 ||
-      B * ((L + 15) / 16) + nseq >= (int64_t)1 << 31)
-    return fail(SSD_ERR_SHAPE, "problem too large");
+  SSD_TRY(selective_shape(B, L, D, N, cu_seqlens != nullptr, &nseq, true));
   const int64_t nact = B * L * D;
   if (nact > 0 && (!x || !dt || !dy || !dx || !ddt)) return fail(SSD_ERR_NULL, "x, dt, dy, dx and ddt are required");
   if (B * L * N > 0 && (!Bm || !Cm || !dBm || !dCm)) return fail(SSD_ERR_NULL, "Bm, Cm, dBm and dCm are required");
@@ -469,10 +526,10 @@ int ssd_selective_scan_backward(int64_t B, int64_t L, int64_t D, int64_t N, int 
     SSD_TRY(hip_status(ssd::launch_copy_or_zero(ddt_bias, nullptr, D, s), "selective_scan_backward"));
     return hip_status(ssd::launch_copy_or_zero(dh0, dh_last, nseq * D * N, s), "selective_scan_backward");
   }
+  SSD_TRY(check_workspace(workspace, workspace_bytes, selective_bwd_ws(B, L, D, N, cu_seqlens != nullptr, nseq), all));
   ssd::SelectiveBwdArgs a{B, L, D, N, in_dtype == SSD_BF16, out_dtype == SSD_BF16, x, dt, A, Bm, Cm, Dskip, z,
                           dt_bias, dt_softplus ? 1 : 0, cu_seqlens, nseq, h0, dy, dh_last, dx, ddt, dA, dBm, dCm, dDskip,
-                          z ? dz : nullptr, ddt_bias, dh0, nullptr};
-  SSD_TRY(get_scratch(stream, kScratchSelectiveBwd, ssd::selective_scan_backward_scratch_bytes(a), &a.scratch));
+                          z ? dz : nullptr, ddt_bias, dh0, workspace};
   return hip_status(ssd::launch_selective_scan_backward(a, s), "selective_scan_backward launch");
 }
 
@@ -605,15 +662,35 @@ int ssd_readout_norm(int64_t rows, int64_t width, int in_dtype, int out_dtype, c
   return hip_status(ssd::launch_readout_norm(a, static_cast<hipStream_t>(stream)), "readout_norm launch");
 }
 
-int ssd_hgrn2_scan_backward(int64_t B, int64_t L, int64_t H, int64_t d, int in_dtype, int out_dtype, const void* q,
-                            const void* k, const void* v, const void* g_logit, float lower_bound, const float* S0,
-                            const float* o, const void* dO, const float* dS_last, void* dq, void* dk, void* dv,
-                            void* dg_logit, float* dS0, void* stream) {
-  SSD_TRY(check_dtypes(in_dtype, out_dtype));
+static int hgrn2_bwd_shape(int64_t B, int64_t L, int64_t H, int64_t d) {
   if (B < 0 || L < 0 || H < 0 || d < 0) return fail(SSD_ERR_SHAPE, "negative size");
   if (!supported_d(d)) return fail(SSD_ERR_SHAPE, "head dim d must be 16, 32, 64 or 128");
   if (too_big({B, L, H, d}) || B * H >= (int64_t)1 << 30 || H * d >= (int64_t)1 << 24)
     return fail(SSD_ERR_SHAPE, "problem too large");
+  return SSD_OK;
+}
+
+static size_t hgrn2_bwd_ws(int64_t B, int64_t L, int64_t H, int64_t d, int in_dtype, bool have_o) {
+  if (B * H == 0 || L == 0) return 0;
+  ssd::Hgrn2BwdArgs a{};
+  a.B = B; a.L = L; a.H = H; a.d = d; a.in_bf16 = in_dtype == SSD_BF16;
+  a.o = have_o ? reinterpret_cast<const float*>(&a) : nullptr;  // only whether it is given matters
+  return ssd::hgrn2_scan_backward_scratch_bytes(a);
+}
+
+int ssd_hgrn2_scan_backward_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t d, int in_dtype, int have_o,
+                                            size_t* bytes) {
+  if (in_dtype != SSD_F32 && in_dtype != SSD_BF16) return fail(SSD_ERR_DTYPE, "in_dtype must be SSD_F32 or SSD_BF16");
+  SSD_TRY(hgrn2_bwd_shape(B, L, H, d));
+  return ws_query(bytes, hgrn2_bwd_ws(B, L, H, d, in_dtype, have_o != 0));
+}
+
+int ssd_hgrn2_scan_backward(int64_t B, int64_t L, int64_t H, int64_t d, int in_dtype, int out_dtype, const void* q,
+                            const void* k, const void* v, const void* g_logit, float lower_bound, const float* S0,
+                            const float* o, const void* dO, const float* dS_last, void* dq, void* dk, void* dv,
+                            void* dg_logit, float* dS0, void* workspace, size_t workspace_bytes, void* stream) {
+  SSD_TRY(check_dtypes(in_dtype, out_dtype));
+  SSD_TRY(hgrn2_bwd_shape(B, L, H, d));
   if (!(lower_bound >= 0.0f && lower_bound <= 1.0f)) return fail(SSD_ERR_VALUE, "lower_bound must be in [0, 1]");
   const int64_t nact = B * L * H * d;
   if (nact > 0 && (!q || !k || !v || !g_logit || !dO))
@@ -634,9 +711,9 @@ int ssd_hgrn2_scan_backward(int64_t B, int64_t L, int64_t H, int64_t d, int in_d
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (B * H == 0) return ok();
   if (L == 0) return hip_status(ssd::launch_copy_or_zero(dS0, dS_last, B * H * d * d, s), "hgrn2_scan_backward");
+  SSD_TRY(check_workspace(workspace, workspace_bytes, hgrn2_bwd_ws(B, L, H, d, in_dtype, o != nullptr), all));
   ssd::Hgrn2BwdArgs a{B,  L,  H,  d,  in_dtype == SSD_BF16, out_dtype == SSD_BF16, q, k, v, g_logit, lower_bound,
-                      S0, o,  dO, dS_last, dq, dk, dv, dg_logit, dS0, nullptr};
-  SSD_TRY(get_scratch(stream, kScratchHgrn2Bwd, ssd::hgrn2_scan_backward_scratch_bytes(a), &a.scratch));
+                      S0, o,  dO, dS_last, dq, dk, dv, dg_logit, dS0, workspace};
   return hip_status(ssd::launch_hgrn2_scan_backward(a, s), "hgrn2_scan_backward launch");
 }
 

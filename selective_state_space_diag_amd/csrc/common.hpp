@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.hpp"  // WaitCfg
+
 namespace ssd {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -245,10 +247,8 @@ struct LookbackCtl {
   alignas(128) unsigned long long tick;
   unsigned int done;      // workgroups finished (single-counter kernels)
   unsigned int done_all;  // home classes whose workgroups have all finished
-  unsigned int error;     // set if a bounded wait ever expired (must never happen)
+  unsigned int error;     // set when a bounded wait expires (read and cleared by the host)
 };
 constexpr int64_t kCtlBytes = (int64_t)((sizeof(LookbackCtl) + 255) / 256 * 256);
-
-constexpr unsigned int kSpinLimit = 1u << 20;  // each spin is a memory round trip: ~1-2 s bound
 
 }  // namespace ssd

@@ -593,7 +593,7 @@ struct BwdLayout {
 
 size_t hgrn2_scan_backward_scratch_bytes(const Hgrn2BwdArgs& a) {
   const BwdLayout lay(a);
-  return lay.state + lay.ckpt + lay.outs;
+  return workspace_head_bytes() + lay.state + lay.ckpt + lay.outs;
 }
 
 hipError_t launch_hgrn2_row_sweep(const Hgrn2ScanArgs& a, hipStream_t s) {
@@ -625,7 +625,7 @@ hipError_t launch_hgrn2_key_scan(const Hgrn2ScanArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_hgrn2_scan_backward(const Hgrn2BwdArgs& a, hipStream_t s) {
-  char* scratch = static_cast<char*>(a.scratch);
+  char* scratch = static_cast<char*>(a.scratch) + workspace_head_bytes();
   const BwdLayout lay(a);
   float* S_L = reinterpret_cast<float*>(scratch);
   float* ckpt = lay.ckpt ? reinterpret_cast<float*>(scratch + lay.state) : nullptr;

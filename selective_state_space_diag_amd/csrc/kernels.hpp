@@ -7,6 +7,23 @@
 
 namespace ssd {
 
+// ------------------------------------------------------------------ workspaces and bounded waits
+// Every workspace starts with a lookback control block (work tickets, the launch counter, and the
+// word in which a launch records a bounded wait that expired); the rest is the family's own layout.
+size_t workspace_head_bytes();
+size_t workspace_error_offset();  // byte offset of the expired-wait word within the head
+
+// How the bounded waits of one launch behave: the polls before a wait gives up (each poll is a
+// memory round trip, so the default bounds a wait at about a second), and an offset added to the
+// epoch a waiting workgroup accepts (always 0, except from the timeout test hook, which makes every
+// wait target words no launch writes).  A wait that gives up records it in the control block and
+// hands on NaN as the carry, so every output that depends on it reads NaN.
+constexpr unsigned int kSpinLimit = 1u << 20;
+struct WaitCfg {
+  unsigned int spin_limit = kSpinLimit;
+  unsigned int skew = 0;
+};
+
 // ------------------------------------------------------------------ state-size-1 scans
 // (RG-LRU and MinMax share one kernel template and its lookback scratch layout)
 // Lookback scratch (control block + words) of a state-size-1 scan.
@@ -24,6 +41,7 @@ struct RglruScanArgs {
   float* h_last;
   float* chunk_states;  // [B][ceil(L/64)][D] state entering each 64-step chunk, or NULL
   void* scratch;        // scan1_scratch_bytes
+  WaitCfg wait;
 };
 hipError_t launch_rglru_scan(const RglruScanArgs& a, hipStream_t s);
 
@@ -56,6 +74,7 @@ struct RglruBwdArgs {
   float* da_log;          // [D]
   float* dh0;             // [B][D] or NULL
   void* scratch;          // rglru_bwd_scratch_bytes
+  WaitCfg wait;
 };
 size_t rglru_bwd_scratch_bytes(int64_t B, int64_t L, int64_t D);
 hipError_t launch_rglru_scan_backward(const RglruBwdArgs& a, hipStream_t s);
@@ -70,6 +89,7 @@ struct MinmaxScanArgs {
   float* x_last;
   float* chunk_states;  // as RglruScanArgs
   void* scratch;        // scan1_scratch_bytes
+  WaitCfg wait;
 };
 hipError_t launch_minmax_scan(const MinmaxScanArgs& a, hipStream_t s);
 
@@ -85,6 +105,7 @@ struct MinmaxBwdArgs {
   void *dr, *ds, *dgate;  // out dtype; dgate may be NULL
   float* dx0;             // [B][D] or NULL
   void* scratch;          // minmax_bwd_scratch_bytes
+  WaitCfg wait;
 };
 size_t minmax_bwd_scratch_bytes(int64_t B, int64_t L, int64_t D);
 hipError_t launch_minmax_scan_backward(const MinmaxBwdArgs& a, hipStream_t s);

@@ -57,6 +57,7 @@ struct Scan1Params {
   float* carry_out;    // [B][n_chunks][D]: state entering each chunk (record passes)
   LookbackCtl* ctl;
   unsigned long long* words;  // [unit][3][tile width]: aggregate a, aggregate b, inclusive h
+  WaitCfg wait;
 };
 
 // ------------------------------------------------------------------ RG-LRU step
@@ -302,11 +303,12 @@ __device__ __forceinline__ void fetch_gate(const Scan1Params& p, const Unit& u, 
 // the inclusive state.
 template <class Op, int TW>
 __device__ __forceinline__ float lookback_carry(LookbackCtl* ctl, unsigned long long* words, int64_t seq_unit,
-                                                int64_t cix, int64_t n_chunks, int j, uint32_t E, float Ac, float Bc,
-                                                float init, float* incl) {
+                                                int64_t cix, int64_t n_chunks, int j, uint32_t E, const WaitCfg& wc,
+                                                float Ac, float Bc, float init, float* incl) {
   unsigned long long* W = words + (seq_unit + cix) * 3 * TW;
   const int64_t base = (cix / kBlock) * kBlock;
   const int nprev = (int)(cix - base);  // aggregates of block-mates before cix
+  const uint32_t Ew = E + wc.skew;      // the epoch accepted while waiting (E unless testing timeouts)
   if (cix + 1 < base + kBlock && cix + 1 < n_chunks) {
     word_store(&W[0 * TW + j], E, Ac);
     word_store(&W[1 * TW + j], E, Bc);
@@ -314,7 +316,7 @@ __device__ __forceinline__ float lookback_carry(LookbackCtl* ctl, unsigned long 
   // words: [0] inclusive of chunk base-1 (if base > 0), then (a, b) of chunks base .. cix-1
   unsigned long long wd[1 + 2 * (kBlock - 1)];
   const unsigned long long* Wb = words + (seq_unit + base - 1) * 3 * TW;
-  wd[0] = base > 0 ? word_load(&Wb[2 * TW + j]) : ((unsigned long long)E << 32);
+  wd[0] = base > 0 ? word_load(&Wb[2 * TW + j]) : ((unsigned long long)Ew << 32);
 #pragma unroll
   for (int q = 0; q < kBlock - 1; ++q) {
     const unsigned long long* Wq = words + (seq_unit + base + q) * 3 * TW;
@@ -322,30 +324,34 @@ __device__ __forceinline__ float lookback_carry(LookbackCtl* ctl, unsigned long 
       wd[1 + 2 * q] = word_load(&Wq[0 * TW + j]);
       wd[2 + 2 * q] = word_load(&Wq[1 * TW + j]);
     } else {
-      wd[1 + 2 * q] = wd[2 + 2 * q] = (unsigned long long)E << 32;
+      wd[1 + 2 * q] = wd[2 + 2 * q] = (unsigned long long)Ew << 32;
     }
   }
   unsigned int spins = 0;
+  bool all;
   while (true) {
-    bool all = word_ready(wd[0], E);
+    all = word_ready(wd[0], Ew);
 #pragma unroll
-    for (int q = 0; q < 2 * (kBlock - 1); ++q) all = all && word_ready(wd[1 + q], E);
-    if (all || spins >= kSpinLimit) break;
+    for (int q = 0; q < 2 * (kBlock - 1); ++q) all = all && word_ready(wd[1 + q], Ew);
+    if (all || spins >= wc.spin_limit) break;
     ++spins;
     __builtin_amdgcn_s_sleep(1);
-    if (!word_ready(wd[0], E)) wd[0] = word_load(&Wb[2 * TW + j]);
+    if (!word_ready(wd[0], Ew)) wd[0] = word_load(&Wb[2 * TW + j]);
 #pragma unroll
     for (int q = 0; q < kBlock - 1; ++q) {
       const unsigned long long* Wq = words + (seq_unit + base + q) * 3 * TW;
-      if (!word_ready(wd[1 + 2 * q], E)) wd[1 + 2 * q] = word_load(&Wq[0 * TW + j]);
-      if (!word_ready(wd[2 + 2 * q], E)) wd[2 + 2 * q] = word_load(&Wq[1 * TW + j]);
+      if (!word_ready(wd[1 + 2 * q], Ew)) wd[1 + 2 * q] = word_load(&Wq[0 * TW + j]);
+      if (!word_ready(wd[2 + 2 * q], Ew)) wd[2 + 2 * q] = word_load(&Wq[1 * TW + j]);
     }
   }
-  if (spins >= kSpinLimit) atomicOr(&ctl->error, 1u);
   float hin = base > 0 ? word_value(wd[0]) : init;
 #pragma unroll
   for (int q = 0; q < kBlock - 1; ++q)
     if (q < nprev) hin = Op::apply(word_value(wd[1 + 2 * q]), word_value(wd[2 + 2 * q]), hin);
+  if (!all) {  // the wait gave up: record it, and hand on NaN rather than a carry built from stale words
+    atomicOr(&ctl->error, 1u);
+    hin = __builtin_nanf("");
+  }
   *incl = Op::apply(Ac, Bc, hin);
   if (cix == base + kBlock - 1 && cix + 1 < n_chunks) word_store(&W[2 * TW + j], E, *incl);
   return hin;
@@ -479,7 +485,7 @@ void scan1_kernel(Scan1Params p) {
       }
       const float init = p.h0 ? p.h0[u.b * p.D + (j_ok ? ch : p.D - 1)] : 0.0f;
       float incl;
-      const float hin = lookback_carry<Op, TW>(p.ctl, p.words, seq_unit, u.c, p.n_chunks, j, E, Ac, Bc, init, &incl);
+      const float hin = lookback_carry<Op, TW>(p.ctl, p.words, seq_unit, u.c, p.n_chunks, j, E, p.wait, Ac, Bc, init, &incl);
       if (p.h_last && j_ok && u.c == p.n_chunks - 1) p.h_last[u.b * p.D + ch] = incl;
       if ((RECORD || p.carry_out) && j_ok) p.carry_out[(u.b * p.n_chunks + u.c) * p.D + ch] = hin;
       s_carry[j] = hin;
@@ -589,6 +595,7 @@ struct Bwd1Params {
   float* dh0;            // [B][D] or NULL
   LookbackCtl* ctl;
   unsigned long long* words;
+  WaitCfg wait;
 };
 
 // gelu'(v) = Phi(v) + v phi(v), with Phi through the same erf as gelu_f.
@@ -726,7 +733,7 @@ __global__ __launch_bounds__(kBWaves * 64) void rglru_bwd_kernel(Bwd1Params p) {
       const int64_t chj = k * TW + j;
       const float init = p.dh_last ? p.dh_last[b * p.D + (chj < p.D ? chj : p.D - 1)] : 0.0f;
       float incl;
-      s_qin[j] = lookback_carry<AffineOp, TW>(p.ctl, p.words, seq_unit, cr, p.n_chunks, j, E, Ac, Bc, init, &incl);
+      s_qin[j] = lookback_carry<AffineOp, TW>(p.ctl, p.words, seq_unit, cr, p.n_chunks, j, E, p.wait, Ac, Bc, init, &incl);
     }
     __syncthreads();
 
@@ -830,6 +837,7 @@ struct MmBwdParams {
   float* dx0;            // [B][D] or NULL
   LookbackCtl* ctl;
   unsigned long long* words;
+  WaitCfg wait;
 };
 
 // d min(u, w) / du and d max(u, w) / du under the convention above.
@@ -995,7 +1003,7 @@ __global__ __launch_bounds__(kBWaves * 64) __attribute__((amdgpu_waves_per_eu(4)
       const int64_t chj = k * TW + j;
       const float init = p.dx_last ? p.dx_last[b * p.D + (chj < p.D ? chj : p.D - 1)] : 0.0f;
       float incl;
-      s_qin[j] = lookback_carry<AffineOp, TW>(p.ctl, p.words, seq_unit, cr, p.n_chunks, j, E, Ac, Bc, init, &incl);
+      s_qin[j] = lookback_carry<AffineOp, TW>(p.ctl, p.words, seq_unit, cr, p.n_chunks, j, E, p.wait, Ac, Bc, init, &incl);
     }
     __syncthreads();
 
@@ -1139,6 +1147,9 @@ hipError_t launch_update_op(const Upd1Params& p, int in_bf16, int out_bf16, hipS
 
 }  // namespace
 
+size_t workspace_head_bytes() { return (size_t)kCtlBytes; }
+size_t workspace_error_offset() { return offsetof(LookbackCtl, error); }
+
 size_t scan1_scratch_bytes(int64_t B, int64_t L, int64_t D) {
   const int V = vec_width(D);
   const int64_t TW = 64 * V;
@@ -1153,6 +1164,7 @@ hipError_t launch_rglru_scan(const RglruScanArgs& a, hipStream_t s) {
   p.in[0] = a.x; p.in[1] = a.r_logit; p.in[2] = a.i_logit;
   p.gate = a.gate;
   p.a_log = a.a_log; p.c = a.c; p.h0 = a.h0; p.y = a.y; p.h_last = a.h_last; p.carry_out = a.chunk_states;
+  p.wait = a.wait;
   return launch_scan_op<AffineOp>(p, a.in_bf16, a.out_bf16, a.scratch, s);
 }
 
@@ -1162,6 +1174,7 @@ hipError_t launch_minmax_scan(const MinmaxScanArgs& a, hipStream_t s) {
   p.in[0] = a.r; p.in[1] = a.s;
   p.gate = a.gate;
   p.h0 = a.x0; p.y = a.y; p.h_last = a.x_last; p.carry_out = a.chunk_states;
+  p.wait = a.wait;
   return launch_scan_op<MinMaxOp>(p, a.in_bf16, a.out_bf16, a.scratch, s);
 }
 
@@ -1212,6 +1225,7 @@ hipError_t launch_rglru_scan_backward(const RglruBwdArgs& a, hipStream_t s) {
     f.B = a.B; f.L = a.L; f.D = a.D;
     f.in[0] = a.x; f.in[1] = a.r_logit; f.in[2] = a.i_logit;
     f.a_log = a.a_log; f.c = a.c; f.h0 = a.h0; f.y = nullptr; f.h_last = nullptr; f.carry_out = rec;
+    f.wait = a.wait;
     e = launch_record_op<AffineOp>(f, a.in_bf16, a.scratch, s);
     if (e != hipSuccess) return e;
     carry = rec;
@@ -1226,6 +1240,7 @@ hipError_t launch_rglru_scan_backward(const RglruBwdArgs& a, hipStream_t s) {
   q.dx = a.dx; q.dr = a.dr_logit; q.di = a.di_logit; q.dgate = a.dgate; q.dalog_part = dal; q.dh0 = a.dh0;
   q.ctl = static_cast<LookbackCtl*>(a.scratch);
   q.words = reinterpret_cast<unsigned long long*>(base + kCtlBytes);
+  q.wait = a.wait;
   const int64_t units = a.B * q.n_tiles * n_chunks;
   if (V == 2) e = launch_bwd_dt<2>(q, a.gate != nullptr, a.in_bf16, a.out_bf16, units, s);
   else e = launch_bwd_dt<1>(q, a.gate != nullptr, a.in_bf16, a.out_bf16, units, s);
@@ -1273,6 +1288,7 @@ hipError_t launch_minmax_scan_backward(const MinmaxBwdArgs& a, hipStream_t s) {
     f.B = a.B; f.L = a.L; f.D = a.D;
     f.in[0] = a.r; f.in[1] = a.s;
     f.h0 = a.x0; f.y = nullptr; f.h_last = nullptr; f.carry_out = rec;
+    f.wait = a.wait;
     const hipError_t e = launch_record_op<MinMaxOp>(f, a.in_bf16, a.scratch, s);
     if (e != hipSuccess) return e;
     carry = rec;
@@ -1286,6 +1302,7 @@ hipError_t launch_minmax_scan_backward(const MinmaxBwdArgs& a, hipStream_t s) {
   q.dr = a.dr; q.ds = a.ds; q.dgate = a.dgate; q.dx0 = a.dx0;
   q.ctl = static_cast<LookbackCtl*>(a.scratch);
   q.words = reinterpret_cast<unsigned long long*>(base + kCtlBytes);
+  q.wait = a.wait;
   const int64_t units = a.B * q.n_tiles * n_chunks;
   return V == 2 ? launch_mm_bwd_dt<2>(q, a.gate != nullptr, a.in_bf16, a.out_bf16, units, s)
                 : launch_mm_bwd_dt<1>(q, a.gate != nullptr, a.in_bf16, a.out_bf16, units, s);

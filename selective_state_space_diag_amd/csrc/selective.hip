@@ -982,7 +982,7 @@ int64_t selective_segment_len(const SelectiveScanArgs& a) { return make_plan(a).
 
 size_t selective_scan_scratch_bytes(const SelectiveScanArgs& a) {
   const Plan pl = make_plan(a);
-  size_t bytes = 3 * align256((size_t)pl.U * a.N * a.D * sizeof(float));
+  size_t bytes = workspace_head_bytes() + 3 * align256((size_t)pl.U * a.N * a.D * sizeof(float));
   if (a.cu_seqlens) bytes += align256(256 + (size_t)pl.U * sizeof(int2)) + align256((size_t)a.nseq * sizeof(int2));
   return bytes;
 }
@@ -994,7 +994,7 @@ hipError_t launch_selective_scan(const SelectiveScanArgs& a, hipStream_t s) {
   p.cu = a.cu_seqlens; p.units = nullptr; p.n_units = nullptr; p.seq_units = nullptr;
   p.x = a.x; p.dt = a.dt; p.A = a.A; p.Bm = a.Bm; p.Cm = a.Cm; p.Dskip = a.Dskip; p.z = a.z;
   p.dt_bias = a.dt_bias; p.h0 = a.h0; p.y = a.y; p.h_last = a.h_last;
-  char* base = static_cast<char*>(a.scratch);
+  char* base = static_cast<char*>(a.scratch) + workspace_head_bytes();
   const size_t agg = align256((size_t)pl.U * a.N * a.D * sizeof(float));
   p.aggP = reinterpret_cast<float*>(base);
   p.aggH = reinterpret_cast<float*>(base + agg);
@@ -1066,12 +1066,12 @@ void launch_fwd_carry_t(const SelParams& f, int64_t U, bool softplus, hipStream_
 
 size_t selective_scan_backward_scratch_bytes(const SelectiveBwdArgs& a) {
   const BwdLayout l = bwd_layout(a);
-  return 5 * l.state + 2 * l.row + 2 * l.bc + l.slices + l.tbl + l.seqtbl;
+  return workspace_head_bytes() + 5 * l.state + 2 * l.row + 2 * l.bc + l.slices + l.tbl + l.seqtbl;
 }
 
 hipError_t launch_selective_scan_backward(const SelectiveBwdArgs& a, hipStream_t s) {
   const BwdLayout l = bwd_layout(a);
-  char* base = static_cast<char*>(a.scratch);
+  char* base = static_cast<char*>(a.scratch) + workspace_head_bytes();
   float* carry = reinterpret_cast<float*>(base);
   float* aggP = reinterpret_cast<float*>(base + l.state);
   float* aggQ = reinterpret_cast<float*>(base + 2 * l.state);

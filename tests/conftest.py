@@ -25,3 +25,17 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _no_expired_waits(request):
+    """After every GPU test: no launch on the test's stream had a bounded wait between workgroups expire
+    (ssd_workspace_check on every workspace the binding keeps for that stream)."""
+    yield
+    if "gpu" not in request.keywords:
+        return
+    import torch
+    if not torch.cuda.is_available():
+        return
+    import selective_state_space_diag_amd as ssd
+    ssd.workspace_check()

@@ -51,3 +51,33 @@ def host(t):
     if t.dtype == torch.bfloat16:
         return t.float().cpu().numpy().astype(np.float64)
     return t.cpu().numpy().astype(np.float64)
+
+
+def parallel_map(fn, items):
+    """fn over items on a small thread pool (the oracle's C loops release the GIL), results in order."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=max(1, min(16, os.cpu_count() or 1))) as ex:
+        return list(ex.map(fn, items))
+
+
+def spread_heads(B, H):
+    """(b, h) pairs of the full-size HGRN2 checks: every head of four batch rows of both parities, so
+    every head index, every (b, h) parity and every position of a head's workgroups modulo the 8 XCDs
+    is covered (64 heads at B = 8, H = 16)."""
+    rows = sorted({0, min(3, B - 1), min(5, B - 1), B - 1})
+    return [(b, h) for b in rows for h in range(H)]
+
+
+def spread_channels(D, n_random, seed, block=256, scale_blocks=4):
+    """Channels of the full-size selective checks: the first and last channel of every 256-channel
+    workgroup (which include the edges of every scale block) plus seeded random ones."""
+    import numpy as np
+    edges = set()
+    for c0 in range(0, D, block):
+        edges.update((c0, min(c0 + block, D) - 1))
+    for s in range(scale_blocks):
+        edges.update((s * D // scale_blocks, (s + 1) * D // scale_blocks - 1))
+    rng = np.random.default_rng(seed)
+    rest = [c for c in rng.permutation(D) if c not in edges][:n_random]
+    return np.array(sorted(edges | set(int(c) for c in rest)))

@@ -8,7 +8,7 @@ import pytest
 import oracle
 import selective_state_space_diag_amd as ssd
 from selective_state_space_diag_amd import synth
-from tests.helpers import TOL, assert_close, f64, host, to_dev
+from tests.helpers import TOL, assert_close, f64, host, parallel_map, spread_heads, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -81,37 +81,42 @@ def test_bf16_output():
     assert bool((diff <= o32.abs().clamp_min(1e-30) * 2.0 ** -7).all())
 
 
+def _full_size_heads(inp, o, S, fn=None):
+    """Every output and the final state of 64 heads (spread_heads) vs the oracle run on each head alone."""
+    B, L, H, d = inp.t["q"].shape
+    fn = fn or oracle.hgrn2_scan
+    oh, Sh = o.cpu().double().numpy(), S.cpu().double().numpy() if S is not None else None
+    pairs = spread_heads(B, H)
+
+    def run(bh):
+        b, h = bh
+        g = lambda n: synth.bf16_to_f64(inp.t[n].data[b:b + 1, :, h:h + 1])
+        return fn(g("q"), g("k"), g("v"), g("g_logit"), inp.s["lower_bound"])
+
+    for (b, h), (orf, Sr) in zip(pairs, parallel_map(run, pairs)):
+        assert_close(oh[b:b + 1, :, h:h + 1], orf, TOL[synth.BF16], f"o head {b},{h}")
+        if Sh is not None:
+            assert_close(Sh[b:b + 1, h:h + 1], Sr, TOL[synth.BF16], f"S head {b},{h}")
+    return len(pairs)
+
+
 def test_hgrn2_workload_full_size_sampled_heads():
-    """B=8, H=16, d=128, L=4096 bf16 at full size; every output of 4 sampled heads vs the oracle."""
+    """B=8, H=16, d=128, L=4096 bf16 at full size (the chunked MFMA form): every output and the final
+    state of 64 heads (four batch rows of both parities, every head index) vs the oracle."""
     import torch
     inp = synth.workload_inputs("hgrn2")
     o, S = gpu_run(inp)
     torch.cuda.synchronize()
-    B, L, H, d = inp.t["q"].shape
-    rng = np.random.default_rng(3)
-    for _ in range(4):
-        b, h = int(rng.integers(B)), int(rng.integers(H))
-        g = lambda n: synth.bf16_to_f64(inp.t[n].data[b:b + 1, :, h:h + 1])
-        orf, Sr = oracle.hgrn2_scan(g("q"), g("k"), g("v"), g("g_logit"), inp.s["lower_bound"])
-        assert_close(host(o[b:b + 1, :, h:h + 1]), orf, TOL[synth.BF16], f"o head {b},{h}")
-        assert_close(host(S[b:b + 1, h:h + 1]), Sr, TOL[synth.BF16], f"S head {b},{h}")
+    assert _full_size_heads(inp, o, S) == 64
     assert torch.isfinite(o).all()
 
 
 def test_full_size_default_lower_bound_sampled_heads():
-    """The same workload with the page's default lower bound 0 (the register-sweep path): every
-    output of 3 sampled heads and their final states vs the oracle."""
+    """The same workload with the page's default lower bound 0: 64 heads and their final states."""
     import torch
     inp = synth.workload_inputs("hgrn2")
     inp.s["lower_bound"] = 0.0
     o, S = gpu_run(inp)
     torch.cuda.synchronize()
-    B, L, H, d = inp.t["q"].shape
-    rng = np.random.default_rng(4)
-    for _ in range(3):
-        b, h = int(rng.integers(B)), int(rng.integers(H))
-        g = lambda n: synth.bf16_to_f64(inp.t[n].data[b:b + 1, :, h:h + 1])
-        orf, Sr = oracle.hgrn2_scan(g("q"), g("k"), g("v"), g("g_logit"), 0.0)
-        assert_close(host(o[b:b + 1, :, h:h + 1]), orf, TOL[synth.BF16], f"o head {b},{h}")
-        assert_close(host(S[b:b + 1, h:h + 1]), Sr, TOL[synth.BF16], f"S head {b},{h}")
+    assert _full_size_heads(inp, o, S) == 64
     assert torch.isfinite(o).all()

@@ -67,17 +67,20 @@ def test_every_output_written_and_deterministic():
     x, r, i = (to_dev(inp.t[n]) for n in ("x", "r_logit", "i_logit"))
     a_log = to_dev(inp.p["a_log"])
     outs = []
+    need = ssd._ws_bytes("rglru_scan", 2, 333, 384)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")  # the caller's own workspace, reused
     for _ in range(2):
         y = torch.full((2, 333, 384), float("nan"), device="cuda")
         hl = torch.full((2, 384), float("nan"), device="cuda")
         st = ssd.lib().ssd_rglru_scan(2, 333, 384, ssd.SSD_BF16, ssd.SSD_F32, x.data_ptr(), r.data_ptr(),
                                       i.data_ptr(), a_log.data_ptr(), 8.0, None, None, y.data_ptr(), hl.data_ptr(),
-                                      None, torch.cuda.current_stream().cuda_stream)
+                                      None, ws.data_ptr(), need, torch.cuda.current_stream().cuda_stream)
         assert st == 0
         torch.cuda.synchronize()
         assert not torch.isnan(y).any() and not torch.isnan(hl).any()
         outs.append((y.clone(), hl.clone()))
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    assert ssd.lib().ssd_workspace_check(ws.data_ptr(), torch.cuda.current_stream().cuda_stream) == 0
 
 
 def test_decode_steps_equal_scan_and_oracle():

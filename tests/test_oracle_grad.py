@@ -101,7 +101,7 @@ def test_minmax_grads_route_and_split_at_ties():
     assert G["ds"][0, 0, 0] == 0.5 and G["dr"][0, 0, 0] == 0.25 and G["dx0"][0, 0] == 0.25
 
 
-def _selective_case(seed, softplus=True, clamp=False):
+def _selective_case(seed, softplus=True, clamp=False, threshold=False):
     rng = np.random.default_rng(seed)
     B, L, D, N = 2, 6, 3, 4
     x, z, dy = (rng.standard_normal((B, L, D)) for _ in range(3))
@@ -109,17 +109,28 @@ def _selective_case(seed, softplus=True, clamp=False):
     A = -rng.uniform(0.5, 3.0, size=(D, N))
     Bm, Cm = (rng.standard_normal((B, L, N)) * 0.5 for _ in range(2))
     Dskip, dt_bias = rng.standard_normal(D), rng.standard_normal(D) * 0.3
-    if clamp:  # channel 0: positive A, small steps except one large step at t = 2, where the clamp at 20
-        A[0, :] = [30.0, 45.0, 0.3, 60.0]  # acts on states 0, 1, 3 (away from its edge) and the state
-        dt[:, :, 0] = 0.05 - dt_bias[0]    # grows by e^20 once
-        dt[:, 2, 0] = 1.0 - dt_bias[0]
     h0, dhl = rng.standard_normal((B, D, N)), rng.standard_normal((B, D, N))
+    if clamp:  # channel 0: positive A, steps delta = 0.01 except delta = 1 at t = 2, where the clamp at 20 acts
+        A[0, :] = [30.0, 45.0, 0.3, 60.0]  # on states 0, 1, 3 (10 to 40 beyond its edge) and they grow by e^20
+        delta = np.full(L, 0.01)           # once; a tiny h0 and no input before that step keep the loss and
+        delta[2] = 1.0                     # the gradients of order one, so differences stay precise
+        v = np.log(np.expm1(delta)) if softplus else delta  # dt + dt_bias giving these steps
+        dt[:, :, 0] = v - dt_bias[0]
+        h0[:, 0, :] *= 1e-8
+        x[:, :2, 0] = 0.0
+    if threshold:  # channel 1: dt + dt_bias on both sides of softplus's threshold at 20, at least 0.3 away
+        dt[:, :, 1] = np.array([18.5, 19.7, 20.3, 21.0, 24.0, 19.0]) - dt_bias[1]
     return dict(x=x, dt=dt, A=A, Bm=Bm, Cm=Cm, Dskip=Dskip, z=z, dt_bias=dt_bias, h0=h0), dy, dhl
 
 
-@pytest.mark.parametrize("softplus,clamp", [(True, False), (False, False)])
-def test_selective_grads_match_central_differences(softplus, clamp):
-    k, dy, dhl = _selective_case(31 + softplus + 2 * clamp, softplus, clamp)
+# clamp: channel 0 has positive A and steps that put delta*A above the clamp at 20 (no gradient through
+# the clamped exponent); threshold: channel 1 has dt + dt_bias around softplus's threshold at 20, where
+# delta = dt + dt_bias exactly and its derivative is 1 (only with softplus on)
+@pytest.mark.parametrize("softplus,clamp,threshold", [(True, False, False), (False, False, False),
+                                                      (True, True, False), (False, True, False),
+                                                      (True, False, True)])
+def test_selective_grads_match_central_differences(softplus, clamp, threshold):
+    k, dy, dhl = _selective_case(31 + softplus + 2 * clamp + 4 * threshold, softplus, clamp, threshold)
     G = og.selective_scan_grads(k["x"], k["dt"], k["A"], k["Bm"], k["Cm"], dy, Dskip=k["Dskip"], z=k["z"],
                                 dt_bias=k["dt_bias"], dt_softplus=softplus, h0=k["h0"], dh_last=dhl)
 
