@@ -140,6 +140,19 @@ int ssd_rglru_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype,
  * SSD_ERR_SHAPE (sizes the scan rejects).  The other queries below follow the same convention. */
 int ssd_rglru_scan_workspace_bytes(int64_t B, int64_t L, int64_t D, size_t* bytes);
 
+/* ssd_rglru_scan without a workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation).  The same kernels
+ * run on a fixed scratch array the library holds per GPU (SSD_NOALLOC_SCRATCH_BYTES, taken when the
+ * library's device code loads on that GPU and kept until the process ends); the call allocates nothing.
+ * All calls on one GPU share that array, so calls whose work may overlap on one GPU (different streams,
+ * unordered threads) race; calls ordered on one stream do not.  Arguments, results and errors as
+ * ssd_rglru_scan, plus SSD_ERR_SHAPE when ssd_rglru_scan_workspace_bytes exceeds the array's size. */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int ssd_rglru_scan_noalloc(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype,
+                           const void* x, const void* r_logit, const void* i_logit,
+                           const float* a_log, float c, const float* h0, const void* gate,
+                           void* y, float* h_last, float* chunk_states, void* stream);
+
 /* Gradients of ssd_rglru_scan (reverse-time adjoint; the pages train through autograd and print no
  * backward pass, so this is the gradient of the forward definition above) for the loss
  *     sum_{b,t,d} dy * y  +  sum_{b,d} dh_last * h_last:

@@ -8,7 +8,7 @@ HIP kernels.  There is no CPU or eager fallback: importing works without a GPU,
 but each call raises if the library is not built or no GPU is present.
 
 Entry points (same names as the C ABI without the ``ssd_`` prefix):
-    rglru_scan, rglru_scan_backward, rglru_update,
+    rglru_scan, rglru_scan_noalloc, rglru_scan_backward, rglru_update,
     minmax_scan, minmax_scan_backward, minmax_update,
     causal_conv1d, causal_conv1d_update,
     selective_scan, selective_scan_backward, selective_update,
@@ -48,7 +48,7 @@ EXPORTS = ("ssd_status_str", "ssd_last_error", "ssd_version", "ssd_testing_lookb
            "ssd_readout_norm", "ssd_rglru_scan_workspace_bytes", "ssd_rglru_scan_backward_workspace_bytes",
            "ssd_minmax_scan_workspace_bytes", "ssd_minmax_scan_backward_workspace_bytes",
            "ssd_selective_scan_workspace_bytes", "ssd_selective_scan_backward_workspace_bytes",
-           "ssd_hgrn2_scan_backward_workspace_bytes")
+           "ssd_hgrn2_scan_backward_workspace_bytes", "ssd_rglru_scan_noalloc")
 
 
 class SSDError(RuntimeError):
@@ -86,6 +86,8 @@ def lib() -> ctypes.CDLL:
         L.ssd_workspace_check.argtypes = [_vp, _vp]
         L.ssd_rglru_scan.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _fp, ctypes.c_float,
                                      _fp, _vp, _vp, _fp, _fp, _vp, _sz, _vp]
+        L.ssd_rglru_scan_noalloc.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _fp,
+                                             ctypes.c_float, _fp, _vp, _vp, _fp, _fp, _vp]
         L.ssd_rglru_update.argtypes = [_i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _fp, ctypes.c_float, _vp,
                                        _fp, _vp, _vp]
         L.ssd_rglru_scan_backward.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _fp,
@@ -278,6 +280,32 @@ def rglru_scan(x, r_logit, i_logit, a_log, c: float = 8.0, h0=None, return_last_
                               _dev(chunk_states, "chunk_states", chunk_states_shape(B, L, D), torch.float32),
                               wp, wn, _stream(x.device))
     _raise(st, "rglru_scan")
+    return (y, h_last) if return_last_state else y
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # SSD_NOALLOC_SCRATCH_BYTES of ssd.h
+
+
+def rglru_scan_noalloc(x, r_logit, i_logit, a_log, c: float = 8.0, h0=None, return_last_state: bool = False,
+                       out_dtype=None, gate=None, chunk_states=None, y=None, h_last=None):
+    """``rglru_scan`` through ``ssd_rglru_scan_noalloc``: no workspace, the library's fixed per-GPU scratch
+    (for callers that cannot allocate; calls that overlap on one GPU race).  ``y`` / ``h_last`` may be
+    given preallocated.  Returns y, or (y, h_last)."""
+    torch = _torch()
+    B, L, D = x.shape
+    code = _act([x, r_logit, i_logit, gate], ["x", "r_logit", "i_logit", "gate"])
+    oc = _out_code(out_dtype)
+    if y is None:
+        y = torch.empty((B, L, D), device=x.device, dtype=torch.bfloat16 if oc == SSD_BF16 else torch.float32)
+    if return_last_state and h_last is None:
+        h_last = torch.empty((B, D), device=x.device, dtype=torch.float32)
+    st = lib().ssd_rglru_scan_noalloc(B, L, D, code, oc, _dev(x, "x"), _dev(r_logit, "r_logit", x.shape),
+                                      _dev(i_logit, "i_logit", x.shape), _dev(a_log, "a_log", (D,), torch.float32),
+                                      float(c), _dev(h0, "h0", (B, D), torch.float32), _dev(gate, "gate", x.shape),
+                                      _dev(y, "y", (B, L, D)), _dev(h_last, "h_last", (B, D), torch.float32),
+                                      _dev(chunk_states, "chunk_states", chunk_states_shape(B, L, D), torch.float32),
+                                      _stream(x.device))
+    _raise(st, "rglru_scan_noalloc")
     return (y, h_last) if return_last_state else y
 
 
@@ -613,7 +641,7 @@ def readout_norm(o, gate=None, weight=None, bias=None, eps: float = 1e-5, out_dt
     return y
 
 
-__all__ = ["chunk_states_shape", "SCAN_CHUNK", "rglru_scan", "rglru_scan_backward", "rglru_update", "selective_scan",
+__all__ = ["chunk_states_shape", "SCAN_CHUNK", "rglru_scan", "rglru_scan_noalloc", "rglru_scan_backward", "rglru_update", "selective_scan",
            "selective_scan_backward", "selective_update", "hgrn2_scan", "hgrn2_scan_backward", "hgrn2_update",
            "readout_norm", "minmax_scan", "minmax_update", "minmax_scan_backward", "causal_conv1d",
            "causal_conv1d_update", "workspace_check", "testing_lookback", "lib", "LIB_PATH", "EXPORTS", "SSDError",

@@ -214,6 +214,39 @@ int ssd_rglru_scan(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype,
   return hip_status(ssd::launch_rglru_scan(a, s), "rglru_scan launch");
 }
 
+int ssd_rglru_scan_noalloc(int64_t B, int64_t L, int64_t D, int in_dtype, int out_dtype, const void* x,
+                           const void* r_logit, const void* i_logit, const float* a_log, float c, const float* h0,
+                           const void* gate, void* y, float* h_last, float* chunk_states, void* stream) {
+  SSD_TRY(check_dtypes(in_dtype, out_dtype));
+  SSD_TRY(scan1_shape(B, L, D));
+  if (!std::isfinite(c)) return fail(SSD_ERR_VALUE, "c must be finite");
+  const int64_t nact = B * L * D;
+  if (nact > 0 && (!x || !r_logit || !i_logit || !y)) return fail(SSD_ERR_NULL, "x, r_logit, i_logit and y are required");
+  if (B * D > 0 && !a_log) return fail(SSD_ERR_NULL, "a_log is required");
+  const size_t ab = (size_t)nact * esize(in_dtype), yb = (size_t)nact * esize(out_dtype);
+  const size_t sb = (size_t)(B * D) * 4;
+  std::vector<Span> ins = {{"x", x, ab}, {"r_logit", r_logit, ab}, {"i_logit", i_logit, ab},
+                           {"a_log", a_log, (size_t)D * 4}, {"h0", h0, sb}, {"gate", gate, ab}};
+  std::vector<Span> outs = {{"y", y, yb}, {"h_last", h_last, sb}, {"chunk_states", chunk_states, chunk_bytes(B, L, D)}};
+  std::vector<Span> all = ins;
+  all.insert(all.end(), outs.begin(), outs.end());
+  SSD_TRY(check_align(all));
+  SSD_TRY(check_alias(outs, ins));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (B * D == 0) return ok();
+  if (L == 0) return hip_status(ssd::launch_copy_or_zero(h_last, h0, B * D, s), "rglru_scan_noalloc");
+  const size_t need = ssd::scan1_scratch_bytes(B, L, D);
+  if (need > ssd::kNoAllocScratchBytes)
+    return fail(SSD_ERR_SHAPE, "rglru_scan_noalloc: the problem needs " + std::to_string(need) +
+                                   " bytes of scratch, above the fixed " +
+                                   std::to_string(ssd::kNoAllocScratchBytes) + " (use ssd_rglru_scan)");
+  void* scratch = nullptr;
+  SSD_TRY(hip_status(ssd::noalloc_scratch(&scratch), "rglru_scan_noalloc scratch address"));
+  ssd::RglruScanArgs a{B, L, D, in_dtype == SSD_BF16, out_dtype == SSD_BF16, x, r_logit, i_logit, a_log, c, h0, gate,
+                       y, h_last, chunk_states, scratch, wait_cfg()};
+  return hip_status(ssd::launch_rglru_scan(a, s), "rglru_scan_noalloc launch");
+}
+
 int ssd_rglru_update(int64_t B, int64_t D, int in_dtype, int out_dtype, const void* x, const void* r_logit,
                      const void* i_logit, const float* a_log, float c, const void* gate, float* state, void* y,
                      void* stream) {

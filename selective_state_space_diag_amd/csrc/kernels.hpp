@@ -44,6 +44,10 @@ struct RglruScanArgs {
   WaitCfg wait;
 };
 hipError_t launch_rglru_scan(const RglruScanArgs& a, hipStream_t s);
+// The fixed per-device scratch of ssd_rglru_scan_noalloc: its device address on the current device
+// (looked up once per device); it holds kNoAllocScratchBytes.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+hipError_t noalloc_scratch(void** out);
 
 struct RglruUpdateArgs {
   int64_t B, D;

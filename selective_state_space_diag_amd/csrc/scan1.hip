@@ -1158,6 +1158,36 @@ size_t scan1_scratch_bytes(int64_t B, int64_t L, int64_t D) {
   return (size_t)kCtlBytes + (size_t)(B * n_tiles * n_chunks) * 3 * TW * sizeof(unsigned long long);
 }
 
+// ------------------------------------------------------------------ fixed device scratch
+// The lookback scratch of ssd_rglru_scan_noalloc, for callers that cannot allocate: one array per
+// GPU, zero at module load and left ready for the next launch by every launch (the launch counter
+// and ticket resets of the lookback protocol), so it is never cleared again.  Every call on a GPU
+// shares it: calls whose work overlaps on one GPU race.  Host code uses only the per-device address
+// from hipGetSymbolAddress, never the array's name (a host-side stand-in).
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_noalloc_mu;
+void* g_noalloc_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (!g_noalloc_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));  // with device `dev` current
+    if (e != hipSuccess) return e;
+    g_noalloc_ptr[dev] = ptr;
+  }
+  *out = g_noalloc_ptr[dev];
+  return hipSuccess;
+}
+
 hipError_t launch_rglru_scan(const RglruScanArgs& a, hipStream_t s) {
   Scan1Params p{};
   p.B = a.B; p.L = a.L; p.D = a.D;
