@@ -1,26 +1,33 @@
 #!/usr/bin/env python3
 """Throughput of the gfx950 gated diagonal linear-recurrence scans on one MI355X.
 
-Headline (the JSON ``value``): the multi-scale selective scan at B=4, L=2048, D=1536, N=16,
-bf16 inputs, fp32 state and output, in state updates per second.  One step is one full
-selective scan (softplus, discretisation, recurrence, readout, skip and silu gate) over one
-batch of synthetic input already resident in HBM.  Three input sets rotate so the 256 MB
-Infinity Cache cannot serve the 126 MB working set.
+Headline (the JSON ``value``): the packed variable-length multi-scale selective scan, L = 131072
+tokens in 32 sequences (lengths log-uniform in [512, 16384], rescaled to sum to L), D = 4096 channels,
+N = 16 states, 4 scales, bf16 inputs, fp32 state and output, in state updates per second.  One step is
+one full scan (softplus of dt, discretisation, recurrence with a state reset at every sequence start,
+readout, skip and silu gate) over inputs already resident in HBM.  The 5.4 GB it moves per step is 21
+times the 256 MB Infinity Cache, so one input set suffices.
 
 The JSON line also carries:
-  roofline      the dominant kernel against its roofline, with per-step HIP-event timing on
-                the stream the kernels run on;
-  cpu_baseline  the fp64 CPU oracle timed on the host (reported baseline, not a target);
-  forms         the other workloads (RG-LRU fp32 and bf16, RG-LRU decode, HGRN2, packed
-                variable-length selective scan) with their own throughput and GB/s.
+  roofline      the headline call against the HBM roofline (algorithmic bytes / time), with per-step
+                HIP-event timing on the stream the kernels run on, median and min, the fraction of the
+                measured device-copy rate, the fp32 ALU fraction beside it, and the HBM traffic recorded
+                by rocprofv3 counters (profiles/), null once the kernel sources changed;
+  cpu_baseline  the fp64 CPU oracle on a sample of the same workload (512 channels, every sequence),
+                timed with one thread and with every host thread it may use (reported, not a target);
+  forms         the other workloads with their own throughput, GB/s, median and min.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-forms] [--no-cpu-baseline]
+                       [--only NAME] [--copy-calibration-mb MB]
+``--only NAME`` runs one workload (``headline`` or a form name) and prints its record alone: the
+profiling commands under profiles/ use it.
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -35,6 +42,10 @@ FP32_VECTOR_TFLOPS = 157.3   # MI355X fp32 vector, published (counts packed two-
 # 16 lanes x 2 flops per FMA x 2.4 GHz
 FP32_SCALAR_FMA_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 BF16_MFMA_TFLOPS = 2500.0    # MI355X dense bf16 matrix, published
+
+HEADLINE = dict(L=131072, D=4096, N=16, nseq=32, scales=4, seed=1004)
+HEADLINE_KERNELS = ["selective_state_space_diag_amd/csrc/selective.hip",
+                    "selective_state_space_diag_amd/csrc/common.hpp"]
 
 
 # ----------------------------------------------------------------------------- algorithmic sizes
@@ -117,10 +128,10 @@ WARM_SECONDS = 0.3  # untimed running before each timed region, so clocks have l
 
 
 def time_calls(fn, n_sets, steps, warmup):
-    """Run ``fn(i % n_sets)`` at least ``warmup`` times and for at least WARM_SECONDS, then time
-    ``steps`` back-to-back calls between one pair of HIP events on torch's current stream (the stream
-    the library launches on), synchronizing before and after.  Returns (ms per step from the events,
-    ms per step from the host clock)."""
+    """Run ``fn(i % n_sets)`` at least ``warmup`` times and for at least WARM_SECONDS, then time ``steps``
+    back-to-back calls with a HIP event between consecutive calls, on torch's current stream (the stream
+    the library launches on), synchronizing before and after.  Returns a dict: ms (mean per step over the
+    timed region), median_ms, min_ms (per step), host_ms (host clock per step)."""
     import torch
     t_warm = time.perf_counter()
     i = 0
@@ -130,15 +141,29 @@ def time_calls(fn, n_sets, steps, warmup):
         if i % 16 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    start.record()
+    ev[0].record()
     for i in range(steps):
         fn(i % n_sets)
-    end.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3
-    return start.elapsed_time(end) / steps, wall / steps
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return dict(ms=ev[0].elapsed_time(ev[-1]) / steps, median_ms=statistics.median(per), min_ms=min(per),
+                host_ms=wall / steps)
+
+
+def copy_rate_gbs(device, mib=2048, reps=10):
+    """Device-to-device copy rate (read + write bytes / time) of a plain torch copy of ``mib`` MiB."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, device=device)
+    dst = torch.empty_like(src)
+    t = time_calls(lambda k: dst.copy_(src), 1, reps, 2)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n * 4 / (t["median_ms"] * 1e-3) / 1e9
 
 
 def dev_bf16(bits, device):
@@ -146,21 +171,149 @@ def dev_bf16(bits, device):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
 
 
+class Gen:
+    """Seeded normal / uniform draws on the GPU (torch's Philox generator), for the large workloads."""
+
+    def __init__(self, device, seed):
+        import torch
+        self.torch = torch
+        self.device = device
+        self.g = torch.Generator(device=device)
+        self.g.manual_seed(seed)
+
+    def randn(self, shape, std=1.0, mean=0.0, dtype=None):
+        t = self.torch.randn(shape, generator=self.g, device=self.device, dtype=self.torch.float32)
+        t = t * std + mean
+        return t.to(dtype or self.torch.bfloat16)
+
+    def uniform(self, shape, lo, hi):
+        return self.torch.empty(shape, device=self.device).uniform_(lo, hi, generator=self.g)
+
+
+def selective_gpu_inputs(gen, B, L, D, N, scales=4, structured_A=True):
+    """The selective workload's distributions drawn on the GPU: A multi-scale (or unstructured),
+    delta = delta0[d] exp(N(0, 0.1)) passed as dt = softplus^-1(delta) in bf16, x, z ~ N(0, 1),
+    B, C ~ N(0, 1/N), skip D = 1."""
+    import torch
+    from selective_state_space_diag_amd import synth
+    x, z = gen.randn((B, L, D)), gen.randn((B, L, D))
+    if structured_A:
+        A = torch.from_numpy(synth.multiscale_A(D, N, scales)).to(gen.device)
+    else:
+        A = -torch.exp(gen.uniform((D, N), np.log(0.5), np.log(64.0)))
+    delta0 = torch.exp(gen.uniform((D,), np.log(1e-3), np.log(1e-1)))
+    dt = torch.empty((B, L, D), device=gen.device, dtype=torch.bfloat16)
+    for b in range(B):  # row by row: the fp32 intermediates of one batch row at a time
+        delta = torch.exp(gen.randn((1, L, D), std=0.1, dtype=torch.float32)) * delta0
+        dt[b] = (delta + torch.log(-torch.expm1(-delta))).to(torch.bfloat16)[0]
+        del delta
+    Bm, Cm = gen.randn((B, L, N), std=1.0 / N), gen.randn((B, L, N), std=1.0 / N)
+    return dict(x=x, z=z, A=A, dt=dt, Bm=Bm, Cm=Cm, Dskip=torch.ones(D, device=gen.device))
+
+
+def record_of(t, updates, nbytes, extra=None, name=None):
+    d = dict(ms=round(t["ms"], 5), median_ms=round(t["median_ms"], 5), min_ms=round(t["min_ms"], 5),
+             state_updates_per_s=updates / (t["ms"] * 1e-3), hbm_gbs=nbytes / (t["ms"] * 1e-3) / 1e9,
+             hbm_frac=nbytes / (t["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, algorithmic_bytes=nbytes,
+             state_updates=updates)
+    if extra:
+        d.update(extra)
+    if name:
+        print(f"# {name}: {t['ms']:.4f} ms (median {t['median_ms']:.4f}, min {t['min_ms']:.4f})  "
+              f"{d['state_updates_per_s']:.3e} upd/s  {d['hbm_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+    return d
+
+
 # ----------------------------------------------------------------------------- headline
 def headline(args, device):
+    """The packed varlen selective scan (L = 131072, 32 sequences, D = 4096, N = 16)."""
     import torch
     import selective_state_space_diag_amd as ssd
     from selective_state_space_diag_amd import synth
 
-    cfg = synth.WORKLOADS["selective"]
-    B, L, D, N = cfg["B"], cfg["L"], cfg["D"], cfg["N"]
-    n_sets = 3
+    c = HEADLINE
+    Lt, D, N, ns = c["L"], c["D"], c["N"], c["nseq"]
+    lengths = synth.varlen_lengths(Lt, ns, c["seed"])
+    cu_host = synth.cu_seqlens_from_lengths(lengths)
+    cu = torch.from_numpy(cu_host).to(device)
+    inp = selective_gpu_inputs(Gen(device, c["seed"]), 1, Lt, D, N, c["scales"])
+
+    def step(i):
+        return ssd.selective_scan(inp["x"], inp["dt"], inp["A"], inp["Bm"], inp["Cm"], Dskip=inp["Dskip"],
+                                  z=inp["z"], cu_seqlens=cu, check_cu_seqlens=False)
+
+    t = time_calls(step, 1, args.steps, args.warmup)
+    updates = Lt * D * N
+    nbytes = selective_bytes(1, Lt, D, N, nseq=ns)
+    return dict(t=t, updates=updates, bytes=nbytes, inputs=inp, cu=cu_host, lengths=lengths)
+
+
+def cpu_baseline(head, max_threads=16):
+    """The fp64 oracle (unchanged, as the tests use it) on a bounded sample of the headline workload:
+    512 channels (every 8th, so all four scale blocks) over all 131072 rows and all 32 sequences, the
+    same input bits as the GPU run; timed once with one thread and once split over the host threads
+    this process may use (at most 16, the host share of one GPU), one thread per channel group."""
+    import torch
+    from concurrent.futures import ThreadPoolExecutor
+    import oracle
+
+    inp = head["inputs"]
+    D = inp["x"].shape[2]
+    ds = torch.arange(0, D, 8, device=inp["x"].device)
+    h = lambda t: t[:, :, ds].double().cpu().numpy()
+    x, dt, z = h(inp["x"]), h(inp["dt"]), h(inp["z"])
+    Bm, Cm = inp["Bm"].double().cpu().numpy(), inp["Cm"].double().cpu().numpy()
+    A = inp["A"][ds].double().cpu().numpy()
+    Dskip = inp["Dskip"][ds].double().cpu().numpy()
+    cu = head["cu"]
+    oracle.lib()
+    nch = len(ds)
+    updates = x.shape[1] * nch * A.shape[1]
+
+    def run(sl):
+        oracle.selective_scan(np.ascontiguousarray(x[:, :, sl]), np.ascontiguousarray(dt[:, :, sl]), A[sl], Bm, Cm,
+                              Dskip=Dskip[sl], z=np.ascontiguousarray(z[:, :, sl]), dt_softplus=True, cu_seqlens=cu)
+
+    t0 = time.perf_counter()
+    run(slice(0, nch))
+    one = time.perf_counter() - t0
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        avail = os.cpu_count() or 1
+    nthr = max(1, min(avail, max_threads))
+    groups = [slice(i * nch // nthr, (i + 1) * nch // nthr) for i in range(nthr)]
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=nthr) as ex:
+        list(ex.map(run, groups))
+    many = time.perf_counter() - t0
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
+    return dict(value=updates / many, unit="state-updates/s", cores=nthr, kind="oracle",
+                sample=f"512 of 4096 channels (every 8th) of the headline workload, all 131072 rows and 32 "
+                       f"sequences, {updates} state updates, fp64; {many:.2f} s on {nthr} threads, "
+                       f"{one:.2f} s on 1 thread",
+                single_thread_value=updates / one, host_nproc=os.cpu_count(), host_threads_allowed=avail,
+                cpu_model=model)
+
+
+# ----------------------------------------------------------------------------- other workloads
+def form_selective_cfg(args, device):
+    """The batched selective scan B=4 L=2048 D=1536 N=16, three rotating input sets (126 MB each, so the
+    256 MB Infinity Cache cannot hold the working set)."""
+    import torch
+    import selective_state_space_diag_amd as ssd
+    from selective_state_space_diag_amd import synth
+    B, L, D, N = 4, 2048, 1536, 16
     sets = []
-    host_inputs = None
-    for k in range(n_sets):
+    for k in range(3):
         inp = synth.workload_inputs("selective", seed=1001 + 100 * k)
-        if k == 0:
-            host_inputs = inp
         t = {n: dev_bf16(v.data, device) for n, v in inp.t.items()}
         sets.append(dict(t=t, A=torch.from_numpy(inp.p["A"]).to(device),
                          Dskip=torch.from_numpy(inp.p["Dskip"]).to(device)))
@@ -168,150 +321,147 @@ def headline(args, device):
     def step(i):
         s = sets[i]
         t = s["t"]
-        return ssd.selective_scan(t["x"], t["dt"], s["A"], t["Bm"], t["Cm"], Dskip=s["Dskip"], z=t["z"],
-                                  dt_softplus=True)
+        return ssd.selective_scan(t["x"], t["dt"], s["A"], t["Bm"], t["Cm"], Dskip=s["Dskip"], z=t["z"])
 
-    ms, wall = time_calls(step, n_sets, args.steps, args.warmup)
-    updates = B * L * D * N
-    nbytes = selective_bytes(B, L, D, N)
-    res = dict(ms=ms, updates=updates, bytes=nbytes, host_ms=wall)
-    return res, host_inputs
+    t = time_calls(step, 3, 50, 5)
+    return record_of(t, B * L * D * N, selective_bytes(B, L, D, N),
+                     dict(alu_tflops=B * L * D * N * SELECTIVE_FLOPS_PER_UPDATE / (t["ms"] * 1e-3) / 1e12),
+                     "selective_B4_L2048_D1536_N16")
 
 
-def cpu_baseline(host_inputs, min_seconds: float = 10.0):
-    """The fp64 oracle on the whole headline workload (4 x 2048 x 1536 x 16), run back to back until
-    at least ``min_seconds`` have passed (one pass takes about a second)."""
-    import oracle
-    t = host_inputs.t
-    x, dt, z, Bm, Cm = (t[n].f64() for n in ("x", "dt", "z", "Bm", "Cm"))
-    A = host_inputs.p["A"].astype(np.float64)
-    Dskip = host_inputs.p["Dskip"].astype(np.float64)
-    oracle.lib()
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.selective_scan(x, dt, A, Bm, Cm, Dskip=Dskip, z=z, dt_softplus=True)
-        reps += 1
-        sec = time.perf_counter() - t0
-        if sec >= min_seconds:
-            break
-    updates = reps * x.shape[0] * x.shape[1] * x.shape[2] * A.shape[1]
-    return dict(value=updates / sec, unit="state-updates/s", cores=1, kind="oracle",
-                sample=f"the whole headline workload (4x2048x1536 channels x 16 states) {reps} times back to back, "
-                       f"{updates} updates in {sec:.1f} s, single-threaded fp64")
+def form_selective_unstructured(args, device):
+    import selective_state_space_diag_amd as ssd
+    B, L, D, N = 4, 2048, 1536, 16
+    inp = selective_gpu_inputs(Gen(device, 7), B, L, D, N, structured_A=False)
+    t = time_calls(lambda k: ssd.selective_scan(inp["x"], inp["dt"], inp["A"], inp["Bm"], inp["Cm"],
+                                                Dskip=inp["Dskip"], z=inp["z"]), 1, 30, 3)
+    return record_of(t, B * L * D * N, selective_bytes(B, L, D, N), None,
+                     "selective_unstructured_A_B4_L2048_D1536_N16")
 
 
-# ----------------------------------------------------------------------------- other workloads
-def forms(args, device):
+def form_selective_backward(args, device):
+    import selective_state_space_diag_amd as ssd
+    B, L, D, N = 4, 2048, 1536, 16
+    gen = Gen(device, 8)
+    inp = selective_gpu_inputs(gen, B, L, D, N)
+    dy = gen.randn((B, L, D))
+    t = time_calls(lambda k: ssd.selective_scan_backward(inp["x"], inp["dt"], inp["A"], inp["Bm"], inp["Cm"], dy,
+                                                         Dskip=inp["Dskip"], z=inp["z"]), 1, 10, 2)
+    return record_of(t, B * L * D * N, selective_bwd_bytes(B, L, D, N), None, "selective_backward_bf16_B4_L2048_D1536_N16")
+
+
+def form_rglru_small(args, device):
     import torch
     import selective_state_space_diag_amd as ssd
-    from selective_state_space_diag_amd import synth
-
-    out = {}
-    gen = torch.Generator(device=device)
-    gen.manual_seed(7)
-
-    def randn(shape, std=1.0, mean=0.0, dtype=torch.bfloat16):
-        t = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
-        return (t * std + mean).to(dtype)
-
-    def record(name, ms, updates, nbytes, extra=None):
-        d = dict(ms=round(ms, 5), state_updates_per_s=updates / (ms * 1e-3),
-                 hbm_gbs=nbytes / (ms * 1e-3) / 1e9, hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                 algorithmic_bytes=nbytes, state_updates=updates)
-        if extra:
-            d.update(extra)
-        out[name] = d
-        print(f"# {name}: {ms:.4f} ms  {d['state_updates_per_s']:.3e} upd/s  {d['hbm_gbs']:.0f} GB/s",
-              file=sys.stderr, flush=True)
-
-    # --- headline shape with unstructured A (no integer-multiple rows): one exponential per state
-    B, L, D, N = 4, 2048, 1536, 16
-    x, z = randn((B, L, D)), randn((B, L, D))
-    A = -torch.exp(torch.empty(D, N, device=device).uniform_(np.log(0.5), np.log(64.0), generator=gen))
-    delta0 = torch.exp(torch.empty(D, device=device).uniform_(np.log(1e-3), np.log(1e-1), generator=gen))
-    delta = torch.exp(randn((B, L, D), std=0.1, dtype=torch.float32)) * delta0
-    dt = (delta + torch.log(-torch.expm1(-delta))).to(torch.bfloat16)
-    del delta
-    Bm, Cm = randn((B, L, N), std=1.0 / N), randn((B, L, N), std=1.0 / N)
-    Dskip = torch.ones(D, device=device)
-    ms = time_calls(lambda kk: ssd.selective_scan(x, dt, A, Bm, Cm, Dskip=Dskip, z=z), 1, 30, 3)[0]
-    record("selective_unstructured_A_B4_L2048_D1536_N16", ms, B * L * D * N, selective_bytes(B, L, D, N))
-
-    # --- gradients of the selective scan on the headline shape (dy ~ N(0, 1), h0 and dh_last zero)
-    dy = randn((B, L, D))
-    ms = time_calls(lambda kk: ssd.selective_scan_backward(x, dt, A, Bm, Cm, dy, Dskip=Dskip, z=z), 1, 10, 2)[0]
-    record("selective_backward_bf16_B4_L2048_D1536_N16", ms, B * L * D * N, selective_bwd_bytes(B, L, D, N))
-    del x, z, dt, Bm, Cm, dy
-
-    # --- RG-LRU fp32, B=2 L=128 D=64 (latency bound)
     B, L, D = 2, 128, 64
-    x, r, i = (randn((B, L, D), dtype=torch.float32) for _ in range(3))
-    a_log = torch.log(torch.empty(D, device=device).uniform_(0.9, 0.999, generator=gen))
-    ms = time_calls(lambda k: ssd.rglru_scan(x, r, i, a_log, 8.0), 1, 50, 5)[0]
-    record("rglru_fp32_B2_L128_D64", ms, B * L * D, rglru_bytes(B, L, D, 4, 4))
+    gen = Gen(device, 9)
+    x, r, i = (gen.randn((B, L, D), dtype=torch.float32) for _ in range(3))
+    a_log = torch.log(gen.uniform((D,), 0.9, 0.999))
+    t = time_calls(lambda k: ssd.rglru_scan(x, r, i, a_log, 8.0), 1, 50, 5)
+    return record_of(t, B * L * D, rglru_bytes(B, L, D, 4, 4), None, "rglru_fp32_B2_L128_D64")
 
-    # --- RG-LRU bf16, B=8 L=8192 D=2560
+
+def _rglru_big(device, seed):
+    import torch
     B, L, D = 8, 8192, 2560
-    x, r, i = (randn((B, L, D)) for _ in range(3))
-    a_log = torch.log(torch.empty(D, device=device).uniform_(0.9, 0.999, generator=gen))
-    ms = time_calls(lambda k: ssd.rglru_scan(x, r, i, a_log, 8.0), 1, 10, 2)[0]
-    record("rglru_bf16_B8_L8192_D2560", ms, B * L * D, rglru_bytes(B, L, D))
+    gen = Gen(device, seed)
+    x, r, i = (gen.randn((B, L, D)) for _ in range(3))
+    a_log = torch.log(gen.uniform((D,), 0.9, 0.999))
+    return gen, (B, L, D), x, r, i, a_log
 
-    # --- the same scan with the block's gelu(gate) output multiply fused into its stores
-    gt = randn((B, L, D))
-    ms = time_calls(lambda k: ssd.rglru_scan(x, r, i, a_log, 8.0, gate=gt), 1, 10, 2)[0]
-    record("rglru_gated_bf16_B8_L8192_D2560", ms, B * L * D, rglru_gated_bytes(B, L, D))
-    del gt
 
-    # --- gradients of the RG-LRU scan on the same shape (dy ~ N(0, 1)): with the chunk states a
-    #     training forward saves (1/64 of the states), and recomputing them from the inputs
-    dy = randn((B, L, D))
+def form_rglru(args, device):
+    import selective_state_space_diag_amd as ssd
+    _, (B, L, D), x, r, i, a_log = _rglru_big(device, 10)
+    t = time_calls(lambda k: ssd.rglru_scan(x, r, i, a_log, 8.0), 1, 10, 2)
+    return record_of(t, B * L * D, rglru_bytes(B, L, D), None, "rglru_bf16_B8_L8192_D2560")
+
+
+def form_rglru_gated(args, device):
+    import selective_state_space_diag_amd as ssd
+    gen, (B, L, D), x, r, i, a_log = _rglru_big(device, 11)
+    gt = gen.randn((B, L, D))
+    t = time_calls(lambda k: ssd.rglru_scan(x, r, i, a_log, 8.0, gate=gt), 1, 10, 2)
+    return record_of(t, B * L * D, rglru_gated_bytes(B, L, D), None, "rglru_gated_bf16_B8_L8192_D2560")
+
+
+def form_rglru_noalloc(args, device):
+    import torch
+    import selective_state_space_diag_amd as ssd
+    _, (B, L, D), x, r, i, a_log = _rglru_big(device, 10)
+    y = torch.empty((B, L, D), device=device)
+    t = time_calls(lambda k: ssd.rglru_scan_noalloc(x, r, i, a_log, 8.0, y=y), 1, 10, 2)
+    return record_of(t, B * L * D, rglru_bytes(B, L, D), None, "rglru_noalloc_bf16_B8_L8192_D2560")
+
+
+def form_rglru_backward(args, device):
+    import torch
+    import selective_state_space_diag_amd as ssd
+    gen, (B, L, D), x, r, i, a_log = _rglru_big(device, 12)
+    dy = gen.randn((B, L, D))
     cs = torch.empty(ssd.chunk_states_shape(B, L, D), device=device)
     ssd.rglru_scan(x, r, i, a_log, 8.0, chunk_states=cs)
-    ms = time_calls(lambda k: ssd.rglru_scan_backward(x, r, i, a_log, 8.0, dy, chunk_states=cs), 1, 5, 1)[0]
-    record("rglru_backward_bf16_B8_L8192_D2560", ms, B * L * D, rglru_bwd_bytes(B, L, D) + cs.numel() * 4)
-    ms = time_calls(lambda k: ssd.rglru_scan_backward(x, r, i, a_log, 8.0, dy), 1, 5, 1)[0]
-    record("rglru_backward_recompute_bf16_B8_L8192_D2560", ms, B * L * D, rglru_bwd_bytes(B, L, D))
-    del dy
+    out = {}
+    t = time_calls(lambda k: ssd.rglru_scan_backward(x, r, i, a_log, 8.0, dy, chunk_states=cs), 1, 5, 1)
+    out["rglru_backward_bf16_B8_L8192_D2560"] = record_of(t, B * L * D, rglru_bwd_bytes(B, L, D) + cs.numel() * 4,
+                                                          None, "rglru_backward_bf16_B8_L8192_D2560")
+    t = time_calls(lambda k: ssd.rglru_scan_backward(x, r, i, a_log, 8.0, dy), 1, 5, 1)
+    out["rglru_backward_recompute_bf16_B8_L8192_D2560"] = record_of(
+        t, B * L * D, rglru_bwd_bytes(B, L, D), None, "rglru_backward_recompute_bf16_B8_L8192_D2560")
+    return out
 
-    # --- MinMax scan on the same shape (r, s ~ N(0, 1))
-    ms = time_calls(lambda k: ssd.minmax_scan(r, i), 1, 10, 2)[0]
-    record("minmax_bf16_B8_L8192_D2560", ms, B * L * D, minmax_bytes(B, L, D))
 
-    # --- gradients of the MinMax scan on the same shape (dy ~ N(0, 1)), with and without the
-    #     forward's chunk states
-    dy = randn((B, L, D))
+def form_minmax(args, device):
+    import torch
+    import selective_state_space_diag_amd as ssd
+    gen, (B, L, D), x, r, i, a_log = _rglru_big(device, 13)
+    out = {}
+    t = time_calls(lambda k: ssd.minmax_scan(r, i), 1, 10, 2)
+    out["minmax_bf16_B8_L8192_D2560"] = record_of(t, B * L * D, minmax_bytes(B, L, D), None,
+                                                  "minmax_bf16_B8_L8192_D2560")
+    dy = gen.randn((B, L, D))
+    cs = torch.empty(ssd.chunk_states_shape(B, L, D), device=device)
     ssd.minmax_scan(r, i, chunk_states=cs)
-    ms = time_calls(lambda k: ssd.minmax_scan_backward(r, i, dy, chunk_states=cs), 1, 5, 1)[0]
-    record("minmax_backward_bf16_B8_L8192_D2560", ms, B * L * D, minmax_bwd_bytes(B, L, D) + cs.numel() * 4)
-    ms = time_calls(lambda k: ssd.minmax_scan_backward(r, i, dy), 1, 5, 1)[0]
-    record("minmax_backward_recompute_bf16_B8_L8192_D2560", ms, B * L * D, minmax_bwd_bytes(B, L, D))
-    del dy, cs
+    t = time_calls(lambda k: ssd.minmax_scan_backward(r, i, dy, chunk_states=cs), 1, 5, 1)
+    out["minmax_backward_bf16_B8_L8192_D2560"] = record_of(t, B * L * D, minmax_bwd_bytes(B, L, D) + cs.numel() * 4,
+                                                           None, "minmax_backward_bf16_B8_L8192_D2560")
+    t = time_calls(lambda k: ssd.minmax_scan_backward(r, i, dy), 1, 5, 1)
+    out["minmax_backward_recompute_bf16_B8_L8192_D2560"] = record_of(
+        t, B * L * D, minmax_bwd_bytes(B, L, D), None, "minmax_backward_recompute_bf16_B8_L8192_D2560")
+    return out
 
-    # --- causal depthwise conv (width 4) in front of the RG-LRU, same shape
+
+def form_conv(args, device):
+    import selective_state_space_diag_amd as ssd
+    gen, (B, L, D), x, r, i, a_log = _rglru_big(device, 14)
     W = 4
-    wconv = torch.empty(D, W, device=device).uniform_(-0.5, 0.5, generator=gen)
-    bconv = torch.empty(D, device=device).uniform_(-0.5, 0.5, generator=gen)
-    ms = time_calls(lambda k: ssd.causal_conv1d(x, wconv, bias=bconv), 1, 10, 2)[0]
-    record("causal_conv1d_bf16_B8_L8192_D2560_W4", ms, B * L * D, conv_bytes(B, L, D, W))
-    del x, r, i
+    wconv = gen.uniform((D, W), -0.5, 0.5)
+    bconv = gen.uniform((D,), -0.5, 0.5)
+    t = time_calls(lambda k: ssd.causal_conv1d(x, wconv, bias=bconv), 1, 10, 2)
+    return record_of(t, B * L * D, conv_bytes(B, L, D, W), None, "causal_conv1d_bf16_B8_L8192_D2560_W4")
 
-    # --- RG-LRU decode, B=256 D=2560, 256 steps carrying the state (one launch per step)
+
+def form_rglru_decode(args, device):
+    """256 RG-LRU decode steps at B = 256, D = 2560 carrying the state: one launch per step from Python,
+    and the same 256 launches captured once in a HIP graph and replayed."""
+    import torch
+    import selective_state_space_diag_amd as ssd
     B, D, S = 256, 2560, 256
-    xs, rs, is_ = (randn((S, B, D)) for _ in range(3))
+    gen = Gen(device, 15)
+    xs, rs, is_ = (gen.randn((S, B, D)) for _ in range(3))
+    a_log = torch.log(gen.uniform((D,), 0.9, 0.999))
     state = torch.zeros(B, D, device=device)
 
     def decode(k):
         for s in range(S):
             ssd.rglru_update(xs[s], rs[s], is_[s], a_log, 8.0, state)
 
-    ms = time_calls(decode, 1, 3, 1)[0]
     per_step_bytes = B * D * (3 * 2 + 4 + 4 + 4)
-    record("rglru_decode_B256_D2560_256steps", ms, B * D * S, per_step_bytes * S,
-           dict(us_per_step=ms * 1e3 / S))
-
-    # --- the same 256 decode steps captured once in a HIP graph and replayed (identical kernels)
+    out = {}
+    t = time_calls(decode, 1, 3, 1)
+    out["rglru_decode_B256_D2560_256steps"] = record_of(t, B * D * S, per_step_bytes * S,
+                                                        dict(us_per_step=t["ms"] * 1e3 / S),
+                                                        "rglru_decode_B256_D2560_256steps")
     state_g = torch.zeros(B, D, device=device)
     graph = torch.cuda.CUDAGraph()
     cap = torch.cuda.Stream()
@@ -323,93 +473,148 @@ def forms(args, device):
         with torch.cuda.graph(graph, stream=cap):
             decode_g()
     torch.cuda.synchronize()
-    ms = time_calls(lambda k: graph.replay(), 1, 5, 1)[0]
-    record("rglru_decode_B256_D2560_256steps_hipgraph", ms, B * D * S, per_step_bytes * S,
-           dict(us_per_step=ms * 1e3 / S))
-    del xs, rs, is_, graph
+    t = time_calls(lambda k: graph.replay(), 1, 5, 1)
+    out["rglru_decode_B256_D2560_256steps_hipgraph"] = record_of(t, B * D * S, per_step_bytes * S,
+                                                                 dict(us_per_step=t["ms"] * 1e3 / S),
+                                                                 "rglru_decode_B256_D2560_256steps_hipgraph")
+    return out
 
-    # --- HGRN2 bf16, B=8 H=16 d=128 L=4096, lower bound 0.5
+
+def _hgrn2_inputs(device, seed):
     B, L, H, dd = 8, 4096, 16, 128
-    q, k, v = (randn((B, L, H, dd), std=dd ** -0.5) for _ in range(3))
-    g = randn((B, L, H, dd), mean=2.0)
-    ms = time_calls(lambda kk: ssd.hgrn2_scan(q, k, v, g, 0.5), 1, 5, 1)[0]
+    gen = Gen(device, seed)
+    q, k, v = (gen.randn((B, L, H, dd), std=dd ** -0.5) for _ in range(3))
+    g = gen.randn((B, L, H, dd), mean=2.0)
+    return gen, (B, L, H, dd), q, k, v, g
+
+
+def form_hgrn2(args, device):
+    import selective_state_space_diag_amd as ssd
+    _, (B, L, H, dd), q, k, v, g = _hgrn2_inputs(device, 16)
+    t = time_calls(lambda kk: ssd.hgrn2_scan(q, k, v, g, 0.5), 1, 10, 2)
     flops = 2 * B * L * H * (2 * 64 * dd + 2 * dd * dd)  # chunked form at chunk 64
-    record("hgrn2_bf16_B8_H16_d128_L4096", ms, B * L * H * dd * dd, hgrn2_bytes(B, L, H, dd),
-           dict(mfma_equiv_tflops=flops / (ms * 1e-3) / 1e12,
-                mfma_util=flops / (ms * 1e-3) / 1e12 / BF16_MFMA_TFLOPS))
+    return record_of(t, B * L * H * dd * dd, hgrn2_bytes(B, L, H, dd),
+                     dict(mfma_equiv_tflops=flops / (t["ms"] * 1e-3) / 1e12,
+                          mfma_util=flops / (t["ms"] * 1e-3) / 1e12 / BF16_MFMA_TFLOPS),
+                     "hgrn2_bf16_B8_H16_d128_L4096")
 
-    # --- the same scan at the page's default lower bound 0 (the register sweep: 5 d^2 fp32 flops per
-    #     token and head; the chunked MFMA form needs lower bounds >= 2^-1.5)
-    ms = time_calls(lambda kk: ssd.hgrn2_scan(q, k, v, g, 0.0), 1, 3, 1)[0]
+
+def form_hgrn2_lb0(args, device):
+    import selective_state_space_diag_amd as ssd
+    _, (B, L, H, dd), q, k, v, g = _hgrn2_inputs(device, 16)
+    t = time_calls(lambda kk: ssd.hgrn2_scan(q, k, v, g, 0.0), 1, 3, 1)
     rflops = 5 * B * L * H * dd * dd
-    record("hgrn2_lb0_bf16_B8_H16_d128_L4096", ms, B * L * H * dd * dd, hgrn2_bytes(B, L, H, dd),
-           dict(valu_tflops=rflops / (ms * 1e-3) / 1e12, valu_frac=rflops / (ms * 1e-3) / 1e12 / FP32_SCALAR_FMA_TFLOPS))
+    return record_of(t, B * L * H * dd * dd, hgrn2_bytes(B, L, H, dd),
+                     dict(valu_tflops=rflops / (t["ms"] * 1e-3) / 1e12,
+                          valu_frac=rflops / (t["ms"] * 1e-3) / 1e12 / FP32_SCALAR_FMA_TFLOPS),
+                     "hgrn2_lb0_bf16_B8_H16_d128_L4096")
 
-    # --- gradients of the HGRN2 scan on the same shape (do ~ N(0, 1/d)), given the forward's fp32
-    #     output; the three sweeps execute 15 d^2 fp32 flops per token and head (two state updates of
-    #     3 d^2, the adjoint update twice, three d^2 matrix-vector products)
-    do = randn((B, L, H, dd), std=dd ** -0.5)
+
+def form_hgrn2_backward(args, device):
+    import selective_state_space_diag_amd as ssd
+    gen, (B, L, H, dd), q, k, v, g = _hgrn2_inputs(device, 16)
+    do = gen.randn((B, L, H, dd), std=dd ** -0.5)
     o = ssd.hgrn2_scan(q, k, v, g, 0.5)
-    ms = time_calls(lambda kk: ssd.hgrn2_scan_backward(q, k, v, g, 0.5, do, o=o), 1, 3, 1)[0]
+    t = time_calls(lambda kk: ssd.hgrn2_scan_backward(q, k, v, g, 0.5, do, o=o), 1, 3, 1)
     vflops = 15 * B * L * H * dd * dd
-    record("hgrn2_backward_bf16_B8_H16_d128_L4096", ms, B * L * H * dd * dd, hgrn2_bwd_bytes(B, L, H, dd),
-           dict(valu_tflops=vflops / (ms * 1e-3) / 1e12, valu_frac=vflops / (ms * 1e-3) / 1e12 / FP32_SCALAR_FMA_TFLOPS))
-    del do
+    return record_of(t, B * L * H * dd * dd, hgrn2_bwd_bytes(B, L, H, dd),
+                     dict(valu_tflops=vflops / (t["ms"] * 1e-3) / 1e12,
+                          valu_frac=vflops / (t["ms"] * 1e-3) / 1e12 / FP32_SCALAR_FMA_TFLOPS),
+                     "hgrn2_backward_bf16_B8_H16_d128_L4096")
 
-    # --- the key-axis gate reading on the same inputs (a register sweep: 5 d^2 fp32 flops per token
-    #     and head, the state update and the readout)
-    ms = time_calls(lambda kk: ssd.hgrn2_scan(q, k, v, g, 0.5, gate_axis="key"), 1, 3, 1)[0]
+
+def form_hgrn2_key(args, device):
+    import selective_state_space_diag_amd as ssd
+    _, (B, L, H, dd), q, k, v, g = _hgrn2_inputs(device, 16)
+    t = time_calls(lambda kk: ssd.hgrn2_scan(q, k, v, g, 0.5, gate_axis="key"), 1, 3, 1)
     kflops = 5 * B * L * H * dd * dd
-    record("hgrn2_key_gate_bf16_B8_H16_d128_L4096", ms, B * L * H * dd * dd, hgrn2_bytes(B, L, H, dd),
-           dict(valu_tflops=kflops / (ms * 1e-3) / 1e12, valu_frac=kflops / (ms * 1e-3) / 1e12 / FP32_SCALAR_FMA_TFLOPS))
+    return record_of(t, B * L * H * dd * dd, hgrn2_bytes(B, L, H, dd),
+                     dict(valu_tflops=kflops / (t["ms"] * 1e-3) / 1e12,
+                          valu_frac=kflops / (t["ms"] * 1e-3) / 1e12 / FP32_SCALAR_FMA_TFLOPS),
+                     "hgrn2_key_gate_bf16_B8_H16_d128_L4096")
 
-    # --- readout LayerNorm over the hidden size (H d = 2048) with the silu output gate, on the scan's
-    #     fp32 output: o read (fp32), gate read (bf16), y written (fp32)
-    ogate = randn((B, L, H * dd))
+
+def form_readout_norm(args, device):
+    import torch
+    import selective_state_space_diag_amd as ssd
+    gen, (B, L, H, dd), q, k, v, g = _hgrn2_inputs(device, 16)
+    o = ssd.hgrn2_scan(q, k, v, g, 0.5)
+    del q, k, v, g
+    ogate = gen.randn((B, L, H * dd))
     wn, bn = torch.ones(H * dd, device=device), torch.zeros(H * dd, device=device)
     o2 = o.view(B, L, H * dd)
-    ms = time_calls(lambda kk: ssd.readout_norm(o2, gate=ogate, weight=wn, bias=bn), 1, 10, 2)[0]
-    record("readout_norm_B8_L4096_width2048", ms, B * L * H * dd, B * L * H * dd * (4 + 2 + 4) + H * dd * 8)
-    del q, k, v, g, o, o2, ogate
+    t = time_calls(lambda kk: ssd.readout_norm(o2, gate=ogate, weight=wn, bias=bn), 1, 10, 2)
+    return record_of(t, B * L * H * dd, B * L * H * dd * (4 + 2 + 4) + H * dd * 8, None,
+                     "readout_norm_B8_L4096_width2048")
 
-    # --- packed varlen selective, L=131072, 32 sequences, D=4096, N=16
-    Lt, D, N, ns = 131072, 4096, 16, 32
-    lengths = synth.varlen_lengths(Lt, ns, 1004)
-    cu = torch.from_numpy(synth.cu_seqlens_from_lengths(lengths)).to(device)
-    x, z = randn((1, Lt, D)), randn((1, Lt, D))
-    A = torch.from_numpy(synth.multiscale_A(D, N, 4)).to(device)
-    delta0 = torch.exp(torch.empty(D, device=device).uniform_(np.log(1e-3), np.log(1e-1), generator=gen))
-    delta = torch.exp(randn((1, Lt, D), std=0.1, dtype=torch.float32)) * delta0
-    dt = (delta + torch.log(-torch.expm1(-delta))).to(torch.bfloat16)
-    del delta
-    Bm, Cm = randn((1, Lt, N), std=1.0 / N), randn((1, Lt, N), std=1.0 / N)
-    Dskip = torch.ones(D, device=device)
-    ms = time_calls(lambda kk: ssd.selective_scan(x, dt, A, Bm, Cm, Dskip=Dskip, z=z, cu_seqlens=cu,
-                                                  check_cu_seqlens=False), 1, 5, 1)[0]
-    record("selective_varlen_L131072_D4096_N16_32seq", ms, Lt * D * N, selective_bytes(1, Lt, D, N, nseq=ns))
 
-    # --- gradients of the packed varlen scan (dy ~ N(0, 1))
-    dy = randn((1, Lt, D))
-    ms = time_calls(lambda kk: ssd.selective_scan_backward(x, dt, A, Bm, Cm, dy, Dskip=Dskip, z=z, cu_seqlens=cu,
-                                                           check_cu_seqlens=False), 1, 2, 1)[0]
-    record("selective_backward_varlen_L131072_D4096_N16_32seq", ms, Lt * D * N, selective_bwd_bytes(1, Lt, D, N))
-    return out
+def form_selective_varlen_backward(args, device):
+    import torch
+    import selective_state_space_diag_amd as ssd
+    from selective_state_space_diag_amd import synth
+    c = HEADLINE
+    Lt, D, N, ns = c["L"], c["D"], c["N"], c["nseq"]
+    cu = torch.from_numpy(synth.cu_seqlens_from_lengths(synth.varlen_lengths(Lt, ns, c["seed"]))).to(device)
+    gen = Gen(device, 17)
+    inp = selective_gpu_inputs(gen, 1, Lt, D, N)
+    dy = gen.randn((1, Lt, D))
+    t = time_calls(lambda kk: ssd.selective_scan_backward(inp["x"], inp["dt"], inp["A"], inp["Bm"], inp["Cm"], dy,
+                                                          Dskip=inp["Dskip"], z=inp["z"], cu_seqlens=cu,
+                                                          check_cu_seqlens=False), 1, 2, 1)
+    return record_of(t, Lt * D * N, selective_bwd_bytes(1, Lt, D, N), None,
+                     "selective_backward_varlen_L131072_D4096_N16_32seq")
+
+
+FORMS = {
+    "selective_B4_L2048_D1536_N16": form_selective_cfg,
+    "selective_unstructured_A_B4_L2048_D1536_N16": form_selective_unstructured,
+    "selective_backward_bf16_B4_L2048_D1536_N16": form_selective_backward,
+    "rglru_fp32_B2_L128_D64": form_rglru_small,
+    "rglru_bf16_B8_L8192_D2560": form_rglru,
+    "rglru_gated_bf16_B8_L8192_D2560": form_rglru_gated,
+    "rglru_noalloc_bf16_B8_L8192_D2560": form_rglru_noalloc,
+    "rglru_backward": form_rglru_backward,
+    "minmax": form_minmax,
+    "causal_conv1d_bf16_B8_L8192_D2560_W4": form_conv,
+    "rglru_decode": form_rglru_decode,
+    "hgrn2_bf16_B8_H16_d128_L4096": form_hgrn2,
+    "hgrn2_lb0_bf16_B8_H16_d128_L4096": form_hgrn2_lb0,
+    "hgrn2_backward_bf16_B8_H16_d128_L4096": form_hgrn2_backward,
+    "hgrn2_key_gate_bf16_B8_H16_d128_L4096": form_hgrn2_key,
+    "readout_norm_B8_L4096_width2048": form_readout_norm,
+    "selective_backward_varlen_L131072_D4096_N16_32seq": form_selective_varlen_backward,
+}
+
+
+def run_form(name, args, device):
+    """Records of one form (a dict name -> record); frees its device memory afterwards."""
+    import torch
+    r = FORMS[name](args, device)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if isinstance(r, dict) and "ms" not in r:
+        return r
+    return {name: r}
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-forms", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default=None, help="run one workload: 'headline' or a form name " + ", ".join(FORMS))
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="first run a plain device-to-device tensor copy of this many MiB three times (a known-size "
                          "kernel for scaling hardware traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: the scans shard with no communication across channels, batches "
-              "and heads, and this build runs on a single MI355X; use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: this build runs on a single MI355X (the scans shard with no "
+              "communication across channels, sequences and heads; see DESIGN.md); use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.only is not None and args.only != "headline" and args.only not in FORMS:
+        print(f"unknown workload {args.only!r}; choose 'headline' or one of: {', '.join(FORMS)}", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -427,16 +632,24 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+        torch.cuda.empty_cache()
 
-    head, host_inputs = headline(args, device)
-    ms = head["ms"]
+    if args.only is not None and args.only != "headline":
+        print(json.dumps({"only": args.only, "forms": run_form(args.only, args, device)}), flush=True)
+        return
+
+    copy_gbs = copy_rate_gbs(device)
+    head = headline(args, device)
+    t = head["t"]
+    ms = t["ms"]
     value = head["updates"] / (ms * 1e-3)
     call_s = ms * 1e-3
-    achieved_tflops = head["updates"] * SELECTIVE_FLOPS_PER_UPDATE / call_s / 1e12
     hbm_gbs = head["bytes"] / call_s / 1e9
-    print(f"# headline: {ms:.4f} ms/step (host clock {head['host_ms']:.4f}), {value:.3e} upd/s, "
-          f"{hbm_gbs:.0f} GB/s", file=sys.stderr, flush=True)
-
+    alu_tflops = head["updates"] * SELECTIVE_FLOPS_PER_UPDATE / call_s / 1e12
+    print(f"# headline: {ms:.4f} ms/step (median {t['median_ms']:.4f}, min {t['min_ms']:.4f}, host clock "
+          f"{t['host_ms']:.4f}), {value:.3e} upd/s, {hbm_gbs:.0f} GB/s; device copy {copy_gbs:.0f} GB/s",
+          file=sys.stderr, flush=True)
+    c = HEADLINE
     line = {
         "metric": "scan state-updates/s + achieved HBM GB/s (% of peak), fwd, 1 MI355X",
         "value": value,
@@ -445,31 +658,49 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "median_ms_per_step": t["median_ms"],
+        "min_ms_per_step": t["min_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "multi-scale selective scan, B=4 L=2048 D=1536 N=16, 4 scales, bf16 in, "
-                               "fp32 state and out, softplus dt, skip D=1, silu(z) gate",
-                   "B": 4, "L": 2048, "D": 1536, "N": 16, "input_dtype": "bf16", "output_dtype": "f32"},
+        "config": {"workload": "packed variable-length multi-scale selective scan, L=131072 tokens in 32 sequences "
+                               "(lengths log-uniform in [512, 16384], rescaled to sum to L; state reset at each "
+                               "start), D=4096, N=16, 4 scales, bf16 in, fp32 state and out, softplus dt, skip D=1, "
+                               "silu(z) gate",
+                   "L": c["L"], "nseq": c["nseq"], "D": c["D"], "N": c["N"], "input_dtype": "bf16",
+                   "output_dtype": "f32"},
         "hbm": {"achieved_gbs": hbm_gbs, "peak_gbs": HBM_PEAK_GBS, "frac": hbm_gbs / HBM_PEAK_GBS,
-                "algorithmic_bytes": head["bytes"]},
-        "roofline": {"bound": "alu", "achieved": achieved_tflops, "peak": FP32_SCALAR_FMA_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved_tflops / FP32_SCALAR_FMA_TFLOPS,
-                     "peak_basis": "fp32 FMA without packed instructions: 256 CU x 64 lanes x 2 flop x 2.4 GHz; "
-                                   "published 157.3 counts packed FMA",
-                     "published_peak": FP32_VECTOR_TFLOPS,
-                     "traffic": profiled_traffic("selective_scan_B4_L2048_D1536_N16.md",
-                                                 ["selective_state_space_diag_amd/csrc/selective.hip",
-                                                  "selective_state_space_diag_amd/csrc/common.hpp"]),
-                     "kernel": "selective scan call: aggregate + carry + scan kernels",
-                     "flops_per_update": SELECTIVE_FLOPS_PER_UPDATE, "ms_per_call": ms},
+                "algorithmic_bytes": head["bytes"], "device_copy_gbs": copy_gbs,
+                "frac_of_device_copy": hbm_gbs / copy_gbs},
+        "roofline": {"bound": "hbm", "achieved": hbm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": hbm_gbs / HBM_PEAK_GBS,
+                     "traffic": profiled_traffic("selective_varlen_L131072_D4096_N16.md", HEADLINE_KERNELS),
+                     "kernel": "one packed varlen selective scan call (its kernels, back to back)",
+                     "algorithmic_bytes_per_call": head["bytes"], "ms_per_call": ms,
+                     "median_ms_per_call": t["median_ms"], "min_ms_per_call": t["min_ms"],
+                     "frac_of_device_copy": hbm_gbs / copy_gbs,
+                     "alu": {"achieved_tflops": alu_tflops, "flops_per_update": SELECTIVE_FLOPS_PER_UPDATE,
+                             "frac_of_published_fp32": alu_tflops / FP32_VECTOR_TFLOPS,
+                             "frac_of_non_packed_fma": alu_tflops / FP32_SCALAR_FMA_TFLOPS,
+                             "published_peak_tflops": FP32_VECTOR_TFLOPS,
+                             "non_packed_peak_tflops": FP32_SCALAR_FMA_TFLOPS}},
     }
+    if args.only == "headline":
+        print(json.dumps(line), flush=True)
+        return
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(host_inputs)
+        line["cpu_baseline"] = cpu_baseline(head)
+        print(f"# cpu_baseline: {line['cpu_baseline']['value']:.3e} upd/s on {line['cpu_baseline']['cores']} "
+              f"threads ({line['cpu_baseline']['single_thread_value']:.3e} on one)", file=sys.stderr, flush=True)
+    del head
+    torch.cuda.empty_cache()
     if not args.no_forms:
-        line["forms"] = forms(args, device)
+        forms = {}
+        for name in FORMS:
+            forms.update(run_form(name, args, device))
+        line["forms"] = forms
     print(json.dumps(line), flush=True)
 
 

@@ -199,6 +199,21 @@ __device__ __forceinline__ float softplus_f(float v) {
   return v > 20.0f ? v : r;
 }
 
+// softplus for bf16 inputs: log(1 + e^v) from the hardware exp2 and log2 alone, identity above 20.
+// Forming 1 + e^v rounds away up to 2^-24 of absolute value, i.e. 2^-24 / e^v of the result in relative
+// terms (6e-5 at delta = 1e-3, the smallest step of the selective workloads; below e^v = 2^-24 the step
+// rounds to 0 where it is under 6e-8).  A bf16 dt is itself only known to 2^-9 of its value, which moves
+// delta by about |dt| 2^-9 in relative terms, 30 to 200 times more; softplus_f's exponent and log1p
+// corrections are kept for fp32 inputs.
+__device__ __forceinline__ float softplus_plain_f(float v) {
+  const float r = hw_log2(1.0f + hw_exp2(v * kLog2e)) * kLn2;
+  return v > 20.0f ? v : r;
+}
+
+// The softplus a kernel with input type Tin uses (see softplus_plain_f).
+template <typename Tin> __device__ __forceinline__ float softplus_in(float v) { return softplus_f(v); }
+template <> __device__ __forceinline__ float softplus_in<bf16_t>(float v) { return softplus_plain_f(v); }
+
 // 1 - 2^x for x <= 0, accurate also near x = 0 (where 1 - 2^x cancels): for |x ln2| < 0.25 the
 // Taylor series of -expm1 to degree 6 (truncation < 5e-8 relative), else 1 - 2^x directly.
 __device__ __forceinline__ float one_minus_exp2x(float x) {

@@ -135,10 +135,10 @@ struct BCStage {
 enum Disc { kClamp = 0, kExp = 1 };
 
 // One row of one channel: discretise, advance the N states, optionally read out.
-template <int NS, bool SOFTPLUS, int DISC, bool READOUT, bool GATE>
+template <typename Tin, int NS, bool SOFTPLUS, int DISC, bool READOUT, bool GATE>
 __device__ __forceinline__ float row_step(float xx, float dd, float zz, const float* bc, const float* A2, float dskip,
                                           float* h, float* e, float& sum_delta) {
-  const float delta = SOFTPLUS ? softplus_f(dd) : dd;
+  const float delta = SOFTPLUS ? softplus_in<Tin>(dd) : dd;
   const float dx = delta * xx;
   float acc = 0.0f;
 #pragma unroll
@@ -225,7 +225,7 @@ __device__ __forceinline__ void run_rows(const SelParams& p, int64_t row0, int64
 #pragma unroll
           for (int q = 0; q < PR; ++q) bc[q] = cur[(i - r_begin) * PR + q];
         }
-        const float y = row_step<NS, SOFTPLUS, DISC, READOUT, GATE>(xx, dd, zz, bc, A2, dskip, h, e, sum_delta);
+        const float y = row_step<Tin, NS, SOFTPLUS, DISC, READOUT, GATE>(xx, dd, zz, bc, A2, dskip, h, e, sum_delta);
         if (READOUT) win<Tout, 1>::store(wy, lane_out, (uint32_t)i * row_out, &y);
         // keep rows in program order so the B / C of later rows are not all read into registers early
         __builtin_amdgcn_sched_barrier(0);
@@ -239,7 +239,7 @@ __device__ __forceinline__ void run_rows(const SelParams& p, int64_t row0, int64
         float bc[PR];
 #pragma unroll
         for (int q = 0; q < PR; ++q) bc[q] = cur[(i - r_begin) * PR + q];
-        const float y = row_step<NS, SOFTPLUS, DISC, READOUT, GATE>(
+        const float y = row_step<Tin, NS, SOFTPLUS, DISC, READOUT, GATE>(
             W::get(rx[k], 0), W::get(rd[k], 0) + bias, GATE ? W::get(rz[k], 0) : 0.0f, bc, A2, dskip, h, e,
             sum_delta);
         if (READOUT) win<Tout, 1>::store(wy, lane_out, (uint32_t)i * row_out, &y);
@@ -434,7 +434,7 @@ __global__ __launch_bounds__(kThreads) void selective_update_kernel(
   const int64_t b = idx / D;
   const int64_t d = idx - b * D;
   float dd = io<Tin>::load(dt, idx) + (dt_bias ? dt_bias[d] : 0.0f);
-  const float delta = SOFTPLUS ? softplus_f(dd) : dd;
+  const float delta = SOFTPLUS ? softplus_in<Tin>(dd) : dd;
   const float xx = io<Tin>::load(x, idx);
   const float dx = delta * xx;
   float acc = 0.0f;
@@ -711,7 +711,7 @@ __global__ __launch_bounds__(kThreads) void selective_bwd_agg_kernel(SelBwdParam
     const float v = W::get(W::load(wdt, lane_in, ro), 0) + bias;
     const float dyv = W::get(W::load(wdy, lane_in, ro), 0);
     const float g = GATE ? silu_acc_f(W::get(W::load(wzz, lane_in, ro), 0)) : 1.0f;
-    delta[t] = t < R ? (SOFTPLUS ? softplus_f(v) : v) : 0.0f;  // rows past the sequence: identity
+    delta[t] = t < R ? (SOFTPLUS ? softplus_in<Tin>(v) : v) : 0.0f;  // rows past the sequence: identity
     ds[t] = t < R ? dyv * g : 0.0f;
   }
   __syncthreads();
@@ -798,7 +798,7 @@ __global__ __launch_bounds__(kThreads) void selective_bwd_kernel(SelBwdParams p)
     const float xx = ld(wxx, t);
     const float dyv = ld(wdy, t);
     const float g = GATE ? silu_acc_f(ld(wzz, t)) : 1.0f;
-    delta[t] = ok ? (SOFTPLUS ? softplus_f(v) : v) : 0.0f;
+    delta[t] = ok ? (SOFTPLUS ? softplus_in<Tin>(v) : v) : 0.0f;
     dx_[t] = delta[t] * (ok ? xx : 0.0f);
     ds[t] = ok ? dyv * g : 0.0f;
   }
