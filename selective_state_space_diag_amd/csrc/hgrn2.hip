@@ -4,8 +4,8 @@
 //   g_i = lb + (1 - lb) sigmoid(g_logit_i),  S[i][j] = g_i S[i][j] + v_i k_j,  o_i = sum_j S[i][j] q_j.
 // The gate scales row i of S (the value index); rows evolve independently of each other.
 //
-// The chunked MFMA form below takes bf16 inputs with d = 128 and lower bounds >= 2^-1.5; the other
-// cases run the row-gated register sweep of hgrn2_sweep.hip.
+// The chunked MFMA form below takes bf16 inputs with d = 128 and any lower bound; the other cases
+// (fp32 inputs, other head dims) run the row-gated register sweep of hgrn2_sweep.hip.
 #include "common.hpp"
 #include "h2_layout.hpp"
 #include "kernels.hpp"
@@ -61,8 +61,13 @@ __global__ __launch_bounds__(256) void hgrn2_update_kernel(int64_t rows, int64_t
 // accumulation.  Q, K are bf16 inputs and enter exactly; every derived operand (Q K^T, W, the state
 // copy) is split into a bf16 pair hi + lo, so its products carry about 16 significant bits instead
 // of 8; the state S itself stays in fp32 accumulators for the whole sequence.
-// Gamma_C >= lower_bound^64 must stay far from underflow: the launcher uses this form only for
-// lower_bound >= 2^-1.5 (Gamma_C >= 2^-96); smaller bounds take the register sweep.
+// The products above need Gamma_C far from underflow: W would lose the early tokens of a chunk and
+// O divides by Gamma_C.  Every chunk checks Gamma_C >= 2^-96 for all value rows of the workgroup
+// (always true for lower_bound >= 2^-1.5, and for gates drawn away from saturation at any lower
+// bound: 64 tokens would need an average gate below 2^-1.5).  A chunk that fails the check (gates
+// saturated near 0, NaN gates) is processed token by token instead: the workgroup reloads the chunk's
+// values and gate logits into LDS and applies S = diag(g) S + v k^T and o = S q to the fp32 state
+// it holds in its accumulators, one token at a time; no ratio of gate products is formed there.
 //
 // Workgroup = (batch, head, half of the 128 value rows), 8 waves.  Wave (r, h) (r = wave % 4,
 // h = wave / 4) owns value rows i in [16r, 16r+16) of the half, the state columns j of tiles
@@ -128,7 +133,17 @@ struct H2Lds {
   uint2 qk[10][2][64];             // causal Q K^T tiles (st <= tt) as bf16 pairs: [tile][hi, lo][lane]
   uint16_t gstage[kCh * kRows];    // next chunk's gate logits and values [t][i] (gv layout)
   uint16_t vstage[kCh * kRows];
+  // per chunk parity: first token of each row with a non-finite gate or value, then a flag that some row has one
+  int nanpos[2][kRows + 4];
 };
+
+// The token-by-token path of a chunk that fails the Gamma_C check reuses LDS that the products of that
+// chunk do not touch: the chunk's values and gate logits go to w and w_lo (row-major [t][i]), and the
+// two state halves' partial readouts to gam (half 0) and sx (half 1), as [t][i] fp32.
+constexpr float kGammaFloor = 0x1p-96f;
+static_assert(sizeof(float) * kCh * kRows <= sizeof(H2Lds::gam), "partial readouts of half 0 fit in gam");
+static_assert(sizeof(float) * kCh * kRows <= sizeof(H2Lds::sx), "partial readouts of half 1 fit in sx");
+static_assert(sizeof(uint16_t) * kCh * kRows <= sizeof(H2Lds::w), "the chunk's values fit in w");
 
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 // Transposing LDS read: in each 16-lane group, lane 4b + c passes the address of 4 consecutive
@@ -189,8 +204,14 @@ __device__ __forceinline__ void h2_stage_gates(H2Lds& sm, int tid, const H2GateP
 // Gates, part 1: thread (column gi = lane, token group gp = wave) reads its 8 staged gate logits and
 // values (two transposing reads each), forms g = lb + (1 - lb) sigmoid(logit) (1 past the chunk's
 // valid tokens) and its running products, and publishes the group product.
+// A NaN gate or a non-finite value would reach the chunk's earlier outputs of its row through the
+// products (which divide by Gamma_C, and multiply masked-out entries, zeros, by W).  GUARD: the gate is
+// made NaN, so Gamma_C fails the check and the chunk goes token by token.  Otherwise the gate becomes 1
+// and the value 0 (the products stay finite and exact for the tokens before it) and the token is
+// recorded in nanpos, from which the row's outputs and its state are set to NaN.
+template <bool GUARD>
 __device__ __forceinline__ void h2_gate1(H2Lds& sm, int lane, int gp, int valid, float lb, float one_m_lb,
-                                         float (&gam_run)[kGateTok], float (&vv)[kGateTok]) {
+                                         float (&gam_run)[kGateTok], float (&vv)[kGateTok], int* nanpos) {
   const int o0 = h2::gv_gate_off(lane & 15, lane >> 4, gp, 0), o1 = h2::gv_gate_off(lane & 15, lane >> 4, gp, 1);
   const uint2 g0 = lds_tr(&sm.gstage[o0]), g1 = lds_tr(&sm.gstage[o1]);
   const uint2 v0 = lds_tr(&sm.vstage[o0]), v1 = lds_tr(&sm.vstage[o1]);
@@ -201,6 +222,25 @@ __device__ __forceinline__ void h2_gate1(H2Lds& sm, int lane, int gp, int valid,
     const float glog = (u & 1) ? bf16_hi(gw[u >> 1]) : bf16_lo(gw[u >> 1]);
     gv[u] = fmaf(one_m_lb, sigmoid_f(glog), lb);
     vv[u] = (u & 1) ? bf16_hi(vw[u >> 1]) : bf16_lo(vw[u >> 1]);
+  }
+  // z = sum of x * 0 over the gates and values is NaN exactly when one of them is not finite
+  float z = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kGateTok; ++u) z = fmaf(gv[u], 0.0f, fmaf(vv[u], 0.0f, z));
+  if (z != z) {
+#pragma unroll
+    for (int u = 0; u < kGateTok; ++u) {
+      if (!(__builtin_isfinite(gv[u]) && __builtin_isfinite(vv[u]))) {
+        if (GUARD) {
+          gv[u] = __builtin_nanf("");
+        } else {
+          gv[u] = 1.0f;
+          vv[u] = 0.0f;
+          atomicMin(&nanpos[lane], gp * kGateTok + u);
+          nanpos[kRows] = 1;  // the slot's anybad flag (laid out right after its rows)
+        }
+      }
+    }
   }
   if (valid < kCh) {  // ragged last chunk: tokens past it leave the state unchanged
 #pragma unroll
@@ -363,7 +403,95 @@ __device__ __forceinline__ void h2_out(__amdgpu_buffer_rsrc_t wo, uint32_t row_b
   }
 }
 
+// One chunk token by token (the chunk failed the Gamma_C check).  Wave (rt, half_t) holds S^T[j][i] for
+// j = 16 (4 half_t + q) + 4 lg + r and i = iw + l16; per token it applies S[i][j] = g_i S[i][j] + v_i k_j
+// to those entries and sums S[i][j] q_j over them, then over the wave's lane groups; the two halves of j
+// meet in LDS after the chunk.  Reads Q and K from the chunk's tiles, loads the chunk's values and gate
+// logits itself.  Called by every thread of the workgroup, after a barrier that follows the last use of
+// w, w_lo, gam and sx by the chunk's own products (none here), and ends with a barrier.
+// (Out of line, with the state passed and returned by value: the rare path then costs the main loop no
+// registers, and the state stays in registers there.)
+struct H2State {
+  floatx4_t q[4];
+};
 template <typename Tout>
+__device__ __forceinline__ H2State h2_chunk_tokens(const H2Params& p, H2Lds& sm, const uint16_t* Qs, const uint16_t* Ks,
+                                                int64_t b, int64_t hh, int i0, int64_t t0, int valid, int tid,
+                                                int half_t, int iw, float lb, float one_m_lb, H2State S) {
+  const int lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
+  // the chunk's gate logits and values, row-major [t][i] over the workgroup's 64 value rows
+  {
+    H2GatePrefetch f;
+    h2_fetch_gates(p, b, hh, i0, t0, tid, f);
+    const int t = tid >> 3, c0 = 8 * (tid & 7);
+    *reinterpret_cast<v4i_t*>(&sm.w_lo[t * kRows + c0]) = f.g;
+    *reinterpret_cast<v4i_t*>(&sm.w[t * kRows + c0]) = f.v;
+  }
+  __syncthreads();
+  float* part = half_t ? reinterpret_cast<float*>(&sm.sx[0][0][0][0][0]) : &sm.gam[0][0];
+  const int i = iw + l16;
+#pragma unroll 1
+  for (int t = 0; t < valid; ++t) {
+    const float g = fmaf(one_m_lb, sigmoid_f(bf16_to_f32(sm.w_lo[t * kRows + i])), lb);
+    const float v = bf16_to_f32(sm.w[t * kRows + i]);
+    float acc = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int j0 = 16 * (4 * half_t + q) + 4 * lg;
+      const uint2 kk = *reinterpret_cast<const uint2*>(&Ks[qk_off(t, j0)]);
+      const uint2 qq = *reinterpret_cast<const uint2*>(&Qs[qk_off(t, j0)]);
+      const float kj[4] = {bf16_lo(kk.x), bf16_hi(kk.x), bf16_lo(kk.y), bf16_hi(kk.y)};
+      const float qj[4] = {bf16_lo(qq.x), bf16_hi(qq.x), bf16_lo(qq.y), bf16_hi(qq.y)};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        S.q[q][r] = fmaf(g, S.q[q][r], v * kj[r]);
+        acc = fmaf(S.q[q][r], qj[r], acc);
+      }
+    }
+    acc += __shfl_xor(acc, 16);
+    acc += __shfl_xor(acc, 32);
+    if (lg == 0) part[t * kRows + i] = acc;
+  }
+  __syncthreads();
+  // o[t][i] = half 0 + half 1, 8 outputs per thread
+  const float* p0 = &sm.gam[0][0];
+  const float* p1 = reinterpret_cast<const float*>(&sm.sx[0][0][0][0][0]);
+  const auto wo = h2_out_window<Tout>(p, b, hh, i0, t0, valid);
+  const uint32_t row_bytes = (uint32_t)(p.H * kDh * (int64_t)sizeof(Tout));
+#pragma unroll 1
+  for (int e = 0; e < kCh * kRows / (kWaves * 64); ++e) {
+    const int idx = e * kWaves * 64 + tid;
+    const int t = idx >> 6, ii = idx & 63;
+    if (t < valid) {
+      const float o = p0[t * kRows + ii] + p1[t * kRows + ii];
+      win<Tout, 1>::store(wo, (uint32_t)(ii * (int)sizeof(Tout)), (uint32_t)t * row_bytes, &o);
+    }
+  }
+  __syncthreads();  // gam and sx are written again by the next chunk
+  return S;
+}
+
+// NaN over the outputs of this wave's tiles (rows iw .. iw + 15, its two token tiles) at or after the first
+// non-finite token of their row (nanpos; kCh where there is none).
+template <typename Tout>
+__device__ __forceinline__ void h2_out_nan(__amdgpu_buffer_rsrc_t wo, uint32_t row_bytes, const int* nanpos, int iw,
+                                        int lane, int half_t) {
+  const float qnan = __builtin_nanf("");
+#pragma unroll 1
+  for (int a = 0; a < 2; ++a) {
+    const int tt = half_t ? (a ? 2 : 1) : (a ? 3 : 0);
+#pragma unroll 1
+    for (int e = lane; e < 16 * 16; e += 64) {
+      const int t = 16 * tt + (e >> 4), i = iw + (e & 15);
+      if (t >= nanpos[i]) win<Tout, 1>::store(wo, (uint32_t)(i * (int)sizeof(Tout)), (uint32_t)t * row_bytes, &qnan);
+    }
+  }
+}
+
+// GUARD: the Gamma_C check and the token-by-token path are compiled in.  Lower bounds >= 2^-1.5 cannot
+// fail the check (Gamma_C >= lower_bound^64 >= 2^-96) and take the instantiation without them, whose
+// main loop keeps its registers to itself.
+template <typename Tout, bool GUARD>
 __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
   __shared__ H2Lds sm;
   const int tid = threadIdx.x;
@@ -405,8 +533,9 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
   h2_fetch_gates(p, b, hh, i0, 0, tid, fg);
   h2_stage_gates(sm, tid, fg);
   if (nchunks > 1) h2_fetch_gates(p, b, hh, i0, kCh, tid, fg);
+  if (tid < 2 * (kRows + 4)) sm.nanpos[tid / (kRows + 4)][tid % (kRows + 4)] = tid % (kRows + 4) < kRows ? kCh : 0;
   __syncthreads();
-  h2_gate1(sm, tid & 63, wave, (int)min((int64_t)kCh, p.L), lb, one_m_lb, gam_run, vv);
+  h2_gate1<GUARD>(sm, tid & 63, wave, (int)min((int64_t)kCh, p.L), lb, one_m_lb, gam_run, vv, sm.nanpos[0]);
   for (int64_t c = 0; c < nchunks; ++c) {
     // Per-lane LDS addresses are loop-invariant and stay in registers across chunks: the LDS use
     // already limits the kernel to two waves per SIMD, so the registers they take are free.
@@ -466,7 +595,11 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
         pre *= q2 < gp ? gq[q2] : 1.0f;
         all *= gq[q2];
       }
-      if (gp == 0) sm.gcol[gi] = all;
+      if (gp == 0) {
+        sm.gcol[gi] = all;
+        sm.nanpos[(c + 1) & 1][gi] = kCh;  // the slot of chunk c - 1, free since the first barrier
+        if (gi == 0) sm.nanpos[(c + 1) & 1][kRows] = 0;
+      }
       const int xg = h2::vw_gate_lane(gi, gp);
 #pragma unroll
       for (int u = 0; u < kGateTok; u += 2) {
@@ -493,12 +626,33 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
     }
     __syncthreads();  // Gamma, W, Gamma_C, Q K^T tiles visible
 
+    // ---- a chunk whose decay over the chunk underflows the products' range goes token by token
+    if (GUARD && !__all(sm.gcol[lane] >= kGammaFloor)) {
+      H2State st{{S[0], S[1], S[2], S[3]}};
+      st = h2_chunk_tokens<Tout>(p, sm, Qs, Ks, b, hh, i0, t0, valid, tid, half_t, iw, lb, one_m_lb, st);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) S[q] = st.q[q];
+      if (c + 1 < nchunks)
+        h2_gate1<GUARD>(sm, lane, gp, (int)min((int64_t)kCh, p.L - t0 - kCh), lb, one_m_lb, gam_run, vv,
+                        sm.nanpos[(c + 1) & 1]);
+      continue;
+    }
+
     // ---- O^T for this half's token tiles
     {
       const auto wo = h2_out_window<Tout>(p, b, hh, i0, t0, valid);
       const uint32_t row_bytes = (uint32_t)(p.H * kDh * (int64_t)sizeof(Tout));
       if (half_t == 0) h2_out<0, Tout>(wo, row_bytes, sm, iw, lane, os);
       else h2_out<1, Tout>(wo, row_bytes, sm, iw, lane, os);
+      // a non-finite gate or value: its row reads NaN from that token on (this wave's outputs again), and
+      // so does its state (NaN stays NaN through the state update below)
+      if (!GUARD && __builtin_amdgcn_readfirstlane(sm.nanpos[c & 1][kRows]) != 0) {
+        h2_out_nan<Tout>(wo, row_bytes, sm.nanpos[c & 1], iw, lane, half_t);
+        if (sm.nanpos[c & 1][iw + l16] < kCh) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) S[q] = floatx4_t{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+        }
+      }
     }
 
     // ---- state update on this wave's tiles: S^T = S^T Gamma_C[i] + K^T W  (slots s = 32 ks + 8 lg + e)
@@ -528,7 +682,9 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
       }
     }
     // ---- gate part 1 of the next chunk (its inputs were staged before the last barrier)
-    if (c + 1 < nchunks) h2_gate1(sm, lane, gp, (int)min((int64_t)kCh, p.L - t0 - kCh), lb, one_m_lb, gam_run, vv);
+    if (c + 1 < nchunks)
+      h2_gate1<GUARD>(sm, lane, gp, (int)min((int64_t)kCh, p.L - t0 - kCh), lb, one_m_lb, gam_run, vv,
+                      sm.nanpos[(c + 1) & 1]);
   }
 
   if (p.S_last) {
@@ -548,17 +704,22 @@ hipError_t launch_hgrn2_scan(const Hgrn2ScanArgs& a, hipStream_t s) {
   p.B = a.B; p.L = a.L; p.H = a.H; p.d = a.d;
   p.q = a.q; p.k = a.k; p.v = a.v; p.g = a.g_logit; p.lb = a.lower_bound;
   p.S0 = a.S0; p.o = a.o; p.S_last = a.S_last;
-  // chunked MFMA form: bf16 inputs, d = 128, lower_bound >= 2^-1.5 (see hgrn2_chunk_kernel); a
-  // chunk's rows of one head span under 2^31 bytes (buffer windows) for H < 2^16
-  if (a.in_bf16 && a.d == kDh && a.lower_bound >= 0.35355339f && a.H < 65536) {
+  // chunked MFMA form: bf16 inputs, d = 128, any lower bound (a chunk whose gate product underflows
+  // goes token by token inside it, see hgrn2_chunk_kernel); a chunk's rows of one head span under
+  // 2^31 bytes (buffer windows) for H < 2^16
+  if (a.in_bf16 && a.d == kDh && a.H < 65536) {
     const dim3 grid((unsigned)(a.B * a.H * 2));
-    if (a.out_bf16)
-      hipLaunchKernelGGL((hgrn2_chunk_kernel<bf16_t>), grid, dim3(kWaves * 64), 0, s, p);
-    else
-      hipLaunchKernelGGL((hgrn2_chunk_kernel<float>), grid, dim3(kWaves * 64), 0, s, p);
+    const bool guard = !(a.lower_bound >= 0.35355339f);  // lower_bound^64 >= 2^-96 otherwise
+    if (a.out_bf16) {
+      if (guard) hipLaunchKernelGGL((hgrn2_chunk_kernel<bf16_t, true>), grid, dim3(kWaves * 64), 0, s, p);
+      else hipLaunchKernelGGL((hgrn2_chunk_kernel<bf16_t, false>), grid, dim3(kWaves * 64), 0, s, p);
+    } else {
+      if (guard) hipLaunchKernelGGL((hgrn2_chunk_kernel<float, true>), grid, dim3(kWaves * 64), 0, s, p);
+      else hipLaunchKernelGGL((hgrn2_chunk_kernel<float, false>), grid, dim3(kWaves * 64), 0, s, p);
+    }
     return hipGetLastError();
   }
-  // other cases (smaller lower bounds, fp32 inputs, other head dims): the register sweep
+  // other cases (fp32 inputs, other head dims): the register sweep
   return launch_hgrn2_row_sweep(a, s);
 }
 

@@ -2,8 +2,9 @@
 against the fp64 oracle:
   * softplus's threshold: delta = dt + dt_bias exactly above 20 (torch's softplus), forward and gradients,
     up to arguments where e^v overflows fp32;
-  * the chunked MFMA form of HGRN2 where its numeric guard binds: lower bound just above 2^-1.5 with
-    gates saturated at the bound over whole chunks (the in-chunk decay reaches about 2^-94);
+  * the chunked MFMA form of HGRN2 where its decay check binds: gates saturated at the lower bound over
+    whole chunks, at bounds where the in-chunk decay stays above 2^-96 (just above 2^-1.5) and where it
+    does not (0.2, 0), so chunks go token by token; every chunk token by token; a NaN gate;
   * the decode steps at the benchmark shapes (HGRN2 B = 8, H = 16, d = 128 with either gate axis) and
     the selective decode step at B = 1 and with fp32 inputs.
 Tolerances as everywhere: max|err| <= tau * RMS(oracle), tau = 1e-5 (fp32 inputs) or 2e-2 (bf16)."""
@@ -121,10 +122,12 @@ def saturated_hgrn2(seed, lb=0.36, B=2, L=200, H=3):
     return inp
 
 
-@pytest.mark.parametrize("lb", [0.36, 0.354])
+@pytest.mark.parametrize("lb", [0.36, 0.354, 0.2, 0.0])
 def test_hgrn2_chunked_form_with_saturated_gates(lb):
-    """lb >= 2^-1.5 = 0.35355 with bf16 inputs and d = 128 takes the chunked MFMA form; gates saturated at
-    the bound over a chunk give in-chunk decays down to lb^64 (2^-94.3 at 0.36, 2^-95.9 at 0.354)."""
+    """bf16 inputs with d = 128 take the chunked MFMA form at any lower bound.  Gates saturated at the
+    bound over a chunk give in-chunk decays down to lb^64: 2^-94.3 at 0.36 and 2^-95.9 at 0.354 (the
+    products' range still holds), 2^-148.6 at 0.2 and about 10^-830 at 0 (the chunk goes token by token).
+    Chunk 0 has ordinary gates, so every sequence mixes the two ways through a chunk."""
     import torch
     inp = saturated_hgrn2(9400 + int(lb * 1000), lb=lb)
     t = {n: to_dev(v) for n, v in inp.t.items()}
@@ -138,6 +141,42 @@ def test_hgrn2_chunked_form_with_saturated_gates(lb):
     for b in range(o.shape[0]):
         for h in range(o.shape[2]):
             assert_close(host(o[b, :, h]), orf[b, :, h], TOL[synth.BF16], f"o head {b},{h}")
+
+
+def test_hgrn2_chunked_form_all_chunks_token_by_token():
+    """Every gate at the bound 0 (logit -30 everywhere): every chunk of every head fails the decay check;
+    with an S0 and a ragged last chunk."""
+    import torch
+    inp = synth.hgrn2_inputs(2, 64 * 3 + 9, 2, 128, synth.BF16, 9450, lower_bound=0.0, with_S0=True)
+    g = np.full(inp.t["g_logit"].shape, -30.0, dtype=np.float32)
+    g[:, :, :, 5] = 3.0  # one channel with gates near 1 keeps a long memory
+    inp.t["g_logit"] = synth.Tensor(synth.BF16, synth.f32_to_bf16_bits(g))
+    t = {n: to_dev(v) for n, v in inp.t.items()}
+    o, S = ssd.hgrn2_scan(t["q"], t["k"], t["v"], t["g_logit"], 0.0, S0=to_dev(inp.p["S0"]), return_last_state=True)
+    torch.cuda.synchronize()
+    orf, Sr = oracle.hgrn2_scan(f64(inp.t["q"]), f64(inp.t["k"]), f64(inp.t["v"]), f64(inp.t["g_logit"]), 0.0,
+                                f64(inp.p["S0"]))
+    assert_close(host(o), orf, TOL[synth.BF16], "o")
+    assert_close(host(S), Sr, TOL[synth.BF16], "S_last")
+
+
+def test_hgrn2_chunked_form_nan_gate_propagates():
+    """A NaN gate logit makes its value row NaN from that token on, as in the recurrence; other rows and
+    heads keep the oracle's values."""
+    import torch
+    inp = synth.hgrn2_inputs(1, 150, 2, 128, synth.BF16, 9460, lower_bound=0.5)
+    g = synth.bf16_to_f32(inp.t["g_logit"].data).copy()
+    g[0, 70, 1, 9] = np.nan
+    inp.t["g_logit"] = synth.Tensor(synth.BF16, synth.f32_to_bf16_bits(g))
+    t = {n: to_dev(v) for n, v in inp.t.items()}
+    o = ssd.hgrn2_scan(t["q"], t["k"], t["v"], t["g_logit"], 0.5)
+    torch.cuda.synchronize()
+    oh = host(o)
+    orf, _ = oracle.hgrn2_scan(f64(inp.t["q"]), f64(inp.t["k"]), f64(inp.t["v"]), f64(inp.t["g_logit"]), 0.5)
+    assert np.all(np.isnan(oh[0, 70:, 1, 9])) and np.all(np.isnan(orf[0, 70:, 1, 9]))
+    mask = np.ones(oh.shape, dtype=bool)
+    mask[0, 70:, 1, 9] = False
+    assert_close(oh[mask], orf[mask], TOL[synth.BF16], "o outside the NaN row")
 
 
 # ----------------------------------------------------------------------------- decode at the benchmark shapes
