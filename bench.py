@@ -44,8 +44,38 @@ FP32_SCALAR_FMA_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 BF16_MFMA_TFLOPS = 2500.0    # MI355X dense bf16 matrix, published
 
 HEADLINE = dict(L=131072, D=4096, N=16, nseq=32, scales=4, seed=1004)
-HEADLINE_KERNELS = ["selective_state_space_diag_amd/csrc/selective.hip",
-                    "selective_state_space_diag_amd/csrc/common.hpp"]
+
+_CSRC = "selective_state_space_diag_amd/csrc/"
+_SEL_SOURCES = [_CSRC + f for f in ("selective.hip", "common.hpp", "kernels.hpp")]
+_H2_SOURCES = [_CSRC + f for f in ("hgrn2.hip", "h2_layout.hpp", "common.hpp", "kernels.hpp")]
+_SCAN1_SOURCES = [_CSRC + f for f in ("scan1.hip", "common.hpp", "kernels.hpp")]
+# Workload -> (summary file under profiles/, what one call is, the kernel sources the summary's counter
+# figures hold for: a figure is used only while the sha256 of these files is the one stored with it).
+PROFILES = {
+    "headline": ("selective_varlen_L131072_D4096_N16.md",
+                 "Packed varlen selective scan, L=131072 tokens in 32 sequences, D=4096, N=16, bf16 in, fp32 out; "
+                 "one call = planner + aggregate + carry + scan kernels", _SEL_SOURCES),
+    "selective_B4_L2048_D1536_N16": ("selective_scan_B4_L2048_D1536_N16.md",
+                                     "Batched selective scan B=4 L=2048 D=1536 N=16, bf16 in, fp32 out; one call = "
+                                     "aggregate + carry + scan kernels", _SEL_SOURCES),
+    "hgrn2_bf16_B8_H16_d128_L4096": ("hgrn2_scan_B8_H16_d128_L4096.md",
+                                     "HGRN2 scan B=8 H=16 d=128 L=4096, bf16 in, fp32 out, lower bound 0.5; one call "
+                                     "= one chunked MFMA kernel", _H2_SOURCES),
+    "hgrn2_lb0_bf16_B8_H16_d128_L4096": ("hgrn2_lb0_scan_B8_H16_d128_L4096.md",
+                                         "HGRN2 scan B=8 H=16 d=128 L=4096, bf16 in, fp32 out, lower bound 0 (the "
+                                         "chunked MFMA kernel with the per-chunk decay check)", _H2_SOURCES),
+    "rglru_bf16_B8_L8192_D2560": ("rglru_scan_B8_L8192_D2560.md",
+                                  "RG-LRU scan B=8 L=8192 D=2560, bf16 in, fp32 out; one call = one lookback kernel",
+                                  _SCAN1_SOURCES),
+}
+
+
+def sources_sha256(sources):
+    import hashlib
+    h = hashlib.sha256()
+    for f in sources:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()
 
 
 # ----------------------------------------------------------------------------- algorithmic sizes
@@ -105,22 +135,23 @@ def hgrn2_bwd_bytes(B, L, H, d, in_b=2, out_b=4):
     return B * L * H * d * (5 * in_b + 4 + 4 * out_b)
 
 
-def profiled_traffic(profile, sources):
-    """HBM bytes per call recorded by rocprofv3 counter runs in profiles/<profile>, if the kernel
-    sources are unchanged since (their sha256 is stored with the figure); else None."""
-    import hashlib
+def profiled_traffic(workload):
+    """HBM bytes per call recorded by rocprofv3 counter runs in the workload's summary under profiles/,
+    if its kernel sources are unchanged since (their sha256 is stored with the figure); else None."""
     import re
-    path = os.path.join(ROOT, "profiles", profile)
+    if workload not in PROFILES:
+        return None
+    fname, _, sources = PROFILES[workload]
+    path = os.path.join(ROOT, "profiles", fname)
     if not os.path.exists(path):
         return None
     m = re.search(r"<!-- profile-data: (\{.*\}) -->", open(path).read())
     if not m:
         return None
     data = json.loads(m.group(1))
-    h = hashlib.sha256()
-    for f in sources:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    return data["traffic_bytes_per_call"] if h.hexdigest() == data["kernel_sources_sha256"] else None
+    if data.get("kernel_sources_sha256") != sources_sha256(sources):
+        return None
+    return data.get("traffic_bytes_per_call")
 
 
 # ----------------------------------------------------------------------------- timing helpers
@@ -592,9 +623,177 @@ def run_form(name, args, device):
     r = FORMS[name](args, device)
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
-    if isinstance(r, dict) and "ms" not in r:
-        return r
-    return {name: r}
+    recs = r if isinstance(r, dict) and "ms" not in r else {name: r}
+    for n, rec in recs.items():
+        if n in PROFILES:
+            rec["traffic_bytes"] = profiled_traffic(n)
+    return recs
+
+
+# ----------------------------------------------------------------------------- profile summaries
+def _csv_rows(folder, suffix):
+    import csv
+    import glob
+    for f in sorted(glob.glob(os.path.join(folder, "**", "*" + suffix), recursive=True)):
+        with open(f) as fh:
+            yield from csv.DictReader(fh)
+
+
+def _short_kernel(name):
+    """Kernel name without 'void', the library's namespaces and the parameter list."""
+    n = name.replace("void ", "", 1).replace("ssd::(anonymous namespace)::", "")
+    depth = 0
+    for i, ch in enumerate(n):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return n[:i]
+    return n
+
+
+def _last_json(path):
+    if not os.path.exists(path):
+        return None
+    rec = None
+    for line in open(path):
+        line = line.strip()
+        if line.startswith("{"):
+            try:
+                rec = json.loads(line)
+            except ValueError:
+                pass
+    return rec
+
+
+def summarize_profile(folder, workload):
+    """Markdown summary of the rocprofv3 runs of one workload in ``folder``:
+    trace/ (--kernel-trace --stats, csv) with the bench output in trace.log, pmc_FETCH_SIZE/ and
+    pmc_WRITE_SIZE/ (each run started with --copy-calibration-mb, the size printed in its log),
+    optionally pmc_SQ/ (instruction counters), and commands.txt (the commands that made them).
+    Only the library's kernels (namespace ssd) are listed.  Per-call figures count each kernel as many
+    times per call as its dispatches divided by those of the kernel with the largest total time."""
+    import re
+    fname, title, sources = PROFILES[workload]
+    lib = lambda n: "ssd::" in (n or "")
+    # durations: kernel trace and rocprofv3's own statistics
+    dur, shape = {}, {}
+    for r in _csv_rows(os.path.join(folder, "trace"), "kernel_trace.csv"):
+        n = r.get("Kernel_Name")
+        if not lib(n):
+            continue
+        dur.setdefault(n, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        shape[n] = (r.get("Grid_Size") or r.get("Grid_Size_X"), r.get("Workgroup_Size") or r.get("Workgroup_Size_X"),
+                    r.get("VGPR_Count") or r.get("Arch_VGPR_Count"), r.get("LDS_Block_Size") or r.get("LDS_Size"))
+    stats = {r["Name"]: float(r["AverageNs"]) / 1e3 for r in _csv_rows(os.path.join(folder, "trace"), "kernel_stats.csv")
+             if lib(r.get("Name"))}
+    if not dur:
+        raise SystemExit(f"no library kernels in {folder}/trace")
+    dom = max(dur, key=lambda n: sum(dur[n]))
+    mult = {n: int(round(len(v) / len(dur[dom]))) for n, v in dur.items()}
+
+    def counters(sub):
+        """{kernel: {counter: [per-dispatch value]}} and the ordered copy-kernel dispatches."""
+        per, names = {}, {}
+        for r in _csv_rows(os.path.join(folder, sub), "counter_collection.csv"):
+            d = int(r.get("Dispatch_Id") or r.get("Correlation_Id"))
+            names[d] = r.get("Kernel_Name")
+            per.setdefault(d, {}).setdefault(r["Counter_Name"], 0.0)
+            per[d][r["Counter_Name"]] += float(r["Counter_Value"])
+        out, copies = {}, []
+        for d in sorted(per):
+            n = names[d]
+            if "copyBuffer" in (n or ""):
+                copies.append(per[d])
+            for c, v in per[d].items():
+                out.setdefault(n, {}).setdefault(c, []).append(v)
+        return out, copies
+
+    med = lambda v: statistics.median(v) if v else float("nan")
+    lines = [f"# {title}", ""]
+    cmd_path = os.path.join(folder, "commands.txt")
+    if os.path.exists(cmd_path):
+        lines += ["Commands (on one MI355X, from the repository root `$REPO`; `$OUT` = an output folder):", ""]
+        lines += [f"* `{c.strip().replace('<file>.md', fname)}`" for c in open(cmd_path) if c.strip()]
+        lines += [""]
+    rec = _last_json(os.path.join(folder, "trace.log"))
+    call = None
+    if rec is not None:
+        call = rec if "metric" in rec else next(iter(rec.get("forms", {}).values()), None)
+    lines += ["## Kernel durations (kernel trace)", "",
+              "| kernel | grid threads | wg | VGPRs | LDS B | dispatches | per call | avg µs (--stats) | median µs | min µs |",
+              "|---|---|---|---|---|---|---|---|---|---|"]
+    order = sorted(dur, key=lambda n: -sum(dur[n]))
+    for n in order:
+        g, w, vg, lds = shape[n]
+        lines.append(f"| `{_short_kernel(n)}` | {g} | {w} | {vg} | {lds} | {len(dur[n])} | {mult[n]} | "
+                     f"{stats.get(n, float('nan')):.2f} | {med(dur[n]):.2f} | {min(dur[n]):.2f} |")
+    per_call_us = sum(mult[n] * stats.get(n, sum(dur[n]) / len(dur[n])) for n in dur)
+    lines += ["", f"Sum of the average kernel durations per call: {per_call_us:.1f} µs."]
+    if call is not None:
+        lines += [f"The bench's HIP-event timing of the same command: {call.get('ms_per_step', call.get('ms')) * 1e3:.1f} µs "
+                  f"per call (mean over the timed steps; median {call.get('median_ms_per_step', call.get('median_ms')) * 1e3:.1f} µs)."]
+    data = {"kernel_sources_sha256": sources_sha256(sources)}
+    # traffic
+    fetch, fcopies = counters("pmc_FETCH_SIZE")
+    write, wcopies = counters("pmc_WRITE_SIZE")
+    if fetch and write:
+        def calib(sub, copies, counter):
+            m = re.search(r"# copy calibration: (\d+) copies of (\d+) bytes", open(os.path.join(folder, sub + ".log")).read())
+            k, nbytes = int(m.group(1)), int(m.group(2))
+            kib = statistics.median(c[counter] for c in copies[:k])
+            return nbytes / (kib * 1024.0), kib, nbytes
+        ff, fkib, cb = calib("pmc_FETCH_SIZE", fcopies, "FETCH_SIZE")
+        fw, wkib, _ = calib("pmc_WRITE_SIZE", wcopies, "WRITE_SIZE")
+        lines += ["", "## HBM traffic (FETCH_SIZE and WRITE_SIZE, one counter per run)", "",
+                  f"A plain device copy of {cb} bytes run first in the same processes reads back {fkib:.0f} KiB "
+                  f"FETCH_SIZE and {wkib:.0f} KiB WRITE_SIZE per dispatch, so bytes read = FETCH_SIZE × 1024 × {ff:.3f} "
+                  f"and bytes written = WRITE_SIZE × 1024 × {fw:.3f}.", "",
+                  "| kernel | FETCH_SIZE KiB / dispatch (median) | WRITE_SIZE KiB / dispatch | read MB / dispatch | "
+                  "written MB / dispatch |", "|---|---|---|---|---|"]
+        traffic = 0.0
+        for n in order:
+            fk, wk = med(fetch.get(n, {}).get("FETCH_SIZE", [])), med(write.get(n, {}).get("WRITE_SIZE", []))
+            rd, wr = fk * 1024 * ff, wk * 1024 * fw
+            lines.append(f"| `{_short_kernel(n)}` | {fk:.1f} | {wk:.1f} | {rd / 1e6:.1f} | {wr / 1e6:.1f} |")
+            traffic += mult[n] * (rd + wr)
+        data["traffic_bytes_per_call"] = int(traffic)
+        alg = None
+        if call is not None:
+            alg = call["roofline"]["algorithmic_bytes_per_call"] if "roofline" in call else call.get("algorithmic_bytes")
+        if alg:
+            data["algorithmic_bytes_per_call"] = int(alg)
+            lines += ["", f"Algorithmic bytes per call: {int(alg):,}. Measured HBM traffic per call: {int(traffic):,} B "
+                          f"({traffic / alg:.2f}× algorithmic)."]
+    # instruction counters
+    sq, _ = counters("pmc_SQ")
+    if sq:
+        lines += ["", "## Instruction counters (one run; medians per dispatch)", "",
+                  "SQ counters are summed over the chip; GRBM_GUI_ACTIVE is summed over the 8 XCDs, so cycles = "
+                  "GRBM_GUI_ACTIVE / 8 (the implied clock is cycles / kernel duration). VALU issue = (SQ_INSTS_VALU − "
+                  "SQ_INSTS_MFMA) × 4 / (1024 SIMDs × cycles): a wave64 instruction occupies a 16-lane SIMD for 4 "
+                  "cycles (transcendentals included, which issue at a lower rate); MFMA busy = "
+                  "SQ_VALU_MFMA_BUSY_CYCLES / (1024 × cycles), rocprofv3's MfmaUtil.", "",
+                  "| kernel | waves | VALU instr | of which transcendental | MFMA instr | bf16 MFMA flops | LDS instr | "
+                  "cycles | implied GHz | VALU issue | MFMA busy |", "|---|---|---|---|---|---|---|---|---|---|---|"]
+        for n in order:
+            c = {k: med(v) for k, v in sq.get(n, {}).items()}
+            if not c:
+                continue
+            cyc = c.get("GRBM_GUI_ACTIVE", float("nan")) / 8
+            ghz = cyc / (stats.get(n, med(dur[n])) * 1e3)
+            valu, mfma = c.get("SQ_INSTS_VALU", 0.0), c.get("SQ_INSTS_MFMA", 0.0)
+            lines.append(
+                f"| `{_short_kernel(n)}` | {c.get('SQ_WAVES', 0):.0f} | {valu:.3e} | {c.get('SQ_INSTS_VALU_TRANS_F32', 0):.3e} | "
+                f"{mfma:.3e} | {c.get('SQ_INSTS_VALU_MFMA_MOPS_BF16', 0) * 512:.3e} | {c.get('SQ_INSTS_LDS', 0):.3e} | "
+                f"{cyc:.3e} | {ghz:.2f} | {100 * (valu - mfma) * 4 / (1024 * cyc):.1f} % | "
+                f"{100 * c.get('SQ_VALU_MFMA_BUSY_CYCLES', 0) / (1024 * cyc):.1f} % |")
+            data.setdefault("counters", {})[_short_kernel(n)] = {k: round(v, 1) for k, v in c.items()}
+    lines += ["", f"Kernel sources these figures hold for: {', '.join('`' + f + '`' for f in sources)} "
+                  f"(sha256 below; the bench reports the traffic only while it matches).", "",
+              "<!-- profile-data: " + json.dumps({k: v for k, v in data.items() if k != "counters"}) + " -->"]
+    return "\n".join(lines) + "\n"
 
 
 def main():
@@ -605,10 +804,15 @@ def main():
     ap.add_argument("--no-forms", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None, help="run one workload: 'headline' or a form name " + ", ".join(FORMS))
+    ap.add_argument("--summarize", metavar="DIR", default=None,
+                    help="write the markdown summary of the rocprofv3 runs of workload --only in DIR (no GPU use)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="first run a plain device-to-device tensor copy of this many MiB three times (a known-size "
                          "kernel for scaling hardware traffic counters)")
     args = ap.parse_args()
+    if args.summarize is not None:
+        sys.stdout.write(summarize_profile(args.summarize, args.only or "headline"))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build runs on a single MI355X (the scans shard with no "
               "communication across channels, sequences and heads; see DESIGN.md); use --gpus 1.", file=sys.stderr)
@@ -631,6 +835,7 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
+        print(f"# copy calibration: 3 copies of {n * 4} bytes", file=sys.stderr, flush=True)
         del src, dst
         torch.cuda.empty_cache()
 
@@ -676,7 +881,7 @@ def main():
                 "frac_of_device_copy": hbm_gbs / copy_gbs},
         "roofline": {"bound": "hbm", "achieved": hbm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": hbm_gbs / HBM_PEAK_GBS,
-                     "traffic": profiled_traffic("selective_varlen_L131072_D4096_N16.md", HEADLINE_KERNELS),
+                     "traffic": profiled_traffic("headline"),
                      "kernel": "one packed varlen selective scan call (its kernels, back to back)",
                      "algorithmic_bytes_per_call": head["bytes"], "ms_per_call": ms,
                      "median_ms_per_call": t["median_ms"], "min_ms_per_call": t["min_ms"],
