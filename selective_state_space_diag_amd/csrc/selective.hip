@@ -9,10 +9,18 @@
 //
 // Time parallelism: each sequence is cut into segments of T rows.  Pass 1 runs every segment
 // except a sequence's last from a zero state and stores its aggregate per state (P = prod abar,
-// H = end state).  Pass 2 folds the aggregates of the earlier segments of the same sequence onto
-// h0 to get its carry-in, then runs the full recurrence with the readout, skip and gate, writing
-// y (and the final state for a sequence's last segment).  No workgroup waits for another: the
-// only dependency is the kernel boundary between the passes.
+// H = end state).  A carry pass folds the aggregates of the earlier segments of the same sequence
+// onto h0, and pass 2 runs the full recurrence from that carry-in with the readout, skip and gate,
+// writing y (and the final state for a sequence's last segment).  No workgroup waits for another:
+// the only dependency is the kernel boundary between the passes.
+//
+// Packed sequences with bf16 inputs take a second plan: a sequence is scanned from its start to its
+// end by one workgroup per channel block unless it is longer than X rows (a fraction of the rows
+// each compute unit scans on average); a longer one is cut into as few equal pieces as keep them
+// within X.  Only the rows before a sequence's last piece pass through the aggregate kernel (in
+// blocks of 256 rows), the carry kernel writes the carry-in of each later piece, and the scan units
+// run longest first so that the long ones end with the rest.  For the 32-sequence benchmark shape
+// half the rows are aggregated instead of nearly all.
 //
 // When dt goes through softplus (delta >= 0) and every A of the wave is <= 0, delta*A <= 0 and
 // the clamp at 20 cannot act; that wave-uniform case skips it and forms P as 2^(A sum delta).
@@ -52,15 +60,37 @@ struct SelParams {
   float* aggH;   // [unit][N][D]  state reached from zero at the segment end
   float* carry;  // [unit][N][D]  state entering the segment
   const int2* seq_units;  // varlen: (first unit, unit count) per sequence
+  // Packed varlen forward plan (NULL for the other launches): scan units of whole sequences or of
+  // long sequences cut into a few pieces, longest first; aggregates only for the rows before a
+  // sequence's last piece.
+  const int* vcount;      // [0] scan units, [1] aggregate units
+  const int4* vscan;      // (sequence, first row in the sequence, rows, carry slot or -1)
+  const int4* vagg;       // (sequence, first row in the sequence, rows, 0)
+  const int4* vseq;       // per sequence: (first aggregate unit, aggregate units, aggregate units per
+                          //  scan piece, first carry slot)
+  int64_t nblk;           // channel blocks (the packed plan's scan grid is units x channel blocks)
 };
 
 struct Unit {
-  int64_t seq, seg, row0, row1;
+  int64_t seq, seg, row0, row1, carry;
   bool last, valid;
 };
 
 __device__ __forceinline__ Unit unit_of(const SelParams& p, int64_t u) {
   Unit r;
+  r.carry = -1;
+  if (p.vscan != nullptr) {
+    r.valid = u < (int64_t)p.vcount[0];
+    if (!r.valid) return r;
+    const int4 e = p.vscan[u];
+    r.seq = e.x;
+    r.row0 = (int64_t)p.cu[r.seq] + e.y;
+    r.row1 = r.row0 + e.z;
+    r.carry = e.w;
+    r.seg = e.w < 0 ? 0 : 1;
+    r.last = (r.row1 == (int64_t)p.cu[r.seq + 1]);
+    return r;
+  }
   if (p.cu == nullptr) {
     r.seq = u / p.nseg;
     r.seg = u - r.seq * p.nseg;
@@ -266,8 +296,16 @@ __device__ __forceinline__ int load_A(const SelParams& p, int64_t dl, float* A2)
 template <typename Tin, int NS, bool SOFTPLUS>
 __global__ __launch_bounds__(kThreads, 4) void selective_aggregate_kernel(SelParams p) {
   const int64_t u = blockIdx.x;
-  const Unit U = unit_of(p, u);
-  if (!U.valid || U.last) return;
+  Unit U;
+  if (p.vagg != nullptr) {  // packed plan: aggregate unit u (never a sequence's last rows)
+    if (u >= (int64_t)p.vcount[1]) return;
+    const int4 e = p.vagg[u];
+    U.row0 = (int64_t)p.cu[e.x] + e.y;
+    U.row1 = U.row0 + e.z;
+  } else {
+    U = unit_of(p, u);
+    if (!U.valid || U.last) return;
+  }
   const int64_t d = (int64_t)blockIdx.y * kThreads + threadIdx.x;
   const bool active = d < p.D;
   const int64_t dl = active ? d : p.D - 1;  // lanes past D recompute channel D-1, store nothing
@@ -306,10 +344,13 @@ __device__ __forceinline__ void scan_rows(const SelParams& p, const Unit& U, int
 
 template <typename Tin, typename Tout, int NS, bool SOFTPLUS>
 __global__ __launch_bounds__(kThreads) void selective_scan_kernel(SelParams p) {
-  const int64_t u = blockIdx.x;
+  // packed plan: one-dimensional grid, unit-major (a unit's channel blocks are dispatched together,
+  // longest units first); otherwise (unit, channel block)
+  const int64_t u = p.vscan ? (int64_t)blockIdx.x / p.nblk : (int64_t)blockIdx.x;
+  const int64_t cb = p.vscan ? (int64_t)blockIdx.x - u * p.nblk : (int64_t)blockIdx.y;
   const Unit U = unit_of(p, u);
   if (!U.valid) return;
-  const int64_t d = (int64_t)blockIdx.y * kThreads + threadIdx.x;
+  const int64_t d = cb * kThreads + threadIdx.x;
   const bool active = d < p.D;
   const int64_t dl = active ? d : p.D - 1;  // lanes past D recompute channel D-1 exactly
   float A2[NS];
@@ -323,8 +364,9 @@ __global__ __launch_bounds__(kThreads) void selective_scan_kernel(SelParams p) {
 #pragma unroll
     for (int n = 0; n < NS; ++n) h[n] = p.h0 ? p.h0[(U.seq * p.D + dl) * NS + n] : 0.0f;
   } else {
+    const int64_t slot = p.vscan ? U.carry : u;
 #pragma unroll
-    for (int n = 0; n < NS; ++n) h[n] = p.carry[(u * NS + n) * p.D + dl];
+    for (int n = 0; n < NS; ++n) h[n] = p.carry[(slot * NS + n) * p.D + dl];
   }
   float sum_delta = 0.0f;
   __shared__ float lds[2 * BCStage<NS, true>::PER_BLOCK];
@@ -378,6 +420,156 @@ __global__ __launch_bounds__(kThreads) void selective_carry_kernel(SelParams p) 
       const int64_t s = s0 + q;
       if (s > 0 && s < count) p.carry[((first + s) * NS + n) * p.D + d] = h;
       if (s + 1 < count) h = fmaf(P[q], h, H[q]);  // a sequence's last segment has no aggregate
+    }
+  }
+}
+
+// Packed plan: one thread per (sequence, state n, channel d) folds the sequence's aggregate units in
+// order from h0 (or zero) and writes the state after every q of them: the carry of the next piece.
+template <int NS>
+__global__ __launch_bounds__(kThreads) void selective_vcarry_kernel(SelParams p) {
+  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t per_seq = NS * p.D;
+  const int64_t seq = gid / per_seq;
+  if (seq >= p.nseq) return;
+  const int64_t e = gid - seq * per_seq;  // n * D + d
+  const int64_t n = e / p.D;
+  const int64_t d = e - n * p.D;
+  const int4 info = p.vseq[seq];
+  const int64_t first = info.x, count = info.y, q = info.z, cfirst = info.w;
+  if (count == 0) return;
+  float h = p.h0 ? p.h0[(seq * p.D + d) * NS + n] : 0.0f;
+  int64_t in_piece = 0, piece = 0;
+  constexpr int K = 32;
+  for (int64_t s0 = 0; s0 < count; s0 += K) {
+    float P[K], H[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int64_t idx = ((first + min(s0 + k, count - 1)) * NS + n) * p.D + d;
+      P[k] = p.aggP[idx];
+      H[k] = p.aggH[idx];
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      if (s0 + k < count) {
+        h = fmaf(P[k], h, H[k]);
+        if (++in_piece == q) {
+          in_piece = 0;
+          p.carry[((cfirst + piece) * NS + n) * p.D + d] = h;
+          ++piece;
+        }
+      }
+    }
+  }
+}
+
+// Pieces of a packed sequence of `len` rows: unsplit up to X rows, else cut into pieces of a
+// multiple of Y rows (all but the last full), as few as keep them within X.
+struct Pieces {
+  int64_t len, piece, count;  // rows, rows of every piece but the last, pieces
+};
+__device__ __forceinline__ Pieces pieces_of(int64_t len, int64_t X, int64_t Y) {
+  Pieces r;
+  r.len = len;
+  if (len <= X) {
+    r.piece = len;
+    r.count = len > 0 ? 1 : 0;
+    return r;
+  }
+  const int64_t p = (len + X - 1) / X;
+  r.piece = ((len + p - 1) / p + Y - 1) / Y * Y;
+  r.count = (len + r.piece - 1) / r.piece;
+  return r;
+}
+
+constexpr int kLenBuckets = 256;  // scan units are ordered by floor(8 log2(rows)), longest first
+__device__ __forceinline__ int len_bucket(int64_t rows) {
+  const int b = (int)(8.0f * __builtin_amdgcn_logf((float)rows));
+  return b < 0 ? 0 : (b >= kLenBuckets ? kLenBuckets - 1 : b);
+}
+
+// Inclusive sum over the 1024 threads of the workgroup (all threads must call it).
+__device__ __forceinline__ int block_inclusive_sum(int v, int* buf) {
+  buf[threadIdx.x] = v;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int add = threadIdx.x >= off ? buf[threadIdx.x - off] : 0;
+    __syncthreads();
+    buf[threadIdx.x] += add;
+    __syncthreads();
+  }
+  const int r = buf[threadIdx.x];
+  __syncthreads();
+  return r;
+}
+
+// Packed plan, one workgroup: per-sequence table, aggregate units (Y rows each, every row before a
+// sequence's last piece), scan units ordered by length (longest first; the order among units of
+// one length bucket is not fixed, and no result depends on it), the unit counts, and the final state
+// of zero-length sequences (= their initial state, or zero).
+__global__ __launch_bounds__(1024) void selective_vplan_kernel(const int32_t* cu, int64_t nseq, int64_t X, int64_t Y,
+                                                               int* count, int4* scan, int4* agg, int4* seqtab,
+                                                               int64_t D, int64_t N, const float* h0, float* h_last) {
+  __shared__ int s_buf[1024];
+  __shared__ int s_hist[kLenBuckets];
+  __shared__ int s_base_agg, s_base_carry, s_units;
+  for (int b = threadIdx.x; b < kLenBuckets; b += 1024) s_hist[b] = 0;
+  if (threadIdx.x == 0) { s_base_agg = 0; s_base_carry = 0; s_units = 0; }
+  __syncthreads();
+  // pass 1: slots, per-sequence table, aggregate units, length histogram of the scan units
+  for (int64_t blk = 0; blk < nseq; blk += 1024) {
+    const int64_t sq = blk + threadIdx.x;
+    Pieces pc{0, 0, 0};
+    if (sq < nseq) pc = pieces_of((int64_t)cu[sq + 1] - cu[sq], X, Y);
+    const int q = pc.count > 1 ? (int)(pc.piece / Y) : 1;
+    const int nagg = pc.count > 1 ? (int)((pc.count - 1) * q) : 0;
+    const int ncarry = pc.count > 1 ? (int)(pc.count - 1) : 0;
+    const int ia = block_inclusive_sum(nagg, s_buf);
+    const int ic = block_inclusive_sum(ncarry, s_buf);
+    const int iu = block_inclusive_sum((int)pc.count, s_buf);
+    const int first_agg = s_base_agg + ia - nagg, first_carry = s_base_carry + ic - ncarry;
+    if (sq < nseq) {
+      seqtab[sq] = make_int4(first_agg, nagg, q, first_carry);
+      for (int j = 0; j < nagg; ++j) agg[first_agg + j] = make_int4((int)sq, (int)(j * Y), (int)Y, 0);
+      for (int64_t k = 0; k < pc.count; ++k) {
+        const int64_t rows = k + 1 < pc.count ? pc.piece : pc.len - k * pc.piece;
+        atomicAdd(&s_hist[len_bucket(rows)], 1);
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x == 1023) { s_base_agg += ia; s_base_carry += ic; s_units += iu; }
+    __syncthreads();
+  }
+  // bucket offsets, longest bucket first: thread t holds bucket kLenBuckets - 1 - t
+  {
+    const int b = kLenBuckets - 1 - (int)threadIdx.x;
+    const int c = b >= 0 ? s_hist[b] : 0;
+    const int incl = block_inclusive_sum(c, s_buf);
+    if (b >= 0) s_hist[b] = incl - c;
+    __syncthreads();
+  }
+  // pass 2: scan units into their buckets
+  for (int64_t blk = 0; blk < nseq; blk += 1024) {
+    const int64_t sq = blk + threadIdx.x;
+    if (sq < nseq) {
+      const Pieces pc = pieces_of((int64_t)cu[sq + 1] - cu[sq], X, Y);
+      const int first_carry = seqtab[sq].w;
+      for (int64_t k = 0; k < pc.count; ++k) {
+        const int64_t rows = k + 1 < pc.count ? pc.piece : pc.len - k * pc.piece;
+        const int pos = atomicAdd(&s_hist[len_bucket(rows)], 1);
+        scan[pos] = make_int4((int)sq, (int)(k * pc.piece), (int)rows, k == 0 ? -1 : first_carry + (int)k - 1);
+      }
+    }
+  }
+  if (threadIdx.x == 0) {
+    count[0] = s_units;
+    count[1] = s_base_agg;
+  }
+  if (h_last) {
+    for (int64_t sq = 0; sq < nseq; ++sq) {
+      if (cu[sq + 1] != cu[sq]) continue;
+      for (int64_t e = threadIdx.x; e < D * N; e += 1024)
+        h_last[sq * D * N + e] = h0 ? h0[sq * D * N + e] : 0.0f;
     }
   }
 }
@@ -502,6 +694,22 @@ hipError_t launch_by_n(const SelParams& p, int64_t U, bool softplus, hipStream_t
 }
 
 template <typename Tin, typename Tout, int NS>
+hipError_t launch_packed(const SelParams& p, int64_t A, int64_t S, bool softplus, hipStream_t s) {
+  const dim3 agrid((unsigned)A, (unsigned)p.nblk);
+  if (A > 0) {
+    if (softplus) hipLaunchKernelGGL((selective_aggregate_kernel<Tin, NS, true>), agrid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((selective_aggregate_kernel<Tin, NS, false>), agrid, dim3(kThreads), 0, s, p);
+    const int64_t nthreads = p.nseq * NS * p.D;
+    hipLaunchKernelGGL((selective_vcarry_kernel<NS>), dim3((unsigned)((nthreads + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, s, p);
+  }
+  const dim3 sgrid((unsigned)(S * p.nblk));
+  if (softplus) hipLaunchKernelGGL((selective_scan_kernel<Tin, Tout, NS, true>), sgrid, dim3(kThreads), 0, s, p);
+  else hipLaunchKernelGGL((selective_scan_kernel<Tin, Tout, NS, false>), sgrid, dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+template <typename Tin, typename Tout, int NS>
 void launch_update_n(const SelectiveUpdateArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)((a.B * a.D + kThreads - 1) / kThreads));
   if (a.dt_softplus)
@@ -525,7 +733,20 @@ void launch_update_t(const SelectiveUpdateArgs& a, hipStream_t s) {
 
 struct Plan {
   int64_t T, nseg, U;
+  // packed varlen forward plan (packed = true): pieces of at most X rows, aggregate units of Y rows;
+  // bounds on aggregate units (A), carry slots (C) and scan units (S)
+  bool packed;
+  int64_t X, Y, A, C, S;
 };
+
+// Packed varlen plan.  A sequence is scanned by one workgroup per channel block, from its start to
+// its end, unless it is longer than X rows; then it is cut into as few pieces as keep them within X,
+// and only the rows before its last piece pass through the aggregate kernel.  X is a fraction of the
+// rows each compute unit scans on average, so that the longest pieces, started first, end with the
+// rest; the scan units go longest first.
+constexpr int64_t kPieceNum = 3, kPieceDen = 8;  // X = rows per compute unit * kPieceNum / kPieceDen
+constexpr int64_t kAggRows = 256;                // Y
+
 
 // Longest segment whose rows span under 2^31 bytes of any activation (buffer windows).
 int64_t max_segment(int64_t D) {
@@ -534,7 +755,7 @@ int64_t max_segment(int64_t D) {
 }
 
 Plan make_plan(const SelectiveScanArgs& a) {
-  Plan pl;
+  Plan pl{};
   const int64_t kTargetWaves = device_cus() * kScanWavesPerCU;
   const int64_t max_T = max_segment(a.D);
   const int64_t waves_per_row = (a.D + 63) / 64;
@@ -564,11 +785,34 @@ Plan make_plan(const SelectiveScanArgs& a) {
     pl.T = T;
     pl.nseg = 0;
     pl.U = (a.L + T - 1) / T + a.nseq;  // upper bound on sum of ceil(len / T)
+    // the packed plan, when its one-dimensional scan grid fits
+    const int64_t nblk = (a.D + kThreads - 1) / kThreads;
+    const int64_t per_cu = (a.L * nblk + device_cus() - 1) / device_cus();
+    int64_t X = (per_cu * kPieceNum / kPieceDen + kAggRows - 1) / kAggRows * kAggRows;
+    if (X < kAggRows) X = kAggRows;
+    if (X > max_T) X = max_T / kAggRows * kAggRows;
+    pl.X = X;
+    pl.Y = kAggRows;
+    pl.A = (a.L + pl.Y - 1) / pl.Y;  // aggregate units are whole Y-row blocks inside one sequence
+    pl.C = (a.L + X - 1) / X;        // a sequence of len > X rows has ceil(len / X) - 1 <= len / X carries
+    pl.S = a.nseq + pl.C;            // scan units: one per sequence plus one per carry
+    pl.packed = X >= kAggRows && pl.S * nblk * kThreads < ((int64_t)1 << 31) && pl.A < ((int64_t)1 << 31);
   }
   return pl;
 }
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+template <typename Tin, typename Tout>
+hipError_t launch_packed_by_n(const SelParams& p, const Plan& pl, bool softplus, hipStream_t s) {
+  switch (p.N) {
+    case 1: return launch_packed<Tin, Tout, 1>(p, pl.A, pl.S, softplus, s);
+    case 2: return launch_packed<Tin, Tout, 2>(p, pl.A, pl.S, softplus, s);
+    case 4: return launch_packed<Tin, Tout, 4>(p, pl.A, pl.S, softplus, s);
+    case 8: return launch_packed<Tin, Tout, 8>(p, pl.A, pl.S, softplus, s);
+    default: return launch_packed<Tin, Tout, 16>(p, pl.A, pl.S, softplus, s);
+  }
+}
 
 // ============================================================================= backward
 // Gradients of the batched scan for the loss sum dy y + sum dh_last h_last.  With s_t the readout
@@ -980,21 +1224,54 @@ void launch_bwd_t(const SelBwdParams& q, int64_t N, int64_t U, int64_t nseq, boo
 
 int64_t selective_segment_len(const SelectiveScanArgs& a) { return make_plan(a).T; }
 
+// The packed plan serves bf16 inputs; fp32 inputs keep segments of the first plan.  An fp32
+// recurrence advanced row by row loses accuracy on slowly decaying states (abar near 1 is held to
+// 2^-24, a relative error of 2^-24 / (1 - abar) in the decay) over long runs, while the aggregate
+// and carry passes apply a segment's decay product exp2(A sum delta) in one rounding, so short
+// segments keep fp32 results within the fp32-input tolerance.
+bool use_packed_plan(const SelectiveScanArgs& a, const Plan& pl) { return a.cu_seqlens && pl.packed && a.in_bf16; }
+
 size_t selective_scan_scratch_bytes(const SelectiveScanArgs& a) {
   const Plan pl = make_plan(a);
   size_t bytes = workspace_head_bytes() + 3 * align256((size_t)pl.U * a.N * a.D * sizeof(float));
   if (a.cu_seqlens) bytes += align256(256 + (size_t)pl.U * sizeof(int2)) + align256((size_t)a.nseq * sizeof(int2));
+  if (a.cu_seqlens && pl.packed) {  // the query does not know the input dtype: room for either plan
+    const size_t st = (size_t)a.N * a.D * sizeof(float);
+    const size_t packed = workspace_head_bytes() + 2 * align256((size_t)pl.A * st) + align256((size_t)pl.C * st) +
+                          256 + align256((size_t)pl.S * sizeof(int4)) + align256((size_t)pl.A * sizeof(int4)) +
+                          align256((size_t)a.nseq * sizeof(int4));
+    if (packed > bytes) bytes = packed;
+  }
   return bytes;
 }
 
 hipError_t launch_selective_scan(const SelectiveScanArgs& a, hipStream_t s) {
   const Plan pl = make_plan(a);
-  SelParams p;
+  SelParams p{};
   p.L = a.L; p.D = a.D; p.N = a.N; p.nseq = a.nseq; p.T = pl.T; p.nseg = pl.nseg;
   p.cu = a.cu_seqlens; p.units = nullptr; p.n_units = nullptr; p.seq_units = nullptr;
   p.x = a.x; p.dt = a.dt; p.A = a.A; p.Bm = a.Bm; p.Cm = a.Cm; p.Dskip = a.Dskip; p.z = a.z;
   p.dt_bias = a.dt_bias; p.h0 = a.h0; p.y = a.y; p.h_last = a.h_last;
+  p.nblk = (a.D + kThreads - 1) / kThreads;
   char* base = static_cast<char*>(a.scratch) + workspace_head_bytes();
+  if (use_packed_plan(a, pl)) {
+    const size_t st = (size_t)a.N * a.D * sizeof(float);
+    char* q = base;
+    p.aggP = reinterpret_cast<float*>(q); q += align256((size_t)pl.A * st);
+    p.aggH = reinterpret_cast<float*>(q); q += align256((size_t)pl.A * st);
+    p.carry = reinterpret_cast<float*>(q); q += align256((size_t)pl.C * st);
+    int* count = reinterpret_cast<int*>(q); q += 256;
+    int4* scan = reinterpret_cast<int4*>(q); q += align256((size_t)pl.S * sizeof(int4));
+    int4* aggt = reinterpret_cast<int4*>(q); q += align256((size_t)pl.A * sizeof(int4));
+    int4* seqt = reinterpret_cast<int4*>(q);
+    p.vcount = count; p.vscan = scan; p.vagg = aggt; p.vseq = seqt;
+    hipLaunchKernelGGL(selective_vplan_kernel, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.nseq, pl.X, pl.Y, count,
+                       scan, aggt, seqt, a.D, a.N, a.h0, a.h_last);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return a.out_bf16 ? launch_packed_by_n<bf16_t, bf16_t>(p, pl, a.dt_softplus != 0, s)
+                      : launch_packed_by_n<bf16_t, float>(p, pl, a.dt_softplus != 0, s);
+  }
   const size_t agg = align256((size_t)pl.U * a.N * a.D * sizeof(float));
   p.aggP = reinterpret_cast<float*>(base);
   p.aggH = reinterpret_cast<float*>(base + agg);
