@@ -389,7 +389,26 @@ def form_rglru_small(args, device):
     x, r, i = (gen.randn((B, L, D), dtype=torch.float32) for _ in range(3))
     a_log = torch.log(gen.uniform((D,), 0.9, 0.999))
     t = time_calls(lambda k: ssd.rglru_scan(x, r, i, a_log, 8.0), 1, 50, 5)
-    return record_of(t, B * L * D, rglru_bytes(B, L, D, 4, 4), None, "rglru_fp32_B2_L128_D64")
+    out = {"rglru_fp32_B2_L128_D64": record_of(t, B * L * D, rglru_bytes(B, L, D, 4, 4), None,
+                                               "rglru_fp32_B2_L128_D64")}
+    # the same call 64 times from one HIP graph: the device time of a call without the host's
+    # per-call cost
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        ssd.rglru_scan(x, r, i, a_log, 8.0)  # workspace for the capture stream, outside the capture
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            for _ in range(64):
+                ssd.rglru_scan(x, r, i, a_log, 8.0)
+    torch.cuda.synchronize()
+    t = time_calls(lambda k: graph.replay(), 1, 10, 2)
+    t = {k: v / 64 for k, v in t.items()}
+    out["rglru_fp32_B2_L128_D64_hipgraph"] = record_of(t, B * L * D, rglru_bytes(B, L, D, 4, 4),
+                                                       dict(us_per_call=t["ms"] * 1e3),
+                                                       "rglru_fp32_B2_L128_D64_hipgraph")
+    return out
 
 
 def _rglru_big(device, seed):
@@ -505,9 +524,23 @@ def form_rglru_decode(args, device):
             decode_g()
     torch.cuda.synchronize()
     t = time_calls(lambda k: graph.replay(), 1, 5, 1)
-    out["rglru_decode_B256_D2560_256steps_hipgraph"] = record_of(t, B * D * S, per_step_bytes * S,
-                                                                 dict(us_per_step=t["ms"] * 1e3 / S),
-                                                                 "rglru_decode_B256_D2560_256steps_hipgraph")
+    # reference: a plain device copy moving the same bytes per step (half read, half written), 256
+    # times from one HIP graph: the latency floor of one round trip to memory at this size
+    src = torch.empty(per_step_bytes // 8, dtype=torch.float32, device=device)
+    dst = torch.empty_like(src)
+    cgraph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(cgraph, stream=cap):
+            for _ in range(S):
+                dst.copy_(src)
+    torch.cuda.synchronize()
+    tc = time_calls(lambda k: cgraph.replay(), 1, 5, 1)
+    out["rglru_decode_B256_D2560_256steps_hipgraph"] = record_of(
+        t, B * D * S, per_step_bytes * S, dict(us_per_step=t["ms"] * 1e3 / S, same_bytes_copy_us=tc["ms"] * 1e3 / S),
+        "rglru_decode_B256_D2560_256steps_hipgraph")
+    print(f"#   same-size device copy from a graph: {tc['ms'] * 1e3 / S:.2f} us per step", file=sys.stderr, flush=True)
     return out
 
 

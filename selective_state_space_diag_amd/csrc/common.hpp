@@ -153,7 +153,6 @@ template <int P> struct win<bf16_t, 2, P> {
     __builtin_amdgcn_raw_buffer_store_b32(d, w, (int)lane_off, (int)row_off, P);
   }
 };
-
 // ------------------------------------------------------------------ hardware transcendentals
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }

@@ -534,6 +534,82 @@ void scan1_kernel(Scan1Params p) {
   }
 }
 
+// ------------------------------------------------------------------ short sequences
+// L <= NW * SPW: one workgroup of NW waves per (batch row, tile of 64 channels, one per lane) covers
+// every step at once (wave w owns steps [SPW w, SPW w + SPW)); the wave aggregates meet in LDS and
+// each wave starts from h0 folded through the aggregates of the waves before it.  No tickets, no
+// lookback, no workspace traffic: the whole scan is one round of loads, the combine and the stores,
+// with few steps per lane so that the dependent chain of each lane stays short.
+constexpr int kShortSpw = 8;  // steps per wave
+template <class Op, typename Tin, typename Tout, bool GATE, int NW>
+__global__ __launch_bounds__(NW * 64) void scan1_short_kernel(Scan1Params p) {
+  constexpr int SPW = kShortSpw;
+  __shared__ float s_aggA[NW][64];
+  __shared__ float s_aggB[NW][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  using LD = win<Tin, 1, kStreaming>;
+  const int64_t n_tiles = (p.D + 63) / 64;
+  const int64_t b = blockIdx.x / n_tiles;
+  const int64_t ch0 = (blockIdx.x - b * n_tiles) * 64 + lane;
+  const bool ch_ok = ch0 < p.D;
+  const int64_t chl = ch_ok ? ch0 : p.D - 1;
+  const uint32_t lo_in = (uint32_t)(chl * (int64_t)sizeof(Tin));
+  const uint32_t rows_in = (uint32_t)(p.D * (int64_t)sizeof(Tin));
+  const int t0 = wave * SPW;
+  const int last = (int)p.L - 1;
+  typename LD::raw raw[Op::kIn][SPW];
+  typename LD::raw graw[GATE ? SPW : 1];
+  {
+    __amdgpu_buffer_rsrc_t w[Op::kIn];
+#pragma unroll
+    for (int q = 0; q < Op::kIn; ++q)
+      w[q] = make_window(static_cast<const char*>(p.in[q]) + b * p.L * p.D * (int64_t)sizeof(Tin), (uint32_t)(p.L * rows_in));
+    const auto wg = make_window(static_cast<const char*>(GATE ? p.gate : p.in[0]) + b * p.L * p.D * (int64_t)sizeof(Tin),
+                                (uint32_t)(p.L * rows_in));
+#pragma unroll
+    for (int st = 0; st < SPW; ++st) {
+      const uint32_t ro = (uint32_t)min(t0 + st, last) * rows_in;  // steps past L read the last row
+#pragma unroll
+      for (int q = 0; q < Op::kIn; ++q) raw[q][st] = LD::load(w[q], lo_in, ro);
+      if (GATE) graw[st] = LD::load(wg, lo_in, ro);
+    }
+  }
+  const typename Op::Chan cc = Op::chan(p, Op::param(p, chl));
+  float av[SPW], bv[SPW], Ag = Op::id_a(), Bg = Op::id_b();
+#pragma unroll
+  for (int st = 0; st < SPW; ++st) {
+    const bool ok = t0 + st < p.L;
+    float in[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int q = 0; q < Op::kIn; ++q) in[q] = LD::get(raw[q][st], 0);
+    float a, bb;
+    Op::step(in, cc, a, bb);
+    av[st] = ok ? a : Op::id_a();  // steps past L are the identity map
+    bv[st] = ok ? bb : Op::id_b();
+    Bg = Op::apply(av[st], bv[st], Bg);
+    Ag = Op::fold_a(av[st], Ag);
+  }
+  s_aggA[wave][lane] = Ag;
+  s_aggB[wave][lane] = Bg;
+  __syncthreads();
+  float h = p.h0 ? p.h0[b * p.D + chl] : 0.0f;
+  for (int w = 0; w < wave; ++w) h = Op::apply(s_aggA[w][lane], s_aggB[w][lane], h);
+  // the state entering each 64-step chunk is the carry of the wave that starts it
+  if (p.carry_out && ch_ok && (t0 % kChunk) == 0 && t0 < p.L) p.carry_out[(b * p.n_chunks + t0 / kChunk) * p.D + ch0] = h;
+  const auto wy = make_window(static_cast<char*>(p.y) + b * p.L * p.D * (int64_t)sizeof(Tout),
+                              (uint32_t)(p.L * p.D * (int64_t)sizeof(Tout)));
+  const uint32_t lo_out = (uint32_t)(chl * (int64_t)sizeof(Tout)), rows_out = (uint32_t)(p.D * (int64_t)sizeof(Tout));
+#pragma unroll
+  for (int st = 0; st < SPW; ++st) {
+    h = Op::apply(av[st], bv[st], h);
+    const float out = GATE ? Op::gated(h, LD::get(graw[GATE ? st : 0], 0)) : h;
+    if (ch_ok && t0 + st < p.L) win<Tout, 1, kStreaming>::store(wy, lo_out, (uint32_t)(t0 + st) * rows_out, &out);
+  }
+  // steps past L are identities, so the last wave ends holding h_L
+  if (p.h_last && ch_ok && wave == NW - 1) p.h_last[b * p.D + ch0] = h;
+}
+
 // ------------------------------------------------------------------ decode steps
 struct Upd1Params {
   int64_t B, D;
@@ -561,6 +637,61 @@ __global__ __launch_bounds__(256) void update1_kernel(Upd1Params p) {
   const float h = Op::apply(a, b, p.state[idx]);
   p.state[idx] = h;
   io<Tout>::store(p.y, idx, GATE ? Op::gated(h, io<Tin>::load(p.gate, idx)) : h);
+}
+
+// Decode step with V consecutive channels per vector and U vectors per lane (D a multiple of V,
+// every operand under 2^31 bytes): x / r / i / gate, the state and y go through buffer windows with
+// 32-bit offsets, one 2V- or 4V-byte access per operand and vector; the channel parameters come in
+// one access as well.  All loads of a lane are issued before any arithmetic: a decode step is one
+// round trip to memory.
+template <class Op, typename Tin, typename Tout, bool GATE, int V, int U>
+__global__ __launch_bounds__(256) void update1v_kernel(Upd1Params p) {
+  const uint32_t n = (uint32_t)(p.B * p.D / V);  // vectors of V channels
+  const uint32_t per_row = (uint32_t)(p.D / V);
+  const uint32_t elems = (uint32_t)(p.B * p.D);
+  Scan1Params q{};
+  q.a_log = p.a_log;
+  q.c = p.c;
+  using Wi = win<Tin, V>;
+  using Wf = win<float, V>;
+  __amdgpu_buffer_rsrc_t win_in[3];
+#pragma unroll
+  for (int k = 0; k < Op::kIn; ++k) win_in[k] = make_window(p.in[k], elems * sizeof(Tin));
+  const auto wgt = make_window(GATE ? p.gate : p.in[0], elems * sizeof(Tin));
+  const auto ws = make_window(p.state, elems * sizeof(float));
+  const auto wa = make_window(p.a_log ? p.a_log : p.state, (uint32_t)(p.D * sizeof(float)));
+  uint32_t g[U];
+  typename Wi::raw rin[U][3], rg[U];
+  typename Wf::raw rs[U], ra[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    g[u] = blockIdx.x * (256u * U) + u * 256u + threadIdx.x;
+    const uint32_t gc = g[u] < n ? g[u] : n - 1;  // lanes past the end reread the last vector
+    const uint32_t d0 = (gc % per_row) * V;
+#pragma unroll
+    for (int k = 0; k < Op::kIn; ++k) rin[u][k] = Wi::load(win_in[k], gc * V * sizeof(Tin), 0);
+    if (GATE) rg[u] = Wi::load(wgt, gc * V * sizeof(Tin), 0);
+    rs[u] = Wf::load(ws, gc * V * sizeof(float), 0);
+    if (p.a_log) ra[u] = Wf::load(wa, d0 * sizeof(float), 0);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float h[V], y[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      float in[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int k = 0; k < Op::kIn; ++k) in[k] = Wi::get(rin[u][k], v);
+      float a, b;
+      Op::step(in, Op::chan(q, p.a_log ? Wf::get(ra[u], v) : 0.0f), a, b);
+      h[v] = Op::apply(a, b, Wf::get(rs[u], v));
+      y[v] = GATE ? Op::gated(h[v], Wi::get(rg[u], v)) : h[v];
+    }
+    if (g[u] < n) {
+      Wf::store(ws, g[u] * V * sizeof(float), 0, h);
+      win<Tout, V>::store(make_window(p.y, elems * sizeof(Tout)), g[u] * V * sizeof(Tout), 0, y);
+    }
+  }
 }
 
 // ------------------------------------------------------------------ RG-LRU backward
@@ -1117,19 +1248,65 @@ hipError_t launch_record_op(Scan1Params& p, int in_bf16, void* scratch, hipStrea
   return in_bf16 ? launch_scan_t<Op, bf16_t, float, 1, false, true>(p, s) : launch_scan_t<Op, float, float, 1, false, true>(p, s);
 }
 
+template <class Op, bool GATE, int NW>
+hipError_t launch_short_dt(const Scan1Params& p, int in_bf16, int out_bf16, hipStream_t s) {
+  const dim3 grid((unsigned)(p.B * ((p.D + 63) / 64))), block(NW * 64);
+  if (!in_bf16)
+    hipLaunchKernelGGL((scan1_short_kernel<Op, float, float, GATE, NW>), grid, block, 0, s, p);
+  else if (out_bf16)
+    hipLaunchKernelGGL((scan1_short_kernel<Op, bf16_t, bf16_t, GATE, NW>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((scan1_short_kernel<Op, bf16_t, float, GATE, NW>), grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+template <class Op, bool GATE>
+hipError_t launch_short_g(const Scan1Params& p, int in_bf16, int out_bf16, hipStream_t s) {
+  if (p.L <= 4 * kShortSpw) return launch_short_dt<Op, GATE, 4>(p, in_bf16, out_bf16, s);
+  if (p.L <= 8 * kShortSpw) return launch_short_dt<Op, GATE, 8>(p, in_bf16, out_bf16, s);
+  return launch_short_dt<Op, GATE, 16>(p, in_bf16, out_bf16, s);
+}
+
+// Sequences of at most this many steps take the one-pass short kernel.
+constexpr int64_t kShortSteps = 16 * kShortSpw;
+
 template <class Op>
 hipError_t launch_scan_op(Scan1Params& p, int in_bf16, int out_bf16, void* scratch, hipStream_t s) {
   const int V = vec_width(p.D);
   scan_geometry<Op>(p, scratch);
   const bool gate = p.gate != nullptr;
+  if (p.L <= kShortSteps && p.B * ((p.D + 63) / 64) < ((int64_t)1 << 31) && p.L * p.D * 4 < ((int64_t)1 << 31))
+    return gate ? launch_short_g<Op, true>(p, in_bf16, out_bf16, s) : launch_short_g<Op, false>(p, in_bf16, out_bf16, s);
   if (V == 2)
     return gate ? launch_scan_dt<Op, 2, true>(p, in_bf16, out_bf16, s) : launch_scan_dt<Op, 2, false>(p, in_bf16, out_bf16, s);
   return gate ? launch_scan_dt<Op, 1, true>(p, in_bf16, out_bf16, s) : launch_scan_dt<Op, 1, false>(p, in_bf16, out_bf16, s);
 }
 
+// Vectors per lane in the decode step, and channels per vector (below): a step is one round trip to
+// memory followed by a short chain of arithmetic per lane, so many short lanes finish first.  Measured
+// at B = 256, D = 2560 bf16 from a HIP graph: 2 channels x 1 vector 3.9 us per step, 4 x 1 4.2 us,
+// 1 x 1 4.4 us, 4 x 2 5.0 us (a plain device copy of the same bytes: 2.6 us).
+constexpr int kUpdVectors = 1;
+template <class Op, bool GATE, int V>
+hipError_t launch_update_v(const Upd1Params& p, int in_bf16, int out_bf16, hipStream_t s) {
+  constexpr int U = kUpdVectors;
+  const dim3 grid((unsigned)((p.B * p.D / V + 256 * U - 1) / (256 * U)));
+  if (!in_bf16)
+    hipLaunchKernelGGL((update1v_kernel<Op, float, float, GATE, V, U>), grid, dim3(256), 0, s, p);
+  else if (out_bf16)
+    hipLaunchKernelGGL((update1v_kernel<Op, bf16_t, bf16_t, GATE, V, U>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((update1v_kernel<Op, bf16_t, float, GATE, V, U>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 template <class Op, bool GATE>
 hipError_t launch_update_g(const Upd1Params& p, int in_bf16, int out_bf16, hipStream_t s) {
   const int64_t n = p.B * p.D;
+  // vector path: every operand (the fp32 state is the largest) under 2^31 bytes
+  if (n * (int64_t)sizeof(float) < ((int64_t)1 << 31)) {
+    if (p.D % 2 == 0) return launch_update_v<Op, GATE, 2>(p, in_bf16, out_bf16, s);
+  }
   const dim3 grid((unsigned)((n + 255) / 256));
   if (!in_bf16)
     hipLaunchKernelGGL((update1_kernel<Op, float, float, GATE>), grid, dim3(256), 0, s, p);

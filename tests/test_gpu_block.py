@@ -150,9 +150,10 @@ def test_minmax_bf16_output_is_exact_for_bf16_states():
     same_bits(f32_host(y), yr, "bf16 y")  # every state is a bf16 input value or the zero start
 
 
-def test_minmax_decode_steps_bitwise():
+@pytest.mark.parametrize("D", [130, 131, 200])
+def test_minmax_decode_steps_bitwise(D):
     import torch
-    B, L, D = 4, 20, 200
+    B, L = 4, 20
     inp = synth.minmax_inputs(B, L, D, synth.BF16, 2600, with_x0=True, ties=True)
     r, s = to_dev(inp.t["r"]), to_dev(inp.t["s"])
     state = to_dev(inp.p["x0"]).clone()

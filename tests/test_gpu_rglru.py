@@ -102,6 +102,48 @@ def test_decode_steps_equal_scan_and_oracle():
     assert_close(host(y_dec), host(y_scan), 1e-5, "decode vs scan")
 
 
+@pytest.mark.parametrize("D", [1, 130, 258, 321, 2560])
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+def test_decode_channel_widths(D, dtype):
+    """Decode steps at both widths of the decode kernel (two channels per lane for even D, one for odd
+    D), fp32 and bf16 inputs, against the oracle."""
+    import torch
+    B, L = 3, 6
+    inp = synth.rglru_inputs(B, L, D, dtype, 60 + D, with_h0=True)
+    x, r, i = (to_dev(inp.t[n]) for n in ("x", "r_logit", "i_logit"))
+    a_log = to_dev(inp.p["a_log"])
+    state = to_dev(inp.p["h0"]).clone()
+    ys = [ssd.rglru_update(x[:, t].contiguous(), r[:, t].contiguous(), i[:, t].contiguous(), a_log, 8.0, state)
+          for t in range(L)]
+    torch.cuda.synchronize()
+    yr, hr = oracle.rglru_scan(f64(inp.t["x"]), f64(inp.t["r_logit"]), f64(inp.t["i_logit"]), f64(inp.p["a_log"]),
+                               8.0, f64(inp.p["h0"]))
+    assert_close(np.stack([host(v) for v in ys], axis=1), yr, TOL[dtype], "decode y")
+    assert_close(host(state), hr, TOL[dtype], "decode state")
+
+
+@pytest.mark.parametrize("L", [40, 100])
+def test_short_scan_chunk_states(L):
+    """Scans of at most 128 steps take the one-pass kernel; its chunk_states hold h0 and, past 64
+    steps, the state after step 64, as the oracle gives them."""
+    import torch
+    B, D = 2, 130
+    inp = synth.rglru_inputs(B, L, D, synth.F32, 70 + L, with_h0=True)
+    x, r, i = (to_dev(inp.t[n]) for n in ("x", "r_logit", "i_logit"))
+    cs = torch.full(ssd.chunk_states_shape(B, L, D), float("nan"), device="cuda")
+    y, hl = ssd.rglru_scan(x, r, i, to_dev(inp.p["a_log"]), 8.0, h0=to_dev(inp.p["h0"]), return_last_state=True,
+                           chunk_states=cs)
+    torch.cuda.synchronize()
+    yr, hr = oracle.rglru_scan(f64(inp.t["x"]), f64(inp.t["r_logit"]), f64(inp.t["i_logit"]), f64(inp.p["a_log"]),
+                               8.0, f64(inp.p["h0"]))
+    assert_close(host(y), yr, TOL[synth.F32], "y")
+    assert_close(host(hl), hr, TOL[synth.F32], "h_last")
+    states = host(cs)
+    assert_close(states[:, 0], f64(inp.p["h0"]), TOL[synth.F32], "state entering chunk 0")
+    if L > 64:
+        assert_close(states[:, 1], yr[:, 63], TOL[synth.F32], "state entering chunk 1")
+
+
 def test_decode_steps_replayed_from_a_hip_graph():
     """Decode steps captured once in a HIP graph: every replay, with eager work and synchronisations
     between replays, equals the same steps run eagerly."""
