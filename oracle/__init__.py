@@ -19,7 +19,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ssd_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# SSD_ORACLE_LIBRARY names another build of the same C file (a sanitizer build in the tests)
+_LIB_PATH = os.environ.get("SSD_ORACLE_LIBRARY") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 _dp = ctypes.POINTER(ctypes.c_double)

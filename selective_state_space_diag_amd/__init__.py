@@ -29,7 +29,9 @@ from typing import Optional
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libssd.so")
+# SSD_LIBRARY names another build of the same library (for instance one whose host code carries a
+# sanitizer); by default the in-tree libssd.so.
+LIB_PATH = os.environ.get("SSD_LIBRARY") or os.path.join(_PKG, "libssd.so")
 
 SSD_F32, SSD_BF16 = 0, 1
 STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_DTYPE", 4: "SSD_ERR_ALIGN",
