@@ -18,8 +18,9 @@
 // end by one workgroup per channel block unless it is longer than X rows (a fraction of the rows
 // each compute unit scans on average); a longer one is cut into as few equal pieces as keep them
 // within X.  Only the rows before a sequence's last piece pass through the aggregate kernel (in
-// blocks of 256 rows), the carry kernel writes the carry-in of each later piece, and the scan units
-// run longest first so that the long ones end with the rest.  For the 32-sequence benchmark shape
+// blocks of 256 rows), a small kernel folds each piece's blocks into the piece's aggregate, a later
+// piece folds h0 through the earlier pieces' aggregates, and the scan units run longest first so
+// that the long ones end with the rest.  For the 32-sequence benchmark shape
 // half the rows are aggregated instead of nearly all.
 //
 // When dt goes through softplus (delta >= 0) and every A of the wave is <= 0, delta*A <= 0 and
@@ -63,11 +64,14 @@ struct SelParams {
   // Packed varlen forward plan (NULL for the other launches): scan units of whole sequences or of
   // long sequences cut into a few pieces, longest first; aggregates only for the rows before a
   // sequence's last piece.
-  const int* vcount;      // [0] scan units, [1] aggregate units
+  const int* vcount;      // [0] scan units, [1] aggregate units, [2] pieces with an aggregate
   const int4* vscan;      // (sequence, first row in the sequence, rows, carry slot or -1)
-  const int4* vagg;       // (sequence, first row in the sequence, rows, 0)
+  const int4* vagg;       // (sequence, first row in the sequence, rows, piece slot)
   const int4* vseq;       // per sequence: (first aggregate unit, aggregate units, aggregate units per
-                          //  scan piece, first carry slot)
+                          //  scan piece, first piece slot)
+  const int2* vpiece;     // per piece slot: (first aggregate unit, aggregate units)
+  float* pieceP;          // [piece slot][N][D]: prod abar over a piece (every piece but a sequence's last)
+  float* pieceH;          // [piece slot][N][D]: the state a piece reaches from zero
   int64_t nblk;           // channel blocks (the packed plan's scan grid is units x channel blocks)
 };
 
@@ -299,9 +303,9 @@ __global__ __launch_bounds__(kThreads, 4) void selective_aggregate_kernel(SelPar
   Unit U;
   if (p.vagg != nullptr) {  // packed plan: aggregate unit u (never a sequence's last rows)
     if (u >= (int64_t)p.vcount[1]) return;
-    const int4 e = p.vagg[u];
-    U.row0 = (int64_t)p.cu[e.x] + e.y;
-    U.row1 = U.row0 + e.z;
+    const int4 ve = p.vagg[u];
+    U.row0 = (int64_t)p.cu[ve.x] + ve.y;
+    U.row1 = U.row0 + ve.z;
   } else {
     U = unit_of(p, u);
     if (!U.valid || U.last) return;
@@ -329,6 +333,51 @@ __global__ __launch_bounds__(kThreads, 4) void selective_aggregate_kernel(SelPar
     const float P = disc == kExp ? hw_exp2(A2[n] * sum_delta) : hw_exp2(e[n]);
     p.aggP[(u * NS + n) * p.D + d] = P;
     p.aggH[(u * NS + n) * p.D + d] = h[n];
+  }
+}
+
+// Packed plan: one workgroup per (piece, channel block) folds the piece's aggregate units in order
+// into the piece's aggregate (prod abar and the state reached from zero); units in rounds of JB with
+// all their loads in flight together.
+template <int NS>
+__global__ __launch_bounds__(kThreads) void selective_vpiece_kernel(SelParams p) {
+  const int64_t slot = blockIdx.x;
+  if (slot >= (int64_t)p.vcount[2]) return;
+  const int64_t d = (int64_t)blockIdx.y * kThreads + threadIdx.x;
+  if (d >= p.D) return;
+  const int2 pc = p.vpiece[slot];
+  const int64_t first = pc.x;
+  const int q = pc.y;
+  float Pp[NS], Hp[NS];
+#pragma unroll
+  for (int n = 0; n < NS; ++n) { Pp[n] = 1.0f; Hp[n] = 0.0f; }
+  constexpr int JB = 4;
+  for (int j0 = 0; j0 < q; j0 += JB) {
+    float Pj[JB][NS], Hj[JB][NS];
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj) {
+      const int64_t base = (first + min(j0 + jj, q - 1)) * NS * p.D + d;
+#pragma unroll
+      for (int n = 0; n < NS; ++n) {
+        Pj[jj][n] = p.aggP[base + n * p.D];
+        Hj[jj][n] = p.aggH[base + n * p.D];
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj) {
+      if (j0 + jj < q) {
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+          Hp[n] = fmaf(Pj[jj][n], Hp[n], Hj[jj][n]);
+          Pp[n] *= Pj[jj][n];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    p.pieceP[(slot * NS + n) * p.D + d] = Pp[n];
+    p.pieceH[(slot * NS + n) * p.D + d] = Hp[n];
   }
 }
 
@@ -363,10 +412,19 @@ __global__ __launch_bounds__(kThreads) void selective_scan_kernel(SelParams p) {
   if (U.seg == 0) {
 #pragma unroll
     for (int n = 0; n < NS; ++n) h[n] = p.h0 ? p.h0[(U.seq * p.D + dl) * NS + n] : 0.0f;
-  } else {
-    const int64_t slot = p.vscan ? U.carry : u;
+  } else if (p.vscan) {
+    // packed plan: h0 folded through the aggregates of the sequence's earlier pieces
+    const int64_t first = p.vseq[U.seq].w;
 #pragma unroll
-    for (int n = 0; n < NS; ++n) h[n] = p.carry[(slot * NS + n) * p.D + dl];
+    for (int n = 0; n < NS; ++n) h[n] = p.h0 ? p.h0[(U.seq * p.D + dl) * NS + n] : 0.0f;
+    for (int64_t j = first; j <= U.carry; ++j) {
+#pragma unroll
+      for (int n = 0; n < NS; ++n)
+        h[n] = fmaf(p.pieceP[(j * NS + n) * p.D + dl], h[n], p.pieceH[(j * NS + n) * p.D + dl]);
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < NS; ++n) h[n] = p.carry[(u * NS + n) * p.D + dl];
   }
   float sum_delta = 0.0f;
   __shared__ float lds[2 * BCStage<NS, true>::PER_BLOCK];
@@ -424,45 +482,6 @@ __global__ __launch_bounds__(kThreads) void selective_carry_kernel(SelParams p) 
   }
 }
 
-// Packed plan: one thread per (sequence, state n, channel d) folds the sequence's aggregate units in
-// order from h0 (or zero) and writes the state after every q of them: the carry of the next piece.
-template <int NS>
-__global__ __launch_bounds__(kThreads) void selective_vcarry_kernel(SelParams p) {
-  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t per_seq = NS * p.D;
-  const int64_t seq = gid / per_seq;
-  if (seq >= p.nseq) return;
-  const int64_t e = gid - seq * per_seq;  // n * D + d
-  const int64_t n = e / p.D;
-  const int64_t d = e - n * p.D;
-  const int4 info = p.vseq[seq];
-  const int64_t first = info.x, count = info.y, q = info.z, cfirst = info.w;
-  if (count == 0) return;
-  float h = p.h0 ? p.h0[(seq * p.D + d) * NS + n] : 0.0f;
-  int64_t in_piece = 0, piece = 0;
-  constexpr int K = 32;
-  for (int64_t s0 = 0; s0 < count; s0 += K) {
-    float P[K], H[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int64_t idx = ((first + min(s0 + k, count - 1)) * NS + n) * p.D + d;
-      P[k] = p.aggP[idx];
-      H[k] = p.aggH[idx];
-    }
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      if (s0 + k < count) {
-        h = fmaf(P[k], h, H[k]);
-        if (++in_piece == q) {
-          in_piece = 0;
-          p.carry[((cfirst + piece) * NS + n) * p.D + d] = h;
-          ++piece;
-        }
-      }
-    }
-  }
-}
-
 // Pieces of a packed sequence of `len` rows: unsplit up to X rows, else cut into pieces of a
 // multiple of Y rows (all but the last full), as few as keep them within X.
 struct Pieces {
@@ -488,28 +507,40 @@ __device__ __forceinline__ int len_bucket(int64_t rows) {
   return b < 0 ? 0 : (b >= kLenBuckets ? kLenBuckets - 1 : b);
 }
 
-// Inclusive sum over the 1024 threads of the workgroup (all threads must call it).
+// Inclusive sum over the 1024 threads of the workgroup (all threads must call it): within each wave
+// by shuffles, then over the 16 wave totals by wave 0.
 __device__ __forceinline__ int block_inclusive_sum(int v, int* buf) {
-  buf[threadIdx.x] = v;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int add = threadIdx.x >= off ? buf[threadIdx.x - off] : 0;
-    __syncthreads();
-    buf[threadIdx.x] += add;
-    __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(v, off);
+    if (lane >= off) v += t;
   }
-  const int r = buf[threadIdx.x];
+  if (lane == 63) buf[wave] = v;
   __syncthreads();
+  if (wave == 0) {
+    int w = lane < 16 ? buf[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int t = __shfl_up(w, off);
+      if (lane >= off) w += t;
+    }
+    if (lane < 16) buf[lane] = w;
+  }
+  __syncthreads();
+  const int r = v + (wave > 0 ? buf[wave - 1] : 0);
+  __syncthreads();  // buf is reused by the next call
   return r;
 }
 
 // Packed plan, one workgroup: per-sequence table, aggregate units (Y rows each, every row before a
 // sequence's last piece), scan units ordered by length (longest first; the order among units of
-// one length bucket is not fixed, and no result depends on it), the unit counts, and the final state
-// of zero-length sequences (= their initial state, or zero).
+// one length bucket is not fixed, and no result depends on it), the pieces' aggregate units, the
+// counts, and the final state of zero-length sequences (= their initial state, or zero).
 __global__ __launch_bounds__(1024) void selective_vplan_kernel(const int32_t* cu, int64_t nseq, int64_t X, int64_t Y,
                                                                int* count, int4* scan, int4* agg, int4* seqtab,
-                                                               int64_t D, int64_t N, const float* h0, float* h_last) {
+                                                               int2* piece, int64_t D, int64_t N, const float* h0,
+                                                               float* h_last) {
   __shared__ int s_buf[1024];
   __shared__ int s_hist[kLenBuckets];
   __shared__ int s_base_agg, s_base_carry, s_units;
@@ -530,7 +561,8 @@ __global__ __launch_bounds__(1024) void selective_vplan_kernel(const int32_t* cu
     const int first_agg = s_base_agg + ia - nagg, first_carry = s_base_carry + ic - ncarry;
     if (sq < nseq) {
       seqtab[sq] = make_int4(first_agg, nagg, q, first_carry);
-      for (int j = 0; j < nagg; ++j) agg[first_agg + j] = make_int4((int)sq, (int)(j * Y), (int)Y, 0);
+      for (int j = 0; j < nagg; ++j) agg[first_agg + j] = make_int4((int)sq, (int)(j * Y), (int)Y, first_carry + j / q);
+      for (int k = 0; k < ncarry; ++k) piece[first_carry + k] = make_int2(first_agg + k * q, q);
       for (int64_t k = 0; k < pc.count; ++k) {
         const int64_t rows = k + 1 < pc.count ? pc.piece : pc.len - k * pc.piece;
         atomicAdd(&s_hist[len_bucket(rows)], 1);
@@ -548,11 +580,16 @@ __global__ __launch_bounds__(1024) void selective_vplan_kernel(const int32_t* cu
     if (b >= 0) s_hist[b] = incl - c;
     __syncthreads();
   }
-  // pass 2: scan units into their buckets
+  // pass 2: scan units into their buckets; zero-length sequences get h_last = h0 (or zero)
+  __shared__ int s_empty[1024];
+  __shared__ int s_nempty;
   for (int64_t blk = 0; blk < nseq; blk += 1024) {
     const int64_t sq = blk + threadIdx.x;
+    if (threadIdx.x == 0) s_nempty = 0;
+    __syncthreads();
     if (sq < nseq) {
       const Pieces pc = pieces_of((int64_t)cu[sq + 1] - cu[sq], X, Y);
+      if (pc.len == 0 && h_last) s_empty[atomicAdd(&s_nempty, 1)] = (int)sq;
       const int first_carry = seqtab[sq].w;
       for (int64_t k = 0; k < pc.count; ++k) {
         const int64_t rows = k + 1 < pc.count ? pc.piece : pc.len - k * pc.piece;
@@ -560,17 +597,17 @@ __global__ __launch_bounds__(1024) void selective_vplan_kernel(const int32_t* cu
         scan[pos] = make_int4((int)sq, (int)(k * pc.piece), (int)rows, k == 0 ? -1 : first_carry + (int)k - 1);
       }
     }
+    __syncthreads();
+    for (int k = 0; k < s_nempty; ++k) {
+      const int64_t es = s_empty[k];
+      for (int64_t e = threadIdx.x; e < D * N; e += 1024) h_last[es * D * N + e] = h0 ? h0[es * D * N + e] : 0.0f;
+    }
+    __syncthreads();
   }
   if (threadIdx.x == 0) {
     count[0] = s_units;
     count[1] = s_base_agg;
-  }
-  if (h_last) {
-    for (int64_t sq = 0; sq < nseq; ++sq) {
-      if (cu[sq + 1] != cu[sq]) continue;
-      for (int64_t e = threadIdx.x; e < D * N; e += 1024)
-        h_last[sq * D * N + e] = h0 ? h0[sq * D * N + e] : 0.0f;
-    }
+    count[2] = s_base_carry;
   }
 }
 
@@ -694,14 +731,12 @@ hipError_t launch_by_n(const SelParams& p, int64_t U, bool softplus, hipStream_t
 }
 
 template <typename Tin, typename Tout, int NS>
-hipError_t launch_packed(const SelParams& p, int64_t A, int64_t S, bool softplus, hipStream_t s) {
+hipError_t launch_packed(const SelParams& p, int64_t A, int64_t C, int64_t S, bool softplus, hipStream_t s) {
   const dim3 agrid((unsigned)A, (unsigned)p.nblk);
   if (A > 0) {
     if (softplus) hipLaunchKernelGGL((selective_aggregate_kernel<Tin, NS, true>), agrid, dim3(kThreads), 0, s, p);
     else hipLaunchKernelGGL((selective_aggregate_kernel<Tin, NS, false>), agrid, dim3(kThreads), 0, s, p);
-    const int64_t nthreads = p.nseq * NS * p.D;
-    hipLaunchKernelGGL((selective_vcarry_kernel<NS>), dim3((unsigned)((nthreads + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((selective_vpiece_kernel<NS>), dim3((unsigned)C, (unsigned)p.nblk), dim3(kThreads), 0, s, p);
   }
   const dim3 sgrid((unsigned)(S * p.nblk));
   if (softplus) hipLaunchKernelGGL((selective_scan_kernel<Tin, Tout, NS, true>), sgrid, dim3(kThreads), 0, s, p);
@@ -806,11 +841,11 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 template <typename Tin, typename Tout>
 hipError_t launch_packed_by_n(const SelParams& p, const Plan& pl, bool softplus, hipStream_t s) {
   switch (p.N) {
-    case 1: return launch_packed<Tin, Tout, 1>(p, pl.A, pl.S, softplus, s);
-    case 2: return launch_packed<Tin, Tout, 2>(p, pl.A, pl.S, softplus, s);
-    case 4: return launch_packed<Tin, Tout, 4>(p, pl.A, pl.S, softplus, s);
-    case 8: return launch_packed<Tin, Tout, 8>(p, pl.A, pl.S, softplus, s);
-    default: return launch_packed<Tin, Tout, 16>(p, pl.A, pl.S, softplus, s);
+    case 1: return launch_packed<Tin, Tout, 1>(p, pl.A, pl.C, pl.S, softplus, s);
+    case 2: return launch_packed<Tin, Tout, 2>(p, pl.A, pl.C, pl.S, softplus, s);
+    case 4: return launch_packed<Tin, Tout, 4>(p, pl.A, pl.C, pl.S, softplus, s);
+    case 8: return launch_packed<Tin, Tout, 8>(p, pl.A, pl.C, pl.S, softplus, s);
+    default: return launch_packed<Tin, Tout, 16>(p, pl.A, pl.C, pl.S, softplus, s);
   }
 }
 
@@ -1237,8 +1272,9 @@ size_t selective_scan_scratch_bytes(const SelectiveScanArgs& a) {
   if (a.cu_seqlens) bytes += align256(256 + (size_t)pl.U * sizeof(int2)) + align256((size_t)a.nseq * sizeof(int2));
   if (a.cu_seqlens && pl.packed) {  // the query does not know the input dtype: room for either plan
     const size_t st = (size_t)a.N * a.D * sizeof(float);
-    const size_t packed = workspace_head_bytes() + 2 * align256((size_t)pl.A * st) + align256((size_t)pl.C * st) +
-                          256 + align256((size_t)pl.S * sizeof(int4)) + align256((size_t)pl.A * sizeof(int4)) +
+    const size_t packed = workspace_head_bytes() + 2 * align256((size_t)pl.A * st) + 2 * align256((size_t)pl.C * st) +
+                          align256((size_t)pl.C * sizeof(int2)) + 256 +
+                          align256((size_t)pl.S * sizeof(int4)) + align256((size_t)pl.A * sizeof(int4)) +
                           align256((size_t)a.nseq * sizeof(int4));
     if (packed > bytes) bytes = packed;
   }
@@ -1259,14 +1295,16 @@ hipError_t launch_selective_scan(const SelectiveScanArgs& a, hipStream_t s) {
     char* q = base;
     p.aggP = reinterpret_cast<float*>(q); q += align256((size_t)pl.A * st);
     p.aggH = reinterpret_cast<float*>(q); q += align256((size_t)pl.A * st);
-    p.carry = reinterpret_cast<float*>(q); q += align256((size_t)pl.C * st);
+    p.pieceP = reinterpret_cast<float*>(q); q += align256((size_t)pl.C * st);
+    p.pieceH = reinterpret_cast<float*>(q); q += align256((size_t)pl.C * st);
+    int2* piece = reinterpret_cast<int2*>(q); q += align256((size_t)pl.C * sizeof(int2));
     int* count = reinterpret_cast<int*>(q); q += 256;
     int4* scan = reinterpret_cast<int4*>(q); q += align256((size_t)pl.S * sizeof(int4));
     int4* aggt = reinterpret_cast<int4*>(q); q += align256((size_t)pl.A * sizeof(int4));
     int4* seqt = reinterpret_cast<int4*>(q);
-    p.vcount = count; p.vscan = scan; p.vagg = aggt; p.vseq = seqt;
+    p.vcount = count; p.vscan = scan; p.vagg = aggt; p.vseq = seqt; p.vpiece = piece;
     hipLaunchKernelGGL(selective_vplan_kernel, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.nseq, pl.X, pl.Y, count,
-                       scan, aggt, seqt, a.D, a.N, a.h0, a.h_last);
+                       scan, aggt, seqt, piece, a.D, a.N, a.h0, a.h_last);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return a.out_bf16 ? launch_packed_by_n<bf16_t, bf16_t>(p, pl, a.dt_softplus != 0, s)
