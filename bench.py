@@ -49,6 +49,9 @@ _CSRC = "selective_state_space_diag_amd/csrc/"
 _SEL_SOURCES = [_CSRC + f for f in ("selective.hip", "common.hpp", "kernels.hpp")]
 _H2_SOURCES = [_CSRC + f for f in ("hgrn2.hip", "h2_layout.hpp", "common.hpp", "kernels.hpp")]
 _SCAN1_SOURCES = [_CSRC + f for f in ("scan1.hip", "common.hpp", "kernels.hpp")]
+_SWEEP_SOURCES = [_CSRC + f for f in ("hgrn2_sweep.hip", "common.hpp", "kernels.hpp")]
+_CONV_SOURCES = [_CSRC + f for f in ("conv1d.hip", "common.hpp", "kernels.hpp")]
+_NORM_SOURCES = [_CSRC + f for f in ("norm.hip", "common.hpp", "kernels.hpp")]
 # Workload -> (summary file under profiles/, what one call is, the kernel sources the summary's counter
 # figures hold for: a figure is used only while the sha256 of these files is the one stored with it).
 PROFILES = {
@@ -67,6 +70,39 @@ PROFILES = {
     "rglru_bf16_B8_L8192_D2560": ("rglru_scan_B8_L8192_D2560.md",
                                   "RG-LRU scan B=8 L=8192 D=2560, bf16 in, fp32 out; one call = one lookback kernel",
                                   _SCAN1_SOURCES),
+    "rglru_gated_bf16_B8_L8192_D2560": ("rglru_gated_scan_B8_L8192_D2560.md",
+                                        "RG-LRU scan with the gelu(gate) output multiply, B=8 L=8192 D=2560, bf16 in, "
+                                        "fp32 out; one call = one lookback kernel", _SCAN1_SOURCES),
+    "rglru_fp32_B2_L128_D64": ("rglru_scan_B2_L128_D64_fp32.md",
+                               "RG-LRU scan B=2 L=128 D=64 fp32 (one-pass short kernel), called from Python and 64 "
+                               "times from a HIP graph", _SCAN1_SOURCES),
+    "rglru_backward": ("rglru_backward_B8_L8192_D2560.md",
+                       "RG-LRU backward B=8 L=8192 D=2560 bf16: a forward with chunk states, then the backward with "
+                       "them and without them (record pass)", _SCAN1_SOURCES),
+    "minmax": ("minmax_B8_L8192_D2560.md",
+               "MinMax scan B=8 L=8192 D=2560 bf16, a forward with chunk states, and the backward with them and "
+               "without them (record pass)", _SCAN1_SOURCES),
+    "rglru_decode": ("rglru_update_B256_D2560.md",
+                     "RG-LRU decode steps B=256 D=2560 bf16: 256 steps from Python, then from a HIP graph, then a "
+                     "same-size device copy from a graph", _SCAN1_SOURCES),
+    "causal_conv1d_bf16_B8_L8192_D2560_W4": ("causal_conv1d_B8_L8192_D2560_W4.md",
+                                             "Causal depthwise conv W=4, B=8 L=8192 D=2560 bf16; one call = one "
+                                             "kernel", _CONV_SOURCES),
+    "selective_backward_bf16_B4_L2048_D1536_N16": ("selective_backward_B4_L2048_D1536_N16.md",
+                                                   "Selective scan backward B=4 L=2048 D=1536 N=16 bf16 in, fp32 "
+                                                   "gradients", _SEL_SOURCES),
+    "selective_backward_varlen_L131072_D4096_N16_32seq": ("selective_backward_varlen_L131072_D4096_N16.md",
+                                                          "Packed varlen selective scan backward, L=131072 in 32 "
+                                                          "sequences, D=4096 N=16 bf16", _SEL_SOURCES),
+    "hgrn2_backward_bf16_B8_H16_d128_L4096": ("hgrn2_backward_B8_H16_d128_L4096.md",
+                                              "HGRN2 backward B=8 H=16 d=128 L=4096 bf16, the forward output given "
+                                              "(one forward call first)", _SWEEP_SOURCES),
+    "hgrn2_key_gate_bf16_B8_H16_d128_L4096": ("hgrn2_key_gate_scan_B8_H16_d128_L4096.md",
+                                              "HGRN2 scan with the gate on the key axis, B=8 H=16 d=128 L=4096 bf16 "
+                                              "(register sweep)", _SWEEP_SOURCES),
+    "readout_norm_B8_L4096_width2048": ("readout_norm_B8_L4096_width2048.md",
+                                        "Readout LayerNorm and silu gate over 32768 rows of 2048 features (one HGRN2 "
+                                        "forward call first)", _NORM_SOURCES),
 }
 
 
@@ -751,9 +787,12 @@ def summarize_profile(folder, workload):
         lines += [f"* `{c.strip().replace('<file>.md', fname)}`" for c in open(cmd_path) if c.strip()]
         lines += [""]
     rec = _last_json(os.path.join(folder, "trace.log"))
-    call = None
+    call = None  # the run's one record (per-call figures are given only when the run has exactly one)
     if rec is not None:
-        call = rec if "metric" in rec else next(iter(rec.get("forms", {}).values()), None)
+        if "metric" in rec:
+            call = rec
+        elif len(rec.get("forms", {})) == 1:
+            call = next(iter(rec["forms"].values()))
     lines += ["## Kernel durations (kernel trace)", "",
               "| kernel | grid threads | wg | VGPRs | LDS B | dispatches | per call | avg µs (--stats) | median µs | min µs |",
               "|---|---|---|---|---|---|---|---|---|---|"]
@@ -763,7 +802,12 @@ def summarize_profile(folder, workload):
         lines.append(f"| `{_short_kernel(n)}` | {g} | {w} | {vg} | {lds} | {len(dur[n])} | {mult[n]} | "
                      f"{stats.get(n, float('nan')):.2f} | {med(dur[n]):.2f} | {min(dur[n]):.2f} |")
     per_call_us = sum(mult[n] * stats.get(n, sum(dur[n]) / len(dur[n])) for n in dur)
-    lines += ["", f"Sum of the average kernel durations per call: {per_call_us:.1f} µs."]
+    if call is not None:
+        lines += ["", f"Sum of the average kernel durations per call: {per_call_us:.1f} µs."]
+    elif rec is not None:
+        lines += ["", "The run times several calls (the bench's records below); the kernel rows cover them all:", ""]
+        lines += [f"* `{n}`: {r.get('ms', float('nan')) * 1e3:.1f} µs per step (median "
+                  f"{r.get('median_ms', float('nan')) * 1e3:.1f} µs)" for n, r in rec.get("forms", {}).items()]
     if call is not None:
         lines += [f"The bench's HIP-event timing of the same command: {call.get('ms_per_step', call.get('ms')) * 1e3:.1f} µs "
                   f"per call (mean over the timed steps; median {call.get('median_ms_per_step', call.get('median_ms')) * 1e3:.1f} µs)."]
@@ -785,13 +829,14 @@ def summarize_profile(folder, workload):
                   f"and bytes written = WRITE_SIZE × 1024 × {fw:.3f}.", "",
                   "| kernel | FETCH_SIZE KiB / dispatch (median) | WRITE_SIZE KiB / dispatch | read MB / dispatch | "
                   "written MB / dispatch |", "|---|---|---|---|---|"]
-        traffic = 0.0
+        traffic = 0.0  # per call: meaningful only for a run with one record
         for n in order:
             fk, wk = med(fetch.get(n, {}).get("FETCH_SIZE", [])), med(write.get(n, {}).get("WRITE_SIZE", []))
             rd, wr = fk * 1024 * ff, wk * 1024 * fw
             lines.append(f"| `{_short_kernel(n)}` | {fk:.1f} | {wk:.1f} | {rd / 1e6:.1f} | {wr / 1e6:.1f} |")
             traffic += mult[n] * (rd + wr)
-        data["traffic_bytes_per_call"] = int(traffic)
+        if call is not None:
+            data["traffic_bytes_per_call"] = int(traffic)
         alg = None
         if call is not None:
             alg = call["roofline"]["algorithmic_bytes_per_call"] if "roofline" in call else call.get("algorithmic_bytes")
