@@ -767,39 +767,74 @@ __global__ __launch_bounds__(kBWaves * 64) void rglru_bwd_kernel(Bwd1Params p) {
   }
   __syncthreads();
   const uint32_t E = __builtin_amdgcn_readfirstlane(s_epoch);
-  for (int parity = 0;; parity ^= 1) {
-    const unsigned long long ticket = uniform_ticket(s_tick[parity]);
-    if (ticket == kNoUnit) break;
-    const SeqChunk sc = unit_seq_chunk(ticket, n_seq);
-    const int64_t cr = sc.chunk;  // reverse chunk index
-    const int64_t c = p.n_chunks - 1 - cr;
-    const int64_t b = sc.seq / p.n_tiles, k = sc.seq - b * p.n_tiles;
-    const int rows = (int)min<int64_t>(kChunk, p.L - c * kChunk);
+  constexpr int es = sizeof(Tin);
+  const uint32_t row_in = (uint32_t)(p.D * es);
+  // Geometry of a unit (its reverse and forward chunk index, batch row, tile and rows) and the
+  // window over its rows of one [B, L, D] array with e-byte elements.
+  struct G {
+    int64_t cr, c, b, k;
+    int rows;
+  };
+  auto geom = [&](unsigned long long t) {
+    const SeqChunk sc = unit_seq_chunk(t, n_seq);
+    G g;
+    g.cr = sc.chunk;
+    g.c = p.n_chunks - 1 - g.cr;
+    g.b = sc.seq / p.n_tiles;
+    g.k = sc.seq - g.b * p.n_tiles;
+    g.rows = (int)min<int64_t>(kChunk, p.L - g.c * kChunk);
+    return g;
+  };
+  auto window_of = [&](const G& g, const void* a, int e) {
+    return make_window(static_cast<const char*>(a) + ((g.b * p.L + g.c * kChunk) * p.D) * e, (uint32_t)(g.rows * p.D * e));
+  };
+  // Loads of a unit's x, r, i and dy rows (rows past the chunk read its last row; results unused).
+  // Without an output gate the next unit's rows are loaded while this unit resolves its carry and
+  // writes its gradients (PREFETCH); with one, the registers are not there and each unit loads its
+  // own rows first.
+  constexpr bool PREFETCH = !GATE;
+  typedef typename LD::raw Raw4[4][kBSteps];
+  auto fetch4 = [&](unsigned long long t, Raw4& r4) {
+    const G g = geom(t);
+    const int64_t c0 = g.k * TW + (int64_t)lane * V;
+    const uint32_t li = (uint32_t)((c0 < p.D ? c0 : p.D - V) * es);
+    const auto w0 = window_of(g, p.x, es), w1 = window_of(g, p.r, es), w2 = window_of(g, p.i, es),
+               w3 = window_of(g, p.dy, es);
+  #pragma unroll
+    for (int s = 0; s < kBSteps; ++s) {
+      const uint32_t ro = (uint32_t)min(wave * kBSteps + s, g.rows - 1) * row_in;
+      r4[0][s] = LD::load(w0, li, ro);
+      r4[1][s] = LD::load(w1, li, ro);
+      r4[2][s] = LD::load(w2, li, ro);
+      r4[3][s] = LD::load(w3, li, ro);
+    }
+  };
+  Raw4 cur, nxt;
+  unsigned long long ticket = uniform_ticket(s_tick[0]);
+  if (ticket != kNoUnit) fetch4(ticket, cur);
+  for (int parity = 0; ticket != kNoUnit; parity ^= 1) {
+    const G gu = geom(ticket);
+    const int64_t cr = gu.cr, c = gu.c, b = gu.b, k = gu.k;
+    const int rows = gu.rows;
     const int64_t ch0 = k * TW + (int64_t)lane * V;
     const bool ch_ok = ch0 < p.D;  // V = 2 only when D is even
     const int64_t chl = ch_ok ? ch0 : p.D - V;
     const int64_t t0 = c * kChunk + (int64_t)wave * kBSteps;
     const int nvalid = rows - wave * kBSteps;
-
-    // ---- loads of the unit's rows (rows past the chunk read its last row; results unused)
-    constexpr int es = sizeof(Tin);
-    auto window = [&](const void* a, int e) {
-      return make_window(static_cast<const char*>(a) + ((b * p.L + c * kChunk) * p.D) * e, (uint32_t)(rows * p.D * e));
-    };
-    const auto wx = window(p.x, es), wr = window(p.r, es), wi = window(p.i, es), wd = window(p.dy, es);
-    const auto wg = window(GATE ? p.gate : p.x, es);
-    const uint32_t row_in = (uint32_t)(p.D * es), lane_in = (uint32_t)(chl * es);
-    typename LD::raw rx[kBSteps], rrl[kBSteps], ril[kBSteps], rdy[kBSteps], rg[GATE ? kBSteps : 1];
+    auto window = [&](const void* a, int e) { return window_of(gu, a, e); };
+    const uint32_t lane_in = (uint32_t)(chl * es);
+    typename LD::raw(&rx)[kBSteps] = cur[0];
+    typename LD::raw(&rrl)[kBSteps] = cur[1];
+    typename LD::raw(&ril)[kBSteps] = cur[2];
+    typename LD::raw(&rdy)[kBSteps] = cur[3];
+    typename LD::raw rg[GATE ? kBSteps : 1];
+    if (GATE) {
+      const auto wg = window(p.gate, es);
   #pragma unroll
-    for (int s = 0; s < kBSteps; ++s) {
-      const uint32_t ro = (uint32_t)min(wave * kBSteps + s, rows - 1) * row_in;
-      rx[s] = LD::load(wx, lane_in, ro);
-      rrl[s] = LD::load(wr, lane_in, ro);
-      ril[s] = LD::load(wi, lane_in, ro);
-      rdy[s] = LD::load(wd, lane_in, ro);
-      if (GATE) rg[GATE ? s : 0] = LD::load(wg, lane_in, ro);
+      for (int s = 0; s < kBSteps; ++s)
+        rg[GATE ? s : 0] = LD::load(wg, lane_in, (uint32_t)min(wave * kBSteps + s, rows - 1) * row_in);
     }
-    uint32_t m_next = 0;  // next unit, one ahead (thread 0; resolved at the end of this unit)
+    uint32_t m_next = 0;  // next unit, one ahead (thread 0; resolved before the first barrier)
     if (threadIdx.x == 0) m_next = take_begin(p.ctl, xc, left);
     float kc[V];
   #pragma unroll
@@ -848,7 +883,10 @@ __global__ __launch_bounds__(kBWaves * 64) void rglru_bwd_kernel(Bwd1Params p) {
       s_rA[wave][lane * V + v] = rA[v];
       s_rB[wave][lane * V + v] = rB[v];
     }
-    __syncthreads();
+    if (threadIdx.x == 0) s_tick[parity ^ 1] = take_end(p.ctl, n_seq, (uint32_t)p.n_chunks, xc, left, m_next);
+    __syncthreads();  // wave aggregates in LDS; the next ticket is visible
+    const unsigned long long next = uniform_ticket(s_tick[parity ^ 1]);
+    if (PREFETCH && next != kNoUnit) fetch4(next, nxt);  // in flight during this unit's lookback and stores
 
     // ---- waves 0 .. V-1: chunk reverse aggregate, publish, reverse carry (lookback over later
     //      chunks), one channel of the tile per lane
@@ -933,8 +971,18 @@ __global__ __launch_bounds__(kBWaves * 64) void rglru_bwd_kernel(Bwd1Params p) {
         p.dalog_part[(b * p.n_chunks + c) * p.D + chj] = acc;
       }
     }
-    if (threadIdx.x == 0) s_tick[parity ^ 1] = take_end(p.ctl, n_seq, (uint32_t)p.n_chunks, xc, left, m_next);
-    __syncthreads();  // this unit's LDS is free; the next ticket is visible
+    __syncthreads();  // this unit's LDS is free
+    if (next != kNoUnit) {
+      if (PREFETCH) {
+  #pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+  #pragma unroll
+          for (int s = 0; s < kBSteps; ++s) cur[q4][s] = nxt[q4][s];
+      } else {
+        fetch4(next, cur);
+      }
+    }
+    ticket = next;
   }
   if (threadIdx.x == 0) finish_launch(p.ctl, E);
 }
