@@ -319,7 +319,7 @@ int ssd_selective_scan_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t 
  *   dA                  : [D, N] fp32;  dDskip, ddt_bias : [D] fp32 or NULL;
  *   dh0                 : [B or nseq, D, N] fp32 or NULL (a zero-length sequence gets its dh_last)
  * Every output is overwritten (not accumulated).  The forward states are recomputed (the workspace
- * holds per-16-row-segment states, about 5 x B * ceil(L/16) * D * N fp32; see "Workspaces", size
+ * holds per-64-row-unit states, about 6 x B * ceil(L/64) * D * N fp32; see "Workspaces", size
  * from ssd_selective_scan_backward_workspace_bytes).  Reductions run in a fixed order: results are
  * deterministic.  Errors as ssd_selective_scan, plus SSD_ERR_NULL for missing dy / dx / ddt / dBm /
  * dCm / dA (or dz with z). */

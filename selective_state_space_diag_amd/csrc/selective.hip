@@ -857,20 +857,26 @@ hipError_t launch_packed_by_n(const SelParams& p, const Plan& pl, bool softplus,
 //   dC_tn = sum_d ds_t h_tn,  dB_tn = sum_d g_tn delta_t x_t,  and with m = [delta A <= 20] (the clamp
 //   passes no gradient above 20): d delta_t = x_t sum_n g B + sum_n m g h_{t-1} abar A_n,
 //   dA_n = sum m g h_{t-1} abar delta,  d dt = d delta softplus'(dt + bias),  d dt_bias = sum d dt.
-// Passes over segments of kBT rows, one lane per channel as in the forward:
-//   1. the forward's aggregate and carry passes (segment length kBT): the state entering each segment;
-//   2. reverse aggregates of segments >= 1: q at the segment's start from q = 0 at its end, prod abar;
-//   3. reverse carry: q at each segment's end;
-//   4. per segment: for one state at a time, forward through the rows keeping h_{t-1} and abar, then
-//      back, accumulating the row gradients; dB and dC are summed over the workgroup's channels by a
-//      lane butterfly and across its waves in LDS; dA, dDskip and d dt_bias leave per-segment sums;
-//   5. fixed-order sums of the partial results.
-constexpr int kBT = 16;  // rows per backward segment
+// Passes over units of kBU rows (kBS sub-blocks of kBT rows), one lane per channel as in the forward:
+//   1. per unit, from zero, in one sweep over its rows: the state it reaches (H), prod abar (P), and
+//      q at its first row from q = 0 past its end (Q = sum_t (prod_{s <= t} abar_s) ds_t C_t);
+//   2. one thread per (sequence, state, channel): the state entering each unit (forward) and q at
+//      each unit's end (reverse);
+//   3. per unit: a forward sweep from its entering state gives the states at its sub-block starts
+//      (bf16 inputs: its raw dt and x stay in LDS for the rest of the unit); then the sub-blocks
+//      from the last to the first, each one state at a time: forward through its rows keeping
+//      h_{t-1} and abar, back through them carrying q, accumulating the row gradients; dB and dC
+//      are summed over the workgroup's channels by a lane butterfly and across its waves in LDS;
+//      dA, dDskip and d dt_bias leave per-unit sums;
+//   4. fixed-order sums of the partial results.
+constexpr int kBT = 16;         // rows per sub-block (the register tile of pass 3)
+constexpr int kBS = 4;          // sub-blocks per unit
+constexpr int kBU = kBT * kBS;  // rows per unit
 
 struct SelBwdParams {
-  int64_t L, D, nseg, nblk, BL;  // batched: L rows per sequence, nseg segments each; BL rows in all
+  int64_t L, D, nseg, nblk, BL;  // batched: L rows per sequence, nseg units each; BL rows in all
   const int32_t* cu;             // packed varlen: boundaries, or NULL (then the fields below are unused)
-  const int2* units;             // (sequence, segment) per unit
+  const int2* units;             // (sequence, unit index within it) per unit
   const int* n_units;            // number of units (device)
   const int2* seq_units;         // (first unit, unit count) per sequence
   const void* x;
@@ -884,34 +890,36 @@ struct SelBwdParams {
   const float* h0;
   const void* dy;
   const float* dh_last;
-  const float* carry;  // [unit][N][D] state entering segments >= 1 (pass 1)
-  float* aggP;         // [unit][N][D] prod abar of the segment (pass 2)
-  float* aggQ;         // [unit][N][D] q at the segment's start from 0 at its end (pass 2)
-  float* qend;         // [unit][N][D] q at the segment's end (pass 3)
+  float* aggP;  // [unit][N][D] prod abar over the unit (pass 1)
+  float* aggH;  // [unit][N][D] the state the unit reaches from 0
+  float* aggQ;  // [unit][N][D] q at the unit's first row from 0 past its end
+  float* hin;   // [unit][N][D] the state entering the unit (pass 2)
+  float* qend;  // [unit][N][D] q past the unit's last row (pass 2)
   void* dx;
   void* ddt;
   void* dz;
-  float* dBm_part;     // [nblk][B L][N] per channel block
+  float* dBm_part;  // [nblk][B L][N] per channel block
   float* dCm_part;
-  float* dA_part;      // [unit][N][D]
-  float* dD_part;      // [unit][D]
-  float* dbias_part;   // [unit][D]
-  float* dh0;          // [B][D][N] or NULL
+  float* dA_part;     // [unit][N][D]
+  float* dD_part;     // [unit][D]
+  float* dbias_part;  // [unit][D]
+  float* dh0;         // [B][D][N] or NULL
 };
 
-// Unit u of the backward passes: its sequence, segment, first row and row count.
+// Unit u of the backward passes: its sequence, first row and row count, and whether it is its
+// sequence's first and last.
 struct BUnit {
-  int64_t seq, seg, row0;
+  int64_t seq, row0;
   int R;
-  bool valid;
+  bool valid, first, last;
 };
 __device__ __forceinline__ BUnit bwd_unit(const SelBwdParams& p, int64_t u) {
   BUnit r;
-  int64_t end;
+  int64_t seg, end;
   if (p.cu == nullptr) {
     r.seq = u / p.nseg;
-    r.seg = u - r.seq * p.nseg;
-    r.row0 = r.seq * p.L + r.seg * kBT;
+    seg = u - r.seq * p.nseg;
+    r.row0 = r.seq * p.L + seg * kBU;
     end = (r.seq + 1) * p.L;
     r.valid = true;
   } else {
@@ -919,98 +927,241 @@ __device__ __forceinline__ BUnit bwd_unit(const SelBwdParams& p, int64_t u) {
     if (!r.valid) return r;
     const int2 e = p.units[u];
     r.seq = e.x;
-    r.seg = e.y;
-    r.row0 = (int64_t)p.cu[r.seq] + r.seg * kBT;
+    seg = e.y;
+    r.row0 = (int64_t)p.cu[r.seq] + seg * kBU;
     end = p.cu[r.seq + 1];
   }
-  r.R = (int)min<int64_t>(kBT, end - r.row0);
+  r.R = (int)min<int64_t>(kBU, end - r.row0);
+  r.first = seg == 0;
+  r.last = r.row0 + r.R == end;
   return r;
 }
 
+// The step of row t for the backward passes: v = dt + bias, delta = softplus(v) (or v).  With fp32
+// inputs the sum is carried as s + err (a two-sum: err is the exact rounding error of s) and the
+// softplus and its derivative take err to first order.  Rounding dt + bias (|dt| of a few units) loses
+// up to 2^-24 |dt| of absolute value, which softplus passes on relative to its far smaller result; left
+// in, it is the largest error of d dt (a third of the fp32 total in an emulation of these passes).
+struct StepIn {
+  float s, err;
+};
+template <typename Tin>
+__device__ __forceinline__ StepIn step_in(float dt, float bias) {
+  StepIn r;
+  r.s = dt + bias;
+  if constexpr (sizeof(Tin) == 2) {
+    r.err = 0.0f;
+  } else {
+    const float bb = r.s - dt;
+    r.err = (dt - (r.s - bb)) + (bias - bb);
+  }
+  return r;
+}
+template <typename Tin, bool SOFTPLUS>
+__device__ __forceinline__ float step_delta(StepIn v) {
+  if (!SOFTPLUS) return v.s;
+  const float sp = softplus_in<Tin>(v.s);
+  if constexpr (sizeof(Tin) == 2) {
+    return sp;
+  } else {
+    const float sg = hw_exp2((v.s - sp) * kLog2e);  // softplus'(s) = sigmoid(s) = e^(s - softplus(s))
+    return v.s > 20.0f ? sp : fmaf(sg, v.err, sp);
+  }
+}
 // softplus'(v) as torch takes it: sigmoid(v), and 1 above the threshold 20.
-__device__ __forceinline__ float softplus_grad_f(float v) { return v > 20.0f ? 1.0f : sigmoid_acc_f(v); }
+template <typename Tin>
+__device__ __forceinline__ float step_grad(StepIn v) {
+  if (v.s > 20.0f) return 1.0f;
+  const float sg = sigmoid_acc_f(v.s);
+  if constexpr (sizeof(Tin) == 2) return sg;
+  else return fmaf(sg * (1.0f - sg), v.err, sg);
+}
 // silu'(z) = sigmoid(z) (1 + z (1 - sigmoid(z)))
 __device__ __forceinline__ float silu_grad_f(float z) {
   const float sg = sigmoid_acc_f(z);
   return sg * fmaf(z, 1.0f - sg, 1.0f);
 }
 
-// Sum of v[j] over the 64 lanes of the wave, for 16 values j at once: each exchange step halves the
-// values a lane keeps (the half picked by one lane bit) and adds its partner's other half.  On return
-// lanes with (lane & 3) == 0 hold the total of value (lane >> 2) & 15 in v[0].
-template <int HALF>
-__device__ __forceinline__ void wave_sum_step(float (&v)[16], int lane) {
-  constexpr int kBit = HALF * 4;  // 32, 16, 8, 4 for HALF = 8, 4, 2, 1
-  const bool hi = (lane & kBit) != 0;
+// The lane's row of A scaled to base 2, and the wave's discretisation (as load_A).
+template <int NS, bool SOFTPLUS>
+__device__ __forceinline__ int bwd_load_A(const float* A, int64_t dl, float* A2) {
+  bool nonpos = true;
 #pragma unroll
-  for (int i = 0; i < HALF; ++i) {
-    const float send = hi ? v[i] : v[i + HALF];
-    const float keep = hi ? v[i + HALF] : v[i];
-    v[i] = keep + __shfl_xor(send, kBit);
+  for (int n = 0; n < NS; ++n) {
+    const float a = A[dl * NS + n];
+    A2[n] = a * kLog2e;
+    nonpos = nonpos && !(a > 0.0f);
   }
-}
-__device__ __forceinline__ void wave_sum16(float (&v)[16], int lane) {
-  wave_sum_step<8>(v, lane);
-  wave_sum_step<4>(v, lane);
-  wave_sum_step<2>(v, lane);
-  wave_sum_step<1>(v, lane);
-  v[0] += __shfl_xor(v[0], 2);
-  v[0] += __shfl_xor(v[0], 1);
+  return (SOFTPLUS && __all(nonpos)) ? kExp : kClamp;
 }
 
-// Pass 2: reverse aggregates of segments >= 1 (a sequence's first segment needs none).
+// The unit's rows of B and C, as fp32 [row][n] (rows past the unit read as 0).
+template <typename Tin, int NS>
+__device__ __forceinline__ void stage_bc(const SelBwdParams& p, int64_t row0, int R, float* sB, float* sC) {
+  for (int e = threadIdx.x; e < kBU * NS; e += kThreads) {
+    const int t = e / NS;
+    const int64_t idx = (row0 + min(t, R - 1)) * NS + (e - t * NS);
+    sB[e] = t < R ? io<Tin>::load(p.Bm, idx) : 0.0f;
+    sC[e] = t < R ? io<Tin>::load(p.Cm, idx) : 0.0f;
+  }
+}
+
+// Sum of v[j] over the 64 lanes of the wave, for 16 values j at once: each exchange step halves the
+// values a lane keeps (the half picked by one lane bit) and adds its partner's other half.  On return
+// lanes with (lane & 3) == 0 hold the total of value (lane >> 2) & 15 in v[0].  All exchanges are VALU
+// lane moves: v_permlane32_swap / v_permlane16_swap for partners 32 and 16 lanes apart (the pair
+// (v[i], v[i + H]) comes back as (lower half of both, upper half of both), so one add leaves each half
+// with the sum of the value it keeps), then DPP within a row of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppRor8 = 0x128;        // lane l of a row reads lane (l + 8) mod 16
+constexpr int kDppHalfMirror = 0x141;  // lane l of 8 reads lane 7 - l
+constexpr int kDppQuad2301 = 0x4E;     // lane l of 4 reads l ^ 2
+constexpr int kDppQuad1032 = 0xB1;     // lane l of 4 reads l ^ 1
+__device__ __forceinline__ void wave_sum16(float (&v)[16], int lane) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {  // lanes 32 apart: the lower half keeps v[i], the upper v[i + 8]
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 8]), false, false);
+    v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // rows 16 apart: even rows keep v[i], odd rows v[i + 4]
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 4]), false, false);
+    v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  const bool b3 = (lane & 8) != 0, b2 = (lane & 4) != 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {  // lanes 8 apart
+    const float lo = v[i] + dpp_mov<kDppRor8>(v[i]), hi = v[i + 2] + dpp_mov<kDppRor8>(v[i + 2]);
+    v[i] = b3 ? hi : lo;
+  }
+  {  // lanes 4 apart (l and 7 - l differ in bit 2 and agree above it)
+    const float lo = v[0] + dpp_mov<kDppHalfMirror>(v[0]), hi = v[1] + dpp_mov<kDppHalfMirror>(v[1]);
+    v[0] = b2 ? hi : lo;
+  }
+  v[0] += dpp_mov<kDppQuad2301>(v[0]);
+  v[0] += dpp_mov<kDppQuad1032>(v[0]);
+}
+
+// ----------------------------------------------------------------------------- pass 1
+// Within a unit the rows go in blocks of kBT: a block's state from zero (Hk) and its weighted adjoint
+// sum (Qk, with the running product of abar restarted at the block) are folded into the unit's with the
+// block's decay product applied as one exponential, 2^(A2 sum delta) (2^(sum of the clamped exponents)
+// when the clamp can act), so no product of rounded decays runs longer than a block.
+template <typename Tin, int NS, bool SOFTPLUS, bool GATE, int DISC>
+__device__ __forceinline__ void bwd_agg_rows(const SelBwdParams& p, int64_t row0, int R, int64_t dl,
+                                             const float* A2, float bias, const float* sB, const float* sC,
+                                             float* P, float* H, float* Q) {
+  using W = win<Tin, 1>;
+  constexpr int es = sizeof(Tin);
+  static_assert(kBT % kPrefetch == 0, "blocks hold whole prefetch groups");
+  const auto wdt = unit_window(p.dt, row0, R, p.D, es), wxx = unit_window(p.x, row0, R, p.D, es);
+  const auto wdy = unit_window(p.dy, row0, R, p.D, es), wzz = unit_window(GATE ? p.z : p.dy, row0, R, p.D, es);
+  const uint32_t lane_in = (uint32_t)(dl * es), row_in = (uint32_t)(p.D * es);
+  typename W::raw rd[kPrefetch], rx[kPrefetch], ry[kPrefetch], rz[kPrefetch];
+#pragma unroll
+  for (int k = 0; k < kPrefetch; ++k) {
+    const uint32_t ro = (uint32_t)min(k, R - 1) * row_in;
+    rd[k] = W::load(wdt, lane_in, ro);
+    rx[k] = W::load(wxx, lane_in, ro);
+    ry[k] = W::load(wdy, lane_in, ro);
+    if (GATE) rz[k] = W::load(wzz, lane_in, ro);
+  }
+  float es_tot[NS];     // the clamped exponents summed over the blocks done (clamp variant)
+  float sd_tot = 0.0f;  // delta summed over the blocks done
+#pragma unroll
+  for (int n = 0; n < NS; ++n) { H[n] = 0.0f; Q[n] = 0.0f; es_tot[n] = 0.0f; }
+  for (int blk0 = 0; blk0 < R; blk0 += kBT) {
+    float hk[NS], qk[NS], cp[NS], es_k[NS];
+    float sd_k = 0.0f;
+#pragma unroll
+    for (int n = 0; n < NS; ++n) { hk[n] = 0.0f; qk[n] = 0.0f; cp[n] = 1.0f; es_k[n] = 0.0f; }
+    for (int base = blk0; base < blk0 + kBT; base += kPrefetch) {
+#pragma unroll
+      for (int k = 0; k < kPrefetch; ++k) {
+        const int i = base + k;
+        const StepIn sv = step_in<Tin>(W::get(rd[k], 0), bias);
+        const float xx = W::get(rx[k], 0), dyv = W::get(ry[k], 0);
+        const float zz = GATE ? W::get(rz[k], 0) : 0.0f;
+        const uint32_t ro = (uint32_t)min(i + kPrefetch, R - 1) * row_in;
+        rd[k] = W::load(wdt, lane_in, ro);
+        rx[k] = W::load(wxx, lane_in, ro);
+        ry[k] = W::load(wdy, lane_in, ro);
+        if (GATE) rz[k] = W::load(wzz, lane_in, ro);
+        if (i < R) {
+          const float delta = step_delta<Tin, SOFTPLUS>(sv);
+          const float dxv = delta * xx;
+          const float dsv = GATE ? dyv * silu_acc_f(zz) : dyv;
+          const float* b = sB + i * NS;
+          const float* c = sC + i * NS;
+#pragma unroll
+          for (int n = 0; n < NS; ++n) {
+            float e = delta * A2[n];
+            if (DISC == kClamp) {
+              e = e > kClampLog2 ? kClampLog2 : e;
+              es_k[n] += e;
+            }
+            const float ab = hw_exp2(e);
+            hk[n] = fmaf(ab, hk[n], dxv * b[n]);
+            cp[n] *= ab;
+            qk[n] = fmaf(cp[n], dsv * c[n], qk[n]);
+            if (NS > 8 && (n & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+          }
+          sd_k += delta;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // fold the block: H = P_k H + Hk;  Q += (decay of the blocks before) Qk
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+      const float before = DISC == kClamp ? hw_exp2(es_tot[n]) : hw_exp2(A2[n] * sd_tot);
+      Q[n] = fmaf(before, qk[n], Q[n]);
+      const float Pk = DISC == kClamp ? hw_exp2(es_k[n]) : hw_exp2(A2[n] * sd_k);
+      H[n] = fmaf(Pk, H[n], hk[n]);
+      es_tot[n] += es_k[n];
+    }
+    sd_tot += sd_k;
+  }
+#pragma unroll
+  for (int n = 0; n < NS; ++n) P[n] = DISC == kClamp ? hw_exp2(es_tot[n]) : hw_exp2(A2[n] * sd_tot);
+}
+
 template <typename Tin, int NS, bool SOFTPLUS, bool GATE>
 __global__ __launch_bounds__(kThreads) void selective_bwd_agg_kernel(SelBwdParams p) {
   const int64_t u = blockIdx.x;
   const BUnit U = bwd_unit(p, u);
-  if (!U.valid || U.seg == 0) return;
-  const int64_t row0 = U.row0;
-  const int R = U.R;
+  if (!U.valid || (U.first && U.last)) return;  // a sequence of one unit needs no aggregates
   const int64_t d = (int64_t)blockIdx.y * kThreads + threadIdx.x;
   const bool active = d < p.D;
-  const int64_t dl = active ? d : p.D - 1;
-  __shared__ float sC[kBT * NS];
-  for (int e = threadIdx.x; e < kBT * NS; e += kThreads) {
-    const int t = e / NS;
-    sC[e] = t < R ? io<Tin>::load(p.Cm, (row0 + t) * NS + (e - t * NS)) : 0.0f;
-  }
+  const int64_t dl = active ? d : p.D - 1;  // lanes past D recompute channel D-1 and store nothing
+  __shared__ float sB[kBU * NS], sC[kBU * NS];
+  stage_bc<Tin, NS>(p, U.row0, U.R, sB, sC);
   float A2[NS];
-#pragma unroll
-  for (int n = 0; n < NS; ++n) A2[n] = p.A[dl * NS + n] * kLog2e;
+  const int disc = bwd_load_A<NS, SOFTPLUS>(p.A, dl, A2);
   const float bias = p.dt_bias ? p.dt_bias[dl] : 0.0f;
-  using W = win<Tin, 1>;
-  constexpr int es = sizeof(Tin);
-  const auto wdt = unit_window(p.dt, row0, R, p.D, es), wdy = unit_window(p.dy, row0, R, p.D, es);
-  const auto wzz = unit_window(GATE ? p.z : p.dt, row0, R, p.D, es);
-  const uint32_t lane_in = (uint32_t)(dl * es), row_in = (uint32_t)(p.D * es);
-  float delta[kBT], ds[kBT];
-#pragma unroll
-  for (int t = 0; t < kBT; ++t) {
-    const uint32_t ro = (uint32_t)min(t, R - 1) * row_in;
-    const float v = W::get(W::load(wdt, lane_in, ro), 0) + bias;
-    const float dyv = W::get(W::load(wdy, lane_in, ro), 0);
-    const float g = GATE ? silu_acc_f(W::get(W::load(wzz, lane_in, ro), 0)) : 1.0f;
-    delta[t] = t < R ? (SOFTPLUS ? softplus_in<Tin>(v) : v) : 0.0f;  // rows past the sequence: identity
-    ds[t] = t < R ? dyv * g : 0.0f;
-  }
   __syncthreads();
+  float P[NS], H[NS], Q[NS];
+  if (disc == kExp)
+    bwd_agg_rows<Tin, NS, SOFTPLUS, GATE, kExp>(p, U.row0, U.R, dl, A2, bias, sB, sC, P, H, Q);
+  else
+    bwd_agg_rows<Tin, NS, SOFTPLUS, GATE, kClamp>(p, U.row0, U.R, dl, A2, bias, sB, sC, P, H, Q);
   if (!active) return;
-#pragma unroll 1
-  for (int n = 0; n < NS; ++n) {
-    float q = 0.0f, e_sum = 0.0f;
 #pragma unroll
-    for (int t = kBT - 1; t >= 0; --t) {
-      float e = delta[t] * A2[n];
-      e = e > kClampLog2 ? kClampLog2 : e;
-      e_sum += e;
-      q = hw_exp2(e) * fmaf(ds[t], sC[t * NS + n], q);
-    }
-    p.aggQ[(u * NS + n) * p.D + d] = q;
-    p.aggP[(u * NS + n) * p.D + d] = hw_exp2(e_sum);
+  for (int n = 0; n < NS; ++n) {
+    const int64_t idx = (u * NS + n) * p.D + d;
+    p.aggP[idx] = P[n];
+    p.aggH[idx] = H[n];
+    p.aggQ[idx] = Q[n];
   }
 }
 
-// Pass 3: one thread per (sequence, state, channel), segments from the last to the first.
+// ----------------------------------------------------------------------------- pass 2
+// One thread per (sequence, state, channel): units in order for the entering states, then in reverse
+// for q; the aggregates of kCarryBatch units are loaded together ahead of their sequential use.
+constexpr int kCarryBatch = 8;
 template <int NS>
 __global__ __launch_bounds__(kThreads) void selective_bwd_carry_kernel(SelBwdParams p, int64_t nseq) {
   const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -1025,167 +1176,374 @@ __global__ __launch_bounds__(kThreads) void selective_bwd_carry_kernel(SelBwdPar
     first = r.x;
     count = r.y;
   }
+  const int64_t base = (first * NS + n) * p.D + d, stride = NS * p.D;
+  float h = p.h0 ? p.h0[(seq * p.D + d) * NS + n] : 0.0f;
+  for (int64_t s0 = 0; s0 < count; s0 += kCarryBatch) {
+    float Pv[kCarryBatch], Hv[kCarryBatch];
+#pragma unroll
+    for (int k = 0; k < kCarryBatch; ++k) {
+      const int64_t s = s0 + k;
+      const bool need = s + 1 < count;  // the last unit's aggregate is not used
+      Pv[k] = need ? p.aggP[base + s * stride] : 0.0f;
+      Hv[k] = need ? p.aggH[base + s * stride] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < kCarryBatch; ++k) {
+      const int64_t s = s0 + k;
+      if (s < count) {
+        p.hin[base + s * stride] = h;
+        h = fmaf(Pv[k], h, Hv[k]);
+      }
+    }
+  }
   float q = p.dh_last ? p.dh_last[(seq * p.D + d) * NS + n] : 0.0f;
   if (count == 0 && p.dh0) p.dh0[(seq * p.D + d) * NS + n] = q;  // empty sequence: dh0 = dh_last
-  for (int64_t s = count - 1; s >= 0; --s) {
-    const int64_t idx = ((first + s) * NS + n) * p.D + d;
-    p.qend[idx] = q;
-    if (s > 0) q = fmaf(p.aggP[idx], q, p.aggQ[idx]);
+  for (int64_t s0 = count - 1; s0 >= 0; s0 -= kCarryBatch) {
+    float Pv[kCarryBatch], Qv[kCarryBatch];
+#pragma unroll
+    for (int k = 0; k < kCarryBatch; ++k) {
+      const int64_t s = s0 - k;
+      const bool need = s > 0;  // the first unit's aggregate is not used
+      Pv[k] = need ? p.aggP[base + s * stride] : 0.0f;
+      Qv[k] = need ? p.aggQ[base + s * stride] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < kCarryBatch; ++k) {
+      const int64_t s = s0 - k;
+      if (s >= 0) {
+        p.qend[base + s * stride] = q;
+        q = fmaf(Pv[k], q, Qv[k]);
+      }
+    }
   }
 }
 
-// Pass 4.
-template <typename Tin, typename Tout, int NS, bool SOFTPLUS, bool GATE>
-__global__ __launch_bounds__(kThreads) void selective_bwd_kernel(SelBwdParams p) {
-  static_assert(kBT == 16, "the dB / dC butterfly sums 16 rows");
-  const int64_t u = blockIdx.x;
-  const BUnit U = bwd_unit(p, u);
-  if (!U.valid) return;
-  const int64_t seq = U.seq, seg = U.seg, row0 = U.row0;
+// ----------------------------------------------------------------------------- pass 3
+// LDS of one unit.  With bf16 inputs the unit's raw dt and x stay here from the forward sweep to the
+// last sub-block; dy and z pass through a two-slot ring (the sub-block being worked on and the next).
+template <typename Raw, int NS, bool STASH>
+struct BwdLds {
+  Raw dt[STASH ? kBU : 1][kThreads];
+  Raw x[STASH ? kBU : 1][kThreads];
+  Raw dy[2][kBT][kThreads];
+  Raw z[2][kBT][kThreads];
+  float ab[kBT][kThreads];  // one state's abar and h_{t-1} over the sub-block, per thread
+  float hp[kBT][kThreads];
+  float B[kBU * NS], C[kBU * NS];    // [row][n]
+  alignas(16) float Bt[NS][kBU];     // [n][row]: one state's rows of a sub-block are contiguous
+  alignas(16) float Ct[NS][kBU];
+  float redB[NS][kThreads / 64][kBT], redC[NS][kThreads / 64][kBT];
+};
+
+template <typename Tin, typename Tout, int NS, bool SOFTPLUS, bool GATE, int DISC, typename Lds>
+__device__ __forceinline__ void bwd_grad_unit(const SelBwdParams& p, const BUnit& U, int64_t u, int64_t d,
+                                              int64_t dl, bool active, Lds& S) {
+  constexpr bool STASH = sizeof(Tin) == 2;
+  using W = win<Tin, 1>;
+  using Raw = typename W::raw;
+  constexpr int es = sizeof(Tin);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row0 = U.row0;
   const int R = U.R;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t d = (int64_t)blockIdx.y * kThreads + threadIdx.x;
-  const bool active = d < p.D;
-  const int64_t dl = active ? d : p.D - 1;  // lanes past D recompute channel D-1 and store nothing
-  __shared__ float sB[kBT * NS], sC[kBT * NS];
-  __shared__ float sRedB[NS][kThreads / 64][kBT], sRedC[NS][kThreads / 64][kBT];
-  __shared__ float sAb[kBT][kThreads], sHp[kBT][kThreads];  // one state's abar and h_{t-1}, per thread
-  for (int e = threadIdx.x; e < kBT * NS; e += kThreads) {
-    const int t = e / NS;
-    const int64_t idx = (row0 + min(t, R - 1)) * NS + (e - t * NS);
-    sB[e] = io<Tin>::load(p.Bm, idx);
-    sC[e] = io<Tin>::load(p.Cm, idx);
-  }
+  const int nsb = (R + kBT - 1) / kBT;
+  const auto wdt = unit_window(p.dt, row0, R, p.D, es), wxx = unit_window(p.x, row0, R, p.D, es);
+  const auto wdy = unit_window(p.dy, row0, R, p.D, es), wzz = unit_window(GATE ? p.z : p.dy, row0, R, p.D, es);
+  const uint32_t lane_in = (uint32_t)(dl * es), row_in = (uint32_t)(p.D * es);
+  auto ro_of = [&](int r) { return (uint32_t)min(r, R - 1) * row_in; };
   const float bias = p.dt_bias ? p.dt_bias[dl] : 0.0f;
   const float dskip = p.Dskip ? p.Dskip[dl] : 0.0f;
-  // per row: delta, x, ds = dy silu(z); rows past the sequence are exact identities (delta = x = ds = 0).
-  // (dt, dy and z are read again for the row gradients at the end, from L2.)
-  using W = win<Tin, 1>;
-  constexpr int es = sizeof(Tin);
-  const auto wdt = unit_window(p.dt, row0, R, p.D, es), wxx = unit_window(p.x, row0, R, p.D, es);
-  const auto wdy = unit_window(p.dy, row0, R, p.D, es), wzz = unit_window(GATE ? p.z : p.x, row0, R, p.D, es);
-  const uint32_t lane_in = (uint32_t)(dl * es), row_in = (uint32_t)(p.D * es);
-  auto ld = [&](const __amdgpu_buffer_rsrc_t& w, int t) {
-    return W::get(W::load(w, lane_in, (uint32_t)min(t, R - 1) * row_in), 0);
-  };
-  float delta[kBT], dx_[kBT], ds[kBT];  // dx_ = delta x
-#pragma unroll
-  for (int t = 0; t < kBT; ++t) {
-    const bool ok = t < R;
-    const float v = ld(wdt, t) + bias;
-    const float xx = ld(wxx, t);
-    const float dyv = ld(wdy, t);
-    const float g = GATE ? silu_acc_f(ld(wzz, t)) : 1.0f;
-    delta[t] = ok ? (SOFTPLUS ? softplus_in<Tin>(v) : v) : 0.0f;
-    dx_[t] = delta[t] * (ok ? xx : 0.0f);
-    ds[t] = ok ? dyv * g : 0.0f;
-  }
-  float sacc[kBT], GB[kBT], MA[kBT];
-#pragma unroll
-  for (int t = 0; t < kBT; ++t) { sacc[t] = 0.0f; GB[t] = 0.0f; MA[t] = 0.0f; }
-  __syncthreads();
 
-  // the state's entering value, its value of q at the segment's end and its A, loaded one state ahead
-  auto h_in = [&](int n) {
-    return seg == 0 ? (p.h0 ? p.h0[(seq * p.D + dl) * NS + n] : 0.0f) : p.carry[(u * NS + n) * p.D + dl];
-  };
-  float nx_h = h_in(0), nx_q = p.qend[u * NS * p.D + dl], nx_A = p.A[dl * NS];
-#pragma unroll 1
-  for (int n = 0; n < NS; ++n) {
-    const float An = nx_A;
-    const float A2 = An * kLog2e;
-    float h = nx_h;
-    float q = nx_q;
-    if (n + 1 < NS) {
-      nx_h = h_in(n + 1);
-      nx_q = p.qend[(u * NS + n + 1) * p.D + dl];
-      nx_A = p.A[dl * NS + n + 1];
-    }
-    // forward through the rows (abar and h_{t-1} of this state kept in LDS for the way back)
-    float v[16];
-    uint32_t live = 0;  // bit t: the clamp does not act at row t
+  // dy and z of the last sub-block into its ring slot
+  {
+    const int j = nsb - 1;
 #pragma unroll
     for (int t = 0; t < kBT; ++t) {
-      float e = delta[t] * A2;
-      live |= (e <= kClampLog2 ? 1u : 0u) << t;
-      e = e > kClampLog2 ? kClampLog2 : e;
-      const float ab = hw_exp2(e);
-      sAb[t][threadIdx.x] = ab;
-      sHp[t][threadIdx.x] = h;
-      h = fmaf(ab, h, dx_[t] * sB[t * NS + n]);
-      sacc[t] = fmaf(sC[t * NS + n], h, sacc[t]);
-      v[t] = active ? ds[t] * h : 0.0f;  // this lane's share of dC_tn (idle lanes add nothing)
-    }
-    wave_sum16(v, lane);
-    if ((lane & 3) == 0) sRedC[n][wave][(lane >> 2) & 15] = v[0];
-    // (a compiler-only memory fence: abar and h_{t-1} are read back from LDS rather than kept live)
-    asm volatile("" ::: "memory");
-    // back through the rows
-    float dA = 0.0f;
-#pragma unroll
-    for (int t = kBT - 1; t >= 0; --t) {
-      const float ab = sAb[t][threadIdx.x], hp = sHp[t][threadIdx.x];
-      const float g = fmaf(ds[t], sC[t * NS + n], q);
-      q = ab * g;
-      const float mab = (live >> t) & 1u ? (g * hp) * ab : 0.0f;  // d abar times abar, unclamped rows
-      MA[t] = fmaf(mab, An, MA[t]);
-      dA = fmaf(mab, delta[t], dA);
-      GB[t] = fmaf(g, sB[t * NS + n], GB[t]);
-      v[t] = active ? g * dx_[t] : 0.0f;  // this lane's share of dB_tn
-    }
-    wave_sum16(v, lane);
-    if ((lane & 3) == 0) sRedB[n][wave][(lane >> 2) & 15] = v[0];
-    if (active) {
-      p.dA_part[(u * NS + n) * p.D + d] = dA;
-      if (seg == 0 && p.dh0) p.dh0[(seq * p.D + d) * NS + n] = q;
+      S.dy[j & 1][t][tid] = W::load(wdy, lane_in, ro_of(j * kBT + t));
+      if (GATE) S.z[j & 1][t][tid] = W::load(wzz, lane_in, ro_of(j * kBT + t));
     }
   }
 
-  // row gradients
+  // ---- forward sweep: the states at the sub-block starts.  After it s3 holds the start of sub-block
+  // nsb-1, s2 of nsb-2, s1 of nsb-3, s0 of nsb-4 (those that exist).
+  float s0[NS], s1[NS], s2[NS], s3[NS];
+  {
+    float A2[NS], h[NS];
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+      A2[n] = p.A[dl * NS + n] * kLog2e;
+      h[n] = p.hin[(u * NS + n) * p.D + dl];
+      s0[n] = 0.0f; s1[n] = 0.0f; s2[n] = 0.0f; s3[n] = h[n];
+    }
+    const int nload = STASH ? nsb : nsb - 1;  // 16-row blocks read here
+    Raw rd[kBT], rx[kBT];
+    if (nload > 0) {
+#pragma unroll
+      for (int t = 0; t < kBT; ++t) {
+        rd[t] = W::load(wdt, lane_in, ro_of(t));
+        rx[t] = W::load(wxx, lane_in, ro_of(t));
+      }
+    }
+    for (int k = 0; k < nload; ++k) {
+      Raw nd[kBT], nx[kBT];
+      if (k + 1 < nload) {
+#pragma unroll
+        for (int t = 0; t < kBT; ++t) {
+          nd[t] = W::load(wdt, lane_in, ro_of((k + 1) * kBT + t));
+          nx[t] = W::load(wxx, lane_in, ro_of((k + 1) * kBT + t));
+        }
+      }
+      if constexpr (STASH) {
+#pragma unroll
+        for (int t = 0; t < kBT; ++t) {
+          S.dt[k * kBT + t][tid] = rd[t];
+          S.x[k * kBT + t][tid] = rx[t];
+        }
+      }
+      if (k < nsb - 1) {  // every row of this block is inside the unit
+        // the block's state from zero, then h = (decay of the block, one exponential) h + that
+        float hk[NS], es_k[NS];
+        float sd_k = 0.0f;
+#pragma unroll
+        for (int n = 0; n < NS; ++n) { hk[n] = 0.0f; es_k[n] = 0.0f; }
+#pragma unroll
+        for (int t = 0; t < kBT; ++t) {
+          const float delta = step_delta<Tin, SOFTPLUS>(step_in<Tin>(W::get(rd[t], 0), bias));
+          const float dxv = delta * W::get(rx[t], 0);
+          const float* b = S.B + (k * kBT + t) * NS;
+#pragma unroll
+          for (int n = 0; n < NS; ++n) {
+            float e = delta * A2[n];
+            if (DISC == kClamp) {
+              e = e > kClampLog2 ? kClampLog2 : e;
+              es_k[n] += e;
+            }
+            hk[n] = fmaf(hw_exp2(e), hk[n], dxv * b[n]);
+            if (NS > 8 && (n & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+          }
+          sd_k += delta;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+          const float Pk = DISC == kClamp ? hw_exp2(es_k[n]) : hw_exp2(A2[n] * sd_k);
+          h[n] = fmaf(Pk, h[n], hk[n]);
+          s0[n] = s1[n]; s1[n] = s2[n]; s2[n] = s3[n]; s3[n] = h[n];
+        }
+      }
+      if (k + 1 < nload) {
+#pragma unroll
+        for (int t = 0; t < kBT; ++t) { rd[t] = nd[t]; rx[t] = nx[t]; }
+      }
+    }
+  }
+
+  // ---- the sub-blocks, last to first
   using WO = win<Tout, 1>;
   const auto wox = unit_window(p.dx, row0, R, p.D, sizeof(Tout)), wot = unit_window(p.ddt, row0, R, p.D, sizeof(Tout));
   const auto woz = unit_window(GATE ? p.dz : p.dx, row0, R, p.D, sizeof(Tout));
   const uint32_t lane_out = (uint32_t)(dl * (int64_t)sizeof(Tout)), row_out = (uint32_t)(p.D * (int64_t)sizeof(Tout));
-  float dsum = 0.0f, bsum = 0.0f;
+  float qv[NS], dAv[NS];
 #pragma unroll
-  for (int t = 0; t < kBT; ++t) {
-    const float xx = t < R ? ld(wxx, t) : 0.0f;
-    const float ddelta = fmaf(xx, GB[t], MA[t]);
-    const float gdt = SOFTPLUS ? ddelta * softplus_grad_f(ld(wdt, t) + bias) : ddelta;
-    const float gx = fmaf(ds[t], dskip, delta[t] * GB[t]);
-    float gz = 0.0f;
-    if (GATE) gz = ld(wdy, t) * silu_grad_f(ld(wzz, t)) * fmaf(dskip, xx, sacc[t]);
-    dsum = fmaf(ds[t], xx, dsum);
-    if (t < R) bsum += gdt;
-    if (active && t < R) {
-      WO::store(wox, lane_out, (uint32_t)t * row_out, &gx);
-      WO::store(wot, lane_out, (uint32_t)t * row_out, &gdt);
-      if (GATE) WO::store(woz, lane_out, (uint32_t)t * row_out, &gz);
+  for (int n = 0; n < NS; ++n) {
+    qv[n] = p.qend[(u * NS + n) * p.D + dl];
+    dAv[n] = 0.0f;
+  }
+  float dsum = 0.0f, bsum = 0.0f;
+  for (int j = nsb - 1; j >= 0; --j) {
+    const int slot = j & 1;
+    const int Rj = min(kBT, R - j * kBT);
+    const int r0 = j * kBT;
+    // the previous sub-block's dy and z: loaded now, put in the other slot after the state loop
+    Raw ny[kBT], nz[kBT];
+    if (j > 0) {
+#pragma unroll
+      for (int t = 0; t < kBT; ++t) {
+        ny[t] = W::load(wdy, lane_in, (uint32_t)(r0 - kBT + t) * row_in);
+        if (GATE) nz[t] = W::load(wzz, lane_in, (uint32_t)(r0 - kBT + t) * row_in);
+      }
     }
+    __syncthreads();  // this sub-block's ring slot and the stash are written; red is free again
+    auto raw_dt = [&](int t) { return STASH ? S.dt[r0 + t][tid] : W::load(wdt, lane_in, ro_of(r0 + t)); };
+    auto raw_x = [&](int t) { return STASH ? S.x[r0 + t][tid] : W::load(wxx, lane_in, ro_of(r0 + t)); };
+    // per row: delta, delta x, ds = dy silu(z); rows past the unit and lanes past D: exact zeros
+    float delta[kBT], dx_[kBT], ds[kBT];
+#pragma unroll
+    for (int t = 0; t < kBT; ++t) {
+      const bool ok = t < Rj;
+      const float xx = W::get(raw_x(t), 0);
+      const float dyv = W::get(S.dy[slot][t][tid], 0);
+      const float g = GATE ? silu_acc_f(W::get(S.z[slot][t][tid], 0)) : 1.0f;
+      const float dl_ = step_delta<Tin, SOFTPLUS>(step_in<Tin>(W::get(raw_dt(t), 0), bias));
+      delta[t] = ok ? dl_ : 0.0f;
+      dx_[t] = ok && active ? dl_ * xx : 0.0f;
+      ds[t] = ok && active ? dyv * g : 0.0f;
+      if (ok) dsum = fmaf(ds[t], xx, dsum);
+    }
+    float sd_j = 0.0f;  // delta summed over the sub-block (rows past the unit add 0)
+#pragma unroll
+    for (int t = 0; t < kBT; ++t) sd_j += delta[t];
+    float sacc[kBT], GB[kBT], MA[kBT];
+#pragma unroll
+    for (int t = 0; t < kBT; ++t) { sacc[t] = 0.0f; GB[t] = 0.0f; MA[t] = 0.0f; }
+
+#pragma unroll 1
+    for (int n = 0; n < NS; ++n) {
+      const float An = p.A[dl * NS + n];
+      const float A2 = An * kLog2e;
+      // this state's B and C over the sub-block's rows, read four rows at a time
+      const float4* Bn4 = reinterpret_cast<const float4*>(&S.Bt[n][r0]);
+      const float4* Cn4 = reinterpret_cast<const float4*>(&S.Ct[n][r0]);
+      float h = s3[n];
+      const float q_in = qv[n];
+      float q = q_in;
+      // forward through the rows (abar and h_{t-1} of this state kept in LDS for the way back)
+      float v[16];
+      uint32_t live = 0;  // bit t: the clamp does not act at row t
+      float es_j = 0.0f;  // the clamped exponents summed (clamp variant, last row first)
+#pragma unroll
+      for (int t4 = 0; t4 < kBT / 4; ++t4) {
+        const float4 b4 = Bn4[t4], c4 = Cn4[t4];
+        const float bb[4] = {b4.x, b4.y, b4.z, b4.w}, cc[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int t = 4 * t4 + k;
+          float e = delta[t] * A2;
+          if (DISC == kClamp) {
+            live |= (e <= kClampLog2 ? 1u : 0u) << t;
+            e = e > kClampLog2 ? kClampLog2 : e;
+          }
+          const float ab = hw_exp2(e);
+          S.ab[t][tid] = ab;
+          S.hp[t][tid] = h;
+          h = fmaf(ab, h, dx_[t] * bb[k]);
+          sacc[t] = fmaf(cc[k], h, sacc[t]);
+          v[t] = ds[t] * h;  // this lane's share of dC_tn
+        }
+      }
+      wave_sum16(v, lane);
+      if ((lane & 3) == 0) S.redC[n][wave][(lane >> 2) & 15] = v[0];
+      // (a compiler-only memory fence: abar and h_{t-1} are read back from LDS rather than kept live)
+      asm volatile("" ::: "memory");
+      float dA = 0.0f;
+      float qz = 0.0f;  // q from zero past the sub-block's end
+#pragma unroll
+      for (int t4 = kBT / 4 - 1; t4 >= 0; --t4) {
+        const float4 b4 = Bn4[t4], c4 = Cn4[t4];
+        const float bb[4] = {b4.x, b4.y, b4.z, b4.w}, cc[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+        for (int k = 3; k >= 0; --k) {
+          const int t = 4 * t4 + k;
+          const float ab = S.ab[t][tid], hp = S.hp[t][tid];
+          const float g = fmaf(ds[t], cc[k], q);
+          q = ab * g;
+          qz = ab * fmaf(ds[t], cc[k], qz);
+          float mab = (g * hp) * ab;  // d abar times abar
+          if (DISC == kClamp) {
+            mab = (live >> t) & 1u ? mab : 0.0f;  // no gradient through the clamp
+            const float e = delta[t] * A2;          // the clamped exponents summed from the sub-block's end
+            es_j += e > kClampLog2 ? kClampLog2 : e;
+          }
+          MA[t] = fmaf(mab, An, MA[t]);
+          dA = fmaf(mab, delta[t], dA);
+          GB[t] = fmaf(g, bb[k], GB[t]);
+          v[t] = g * dx_[t];  // this lane's share of dB_tn
+        }
+      }
+      wave_sum16(v, lane);
+      if ((lane & 3) == 0) S.redB[n][wave][(lane >> 2) & 15] = v[0];
+      // q entering the earlier sub-block: q from zero plus q_in carried by the sub-block's decay product
+      // taken as one exponential, so no chain of rounded decays runs past a sub-block
+      const float Pj = DISC == kClamp ? hw_exp2(es_j) : hw_exp2(A2 * sd_j);
+      qv[n] = fmaf(Pj, q_in, qz);
+      dAv[n] += dA;
+    }
+
+    // row gradients
+#pragma unroll
+    for (int t = 0; t < kBT; ++t) {
+      if (t < Rj) {
+        const float xx = W::get(raw_x(t), 0);
+        const float ddelta = fmaf(xx, GB[t], MA[t]);
+        const float gdt = SOFTPLUS ? ddelta * step_grad<Tin>(step_in<Tin>(W::get(raw_dt(t), 0), bias)) : ddelta;
+        const float gx = fmaf(ds[t], dskip, delta[t] * GB[t]);
+        float gz = 0.0f;
+        if (GATE) {
+          const float dyv = W::get(S.dy[slot][t][tid], 0), zz = W::get(S.z[slot][t][tid], 0);
+          gz = dyv * silu_grad_f(zz) * fmaf(dskip, xx, sacc[t]);
+        }
+        bsum += gdt;
+        if (active) {
+          WO::store(wox, lane_out, (uint32_t)(r0 + t) * row_out, &gx);
+          WO::store(wot, lane_out, (uint32_t)(r0 + t) * row_out, &gdt);
+          if (GATE) WO::store(woz, lane_out, (uint32_t)(r0 + t) * row_out, &gz);
+        }
+      }
+    }
+    if (j > 0) {
+#pragma unroll
+      for (int t = 0; t < kBT; ++t) {
+        S.dy[slot ^ 1][t][tid] = ny[t];
+        if (GATE) S.z[slot ^ 1][t][tid] = nz[t];
+      }
+    }
+    // dB / dC of this sub-block's rows for this channel block: the waves' sums, in wave order
+    __syncthreads();
+    for (int e = tid; e < NS * kBT; e += kThreads) {
+      const int n = e / kBT, t = e - n * kBT;
+      float sb = 0.0f, sc = 0.0f;
+#pragma unroll
+      for (int wv = 0; wv < kThreads / 64; ++wv) {
+        sb += S.redB[n][wv][t];
+        sc += S.redC[n][wv][t];
+      }
+      if (t < Rj) {
+        const int64_t row = (int64_t)blockIdx.y * p.BL + row0 + r0 + t;
+        p.dBm_part[row * NS + n] = sb;
+        p.dCm_part[row * NS + n] = sc;
+      }
+    }
+    // the next (earlier) sub-block starts where s2 said
+#pragma unroll
+    for (int n = 0; n < NS; ++n) { s3[n] = s2[n]; s2[n] = s1[n]; s1[n] = s0[n]; }
   }
   if (active) {
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+      p.dA_part[(u * NS + n) * p.D + d] = dAv[n];
+      if (U.first && p.dh0) p.dh0[(U.seq * p.D + d) * NS + n] = qv[n];
+    }
     p.dD_part[u * p.D + d] = dsum;
     p.dbias_part[u * p.D + d] = bsum;
   }
-  // dB / dC of this channel block: the waves' sums, in wave order
-  __syncthreads();
-  for (int e = threadIdx.x; e < NS * kBT; e += kThreads) {
-    const int n = e / kBT, t = e - n * kBT;
-    float sb = 0.0f, sc = 0.0f;
-#pragma unroll
-    for (int wv = 0; wv < kThreads / 64; ++wv) {
-      sb += sRedB[n][wv][t];
-      sc += sRedC[n][wv][t];
-    }
-    if (t < R) {
-      p.dBm_part[((int64_t)blockIdx.y * p.BL + row0 + t) * NS + n] = sb;
-      p.dCm_part[((int64_t)blockIdx.y * p.BL + row0 + t) * NS + n] = sc;
-    }
-  }
 }
 
-// Pass 5: fixed-order sums.  dBm, dCm: over channel blocks; dA [D][N], dDskip, d dt_bias: over units.
+template <typename Tin, typename Tout, int NS, bool SOFTPLUS, bool GATE>
+__global__ __launch_bounds__(kThreads, 1) void selective_bwd_kernel(SelBwdParams p) {
+  const int64_t u = blockIdx.x;
+  const BUnit U = bwd_unit(p, u);
+  if (!U.valid) return;
+  const int64_t d = (int64_t)blockIdx.y * kThreads + threadIdx.x;
+  const bool active = d < p.D;
+  const int64_t dl = active ? d : p.D - 1;  // lanes past D recompute channel D-1 and store nothing
+  __shared__ BwdLds<typename win<Tin, 1>::raw, NS, sizeof(Tin) == 2> S;
+  stage_bc<Tin, NS>(p, U.row0, U.R, S.B, S.C);
+  for (int e = threadIdx.x; e < kBU * NS; e += kThreads) {
+    const int n = e / kBU, t = e - n * kBU;
+    const int64_t idx = (U.row0 + min(t, U.R - 1)) * NS + n;
+    S.Bt[n][t] = t < U.R ? io<Tin>::load(p.Bm, idx) : 0.0f;
+    S.Ct[n][t] = t < U.R ? io<Tin>::load(p.Cm, idx) : 0.0f;
+  }
+  bool nonpos = true;
+#pragma unroll
+  for (int n = 0; n < NS; ++n) nonpos = nonpos && !(p.A[dl * NS + n] > 0.0f);
+  __syncthreads();
+  if (SOFTPLUS && __all(nonpos))
+    bwd_grad_unit<Tin, Tout, NS, SOFTPLUS, GATE, kExp>(p, U, u, d, dl, active, S);
+  else
+    bwd_grad_unit<Tin, Tout, NS, SOFTPLUS, GATE, kClamp>(p, U, u, d, dl, active, S);
+}
+
+// Pass 4: fixed-order sums.  dBm, dCm: over channel blocks; dA [D][N], dDskip, d dt_bias: over units.
 template <typename Tout>
 __global__ __launch_bounds__(kThreads) void selective_bwd_bc_kernel(const float* PB, const float* PC, int64_t nblk,
                                                                     int64_t total, void* dBm, void* dCm) {
@@ -1226,16 +1584,20 @@ __global__ __launch_bounds__(kThreads) void selective_bwd_final_kernel(const flo
   out[d * N + n] = acc;
 }
 
-template <typename Tin, typename Tout, int NS, bool SOFTPLUS>
-void launch_bwd_n(const SelBwdParams& q, int64_t U, int64_t nseq, bool gate, hipStream_t s) {
+template <typename Tin, typename Tout, int NS, bool SOFTPLUS, bool GATE>
+void launch_bwd_g(const SelBwdParams& q, int64_t U, int64_t nseq, hipStream_t s) {
   const dim3 grid((unsigned)U, (unsigned)q.nblk), blk(kThreads);
-  if (gate) hipLaunchKernelGGL((selective_bwd_agg_kernel<Tin, NS, SOFTPLUS, true>), grid, blk, 0, s, q);
-  else hipLaunchKernelGGL((selective_bwd_agg_kernel<Tin, NS, SOFTPLUS, false>), grid, blk, 0, s, q);
+  hipLaunchKernelGGL((selective_bwd_agg_kernel<Tin, NS, SOFTPLUS, GATE>), grid, blk, 0, s, q);
   const int64_t nthreads = nseq * NS * q.D;
   hipLaunchKernelGGL((selective_bwd_carry_kernel<NS>), dim3((unsigned)((nthreads + kThreads - 1) / kThreads)), blk, 0,
                      s, q, nseq);
-  if (gate) hipLaunchKernelGGL((selective_bwd_kernel<Tin, Tout, NS, SOFTPLUS, true>), grid, blk, 0, s, q);
-  else hipLaunchKernelGGL((selective_bwd_kernel<Tin, Tout, NS, SOFTPLUS, false>), grid, blk, 0, s, q);
+  hipLaunchKernelGGL((selective_bwd_kernel<Tin, Tout, NS, SOFTPLUS, GATE>), grid, blk, 0, s, q);
+}
+
+template <typename Tin, typename Tout, int NS, bool SOFTPLUS>
+void launch_bwd_n(const SelBwdParams& q, int64_t U, int64_t nseq, bool gate, hipStream_t s) {
+  if (gate) launch_bwd_g<Tin, Tout, NS, SOFTPLUS, true>(q, U, nseq, s);
+  else launch_bwd_g<Tin, Tout, NS, SOFTPLUS, false>(q, U, nseq, s);
 }
 
 template <typename Tin, typename Tout, int NS>
@@ -1341,12 +1703,12 @@ struct BwdLayout {
 BwdLayout bwd_layout(const SelectiveBwdArgs& a) {
   BwdLayout l;
   if (a.cu_seqlens == nullptr) {
-    l.nseg = (a.L + kBT - 1) / kBT;
+    l.nseg = (a.L + kBU - 1) / kBU;
     l.U = a.B * l.nseg;
     l.tbl = l.seqtbl = 0;
   } else {
     l.nseg = 0;
-    l.U = (a.L + kBT - 1) / kBT + a.nseq;  // sum over sequences of ceil(len / kBT)
+    l.U = (a.L + kBU - 1) / kBU + a.nseq;  // sum over sequences of ceil(len / kBU)
     l.tbl = align256(256 + (size_t)l.U * sizeof(int2));
     l.seqtbl = align256((size_t)a.nseq * sizeof(int2));
   }
@@ -1357,81 +1719,57 @@ BwdLayout bwd_layout(const SelectiveBwdArgs& a) {
   l.slices = align256((size_t)(kSumSlices * a.N * a.D) * sizeof(float));
   return l;
 }
-
-template <typename Tin, int NS>
-void launch_fwd_carry(const SelParams& f, int64_t U, bool softplus, hipStream_t s) {
-  const dim3 grid((unsigned)U, (unsigned)((f.D + kThreads - 1) / kThreads));
-  if (softplus) hipLaunchKernelGGL((selective_aggregate_kernel<Tin, NS, true>), grid, dim3(kThreads), 0, s, f);
-  else hipLaunchKernelGGL((selective_aggregate_kernel<Tin, NS, false>), grid, dim3(kThreads), 0, s, f);
-  const int64_t nthreads = f.nseq * NS * f.D;
-  hipLaunchKernelGGL((selective_carry_kernel<NS, 1>), dim3((unsigned)((nthreads + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, s, f);
-}
-template <typename Tin>
-void launch_fwd_carry_t(const SelParams& f, int64_t U, bool softplus, hipStream_t s) {
-  switch (f.N) {
-    case 1: launch_fwd_carry<Tin, 1>(f, U, softplus, s); break;
-    case 2: launch_fwd_carry<Tin, 2>(f, U, softplus, s); break;
-    case 4: launch_fwd_carry<Tin, 4>(f, U, softplus, s); break;
-    case 8: launch_fwd_carry<Tin, 8>(f, U, softplus, s); break;
-    default: launch_fwd_carry<Tin, 16>(f, U, softplus, s); break;
-  }
-}
 }  // namespace
 
 size_t selective_scan_backward_scratch_bytes(const SelectiveBwdArgs& a) {
   const BwdLayout l = bwd_layout(a);
-  return workspace_head_bytes() + 5 * l.state + 2 * l.row + 2 * l.bc + l.slices + l.tbl + l.seqtbl;
+  return workspace_head_bytes() + 6 * l.state + 2 * l.row + 2 * l.bc + l.slices + l.tbl + l.seqtbl;
 }
 
 hipError_t launch_selective_scan_backward(const SelectiveBwdArgs& a, hipStream_t s) {
   const BwdLayout l = bwd_layout(a);
-  char* base = static_cast<char*>(a.scratch) + workspace_head_bytes();
-  float* carry = reinterpret_cast<float*>(base);
-  float* aggP = reinterpret_cast<float*>(base + l.state);
-  float* aggQ = reinterpret_cast<float*>(base + 2 * l.state);
-  float* qend = reinterpret_cast<float*>(base + 3 * l.state);
-  float* dA_part = reinterpret_cast<float*>(base + 4 * l.state);
-  float* dD_part = reinterpret_cast<float*>(base + 5 * l.state);
-  float* dbias_part = reinterpret_cast<float*>(base + 5 * l.state + l.row);
-  float* PB = reinterpret_cast<float*>(base + 5 * l.state + 2 * l.row);
-  float* PC = reinterpret_cast<float*>(base + 5 * l.state + 2 * l.row + l.bc);
-  float* slices = reinterpret_cast<float*>(base + 5 * l.state + 2 * l.row + 2 * l.bc);  // kSumSlices x (N D)
-  char* tbl = base + 5 * l.state + 2 * l.row + 2 * l.bc + l.slices;
+  char* q0 = static_cast<char*>(a.scratch) + workspace_head_bytes();
+  auto take = [&](size_t bytes) {
+    char* r = q0;
+    q0 += bytes;
+    return reinterpret_cast<float*>(r);
+  };
+  float* hin = take(l.state);
+  float* qend = take(l.state);
+  float* aggP = take(l.state);
+  float* aggH = take(l.state);
+  float* aggQ = take(l.state);
+  float* dA_part = take(l.state);
+  float* dD_part = take(l.row);
+  float* dbias_part = take(l.row);
+  float* PB = take(l.bc);
+  float* PC = take(l.bc);
+  float* slices = take(l.slices);  // kSumSlices x (N D)
+  char* tbl = q0;
   int* n_units = nullptr;
   int2 *units = nullptr, *seq_units = nullptr;
   const int64_t nseq = a.cu_seqlens ? a.nseq : a.B;
-  if (a.cu_seqlens) {  // the forward's planner at segment kBT (no h_last to fill)
+  if (a.cu_seqlens) {  // the forward's planner at the unit length kBU (no h_last to fill)
     n_units = reinterpret_cast<int*>(tbl);
     units = reinterpret_cast<int2*>(tbl + 256);
     seq_units = reinterpret_cast<int2*>(tbl + l.tbl);
-    hipLaunchKernelGGL(selective_plan_kernel, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.nseq, (int64_t)kBT, units,
+    hipLaunchKernelGGL(selective_plan_kernel, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.nseq, (int64_t)kBU, units,
                        n_units, seq_units, a.D, a.N, a.h0, (float*)nullptr);
   }
-  // 1. the state entering every segment: the forward's aggregate and carry passes at segment kBT
-  if (a.cu_seqlens || l.nseg > 1) {
-    SelParams f{};
-    f.L = a.L; f.D = a.D; f.N = a.N; f.nseq = nseq; f.T = kBT; f.nseg = l.nseg;
-    f.cu = a.cu_seqlens; f.units = units; f.n_units = n_units; f.seq_units = seq_units;
-    f.x = a.x; f.dt = a.dt; f.A = a.A; f.Bm = a.Bm; f.Cm = a.Cm; f.dt_bias = a.dt_bias; f.h0 = a.h0;
-    f.aggP = aggP; f.aggH = aggQ; f.carry = carry;
-    if (a.in_bf16) launch_fwd_carry_t<bf16_t>(f, l.U, a.dt_softplus != 0, s);
-    else launch_fwd_carry_t<float>(f, l.U, a.dt_softplus != 0, s);
-  }
-  // 2.-4.
+  // passes 1-3
   SelBwdParams q{};
   q.L = a.L; q.D = a.D; q.nseg = l.nseg; q.nblk = l.nblk; q.BL = a.B * a.L;
   q.cu = a.cu_seqlens; q.units = units; q.n_units = n_units; q.seq_units = seq_units;
   q.x = a.x; q.dt = a.dt; q.A = a.A; q.Bm = a.Bm; q.Cm = a.Cm; q.Dskip = a.Dskip; q.z = a.z; q.dt_bias = a.dt_bias;
   q.h0 = a.h0; q.dy = a.dy; q.dh_last = a.dh_last;
-  q.carry = carry; q.aggP = aggP; q.aggQ = aggQ; q.qend = qend;
+  q.aggP = aggP; q.aggH = aggH; q.aggQ = aggQ; q.hin = hin; q.qend = qend;
   q.dx = a.dx; q.ddt = a.ddt; q.dz = a.dz; q.dBm_part = PB; q.dCm_part = PC;
   q.dA_part = dA_part; q.dD_part = dD_part; q.dbias_part = dbias_part; q.dh0 = a.dh0;
   const bool sp = a.dt_softplus != 0, gate = a.z != nullptr;
   if (!a.in_bf16) launch_bwd_t<float, float>(q, a.N, l.U, nseq, sp, gate, s);
   else if (a.out_bf16) launch_bwd_t<bf16_t, bf16_t>(q, a.N, l.U, nseq, sp, gate, s);
   else launch_bwd_t<bf16_t, float>(q, a.N, l.U, nseq, sp, gate, s);
-  // 5. fixed-order sums
+  // pass 4: fixed-order sums
   const int64_t nbc = a.B * a.L * a.N;
   const dim3 blk(kThreads);
   if (a.out_bf16)

@@ -46,6 +46,24 @@ def assert_close(gpu, ref, tol, what=""):
     return e
 
 
+def elem_err(gpu, ref):
+    """max_i |gpu_i - ref_i| / max(|ref_i|, RMS(ref)): each element against its own magnitude, with the
+    RMS as the floor for the small ones."""
+    g = np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    if r.size == 0:
+        return 0.0
+    den = np.maximum(np.abs(r), max(float(np.sqrt(np.mean(r * r))), 1e-30))
+    return float(np.max(np.abs(g - r) / den))
+
+
+def assert_close_elem(gpu, ref, tol, what=""):
+    e = elem_err(gpu, ref)
+    assert np.all(np.isfinite(np.asarray(gpu, dtype=np.float64))), f"{what}: non-finite GPU output"
+    assert e <= tol, f"{what}: max|err|/max(|ref|, RMS) = {e:.3e} > {tol:.1e}"
+    return e
+
+
 def host(t):
     import torch
     if t.dtype == torch.bfloat16:
