@@ -1227,8 +1227,6 @@ struct BwdLds {
   Raw x[STASH ? kBU : 1][kThreads];
   Raw dy[2][kBT][kThreads];
   Raw z[2][kBT][kThreads];
-  float ab[kBT][kThreads];  // one state's abar and h_{t-1} over the sub-block, per thread
-  float hp[kBT][kThreads];
   float B[kBU * NS], C[kBU * NS];    // [row][n]
   alignas(16) float Bt[NS][kBU];     // [n][row]: one state's rows of a sub-block are contiguous
   alignas(16) float Ct[NS][kBU];
@@ -1396,8 +1394,8 @@ __device__ __forceinline__ void bwd_grad_unit(const SelBwdParams& p, const BUnit
       float h = s3[n];
       const float q_in = qv[n];
       float q = q_in;
-      // forward through the rows (abar and h_{t-1} of this state kept in LDS for the way back)
-      float v[16];
+      // forward through the rows, keeping abar and h_{t-1} for the way back
+      float v[16], abr[kBT], hpr[kBT];
       uint32_t live = 0;  // bit t: the clamp does not act at row t
       float es_j = 0.0f;  // the clamped exponents summed (clamp variant, last row first)
 #pragma unroll
@@ -1413,8 +1411,8 @@ __device__ __forceinline__ void bwd_grad_unit(const SelBwdParams& p, const BUnit
             e = e > kClampLog2 ? kClampLog2 : e;
           }
           const float ab = hw_exp2(e);
-          S.ab[t][tid] = ab;
-          S.hp[t][tid] = h;
+          abr[t] = ab;
+          hpr[t] = h;
           h = fmaf(ab, h, dx_[t] * bb[k]);
           sacc[t] = fmaf(cc[k], h, sacc[t]);
           v[t] = ds[t] * h;  // this lane's share of dC_tn
@@ -1422,8 +1420,6 @@ __device__ __forceinline__ void bwd_grad_unit(const SelBwdParams& p, const BUnit
       }
       wave_sum16(v, lane);
       if ((lane & 3) == 0) S.redC[n][wave][(lane >> 2) & 15] = v[0];
-      // (a compiler-only memory fence: abar and h_{t-1} are read back from LDS rather than kept live)
-      asm volatile("" ::: "memory");
       float dA = 0.0f;
       float qz = 0.0f;  // q from zero past the sub-block's end
 #pragma unroll
@@ -1433,7 +1429,7 @@ __device__ __forceinline__ void bwd_grad_unit(const SelBwdParams& p, const BUnit
 #pragma unroll
         for (int k = 3; k >= 0; --k) {
           const int t = 4 * t4 + k;
-          const float ab = S.ab[t][tid], hp = S.hp[t][tid];
+          const float ab = abr[t], hp = hpr[t];
           const float g = fmaf(ds[t], cc[k], q);
           q = ab * g;
           qz = ab * fmaf(ds[t], cc[k], qz);
