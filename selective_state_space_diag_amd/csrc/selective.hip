@@ -937,6 +937,15 @@ __device__ __forceinline__ BUnit bwd_unit(const SelBwdParams& p, int64_t u) {
   return r;
 }
 
+// The sigmoid of the backward passes: with fp32 inputs through exp_split (about 1 ulp), for derivatives
+// that scale whole gradients; with bf16 inputs (a 2e-2 budget) the plain form.
+template <typename Tin>
+__device__ __forceinline__ float sigmoid_in(float v) {
+  if constexpr (sizeof(Tin) == 2) return sigmoid_f(v);
+  else return sigmoid_acc_f(v);
+}
+template <typename Tin>
+__device__ __forceinline__ float silu_in(float z) { return z * sigmoid_in<Tin>(z); }
 // The step of row t for the backward passes: v = dt + bias, delta = softplus(v) (or v).  With fp32
 // inputs the sum is carried as s + err (a two-sum: err is the exact rounding error of s) and the
 // softplus and its derivative take err to first order.  Rounding dt + bias (|dt| of a few units) loses
@@ -972,13 +981,14 @@ __device__ __forceinline__ float step_delta(StepIn v) {
 template <typename Tin>
 __device__ __forceinline__ float step_grad(StepIn v) {
   if (v.s > 20.0f) return 1.0f;
-  const float sg = sigmoid_acc_f(v.s);
+  const float sg = sigmoid_in<Tin>(v.s);
   if constexpr (sizeof(Tin) == 2) return sg;
   else return fmaf(sg * (1.0f - sg), v.err, sg);
 }
 // silu'(z) = sigmoid(z) (1 + z (1 - sigmoid(z)))
-__device__ __forceinline__ float silu_grad_f(float z) {
-  const float sg = sigmoid_acc_f(z);
+template <typename Tin>
+__device__ __forceinline__ float silu_grad_in(float z) {
+  const float sg = sigmoid_in<Tin>(z);
   return sg * fmaf(z, 1.0f - sg, 1.0f);
 }
 
@@ -1093,7 +1103,7 @@ __device__ __forceinline__ void bwd_agg_rows(const SelBwdParams& p, int64_t row0
         if (i < R) {
           const float delta = step_delta<Tin, SOFTPLUS>(sv);
           const float dxv = delta * xx;
-          const float dsv = GATE ? dyv * silu_acc_f(zz) : dyv;
+          const float dsv = GATE ? dyv * silu_in<Tin>(zz) : dyv;
           const float* b = sB + i * NS;
           const float* c = sC + i * NS;
 #pragma unroll
@@ -1161,7 +1171,7 @@ __global__ __launch_bounds__(kThreads) void selective_bwd_agg_kernel(SelBwdParam
 // ----------------------------------------------------------------------------- pass 2
 // One thread per (sequence, state, channel): units in order for the entering states, then in reverse
 // for q; the aggregates of kCarryBatch units are loaded together ahead of their sequential use.
-constexpr int kCarryBatch = 8;
+constexpr int kCarryBatch = 16;
 template <int NS>
 __global__ __launch_bounds__(kThreads) void selective_bwd_carry_kernel(SelBwdParams p, int64_t nseq) {
   const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -1370,7 +1380,7 @@ __device__ __forceinline__ void bwd_grad_unit(const SelBwdParams& p, const BUnit
       const bool ok = t < Rj;
       const float xx = W::get(raw_x(t), 0);
       const float dyv = W::get(S.dy[slot][t][tid], 0);
-      const float g = GATE ? silu_acc_f(W::get(S.z[slot][t][tid], 0)) : 1.0f;
+      const float g = GATE ? silu_in<Tin>(W::get(S.z[slot][t][tid], 0)) : 1.0f;
       const float dl_ = step_delta<Tin, SOFTPLUS>(step_in<Tin>(W::get(raw_dt(t), 0), bias));
       delta[t] = ok ? dl_ : 0.0f;
       dx_[t] = ok && active ? dl_ * xx : 0.0f;
@@ -1465,7 +1475,7 @@ __device__ __forceinline__ void bwd_grad_unit(const SelBwdParams& p, const BUnit
         float gz = 0.0f;
         if (GATE) {
           const float dyv = W::get(S.dy[slot][t][tid], 0), zz = W::get(S.z[slot][t][tid], 0);
-          gz = dyv * silu_grad_f(zz) * fmaf(dskip, xx, sacc[t]);
+          gz = dyv * silu_grad_in<Tin>(zz) * fmaf(dskip, xx, sacc[t]);
         }
         bsum += gdt;
         if (active) {
@@ -1539,45 +1549,85 @@ __global__ __launch_bounds__(kThreads, 1) void selective_bwd_kernel(SelBwdParams
     bwd_grad_unit<Tin, Tout, NS, SOFTPLUS, GATE, kClamp>(p, U, u, d, dl, active, S);
 }
 
-// Pass 4: fixed-order sums.  dBm, dCm: over channel blocks; dA [D][N], dDskip, d dt_bias: over units.
-template <typename Tout>
-__global__ __launch_bounds__(kThreads) void selective_bwd_bc_kernel(const float* PB, const float* PC, int64_t nblk,
-                                                                    int64_t total, void* dBm, void* dCm) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= total) return;
-  float sb = 0.0f, sc = 0.0f;
-  for (int64_t k = 0; k < nblk; ++k) {
-    sb += PB[k * total + i];
-    sc += PC[k * total + i];
-  }
-  io<Tout>::store(dBm, i, sb);
-  io<Tout>::store(dCm, i, sc);
-}
-
-// Sums over units in two fixed-order steps: slice k of kSumSlices adds units [k U / S, (k + 1) U / S),
-// then the slices are added in order.  Column c = n * D + d of [units][N][D] (or d of [units][D]
-// with N = 1) goes to out[d * N + n].
+// Pass 4: fixed-order sums, in two launches.  dBm, dCm: over channel blocks.  dA [D][N], dDskip and
+// d dt_bias: over units in two steps: slice k of kSumSlices adds units [k U / S, (k + 1) U / S), then the
+// slices are added in order.  The unit sums share one column space: c < N D is column c = n D + d of
+// dA's [units][N][D] partials (it goes to dA[d N + n]), then D columns of dDskip's, then D of dt_bias's
+// (those present).
 constexpr int kSumSlices = 32;
-__global__ __launch_bounds__(kThreads) void selective_bwd_slice_kernel(const float* part, int64_t units,
-                                                                       const int* n_units, int64_t width,
-                                                                       float* slices) {
-  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (c >= width) return;
-  if (n_units) units = *n_units;  // packed varlen: the units the planner made
-  const int64_t k = blockIdx.y, u0 = k * units / kSumSlices, u1 = (k + 1) * units / kSumSlices;
-  float acc = 0.0f;
-  for (int64_t u = u0; u < u1; ++u) acc += part[u * width + c];
-  slices[k * width + c] = acc;
+struct BwdSums {
+  const float* PB;
+  const float* PC;
+  int64_t nblk, nbc;  // channel blocks; B L N
+  void* dBm;
+  void* dCm;
+  const float* dA_part;
+  const float* dD_part;     // or NULL
+  const float* dbias_part;  // or NULL
+  int64_t units;
+  const int* n_units;  // packed varlen: the units the planner made, else NULL
+  int64_t N, D, W;     // W = N D + D (dDskip) + D (d dt_bias)
+  float* slices;       // [kSumSlices][W]
+  float* dA;
+  float* dDskip;
+  float* ddt_bias;
+};
+// the partial buffer, its row width and the column within it of unit-sum column c
+__device__ __forceinline__ const float* sum_column(const BwdSums& a, int64_t c, int64_t& width, int64_t& col) {
+  const int64_t ND = a.N * a.D;
+  if (c < ND) {
+    width = ND;
+    col = c;
+    return a.dA_part;
+  }
+  width = a.D;
+  col = c - ND;
+  if (a.dD_part != nullptr) {
+    if (col < a.D) return a.dD_part;
+    col -= a.D;
+  }
+  return a.dbias_part;
 }
-__global__ __launch_bounds__(kThreads) void selective_bwd_final_kernel(const float* slices, int64_t width, int64_t N,
-                                                                       float* out) {
+// Threads [0, nbc): dBm / dCm;  then kSumSlices x W threads: the slices.
+template <typename Tout>
+__global__ __launch_bounds__(kThreads) void selective_bwd_sums_kernel(BwdSums a) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i < a.nbc) {
+    float sb = 0.0f, sc = 0.0f;
+    for (int64_t k = 0; k < a.nblk; ++k) {
+      sb += a.PB[k * a.nbc + i];
+      sc += a.PC[k * a.nbc + i];
+    }
+    io<Tout>::store(a.dBm, i, sb);
+    io<Tout>::store(a.dCm, i, sc);
+    return;
+  }
+  const int64_t j = i - a.nbc;
+  if (j >= kSumSlices * a.W) return;
+  const int64_t k = j / a.W, c = j - k * a.W;
+  const int64_t units = a.n_units ? (int64_t)*a.n_units : a.units;
+  const int64_t u0 = k * units / kSumSlices, u1 = (k + 1) * units / kSumSlices;
+  int64_t width, col;
+  const float* part = sum_column(a, c, width, col);
+  float acc = 0.0f;
+  for (int64_t u = u0; u < u1; ++u) acc += part[u * width + col];
+  a.slices[k * a.W + c] = acc;
+}
+__global__ __launch_bounds__(kThreads) void selective_bwd_final_kernel(BwdSums a) {
   const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (c >= width) return;
+  if (c >= a.W) return;
   float acc = 0.0f;
 #pragma unroll
-  for (int k = 0; k < kSumSlices; ++k) acc += slices[k * width + c];
-  const int64_t D = width / N, n = c / D, d = c - n * D;
-  out[d * N + n] = acc;
+  for (int k = 0; k < kSumSlices; ++k) acc += a.slices[k * a.W + c];
+  const int64_t ND = a.N * a.D;
+  if (c < ND) {
+    const int64_t n = c / a.D, d = c - n * a.D;
+    a.dA[d * a.N + n] = acc;
+  } else if (a.dDskip != nullptr && c < ND + a.D) {
+    a.dDskip[c - ND] = acc;
+  } else {
+    a.ddt_bias[c - ND - (a.dDskip != nullptr ? a.D : 0)] = acc;
+  }
 }
 
 template <typename Tin, typename Tout, int NS, bool SOFTPLUS, bool GATE>
@@ -1712,7 +1762,7 @@ BwdLayout bwd_layout(const SelectiveBwdArgs& a) {
   l.state = align256((size_t)(l.U * a.N * a.D) * sizeof(float));
   l.row = align256((size_t)(l.U * a.D) * sizeof(float));
   l.bc = align256((size_t)(l.nblk * a.B * a.L * a.N) * sizeof(float));
-  l.slices = align256((size_t)(kSumSlices * a.N * a.D) * sizeof(float));
+  l.slices = align256((size_t)(kSumSlices * (a.N + 2) * a.D) * sizeof(float));
   return l;
 }
 }  // namespace
@@ -1766,24 +1816,21 @@ hipError_t launch_selective_scan_backward(const SelectiveBwdArgs& a, hipStream_t
   else if (a.out_bf16) launch_bwd_t<bf16_t, bf16_t>(q, a.N, l.U, nseq, sp, gate, s);
   else launch_bwd_t<bf16_t, float>(q, a.N, l.U, nseq, sp, gate, s);
   // pass 4: fixed-order sums
-  const int64_t nbc = a.B * a.L * a.N;
+  BwdSums sm{};
+  sm.PB = PB; sm.PC = PC; sm.nblk = l.nblk; sm.nbc = a.B * a.L * a.N; sm.dBm = a.dBm; sm.dCm = a.dCm;
+  sm.dA_part = dA_part; sm.dD_part = a.dDskip ? dD_part : nullptr; sm.dbias_part = a.ddt_bias ? dbias_part : nullptr;
+  sm.units = l.U; sm.n_units = n_units; sm.N = a.N; sm.D = a.D;
+  sm.W = a.N * a.D + (a.dDskip ? a.D : 0) + (a.ddt_bias ? a.D : 0);
+  sm.slices = slices; sm.dA = a.dA; sm.dDskip = a.dDskip; sm.ddt_bias = a.ddt_bias;
+  const int64_t nsum = sm.nbc + kSumSlices * sm.W;
   const dim3 blk(kThreads);
   if (a.out_bf16)
-    hipLaunchKernelGGL((selective_bwd_bc_kernel<bf16_t>), dim3((unsigned)((nbc + kThreads - 1) / kThreads)), blk, 0, s,
-                       PB, PC, l.nblk, nbc, a.dBm, a.dCm);
+    hipLaunchKernelGGL((selective_bwd_sums_kernel<bf16_t>), dim3((unsigned)((nsum + kThreads - 1) / kThreads)), blk, 0,
+                       s, sm);
   else
-    hipLaunchKernelGGL((selective_bwd_bc_kernel<float>), dim3((unsigned)((nbc + kThreads - 1) / kThreads)), blk, 0, s,
-                       PB, PC, l.nblk, nbc, a.dBm, a.dCm);
-  // (the three sums use the slice buffer in turn; width <= N D)
-  auto sum_units = [&](const float* part, int64_t width, int64_t n, float* out) {
-    const unsigned nb = (unsigned)((width + kThreads - 1) / kThreads);
-    hipLaunchKernelGGL(selective_bwd_slice_kernel, dim3(nb, kSumSlices), blk, 0, s, part, l.U,
-                       (const int*)n_units, width, slices);
-    hipLaunchKernelGGL(selective_bwd_final_kernel, dim3(nb), blk, 0, s, slices, width, n, out);
-  };
-  sum_units(dA_part, a.N * a.D, a.N, a.dA);
-  if (a.dDskip) sum_units(dD_part, a.D, 1, a.dDskip);
-  if (a.ddt_bias) sum_units(dbias_part, a.D, 1, a.ddt_bias);
+    hipLaunchKernelGGL((selective_bwd_sums_kernel<float>), dim3((unsigned)((nsum + kThreads - 1) / kThreads)), blk, 0,
+                       s, sm);
+  hipLaunchKernelGGL(selective_bwd_final_kernel, dim3((unsigned)((sm.W + kThreads - 1) / kThreads)), blk, 0, s, sm);
   return hipGetLastError();
 }
 
