@@ -1171,7 +1171,7 @@ __global__ __launch_bounds__(kThreads) void selective_bwd_agg_kernel(SelBwdParam
 // ----------------------------------------------------------------------------- pass 2
 // One thread per (sequence, state, channel): units in order for the entering states, then in reverse
 // for q; the aggregates of kCarryBatch units are loaded together ahead of their sequential use.
-constexpr int kCarryBatch = 16;
+constexpr int kCarryBatch = 8;
 template <int NS>
 __global__ __launch_bounds__(kThreads) void selective_bwd_carry_kernel(SelBwdParams p, int64_t nseq) {
   const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
