@@ -890,7 +890,10 @@ struct SelBwdParams {
   const float* h0;
   const void* dy;
   const float* dh_last;
-  float* aggP;  // [unit][N][D] prod abar over the unit (pass 1)
+  float* aggP;    // [unit][N][D] prod abar over the unit (pass 1; clamp variant only, see sdelta)
+  float* sdelta;  // [unit][D] delta summed over the unit: prod abar = 2^(A log2(e) sdelta) where the clamp
+                  // cannot act (softplus steps, A <= 0)
+  int softplus;
   float* aggH;  // [unit][N][D] the state the unit reaches from 0
   float* aggQ;  // [unit][N][D] q at the unit's first row from 0 past its end
   float* hin;   // [unit][N][D] the state entering the unit (pass 2)
@@ -1063,7 +1066,7 @@ __device__ __forceinline__ void wave_sum16(float (&v)[16], int lane) {
 template <typename Tin, int NS, bool SOFTPLUS, bool GATE, int DISC>
 __device__ __forceinline__ void bwd_agg_rows(const SelBwdParams& p, int64_t row0, int R, int64_t dl,
                                              const float* A2, float bias, const float* sB, const float* sC,
-                                             float* P, float* H, float* Q) {
+                                             float* P, float* H, float* Q, float& sdelta) {
   using W = win<Tin, 1>;
   constexpr int es = sizeof(Tin);
   static_assert(kBT % kPrefetch == 0, "blocks hold whole prefetch groups");
@@ -1137,6 +1140,7 @@ __device__ __forceinline__ void bwd_agg_rows(const SelBwdParams& p, int64_t row0
   }
 #pragma unroll
   for (int n = 0; n < NS; ++n) P[n] = DISC == kClamp ? hw_exp2(es_tot[n]) : hw_exp2(A2[n] * sd_tot);
+  sdelta = sd_tot;
 }
 
 template <typename Tin, int NS, bool SOFTPLUS, bool GATE>
@@ -1153,18 +1157,20 @@ __global__ __launch_bounds__(kThreads) void selective_bwd_agg_kernel(SelBwdParam
   const int disc = bwd_load_A<NS, SOFTPLUS>(p.A, dl, A2);
   const float bias = p.dt_bias ? p.dt_bias[dl] : 0.0f;
   __syncthreads();
-  float P[NS], H[NS], Q[NS];
+  float P[NS], H[NS], Q[NS], sd;
   if (disc == kExp)
-    bwd_agg_rows<Tin, NS, SOFTPLUS, GATE, kExp>(p, U.row0, U.R, dl, A2, bias, sB, sC, P, H, Q);
+    bwd_agg_rows<Tin, NS, SOFTPLUS, GATE, kExp>(p, U.row0, U.R, dl, A2, bias, sB, sC, P, H, Q, sd);
   else
-    bwd_agg_rows<Tin, NS, SOFTPLUS, GATE, kClamp>(p, U.row0, U.R, dl, A2, bias, sB, sC, P, H, Q);
+    bwd_agg_rows<Tin, NS, SOFTPLUS, GATE, kClamp>(p, U.row0, U.R, dl, A2, bias, sB, sC, P, H, Q, sd);
   if (!active) return;
+  // prod abar is stored only where the carry cannot rebuild it from the delta sum
+  p.sdelta[u * p.D + d] = sd;
 #pragma unroll
   for (int n = 0; n < NS; ++n) {
     const int64_t idx = (u * NS + n) * p.D + d;
-    p.aggP[idx] = P[n];
-    p.aggH[idx] = H[n];
-    p.aggQ[idx] = Q[n];
+    if (disc == kClamp) p.aggP[idx] = P[n];
+    if (!U.last) p.aggH[idx] = H[n];   // the carry uses H of all units but a sequence's last
+    if (!U.first) p.aggQ[idx] = Q[n];  // and Q of all but its first
   }
 }
 
@@ -1187,6 +1193,14 @@ __global__ __launch_bounds__(kThreads) void selective_bwd_carry_kernel(SelBwdPar
     count = r.y;
   }
   const int64_t base = (first * NS + n) * p.D + d, stride = NS * p.D;
+  // prod abar of unit s: 2^(A log2(e) sdelta) where the clamp cannot act (the aggregate pass computes it
+  // the same way there), else the stored product
+  const float An = p.A[d * NS + n];
+  const bool from_sum = p.softplus && !(An > 0.0f);
+  const float A2 = An * kLog2e;
+  auto prod_src = [&](int64_t s) {  // one load either way: the delta sum or the product
+    return from_sum ? p.sdelta + (first + s) * p.D + d : p.aggP + base + s * stride;
+  };
   float h = p.h0 ? p.h0[(seq * p.D + d) * NS + n] : 0.0f;
   for (int64_t s0 = 0; s0 < count; s0 += kCarryBatch) {
     float Pv[kCarryBatch], Hv[kCarryBatch];
@@ -1194,9 +1208,11 @@ __global__ __launch_bounds__(kThreads) void selective_bwd_carry_kernel(SelBwdPar
     for (int k = 0; k < kCarryBatch; ++k) {
       const int64_t s = s0 + k;
       const bool need = s + 1 < count;  // the last unit's aggregate is not used
-      Pv[k] = need ? p.aggP[base + s * stride] : 0.0f;
+      Pv[k] = need ? *prod_src(s) : 0.0f;
       Hv[k] = need ? p.aggH[base + s * stride] : 0.0f;
     }
+#pragma unroll
+    for (int k = 0; k < kCarryBatch; ++k) Pv[k] = from_sum ? hw_exp2(A2 * Pv[k]) : Pv[k];
 #pragma unroll
     for (int k = 0; k < kCarryBatch; ++k) {
       const int64_t s = s0 + k;
@@ -1214,9 +1230,11 @@ __global__ __launch_bounds__(kThreads) void selective_bwd_carry_kernel(SelBwdPar
     for (int k = 0; k < kCarryBatch; ++k) {
       const int64_t s = s0 - k;
       const bool need = s > 0;  // the first unit's aggregate is not used
-      Pv[k] = need ? p.aggP[base + s * stride] : 0.0f;
+      Pv[k] = need ? *prod_src(s) : 0.0f;
       Qv[k] = need ? p.aggQ[base + s * stride] : 0.0f;
     }
+#pragma unroll
+    for (int k = 0; k < kCarryBatch; ++k) Pv[k] = from_sum ? hw_exp2(A2 * Pv[k]) : Pv[k];
 #pragma unroll
     for (int k = 0; k < kCarryBatch; ++k) {
       const int64_t s = s0 - k;
@@ -1269,6 +1287,13 @@ __device__ __forceinline__ void bwd_grad_unit(const SelBwdParams& p, const BUnit
       S.dy[j & 1][t][tid] = W::load(wdy, lane_in, ro_of(j * kBT + t));
       if (GATE) S.z[j & 1][t][tid] = W::load(wzz, lane_in, ro_of(j * kBT + t));
     }
+  }
+
+  float qv[NS], dAv[NS];
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    qv[n] = p.qend[(u * NS + n) * p.D + dl];
+    dAv[n] = 0.0f;
   }
 
   // ---- forward sweep: the states at the sub-block starts.  After it s3 holds the start of sub-block
@@ -1350,12 +1375,6 @@ __device__ __forceinline__ void bwd_grad_unit(const SelBwdParams& p, const BUnit
   const auto wox = unit_window(p.dx, row0, R, p.D, sizeof(Tout)), wot = unit_window(p.ddt, row0, R, p.D, sizeof(Tout));
   const auto woz = unit_window(GATE ? p.dz : p.dx, row0, R, p.D, sizeof(Tout));
   const uint32_t lane_out = (uint32_t)(dl * (int64_t)sizeof(Tout)), row_out = (uint32_t)(p.D * (int64_t)sizeof(Tout));
-  float qv[NS], dAv[NS];
-#pragma unroll
-  for (int n = 0; n < NS; ++n) {
-    qv[n] = p.qend[(u * NS + n) * p.D + dl];
-    dAv[n] = 0.0f;
-  }
   float dsum = 0.0f, bsum = 0.0f;
   for (int j = nsb - 1; j >= 0; --j) {
     const int slot = j & 1;
@@ -1550,11 +1569,11 @@ __global__ __launch_bounds__(kThreads, 1) void selective_bwd_kernel(SelBwdParams
 }
 
 // Pass 4: fixed-order sums, in two launches.  dBm, dCm: over channel blocks.  dA [D][N], dDskip and
-// d dt_bias: over units in two steps: slice k of kSumSlices adds units [k U / S, (k + 1) U / S), then the
+// d dt_bias: over units in two steps: slice k of S = kSumSlices adds units [k U / S, (k + 1) U / S), then the
 // slices are added in order.  The unit sums share one column space: c < N D is column c = n D + d of
 // dA's [units][N][D] partials (it goes to dA[d N + n]), then D columns of dDskip's, then D of dt_bias's
 // (those present).
-constexpr int kSumSlices = 32;
+constexpr int kSumSlices = 16;
 struct BwdSums {
   const float* PB;
   const float* PC;
@@ -1743,7 +1762,7 @@ hipError_t launch_selective_scan(const SelectiveScanArgs& a, hipStream_t s) {
 namespace {
 struct BwdLayout {
   int64_t nseg, U, nblk;          // U: units (packed varlen: an upper bound)
-  size_t state, row, bc, slices;  // bytes of one [U][N][D], [U][D], [nblk][B L][N], [kSumSlices][N][D] buffer
+  size_t state, row, bc, slices;  // bytes of one [U][N][D], [U][D], [nblk][B L][N] buffer, and the slices
   size_t tbl, seqtbl;             // packed varlen: unit table (after a 256-byte count), per-sequence table
 };
 BwdLayout bwd_layout(const SelectiveBwdArgs& a) {
@@ -1769,7 +1788,7 @@ BwdLayout bwd_layout(const SelectiveBwdArgs& a) {
 
 size_t selective_scan_backward_scratch_bytes(const SelectiveBwdArgs& a) {
   const BwdLayout l = bwd_layout(a);
-  return workspace_head_bytes() + 6 * l.state + 2 * l.row + 2 * l.bc + l.slices + l.tbl + l.seqtbl;
+  return workspace_head_bytes() + 6 * l.state + 3 * l.row + 2 * l.bc + l.slices + l.tbl + l.seqtbl;
 }
 
 hipError_t launch_selective_scan_backward(const SelectiveBwdArgs& a, hipStream_t s) {
@@ -1786,11 +1805,12 @@ hipError_t launch_selective_scan_backward(const SelectiveBwdArgs& a, hipStream_t
   float* aggH = take(l.state);
   float* aggQ = take(l.state);
   float* dA_part = take(l.state);
+  float* sdelta = take(l.row);
   float* dD_part = take(l.row);
   float* dbias_part = take(l.row);
   float* PB = take(l.bc);
   float* PC = take(l.bc);
-  float* slices = take(l.slices);  // kSumSlices x (N D)
+  float* slices = take(l.slices);  // kSumSlices x (N D + 2 D)
   char* tbl = q0;
   int* n_units = nullptr;
   int2 *units = nullptr, *seq_units = nullptr;
@@ -1809,6 +1829,7 @@ hipError_t launch_selective_scan_backward(const SelectiveBwdArgs& a, hipStream_t
   q.x = a.x; q.dt = a.dt; q.A = a.A; q.Bm = a.Bm; q.Cm = a.Cm; q.Dskip = a.Dskip; q.z = a.z; q.dt_bias = a.dt_bias;
   q.h0 = a.h0; q.dy = a.dy; q.dh_last = a.dh_last;
   q.aggP = aggP; q.aggH = aggH; q.aggQ = aggQ; q.hin = hin; q.qend = qend;
+  q.sdelta = sdelta; q.softplus = a.dt_softplus != 0;
   q.dx = a.dx; q.ddt = a.ddt; q.dz = a.dz; q.dBm_part = PB; q.dCm_part = PC;
   q.dA_part = dA_part; q.dD_part = dD_part; q.dbias_part = dbias_part; q.dh0 = a.dh0;
   const bool sp = a.dt_softplus != 0, gate = a.z != nullptr;
