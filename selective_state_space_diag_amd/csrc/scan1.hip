@@ -652,8 +652,8 @@ __global__ __launch_bounds__(256) void update1v_kernel(Upd1Params p) {
   Scan1Params q{};
   q.a_log = p.a_log;
   q.c = p.c;
-  using Wi = win<Tin, V>;
-  using Wf = win<float, V>;
+  using Wi = win<Tin, V, kStreaming>;  // this step's inputs and output are touched once
+  using Wf = win<float, V>;            // the state is read again by the next step
   __amdgpu_buffer_rsrc_t win_in[3];
 #pragma unroll
   for (int k = 0; k < Op::kIn; ++k) win_in[k] = make_window(p.in[k], elems * sizeof(Tin));
@@ -689,7 +689,7 @@ __global__ __launch_bounds__(256) void update1v_kernel(Upd1Params p) {
     }
     if (g[u] < n) {
       Wf::store(ws, g[u] * V * sizeof(float), 0, h);
-      win<Tout, V>::store(make_window(p.y, elems * sizeof(Tout)), g[u] * V * sizeof(Tout), 0, y);
+      win<Tout, V, kStreaming>::store(make_window(p.y, elems * sizeof(Tout)), g[u] * V * sizeof(Tout), 0, y);
     }
   }
 }
@@ -1332,8 +1332,9 @@ hipError_t launch_scan_op(Scan1Params& p, int in_bf16, int out_bf16, void* scrat
 
 // Vectors per lane in the decode step, and channels per vector (below): a step is one round trip to
 // memory followed by a short chain of arithmetic per lane, so many short lanes finish first.  Measured
-// at B = 256, D = 2560 bf16 from a HIP graph: 2 channels x 1 vector 3.9 us per step, 4 x 1 4.2 us,
-// 1 x 1 4.4 us, 4 x 2 5.0 us (a plain device copy of the same bytes: 2.6 us).
+// at B = 256, D = 2560 bf16 from a HIP graph, with the step's inputs and y non-temporal: 2 channels x 1
+// vector 3.26 us per step, 4 x 1 3.51 us, 2 x 2 3.74 us (a plain device copy of the same bytes:
+// 2.6 us); with every access cached, 2 x 1 took 3.9 us.
 constexpr int kUpdVectors = 1;
 template <class Op, bool GATE, int V>
 hipError_t launch_update_v(const Upd1Params& p, int in_bf16, int out_bf16, hipStream_t s) {
