@@ -99,7 +99,8 @@ PROFILES = {
                                               "(one forward call first)", _SWEEP_SOURCES),
     "hgrn2_key_gate_bf16_B8_H16_d128_L4096": ("hgrn2_key_gate_scan_B8_H16_d128_L4096.md",
                                               "HGRN2 scan with the gate on the key axis, B=8 H=16 d=128 L=4096 bf16 "
-                                              "(register sweep)", _SWEEP_SOURCES),
+                                              "in, fp32 out, lower bound 0.5; one call = one chunked MFMA kernel",
+                                              _H2_SOURCES + [_CSRC + "hgrn2_sweep.hip"]),
     "readout_norm_B8_L4096_width2048": ("readout_norm_B8_L4096_width2048.md",
                                         "Readout LayerNorm and silu gate over 32768 rows of 2048 features (one HGRN2 "
                                         "forward call first)", _NORM_SOURCES),
@@ -626,11 +627,11 @@ def form_hgrn2_backward(args, device):
 def form_hgrn2_key(args, device):
     import selective_state_space_diag_amd as ssd
     _, (B, L, H, dd), q, k, v, g = _hgrn2_inputs(device, 16)
-    t = time_calls(lambda kk: ssd.hgrn2_scan(q, k, v, g, 0.5, gate_axis="key"), 1, 3, 1)
-    kflops = 5 * B * L * H * dd * dd
+    t = time_calls(lambda kk: ssd.hgrn2_scan(q, k, v, g, 0.5, gate_axis="key"), 1, 10, 2)
+    flops = 2 * B * L * H * (2 * 64 * dd + 2 * dd * dd)  # chunked form at chunk 64, as for the row gate
     return record_of(t, B * L * H * dd * dd, hgrn2_bytes(B, L, H, dd),
-                     dict(valu_tflops=kflops / (t["ms"] * 1e-3) / 1e12,
-                          valu_frac=kflops / (t["ms"] * 1e-3) / 1e12 / FP32_SCALAR_FMA_TFLOPS),
+                     dict(mfma_equiv_tflops=flops / (t["ms"] * 1e-3) / 1e12,
+                          mfma_util=flops / (t["ms"] * 1e-3) / 1e12 / BF16_MFMA_TFLOPS),
                      "hgrn2_key_gate_bf16_B8_H16_d128_L4096")
 
 

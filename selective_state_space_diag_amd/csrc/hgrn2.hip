@@ -697,7 +697,366 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
   }
 }
 
+// ----------------------------------------------------------------------------- key-axis gate, chunked
+// With the gate on the key axis the recurrence is S_t = S_{t-1} diag(g_t) + v_t k_t^T, o_t = S_t q_t.
+// For Gamma[t][j] = prod_{u<=t} g_u[j] inside a chunk of 64 tokens it unrolls to
+//   O      = (Qt Kt^T (.) M) V + Qt S0^T,      Qt = Q (.) Gamma,   Kt = K (/) Gamma
+//   S_next = S0 diag(Gamma_C) + V^T Kh,        Kh = K (.) Gamma_C (/) Gamma
+// (M causal, diagonal included).  Qt and Kh are bounded by |Q| and |K| (Gamma decreases along the
+// chunk); Kt reaches |K| / Gamma_C, which the fp32 products hold while Gamma_C >= 2^-96, i.e. for every
+// lower bound >= 2^-1.5 (smaller bounds take the register sweep).  The three derived operands are split
+// into bf16 pairs hi + lo like the derived operands of the row-gated form; V enters exactly.
+// The workgroup, wave roles, tile layouts and product shapes are those of hgrn2_chunk_kernel with these
+// operands in place of Q, K and W; the gate step covers all 128 key columns in each of the two
+// workgroups of a head.  A NaN gate, query or key reaches exactly the outputs and state entries the
+// recurrence sends it to (every ratio it enters is masked by assignment, not by multiplication); a
+// non-finite value would reach the row's earlier outputs through masked products (0 * inf), so it
+// enters as 0 and the row's outputs from that token on, and its state, are set to NaN (as in the
+// row-gated kernel).
+struct H2KeyLds {
+  uint16_t qt[2][h2::kQkTile];  // Q (.) Gamma, hi and lo (qk layout)
+  uint16_t kt[2][h2::kQkTile];  // K (/) Gamma
+  uint16_t kh[2][h2::kQkTile];  // K (.) Gamma_C (/) Gamma
+  uint16_t v[kCh * kRows];      // V of the workgroup's value rows (vw layout)
+  uint2 qk[10][2][64];          // causal Qt Kt^T tiles as bf16 pairs: [tile][hi, lo][lane]
+  uint4 sx[4][2][2][2][64];     // incoming state as bf16 pairs: [row tile][half][k-step][hi, lo][lane]
+  alignas(16) float gpart[kGateParts][kDh];  // gate products per token group and key column
+  alignas(16) float gcol[kDh];               // Gamma_C per key column
+  int nanpos[2][kRows + 4];                  // as in H2Lds
+};
+
+// One chunk's inputs of one thread: key columns 2 lane, 2 lane + 1 (bf16 pairs) of q, k and the gate
+// logits, and value row i0 + lane (bf16 in the low half), for tokens 8 gp + u.
+struct H2KeyPrefetch {
+  uint32_t g[kGateTok], q[kGateTok], k[kGateTok], v[kGateTok];
+};
+
+__device__ __forceinline__ void h2k_fetch(const H2Params& p, int64_t b, int64_t hh, int i0, int64_t t0, int lane,
+                                          int gp, H2KeyPrefetch& f) {
+  const int valid = (int)min((int64_t)kCh, p.L - t0);
+  const uint32_t row_bytes = (uint32_t)(p.H * kDh * 2);
+  const auto wq = h2_window(p, p.q, b, hh, t0, valid), wk = h2_window(p, p.k, b, hh, t0, valid);
+  const auto wg = h2_window(p, p.g, b, hh, t0, valid), wv = h2_window(p, p.v, b, hh, t0, valid);
+  const int kc = 4 * lane, vc = 2 * (i0 + lane);
+#pragma unroll
+  for (int u = 0; u < kGateTok; ++u) {
+    const int ro = (int)((uint32_t)(gp * kGateTok + u) * row_bytes);
+    f.g[u] = __builtin_amdgcn_raw_buffer_load_b32(wg, kc, ro, 0);
+    f.q[u] = __builtin_amdgcn_raw_buffer_load_b32(wq, kc, ro, 0);
+    f.k[u] = __builtin_amdgcn_raw_buffer_load_b32(wk, kc, ro, 0);
+    f.v[u] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wv, vc, ro, 0);
+  }
+}
+
+// Gates, part 1: g = lb + (1 - lb) sigmoid(logit) for the thread's two key columns (1 past the chunk's
+// valid tokens), running products over its 8 tokens, group products published; non-finite values of
+// its value row replaced by 0 and the row's first such token recorded.
+__device__ __forceinline__ void h2k_gate1(H2KeyLds& sm, int lane, int gp, int valid, float lb, float one_m_lb,
+                                          H2KeyPrefetch& f, float (&run)[kGateTok][2], int* nanpos) {
+  float r0 = 1.0f, r1 = 1.0f;
+#pragma unroll
+  for (int u = 0; u < kGateTok; ++u) {
+    float g0 = fmaf(one_m_lb, sigmoid_f(bf16_lo(f.g[u])), lb);
+    float g1 = fmaf(one_m_lb, sigmoid_f(bf16_hi(f.g[u])), lb);
+    if (gp * kGateTok + u >= valid) g0 = g1 = 1.0f;
+    r0 *= g0;
+    r1 *= g1;
+    run[u][0] = r0;
+    run[u][1] = r1;
+  }
+  *reinterpret_cast<float2*>(&sm.gpart[gp][2 * lane]) = make_float2(r0, r1);
+  float z = 0.0f;  // NaN exactly when one of the values is not finite
+#pragma unroll
+  for (int u = 0; u < kGateTok; ++u) z = fmaf(bf16_lo(f.v[u]), 0.0f, z);
+  if (z != z) {
+#pragma unroll
+    for (int u = 0; u < kGateTok; ++u) {
+      if (!__builtin_isfinite(bf16_lo(f.v[u]))) {
+        f.v[u] = 0u;
+        atomicMin(&nanpos[lane], gp * kGateTok + u);
+        nanpos[kRows] = 1;
+      }
+    }
+  }
+}
+
+// Gates, part 2: Gamma for the thread's tokens and key columns, the derived operands Qt, Kt, Kh as bf16
+// pairs (row-major qk layout), Gamma_C, and the values (vw layout).
+__device__ __forceinline__ void h2k_gate2(H2KeyLds& sm, int lane, int gp, const H2KeyPrefetch& f,
+                                          const float (&run)[kGateTok][2]) {
+  float pre0 = 1.0f, pre1 = 1.0f, all0 = 1.0f, all1 = 1.0f;
+#pragma unroll
+  for (int q2 = 0; q2 < kGateParts; ++q2) {
+    const float2 gq = *reinterpret_cast<const float2*>(&sm.gpart[q2][2 * lane]);
+    pre0 *= q2 < gp ? gq.x : 1.0f;
+    pre1 *= q2 < gp ? gq.y : 1.0f;
+    all0 *= gq.x;
+    all1 *= gq.y;
+  }
+  if (gp == 0) *reinterpret_cast<float2*>(&sm.gcol[2 * lane]) = make_float2(all0, all1);
+#pragma unroll
+  for (int u = 0; u < kGateTok; ++u) {
+    const int off = h2::qk_off(gp * kGateTok + u, 2 * lane);
+    const float G0 = pre0 * run[u][0], G1 = pre1 * run[u][1];
+    const float k0 = bf16_lo(f.k[u]) * hw_rcp(G0), k1 = bf16_hi(f.k[u]) * hw_rcp(G1);
+    uint32_t hi, lo;
+    split2(bf16_lo(f.q[u]) * G0, bf16_hi(f.q[u]) * G1, hi, lo);
+    *reinterpret_cast<uint32_t*>(&sm.qt[0][off]) = hi;
+    *reinterpret_cast<uint32_t*>(&sm.qt[1][off]) = lo;
+    split2(k0, k1, hi, lo);
+    *reinterpret_cast<uint32_t*>(&sm.kt[0][off]) = hi;
+    *reinterpret_cast<uint32_t*>(&sm.kt[1][off]) = lo;
+    split2(k0 * all0, k1 * all1, hi, lo);
+    *reinterpret_cast<uint32_t*>(&sm.kh[0][off]) = hi;
+    *reinterpret_cast<uint32_t*>(&sm.kh[1][off]) = lo;
+  }
+  const int xg = h2::vw_gate_lane(lane, gp);
+#pragma unroll
+  for (int u = 0; u < kGateTok; ++u) sm.v[h2::vw_gate_wr(lane, xg, gp, u)] = (uint16_t)f.v[u];
+}
+
+// Causal tile ti of Qt Kt^T as D[s][t] (three products per k-step: hi hi, lo hi, hi lo), masked and split
+// into bf16 pairs in LDS (same tile numbering and lane layout as h2_qk_tile).
+__device__ __forceinline__ void h2k_qk_tile(H2KeyLds& sm, int ti, int lane) {
+  const int tt = ti >= 6 ? 3 : ti >= 3 ? 2 : ti >= 1 ? 1 : 0;
+  const int st = ti - tt * (tt + 1) / 2;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int xa = h2::qk_seg_lane(l16, lg);
+  floatx4_t acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int ok = h2::qk_seg_off(l16, xa, st, ks), oq = h2::qk_seg_off(l16, xa, tt, ks);
+    const uint4 kh = *reinterpret_cast<const uint4*>(&sm.kt[0][ok]);
+    const uint4 kl = *reinterpret_cast<const uint4*>(&sm.kt[1][ok]);
+    const uint4 qh = *reinterpret_cast<const uint4*>(&sm.qt[0][oq]);
+    const uint4 ql = *reinterpret_cast<const uint4*>(&sm.qt[1][oq]);
+    acc = mfma(kh, qh, acc);
+    acc = mfma(kl, qh, acc);
+    acc = mfma(kh, ql, acc);
+  }
+  if (st == tt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * lg + r > l16) acc[r] = 0.0f;  // s > t
+  }
+  uint2 hi, lo;
+  split2(acc[0], acc[1], hi.x, lo.x);
+  split2(acc[2], acc[3], hi.y, lo.y);
+  sm.qk[ti][0][lane] = hi;
+  sm.qk[ti][1][lane] = lo;
+}
+
+// Qt S^T part of this half's O^T tiles (the state's k-steps as in h2_out_state).
+template <int H>
+__device__ __forceinline__ void h2k_out_state(const H2KeyLds& sm, int lane, const uint4 (&mine_hi)[2],
+                                              const uint4 (&mine_lo)[2], const uint4 (&other_hi)[2],
+                                              const uint4 (&other_lo)[2], floatx4_t (&os)[2]) {
+  using TL = Tiles<H>;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int xb = h2::qk_quad_lane(l16, lg);
+#pragma unroll
+  for (int a = 0; a < 2; ++a) os[a] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const int o0 = h2::qk_quad_off(l16, lg, xb, TL::tt(a), ks, 0);
+      const int o1 = h2::qk_quad_off(l16, lg, xb, TL::tt(a), ks, 1);
+      const uint2 h0 = *reinterpret_cast<const uint2*>(&sm.qt[0][o0]);
+      const uint2 h1 = *reinterpret_cast<const uint2*>(&sm.qt[0][o1]);
+      const uint2 l0 = *reinterpret_cast<const uint2*>(&sm.qt[1][o0]);
+      const uint2 l1 = *reinterpret_cast<const uint2*>(&sm.qt[1][o1]);
+      const uint4 qh = make_uint4(h0.x, h0.y, h1.x, h1.y), ql = make_uint4(l0.x, l0.y, l1.x, l1.y);
+      const bool own = (ks >> 1) == H;
+      const uint4 sh = own ? mine_hi[ks & 1] : other_hi[ks & 1];
+      const uint4 sl = own ? mine_lo[ks & 1] : other_lo[ks & 1];
+      os[a] = mfma(sh, qh, os[a]);
+      os[a] = mfma(sl, qh, os[a]);
+      os[a] = mfma(sh, ql, os[a]);
+    }
+  }
+}
+
+// O^T tiles of this half: (Qt Kt^T (.) M) V + Qt S^T, V read as A operands like W in h2_out.
+template <int H, typename Tout>
+__device__ __forceinline__ void h2k_out(__amdgpu_buffer_rsrc_t wo, uint32_t row_bytes, const H2KeyLds& sm, int iw,
+                                        int lane, const floatx4_t (&os)[2]) {
+  using TL = Tiles<H>;
+  const int l16 = lane & 15, lg = lane >> 4;
+  uint4 va[2];
+  const int wl = h2::vw_out_lane(l16, lg, iw >> 4);
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const uint2 v0 = lds_tr(&sm.v[h2::vw_out_off(wl, ks, 0)]), v1 = lds_tr(&sm.v[h2::vw_out_off(wl, ks, 1)]);
+    va[ks] = make_uint4(v0.x, v0.y, v1.x, v1.y);
+  }
+  floatx4_t oa[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) oa[a] = os[a];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const int tt = TL::tt(a);
+      if (2 * ks <= tt) {  // key tiles 2 ks, 2 ks + 1; tiles past tt are masked entirely
+        const int t0i = tt * (tt + 1) / 2 + 2 * ks;
+        const bool second = 2 * ks + 1 <= tt;
+        const uint2 h0 = sm.qk[t0i][0][lane], l0 = sm.qk[t0i][1][lane];
+        const uint2 h1 = second ? sm.qk[t0i + 1][0][lane] : make_uint2(0u, 0u);
+        const uint2 l1 = second ? sm.qk[t0i + 1][1][lane] : make_uint2(0u, 0u);
+        oa[a] = mfma(va[ks], make_uint4(h0.x, h0.y, h1.x, h1.y), oa[a]);
+        oa[a] = mfma(va[ks], make_uint4(l0.x, l0.y, l1.x, l1.y), oa[a]);
+      }
+    }
+  }
+  const uint32_t lane_off = (uint32_t)l16 * row_bytes + (uint32_t)(4 * lg * (int)sizeof(Tout));
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+    h2_store4<Tout>::run(wo, lane_off, 16 * TL::tt(a) * row_bytes + iw * (uint32_t)sizeof(Tout), oa[a][0], oa[a][1],
+                         oa[a][2], oa[a][3]);
+}
+
+template <typename Tout>
+__global__ __launch_bounds__(kWaves * 64) void hgrn2_key_chunk_kernel(H2Params p) {
+  __shared__ H2KeyLds sm;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
+  const int rt = wave & 3, half_t = wave >> 2, gp = wave;
+  int64_t bh, half;  // both halves of a head on the same XCD, as in hgrn2_chunk_kernel
+  if ((p.B * p.H) % 8 == 0) {
+    const int64_t xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+    half = slot % 2;
+    bh = (slot / 2) * 8 + xcd;
+  } else {
+    bh = blockIdx.x / 2;
+    half = blockIdx.x % 2;
+  }
+  const int64_t b = bh / p.H, hh = bh - b * p.H;
+  const int i0 = (int)half * kRows;
+  const int iw = 16 * rt;
+  const float lb = p.lb, one_m_lb = 1.0f - p.lb;
+
+  // S^T accumulators: tile q holds S^T[j = 16 (4 half_t + q) + 4 lg + r][i = iw + l16]
+  floatx4_t S[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      S[q][r] = p.S0 ? p.S0[(bh * kDh + i0 + iw + l16) * kDh + 16 * (4 * half_t + q) + 4 * lg + r] : 0.0f;
+
+  const int64_t nchunks = (p.L + kCh - 1) / kCh;
+  H2KeyPrefetch f;
+  float run[kGateTok][2];
+  h2k_fetch(p, b, hh, i0, 0, lane, gp, f);
+  if (tid < 2 * (kRows + 4)) sm.nanpos[tid / (kRows + 4)][tid % (kRows + 4)] = tid % (kRows + 4) < kRows ? kCh : 0;
+  __syncthreads();
+  h2k_gate1(sm, lane, gp, (int)min((int64_t)kCh, p.L), lb, one_m_lb, f, run, sm.nanpos[0]);
+  for (int64_t c = 0; c < nchunks; ++c) {
+    const int64_t t0 = c * kCh;
+    const int valid = (int)min((int64_t)kCh, p.L - t0);
+    const int par = (int)(c & 1);
+    __syncthreads();  // group products of this chunk visible; the previous chunk's products are done
+    h2k_gate2(sm, lane, gp, f, run);
+    if (gp == 0) {
+      sm.nanpos[par ^ 1][lane] = kCh;  // the slot of the next chunk (last read by the previous one)
+      if (lane == 0) sm.nanpos[par ^ 1][kRows] = 0;
+    }
+    if (c + 1 < nchunks) h2k_fetch(p, b, hh, i0, t0 + kCh, lane, gp, f);  // in flight during this chunk
+    uint4 my_hi[2], my_lo[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      split2(S[2 * kk][0], S[2 * kk][1], my_hi[kk].x, my_lo[kk].x);
+      split2(S[2 * kk][2], S[2 * kk][3], my_hi[kk].y, my_lo[kk].y);
+      split2(S[2 * kk + 1][0], S[2 * kk + 1][1], my_hi[kk].z, my_lo[kk].z);
+      split2(S[2 * kk + 1][2], S[2 * kk + 1][3], my_hi[kk].w, my_lo[kk].w);
+      sm.sx[rt][half_t][kk][0][lane] = my_hi[kk];
+      sm.sx[rt][half_t][kk][1][lane] = my_lo[kk];
+    }
+    __syncthreads();  // Qt, Kt, Kh, V, Gamma_C and the state halves visible
+
+    floatx4_t os[2];
+    {
+      uint4 oth_hi[2], oth_lo[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        oth_hi[kk] = sm.sx[rt][1 - half_t][kk][0][lane];
+        oth_lo[kk] = sm.sx[rt][1 - half_t][kk][1][lane];
+      }
+      if (half_t == 0) h2k_out_state<0>(sm, lane, my_hi, my_lo, oth_hi, oth_lo, os);
+      else h2k_out_state<1>(sm, lane, my_hi, my_lo, oth_hi, oth_lo, os);
+    }
+    h2k_qk_tile(sm, wave, lane);
+    if (wave < 2) h2k_qk_tile(sm, wave + 8, lane);
+    __syncthreads();  // Qt Kt^T tiles visible
+
+    {
+      const auto wo = h2_out_window<Tout>(p, b, hh, i0, t0, valid);
+      const uint32_t row_bytes = (uint32_t)(p.H * kDh * (int64_t)sizeof(Tout));
+      if (half_t == 0) h2k_out<0, Tout>(wo, row_bytes, sm, iw, lane, os);
+      else h2k_out<1, Tout>(wo, row_bytes, sm, iw, lane, os);
+      if (__builtin_amdgcn_readfirstlane(sm.nanpos[par][kRows]) != 0) {
+        h2_out_nan<Tout>(wo, row_bytes, sm.nanpos[par], iw, lane, half_t);
+        if (sm.nanpos[par][iw + l16] < kCh) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            S[q] = floatx4_t{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+        }
+      }
+    }
+    // state update: S^T[j][i] = S^T[j][i] Gamma_C[j] + sum_s Kh[s][j] V[s][i]
+    {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 gc = *reinterpret_cast<const float4*>(&sm.gcol[16 * (4 * half_t + q) + 4 * lg]);
+        S[q][0] *= gc.x;
+        S[q][1] *= gc.y;
+        S[q][2] *= gc.z;
+        S[q][3] *= gc.w;
+      }
+      const int ws0 = h2::vw_state_lane(l16, lg, rt, 0), ws1 = h2::vw_state_lane(l16, lg, rt, 1);
+      const int xd = h2::qk_tr_lane(l16, lg);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint2 w0 = lds_tr(&sm.v[h2::vw_state_off(ws0, ks)]), w1 = lds_tr(&sm.v[h2::vw_state_off(ws1, ks)]);
+        const uint4 vb = make_uint4(w0.x, w0.y, w1.x, w1.y);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int jt = 4 * half_t + q;
+          const int o0 = h2::qk_tr_off(l16, lg, xd, ks, 0, jt), o1 = h2::qk_tr_off(l16, lg, xd, ks, 1, jt);
+          const uint2 h0 = lds_tr(&sm.kh[0][o0]), h1 = lds_tr(&sm.kh[0][o1]);
+          const uint2 x0 = lds_tr(&sm.kh[1][o0]), x1 = lds_tr(&sm.kh[1][o1]);
+          S[q] = mfma(make_uint4(h0.x, h0.y, h1.x, h1.y), vb, S[q]);
+          S[q] = mfma(make_uint4(x0.x, x0.y, x1.x, x1.y), vb, S[q]);
+        }
+      }
+    }
+    // gates, part 1, of the next chunk (its inputs were loaded during this chunk)
+    if (c + 1 < nchunks)
+      h2k_gate1(sm, lane, gp, (int)min((int64_t)kCh, p.L - t0 - kCh), lb, one_m_lb, f, run, sm.nanpos[par ^ 1]);
+  }
+
+  if (p.S_last) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        p.S_last[(bh * kDh + i0 + iw + l16) * kDh + 16 * (4 * half_t + q) + 4 * lg + r] = S[q][r];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_hgrn2_key_chunk(const Hgrn2ScanArgs& a, hipStream_t s) {
+  H2Params p;
+  p.B = a.B; p.L = a.L; p.H = a.H; p.d = a.d;
+  p.q = a.q; p.k = a.k; p.v = a.v; p.g = a.g_logit; p.lb = a.lower_bound;
+  p.S0 = a.S0; p.o = a.o; p.S_last = a.S_last;
+  const dim3 grid((unsigned)(a.B * a.H * 2));
+  if (a.out_bf16) hipLaunchKernelGGL((hgrn2_key_chunk_kernel<bf16_t>), grid, dim3(kWaves * 64), 0, s, p);
+  else hipLaunchKernelGGL((hgrn2_key_chunk_kernel<float>), grid, dim3(kWaves * 64), 0, s, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_hgrn2_scan(const Hgrn2ScanArgs& a, hipStream_t s) {
   H2Params p;

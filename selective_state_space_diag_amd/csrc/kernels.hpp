@@ -239,6 +239,8 @@ hipError_t launch_hgrn2_update(const Hgrn2UpdateArgs& a, hipStream_t s);
 hipError_t launch_hgrn2_key_scan(const Hgrn2ScanArgs& a, hipStream_t s);
 // The row-gated scan as a register sweep (the cases the chunked MFMA kernel does not take).
 hipError_t launch_hgrn2_row_sweep(const Hgrn2ScanArgs& a, hipStream_t s);
+// The key-axis-gated scan in chunked MFMA form: bf16 inputs, d = 128, lower_bound >= 2^-1.5.
+hipError_t launch_hgrn2_key_chunk(const Hgrn2ScanArgs& a, hipStream_t s);
 hipError_t launch_hgrn2_key_update(const Hgrn2UpdateArgs& a, hipStream_t s);
 
 // Readout LayerNorm over rows of `width` features (fp32 o), affine, times silu(gate).

@@ -197,12 +197,11 @@ def test_hgrn2_update_benchmark_shape(gate_axis):
     orf, Sr = fn(*(f64(inp.t[n]) for n in ("q", "k", "v", "g_logit")), 0.5, f64(inp.p["S0"]))
     assert_close(host(torch.stack(outs, 1)), orf, TOL[synth.BF16], "decode o")
     assert_close(host(S), Sr, TOL[synth.BF16], "decode S")
-    # the value-axis scan at d = 128 runs the chunked MFMA form, whose derived operands are bf16 hi/lo pairs
-    # (about 16 significant bits, 2^-16 = 1.5e-5 relative per product); the key-axis scan and the decode
-    # steps are both fp32 register arithmetic
-    tight = 1e-4 if gate_axis == "value" else 1e-5
-    assert_close(host(torch.stack(outs, 1)), host(o_scan), tight, "decode o vs scan")
-    assert_close(host(S), host(S_scan), tight, "decode S vs scan")
+    # the scans at d = 128 with bf16 inputs (either gate axis, lower bound 0.5) run the chunked MFMA form,
+    # whose derived operands are bf16 hi/lo pairs (about 16 significant bits, 2^-16 = 1.5e-5 relative per
+    # product); the decode steps are fp32 register arithmetic
+    assert_close(host(torch.stack(outs, 1)), host(o_scan), 1e-4, "decode o vs scan")
+    assert_close(host(S), host(S_scan), 1e-4, "decode S vs scan")
 
 
 @pytest.mark.parametrize("B,dtype", [(1, synth.BF16), (1, synth.F32), (4, synth.F32)])

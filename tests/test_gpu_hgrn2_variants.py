@@ -41,7 +41,7 @@ def test_key_gated_ragged_without_state(L):
 
 
 def test_key_gated_bf16_output():
-    """bf16 output = the fp32 result rounded (the sweep computes identically for both), within 1 ulp."""
+    """bf16 output = the fp32 result rounded (both outputs come from the same fp32 arithmetic), within 1 ulp."""
     import torch
     inp = synth.hgrn2_inputs(2, 100, 2, 128, synth.BF16, 8300, with_S0=True)
     t = {n: to_dev(v) for n, v in inp.t.items()}
