@@ -603,11 +603,11 @@ def form_hgrn2(args, device):
 def form_hgrn2_lb0(args, device):
     import selective_state_space_diag_amd as ssd
     _, (B, L, H, dd), q, k, v, g = _hgrn2_inputs(device, 16)
-    t = time_calls(lambda kk: ssd.hgrn2_scan(q, k, v, g, 0.0), 1, 3, 1)
-    rflops = 5 * B * L * H * dd * dd
+    t = time_calls(lambda kk: ssd.hgrn2_scan(q, k, v, g, 0.0), 1, 10, 2)
+    flops = 2 * B * L * H * (2 * 64 * dd + 2 * dd * dd)  # chunked form at chunk 64
     return record_of(t, B * L * H * dd * dd, hgrn2_bytes(B, L, H, dd),
-                     dict(valu_tflops=rflops / (t["ms"] * 1e-3) / 1e12,
-                          valu_frac=rflops / (t["ms"] * 1e-3) / 1e12 / FP32_SCALAR_FMA_TFLOPS),
+                     dict(mfma_equiv_tflops=flops / (t["ms"] * 1e-3) / 1e12,
+                          mfma_util=flops / (t["ms"] * 1e-3) / 1e12 / BF16_MFMA_TFLOPS),
                      "hgrn2_lb0_bf16_B8_H16_d128_L4096")
 
 
@@ -633,6 +633,17 @@ def form_hgrn2_key(args, device):
                      dict(mfma_equiv_tflops=flops / (t["ms"] * 1e-3) / 1e12,
                           mfma_util=flops / (t["ms"] * 1e-3) / 1e12 / BF16_MFMA_TFLOPS),
                      "hgrn2_key_gate_bf16_B8_H16_d128_L4096")
+
+
+def form_hgrn2_key_lb0(args, device):
+    import selective_state_space_diag_amd as ssd
+    _, (B, L, H, dd), q, k, v, g = _hgrn2_inputs(device, 16)
+    t = time_calls(lambda kk: ssd.hgrn2_scan(q, k, v, g, 0.0, gate_axis="key"), 1, 10, 2)
+    flops = 2 * B * L * H * (2 * 64 * dd + 2 * dd * dd)  # chunked form at chunk 64
+    return record_of(t, B * L * H * dd * dd, hgrn2_bytes(B, L, H, dd),
+                     dict(mfma_equiv_tflops=flops / (t["ms"] * 1e-3) / 1e12,
+                          mfma_util=flops / (t["ms"] * 1e-3) / 1e12 / BF16_MFMA_TFLOPS),
+                     "hgrn2_key_gate_lb0_bf16_B8_H16_d128_L4096")
 
 
 def form_readout_norm(args, device):
@@ -682,6 +693,7 @@ FORMS = {
     "hgrn2_lb0_bf16_B8_H16_d128_L4096": form_hgrn2_lb0,
     "hgrn2_backward_bf16_B8_H16_d128_L4096": form_hgrn2_backward,
     "hgrn2_key_gate_bf16_B8_H16_d128_L4096": form_hgrn2_key,
+    "hgrn2_key_gate_lb0_bf16_B8_H16_d128_L4096": form_hgrn2_key_lb0,
     "readout_norm_B8_L4096_width2048": form_readout_norm,
     "selective_backward_varlen_L131072_D4096_N16_32seq": form_selective_varlen_backward,
 }

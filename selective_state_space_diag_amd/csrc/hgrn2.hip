@@ -703,16 +703,18 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
 //   O      = (Qt Kt^T (.) M) V + Qt S0^T,      Qt = Q (.) Gamma,   Kt = K (/) Gamma
 //   S_next = S0 diag(Gamma_C) + V^T Kh,        Kh = K (.) Gamma_C (/) Gamma
 // (M causal, diagonal included).  Qt and Kh are bounded by |Q| and |K| (Gamma decreases along the
-// chunk); Kt reaches |K| / Gamma_C, which the fp32 products hold while Gamma_C >= 2^-96, i.e. for every
-// lower bound >= 2^-1.5 (smaller bounds take the register sweep).  The three derived operands are split
-// into bf16 pairs hi + lo like the derived operands of the row-gated form; V enters exactly.
+// chunk); Kt reaches |K| / Gamma_C, which the fp32 products hold while Gamma_C >= 2^-96: always for
+// lower bounds >= 2^-1.5.  GUARD (smaller bounds): a chunk with Gamma_C below that for any key column
+// goes token by token on the state the waves hold, as in the row-gated kernel.  The three derived
+// operands are split into bf16 pairs hi + lo like the derived operands of the row-gated form; V enters
+// exactly.
 // The workgroup, wave roles, tile layouts and product shapes are those of hgrn2_chunk_kernel with these
 // operands in place of Q, K and W; the gate step covers all 128 key columns in each of the two
 // workgroups of a head.  A NaN gate, query or key reaches exactly the outputs and state entries the
 // recurrence sends it to (every ratio it enters is masked by assignment, not by multiplication); a
-// non-finite value would reach the row's earlier outputs through masked products (0 * inf), so it
-// enters as 0 and the row's outputs from that token on, and its state, are set to NaN (as in the
-// row-gated kernel).
+// non-finite value would reach the row's earlier outputs through masked products (0 * inf): without
+// GUARD it enters as 0 and the row's outputs from that token on, and its state, are set to NaN (as in
+// the row-gated kernel); with GUARD its chunk goes token by token, which propagates it exactly.
 struct H2KeyLds {
   uint16_t qt[2][h2::kQkTile];  // Q (.) Gamma, hi and lo (qk layout)
   uint16_t kt[2][h2::kQkTile];  // K (/) Gamma
@@ -751,6 +753,7 @@ __device__ __forceinline__ void h2k_fetch(const H2Params& p, int64_t b, int64_t 
 // Gates, part 1: g = lb + (1 - lb) sigmoid(logit) for the thread's two key columns (1 past the chunk's
 // valid tokens), running products over its 8 tokens, group products published; non-finite values of
 // its value row replaced by 0 and the row's first such token recorded.
+template <bool GUARD>
 __device__ __forceinline__ void h2k_gate1(H2KeyLds& sm, int lane, int gp, int valid, float lb, float one_m_lb,
                                           H2KeyPrefetch& f, float (&run)[kGateTok][2], int* nanpos) {
   float r0 = 1.0f, r1 = 1.0f;
@@ -764,20 +767,24 @@ __device__ __forceinline__ void h2k_gate1(H2KeyLds& sm, int lane, int gp, int va
     run[u][0] = r0;
     run[u][1] = r1;
   }
-  *reinterpret_cast<float2*>(&sm.gpart[gp][2 * lane]) = make_float2(r0, r1);
   float z = 0.0f;  // NaN exactly when one of the values is not finite
 #pragma unroll
   for (int u = 0; u < kGateTok; ++u) z = fmaf(bf16_lo(f.v[u]), 0.0f, z);
   if (z != z) {
+    if (GUARD) {
+      r0 = __builtin_nanf("");  // fails the chunk's decay check: the chunk goes token by token
+    } else {
 #pragma unroll
-    for (int u = 0; u < kGateTok; ++u) {
-      if (!__builtin_isfinite(bf16_lo(f.v[u]))) {
-        f.v[u] = 0u;
-        atomicMin(&nanpos[lane], gp * kGateTok + u);
-        nanpos[kRows] = 1;
+      for (int u = 0; u < kGateTok; ++u) {
+        if (!__builtin_isfinite(bf16_lo(f.v[u]))) {
+          f.v[u] = 0u;
+          atomicMin(&nanpos[lane], gp * kGateTok + u);
+          nanpos[kRows] = 1;
+        }
       }
     }
   }
+  *reinterpret_cast<float2*>(&sm.gpart[gp][2 * lane]) = make_float2(r0, r1);
 }
 
 // Gates, part 2: Gamma for the thread's tokens and key columns, the derived operands Qt, Kt, Kh as bf16
@@ -813,6 +820,83 @@ __device__ __forceinline__ void h2k_gate2(H2KeyLds& sm, int lane, int gp, const 
   const int xg = h2::vw_gate_lane(lane, gp);
 #pragma unroll
   for (int u = 0; u < kGateTok; ++u) sm.v[h2::vw_gate_wr(lane, xg, gp, u)] = (uint16_t)f.v[u];
+}
+
+// One chunk token by token (GUARD; the chunk failed the decay check).  The chunk's queries, keys and gate
+// logits are reloaded, row-major [t][j], into the space of the derived operands (unused by this path);
+// wave (rt, half_t) applies S[i][j] = g_j S[i][j] + v_i k_j to its entries S^T[j][i]
+// (j = 16 (4 half_t + q) + 4 lg + r, i = iw + l16) and sums S[i][j] q_j over them, then over its lane
+// groups; the two halves of j meet in LDS (partials in kt[1] and kh[0]) after the chunk.  Values come from
+// the chunk's V tile.  Called by every thread after the barrier that publishes the chunk's gate step; ends
+// with a barrier.  Out of line, with the state passed and returned by value, as h2_chunk_tokens.
+template <typename Tout>
+__device__ __forceinline__ H2State h2k_chunk_tokens(const H2Params& p, H2KeyLds& sm, int64_t b, int64_t hh, int i0,
+                                                   int64_t t0, int valid, int tid, int half_t, int iw, float lb,
+                                                   float one_m_lb, H2State S) {
+  const int lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
+  uint16_t* qr = sm.qt[0];
+  uint16_t* kr = sm.qt[1];
+  uint16_t* gr = sm.kt[0];
+  static_assert(sizeof(uint16_t) * kCh * kDh <= sizeof(sm.qt[0]), "a chunk of one input fits in one operand tile");
+  static_assert(sizeof(float) * kCh * kRows <= sizeof(sm.kt[1]), "the partial readouts of a half fit in one tile");
+  {
+    const uint32_t row_bytes = (uint32_t)(p.H * kDh * 2);
+    const auto wq = h2_window(p, p.q, b, hh, t0, valid), wk = h2_window(p, p.k, b, hh, t0, valid);
+    const auto wg = h2_window(p, p.g, b, hh, t0, valid);
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int idx = it * kWaves * 64 + tid;  // 1024 segments of 8 elements: row t, segment seg
+      const int t = idx >> 4, seg = idx & 15;
+      const int off = (int)((uint32_t)t * row_bytes + (uint32_t)seg * 16);
+      *reinterpret_cast<v4i_t*>(&qr[t * kDh + seg * 8]) = __builtin_amdgcn_raw_buffer_load_b128(wq, off, 0, 0);
+      *reinterpret_cast<v4i_t*>(&kr[t * kDh + seg * 8]) = __builtin_amdgcn_raw_buffer_load_b128(wk, off, 0, 0);
+      *reinterpret_cast<v4i_t*>(&gr[t * kDh + seg * 8]) = __builtin_amdgcn_raw_buffer_load_b128(wg, off, 0, 0);
+    }
+  }
+  __syncthreads();
+  float* part = half_t ? reinterpret_cast<float*>(&sm.kh[0][0]) : reinterpret_cast<float*>(&sm.kt[1][0]);
+  const int i = iw + l16;
+#pragma unroll 1
+  for (int t = 0; t < valid; ++t) {
+    const float v = bf16_to_f32(sm.v[h2::vw_off(t, i)]);
+    float acc = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int j0 = 16 * (4 * half_t + q) + 4 * lg;
+      const uint2 kk = *reinterpret_cast<const uint2*>(&kr[t * kDh + j0]);
+      const uint2 qq = *reinterpret_cast<const uint2*>(&qr[t * kDh + j0]);
+      const uint2 gg = *reinterpret_cast<const uint2*>(&gr[t * kDh + j0]);
+      const float kj[4] = {bf16_lo(kk.x), bf16_hi(kk.x), bf16_lo(kk.y), bf16_hi(kk.y)};
+      const float qj[4] = {bf16_lo(qq.x), bf16_hi(qq.x), bf16_lo(qq.y), bf16_hi(qq.y)};
+      const float gl[4] = {bf16_lo(gg.x), bf16_hi(gg.x), bf16_lo(gg.y), bf16_hi(gg.y)};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float g = fmaf(one_m_lb, sigmoid_f(gl[r]), lb);
+        S.q[q][r] = fmaf(g, S.q[q][r], v * kj[r]);
+        acc = fmaf(S.q[q][r], qj[r], acc);
+      }
+    }
+    acc += __shfl_xor(acc, 16);
+    acc += __shfl_xor(acc, 32);
+    if (lg == 0) part[t * kRows + i] = acc;
+  }
+  __syncthreads();
+  // o[t][i] = half 0 + half 1, 8 outputs per thread
+  const float* p0 = reinterpret_cast<const float*>(&sm.kt[1][0]);
+  const float* p1 = reinterpret_cast<const float*>(&sm.kh[0][0]);
+  const auto wo = h2_out_window<Tout>(p, b, hh, i0, t0, valid);
+  const uint32_t row_bytes = (uint32_t)(p.H * kDh * (int64_t)sizeof(Tout));
+#pragma unroll 1
+  for (int e = 0; e < kCh * kRows / (kWaves * 64); ++e) {
+    const int idx = e * kWaves * 64 + tid;
+    const int t = idx >> 6, ii = idx & 63;
+    if (t < valid) {
+      const float o = p0[t * kRows + ii] + p1[t * kRows + ii];
+      win<Tout, 1>::store(wo, (uint32_t)(ii * (int)sizeof(Tout)), (uint32_t)t * row_bytes, &o);
+    }
+  }
+  __syncthreads();  // the next chunk's gate step writes these tiles again
+  return S;
 }
 
 // Causal tile ti of Qt Kt^T as D[s][t] (three products per k-step: hi hi, lo hi, hi lo), masked and split
@@ -916,7 +1000,7 @@ __device__ __forceinline__ void h2k_out(__amdgpu_buffer_rsrc_t wo, uint32_t row_
                          oa[a][2], oa[a][3]);
 }
 
-template <typename Tout>
+template <typename Tout, bool GUARD>
 __global__ __launch_bounds__(kWaves * 64) void hgrn2_key_chunk_kernel(H2Params p) {
   __shared__ H2KeyLds sm;
   const int tid = threadIdx.x;
@@ -951,7 +1035,7 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_key_chunk_kernel(H2Params p
   h2k_fetch(p, b, hh, i0, 0, lane, gp, f);
   if (tid < 2 * (kRows + 4)) sm.nanpos[tid / (kRows + 4)][tid % (kRows + 4)] = tid % (kRows + 4) < kRows ? kCh : 0;
   __syncthreads();
-  h2k_gate1(sm, lane, gp, (int)min((int64_t)kCh, p.L), lb, one_m_lb, f, run, sm.nanpos[0]);
+  h2k_gate1<GUARD>(sm, lane, gp, (int)min((int64_t)kCh, p.L), lb, one_m_lb, f, run, sm.nanpos[0]);
   for (int64_t c = 0; c < nchunks; ++c) {
     const int64_t t0 = c * kCh;
     const int valid = (int)min((int64_t)kCh, p.L - t0);
@@ -975,6 +1059,18 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_key_chunk_kernel(H2Params p
     }
     __syncthreads();  // Qt, Kt, Kh, V, Gamma_C and the state halves visible
 
+    // ---- a chunk whose decay over the chunk underflows the products' range goes token by token
+    if (GUARD && !__all(sm.gcol[lane] >= kGammaFloor && sm.gcol[lane + 64] >= kGammaFloor)) {
+      H2State st{{S[0], S[1], S[2], S[3]}};
+      st = h2k_chunk_tokens<Tout>(p, sm, b, hh, i0, t0, valid, tid, half_t, iw, lb, one_m_lb, st);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) S[q] = st.q[q];
+      if (c + 1 < nchunks)
+        h2k_gate1<GUARD>(sm, lane, gp, (int)min((int64_t)kCh, p.L - t0 - kCh), lb, one_m_lb, f, run,
+                         sm.nanpos[par ^ 1]);
+      continue;
+    }
+
     floatx4_t os[2];
     {
       uint4 oth_hi[2], oth_lo[2];
@@ -995,7 +1091,7 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_key_chunk_kernel(H2Params p
       const uint32_t row_bytes = (uint32_t)(p.H * kDh * (int64_t)sizeof(Tout));
       if (half_t == 0) h2k_out<0, Tout>(wo, row_bytes, sm, iw, lane, os);
       else h2k_out<1, Tout>(wo, row_bytes, sm, iw, lane, os);
-      if (__builtin_amdgcn_readfirstlane(sm.nanpos[par][kRows]) != 0) {
+      if (!GUARD && __builtin_amdgcn_readfirstlane(sm.nanpos[par][kRows]) != 0) {
         h2_out_nan<Tout>(wo, row_bytes, sm.nanpos[par], iw, lane, half_t);
         if (sm.nanpos[par][iw + l16] < kCh) {
 #pragma unroll
@@ -1033,7 +1129,8 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_key_chunk_kernel(H2Params p
     }
     // gates, part 1, of the next chunk (its inputs were loaded during this chunk)
     if (c + 1 < nchunks)
-      h2k_gate1(sm, lane, gp, (int)min((int64_t)kCh, p.L - t0 - kCh), lb, one_m_lb, f, run, sm.nanpos[par ^ 1]);
+      h2k_gate1<GUARD>(sm, lane, gp, (int)min((int64_t)kCh, p.L - t0 - kCh), lb, one_m_lb, f, run,
+                       sm.nanpos[par ^ 1]);
   }
 
   if (p.S_last) {
@@ -1053,8 +1150,14 @@ hipError_t launch_hgrn2_key_chunk(const Hgrn2ScanArgs& a, hipStream_t s) {
   p.q = a.q; p.k = a.k; p.v = a.v; p.g = a.g_logit; p.lb = a.lower_bound;
   p.S0 = a.S0; p.o = a.o; p.S_last = a.S_last;
   const dim3 grid((unsigned)(a.B * a.H * 2));
-  if (a.out_bf16) hipLaunchKernelGGL((hgrn2_key_chunk_kernel<bf16_t>), grid, dim3(kWaves * 64), 0, s, p);
-  else hipLaunchKernelGGL((hgrn2_key_chunk_kernel<float>), grid, dim3(kWaves * 64), 0, s, p);
+  const bool guard = !(a.lower_bound >= 0.35355339f);  // lower_bound^64 >= 2^-96 otherwise
+  if (a.out_bf16) {
+    if (guard) hipLaunchKernelGGL((hgrn2_key_chunk_kernel<bf16_t, true>), grid, dim3(kWaves * 64), 0, s, p);
+    else hipLaunchKernelGGL((hgrn2_key_chunk_kernel<bf16_t, false>), grid, dim3(kWaves * 64), 0, s, p);
+  } else {
+    if (guard) hipLaunchKernelGGL((hgrn2_key_chunk_kernel<float, true>), grid, dim3(kWaves * 64), 0, s, p);
+    else hipLaunchKernelGGL((hgrn2_key_chunk_kernel<float, false>), grid, dim3(kWaves * 64), 0, s, p);
+  }
   return hipGetLastError();
 }
 

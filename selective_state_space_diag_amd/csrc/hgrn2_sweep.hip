@@ -611,9 +611,10 @@ hipError_t launch_hgrn2_row_sweep(const Hgrn2ScanArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_hgrn2_key_scan(const Hgrn2ScanArgs& a, hipStream_t s) {
-  // chunked MFMA form where its decay ratios stay in range (Gamma_C >= lower_bound^64 >= 2^-96) and a
-  // chunk's rows of one head span under 2^31 bytes (H < 2^16); otherwise the register sweep below
-  if (a.in_bf16 && a.d == 128 && a.H < 65536 && a.lower_bound >= 0.35355339f) return launch_hgrn2_key_chunk(a, s);
+  // chunked MFMA form (bf16 inputs, d = 128, any lower bound: a chunk whose decay underflows the
+  // products' range goes token by token inside it) when a chunk's rows of one head span under 2^31
+  // bytes (H < 2^16); otherwise the register sweep below
+  if (a.in_bf16 && a.d == 128 && a.H < 65536) return launch_hgrn2_key_chunk(a, s);
   H2SweepParams p{};
   p.B = a.B; p.L = a.L; p.H = a.H;
   p.q = a.q; p.k = a.k; p.v = a.v; p.x = a.g_logit; p.lb = a.lower_bound;

@@ -239,7 +239,7 @@ hipError_t launch_hgrn2_update(const Hgrn2UpdateArgs& a, hipStream_t s);
 hipError_t launch_hgrn2_key_scan(const Hgrn2ScanArgs& a, hipStream_t s);
 // The row-gated scan as a register sweep (the cases the chunked MFMA kernel does not take).
 hipError_t launch_hgrn2_row_sweep(const Hgrn2ScanArgs& a, hipStream_t s);
-// The key-axis-gated scan in chunked MFMA form: bf16 inputs, d = 128, lower_bound >= 2^-1.5.
+// The key-axis-gated scan in chunked MFMA form: bf16 inputs, d = 128, any lower bound.
 hipError_t launch_hgrn2_key_chunk(const Hgrn2ScanArgs& a, hipStream_t s);
 hipError_t launch_hgrn2_key_update(const Hgrn2UpdateArgs& a, hipStream_t s);
 
