@@ -96,7 +96,9 @@ PROFILES = {
                                                           "sequences, D=4096 N=16 bf16", _SEL_SOURCES),
     "hgrn2_backward_bf16_B8_H16_d128_L4096": ("hgrn2_backward_B8_H16_d128_L4096.md",
                                               "HGRN2 backward B=8 H=16 d=128 L=4096 bf16, the forward output given "
-                                              "(one forward call first)", _SWEEP_SOURCES),
+                                              "(one forward call first); one call = transposes, three chunked "
+                                              "MFMA passes, the gate-gradient sums",
+                                              _H2_SOURCES + [_CSRC + "hgrn2_sweep.hip"]),
     "hgrn2_key_gate_bf16_B8_H16_d128_L4096": ("hgrn2_key_gate_scan_B8_H16_d128_L4096.md",
                                               "HGRN2 scan with the gate on the key axis, B=8 H=16 d=128 L=4096 bf16 "
                                               "in, fp32 out, lower bound 0.5; one call = one chunked MFMA kernel",
@@ -616,11 +618,12 @@ def form_hgrn2_backward(args, device):
     gen, (B, L, H, dd), q, k, v, g = _hgrn2_inputs(device, 16)
     do = gen.randn((B, L, H, dd), std=dd ** -0.5)
     o = ssd.hgrn2_scan(q, k, v, g, 0.5)
-    t = time_calls(lambda kk: ssd.hgrn2_scan_backward(q, k, v, g, 0.5, do, o=o), 1, 3, 1)
-    vflops = 15 * B * L * H * dd * dd
+    t = time_calls(lambda kk: ssd.hgrn2_scan_backward(q, k, v, g, 0.5, do, o=o), 1, 10, 2)
+    # three adjoint passes in the chunked form (dq, dv, dk), each the forward's products at chunk 64
+    flops = 3 * 2 * B * L * H * (2 * 64 * dd + 2 * dd * dd)
     return record_of(t, B * L * H * dd * dd, hgrn2_bwd_bytes(B, L, H, dd),
-                     dict(valu_tflops=vflops / (t["ms"] * 1e-3) / 1e12,
-                          valu_frac=vflops / (t["ms"] * 1e-3) / 1e12 / FP32_SCALAR_FMA_TFLOPS),
+                     dict(mfma_equiv_tflops=flops / (t["ms"] * 1e-3) / 1e12,
+                          mfma_util=flops / (t["ms"] * 1e-3) / 1e12 / BF16_MFMA_TFLOPS),
                      "hgrn2_backward_bf16_B8_H16_d128_L4096")
 
 

@@ -375,9 +375,15 @@ int ssd_hgrn2_scan(int64_t B, int64_t L, int64_t H, int64_t d, int in_dtype, int
  *   dq, dk, dv, dg_logit : [B, L, H, d] (out dtype);  dS0 : [B, H, d, d] fp32 or NULL
  *   workspace         : see "Workspaces"; size from ssd_hgrn2_scan_backward_workspace_bytes(B, L, H,
  *                       d, in_dtype, have_o) with have_o = (o != NULL)
- * Any lower_bound in [0, 1] (no decay ratios are formed).  Every output is overwritten.  The workspace
- * holds S_last (B * H * d * d fp32) and, for fp32 inputs, the state after every 32nd token (from
- * which the running sum c_t is restarted exactly: B * H * floor((L - 1) / 32) * d * d fp32).
+ * Any lower_bound in [0, 1].  Every output is overwritten.  With bf16 inputs and d = 128 the adjoint
+ * passes run in the chunked matrix form of ssd_hgrn2_scan (dq as the key-axis scan of (dO, v, k) from
+ * S0^T; dv as the row-gated scan backward in time of (k, q, dO) with the next token's gate, from dS_last;
+ * dk as the key-axis scan backward in time of (v, dO, q) from dS_last^T), and c_t is summed over
+ * 64-token segments; the workspace then holds R_0, S0^T, dS_last^T and S_L^T (4 * B * H * d * d fp32),
+ * the segment sums (B * H * ceil(L / 64) * d fp32) and dv in fp32 (B * L * H * d fp32, the sums' input
+ * when the outputs are bf16).  Otherwise (fp32 inputs, other d) the gradients come from register sweeps
+ * and the workspace holds S_last (B * H * d * d fp32) and, for fp32 inputs, the state after every 32nd
+ * token (from which the running sum c_t is restarted exactly: B * H * floor((L - 1) / 32) * d * d fp32).
  * Errors as ssd_hgrn2_scan, plus SSD_ERR_NULL for missing dO, dq, dk, dv or dg_logit, and the
  * workspace errors. */
 int ssd_hgrn2_scan_backward(int64_t B, int64_t L, int64_t H, int64_t d, int in_dtype, int out_dtype,

@@ -161,34 +161,63 @@ struct H2GatePrefetch {
 };
 
 // Window over the rows [t0, t0 + valid) of head hh of batch b in a [B, L, H, 128] bf16 array:
-// row r at byte r * H * 256; rows at or past `valid` fall outside and read as zero.
+// row r at byte r * H * 256; rows at or past `valid` fall outside and read as zero (valid >= 1).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t h2_window(const H2Params& p, const void* a, int64_t b, int64_t hh,
                                                             int64_t t0, int valid) {
   const char* base = static_cast<const char*>(a) + (((b * p.L + t0) * p.H + hh) * kDh) * 2;
   return make_window(base, (uint32_t)((int64_t)(valid - 1) * p.H * kDh * 2 + kDh * 2));
 }
 
+// Where a chunk's tokens lie.  The kernels walk "positions" 0 .. L - 1 in chunks of 64; position t is
+// token t, or with REV (a pass backward in time, for the adjoint recurrence) token L - 1 - t.  A chunk
+// covers the tokens [row0, row0 + valid); position u of the chunk (0 <= u < 64) sits at byte off(u)
+// of a window opened at row0, negative (outside) for u >= valid.  With REV the gate of position t is the
+// gate of the token after it (the adjoint decays by g_{t+1}): its window opens one row later and ends
+// at row L - 1, and the chunk's position 0 at the end of the sequence has gate 1 (first_one).
+template <bool REV>
+struct H2Chunk {
+  int64_t row0;
+  int valid;
+  __device__ __forceinline__ H2Chunk(const H2Params& p, int64_t t0, int valid_) : valid(valid_) {
+    row0 = REV ? p.L - t0 - valid_ : t0;
+  }
+  __device__ __forceinline__ explicit H2Chunk(int valid_) : row0(0), valid(valid_) {}  // offsets only
+  __device__ __forceinline__ int off(int u, uint32_t row_bytes) const {
+    return (REV ? valid - 1 - u : u) * (int)row_bytes;
+  }
+  // window over this chunk's gate rows
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t gate_window(const H2Params& p, int64_t b, int64_t hh) const {
+    if (!REV) return h2_window(p, p.g, b, hh, row0, valid);
+    const int n = (int)min((int64_t)valid, p.L - row0 - 1);  // 0 for a one-token sequence
+    return n > 0 ? h2_window(p, p.g, b, hh, row0 + 1, n) : make_window(p.g, 0u);
+  }
+};
+
+template <bool REV>
 __device__ __forceinline__ void h2_fetch(const H2Params& p, int64_t b, int64_t hh, int64_t t0, int tid,
                                          H2Prefetch& f) {
   const int valid = (int)min((int64_t)kCh, p.L - t0);
+  const H2Chunk<REV> ch(p, t0, valid);
   const uint32_t row_bytes = (uint32_t)(p.H * kDh * 2);
-  const auto wq = h2_window(p, p.q, b, hh, t0, valid), wk = h2_window(p, p.k, b, hh, t0, valid);
+  const auto wq = h2_window(p, p.q, b, hh, ch.row0, valid), wk = h2_window(p, p.k, b, hh, ch.row0, valid);
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
-    const int idx = it * 512 + tid;  // 1024 segments of 8 elements: row t, segment seg
+    const int idx = it * 512 + tid;  // 1024 segments of 8 elements: position t, segment seg
     const int t = idx >> 4, seg = idx & 15;
-    const uint32_t off = (uint32_t)t * row_bytes + (uint32_t)seg * 16;
+    const uint32_t off = (uint32_t)(ch.off(t, row_bytes) + seg * 16);
     f.q[it] = __builtin_amdgcn_raw_buffer_load_b128(wq, (int)off, 0, 0);
     f.k[it] = __builtin_amdgcn_raw_buffer_load_b128(wk, (int)off, 0, 0);
   }
 }
 
+template <bool REV>
 __device__ __forceinline__ void h2_fetch_gates(const H2Params& p, int64_t b, int64_t hh, int i0, int64_t t0, int tid,
                                                H2GatePrefetch& f) {
   const int valid = (int)min((int64_t)kCh, p.L - t0);
+  const H2Chunk<REV> ch(p, t0, valid);
   const uint32_t row_bytes = (uint32_t)(p.H * kDh * 2);
-  const auto wv = h2_window(p, p.v, b, hh, t0, valid), wg = h2_window(p, p.g, b, hh, t0, valid);
-  const uint32_t off = (uint32_t)(tid >> 3) * row_bytes + (uint32_t)(i0 + 8 * (tid & 7)) * 2;
+  const auto wv = h2_window(p, p.v, b, hh, ch.row0, valid), wg = ch.gate_window(p, b, hh);
+  const uint32_t off = (uint32_t)(ch.off(tid >> 3, row_bytes) + (i0 + 8 * (tid & 7)) * 2);
   f.g = __builtin_amdgcn_raw_buffer_load_b128(wg, (int)off, 0, 0);
   f.v = __builtin_amdgcn_raw_buffer_load_b128(wv, (int)off, 0, 0);
 }
@@ -210,8 +239,9 @@ __device__ __forceinline__ void h2_stage_gates(H2Lds& sm, int tid, const H2GateP
 // and the value 0 (the products stay finite and exact for the tokens before it) and the token is
 // recorded in nanpos, from which the row's outputs and its state are set to NaN.
 template <bool GUARD>
-__device__ __forceinline__ void h2_gate1(H2Lds& sm, int lane, int gp, int valid, float lb, float one_m_lb,
-                                         float (&gam_run)[kGateTok], float (&vv)[kGateTok], int* nanpos) {
+__device__ __forceinline__ void h2_gate1(H2Lds& sm, int lane, int gp, int valid, int first_one, float lb,
+                                         float one_m_lb, float (&gam_run)[kGateTok], float (&vv)[kGateTok],
+                                         int* nanpos) {
   const int o0 = h2::gv_gate_off(lane & 15, lane >> 4, gp, 0), o1 = h2::gv_gate_off(lane & 15, lane >> 4, gp, 1);
   const uint2 g0 = lds_tr(&sm.gstage[o0]), g1 = lds_tr(&sm.gstage[o1]);
   const uint2 v0 = lds_tr(&sm.vstage[o0]), v1 = lds_tr(&sm.vstage[o1]);
@@ -242,10 +272,10 @@ __device__ __forceinline__ void h2_gate1(H2Lds& sm, int lane, int gp, int valid,
       }
     }
   }
-  if (valid < kCh) {  // ragged last chunk: tokens past it leave the state unchanged
+  if (valid < kCh || first_one > 0) {  // positions past a ragged chunk leave the state unchanged
 #pragma unroll
     for (int u = 0; u < kGateTok; ++u)
-      if (gp * kGateTok + u >= valid) gv[u] = 1.0f;
+      if (gp * kGateTok + u >= valid || gp * kGateTok + u < first_one) gv[u] = 1.0f;
   }
   float run = 1.0f;
 #pragma unroll
@@ -324,9 +354,9 @@ __device__ __forceinline__ void h2_out_state(const uint16_t* Qs, int lane, const
 // drops stores there, so the ragged last chunk needs no per-lane condition.
 template <typename Tout>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t h2_out_window(const H2Params& p, int64_t b, int64_t hh, int i0,
-                                                                int64_t t0, int valid) {
+                                                                int64_t row0, int valid) {
   constexpr int es = sizeof(Tout);
-  const char* base = static_cast<const char*>(p.o) + (((b * p.L + t0) * p.H + hh) * kDh + i0) * es;
+  const char* base = static_cast<const char*>(p.o) + (((b * p.L + row0) * p.H + hh) * kDh + i0) * es;
   return make_window(base, (uint32_t)((int64_t)(valid - 1) * p.H * kDh * es + kRows * es));
 }
 
@@ -349,9 +379,9 @@ template <> struct h2_store4<bf16_t> {
   }
 };
 
-template <int H, typename Tout>
-__device__ __forceinline__ void h2_out(__amdgpu_buffer_rsrc_t wo, uint32_t row_bytes, H2Lds& sm, int iw, int lane,
-                                       const floatx4_t (&os)[2]) {
+template <int H, typename Tout, bool REV>
+__device__ __forceinline__ void h2_out(__amdgpu_buffer_rsrc_t wo, uint32_t row_bytes, int valid, H2Lds& sm, int iw,
+                                       int lane, const floatx4_t (&os)[2]) {
   using TL = Tiles<H>;
   const int l16 = lane & 15, lg = lane >> 4;
   // W as A operands: slots s = 32 ks + 16 h' + 4 lg + r; lane 4b + c of a group points at
@@ -393,11 +423,13 @@ __device__ __forceinline__ void h2_out(__amdgpu_buffer_rsrc_t wo, uint32_t row_b
 #pragma unroll
   for (int r = 0; r < 4; ++r) igc[r] = hw_rcp(sm.gcol[iw + 4 * lg + r]);
   const uint32_t lane_off = (uint32_t)l16 * row_bytes + (uint32_t)(4 * lg * (int)sizeof(Tout));
+  const H2Chunk<REV> ch(valid);
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     const int t = 16 * TL::tt(a) + l16;
     const float4 gm = *reinterpret_cast<const float4*>(&sm.gam[t][iw + 4 * lg]);
-    h2_store4<Tout>::run(wo, lane_off, 16 * TL::tt(a) * row_bytes + iw * (uint32_t)sizeof(Tout),
+    h2_store4<Tout>::run(wo, REV ? (uint32_t)(ch.off(t, row_bytes) + (4 * lg + iw) * (int)sizeof(Tout)) : lane_off,
+                         REV ? 0u : 16 * TL::tt(a) * row_bytes + iw * (uint32_t)sizeof(Tout),
                          gm.x * fmaf(oa[a][0], igc[0], os[a][0]), gm.y * fmaf(oa[a][1], igc[1], os[a][1]),
                          gm.z * fmaf(oa[a][2], igc[2], os[a][2]), gm.w * fmaf(oa[a][3], igc[3], os[a][3]));
   }
@@ -414,15 +446,16 @@ __device__ __forceinline__ void h2_out(__amdgpu_buffer_rsrc_t wo, uint32_t row_b
 struct H2State {
   floatx4_t q[4];
 };
-template <typename Tout>
+template <typename Tout, bool REV>
 __device__ __forceinline__ H2State h2_chunk_tokens(const H2Params& p, H2Lds& sm, const uint16_t* Qs, const uint16_t* Ks,
                                                 int64_t b, int64_t hh, int i0, int64_t t0, int valid, int tid,
                                                 int half_t, int iw, float lb, float one_m_lb, H2State S) {
   const int lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
+  const H2Chunk<REV> ch(p, t0, valid);
   // the chunk's gate logits and values, row-major [t][i] over the workgroup's 64 value rows
   {
     H2GatePrefetch f;
-    h2_fetch_gates(p, b, hh, i0, t0, tid, f);
+    h2_fetch_gates<REV>(p, b, hh, i0, t0, tid, f);
     const int t = tid >> 3, c0 = 8 * (tid & 7);
     *reinterpret_cast<v4i_t*>(&sm.w_lo[t * kRows + c0]) = f.g;
     *reinterpret_cast<v4i_t*>(&sm.w[t * kRows + c0]) = f.v;
@@ -432,7 +465,7 @@ __device__ __forceinline__ H2State h2_chunk_tokens(const H2Params& p, H2Lds& sm,
   const int i = iw + l16;
 #pragma unroll 1
   for (int t = 0; t < valid; ++t) {
-    const float g = fmaf(one_m_lb, sigmoid_f(bf16_to_f32(sm.w_lo[t * kRows + i])), lb);
+    const float g = (REV && t0 == 0 && t == 0) ? 1.0f : fmaf(one_m_lb, sigmoid_f(bf16_to_f32(sm.w_lo[t * kRows + i])), lb);
     const float v = bf16_to_f32(sm.w[t * kRows + i]);
     float acc = 0.0f;
 #pragma unroll
@@ -456,7 +489,7 @@ __device__ __forceinline__ H2State h2_chunk_tokens(const H2Params& p, H2Lds& sm,
   // o[t][i] = half 0 + half 1, 8 outputs per thread
   const float* p0 = &sm.gam[0][0];
   const float* p1 = reinterpret_cast<const float*>(&sm.sx[0][0][0][0][0]);
-  const auto wo = h2_out_window<Tout>(p, b, hh, i0, t0, valid);
+  const auto wo = h2_out_window<Tout>(p, b, hh, i0, ch.row0, valid);
   const uint32_t row_bytes = (uint32_t)(p.H * kDh * (int64_t)sizeof(Tout));
 #pragma unroll 1
   for (int e = 0; e < kCh * kRows / (kWaves * 64); ++e) {
@@ -464,7 +497,7 @@ __device__ __forceinline__ H2State h2_chunk_tokens(const H2Params& p, H2Lds& sm,
     const int t = idx >> 6, ii = idx & 63;
     if (t < valid) {
       const float o = p0[t * kRows + ii] + p1[t * kRows + ii];
-      win<Tout, 1>::store(wo, (uint32_t)(ii * (int)sizeof(Tout)), (uint32_t)t * row_bytes, &o);
+      win<Tout, 1>::store(wo, (uint32_t)(ii * (int)sizeof(Tout)), (uint32_t)ch.off(t, row_bytes), &o);
     }
   }
   __syncthreads();  // gam and sx are written again by the next chunk
@@ -473,17 +506,19 @@ __device__ __forceinline__ H2State h2_chunk_tokens(const H2Params& p, H2Lds& sm,
 
 // NaN over the outputs of this wave's tiles (rows iw .. iw + 15, its two token tiles) at or after the first
 // non-finite token of their row (nanpos; kCh where there is none).
-template <typename Tout>
-__device__ __forceinline__ void h2_out_nan(__amdgpu_buffer_rsrc_t wo, uint32_t row_bytes, const int* nanpos, int iw,
-                                        int lane, int half_t) {
+template <typename Tout, bool REV>
+__device__ __forceinline__ void h2_out_nan(__amdgpu_buffer_rsrc_t wo, uint32_t row_bytes, int valid, const int* nanpos,
+                                        int iw, int lane, int half_t) {
   const float qnan = __builtin_nanf("");
+  const H2Chunk<REV> ch(valid);
 #pragma unroll 1
   for (int a = 0; a < 2; ++a) {
     const int tt = half_t ? (a ? 2 : 1) : (a ? 3 : 0);
 #pragma unroll 1
     for (int e = lane; e < 16 * 16; e += 64) {
       const int t = 16 * tt + (e >> 4), i = iw + (e & 15);
-      if (t >= nanpos[i]) win<Tout, 1>::store(wo, (uint32_t)(i * (int)sizeof(Tout)), (uint32_t)t * row_bytes, &qnan);
+      if (t >= nanpos[i] && t < valid)
+        win<Tout, 1>::store(wo, (uint32_t)(i * (int)sizeof(Tout)), (uint32_t)ch.off(t, row_bytes), &qnan);
     }
   }
 }
@@ -491,7 +526,7 @@ __device__ __forceinline__ void h2_out_nan(__amdgpu_buffer_rsrc_t wo, uint32_t r
 // GUARD: the Gamma_C check and the token-by-token path are compiled in.  Lower bounds >= 2^-1.5 cannot
 // fail the check (Gamma_C >= lower_bound^64 >= 2^-96) and take the instantiation without them, whose
 // main loop keeps its registers to itself.
-template <typename Tout, bool GUARD>
+template <typename Tout, bool GUARD, bool REV>
 __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
   __shared__ H2Lds sm;
   const int tid = threadIdx.x;
@@ -527,15 +562,16 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
   H2Prefetch f;
   H2GatePrefetch fg;
   float gam_run[kGateTok], vv[kGateTok];
-  h2_fetch(p, b, hh, 0, tid, f);
+  h2_fetch<REV>(p, b, hh, 0, tid, f);
   // gate part 1 of chunk 0; the gates of chunk c + 1 are staged during chunk c and their part 1
   // runs at the end of chunk c, so the gate step overlaps the previous chunk's products
-  h2_fetch_gates(p, b, hh, i0, 0, tid, fg);
+  h2_fetch_gates<REV>(p, b, hh, i0, 0, tid, fg);
   h2_stage_gates(sm, tid, fg);
-  if (nchunks > 1) h2_fetch_gates(p, b, hh, i0, kCh, tid, fg);
+  if (nchunks > 1) h2_fetch_gates<REV>(p, b, hh, i0, kCh, tid, fg);
   if (tid < 2 * (kRows + 4)) sm.nanpos[tid / (kRows + 4)][tid % (kRows + 4)] = tid % (kRows + 4) < kRows ? kCh : 0;
   __syncthreads();
-  h2_gate1<GUARD>(sm, tid & 63, wave, (int)min((int64_t)kCh, p.L), lb, one_m_lb, gam_run, vv, sm.nanpos[0]);
+  h2_gate1<GUARD>(sm, tid & 63, wave, (int)min((int64_t)kCh, p.L), REV ? 1 : 0, lb, one_m_lb, gam_run, vv,
+                  sm.nanpos[0]);
   for (int64_t c = 0; c < nchunks; ++c) {
     // Per-lane LDS addresses are loop-invariant and stay in registers across chunks: the LDS use
     // already limits the kernel to two waves per SIMD, so the registers they take are free.
@@ -569,7 +605,7 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
       sm.sx[rt][half_t][kk][1][lane] = my_lo[kk];
     }
     const int gi = tidv & 63, gp = wave;
-    if (c + 1 < nchunks) h2_fetch(p, b, hh, t0 + kCh, tid, f);  // in flight during this chunk
+    if (c + 1 < nchunks) h2_fetch<REV>(p, b, hh, t0 + kCh, tid, f);  // in flight during this chunk
     __syncthreads();  // Q, K, group products, state halves visible
 
     // ---- partner's half of the incoming state, then Q S^T for this half's token tiles
@@ -622,32 +658,32 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
     // ---- next chunk's gate inputs into LDS; the chunk after that starts loading
     if (c + 1 < nchunks) {
       h2_stage_gates(sm, tidv, fg);
-      if (c + 2 < nchunks) h2_fetch_gates(p, b, hh, i0, t0 + 2 * kCh, tid, fg);
+      if (c + 2 < nchunks) h2_fetch_gates<REV>(p, b, hh, i0, t0 + 2 * kCh, tid, fg);
     }
     __syncthreads();  // Gamma, W, Gamma_C, Q K^T tiles visible
 
     // ---- a chunk whose decay over the chunk underflows the products' range goes token by token
     if (GUARD && !__all(sm.gcol[lane] >= kGammaFloor)) {
       H2State st{{S[0], S[1], S[2], S[3]}};
-      st = h2_chunk_tokens<Tout>(p, sm, Qs, Ks, b, hh, i0, t0, valid, tid, half_t, iw, lb, one_m_lb, st);
+      st = h2_chunk_tokens<Tout, REV>(p, sm, Qs, Ks, b, hh, i0, t0, valid, tid, half_t, iw, lb, one_m_lb, st);
 #pragma unroll
       for (int q = 0; q < 4; ++q) S[q] = st.q[q];
       if (c + 1 < nchunks)
-        h2_gate1<GUARD>(sm, lane, gp, (int)min((int64_t)kCh, p.L - t0 - kCh), lb, one_m_lb, gam_run, vv,
+        h2_gate1<GUARD>(sm, lane, gp, (int)min((int64_t)kCh, p.L - t0 - kCh), 0, lb, one_m_lb, gam_run, vv,
                         sm.nanpos[(c + 1) & 1]);
       continue;
     }
 
     // ---- O^T for this half's token tiles
     {
-      const auto wo = h2_out_window<Tout>(p, b, hh, i0, t0, valid);
+      const auto wo = h2_out_window<Tout>(p, b, hh, i0, H2Chunk<REV>(p, t0, valid).row0, valid);
       const uint32_t row_bytes = (uint32_t)(p.H * kDh * (int64_t)sizeof(Tout));
-      if (half_t == 0) h2_out<0, Tout>(wo, row_bytes, sm, iw, lane, os);
-      else h2_out<1, Tout>(wo, row_bytes, sm, iw, lane, os);
+      if (half_t == 0) h2_out<0, Tout, REV>(wo, row_bytes, valid, sm, iw, lane, os);
+      else h2_out<1, Tout, REV>(wo, row_bytes, valid, sm, iw, lane, os);
       // a non-finite gate or value: its row reads NaN from that token on (this wave's outputs again), and
       // so does its state (NaN stays NaN through the state update below)
       if (!GUARD && __builtin_amdgcn_readfirstlane(sm.nanpos[c & 1][kRows]) != 0) {
-        h2_out_nan<Tout>(wo, row_bytes, sm.nanpos[c & 1], iw, lane, half_t);
+        h2_out_nan<Tout, REV>(wo, row_bytes, valid, sm.nanpos[c & 1], iw, lane, half_t);
         if (sm.nanpos[c & 1][iw + l16] < kCh) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) S[q] = floatx4_t{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
@@ -683,7 +719,7 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
     }
     // ---- gate part 1 of the next chunk (its inputs were staged before the last barrier)
     if (c + 1 < nchunks)
-      h2_gate1<GUARD>(sm, lane, gp, (int)min((int64_t)kCh, p.L - t0 - kCh), lb, one_m_lb, gam_run, vv,
+      h2_gate1<GUARD>(sm, lane, gp, (int)min((int64_t)kCh, p.L - t0 - kCh), 0, lb, one_m_lb, gam_run, vv,
                       sm.nanpos[(c + 1) & 1]);
   }
 
@@ -733,20 +769,24 @@ struct H2KeyPrefetch {
   uint32_t g[kGateTok], q[kGateTok], k[kGateTok], v[kGateTok];
 };
 
+template <bool REV>
 __device__ __forceinline__ void h2k_fetch(const H2Params& p, int64_t b, int64_t hh, int i0, int64_t t0, int lane,
                                           int gp, H2KeyPrefetch& f) {
   const int valid = (int)min((int64_t)kCh, p.L - t0);
+  const H2Chunk<REV> ch(p, t0, valid);
   const uint32_t row_bytes = (uint32_t)(p.H * kDh * 2);
-  const auto wq = h2_window(p, p.q, b, hh, t0, valid), wk = h2_window(p, p.k, b, hh, t0, valid);
-  const auto wg = h2_window(p, p.g, b, hh, t0, valid), wv = h2_window(p, p.v, b, hh, t0, valid);
+  const auto wq = h2_window(p, p.q, b, hh, ch.row0, valid), wk = h2_window(p, p.k, b, hh, ch.row0, valid);
+  const auto wg = ch.gate_window(p, b, hh), wv = h2_window(p, p.v, b, hh, ch.row0, valid);
   const int kc = 4 * lane, vc = 2 * (i0 + lane);
 #pragma unroll
   for (int u = 0; u < kGateTok; ++u) {
-    const int ro = (int)((uint32_t)(gp * kGateTok + u) * row_bytes);
-    f.g[u] = __builtin_amdgcn_raw_buffer_load_b32(wg, kc, ro, 0);
-    f.q[u] = __builtin_amdgcn_raw_buffer_load_b32(wq, kc, ro, 0);
-    f.k[u] = __builtin_amdgcn_raw_buffer_load_b32(wk, kc, ro, 0);
-    f.v[u] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wv, vc, ro, 0);
+    // forward: the position's row as the scalar offset; REV: the whole (possibly negative) offset per lane
+    const int ro = REV ? 0 : ch.off(gp * kGateTok + u, row_bytes);
+    const int rv = REV ? ch.off(gp * kGateTok + u, row_bytes) : 0;
+    f.g[u] = __builtin_amdgcn_raw_buffer_load_b32(wg, kc + rv, ro, 0);
+    f.q[u] = __builtin_amdgcn_raw_buffer_load_b32(wq, kc + rv, ro, 0);
+    f.k[u] = __builtin_amdgcn_raw_buffer_load_b32(wk, kc + rv, ro, 0);
+    f.v[u] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wv, vc + rv, ro, 0);
   }
 }
 
@@ -754,14 +794,14 @@ __device__ __forceinline__ void h2k_fetch(const H2Params& p, int64_t b, int64_t 
 // valid tokens), running products over its 8 tokens, group products published; non-finite values of
 // its value row replaced by 0 and the row's first such token recorded.
 template <bool GUARD>
-__device__ __forceinline__ void h2k_gate1(H2KeyLds& sm, int lane, int gp, int valid, float lb, float one_m_lb,
-                                          H2KeyPrefetch& f, float (&run)[kGateTok][2], int* nanpos) {
+__device__ __forceinline__ void h2k_gate1(H2KeyLds& sm, int lane, int gp, int valid, int first_one, float lb,
+                                          float one_m_lb, H2KeyPrefetch& f, float (&run)[kGateTok][2], int* nanpos) {
   float r0 = 1.0f, r1 = 1.0f;
 #pragma unroll
   for (int u = 0; u < kGateTok; ++u) {
     float g0 = fmaf(one_m_lb, sigmoid_f(bf16_lo(f.g[u])), lb);
     float g1 = fmaf(one_m_lb, sigmoid_f(bf16_hi(f.g[u])), lb);
-    if (gp * kGateTok + u >= valid) g0 = g1 = 1.0f;
+    if (gp * kGateTok + u >= valid || gp * kGateTok + u < first_one) g0 = g1 = 1.0f;
     r0 *= g0;
     r1 *= g1;
     run[u][0] = r0;
@@ -829,11 +869,12 @@ __device__ __forceinline__ void h2k_gate2(H2KeyLds& sm, int lane, int gp, const 
 // groups; the two halves of j meet in LDS (partials in kt[1] and kh[0]) after the chunk.  Values come from
 // the chunk's V tile.  Called by every thread after the barrier that publishes the chunk's gate step; ends
 // with a barrier.  Out of line, with the state passed and returned by value, as h2_chunk_tokens.
-template <typename Tout>
+template <typename Tout, bool REV>
 __device__ __forceinline__ H2State h2k_chunk_tokens(const H2Params& p, H2KeyLds& sm, int64_t b, int64_t hh, int i0,
                                                    int64_t t0, int valid, int tid, int half_t, int iw, float lb,
                                                    float one_m_lb, H2State S) {
   const int lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
+  const H2Chunk<REV> ch(p, t0, valid);
   uint16_t* qr = sm.qt[0];
   uint16_t* kr = sm.qt[1];
   uint16_t* gr = sm.kt[0];
@@ -841,13 +882,13 @@ __device__ __forceinline__ H2State h2k_chunk_tokens(const H2Params& p, H2KeyLds&
   static_assert(sizeof(float) * kCh * kRows <= sizeof(sm.kt[1]), "the partial readouts of a half fit in one tile");
   {
     const uint32_t row_bytes = (uint32_t)(p.H * kDh * 2);
-    const auto wq = h2_window(p, p.q, b, hh, t0, valid), wk = h2_window(p, p.k, b, hh, t0, valid);
-    const auto wg = h2_window(p, p.g, b, hh, t0, valid);
+    const auto wq = h2_window(p, p.q, b, hh, ch.row0, valid), wk = h2_window(p, p.k, b, hh, ch.row0, valid);
+    const auto wg = ch.gate_window(p, b, hh);
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
-      const int idx = it * kWaves * 64 + tid;  // 1024 segments of 8 elements: row t, segment seg
+      const int idx = it * kWaves * 64 + tid;  // 1024 segments of 8 elements: position t, segment seg
       const int t = idx >> 4, seg = idx & 15;
-      const int off = (int)((uint32_t)t * row_bytes + (uint32_t)seg * 16);
+      const int off = ch.off(t, row_bytes) + seg * 16;
       *reinterpret_cast<v4i_t*>(&qr[t * kDh + seg * 8]) = __builtin_amdgcn_raw_buffer_load_b128(wq, off, 0, 0);
       *reinterpret_cast<v4i_t*>(&kr[t * kDh + seg * 8]) = __builtin_amdgcn_raw_buffer_load_b128(wk, off, 0, 0);
       *reinterpret_cast<v4i_t*>(&gr[t * kDh + seg * 8]) = __builtin_amdgcn_raw_buffer_load_b128(wg, off, 0, 0);
@@ -871,7 +912,7 @@ __device__ __forceinline__ H2State h2k_chunk_tokens(const H2Params& p, H2KeyLds&
       const float gl[4] = {bf16_lo(gg.x), bf16_hi(gg.x), bf16_lo(gg.y), bf16_hi(gg.y)};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float g = fmaf(one_m_lb, sigmoid_f(gl[r]), lb);
+        const float g = (REV && t0 == 0 && t == 0) ? 1.0f : fmaf(one_m_lb, sigmoid_f(gl[r]), lb);
         S.q[q][r] = fmaf(g, S.q[q][r], v * kj[r]);
         acc = fmaf(S.q[q][r], qj[r], acc);
       }
@@ -884,7 +925,7 @@ __device__ __forceinline__ H2State h2k_chunk_tokens(const H2Params& p, H2KeyLds&
   // o[t][i] = half 0 + half 1, 8 outputs per thread
   const float* p0 = reinterpret_cast<const float*>(&sm.kt[1][0]);
   const float* p1 = reinterpret_cast<const float*>(&sm.kh[0][0]);
-  const auto wo = h2_out_window<Tout>(p, b, hh, i0, t0, valid);
+  const auto wo = h2_out_window<Tout>(p, b, hh, i0, ch.row0, valid);
   const uint32_t row_bytes = (uint32_t)(p.H * kDh * (int64_t)sizeof(Tout));
 #pragma unroll 1
   for (int e = 0; e < kCh * kRows / (kWaves * 64); ++e) {
@@ -892,7 +933,7 @@ __device__ __forceinline__ H2State h2k_chunk_tokens(const H2Params& p, H2KeyLds&
     const int t = idx >> 6, ii = idx & 63;
     if (t < valid) {
       const float o = p0[t * kRows + ii] + p1[t * kRows + ii];
-      win<Tout, 1>::store(wo, (uint32_t)(ii * (int)sizeof(Tout)), (uint32_t)t * row_bytes, &o);
+      win<Tout, 1>::store(wo, (uint32_t)(ii * (int)sizeof(Tout)), (uint32_t)ch.off(t, row_bytes), &o);
     }
   }
   __syncthreads();  // the next chunk's gate step writes these tiles again
@@ -962,9 +1003,9 @@ __device__ __forceinline__ void h2k_out_state(const H2KeyLds& sm, int lane, cons
 }
 
 // O^T tiles of this half: (Qt Kt^T (.) M) V + Qt S^T, V read as A operands like W in h2_out.
-template <int H, typename Tout>
-__device__ __forceinline__ void h2k_out(__amdgpu_buffer_rsrc_t wo, uint32_t row_bytes, const H2KeyLds& sm, int iw,
-                                        int lane, const floatx4_t (&os)[2]) {
+template <int H, typename Tout, bool REV>
+__device__ __forceinline__ void h2k_out(__amdgpu_buffer_rsrc_t wo, uint32_t row_bytes, int valid, const H2KeyLds& sm,
+                                        int iw, int lane, const floatx4_t (&os)[2]) {
   using TL = Tiles<H>;
   const int l16 = lane & 15, lg = lane >> 4;
   uint4 va[2];
@@ -994,13 +1035,17 @@ __device__ __forceinline__ void h2k_out(__amdgpu_buffer_rsrc_t wo, uint32_t row_
     }
   }
   const uint32_t lane_off = (uint32_t)l16 * row_bytes + (uint32_t)(4 * lg * (int)sizeof(Tout));
+  const H2Chunk<REV> ch(valid);
 #pragma unroll
   for (int a = 0; a < 2; ++a)
-    h2_store4<Tout>::run(wo, lane_off, 16 * TL::tt(a) * row_bytes + iw * (uint32_t)sizeof(Tout), oa[a][0], oa[a][1],
+    h2_store4<Tout>::run(wo,
+                         REV ? (uint32_t)(ch.off(16 * TL::tt(a) + l16, row_bytes) + (4 * lg + iw) * (int)sizeof(Tout))
+                             : lane_off,
+                         REV ? 0u : 16 * TL::tt(a) * row_bytes + iw * (uint32_t)sizeof(Tout), oa[a][0], oa[a][1],
                          oa[a][2], oa[a][3]);
 }
 
-template <typename Tout, bool GUARD>
+template <typename Tout, bool GUARD, bool REV>
 __global__ __launch_bounds__(kWaves * 64) void hgrn2_key_chunk_kernel(H2Params p) {
   __shared__ H2KeyLds sm;
   const int tid = threadIdx.x;
@@ -1032,10 +1077,10 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_key_chunk_kernel(H2Params p
   const int64_t nchunks = (p.L + kCh - 1) / kCh;
   H2KeyPrefetch f;
   float run[kGateTok][2];
-  h2k_fetch(p, b, hh, i0, 0, lane, gp, f);
+  h2k_fetch<REV>(p, b, hh, i0, 0, lane, gp, f);
   if (tid < 2 * (kRows + 4)) sm.nanpos[tid / (kRows + 4)][tid % (kRows + 4)] = tid % (kRows + 4) < kRows ? kCh : 0;
   __syncthreads();
-  h2k_gate1<GUARD>(sm, lane, gp, (int)min((int64_t)kCh, p.L), lb, one_m_lb, f, run, sm.nanpos[0]);
+  h2k_gate1<GUARD>(sm, lane, gp, (int)min((int64_t)kCh, p.L), REV ? 1 : 0, lb, one_m_lb, f, run, sm.nanpos[0]);
   for (int64_t c = 0; c < nchunks; ++c) {
     const int64_t t0 = c * kCh;
     const int valid = (int)min((int64_t)kCh, p.L - t0);
@@ -1046,7 +1091,7 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_key_chunk_kernel(H2Params p
       sm.nanpos[par ^ 1][lane] = kCh;  // the slot of the next chunk (last read by the previous one)
       if (lane == 0) sm.nanpos[par ^ 1][kRows] = 0;
     }
-    if (c + 1 < nchunks) h2k_fetch(p, b, hh, i0, t0 + kCh, lane, gp, f);  // in flight during this chunk
+    if (c + 1 < nchunks) h2k_fetch<REV>(p, b, hh, i0, t0 + kCh, lane, gp, f);  // in flight during this chunk
     uint4 my_hi[2], my_lo[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -1062,11 +1107,11 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_key_chunk_kernel(H2Params p
     // ---- a chunk whose decay over the chunk underflows the products' range goes token by token
     if (GUARD && !__all(sm.gcol[lane] >= kGammaFloor && sm.gcol[lane + 64] >= kGammaFloor)) {
       H2State st{{S[0], S[1], S[2], S[3]}};
-      st = h2k_chunk_tokens<Tout>(p, sm, b, hh, i0, t0, valid, tid, half_t, iw, lb, one_m_lb, st);
+      st = h2k_chunk_tokens<Tout, REV>(p, sm, b, hh, i0, t0, valid, tid, half_t, iw, lb, one_m_lb, st);
 #pragma unroll
       for (int q = 0; q < 4; ++q) S[q] = st.q[q];
       if (c + 1 < nchunks)
-        h2k_gate1<GUARD>(sm, lane, gp, (int)min((int64_t)kCh, p.L - t0 - kCh), lb, one_m_lb, f, run,
+        h2k_gate1<GUARD>(sm, lane, gp, (int)min((int64_t)kCh, p.L - t0 - kCh), 0, lb, one_m_lb, f, run,
                          sm.nanpos[par ^ 1]);
       continue;
     }
@@ -1087,12 +1132,12 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_key_chunk_kernel(H2Params p
     __syncthreads();  // Qt Kt^T tiles visible
 
     {
-      const auto wo = h2_out_window<Tout>(p, b, hh, i0, t0, valid);
+      const auto wo = h2_out_window<Tout>(p, b, hh, i0, H2Chunk<REV>(p, t0, valid).row0, valid);
       const uint32_t row_bytes = (uint32_t)(p.H * kDh * (int64_t)sizeof(Tout));
-      if (half_t == 0) h2k_out<0, Tout>(wo, row_bytes, sm, iw, lane, os);
-      else h2k_out<1, Tout>(wo, row_bytes, sm, iw, lane, os);
+      if (half_t == 0) h2k_out<0, Tout, REV>(wo, row_bytes, valid, sm, iw, lane, os);
+      else h2k_out<1, Tout, REV>(wo, row_bytes, valid, sm, iw, lane, os);
       if (!GUARD && __builtin_amdgcn_readfirstlane(sm.nanpos[par][kRows]) != 0) {
-        h2_out_nan<Tout>(wo, row_bytes, sm.nanpos[par], iw, lane, half_t);
+        h2_out_nan<Tout, REV>(wo, row_bytes, valid, sm.nanpos[par], iw, lane, half_t);
         if (sm.nanpos[par][iw + l16] < kCh) {
 #pragma unroll
           for (int q = 0; q < 4; ++q)
@@ -1129,7 +1174,7 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_key_chunk_kernel(H2Params p
     }
     // gates, part 1, of the next chunk (its inputs were loaded during this chunk)
     if (c + 1 < nchunks)
-      h2k_gate1<GUARD>(sm, lane, gp, (int)min((int64_t)kCh, p.L - t0 - kCh), lb, one_m_lb, f, run,
+      h2k_gate1<GUARD>(sm, lane, gp, (int)min((int64_t)kCh, p.L - t0 - kCh), 0, lb, one_m_lb, f, run,
                        sm.nanpos[par ^ 1]);
   }
 
@@ -1142,7 +1187,241 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_key_chunk_kernel(H2Params p
   }
 }
 
+// ----------------------------------------------------------------------------- backward, chunked form
+// The adjoint recurrences are forward scans of the same two kinds, so the backward runs the chunk kernels
+// above with their inputs exchanged (R_t = dL/dS_t, R_t = do_t q_t^T + diag(g_{t+1}) R_{t+1}):
+//   dq_t = S_t^T do_t : S_t^T = S_{t-1}^T diag(g_t) + k_t v_t^T is the key-axis recurrence with queries do,
+//                       keys v, values k and initial state S0^T (its final state is S_L^T);
+//   dv_t = R_t k_t    : backward in time, R is the row-gated recurrence with queries k, keys q, values do,
+//                       the next token's gate and initial state dS_last (its final state is R_0);
+//   dk_t = R_t^T v_t  : backward in time, R^T is the key-axis recurrence with queries v, keys do, values q
+//                       and initial state dS_last^T.
+// The gate gradient (the derivative with respect to log g_t) is the suffix sum
+//   c_t[i] = sum_{u >= t} (do_u[i] o_u[i] - v_u[i] dv_u[i]) + sum_j dS_last[i][j] S_L[i][j],
+// formed over 64-token segments (per-segment sums, a suffix over segments, then each segment from its
+// end), and dg_logit = c_t (1 - lb) sigmoid'(x_t) / g_t; the first token's is rewritten from the exact
+// g_0 sum_j R_0[i][j] S0[i][j], and dS0 = diag(g_0) R_0.
+constexpr int kGgSeg = 64;  // tokens per segment of the gate-gradient sums
+
+struct H2GradParams {
+  int64_t B, L, H, nseg;
+  float lb;
+  const void* dO;      // in dtype (bf16)
+  const float* o;      // forward output, fp32
+  const void* v;       // bf16
+  const float* dv;     // the value gradient in fp32 (the output itself, or its fp32 form before rounding)
+  void* dv_out;        // bf16 output to write from dv, or null
+  const void* g;       // gate logits, bf16
+  const float* S0;     // [B, H, d, d] or null
+  const float* dS_last;
+  const float* SLt;    // S_L^T when dS_last is given
+  const float* R0;     // [B, H, d, d]: R_0
+  float* part;         // [B * H, nseg, d]: segment sums, then the sums over the later segments
+  void* dg;            // out dtype
+  float* dS0;          // or null
+};
+
+__device__ __forceinline__ float h2_gate_of(float x, float lb) { return fmaf(1.0f - lb, sigmoid_f(x), lb); }
+// (1 - lb) sigmoid'(x) / g, 0 where sigmoid(x) is 0 (as in the chain rule through sigmoid)
+__device__ __forceinline__ float h2_gate_ratio(float x, float lb) {
+  const float s = sigmoid_f(x);
+  const float g = fmaf(1.0f - lb, s, lb);
+  return s == 0.0f ? 0.0f : (1.0f - lb) * s * (1.0f - s) / g;
+}
+
+// dst[m] = src[m]^T for 128 x 128 fp32 matrices; one workgroup per 32 x 32 tile
+__global__ __launch_bounds__(256) void h2_transpose_kernel(const float* src, float* dst) {
+  __shared__ float tile[32][33];
+  const int64_t m = blockIdx.x / 16;
+  const int ti = (int)(blockIdx.x % 16) / 4, tj = (int)(blockIdx.x % 4);
+  const float* s = src + m * kDh * kDh;
+  float* d = dst + m * kDh * kDh;
+  const int c = threadIdx.x & 31, r0 = threadIdx.x >> 5;
+#pragma unroll
+  for (int r = r0; r < 32; r += 8) tile[r][c] = s[(32 * ti + r) * kDh + 32 * tj + c];
+  __syncthreads();
+#pragma unroll
+  for (int r = r0; r < 32; r += 8) d[(32 * tj + r) * kDh + 32 * ti + c] = tile[c][r];
+}
+
+// per (batch, head, segment) and value row: sum over the segment's tokens of do o - v dv
+__global__ __launch_bounds__(kDh) void h2_gate_part_kernel(H2GradParams p) {
+  const int64_t blk = blockIdx.x, bh = blk / p.nseg, seg = blk - bh * p.nseg;
+  const int64_t b = bh / p.H, hh = bh - b * p.H;
+  const int i = threadIdx.x;
+  const int64_t t0 = seg * kGgSeg, t1 = min(t0 + kGgSeg, p.L);
+  float acc = 0.0f;
+#pragma unroll 8
+  for (int64_t t = t0; t < t1; ++t) {
+    const int64_t e = ((b * p.L + t) * p.H + hh) * kDh + i;
+    acc += io<bf16_t>::load(p.dO, e) * p.o[e] - io<bf16_t>::load(p.v, e) * p.dv[e];
+  }
+  p.part[blk * kDh + i] = acc;
+}
+
+// per (batch, head) and value row: the constant term sum_j dS_last[i][j] S_L[i][j], then the sum over the
+// later segments for every segment (in place)
+__global__ __launch_bounds__(kDh) void h2_gate_suffix_kernel(H2GradParams p) {
+  const int64_t bh = blockIdx.x;
+  const int i = threadIdx.x;
+  float run = 0.0f;
+  if (p.dS_last) {
+    const float* dl = p.dS_last + (bh * kDh + i) * kDh;
+    const float* sl = p.SLt + bh * kDh * kDh + i;  // S_L[i][j] = S_L^T[j][i]
+#pragma unroll 8
+    for (int j = 0; j < kDh; ++j) run = fmaf(dl[j], sl[j * kDh], run);
+  }
+  float* pr = p.part + bh * p.nseg * kDh + i;
+  for (int64_t sg = p.nseg - 1; sg >= 0; --sg) {
+    const float own = pr[sg * kDh];
+    pr[sg * kDh] = run;
+    run += own;
+  }
+}
+
+// per (batch, head, segment) and value row: c_t from the segment's end down, dg_logit_t = c_t * ratio; with
+// bf16 outputs it also writes the rounded value gradient (the sums use its fp32 form: the terms cancel)
+template <typename Tg>
+__global__ __launch_bounds__(kDh) void h2_gate_grad_kernel(H2GradParams p) {
+  const int64_t blk = blockIdx.x, bh = blk / p.nseg, seg = blk - bh * p.nseg;
+  const int64_t b = bh / p.H, hh = bh - b * p.H;
+  const int i = threadIdx.x;
+  const int64_t t0 = seg * kGgSeg, t1 = min(t0 + kGgSeg, p.L);
+  float c = p.part[blk * kDh + i];
+#pragma unroll 8
+  for (int64_t t = t1 - 1; t >= t0; --t) {
+    const int64_t e = ((b * p.L + t) * p.H + hh) * kDh + i;
+    const float dv = p.dv[e];
+    c += io<bf16_t>::load(p.dO, e) * p.o[e] - io<bf16_t>::load(p.v, e) * dv;
+    io<Tg>::store(p.dg, e, c * h2_gate_ratio(io<bf16_t>::load(p.g, e), p.lb));
+    if (p.dv_out) io<bf16_t>::store(p.dv_out, e, dv);
+  }
+}
+
+// per (batch, head) and value row: dS0 = g_0 R_0 (row scaling) and the first token's gate gradient from
+// g_0 sum_j R_0[i][j] S0[i][j] (0 without an initial state)
+template <typename Tg>
+__global__ __launch_bounds__(kDh) void h2_gate_first_kernel(H2GradParams p) {
+  const int64_t bh = blockIdx.x, b = bh / p.H, hh = bh - b * p.H;
+  const int i = threadIdx.x;
+  const int64_t e0 = (b * p.L * p.H + hh) * kDh + i;  // token 0
+  const float x0 = io<bf16_t>::load(p.g, e0), g0 = h2_gate_of(x0, p.lb);
+  const float* r = p.R0 + (bh * kDh + i) * kDh;
+  float rs = 0.0f;
+  if (p.S0) {
+    const float* s0 = p.S0 + (bh * kDh + i) * kDh;
+#pragma unroll 8
+    for (int j = 0; j < kDh; ++j) rs = fmaf(r[j], s0[j], rs);
+  }
+  io<Tg>::store(p.dg, e0, g0 * rs * h2_gate_ratio(x0, p.lb));
+  if (p.dS0) {
+    float* d = p.dS0 + (bh * kDh + i) * kDh;
+#pragma unroll 8
+    for (int j = 0; j < kDh; ++j) d[j] = g0 * r[j];
+  }
+}
+
+template <bool REV>
+void h2_launch_row(const H2Params& p, bool out_bf16, bool guard, hipStream_t s) {
+  const dim3 grid((unsigned)(p.B * p.H * 2)), blk(kWaves * 64);
+  if (out_bf16) {
+    if (guard) hipLaunchKernelGGL((hgrn2_chunk_kernel<bf16_t, true, REV>), grid, blk, 0, s, p);
+    else hipLaunchKernelGGL((hgrn2_chunk_kernel<bf16_t, false, REV>), grid, blk, 0, s, p);
+  } else {
+    if (guard) hipLaunchKernelGGL((hgrn2_chunk_kernel<float, true, REV>), grid, blk, 0, s, p);
+    else hipLaunchKernelGGL((hgrn2_chunk_kernel<float, false, REV>), grid, blk, 0, s, p);
+  }
+}
+template <bool REV>
+void h2_launch_key(const H2Params& p, bool out_bf16, bool guard, hipStream_t s) {
+  const dim3 grid((unsigned)(p.B * p.H * 2)), blk(kWaves * 64);
+  if (out_bf16) {
+    if (guard) hipLaunchKernelGGL((hgrn2_key_chunk_kernel<bf16_t, true, REV>), grid, blk, 0, s, p);
+    else hipLaunchKernelGGL((hgrn2_key_chunk_kernel<bf16_t, false, REV>), grid, blk, 0, s, p);
+  } else {
+    if (guard) hipLaunchKernelGGL((hgrn2_key_chunk_kernel<float, true, REV>), grid, blk, 0, s, p);
+    else hipLaunchKernelGGL((hgrn2_key_chunk_kernel<float, false, REV>), grid, blk, 0, s, p);
+  }
+}
+
+// Scratch of the chunked backward: [R_0][S0^T][dS_last^T][S_L^T][segment sums][dv in fp32 (used with bf16
+// outputs)][recomputed o], 256-byte aligned.
+struct H2BwdLayout {
+  size_t mat, part, act, outs;
+  explicit H2BwdLayout(const Hgrn2BwdArgs& a) {
+    mat = ((size_t)(a.B * a.H * a.d * a.d) * 4 + 255) / 256 * 256;
+    part = ((size_t)(a.B * a.H * ((a.L + kGgSeg - 1) / kGgSeg) * a.d) * 4 + 255) / 256 * 256;
+    act = ((size_t)(a.B * a.L * a.H * a.d) * 4 + 255) / 256 * 256;
+    outs = a.o ? 0 : act;
+  }
+};
 }  // namespace
+
+bool hgrn2_backward_chunked(const Hgrn2BwdArgs& a) { return a.in_bf16 && a.d == kDh && a.H < 65536; }
+
+size_t hgrn2_backward_chunked_scratch_bytes(const Hgrn2BwdArgs& a) {
+  const H2BwdLayout lay(a);
+  return workspace_head_bytes() + 4 * lay.mat + lay.part + lay.act + lay.outs;
+}
+
+hipError_t launch_hgrn2_backward_chunked(const Hgrn2BwdArgs& a, hipStream_t s) {
+  const H2BwdLayout lay(a);
+  char* ws = static_cast<char*>(a.scratch) + workspace_head_bytes();
+  float* R0 = reinterpret_cast<float*>(ws);
+  float* S0t = reinterpret_cast<float*>(ws + lay.mat);
+  float* dSlt = reinterpret_cast<float*>(ws + 2 * lay.mat);
+  float* SLt = reinterpret_cast<float*>(ws + 3 * lay.mat);
+  float* part = reinterpret_cast<float*>(ws + 4 * lay.mat);
+  const float* o = a.o;
+  if (!o) {  // the forward output in fp32
+    float* o_tmp = reinterpret_cast<float*>(ws + 4 * lay.mat + lay.part + lay.act);
+    Hgrn2ScanArgs f{a.B, a.L, a.H, a.d, 1, 0, a.q, a.k, a.v, a.g_logit, a.lower_bound, a.S0, o_tmp, nullptr};
+    const hipError_t e = launch_hgrn2_scan(f, s);
+    if (e != hipSuccess) return e;
+    o = o_tmp;
+  }
+  const unsigned nmat = (unsigned)(a.B * a.H);
+  if (a.S0) hipLaunchKernelGGL(h2_transpose_kernel, dim3(nmat * 16), dim3(256), 0, s, a.S0, S0t);
+  if (a.dS_last) hipLaunchKernelGGL(h2_transpose_kernel, dim3(nmat * 16), dim3(256), 0, s, a.dS_last, dSlt);
+  const bool guard = !(a.lower_bound >= 0.35355339f);  // lower_bound^64 >= 2^-96 otherwise
+  const bool ob = a.out_bf16 != 0;
+  H2Params p;
+  p.B = a.B; p.L = a.L; p.H = a.H; p.d = a.d; p.lb = a.lower_bound;
+  // dq: key-axis form on (do, v, k) from S0^T; its final state S_L^T
+  p.q = a.dO; p.k = a.v; p.v = a.k; p.g = a.g_logit;
+  p.S0 = a.S0 ? S0t : nullptr; p.o = a.dq; p.S_last = a.dS_last ? SLt : nullptr;
+  h2_launch_key<false>(p, ob, guard, s);
+  // dv (in fp32: the gate gradient's sums cancel) : row-gated form backward in time on (k, q, do) from
+  // dS_last; its final state R_0
+  float* dv32 = ob ? reinterpret_cast<float*>(ws + 4 * lay.mat + lay.part) : static_cast<float*>(a.dv);
+  p.q = a.k; p.k = a.q; p.v = a.dO;
+  p.S0 = a.dS_last; p.o = dv32; p.S_last = R0;
+  h2_launch_row<true>(p, false, guard, s);
+  // dk: key-axis form backward in time on (v, do, q) from dS_last^T
+  p.q = a.v; p.k = a.dO; p.v = a.q;
+  p.S0 = a.dS_last ? dSlt : nullptr; p.o = a.dk; p.S_last = nullptr;
+  h2_launch_key<true>(p, ob, guard, s);
+  // gate gradient and dS0
+  H2GradParams gp;
+  gp.B = a.B; gp.L = a.L; gp.H = a.H; gp.nseg = (a.L + kGgSeg - 1) / kGgSeg; gp.lb = a.lower_bound;
+  gp.dO = a.dO; gp.o = o; gp.v = a.v; gp.dv = dv32; gp.dv_out = ob ? a.dv : nullptr; gp.g = a.g_logit;
+  gp.S0 = a.S0; gp.dS_last = a.dS_last; gp.SLt = SLt; gp.R0 = R0; gp.part = part; gp.dg = a.dg_logit;
+  gp.dS0 = a.dS0;
+  const unsigned nseg_blocks = (unsigned)(a.B * a.H * gp.nseg);
+  if (ob) {
+    hipLaunchKernelGGL(h2_gate_part_kernel, dim3(nseg_blocks), dim3(kDh), 0, s, gp);
+    hipLaunchKernelGGL(h2_gate_suffix_kernel, dim3(nmat), dim3(kDh), 0, s, gp);
+    hipLaunchKernelGGL(h2_gate_grad_kernel<bf16_t>, dim3(nseg_blocks), dim3(kDh), 0, s, gp);
+    hipLaunchKernelGGL(h2_gate_first_kernel<bf16_t>, dim3(nmat), dim3(kDh), 0, s, gp);
+  } else {
+    hipLaunchKernelGGL(h2_gate_part_kernel, dim3(nseg_blocks), dim3(kDh), 0, s, gp);
+    hipLaunchKernelGGL(h2_gate_suffix_kernel, dim3(nmat), dim3(kDh), 0, s, gp);
+    hipLaunchKernelGGL(h2_gate_grad_kernel<float>, dim3(nseg_blocks), dim3(kDh), 0, s, gp);
+    hipLaunchKernelGGL(h2_gate_first_kernel<float>, dim3(nmat), dim3(kDh), 0, s, gp);
+  }
+  return hipGetLastError();
+}
+
 
 hipError_t launch_hgrn2_key_chunk(const Hgrn2ScanArgs& a, hipStream_t s) {
   H2Params p;
@@ -1152,11 +1431,11 @@ hipError_t launch_hgrn2_key_chunk(const Hgrn2ScanArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.B * a.H * 2));
   const bool guard = !(a.lower_bound >= 0.35355339f);  // lower_bound^64 >= 2^-96 otherwise
   if (a.out_bf16) {
-    if (guard) hipLaunchKernelGGL((hgrn2_key_chunk_kernel<bf16_t, true>), grid, dim3(kWaves * 64), 0, s, p);
-    else hipLaunchKernelGGL((hgrn2_key_chunk_kernel<bf16_t, false>), grid, dim3(kWaves * 64), 0, s, p);
+    if (guard) hipLaunchKernelGGL((hgrn2_key_chunk_kernel<bf16_t, true, false>), grid, dim3(kWaves * 64), 0, s, p);
+    else hipLaunchKernelGGL((hgrn2_key_chunk_kernel<bf16_t, false, false>), grid, dim3(kWaves * 64), 0, s, p);
   } else {
-    if (guard) hipLaunchKernelGGL((hgrn2_key_chunk_kernel<float, true>), grid, dim3(kWaves * 64), 0, s, p);
-    else hipLaunchKernelGGL((hgrn2_key_chunk_kernel<float, false>), grid, dim3(kWaves * 64), 0, s, p);
+    if (guard) hipLaunchKernelGGL((hgrn2_key_chunk_kernel<float, true, false>), grid, dim3(kWaves * 64), 0, s, p);
+    else hipLaunchKernelGGL((hgrn2_key_chunk_kernel<float, false, false>), grid, dim3(kWaves * 64), 0, s, p);
   }
   return hipGetLastError();
 }
@@ -1173,11 +1452,11 @@ hipError_t launch_hgrn2_scan(const Hgrn2ScanArgs& a, hipStream_t s) {
     const dim3 grid((unsigned)(a.B * a.H * 2));
     const bool guard = !(a.lower_bound >= 0.35355339f);  // lower_bound^64 >= 2^-96 otherwise
     if (a.out_bf16) {
-      if (guard) hipLaunchKernelGGL((hgrn2_chunk_kernel<bf16_t, true>), grid, dim3(kWaves * 64), 0, s, p);
-      else hipLaunchKernelGGL((hgrn2_chunk_kernel<bf16_t, false>), grid, dim3(kWaves * 64), 0, s, p);
+      if (guard) hipLaunchKernelGGL((hgrn2_chunk_kernel<bf16_t, true, false>), grid, dim3(kWaves * 64), 0, s, p);
+      else hipLaunchKernelGGL((hgrn2_chunk_kernel<bf16_t, false, false>), grid, dim3(kWaves * 64), 0, s, p);
     } else {
-      if (guard) hipLaunchKernelGGL((hgrn2_chunk_kernel<float, true>), grid, dim3(kWaves * 64), 0, s, p);
-      else hipLaunchKernelGGL((hgrn2_chunk_kernel<float, false>), grid, dim3(kWaves * 64), 0, s, p);
+      if (guard) hipLaunchKernelGGL((hgrn2_chunk_kernel<float, true, false>), grid, dim3(kWaves * 64), 0, s, p);
+      else hipLaunchKernelGGL((hgrn2_chunk_kernel<float, false, false>), grid, dim3(kWaves * 64), 0, s, p);
     }
     return hipGetLastError();
   }

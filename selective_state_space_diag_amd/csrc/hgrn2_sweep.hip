@@ -592,6 +592,7 @@ struct BwdLayout {
 }  // namespace
 
 size_t hgrn2_scan_backward_scratch_bytes(const Hgrn2BwdArgs& a) {
+  if (hgrn2_backward_chunked(a)) return hgrn2_backward_chunked_scratch_bytes(a);
   const BwdLayout lay(a);
   return workspace_head_bytes() + lay.state + lay.ckpt + lay.outs;
 }
@@ -629,6 +630,7 @@ hipError_t launch_hgrn2_key_scan(const Hgrn2ScanArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_hgrn2_scan_backward(const Hgrn2BwdArgs& a, hipStream_t s) {
+  if (hgrn2_backward_chunked(a)) return launch_hgrn2_backward_chunked(a, s);
   char* scratch = static_cast<char*>(a.scratch) + workspace_head_bytes();
   const BwdLayout lay(a);
   float* S_L = reinterpret_cast<float*>(scratch);

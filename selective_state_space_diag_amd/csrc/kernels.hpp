@@ -272,6 +272,11 @@ struct Hgrn2BwdArgs {
 };
 size_t hgrn2_scan_backward_scratch_bytes(const Hgrn2BwdArgs& a);
 hipError_t launch_hgrn2_scan_backward(const Hgrn2BwdArgs& a, hipStream_t s);
+// The backward in chunked MFMA form (bf16 inputs, d = 128, H < 2^16): the cases it takes, its scratch,
+// and its launch (launch_hgrn2_scan_backward dispatches to it).
+bool hgrn2_backward_chunked(const Hgrn2BwdArgs& a);
+size_t hgrn2_backward_chunked_scratch_bytes(const Hgrn2BwdArgs& a);
+hipError_t launch_hgrn2_backward_chunked(const Hgrn2BwdArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------------ utilities
 // dst[i] = src ? src[i] : 0 for i < n (used for empty problems: final state = initial state).
