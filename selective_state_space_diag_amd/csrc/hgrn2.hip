@@ -23,6 +23,13 @@ struct H2Params {
   const float* S0;
   void* o;
   float* S_last;
+  // The backward's dv pass with the gate gradient folded in (see hgrn2_chunk_kernel, TG): the forward
+  // output (fp32), the forward's values (bf16), the gate gradient's initial suffix sum per value row (or
+  // null for 0) and dg_logit.
+  const float* gg_o = nullptr;
+  const void* gg_v = nullptr;
+  const float* gg_c0 = nullptr;
+  void* gg_dg = nullptr;
 };
 
 // Decode step: one wave per value row; o_i reduced across the wave.  KEY: the gate scales the key
@@ -381,7 +388,7 @@ template <> struct h2_store4<bf16_t> {
 
 template <int H, typename Tout, bool REV>
 __device__ __forceinline__ void h2_out(__amdgpu_buffer_rsrc_t wo, uint32_t row_bytes, int valid, H2Lds& sm, int iw,
-                                       int lane, const floatx4_t (&os)[2]) {
+                                       int lane, const floatx4_t (&os)[2], float (&ov)[2][4]) {
   using TL = Tiles<H>;
   const int l16 = lane & 15, lg = lane >> 4;
   // W as A operands: slots s = 32 ks + 16 h' + 4 lg + r; lane 4b + c of a group points at
@@ -428,10 +435,13 @@ __device__ __forceinline__ void h2_out(__amdgpu_buffer_rsrc_t wo, uint32_t row_b
   for (int a = 0; a < 2; ++a) {
     const int t = 16 * TL::tt(a) + l16;
     const float4 gm = *reinterpret_cast<const float4*>(&sm.gam[t][iw + 4 * lg]);
+    ov[a][0] = gm.x * fmaf(oa[a][0], igc[0], os[a][0]);
+    ov[a][1] = gm.y * fmaf(oa[a][1], igc[1], os[a][1]);
+    ov[a][2] = gm.z * fmaf(oa[a][2], igc[2], os[a][2]);
+    ov[a][3] = gm.w * fmaf(oa[a][3], igc[3], os[a][3]);
     h2_store4<Tout>::run(wo, REV ? (uint32_t)(ch.off(t, row_bytes) + (4 * lg + iw) * (int)sizeof(Tout)) : lane_off,
-                         REV ? 0u : 16 * TL::tt(a) * row_bytes + iw * (uint32_t)sizeof(Tout),
-                         gm.x * fmaf(oa[a][0], igc[0], os[a][0]), gm.y * fmaf(oa[a][1], igc[1], os[a][1]),
-                         gm.z * fmaf(oa[a][2], igc[2], os[a][2]), gm.w * fmaf(oa[a][3], igc[3], os[a][3]));
+                         REV ? 0u : 16 * TL::tt(a) * row_bytes + iw * (uint32_t)sizeof(Tout), ov[a][0], ov[a][1],
+                         ov[a][2], ov[a][3]);
   }
 }
 
@@ -526,8 +536,133 @@ __device__ __forceinline__ void h2_out_nan(__amdgpu_buffer_rsrc_t wo, uint32_t r
 // GUARD: the Gamma_C check and the token-by-token path are compiled in.  Lower bounds >= 2^-1.5 cannot
 // fail the check (Gamma_C >= lower_bound^64 >= 2^-96) and take the instantiation without them, whose
 // main loop keeps its registers to itself.
-template <typename Tout, bool GUARD, bool REV>
+__device__ __forceinline__ float h2_gate_of(float x, float lb) { return fmaf(1.0f - lb, sigmoid_f(x), lb); }
+// (1 - lb) sigmoid'(x) / g, 0 where sigmoid(x) is 0 (as in the chain rule through sigmoid)
+__device__ __forceinline__ float h2_gate_ratio(float x, float lb) {
+  const float s = sigmoid_f(x);
+  const float g = fmaf(1.0f - lb, s, lb);
+  return s == 0.0f ? 0.0f : (1.0f - lb) * s * (1.0f - s) / g;
+}
+
+// ---- the gate gradient folded into the backward's dv pass (hgrn2_chunk_kernel with TG)
+struct H2GGWave {
+  float4 o[2];   // forward output at the wave's output elements (position 16 tt + l16, rows iw + 4 lg .. +3)
+  u32x2_t v[2];  // the forward's values there (4 bf16)
+  u32x2_t d[2];  // this pass's values there (do, 4 bf16)
+};
+struct H2GGLane {
+  uint32_t x[kGateTok];  // gate logit (bf16, low half) of the lane's row at positions 8 gp + u
+};
+
+// Issued right after the chunk's outputs, consumed after the state update.
+__device__ __forceinline__ void h2_gg_load(const H2Params& p, int64_t b, int64_t hh, int i0, int64_t t0, int valid,
+                                           int iw, int lane, int half_t, int gp, H2GGWave& w, H2GGLane& l) {
+  const H2Chunk<true> ch(p, t0, valid);
+  const int l16 = lane & 15, lg = lane >> 4;
+  const uint32_t rb2 = (uint32_t)(p.H * kDh * 2), rb4 = 2 * rb2;
+  const char* obase = reinterpret_cast<const char*>(p.gg_o) + (((b * p.L + ch.row0) * p.H + hh) * kDh) * 4;
+  const auto wo = make_window(obase, (uint32_t)((int64_t)(valid - 1) * p.H * kDh * 4 + kDh * 4));
+  const auto wv = h2_window(p, p.gg_v, b, hh, ch.row0, valid), wd = h2_window(p, p.v, b, hh, ch.row0, valid);
+  const auto wx = h2_window(p, p.g, b, hh, ch.row0, valid);  // the token's own gate (this pass reads the next one)
+  const int col = i0 + iw + 4 * lg;
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int t = 16 * (half_t ? (a ? 2 : 1) : (a ? 3 : 0)) + l16;
+    const v4i_t o4 = __builtin_amdgcn_raw_buffer_load_b128(wo, ch.off(t, rb4) + col * 4, 0, 0);
+    w.o[a] = make_float4(__int_as_float(o4.x), __int_as_float(o4.y), __int_as_float(o4.z), __int_as_float(o4.w));
+    w.v[a] = __builtin_amdgcn_raw_buffer_load_b64(wv, ch.off(t, rb2) + col * 2, 0, 0);
+    w.d[a] = __builtin_amdgcn_raw_buffer_load_b64(wd, ch.off(t, rb2) + col * 2, 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < kGateTok; ++u)
+    l.x[u] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wx, ch.off(gp * kGateTok + u, rb2) + (i0 + lane) * 2, 0, 0);
+}
+
+// The chunk's terms e = do o - v dv at the wave's output elements go to LDS ([row][position], 4-position
+// groups XOR-swizzled by the row, in the W tiles' space); thread (row lane, positions 8 gp .. 8 gp + 7)
+// takes a running sum over its positions, the groups' totals meet in LDS (gam's space), and it stores
+// dg_logit for its positions from the running sum carried over the earlier chunks.  Called by every
+// thread after the chunk's state update; no LDS it touches is read again before the next chunk's gate
+// step, which follows that chunk's first barrier.
+template <typename TG>
+__device__ __forceinline__ void h2_gg_step(const H2Params& p, H2Lds& sm, int64_t b, int64_t hh, int i0, int64_t t0,
+                                           int valid, int iw, int lane, int half_t, int gp, float lb,
+                                           const float (&ov)[2][4], const H2GGWave& w, const H2GGLane& l,
+                                           float& carry) {
+  const int l16 = lane & 15, lg = lane >> 4;
+  float ev[2][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    ev[a][0] = bf16_lo(w.d[a].x) * w.o[a].x - bf16_lo(w.v[a].x) * ov[a][0];
+    ev[a][1] = bf16_hi(w.d[a].x) * w.o[a].y - bf16_hi(w.v[a].x) * ov[a][1];
+    ev[a][2] = bf16_lo(w.d[a].y) * w.o[a].z - bf16_lo(w.v[a].y) * ov[a][2];
+    ev[a][3] = bf16_hi(w.d[a].y) * w.o[a].w - bf16_hi(w.v[a].y) * ov[a][3];
+  }
+  float* eT = reinterpret_cast<float*>(&sm.w[0]);  // w and w_lo: 64 x 64 fp32
+  static_assert(sizeof(sm.w) + sizeof(sm.w_lo) == sizeof(float) * kRows * kCh, "the terms fill W's tiles");
+  __syncthreads();  // every wave is past its products: W's tiles and gam are free
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int t = 16 * (half_t ? (a ? 2 : 1) : (a ? 3 : 0)) + l16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = iw + 4 * lg + r;
+      eT[i * kCh + ((((t >> 2) ^ (i & 15))) << 2) + (t & 3)] = ev[a][r];
+    }
+  }
+  __syncthreads();
+  const int gi = lane;
+  const float4 e0 = *reinterpret_cast<const float4*>(&eT[gi * kCh + (((2 * gp) ^ (gi & 15)) << 2)]);
+  const float4 e1 = *reinterpret_cast<const float4*>(&eT[gi * kCh + (((2 * gp + 1) ^ (gi & 15)) << 2)]);
+  float pre[kGateTok];
+  pre[0] = e0.x;
+  pre[1] = pre[0] + e0.y;
+  pre[2] = pre[1] + e0.z;
+  pre[3] = pre[2] + e0.w;
+  pre[4] = pre[3] + e1.x;
+  pre[5] = pre[4] + e1.y;
+  pre[6] = pre[5] + e1.z;
+  pre[7] = pre[6] + e1.w;
+  float* tot = &sm.gam[0][0];  // [group][row]
+  tot[gp * kRows + gi] = pre[kGateTok - 1];
+  __syncthreads();
+  float before = 0.0f, all = 0.0f;
+#pragma unroll
+  for (int g2 = 0; g2 < kGateParts; ++g2) {
+    const float tg = tot[g2 * kRows + gi];
+    before += g2 < gp ? tg : 0.0f;
+    all += tg;
+  }
+  const float base = carry + before;
+  carry += all;
+  const H2Chunk<true> ch(p, t0, valid);
+  constexpr int es = sizeof(TG);
+  const uint32_t rb = (uint32_t)(p.H * kDh * es);
+  char* dbase = static_cast<char*>(p.gg_dg) + (((b * p.L + ch.row0) * p.H + hh) * kDh) * es;
+  const auto wg = make_window(dbase, (uint32_t)((int64_t)(valid - 1) * p.H * kDh * es + kDh * es));
+#pragma unroll
+  for (int u = 0; u < kGateTok; ++u) {
+    const int pos = gp * kGateTok + u;
+    if (pos < valid) {
+      const float dg = (base + pre[u]) * h2_gate_ratio(bf16_lo(l.x[u]), lb);
+      win<TG, 1>::store(wg, (uint32_t)((i0 + gi) * es), (uint32_t)ch.off(pos, rb), &dg);
+    }
+  }
+}
+
+template <typename T> struct IsVoid { static constexpr bool value = false; };
+template <> struct IsVoid<void> { static constexpr bool value = true; };
+
+// TG (not void; REV without GUARD): the backward's dv pass, which also forms the gate gradient.  Running
+// backward in time it meets the tokens in the order of the suffix sum
+// c_t[i] = sum_{u >= t} (do_u[i] o_u[i] - v_u[i] dv_u[i]) + c0[i], so after each chunk's products it
+// forms the chunk's terms at its output elements (do is this pass's values, o and v are loaded), sums
+// them per value row over the chunk's positions (LDS, two exchanges), carries the running sum to the next
+// chunk, and stores dg_logit_t = c_t (1 - lb) sigmoid'(x_t) / g_t (type TG).
+template <typename Tout, bool GUARD, bool REV, typename TG = void>
 __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
+  constexpr bool GG = !IsVoid<TG>::value;
+  static_assert(!GG || (REV && !GUARD), "the gate gradient is folded into the unguarded backward dv pass");
   __shared__ H2Lds sm;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -572,6 +707,7 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
   __syncthreads();
   h2_gate1<GUARD>(sm, tid & 63, wave, (int)min((int64_t)kCh, p.L), REV ? 1 : 0, lb, one_m_lb, gam_run, vv,
                   sm.nanpos[0]);
+  float carry = (GG && p.gg_c0) ? p.gg_c0[bh * kDh + i0 + (tid & 63)] : 0.0f;  // running suffix sum (GG)
   for (int64_t c = 0; c < nchunks; ++c) {
     // Per-lane LDS addresses are loop-invariant and stay in registers across chunks: the LDS use
     // already limits the kernel to two waves per SIMD, so the registers they take are free.
@@ -675,11 +811,15 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
     }
 
     // ---- O^T for this half's token tiles
+    float ov[2][4];
+    H2GGWave gw;  // GG: forward output, values and this pass's values at the wave's output elements
+    H2GGLane gl;  // GG: gate logits of the lane's value row at its 8 positions
     {
       const auto wo = h2_out_window<Tout>(p, b, hh, i0, H2Chunk<REV>(p, t0, valid).row0, valid);
       const uint32_t row_bytes = (uint32_t)(p.H * kDh * (int64_t)sizeof(Tout));
-      if (half_t == 0) h2_out<0, Tout, REV>(wo, row_bytes, valid, sm, iw, lane, os);
-      else h2_out<1, Tout, REV>(wo, row_bytes, valid, sm, iw, lane, os);
+      if (half_t == 0) h2_out<0, Tout, REV>(wo, row_bytes, valid, sm, iw, lane, os, ov);
+      else h2_out<1, Tout, REV>(wo, row_bytes, valid, sm, iw, lane, os, ov);
+      if constexpr (GG) h2_gg_load(p, b, hh, i0, t0, valid, iw, lane, half_t, gp, gw, gl);
       // a non-finite gate or value: its row reads NaN from that token on (this wave's outputs again), and
       // so does its state (NaN stays NaN through the state update below)
       if (!GUARD && __builtin_amdgcn_readfirstlane(sm.nanpos[c & 1][kRows]) != 0) {
@@ -721,6 +861,7 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
     if (c + 1 < nchunks)
       h2_gate1<GUARD>(sm, lane, gp, (int)min((int64_t)kCh, p.L - t0 - kCh), 0, lb, one_m_lb, gam_run, vv,
                       sm.nanpos[(c + 1) & 1]);
+    if constexpr (GG) h2_gg_step<TG>(p, sm, b, hh, i0, t0, valid, iw, lane, half_t, gp, lb, ov, gw, gl, carry);
   }
 
   if (p.S_last) {
@@ -1221,13 +1362,6 @@ struct H2GradParams {
   float* dS0;          // or null
 };
 
-__device__ __forceinline__ float h2_gate_of(float x, float lb) { return fmaf(1.0f - lb, sigmoid_f(x), lb); }
-// (1 - lb) sigmoid'(x) / g, 0 where sigmoid(x) is 0 (as in the chain rule through sigmoid)
-__device__ __forceinline__ float h2_gate_ratio(float x, float lb) {
-  const float s = sigmoid_f(x);
-  const float g = fmaf(1.0f - lb, s, lb);
-  return s == 0.0f ? 0.0f : (1.0f - lb) * s * (1.0f - s) / g;
-}
 
 // dst[m] = src[m]^T for 128 x 128 fp32 matrices; one workgroup per 32 x 32 tile
 __global__ __launch_bounds__(256) void h2_transpose_kernel(const float* src, float* dst) {
@@ -1257,6 +1391,18 @@ __global__ __launch_bounds__(kDh) void h2_gate_part_kernel(H2GradParams p) {
     acc += io<bf16_t>::load(p.dO, e) * p.o[e] - io<bf16_t>::load(p.v, e) * p.dv[e];
   }
   p.part[blk * kDh + i] = acc;
+}
+
+// per (batch, head) and value row: the constant term sum_j dS_last[i][j] S_L[i][j] (S_L^T given)
+__global__ __launch_bounds__(kDh) void h2_gate_c0_kernel(const float* dS_last, const float* SLt, float* c0) {
+  const int64_t bh = blockIdx.x;
+  const int i = threadIdx.x;
+  const float* dl = dS_last + (bh * kDh + i) * kDh;
+  const float* sl = SLt + bh * kDh * kDh + i;
+  float run = 0.0f;
+#pragma unroll 8
+  for (int j = 0; j < kDh; ++j) run = fmaf(dl[j], sl[j * kDh], run);
+  c0[bh * kDh + i] = run;
 }
 
 // per (batch, head) and value row: the constant term sum_j dS_last[i][j] S_L[i][j], then the sum over the
@@ -1391,12 +1537,24 @@ hipError_t launch_hgrn2_backward_chunked(const Hgrn2BwdArgs& a, hipStream_t s) {
   p.q = a.dO; p.k = a.v; p.v = a.k; p.g = a.g_logit;
   p.S0 = a.S0 ? S0t : nullptr; p.o = a.dq; p.S_last = a.dS_last ? SLt : nullptr;
   h2_launch_key<false>(p, ob, guard, s);
-  // dv (in fp32: the gate gradient's sums cancel) : row-gated form backward in time on (k, q, do) from
-  // dS_last; its final state R_0
+  // dv: row-gated form backward in time on (k, q, do) from dS_last; its final state R_0.  Without the
+  // decay check this pass also forms the gate gradient (it meets the tokens in the suffix sum's order);
+  // with it, dv is kept in fp32 (the sums cancel) for the segment kernels below
   float* dv32 = ob ? reinterpret_cast<float*>(ws + 4 * lay.mat + lay.part) : static_cast<float*>(a.dv);
   p.q = a.k; p.k = a.q; p.v = a.dO;
-  p.S0 = a.dS_last; p.o = dv32; p.S_last = R0;
-  h2_launch_row<true>(p, false, guard, s);
+  p.S0 = a.dS_last; p.S_last = R0;
+  if (!guard) {
+    if (a.dS_last) hipLaunchKernelGGL(h2_gate_c0_kernel, dim3(nmat), dim3(kDh), 0, s, a.dS_last, SLt, part);
+    p.o = a.dv;
+    p.gg_o = o; p.gg_v = a.v; p.gg_c0 = a.dS_last ? part : nullptr; p.gg_dg = a.dg_logit;
+    const dim3 grid((unsigned)(a.B * a.H * 2)), blk(kWaves * 64);
+    if (ob) hipLaunchKernelGGL((hgrn2_chunk_kernel<bf16_t, false, true, bf16_t>), grid, blk, 0, s, p);
+    else hipLaunchKernelGGL((hgrn2_chunk_kernel<float, false, true, float>), grid, blk, 0, s, p);
+    p.gg_o = nullptr; p.gg_v = nullptr; p.gg_c0 = nullptr; p.gg_dg = nullptr;
+  } else {
+    p.o = dv32;
+    h2_launch_row<true>(p, false, guard, s);
+  }
   // dk: key-axis form backward in time on (v, do, q) from dS_last^T
   p.q = a.v; p.k = a.dO; p.v = a.q;
   p.S0 = a.dS_last ? dSlt : nullptr; p.o = a.dk; p.S_last = nullptr;
@@ -1408,17 +1566,14 @@ hipError_t launch_hgrn2_backward_chunked(const Hgrn2BwdArgs& a, hipStream_t s) {
   gp.S0 = a.S0; gp.dS_last = a.dS_last; gp.SLt = SLt; gp.R0 = R0; gp.part = part; gp.dg = a.dg_logit;
   gp.dS0 = a.dS0;
   const unsigned nseg_blocks = (unsigned)(a.B * a.H * gp.nseg);
-  if (ob) {
+  if (guard) {
     hipLaunchKernelGGL(h2_gate_part_kernel, dim3(nseg_blocks), dim3(kDh), 0, s, gp);
     hipLaunchKernelGGL(h2_gate_suffix_kernel, dim3(nmat), dim3(kDh), 0, s, gp);
-    hipLaunchKernelGGL(h2_gate_grad_kernel<bf16_t>, dim3(nseg_blocks), dim3(kDh), 0, s, gp);
-    hipLaunchKernelGGL(h2_gate_first_kernel<bf16_t>, dim3(nmat), dim3(kDh), 0, s, gp);
-  } else {
-    hipLaunchKernelGGL(h2_gate_part_kernel, dim3(nseg_blocks), dim3(kDh), 0, s, gp);
-    hipLaunchKernelGGL(h2_gate_suffix_kernel, dim3(nmat), dim3(kDh), 0, s, gp);
-    hipLaunchKernelGGL(h2_gate_grad_kernel<float>, dim3(nseg_blocks), dim3(kDh), 0, s, gp);
-    hipLaunchKernelGGL(h2_gate_first_kernel<float>, dim3(nmat), dim3(kDh), 0, s, gp);
+    if (ob) hipLaunchKernelGGL(h2_gate_grad_kernel<bf16_t>, dim3(nseg_blocks), dim3(kDh), 0, s, gp);
+    else hipLaunchKernelGGL(h2_gate_grad_kernel<float>, dim3(nseg_blocks), dim3(kDh), 0, s, gp);
   }
+  if (ob) hipLaunchKernelGGL(h2_gate_first_kernel<bf16_t>, dim3(nmat), dim3(kDh), 0, s, gp);
+  else hipLaunchKernelGGL(h2_gate_first_kernel<float>, dim3(nmat), dim3(kDh), 0, s, gp);
   return hipGetLastError();
 }
 
