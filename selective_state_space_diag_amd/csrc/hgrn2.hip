@@ -579,14 +579,15 @@ __device__ __forceinline__ void h2_gg_load(const H2Params& p, int64_t b, int64_t
 }
 
 // The chunk's terms e = do o - v dv at the wave's output elements go to LDS ([row][position], 4-position
-// groups XOR-swizzled by the row, in the W tiles' space); thread (row lane, positions 8 gp .. 8 gp + 7)
-// takes a running sum over its positions, the groups' totals meet in LDS (gam's space), and it stores
-// dg_logit for its positions from the running sum carried over the earlier chunks.  Called by every
-// thread after the chunk's state update; no LDS it touches is read again before the next chunk's gate
-// step, which follows that chunk's first barrier.
+// groups XOR-swizzled by the row) in the Q tile of the other parity, which no one reads during this chunk
+// and the next chunk's Q fills only after every thread has passed the second barrier here; thread (row
+// lane, positions 8 gp .. 8 gp + 7) takes a running sum over its positions, the groups' totals meet in
+// gam's space (free once every wave is past its outputs, i.e. past the first barrier here), and it
+// stores dg_logit for its positions from the running sum carried over the earlier chunks.  Called by
+// every thread after the chunk's state update.
 template <typename TG>
-__device__ __forceinline__ void h2_gg_step(const H2Params& p, H2Lds& sm, int64_t b, int64_t hh, int i0, int64_t t0,
-                                           int valid, int iw, int lane, int half_t, int gp, float lb,
+__device__ __forceinline__ void h2_gg_step(const H2Params& p, H2Lds& sm, float* eT, int64_t b, int64_t hh, int i0,
+                                           int64_t t0, int valid, int iw, int lane, int half_t, int gp, float lb,
                                            const float (&ov)[2][4], const H2GGWave& w, const H2GGLane& l,
                                            float& carry) {
   const int l16 = lane & 15, lg = lane >> 4;
@@ -598,9 +599,7 @@ __device__ __forceinline__ void h2_gg_step(const H2Params& p, H2Lds& sm, int64_t
     ev[a][2] = bf16_lo(w.d[a].y) * w.o[a].z - bf16_lo(w.v[a].y) * ov[a][2];
     ev[a][3] = bf16_hi(w.d[a].y) * w.o[a].w - bf16_hi(w.v[a].y) * ov[a][3];
   }
-  float* eT = reinterpret_cast<float*>(&sm.w[0]);  // w and w_lo: 64 x 64 fp32
-  static_assert(sizeof(sm.w) + sizeof(sm.w_lo) == sizeof(float) * kRows * kCh, "the terms fill W's tiles");
-  __syncthreads();  // every wave is past its products: W's tiles and gam are free
+  static_assert(sizeof(sm.q[0]) >= sizeof(float) * kRows * kCh, "the terms fit in a Q tile");
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     const int t = 16 * (half_t ? (a ? 2 : 1) : (a ? 3 : 0)) + l16;
@@ -861,7 +860,9 @@ __global__ __launch_bounds__(kWaves * 64) void hgrn2_chunk_kernel(H2Params p) {
     if (c + 1 < nchunks)
       h2_gate1<GUARD>(sm, lane, gp, (int)min((int64_t)kCh, p.L - t0 - kCh), 0, lb, one_m_lb, gam_run, vv,
                       sm.nanpos[(c + 1) & 1]);
-    if constexpr (GG) h2_gg_step<TG>(p, sm, b, hh, i0, t0, valid, iw, lane, half_t, gp, lb, ov, gw, gl, carry);
+    if constexpr (GG)
+      h2_gg_step<TG>(p, sm, reinterpret_cast<float*>(sm.q[buf ^ 1]), b, hh, i0, t0, valid, iw, lane, half_t, gp, lb,
+                     ov, gw, gl, carry);
   }
 
   if (p.S_last) {
