@@ -627,6 +627,19 @@ def form_hgrn2_backward(args, device):
                      "hgrn2_backward_bf16_B8_H16_d128_L4096")
 
 
+def form_hgrn2_backward_lb0(args, device):
+    import selective_state_space_diag_amd as ssd
+    gen, (B, L, H, dd), q, k, v, g = _hgrn2_inputs(device, 16)
+    do = gen.randn((B, L, H, dd), std=dd ** -0.5)
+    o = ssd.hgrn2_scan(q, k, v, g, 0.0)
+    t = time_calls(lambda kk: ssd.hgrn2_scan_backward(q, k, v, g, 0.0, do, o=o), 1, 10, 2)
+    flops = 3 * 2 * B * L * H * (2 * 64 * dd + 2 * dd * dd)
+    return record_of(t, B * L * H * dd * dd, hgrn2_bwd_bytes(B, L, H, dd),
+                     dict(mfma_equiv_tflops=flops / (t["ms"] * 1e-3) / 1e12,
+                          mfma_util=flops / (t["ms"] * 1e-3) / 1e12 / BF16_MFMA_TFLOPS),
+                     "hgrn2_backward_lb0_bf16_B8_H16_d128_L4096")
+
+
 def form_hgrn2_key(args, device):
     import selective_state_space_diag_amd as ssd
     _, (B, L, H, dd), q, k, v, g = _hgrn2_inputs(device, 16)
@@ -695,6 +708,7 @@ FORMS = {
     "hgrn2_bf16_B8_H16_d128_L4096": form_hgrn2,
     "hgrn2_lb0_bf16_B8_H16_d128_L4096": form_hgrn2_lb0,
     "hgrn2_backward_bf16_B8_H16_d128_L4096": form_hgrn2_backward,
+    "hgrn2_backward_lb0_bf16_B8_H16_d128_L4096": form_hgrn2_backward_lb0,
     "hgrn2_key_gate_bf16_B8_H16_d128_L4096": form_hgrn2_key,
     "hgrn2_key_gate_lb0_bf16_B8_H16_d128_L4096": form_hgrn2_key_lb0,
     "readout_norm_B8_L4096_width2048": form_readout_norm,
