@@ -1059,17 +1059,20 @@ __device__ __forceinline__ void wave_sum16(float (&v)[16], int lane) {
 }
 
 // ----------------------------------------------------------------------------- pass 1
-// Within a unit the rows go in blocks of kBT: a block's state from zero (Hk) and its weighted adjoint
-// sum (Qk, with the running product of abar restarted at the block) are folded into the unit's with the
-// block's decay product applied as one exponential, 2^(A2 sum delta) (2^(sum of the clamped exponents)
-// when the clamp can act), so no product of rounded decays runs longer than a block.
+// Within a unit the rows go in blocks: a block's state from zero (Hk) and its weighted adjoint sum (Qk,
+// with the running product of abar restarted at the block) are folded into the unit's with the block's
+// decay product applied as one exponential, 2^(A2 sum delta) (2^(sum of the clamped exponents) when the
+// clamp can act).  fp32 inputs take blocks of kBT rows, so no product of rounded decays runs longer than
+// that; bf16 inputs take the unit as one block (its 64 rounded decays move the sums by a few fp32 ulps,
+// far below what the inputs' rounding allows).
 template <typename Tin, int NS, bool SOFTPLUS, bool GATE, int DISC>
 __device__ __forceinline__ void bwd_agg_rows(const SelBwdParams& p, int64_t row0, int R, int64_t dl,
                                              const float* A2, float bias, const float* sB, const float* sC,
                                              float* P, float* H, float* Q, float& sdelta) {
   using W = win<Tin, 1>;
   constexpr int es = sizeof(Tin);
-  static_assert(kBT % kPrefetch == 0, "blocks hold whole prefetch groups");
+  constexpr int kBlk = sizeof(Tin) == 2 ? kBU : kBT;  // rows per block
+  static_assert(kBlk % kPrefetch == 0, "blocks hold whole prefetch groups");
   const auto wdt = unit_window(p.dt, row0, R, p.D, es), wxx = unit_window(p.x, row0, R, p.D, es);
   const auto wdy = unit_window(p.dy, row0, R, p.D, es), wzz = unit_window(GATE ? p.z : p.dy, row0, R, p.D, es);
   const uint32_t lane_in = (uint32_t)(dl * es), row_in = (uint32_t)(p.D * es);
@@ -1086,12 +1089,14 @@ __device__ __forceinline__ void bwd_agg_rows(const SelBwdParams& p, int64_t row0
   float sd_tot = 0.0f;  // delta summed over the blocks done
 #pragma unroll
   for (int n = 0; n < NS; ++n) { H[n] = 0.0f; Q[n] = 0.0f; es_tot[n] = 0.0f; }
-  for (int blk0 = 0; blk0 < R; blk0 += kBT) {
+  const int blk_end = kBlk == kBU ? 1 : R;  // one block when the unit is one (R <= kBU)
+  for (int blk0 = 0; blk0 < blk_end; blk0 += kBlk) {
     float hk[NS], qk[NS], cp[NS], es_k[NS];
     float sd_k = 0.0f;
 #pragma unroll
     for (int n = 0; n < NS; ++n) { hk[n] = 0.0f; qk[n] = 0.0f; cp[n] = 1.0f; es_k[n] = 0.0f; }
-    for (int base = blk0; base < blk0 + kBT; base += kPrefetch) {
+#pragma unroll 1
+    for (int base = blk0; base < blk0 + kBlk && base < R; base += kPrefetch) {
 #pragma unroll
       for (int k = 0; k < kPrefetch; ++k) {
         const int i = base + k;
@@ -1265,6 +1270,7 @@ template <typename Tin, typename Tout, int NS, bool SOFTPLUS, bool GATE, int DIS
 __device__ __forceinline__ void bwd_grad_unit(const SelBwdParams& p, const BUnit& U, int64_t u, int64_t d,
                                               int64_t dl, bool active, Lds& S) {
   constexpr bool STASH = sizeof(Tin) == 2;
+  constexpr bool kChainQ = sizeof(Tin) == 2;  // h and q run through the whole unit (bf16 inputs)
   using W = win<Tin, 1>;
   using Raw = typename W::raw;
   constexpr int es = sizeof(Tin);
@@ -1333,11 +1339,12 @@ __device__ __forceinline__ void bwd_grad_unit(const SelBwdParams& p, const BUnit
         }
       }
       if (k < nsb - 1) {  // every row of this block is inside the unit
-        // the block's state from zero, then h = (decay of the block, one exponential) h + that
+        // fp32 inputs: the block's state from zero, then h = (decay of the block, one exponential) h +
+        // that; bf16 inputs: h chained through the block's rows
         float hk[NS], es_k[NS];
         float sd_k = 0.0f;
 #pragma unroll
-        for (int n = 0; n < NS; ++n) { hk[n] = 0.0f; es_k[n] = 0.0f; }
+        for (int n = 0; n < NS; ++n) { hk[n] = kChainQ ? h[n] : 0.0f; es_k[n] = 0.0f; }
 #pragma unroll
         for (int t = 0; t < kBT; ++t) {
           const float delta = step_delta<Tin, SOFTPLUS>(step_in<Tin>(W::get(rd[t], 0), bias));
@@ -1358,8 +1365,12 @@ __device__ __forceinline__ void bwd_grad_unit(const SelBwdParams& p, const BUnit
         }
 #pragma unroll
         for (int n = 0; n < NS; ++n) {
-          const float Pk = DISC == kClamp ? hw_exp2(es_k[n]) : hw_exp2(A2[n] * sd_k);
-          h[n] = fmaf(Pk, h[n], hk[n]);
+          if (kChainQ) {
+            h[n] = hk[n];
+          } else {
+            const float Pk = DISC == kClamp ? hw_exp2(es_k[n]) : hw_exp2(A2[n] * sd_k);
+            h[n] = fmaf(Pk, h[n], hk[n]);
+          }
           s0[n] = s1[n]; s1[n] = s2[n]; s2[n] = s3[n]; s3[n] = h[n];
         }
       }
@@ -1450,7 +1461,7 @@ __device__ __forceinline__ void bwd_grad_unit(const SelBwdParams& p, const BUnit
       wave_sum16(v, lane);
       if ((lane & 3) == 0) S.redC[n][wave][(lane >> 2) & 15] = v[0];
       float dA = 0.0f;
-      float qz = 0.0f;  // q from zero past the sub-block's end
+      float qz = 0.0f;  // q from zero past the sub-block's end (fp32 inputs)
 #pragma unroll
       for (int t4 = kBT / 4 - 1; t4 >= 0; --t4) {
         const float4 b4 = Bn4[t4], c4 = Cn4[t4];
@@ -1461,12 +1472,14 @@ __device__ __forceinline__ void bwd_grad_unit(const SelBwdParams& p, const BUnit
           const float ab = abr[t], hp = hpr[t];
           const float g = fmaf(ds[t], cc[k], q);
           q = ab * g;
-          qz = ab * fmaf(ds[t], cc[k], qz);
+          if (!kChainQ) qz = ab * fmaf(ds[t], cc[k], qz);
           float mab = (g * hp) * ab;  // d abar times abar
           if (DISC == kClamp) {
             mab = (live >> t) & 1u ? mab : 0.0f;  // no gradient through the clamp
-            const float e = delta[t] * A2;          // the clamped exponents summed from the sub-block's end
-            es_j += e > kClampLog2 ? kClampLog2 : e;
+            if (!kChainQ) {
+              const float e = delta[t] * A2;  // the clamped exponents summed from the sub-block's end
+              es_j += e > kClampLog2 ? kClampLog2 : e;
+            }
           }
           MA[t] = fmaf(mab, An, MA[t]);
           dA = fmaf(mab, delta[t], dA);
@@ -1476,10 +1489,16 @@ __device__ __forceinline__ void bwd_grad_unit(const SelBwdParams& p, const BUnit
       }
       wave_sum16(v, lane);
       if ((lane & 3) == 0) S.redB[n][wave][(lane >> 2) & 15] = v[0];
-      // q entering the earlier sub-block: q from zero plus q_in carried by the sub-block's decay product
-      // taken as one exponential, so no chain of rounded decays runs past a sub-block
-      const float Pj = DISC == kClamp ? hw_exp2(es_j) : hw_exp2(A2 * sd_j);
-      qv[n] = fmaf(Pj, q_in, qz);
+      // q entering the earlier sub-block.  fp32 inputs: q from zero plus q_in carried by the sub-block's
+      // decay product taken as one exponential, so no chain of rounded decays runs past a sub-block.
+      // bf16 inputs: the chained q itself (a unit's 64 rounded decays move it by a few fp32 ulps, far
+      // below what the inputs' rounding allows), which saves the second recurrence
+      if (kChainQ) {
+        qv[n] = q;
+      } else {
+        const float Pj = DISC == kClamp ? hw_exp2(es_j) : hw_exp2(A2 * sd_j);
+        qv[n] = fmaf(Pj, q_in, qz);
+      }
       dAv[n] += dA;
     }
 
