@@ -62,16 +62,17 @@ struct SelParams {
   float* carry;  // [unit][N][D]  state entering the segment
   const int2* seq_units;  // varlen: (first unit, unit count) per sequence
   // Packed varlen forward plan (NULL for the other launches): scan units of whole sequences or of
-  // long sequences cut into a few pieces, longest first; aggregates only for the rows before a
-  // sequence's last piece.
-  const int* vcount;      // [0] scan units, [1] aggregate units, [2] pieces with an aggregate
+  // long sequences cut into a few pieces, in two phases (first pieces, then the later ones), longest
+  // first within a phase; aggregates only for the rows of a sequence's middle pieces.
+  const int* vcount;      // [0] scan units, [1] aggregate units, [2] piece slots, [3] scan units of phase 1
   const int4* vscan;      // (sequence, first row in the sequence, rows, carry slot or -1)
   const int4* vagg;       // (sequence, first row in the sequence, rows, piece slot)
   const int4* vseq;       // per sequence: (first aggregate unit, aggregate units, aggregate units per
                           //  scan piece, first piece slot)
-  const int2* vpiece;     // per piece slot: (first aggregate unit, aggregate units)
-  float* pieceP;          // [piece slot][N][D]: prod abar over a piece (every piece but a sequence's last)
-  float* pieceH;          // [piece slot][N][D]: the state a piece reaches from zero
+  const int2* vpiece;     // per piece slot: (first aggregate unit, aggregate units; 0 for a first piece)
+  float* pieceP;          // [piece slot][N][D]: prod abar over a middle piece
+  float* pieceH;          // [piece slot][N][D]: the state a middle piece reaches from zero; a first
+                          //  piece's end state
   int64_t nblk;           // channel blocks (the packed plan's scan grid is units x channel blocks)
 };
 
@@ -297,11 +298,12 @@ __device__ __forceinline__ int load_A(const SelParams& p, int64_t dl, float* A2)
 }
 
 // ----------------------------------------------------------------------------- pass 1: aggregates
+// One aggregate unit of one channel block: the unit's rows from zero, storing prod abar and the state
+// reached per state and channel.
 template <typename Tin, int NS, bool SOFTPLUS>
-__global__ __launch_bounds__(kThreads, 4) void selective_aggregate_kernel(SelParams p) {
-  const int64_t u = blockIdx.x;
+__device__ __forceinline__ void agg_unit(const SelParams& p, int64_t u, int64_t cb, float* lds) {
   Unit U;
-  if (p.vagg != nullptr) {  // packed plan: aggregate unit u (never a sequence's last rows)
+  if (p.vagg != nullptr) {  // packed plan: aggregate unit u (a middle piece's rows)
     if (u >= (int64_t)p.vcount[1]) return;
     const int4 ve = p.vagg[u];
     U.row0 = (int64_t)p.cu[ve.x] + ve.y;
@@ -310,7 +312,7 @@ __global__ __launch_bounds__(kThreads, 4) void selective_aggregate_kernel(SelPar
     U = unit_of(p, u);
     if (!U.valid || U.last) return;
   }
-  const int64_t d = (int64_t)blockIdx.y * kThreads + threadIdx.x;
+  const int64_t d = cb * kThreads + threadIdx.x;
   const bool active = d < p.D;
   const int64_t dl = active ? d : p.D - 1;  // lanes past D recompute channel D-1, store nothing
   float A2[NS];
@@ -320,7 +322,6 @@ __global__ __launch_bounds__(kThreads, 4) void selective_aggregate_kernel(SelPar
 #pragma unroll
   for (int n = 0; n < NS; ++n) { h[n] = 0.0f; e[n] = 0.0f; }
   float sum_delta = 0.0f;
-  __shared__ float lds[2 * BCStage<NS, false>::PER_BLOCK];
   if (disc == kExp)
     run_rows<Tin, float, NS, SOFTPLUS, kExp, false, false>(p, U.row0, U.row1, dl, A2, bias, 0.0f, h, e, sum_delta, lds);
   else
@@ -336,6 +337,12 @@ __global__ __launch_bounds__(kThreads, 4) void selective_aggregate_kernel(SelPar
   }
 }
 
+template <typename Tin, int NS, bool SOFTPLUS>
+__global__ __launch_bounds__(kThreads, 4) void selective_aggregate_kernel(SelParams p) {
+  __shared__ float lds[2 * BCStage<NS, false>::PER_BLOCK];
+  agg_unit<Tin, NS, SOFTPLUS>(p, blockIdx.x, blockIdx.y, lds);
+}
+
 // Packed plan: one workgroup per (piece, channel block) folds the piece's aggregate units in order
 // into the piece's aggregate (prod abar and the state reached from zero); units in rounds of JB with
 // all their loads in flight together.
@@ -348,6 +355,7 @@ __global__ __launch_bounds__(kThreads) void selective_vpiece_kernel(SelParams p)
   const int2 pc = p.vpiece[slot];
   const int64_t first = pc.x;
   const int q = pc.y;
+  if (q == 0) return;  // a first piece's slot: its scan leaves the end state there
   float Pp[NS], Hp[NS];
 #pragma unroll
   for (int n = 0; n < NS; ++n) { Pp[n] = 1.0f; Hp[n] = 0.0f; }
@@ -391,12 +399,9 @@ __device__ __forceinline__ void scan_rows(const SelParams& p, const Unit& U, int
                                                           lds);
 }
 
+// One scan unit of one channel block: the rows from the unit's carry-in, with readout.
 template <typename Tin, typename Tout, int NS, bool SOFTPLUS>
-__global__ __launch_bounds__(kThreads) void selective_scan_kernel(SelParams p) {
-  // packed plan: one-dimensional grid, unit-major (a unit's channel blocks are dispatched together,
-  // longest units first); otherwise (unit, channel block)
-  const int64_t u = p.vscan ? (int64_t)blockIdx.x / p.nblk : (int64_t)blockIdx.x;
-  const int64_t cb = p.vscan ? (int64_t)blockIdx.x - u * p.nblk : (int64_t)blockIdx.y;
+__device__ __forceinline__ void scan_unit(const SelParams& p, int64_t u, int64_t cb, float* lds) {
   const Unit U = unit_of(p, u);
   if (!U.valid) return;
   const int64_t d = cb * kThreads + threadIdx.x;
@@ -413,11 +418,12 @@ __global__ __launch_bounds__(kThreads) void selective_scan_kernel(SelParams p) {
 #pragma unroll
     for (int n = 0; n < NS; ++n) h[n] = p.h0 ? p.h0[(U.seq * p.D + dl) * NS + n] : 0.0f;
   } else if (p.vscan) {
-    // packed plan: h0 folded through the aggregates of the sequence's earlier pieces
+    // packed plan: the first piece's end state folded through the aggregates of the middle pieces
+    // before this one
     const int64_t first = p.vseq[U.seq].w;
 #pragma unroll
-    for (int n = 0; n < NS; ++n) h[n] = p.h0 ? p.h0[(U.seq * p.D + dl) * NS + n] : 0.0f;
-    for (int64_t j = first; j <= U.carry; ++j) {
+    for (int n = 0; n < NS; ++n) h[n] = p.pieceH[(first * NS + n) * p.D + dl];
+    for (int64_t j = first + 1; j <= U.carry; ++j) {
 #pragma unroll
       for (int n = 0; n < NS; ++n)
         h[n] = fmaf(p.pieceP[(j * NS + n) * p.D + dl], h[n], p.pieceH[(j * NS + n) * p.D + dl]);
@@ -427,15 +433,51 @@ __global__ __launch_bounds__(kThreads) void selective_scan_kernel(SelParams p) {
     for (int n = 0; n < NS; ++n) h[n] = p.carry[(u * NS + n) * p.D + dl];
   }
   float sum_delta = 0.0f;
-  __shared__ float lds[2 * BCStage<NS, true>::PER_BLOCK];
   if (p.z)
     scan_rows<Tin, Tout, NS, SOFTPLUS, true>(p, U, disc, dl, A2, bias, dskip, h, e, sum_delta, lds);
   else
     scan_rows<Tin, Tout, NS, SOFTPLUS, false>(p, U, disc, dl, A2, bias, dskip, h, e, sum_delta, lds);
 
-  if (U.last && p.h_last && active) {
+  if (!active) return;
+  if (U.last) {
+    if (p.h_last) {
 #pragma unroll
-    for (int n = 0; n < NS; ++n) p.h_last[(U.seq * p.D + d) * NS + n] = h[n];
+      for (int n = 0; n < NS; ++n) p.h_last[(U.seq * p.D + d) * NS + n] = h[n];
+    }
+  } else if (p.vscan && U.seg == 0) {  // packed plan: a long sequence's first piece
+    const int64_t first = p.vseq[U.seq].w;
+#pragma unroll
+    for (int n = 0; n < NS; ++n) p.pieceH[(first * NS + n) * p.D + d] = h[n];
+  }
+}
+
+// Batched plan and unpacked varlen: grid (unit, channel block).  Packed plan, phase 2: a
+// one-dimensional grid over the scan units after phase 1's, unit-major (a unit's channel blocks are
+// dispatched together, longest units first).
+template <typename Tin, typename Tout, int NS, bool SOFTPLUS>
+__global__ __launch_bounds__(kThreads) void selective_scan_kernel(SelParams p) {
+  __shared__ float lds[2 * BCStage<NS, true>::PER_BLOCK];
+  if (p.vscan) {
+    const int64_t u = blockIdx.x / p.nblk;
+    scan_unit<Tin, Tout, NS, SOFTPLUS>(p, (int64_t)p.vcount[3] + u, (int64_t)blockIdx.x - u * p.nblk, lds);
+  } else {
+    scan_unit<Tin, Tout, NS, SOFTPLUS>(p, blockIdx.x, blockIdx.y, lds);
+  }
+}
+
+// Packed plan, phase 1: the first pieces' scan units (longest first), then the aggregate units of the
+// middle pieces, in one one-dimensional grid, unit-major.
+template <typename Tin, typename Tout, int NS, bool SOFTPLUS>
+__global__ __launch_bounds__(kThreads) void selective_phase1_kernel(SelParams p) {
+  __shared__ float lds[2 * BCStage<NS, true>::PER_BLOCK];  // the larger of the two stages
+  const int64_t s1 = (int64_t)p.vcount[3] * p.nblk;
+  const int64_t b = blockIdx.x;
+  if (b < s1) {
+    const int64_t u = b / p.nblk;
+    scan_unit<Tin, Tout, NS, SOFTPLUS>(p, u, b - u * p.nblk, lds);
+  } else {
+    const int64_t u = (b - s1) / p.nblk;
+    agg_unit<Tin, NS, SOFTPLUS>(p, u, b - s1 - u * p.nblk, lds);
   }
 }
 
@@ -482,22 +524,30 @@ __global__ __launch_bounds__(kThreads) void selective_carry_kernel(SelParams p) 
   }
 }
 
-// Pieces of a packed sequence of `len` rows: unsplit up to X rows, else cut into pieces of a
-// multiple of Y rows (all but the last full), as few as keep them within X.
+// Pieces of a packed sequence of `len` rows: unsplit up to F rows; else a first piece of F rows and
+// the rest cut into pieces of a multiple of Y rows (all but the last full), as few as keep them
+// within P.
 struct Pieces {
-  int64_t len, piece, count;  // rows, rows of every piece but the last, pieces
+  int64_t len, first, piece, count;  // rows, rows of the first piece, of every later piece but the last, pieces
+  __device__ __forceinline__ int64_t rows(int64_t k) const {
+    return k == 0 ? first : (k + 1 < count ? piece : len - first - (k - 1) * piece);
+  }
+  __device__ __forceinline__ int64_t start(int64_t k) const { return k == 0 ? 0 : first + (k - 1) * piece; }
 };
-__device__ __forceinline__ Pieces pieces_of(int64_t len, int64_t X, int64_t Y) {
+__device__ __forceinline__ Pieces pieces_of(int64_t len, int64_t F, int64_t P, int64_t Y) {
   Pieces r;
   r.len = len;
-  if (len <= X) {
-    r.piece = len;
+  r.piece = 0;
+  if (len <= F) {
+    r.first = len;
     r.count = len > 0 ? 1 : 0;
     return r;
   }
-  const int64_t p = (len + X - 1) / X;
-  r.piece = ((len + p - 1) / p + Y - 1) / Y * Y;
-  r.count = (len + r.piece - 1) / r.piece;
+  r.first = F;
+  const int64_t rest = len - F;
+  const int64_t k = (rest + P - 1) / P;
+  r.piece = ((rest + k - 1) / k + Y - 1) / Y * Y;
+  r.count = 1 + (rest + r.piece - 1) / r.piece;
   return r;
 }
 
@@ -533,48 +583,56 @@ __device__ __forceinline__ int block_inclusive_sum(int v, int* buf) {
   return r;
 }
 
-// Packed plan, one workgroup: per-sequence table, aggregate units (Y rows each, every row before a
-// sequence's last piece), scan units ordered by length (longest first; the order among units of
-// one length bucket is not fixed, and no result depends on it), the pieces' aggregate units, the
-// counts, and the final state of zero-length sequences (= their initial state, or zero).
-__global__ __launch_bounds__(1024) void selective_vplan_kernel(const int32_t* cu, int64_t nseq, int64_t X, int64_t Y,
-                                                               int* count, int4* scan, int4* agg, int4* seqtab,
-                                                               int2* piece, int64_t D, int64_t N, const float* h0,
-                                                               float* h_last) {
+// Packed plan, one workgroup.  The scan runs in two phases.  Phase 1 scans every sequence's first
+// piece from its initial state (a long sequence's first piece leaves its end state in the sequence's
+// first piece slot) while the aggregate units cover the middle pieces (every piece but the first and
+// the last), Y rows each; phase 2 scans the later pieces, each from the first piece's end state folded
+// through the aggregates of the middle pieces before it.  Tables: per sequence, the aggregate units,
+// the piece slots (the first piece's is filled by its scan, the others by the piece fold), the scan
+// units of phase 1 then of phase 2, each ordered by length (longest first; the order among units of
+// one length bucket is not fixed, and no result depends on it), the counts, and the final state of
+// zero-length sequences (= their initial state, or zero).
+__global__ __launch_bounds__(1024) void selective_vplan_kernel(const int32_t* cu, int64_t nseq, int64_t F, int64_t P,
+                                                               int64_t Y, int* count, int4* scan, int4* agg,
+                                                               int4* seqtab, int2* piece, int64_t D, int64_t N,
+                                                               const float* h0, float* h_last) {
   __shared__ int s_buf[1024];
-  __shared__ int s_hist[kLenBuckets];
-  __shared__ int s_base_agg, s_base_carry, s_units;
-  for (int b = threadIdx.x; b < kLenBuckets; b += 1024) s_hist[b] = 0;
-  if (threadIdx.x == 0) { s_base_agg = 0; s_base_carry = 0; s_units = 0; }
+  __shared__ int s_hist[2 * kLenBuckets];  // phase 1 buckets, then phase 2 buckets
+  __shared__ int s_base_agg, s_base_carry, s_units, s_first;
+  for (int b = threadIdx.x; b < 2 * kLenBuckets; b += 1024) s_hist[b] = 0;
+  if (threadIdx.x == 0) { s_base_agg = 0; s_base_carry = 0; s_units = 0; s_first = 0; }
   __syncthreads();
   // pass 1: slots, per-sequence table, aggregate units, length histogram of the scan units
   for (int64_t blk = 0; blk < nseq; blk += 1024) {
     const int64_t sq = blk + threadIdx.x;
-    Pieces pc{0, 0, 0};
-    if (sq < nseq) pc = pieces_of((int64_t)cu[sq + 1] - cu[sq], X, Y);
-    const int q = pc.count > 1 ? (int)(pc.piece / Y) : 1;
-    const int nagg = pc.count > 1 ? (int)((pc.count - 1) * q) : 0;
+    Pieces pc{0, 0, 0, 0};
+    if (sq < nseq) pc = pieces_of((int64_t)cu[sq + 1] - cu[sq], F, P, Y);
+    const int q = pc.count > 1 ? (int)(pc.piece / Y) : 0;  // aggregate units per middle piece
+    const int nagg = pc.count > 2 ? (int)((pc.count - 2) * q) : 0;
     const int ncarry = pc.count > 1 ? (int)(pc.count - 1) : 0;
     const int ia = block_inclusive_sum(nagg, s_buf);
     const int ic = block_inclusive_sum(ncarry, s_buf);
     const int iu = block_inclusive_sum((int)pc.count, s_buf);
+    const int i1 = block_inclusive_sum(pc.count > 0 ? 1 : 0, s_buf);
     const int first_agg = s_base_agg + ia - nagg, first_carry = s_base_carry + ic - ncarry;
     if (sq < nseq) {
       seqtab[sq] = make_int4(first_agg, nagg, q, first_carry);
-      for (int j = 0; j < nagg; ++j) agg[first_agg + j] = make_int4((int)sq, (int)(j * Y), (int)Y, first_carry + j / q);
-      for (int k = 0; k < ncarry; ++k) piece[first_carry + k] = make_int2(first_agg + k * q, q);
-      for (int64_t k = 0; k < pc.count; ++k) {
-        const int64_t rows = k + 1 < pc.count ? pc.piece : pc.len - k * pc.piece;
-        atomicAdd(&s_hist[len_bucket(rows)], 1);
-      }
+      for (int j = 0; j < nagg; ++j)
+        agg[first_agg + j] = make_int4((int)sq, (int)(pc.first + j * Y), (int)Y, first_carry + 1 + j / q);
+      if (ncarry > 0) piece[first_carry] = make_int2(0, 0);  // filled by the first piece's scan
+      for (int k = 1; k < ncarry; ++k) piece[first_carry + k] = make_int2(first_agg + (k - 1) * q, q);
+      for (int64_t k = 0; k < pc.count; ++k)
+        atomicAdd(&s_hist[(k == 0 ? 0 : kLenBuckets) + len_bucket(pc.rows(k))], 1);
     }
     __syncthreads();
-    if (threadIdx.x == 1023) { s_base_agg += ia; s_base_carry += ic; s_units += iu; }
+    if (threadIdx.x == 1023) { s_base_agg += ia; s_base_carry += ic; s_units += iu; s_first += i1; }
     __syncthreads();
   }
-  // bucket offsets, longest bucket first: thread t holds bucket kLenBuckets - 1 - t
+  // bucket offsets, phase 1 first, longest bucket first within a phase: thread t < 2 kLenBuckets holds
+  // bucket (t / kLenBuckets) kLenBuckets + kLenBuckets - 1 - t % kLenBuckets
   {
-    const int b = kLenBuckets - 1 - (int)threadIdx.x;
+    const int t = (int)threadIdx.x;
+    const int b = t < 2 * kLenBuckets ? (t / kLenBuckets) * kLenBuckets + kLenBuckets - 1 - t % kLenBuckets : -1;
     const int c = b >= 0 ? s_hist[b] : 0;
     const int incl = block_inclusive_sum(c, s_buf);
     if (b >= 0) s_hist[b] = incl - c;
@@ -588,13 +646,13 @@ __global__ __launch_bounds__(1024) void selective_vplan_kernel(const int32_t* cu
     if (threadIdx.x == 0) s_nempty = 0;
     __syncthreads();
     if (sq < nseq) {
-      const Pieces pc = pieces_of((int64_t)cu[sq + 1] - cu[sq], X, Y);
+      const Pieces pc = pieces_of((int64_t)cu[sq + 1] - cu[sq], F, P, Y);
       if (pc.len == 0 && h_last) s_empty[atomicAdd(&s_nempty, 1)] = (int)sq;
       const int first_carry = seqtab[sq].w;
       for (int64_t k = 0; k < pc.count; ++k) {
-        const int64_t rows = k + 1 < pc.count ? pc.piece : pc.len - k * pc.piece;
-        const int pos = atomicAdd(&s_hist[len_bucket(rows)], 1);
-        scan[pos] = make_int4((int)sq, (int)(k * pc.piece), (int)rows, k == 0 ? -1 : first_carry + (int)k - 1);
+        const int64_t rows = pc.rows(k);
+        const int pos = atomicAdd(&s_hist[(k == 0 ? 0 : kLenBuckets) + len_bucket(rows)], 1);
+        scan[pos] = make_int4((int)sq, (int)pc.start(k), (int)rows, k == 0 ? -1 : first_carry + (int)k - 1);
       }
     }
     __syncthreads();
@@ -608,6 +666,7 @@ __global__ __launch_bounds__(1024) void selective_vplan_kernel(const int32_t* cu
     count[0] = s_units;
     count[1] = s_base_agg;
     count[2] = s_base_carry;
+    count[3] = s_first;
   }
 }
 
@@ -730,17 +789,20 @@ hipError_t launch_by_n(const SelParams& p, int64_t U, bool softplus, hipStream_t
   }
 }
 
+// Packed plan: phase 1 (first pieces and aggregate units; at most one first piece per sequence), the
+// piece fold, phase 2 (the later pieces: at most one per piece slot).
 template <typename Tin, typename Tout, int NS>
-hipError_t launch_packed(const SelParams& p, int64_t A, int64_t C, int64_t S, bool softplus, hipStream_t s) {
-  const dim3 agrid((unsigned)A, (unsigned)p.nblk);
-  if (A > 0) {
-    if (softplus) hipLaunchKernelGGL((selective_aggregate_kernel<Tin, NS, true>), agrid, dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL((selective_aggregate_kernel<Tin, NS, false>), agrid, dim3(kThreads), 0, s, p);
-    hipLaunchKernelGGL((selective_vpiece_kernel<NS>), dim3((unsigned)C, (unsigned)p.nblk), dim3(kThreads), 0, s, p);
+hipError_t launch_packed(const SelParams& p, int64_t A, int64_t C, bool softplus, hipStream_t s) {
+  const dim3 grid1((unsigned)((p.nseq + A) * p.nblk));
+  if (softplus) hipLaunchKernelGGL((selective_phase1_kernel<Tin, Tout, NS, true>), grid1, dim3(kThreads), 0, s, p);
+  else hipLaunchKernelGGL((selective_phase1_kernel<Tin, Tout, NS, false>), grid1, dim3(kThreads), 0, s, p);
+  if (C > 0) {
+    if (A > 0)
+      hipLaunchKernelGGL((selective_vpiece_kernel<NS>), dim3((unsigned)C, (unsigned)p.nblk), dim3(kThreads), 0, s, p);
+    const dim3 grid2((unsigned)(C * p.nblk));
+    if (softplus) hipLaunchKernelGGL((selective_scan_kernel<Tin, Tout, NS, true>), grid2, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((selective_scan_kernel<Tin, Tout, NS, false>), grid2, dim3(kThreads), 0, s, p);
   }
-  const dim3 sgrid((unsigned)(S * p.nblk));
-  if (softplus) hipLaunchKernelGGL((selective_scan_kernel<Tin, Tout, NS, true>), sgrid, dim3(kThreads), 0, s, p);
-  else hipLaunchKernelGGL((selective_scan_kernel<Tin, Tout, NS, false>), sgrid, dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
@@ -768,19 +830,21 @@ void launch_update_t(const SelectiveUpdateArgs& a, hipStream_t s) {
 
 struct Plan {
   int64_t T, nseg, U;
-  // packed varlen forward plan (packed = true): pieces of at most X rows, aggregate units of Y rows;
-  // bounds on aggregate units (A), carry slots (C) and scan units (S)
+  // packed varlen forward plan (packed = true): a first piece of F rows, later pieces of at most P
+  // rows, aggregate units of Y rows; bounds on aggregate units (A), piece slots (C) and scan units (S)
   bool packed;
-  int64_t X, Y, A, C, S;
+  int64_t F, P, Y, A, C, S;
 };
 
 // Packed varlen plan.  A sequence is scanned by one workgroup per channel block, from its start to
-// its end, unless it is longer than X rows; then it is cut into as few pieces as keep them within X,
-// and only the rows before its last piece pass through the aggregate kernel.  X is a fraction of the
-// rows each compute unit scans on average, so that the longest pieces, started first, end with the
-// rest; the scan units go longest first.
-constexpr int64_t kPieceNum = 3, kPieceDen = 8;  // X = rows per compute unit * kPieceNum / kPieceDen
-constexpr int64_t kAggRows = 256;                // Y
+// its end, unless it is longer than F rows; then its first F rows are scanned in phase 1, beside the
+// aggregate units of its middle pieces, and the rest, cut into as few pieces as keep them within P
+// rows, in phase 2 (only the middle pieces pass through the aggregate kernel).  F and P are
+// fractions of the rows each compute unit scans on average, so that in each phase the longest
+// pieces, started first, end with the rest.
+constexpr int64_t kFirstNum = 1, kFirstDen = 4;  // F = rows per compute unit * kFirstNum / kFirstDen
+constexpr int64_t kLaterNum = 1, kLaterDen = 4;  // P = rows per compute unit * kLaterNum / kLaterDen
+constexpr int64_t kAggRows = 256;                 // Y
 
 
 // Longest segment whose rows span under 2^31 bytes of any activation (buffer windows).
@@ -820,18 +884,26 @@ Plan make_plan(const SelectiveScanArgs& a) {
     pl.T = T;
     pl.nseg = 0;
     pl.U = (a.L + T - 1) / T + a.nseq;  // upper bound on sum of ceil(len / T)
-    // the packed plan, when its one-dimensional scan grid fits
+    // the packed plan, when its one-dimensional scan grids fit
     const int64_t nblk = (a.D + kThreads - 1) / kThreads;
     const int64_t per_cu = (a.L * nblk + device_cus() - 1) / device_cus();
-    int64_t X = (per_cu * kPieceNum / kPieceDen + kAggRows - 1) / kAggRows * kAggRows;
-    if (X < kAggRows) X = kAggRows;
-    if (X > max_T) X = max_T / kAggRows * kAggRows;
-    pl.X = X;
+    auto rows_of = [&](int64_t num, int64_t den) {
+      int64_t r = (per_cu * num / den + kAggRows - 1) / kAggRows * kAggRows;
+      if (r < kAggRows) r = kAggRows;
+      if (r > max_T) r = max_T / kAggRows * kAggRows;
+      return r;
+    };
+    pl.P = rows_of(kLaterNum, kLaterDen);
+    pl.F = rows_of(kFirstNum, kFirstDen);
     pl.Y = kAggRows;
     pl.A = (a.L + pl.Y - 1) / pl.Y;  // aggregate units are whole Y-row blocks inside one sequence
-    pl.C = (a.L + X - 1) / X;        // a sequence of len > X rows has ceil(len / X) - 1 <= len / X carries
-    pl.S = a.nseq + pl.C;            // scan units: one per sequence plus one per carry
-    pl.packed = X >= kAggRows && pl.S * nblk * kThreads < ((int64_t)1 << 31) && pl.A < ((int64_t)1 << 31);
+    // a sequence of len > F rows has a slot per piece but its last: ceil((len - F) / P) <=
+    // (len - F) / P + 1 <= len / min(F, P) of them
+    const int64_t m = pl.F < pl.P ? pl.F : pl.P;  // 0 when a Y-row block spans 2^31 bytes
+    pl.C = m > 0 ? (a.L + m - 1) / m : 0;
+    pl.S = a.nseq + pl.C;  // scan units: one per sequence plus one per slot
+    pl.packed = m >= kAggRows && (a.nseq + pl.A) * nblk * kThreads < ((int64_t)1 << 31) &&
+                pl.S * nblk * kThreads < ((int64_t)1 << 31);
   }
   return pl;
 }
@@ -841,11 +913,11 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 template <typename Tin, typename Tout>
 hipError_t launch_packed_by_n(const SelParams& p, const Plan& pl, bool softplus, hipStream_t s) {
   switch (p.N) {
-    case 1: return launch_packed<Tin, Tout, 1>(p, pl.A, pl.C, pl.S, softplus, s);
-    case 2: return launch_packed<Tin, Tout, 2>(p, pl.A, pl.C, pl.S, softplus, s);
-    case 4: return launch_packed<Tin, Tout, 4>(p, pl.A, pl.C, pl.S, softplus, s);
-    case 8: return launch_packed<Tin, Tout, 8>(p, pl.A, pl.C, pl.S, softplus, s);
-    default: return launch_packed<Tin, Tout, 16>(p, pl.A, pl.C, pl.S, softplus, s);
+    case 1: return launch_packed<Tin, Tout, 1>(p, pl.A, pl.C, softplus, s);
+    case 2: return launch_packed<Tin, Tout, 2>(p, pl.A, pl.C, softplus, s);
+    case 4: return launch_packed<Tin, Tout, 4>(p, pl.A, pl.C, softplus, s);
+    case 8: return launch_packed<Tin, Tout, 8>(p, pl.A, pl.C, softplus, s);
+    default: return launch_packed<Tin, Tout, 16>(p, pl.A, pl.C, softplus, s);
   }
 }
 
@@ -1749,8 +1821,8 @@ hipError_t launch_selective_scan(const SelectiveScanArgs& a, hipStream_t s) {
     int4* aggt = reinterpret_cast<int4*>(q); q += align256((size_t)pl.A * sizeof(int4));
     int4* seqt = reinterpret_cast<int4*>(q);
     p.vcount = count; p.vscan = scan; p.vagg = aggt; p.vseq = seqt; p.vpiece = piece;
-    hipLaunchKernelGGL(selective_vplan_kernel, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.nseq, pl.X, pl.Y, count,
-                       scan, aggt, seqt, piece, a.D, a.N, a.h0, a.h_last);
+    hipLaunchKernelGGL(selective_vplan_kernel, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.nseq, pl.F, pl.P, pl.Y,
+                       count, scan, aggt, seqt, piece, a.D, a.N, a.h0, a.h_last);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return a.out_bf16 ? launch_packed_by_n<bf16_t, bf16_t>(p, pl, a.dt_softplus != 0, s)
