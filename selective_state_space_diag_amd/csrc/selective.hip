@@ -57,8 +57,11 @@ struct SelParams {
   const float* h0;
   void* y;
   float* h_last;
-  float* aggP;   // [unit][N][D]  product of abar over the segment
+  float* aggP;   // [unit][N][D]  product of abar over the segment (clamp variant only, see sdelta)
   float* aggH;   // [unit][N][D]  state reached from zero at the segment end
+  float* sdelta;  // [unit][D]   delta summed over the segment: where the clamp cannot act (softplus
+                  //  steps, A_n <= 0) the product of abar is 2^(A_n log2(e) sdelta), as pass 1 forms it
+  int softplus;
   float* carry;  // [unit][N][D]  state entering the segment
   const int2* seq_units;  // varlen: (first unit, unit count) per sequence
   // Packed varlen forward plan (NULL for the other launches): scan units of whole sequences or of
@@ -188,7 +191,7 @@ __device__ __forceinline__ float row_step(float xx, float dd, float zz, const fl
     // states in groups of 8: bounds the exponentials held in flight (register pressure)
     if (NS > 8 && (n & 7) == 7) __builtin_amdgcn_sched_barrier(0);
   }
-  if (DISC != kClamp && !READOUT) sum_delta += delta;
+  if (!READOUT) sum_delta += delta;
   if (READOUT) {
     acc = fmaf(dskip, xx, acc);
     if (GATE) acc *= silu_f(zz);
@@ -328,14 +331,24 @@ __device__ __forceinline__ void agg_unit(const SelParams& p, int64_t u, int64_t 
     run_rows<Tin, float, NS, SOFTPLUS, kClamp, false, false>(p, U.row0, U.row1, dl, A2, bias, 0.0f, h, e, sum_delta,
                                                              lds);
   if (!active) return;
+  // prod abar = 2^(sum of the exponents): A2 sum(delta) without the clamp (rebuilt from the stored
+  // delta sum where it is read), else the clamped sum
+  p.sdelta[u * p.D + d] = sum_delta;
 #pragma unroll
   for (int n = 0; n < NS; ++n) {
-    // prod abar = 2^(sum of the exponents): A2 sum(delta) without the clamp, else the clamped sum
-    const float P = disc == kExp ? hw_exp2(A2[n] * sum_delta) : hw_exp2(e[n]);
-    p.aggP[(u * NS + n) * p.D + d] = P;
+    if (disc == kClamp) p.aggP[(u * NS + n) * p.D + d] = hw_exp2(e[n]);
     p.aggH[(u * NS + n) * p.D + d] = h[n];
   }
 }
+
+// Product of abar over aggregate unit u for state n of channel d: rebuilt from the unit's delta sum
+// where the clamp cannot act, else the stored product.  One load either way (decay_src), issued
+// with the others before any is used (decay_of).
+template <int NS>
+__device__ __forceinline__ const float* decay_src(const SelParams& p, int64_t u, int n, int64_t d, bool from_sum) {
+  return from_sum ? p.sdelta + u * p.D + d : p.aggP + (u * NS + n) * p.D + d;
+}
+__device__ __forceinline__ float decay_of(float v, float A2n, bool from_sum) { return from_sum ? hw_exp2(A2n * v) : v; }
 
 template <typename Tin, int NS, bool SOFTPLUS>
 __global__ __launch_bounds__(kThreads, 4) void selective_aggregate_kernel(SelParams p) {
@@ -356,20 +369,33 @@ __global__ __launch_bounds__(kThreads) void selective_vpiece_kernel(SelParams p)
   const int64_t first = pc.x;
   const int q = pc.y;
   if (q == 0) return;  // a first piece's slot: its scan leaves the end state there
-  float Pp[NS], Hp[NS];
+  float Pp[NS], Hp[NS], A2[NS];
+  bool from_sum[NS];
 #pragma unroll
-  for (int n = 0; n < NS; ++n) { Pp[n] = 1.0f; Hp[n] = 0.0f; }
+  for (int n = 0; n < NS; ++n) {
+    Pp[n] = 1.0f;
+    Hp[n] = 0.0f;
+    const float a = p.A[d * NS + n];
+    A2[n] = a * kLog2e;
+    from_sum[n] = p.softplus && !(a > 0.0f);
+  }
   constexpr int JB = 4;
   for (int j0 = 0; j0 < q; j0 += JB) {
     float Pj[JB][NS], Hj[JB][NS];
 #pragma unroll
     for (int jj = 0; jj < JB; ++jj) {
-      const int64_t base = (first + min(j0 + jj, q - 1)) * NS * p.D + d;
+      const int64_t uj = first + min(j0 + jj, q - 1);
+      const int64_t base = uj * NS * p.D + d;
 #pragma unroll
       for (int n = 0; n < NS; ++n) {
-        Pj[jj][n] = p.aggP[base + n * p.D];
+        Pj[jj][n] = *decay_src<NS>(p, uj, n, d, from_sum[n]);
         Hj[jj][n] = p.aggH[base + n * p.D];
       }
+    }
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj) {
+#pragma unroll
+      for (int n = 0; n < NS; ++n) Pj[jj][n] = decay_of(Pj[jj][n], A2[n], from_sum[n]);
     }
 #pragma unroll
     for (int jj = 0; jj < JB; ++jj) {
@@ -505,16 +531,20 @@ __global__ __launch_bounds__(kThreads) void selective_carry_kernel(SelParams p) 
     count = r.y;
   }
   float h = p.h0 ? p.h0[(seq * p.D + d) * NS + n] : 0.0f;
+  const float a = p.A[d * NS + n];
+  const float A2 = a * kLog2e;
+  const bool from_sum = p.softplus && !(a > 0.0f);
   constexpr int K = 32;
   for (int64_t s0 = 0; s0 < count; s0 += K) {
     float P[K], H[K];
 #pragma unroll
     for (int q = 0; q < K; ++q) {
       const int64_t s = min(s0 + q, count - 1);
-      const int64_t idx = ((first + s) * NS + n) * p.D + d;
-      P[q] = p.aggP[idx];
-      H[q] = p.aggH[idx];
+      P[q] = *decay_src<NS>(p, first + s, (int)n, d, from_sum);
+      H[q] = p.aggH[((first + s) * NS + n) * p.D + d];
     }
+#pragma unroll
+    for (int q = 0; q < K; ++q) P[q] = decay_of(P[q], A2, from_sum);
 #pragma unroll
     for (int q = 0; q < K; ++q) {
       const int64_t s = s0 + q;
@@ -1786,11 +1816,13 @@ bool use_packed_plan(const SelectiveScanArgs& a, const Plan& pl) { return a.cu_s
 
 size_t selective_scan_scratch_bytes(const SelectiveScanArgs& a) {
   const Plan pl = make_plan(a);
-  size_t bytes = workspace_head_bytes() + 3 * align256((size_t)pl.U * a.N * a.D * sizeof(float));
+  size_t bytes = workspace_head_bytes() + 3 * align256((size_t)pl.U * a.N * a.D * sizeof(float)) +
+                 align256((size_t)pl.U * a.D * sizeof(float));
   if (a.cu_seqlens) bytes += align256(256 + (size_t)pl.U * sizeof(int2)) + align256((size_t)a.nseq * sizeof(int2));
   if (a.cu_seqlens && pl.packed) {  // the query does not know the input dtype: room for either plan
     const size_t st = (size_t)a.N * a.D * sizeof(float);
-    const size_t packed = workspace_head_bytes() + 2 * align256((size_t)pl.A * st) + 2 * align256((size_t)pl.C * st) +
+    const size_t packed = workspace_head_bytes() + 2 * align256((size_t)pl.A * st) +
+                          align256((size_t)pl.A * a.D * sizeof(float)) + 2 * align256((size_t)pl.C * st) +
                           align256((size_t)pl.C * sizeof(int2)) + 256 +
                           align256((size_t)pl.S * sizeof(int4)) + align256((size_t)pl.A * sizeof(int4)) +
                           align256((size_t)a.nseq * sizeof(int4));
@@ -1806,6 +1838,7 @@ hipError_t launch_selective_scan(const SelectiveScanArgs& a, hipStream_t s) {
   p.cu = a.cu_seqlens; p.units = nullptr; p.n_units = nullptr; p.seq_units = nullptr;
   p.x = a.x; p.dt = a.dt; p.A = a.A; p.Bm = a.Bm; p.Cm = a.Cm; p.Dskip = a.Dskip; p.z = a.z;
   p.dt_bias = a.dt_bias; p.h0 = a.h0; p.y = a.y; p.h_last = a.h_last;
+  p.softplus = a.dt_softplus != 0;
   p.nblk = (a.D + kThreads - 1) / kThreads;
   char* base = static_cast<char*>(a.scratch) + workspace_head_bytes();
   if (use_packed_plan(a, pl)) {
@@ -1813,6 +1846,7 @@ hipError_t launch_selective_scan(const SelectiveScanArgs& a, hipStream_t s) {
     char* q = base;
     p.aggP = reinterpret_cast<float*>(q); q += align256((size_t)pl.A * st);
     p.aggH = reinterpret_cast<float*>(q); q += align256((size_t)pl.A * st);
+    p.sdelta = reinterpret_cast<float*>(q); q += align256((size_t)pl.A * a.D * sizeof(float));
     p.pieceP = reinterpret_cast<float*>(q); q += align256((size_t)pl.C * st);
     p.pieceH = reinterpret_cast<float*>(q); q += align256((size_t)pl.C * st);
     int2* piece = reinterpret_cast<int2*>(q); q += align256((size_t)pl.C * sizeof(int2));
@@ -1832,8 +1866,9 @@ hipError_t launch_selective_scan(const SelectiveScanArgs& a, hipStream_t s) {
   p.aggP = reinterpret_cast<float*>(base);
   p.aggH = reinterpret_cast<float*>(base + agg);
   p.carry = reinterpret_cast<float*>(base + 2 * agg);
+  p.sdelta = reinterpret_cast<float*>(base + 3 * agg);
   if (a.cu_seqlens) {
-    char* tbl = base + 3 * agg;
+    char* tbl = base + 3 * agg + align256((size_t)pl.U * a.D * sizeof(float));
     const size_t tbl_bytes = align256(256 + (size_t)pl.U * sizeof(int2));
     p.n_units = reinterpret_cast<int*>(tbl);
     p.units = reinterpret_cast<const int2*>(tbl + 256);

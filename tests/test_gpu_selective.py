@@ -147,14 +147,16 @@ def test_varlen_single_sequence_equals_batched(dtype):
     assert_close(host(hv), host(hb), 1e-4, "packed vs batched h_last")
 
 
+@pytest.mark.parametrize("with_h0", [True, False])
 @pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
-def test_varlen_long_sequences_cut_into_pieces(dtype):
-    """Packed sequences longer than the plan's piece length are cut into pieces of whole 256-row
-    aggregate blocks (here 700 -> 256 + 256 + 188, 1300 -> 5 x 256 + 20, 257 -> 256 + 1 rows); the
-    carries between pieces come from the aggregate and carry kernels."""
+def test_varlen_long_sequences_cut_into_pieces(dtype, with_h0):
+    """Packed sequences longer than the plan's piece length are cut into pieces.  bf16 inputs (the
+    two-phase plan, pieces of 256 rows here): 700 -> 256 + 256 + 188 rows (one middle piece), 1300
+    -> 256 + 4 x 256 + 20 (four), 257 -> 256 + 1 (none: the last piece starts from the first piece's
+    end state), 256 and 3 unsplit.  fp32 inputs take 16-row segments with the carry kernel."""
     lengths = [700, 3, 1300, 0, 257, 256]
     cu = synth.cu_seqlens_from_lengths(lengths)
-    inp = synth.selective_inputs(1, int(cu[-1]), 130, 16, dtype, 35, cu_seqlens=cu, with_h0=True)
+    inp = synth.selective_inputs(1, int(cu[-1]), 130, 16, dtype, 35, cu_seqlens=cu, with_h0=with_h0)
     check(inp, TOL[dtype])
 
 
