@@ -57,7 +57,7 @@ _NORM_SOURCES = [_CSRC + f for f in ("norm.hip", "common.hpp", "kernels.hpp")]
 PROFILES = {
     "headline": ("selective_varlen_L131072_D4096_N16.md",
                  "Packed varlen selective scan, L=131072 tokens in 32 sequences, D=4096, N=16, bf16 in, fp32 out; "
-                 "one call = planner + aggregate + carry + scan kernels", _SEL_SOURCES),
+                 "one call = planner + phase 1 (first pieces and aggregate units) + piece fold + phase 2 scan kernels", _SEL_SOURCES),
     "selective_B4_L2048_D1536_N16": ("selective_scan_B4_L2048_D1536_N16.md",
                                      "Batched selective scan B=4 L=2048 D=1536 N=16, bf16 in, fp32 out; one call = "
                                      "aggregate + carry + scan kernels", _SEL_SOURCES),
