@@ -81,7 +81,8 @@ __device__ __forceinline__ float wave_sum(float v) {
 template <typename Tg, typename Tout, int NC>
 __global__ __launch_bounds__(256) void readout_norm_wave_kernel(ReadoutNormArgs a) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  // the wave's row, in scalar registers: the windows over it stay wave-uniform
+  const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (row >= a.rows) return;  // whole wave
   const uint32_t width = (uint32_t)a.width;
   const auto wo = make_window(a.o + row * a.width, width * 4);

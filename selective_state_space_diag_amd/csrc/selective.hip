@@ -204,10 +204,21 @@ __device__ __forceinline__ float row_step(float xx, float dd, float zz, const fl
 // in registers.  Loads and stores are unconditional inside the unrolled groups (indices are
 // clamped in range) so the compiler counts outstanding memory operations exactly; a lane without a
 // channel of its own recomputes channel D-1 bit for bit and rewrites the same value.
+// The workgroup's rows, marked wave-uniform (scalar registers): where the compiler cannot prove it
+// (a unit read from a table in a kernel with two roles), it would otherwise keep the windows built
+// from them in vector registers and wrap every buffer access in a loop over distinct values.
+__device__ __forceinline__ int64_t wave_uniform(int64_t v) {
+  const uint64_t u = (uint64_t)v;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u), hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 template <typename Tin, typename Tout, int NS, bool SOFTPLUS, int DISC, bool READOUT, bool GATE>
 __device__ __forceinline__ void run_rows(const SelParams& p, int64_t row0, int64_t row1, int64_t dl,
                                          const float* A2, float bias, float dskip, float* h, float* e,
                                          float& sum_delta, float* lds) {
+  row0 = wave_uniform(row0);
+  row1 = wave_uniform(row1);
   using W = win<Tin, 1>;
   using Stage = BCStage<NS, READOUT>;
   constexpr int PR = Stage::PER_ROW;
