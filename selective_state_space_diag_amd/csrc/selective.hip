@@ -1377,6 +1377,10 @@ struct BwdLds {
   alignas(16) float Bt[NS][kBU];     // [n][row]: one state's rows of a sub-block are contiguous
   alignas(16) float Ct[NS][kBU];
   float redB[NS][kThreads / 64][kBT], redC[NS][kThreads / 64][kBT];
+  // per lane and state: q entering the current sub-block from its end, and dA summed so far.  The
+  // state loop indexes them by a loop counter; in registers that would be indexed register access
+  // (a mode switch around every read and write)
+  float qv[NS][kThreads], dA[NS][kThreads];
 };
 
 template <typename Tin, typename Tout, int NS, bool SOFTPLUS, bool GATE, int DISC, typename Lds>
@@ -1408,11 +1412,10 @@ __device__ __forceinline__ void bwd_grad_unit(const SelBwdParams& p, const BUnit
     }
   }
 
-  float qv[NS], dAv[NS];
 #pragma unroll
   for (int n = 0; n < NS; ++n) {
-    qv[n] = p.qend[(u * NS + n) * p.D + dl];
-    dAv[n] = 0.0f;
+    S.qv[n][tid] = p.qend[(u * NS + n) * p.D + dl];
+    S.dA[n][tid] = 0.0f;
   }
 
   // ---- forward sweep: the states at the sub-block starts.  After it s3 holds the start of sub-block
@@ -1545,7 +1548,7 @@ __device__ __forceinline__ void bwd_grad_unit(const SelBwdParams& p, const BUnit
       const float4* Bn4 = reinterpret_cast<const float4*>(&S.Bt[n][r0]);
       const float4* Cn4 = reinterpret_cast<const float4*>(&S.Ct[n][r0]);
       float h = s3[n];
-      const float q_in = qv[n];
+      const float q_in = S.qv[n][tid];
       float q = q_in;
       // forward through the rows, keeping abar and h_{t-1} for the way back
       float v[16], abr[kBT], hpr[kBT];
@@ -1607,12 +1610,12 @@ __device__ __forceinline__ void bwd_grad_unit(const SelBwdParams& p, const BUnit
       // bf16 inputs: the chained q itself (a unit's 64 rounded decays move it by a few fp32 ulps, far
       // below what the inputs' rounding allows), which saves the second recurrence
       if (kChainQ) {
-        qv[n] = q;
+        S.qv[n][tid] = q;
       } else {
         const float Pj = DISC == kClamp ? hw_exp2(es_j) : hw_exp2(A2 * sd_j);
-        qv[n] = fmaf(Pj, q_in, qz);
+        S.qv[n][tid] = fmaf(Pj, q_in, qz);
       }
-      dAv[n] += dA;
+      S.dA[n][tid] += dA;
     }
 
     // row gradients
@@ -1666,8 +1669,8 @@ __device__ __forceinline__ void bwd_grad_unit(const SelBwdParams& p, const BUnit
   if (active) {
 #pragma unroll
     for (int n = 0; n < NS; ++n) {
-      p.dA_part[(u * NS + n) * p.D + d] = dAv[n];
-      if (U.first && p.dh0) p.dh0[(U.seq * p.D + d) * NS + n] = qv[n];
+      p.dA_part[(u * NS + n) * p.D + d] = S.dA[n][tid];
+      if (U.first && p.dh0) p.dh0[(U.seq * p.D + d) * NS + n] = S.qv[n][tid];
     }
     p.dD_part[u * p.D + d] = dsum;
     p.dbias_part[u * p.D + d] = bsum;
