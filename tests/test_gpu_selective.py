@@ -118,6 +118,24 @@ def test_clamp_acts_for_positive_A():
     check(inp, TOL[synth.F32])
 
 
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+def test_positive_A_beside_negative_A_with_softplus_steps(dtype, packed):
+    """A few states with A > 0 put their channels' waves on the clamped path, where the other channels
+    of those waves still have A <= 0: the carries rebuild the segment decay of those channels from the
+    segment's delta sum and read the stored products of the others.  Several segments per sequence
+    (packed bf16: first, middle and last pieces), so every kind of carry is used."""
+    if packed:
+        cu = synth.cu_seqlens_from_lengths([700, 130, 1300, 3])
+        inp = synth.selective_inputs(1, int(cu[-1]), 130, 16, dtype, 37, cu_seqlens=cu, with_h0=True)
+    else:
+        inp = synth.selective_inputs(2, 300, 130, 16, dtype, 38, with_h0=True)
+    A = inp.p["A"].copy()
+    A[5, 3] = A[70, 0] = A[129, 15] = 0.004  # slow growth: finite over the longest sequence
+    inp.p["A"] = A
+    check(inp, TOL[dtype])
+
+
 def test_varlen_with_empty_and_unit_sequences():
     lengths = [5, 0, 1, 300, 0, 77, 2, 0]
     cu = synth.cu_seqlens_from_lengths(lengths)
