@@ -644,8 +644,9 @@ __global__ __launch_bounds__(256) void update1_kernel(Upd1Params p) {
 // 32-bit offsets, one 2V- or 4V-byte access per operand and vector; the channel parameters come in
 // one access as well.  All loads of a lane are issued before any arithmetic: a decode step is one
 // round trip to memory.
+constexpr unsigned kUpdThreads = 128;  // workgroup size of the vector decode step (see launch_update_v)
 template <class Op, typename Tin, typename Tout, bool GATE, int V, int U>
-__global__ __launch_bounds__(256) void update1v_kernel(Upd1Params p) {
+__global__ __launch_bounds__(kUpdThreads) void update1v_kernel(Upd1Params p) {
   const uint32_t n = (uint32_t)(p.B * p.D / V);  // vectors of V channels
   const uint32_t per_row = (uint32_t)(p.D / V);
   const uint32_t elems = (uint32_t)(p.B * p.D);
@@ -665,7 +666,7 @@ __global__ __launch_bounds__(256) void update1v_kernel(Upd1Params p) {
   typename Wf::raw rs[U], ra[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    g[u] = blockIdx.x * (256u * U) + u * 256u + threadIdx.x;
+    g[u] = blockIdx.x * (kUpdThreads * U) + u * kUpdThreads + threadIdx.x;
     const uint32_t gc = g[u] < n ? g[u] : n - 1;  // lanes past the end reread the last vector
     const uint32_t d0 = (gc % per_row) * V;
 #pragma unroll
@@ -1332,20 +1333,22 @@ hipError_t launch_scan_op(Scan1Params& p, int in_bf16, int out_bf16, void* scrat
 
 // Vectors per lane in the decode step, and channels per vector (below): a step is one round trip to
 // memory followed by a short chain of arithmetic per lane, so many short lanes finish first.  Measured
-// at B = 256, D = 2560 bf16 from a HIP graph, with the step's inputs and y non-temporal: 2 channels x 1
-// vector 3.26 us per step, 4 x 1 3.51 us, 2 x 2 3.74 us (a plain device copy of the same bytes:
-// 2.6 us); with every access cached, 2 x 1 took 3.9 us.
+// at B = 256, D = 2560 bf16 from a HIP graph, with the step's inputs and y non-temporal, 256-thread
+// workgroups: 2 channels x 1 vector 3.26 us per step, 4 x 1 3.51 us, 2 x 2 3.74 us (a plain device
+// copy of the same bytes: 2.6 us); with every access cached, 2 x 1 took 3.9 us.  Workgroups of 128
+// threads: 3.15-3.19 us (64: 3.68-3.71, 512: 3.37, 1024: 3.66).
 constexpr int kUpdVectors = 1;
 template <class Op, bool GATE, int V>
 hipError_t launch_update_v(const Upd1Params& p, int in_bf16, int out_bf16, hipStream_t s) {
   constexpr int U = kUpdVectors;
-  const dim3 grid((unsigned)((p.B * p.D / V + 256 * U - 1) / (256 * U)));
+  constexpr int64_t per_wg = (int64_t)kUpdThreads * U;
+  const dim3 grid((unsigned)((p.B * p.D / V + per_wg - 1) / per_wg)), block(kUpdThreads);
   if (!in_bf16)
-    hipLaunchKernelGGL((update1v_kernel<Op, float, float, GATE, V, U>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((update1v_kernel<Op, float, float, GATE, V, U>), grid, block, 0, s, p);
   else if (out_bf16)
-    hipLaunchKernelGGL((update1v_kernel<Op, bf16_t, bf16_t, GATE, V, U>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((update1v_kernel<Op, bf16_t, bf16_t, GATE, V, U>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((update1v_kernel<Op, bf16_t, float, GATE, V, U>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((update1v_kernel<Op, bf16_t, float, GATE, V, U>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
