@@ -136,6 +136,20 @@ def test_positive_A_beside_negative_A_with_softplus_steps(dtype, packed):
     check(inp, TOL[dtype])
 
 
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+def test_varlen_more_sequences_than_one_planner_pass(dtype):
+    """1500 packed sequences (the planners take sequences 1024 at a time): short and empty ones on both
+    sides of the 1024 boundary, and three long ones cut into first, middle and last pieces."""
+    rng = np.random.default_rng(39)
+    lengths = rng.integers(0, 24, size=1500)
+    lengths[rng.choice(1500, 200, replace=False)] = 0
+    lengths[[10, 1023, 1024]] = [700, 0, 1300]
+    lengths[1499] = 611
+    cu = synth.cu_seqlens_from_lengths([int(v) for v in lengths])
+    inp = synth.selective_inputs(1, int(cu[-1]), 64, 16, dtype, 40, cu_seqlens=cu, with_h0=True)
+    check(inp, TOL[dtype])
+
+
 def test_varlen_with_empty_and_unit_sequences():
     lengths = [5, 0, 1, 300, 0, 77, 2, 0]
     cu = synth.cu_seqlens_from_lengths(lengths)
